@@ -1,0 +1,23 @@
+"""Float64 CPU oracle for chunked (ring) attention. TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import anything from this package. The product path (the HIP
+library and its Python binding) never calls it and shares no code with it.
+
+Contents:
+  attention.attention    plain masked softmax attention, full score matrix
+  attention.allowed      the element mask from positions and segment IDs
+  attention.merge        the sigmoid/softplus LSE merge
+  attention.chunked      attention per KV chunk folded with ``merge``
+  blockmask.block_mask   tile classes and compacted non-empty tile lists
+
+Every function is pinned by tests under ``tests/test_oracle_*.py`` against
+closed forms, library routines, brute force and invariants; the soft-cap
+formula itself is a reading (the pages give only the parameter), pinned to its
+closed form and its large-cap limit, but not to any value on the pages.
+"""
+from .attention import allowed, attention, merge, chunked, DEFAULT_MASK_VALUE, PAD_SEGMENT_ID
+from .blockmask import block_mask, TILE_EMPTY, TILE_PARTIAL, TILE_FULL
+
+__all__ = ["allowed", "attention", "merge", "chunked", "block_mask", "DEFAULT_MASK_VALUE",
+           "PAD_SEGMENT_ID", "TILE_EMPTY", "TILE_PARTIAL", "TILE_FULL"]

@@ -1,0 +1,163 @@
+"""Plain float64 attention, element mask and LSE merge. TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline may use this.
+
+Sources (the pages):
+  [ring]  ejkernel module source page "ejkernel.kernels._pallas.tpu.ring_attention._ring_splash":
+          _update_out_and_lse (the merge), _ring_attention_forward (causal
+          predicate on shifted q ids, sinks only on the first ring step, fp32
+          accumulators, output cast to the q dtype).
+  [api]   ejkernel API page for the same module: the default mask_value.
+  [kvax]  "Kvax: Flash Attention for JAX" page: flash_attention and
+          create_attention_mask arguments ([B,S,H,D] layouts, positions and
+          segment IDs, padding segment, scale).
+
+The method reaches, up to rounding order, ordinary masked softmax attention
+over the full key set, so ``attention`` is that definition written out: it
+builds every score, masks it, and normalises, with no tiling and no online
+softmax. Readings of points the pages leave open (see the project design notes):
+  * a sink is one extra logit per query head in the normaliser with no value
+    row; it is neither scaled nor capped;
+  * masked pairs are excluded exactly (weight 0); a row with nothing allowed
+    gives out = 0 and lse = -inf (lse = sink with a sink);
+  * the soft cap is cap * tanh(s / cap) on the scaled logit s = scale * q.k;
+  * causal means kv_pos <= q_pos; segments must be equal and not padding;
+  * query head h reads KV head h // (H / Hkv);
+  * lse is the natural log, laid out [B, H, Sq].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# The finite mask value printed on the [api] page, equal to -0.7 * float32 max.
+DEFAULT_MASK_VALUE = -2.381976426469702e38
+# Padding segment ID ([kvax] names the constant without a value; -1 is the reading).
+PAD_SEGMENT_ID = -1
+
+
+def allowed(q_pos, kv_pos, q_seg=None, kv_seg=None, causal=True):
+    """Element mask for one batch row: [Sq, Skv] bool.
+
+    [ring] _ring_attention_forward: the causal mask keeps a key when the query
+    id is >= the key id, ids being positions shifted by the ring offsets.
+    [kvax] flash_attention: tokens attend within their own segment; padding
+    tokens carry the padding segment ID and take part in nothing.
+    """
+    q_pos = np.asarray(q_pos)
+    kv_pos = np.asarray(kv_pos)
+    ok = np.ones((q_pos.shape[0], kv_pos.shape[0]), dtype=bool)
+    if causal:
+        ok &= kv_pos[None, :] <= q_pos[:, None]
+    if q_seg is not None:
+        q_seg = np.asarray(q_seg)
+        kv_seg = np.asarray(kv_seg)
+        ok &= q_seg[:, None] == kv_seg[None, :]
+        ok &= (q_seg != PAD_SEGMENT_ID)[:, None]
+    return ok
+
+
+def attention(q, k, v, *, scale, q_pos, kv_pos, q_seg=None, kv_seg=None, causal=True,
+              softcap=None, sinks=None, rows=None, row_block=512):
+    """Masked softmax attention in float64 from the full score matrix.
+
+    q [B,Sq,H,D], k and v [B,Skv,Hkv,D]; positions [B,Sq] / [B,Skv]; segment
+    IDs the same or None; sinks [H] or None. ``rows`` restricts the query rows
+    computed (for sampled checks). Returns out [B,R,H,D] and lse [B,H,R] in
+    float64, R = Sq or len(rows).
+
+    For query row i of head h (KV head g = h // (H / Hkv)):
+        s_ij  = scale * sum_d q[i,h,d] k[j,g,d];   s_ij = cap*tanh(s_ij/cap) if capped
+        Z_i   = sum over allowed j of exp(s_ij)  (+ exp(sink_h) with sinks)
+        out_i = sum over allowed j of exp(s_ij) v[j,g,:] / Z_i    (0 if Z_i = 0)
+        lse_i = ln Z_i                                            (-inf if Z_i = 0)
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, Sq, H, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    G = H // Hkv
+    row_idx = np.arange(Sq) if rows is None else np.asarray(rows, np.int64)
+    R = row_idx.shape[0]
+    out = np.zeros((B, R, H, D))
+    lse = np.full((B, H, R), -np.inf)
+    for b in range(B):
+        for start in range(0, R, row_block):
+            r = row_idx[start:start + row_block]
+            ok = allowed(np.asarray(q_pos)[b, r], np.asarray(kv_pos)[b],
+                         None if q_seg is None else np.asarray(q_seg)[b, r],
+                         None if kv_seg is None else np.asarray(kv_seg)[b], causal)
+            for h in range(H):
+                g = h // G
+                s = scale * (q[b, r, h, :] @ k[b, :, g, :].T)
+                if softcap is not None:
+                    s = softcap * np.tanh(s / softcap)
+                s = np.where(ok, s, -np.inf)
+                if sinks is not None:
+                    s = np.concatenate([s, np.full((len(r), 1), float(sinks[h]))], axis=1)
+                m = s.max(axis=1)
+                m_safe = np.where(np.isfinite(m), m, 0.0)
+                e = np.exp(s - m_safe[:, None])
+                z = e.sum(axis=1)
+                num = e[:, :Skv] @ v[b, :, g, :]
+                nz = z > 0
+                o = np.zeros_like(num)
+                o[nz] = num[nz] / z[nz, None]
+                out[b, start:start + len(r), h, :] = o
+                lse[b, h, start:start + len(r)] = np.where(nz, m_safe + np.log(np.where(nz, z, 1.0)),
+                                                           -np.inf)
+    return out, lse
+
+
+def merge(out, lse, block_out, block_lse):
+    """Fold one chunk's (block_out, block_lse) into the running (out, lse), float64.
+
+    [ring] _update_out_and_lse: a row whose running lse is -inf takes the
+    block's values; otherwise, with x = block_lse - lse, the output moves
+    toward the block's by the weight sigmoid(x) and lse grows by softplus(x).
+    Layouts: out [B,Sq,H,D], lse [B,H,Sq].
+    """
+    out = np.asarray(out, np.float64)
+    lse = np.asarray(lse, np.float64)
+    block_out = np.asarray(block_out, np.float64)
+    block_lse = np.asarray(block_lse, np.float64)
+    is_first = lse == -np.inf
+    with np.errstate(invalid="ignore", over="ignore"):
+        x = np.where(is_first, 0.0, block_lse - lse)      # lse = -inf rows use the block values
+        sig = 1.0 / (1.0 + np.exp(-x))
+        softplus = np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+    w = np.transpose(sig, (0, 2, 1))[..., None]          # [B,H,Sq] -> [B,Sq,H,1]
+    new_out = out - w * (out - block_out)
+    new_lse = lse + softplus
+    first4 = np.transpose(is_first, (0, 2, 1))[..., None]
+    new_out = np.where(first4, block_out, new_out)
+    new_lse = np.where(is_first, block_lse, new_lse)
+    return new_out, new_lse
+
+
+def chunked(q, k, v, *, scale, q_pos, kv_pos, bounds, order, q_seg=None, kv_seg=None,
+            causal=True, softcap=None, sinks=None, rows=None):
+    """Attention per KV chunk, folded with ``merge`` in the given chunk order.
+
+    [ring] _ring_attention_forward: the running state starts at out = 0,
+    lse = -inf; each step attends to one KV chunk and merges it in; sinks
+    enter only on the first step. ``bounds`` lists each chunk's [start, end)
+    key range; ``order`` lists chunk indices in visiting order. Chunk segment
+    IDs and positions travel with their keys.
+    """
+    q = np.asarray(q, np.float64)
+    B, Sq, H, D = q.shape
+    R = Sq if rows is None else len(rows)
+    acc = np.zeros((B, R, H, D))
+    acc_lse = np.full((B, H, R), -np.inf)
+    for t, c in enumerate(order):
+        a, e = bounds[c]
+        o_c, l_c = attention(q, np.asarray(k)[:, a:e], np.asarray(v)[:, a:e], scale=scale,
+                             q_pos=q_pos, kv_pos=np.asarray(kv_pos)[:, a:e], q_seg=q_seg,
+                             kv_seg=None if kv_seg is None else np.asarray(kv_seg)[:, a:e],
+                             causal=causal, softcap=softcap,
+                             sinks=sinks if t == 0 else None, rows=rows)
+        acc, acc_lse = merge(acc, acc_lse, o_c, l_c)
+    return acc, acc_lse

@@ -1,0 +1,81 @@
+"""Plant one plausible mistake at a time in a copy of the oracle; some pin must fail.
+
+The mistakes are applied to the oracle's own source text on the CPU and run in
+a scratch module; the real oracle is untouched.
+"""
+import importlib
+import os
+import types
+
+import pytest
+
+import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+ATTN_MUTANTS = {
+    "gqa_modulo": ("g = h // G", "g = h % Hkv"),
+    "causal_strict": ("kv_pos[None, :] <= q_pos[:, None]", "kv_pos[None, :] < q_pos[:, None]"),
+    "causal_reversed": ("kv_pos[None, :] <= q_pos[:, None]", "kv_pos[None, :] >= q_pos[:, None]"),
+    "pad_attended": ("ok &= (q_seg != PAD_SEGMENT_ID)[:, None]", "pass"),
+    "segment_compare": ("q_seg[:, None] == kv_seg[None, :]", "q_seg[:, None] >= kv_seg[None, :]"),
+    "scale_dropped": ("s = scale * (", "s = ("),
+    "k_v_swapped": ("@ k[b, :, g, :].T", "@ v[b, :, g, :].T"),
+    "cap_factor_dropped": ("s = softcap * np.tanh(s / softcap)", "s = np.tanh(s / softcap)"),
+    "sink_every_chunk": ("sinks=sinks if t == 0 else None", "sinks=sinks"),
+    "sink_ignored": ("if sinks is not None:\n                    s = np.concatenate",
+                     "if False:\n                    s = np.concatenate"),
+    "merge_sigmoid_sign": ("sig = 1.0 / (1.0 + np.exp(-x))", "sig = 1.0 / (1.0 + np.exp(x))"),
+    "merge_softplus_dropped": ("new_lse = lse + softplus", "new_lse = np.maximum(lse, block_lse)"),
+    "merge_is_first_ignored": ("new_out = np.where(first4, block_out, new_out)", "pass"),
+    "lse_log2": ("m_safe + np.log(np.where", "m_safe + np.log2(np.where"),
+    "normaliser_off": ("o[nz] = num[nz] / z[nz, None]", "o[nz] = num[nz] / (z[nz, None] + 1e-3)"),
+}
+MASK_MUTANTS = {
+    "no_empty_tiles": ("elif tile.any():", "elif True:"),
+    "full_from_first_row": ("if tile.all():", "if tile[0].all():"),
+    "col_idx_unsorted": ("col_idx[qb, :len(nz)] = nz", "col_idx[qb, :len(nz)] = nz[::-1]"),
+}
+
+
+def _load(path, name, old, new):
+    src = open(path).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType(name)
+    mod.__file__ = path
+    exec(compile(src.replace(old, new), path, "exec"), mod.__dict__)
+    return mod
+
+
+def _mutant(which, key):
+    attn_path = os.path.join(ROOT, "oracle", "attention.py")
+    mask_path = os.path.join(ROOT, "oracle", "blockmask.py")
+    if which == "attn":
+        a = _load(attn_path, "mut_attention", *ATTN_MUTANTS[key])
+        m = importlib.import_module("oracle.blockmask")
+    else:
+        a = importlib.import_module("oracle.attention")
+        m = _load(mask_path, "mut_blockmask", *MASK_MUTANTS[key])
+    return types.SimpleNamespace(
+        attention=a.attention, allowed=a.allowed, merge=a.merge, chunked=a.chunked,
+        DEFAULT_MASK_VALUE=a.DEFAULT_MASK_VALUE, block_mask=m.block_mask,
+        TILE_EMPTY=m.TILE_EMPTY, TILE_PARTIAL=m.TILE_PARTIAL, TILE_FULL=m.TILE_FULL)
+
+
+def _caught(ora):
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(ora)
+        except Exception:
+            return pin.__name__
+    return None
+
+
+@pytest.mark.parametrize("key", sorted(ATTN_MUTANTS))
+def test_attention_mutant_caught(key):
+    assert _caught(_mutant("attn", key)) is not None, f"no pin catches mutant {key}"
+
+
+@pytest.mark.parametrize("key", sorted(MASK_MUTANTS))
+def test_blockmask_mutant_caught(key):
+    assert _caught(_mutant("mask", key)) is not None, f"no pin catches mutant {key}"

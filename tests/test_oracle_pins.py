@@ -1,0 +1,10 @@
+"""The float64 oracle against its pins (closed forms, library routines, brute force, invariants)."""
+import pytest
+
+import oracle
+import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(oracle)
