@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked (ring) attention forward on one MI355X.
+
+A step is one ring_attn_fwd_1gpu call over one batch of synthetic input: the
+block-mask build of every chunk, eight chunk launches of the attention kernel
+(the first writes, the rest merge by LSE) and the final cast. The workload is
+long-context causal attention: B=1, H=32 query heads over Hkv=8 KV heads,
+32768 queries, 32768 keys in 8 sequential chunks of 4096, D=128, bf16 q, k
+~ N(0,1) and v ~ U(-1,1). Inputs are resident in HBM before timing starts.
+
+value: effective TFLOP/s = 4*D*H*(non-EMPTY 128x128 tiles over all chunks)*128^2
+       divided by the step time.
+roofline: the attention chunk kernel alone, timed launch by launch with HIP
+       events on the stream it runs on; achieved = its effective FLOPs per
+       launch / its mean launch time, against the dense bf16 MFMA peak.
+cpu_baseline: the float64 oracle on a bounded sample of query rows of the
+       same workload (all heads, all keys), in pair FLOPs per second.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import ring_attention_merge_amd as ram  # noqa: E402
+from ring_attention_merge_amd import workloads as wl  # noqa: E402
+
+METRIC = "effective attention fwd TFLOP/s (unmasked tiles) and % bf16 MFMA peak, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+REF_TILE = 128                  # fixed reference tiling for effective FLOPs
+ATTN_KERNEL = "attn_fwd_bf16<128, false>"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload(name: str):
+    return {
+        "c5": wl.c5_long_causal,
+        "c4": wl.c4_gqa_cap_sinks,
+        "c4mqa": lambda: wl.c4_gqa_cap_sinks(Hkv=1),
+        "c3": wl.c3_packed_docs,
+        "c2": wl.c2_ring_shard,
+    }[name]()
+
+
+def ring_chunk_src(w, c, dev):
+    """Mask source of chunk c of the ring (positions and segments travel with the chunk)."""
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    q_base = (w.q_shard * w.Sq if w.q_shard >= 0 else 0)
+    kp = None if w.kv_pos is None else t(w.kv_pos[:, c * w.chunk:(c + 1) * w.chunk])
+    ks = None if w.kv_seg is None else t(w.kv_seg[:, c * w.chunk:(c + 1) * w.chunk])
+    return ram.MaskSrc(q_pos=t(w.q_pos), kv_pos=kp, q_pos_base=q_base, kv_pos_base=c * w.chunk,
+                       q_seg=t(w.q_seg), kv_seg=ks)
+
+
+def order(w):
+    N = w.n_chunks
+    return [((w.q_shard - t) % N) if w.q_shard >= 0 else t for t in range(N)]
+
+
+def tile_counts(w, desc, dev, tile_q, tile_kv):
+    """Non-EMPTY tiles per chunk at (tile_q, tile_kv), from the library's block-mask builder."""
+    counts = []
+    for c in range(w.n_chunks):
+        d = ram.Desc(**{**desc.__dict__, "block_q": tile_q, "block_kv": tile_kv})
+        bm = ram.alloc_block_mask(d, device=dev)
+        ram.build_block_mask(d, ring_chunk_src(w, c, dev), bm)
+        torch.cuda.synchronize()
+        counts.append(int(bm.row_cnt[: d.B * bm.nQb].sum().item()))
+    return counts
+
+
+def cpu_baseline(w, n_rows: int):
+    import oracle
+    from threadpoolctl import threadpool_info
+    rows = wl.sampled_rows(w.Sq, w.chunk, n=n_rows, seed=2024)
+    q, k, v, sinks = w.as_f64()
+    qp, kp = w.positions()
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, scale=w.scale, q_pos=qp, kv_pos=kp, q_seg=w.q_seg, kv_seg=w.kv_seg,
+                     causal=w.causal, softcap=w.softcap, sinks=sinks, rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = 0
+    for b in range(w.B):
+        ok = oracle.allowed(qp[b, rows], kp[b], None if w.q_seg is None else w.q_seg[b, rows],
+                            None if w.kv_seg is None else w.kv_seg[b], w.causal)
+        pairs += int(ok.sum())
+    flops = 4.0 * w.D * w.H * pairs
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(rows)} of {w.Sq} query rows x all {w.H} heads x all {w.Skv} keys, float64 "
+                      f"numpy oracle (full score rows, BLAS dgemm), {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c5", choices=["c5", "c4", "c4mqa", "c3", "c2"])
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); this path has no multi-GPU "
+              "mode: the ring's chunks run as a sequential loop on one device.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+
+    log(f"generating workload {args.workload} ...")
+    w = workload(args.workload)
+    dcode = ram.RAM_BF16 if w.dtype == "bf16" else ram.RAM_F32
+    desc = ram.Desc(B=w.B, Sq=w.Sq, Skv=w.chunk, H=w.H, Hkv=w.Hkv, D=w.D, dtype=dcode, scale=w.scale,
+                    softcap=w.softcap or 0.0, causal=w.causal)
+    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+    sinks = None if w.sinks is None else w.sinks.to(dev)
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    src = ram.MaskSrc(q_pos=t(w.q_pos), kv_pos=t(w.kv_pos), q_seg=t(w.q_seg), kv_seg=t(w.kv_seg))
+    out = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.Sq, dtype=torch.float32, device=dev)
+    ws = torch.empty(ram.ring_attn_workspace_bytes(desc, w.n_chunks), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ref_tiles = tile_counts(w, desc, dev, REF_TILE, REF_TILE)
+    eff_flops_chunk = [4.0 * w.D * w.H * n * REF_TILE * REF_TILE for n in ref_tiles]
+    eff_flops = sum(eff_flops_chunk)
+    log(f"non-empty {REF_TILE}x{REF_TILE} tiles per chunk: {ref_tiles}; effective FLOPs {eff_flops:.4e}")
+
+    def step():
+        ram.ring_attn_fwd_1gpu(desc, w.n_chunks, w.q_shard, q, k, v, src, sinks, out, lse, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = eff_flops / (ms * 1e-3) / 1e12
+    log(f"step {ms:.3f} ms, {tflops:.1f} effective TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak)")
+
+    # Roofline of the dominant kernel: each chunk launch timed alone on the same stream.
+    bq, bk = ram.kernel_tile(dcode, w.D)
+    dk = ram.Desc(**{**desc.__dict__, "block_q": bq, "block_kv": bk, "kv_stride_b": w.Skv * w.Hkv * w.D})
+    masks, srcs = [], []
+    for c in range(w.n_chunks):
+        srcs.append(ring_chunk_src(w, c, dev))
+        bm = ram.alloc_block_mask(dk, device=dev)
+        ram.build_block_mask(dk, srcs[c], bm)
+        masks.append(bm)
+    acc = torch.empty(w.B, w.Sq, w.H, w.D, dtype=torch.float32, device=dev)
+    acc_lse = torch.empty(w.B, w.H, w.Sq, dtype=torch.float32, device=dev)
+    kv_elems = w.chunk * w.Hkv * w.D
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(w.n_chunks)]
+    reps = max(1, args.steps // 2)
+    per_chunk_ms = [0.0] * w.n_chunks
+    for rep in range(reps + 1):
+        for t_, c in enumerate(order(w)):
+            kc = k.view(-1)[c * kv_elems:]
+            vc = v.view(-1)[c * kv_elems:]
+            a, b = evs[t_]
+            a.record(stream)
+            ram.attn_fwd_chunk(dk, q, kc, vc, srcs[c], masks[c],
+                               sinks if t_ == 0 else None, 0 if t_ == 0 else 1, acc, acc_lse, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        if rep > 0:                      # first pass is a warm-up
+            for t_ in range(w.n_chunks):
+                per_chunk_ms[t_] += evs[t_][0].elapsed_time(evs[t_][1]) / reps
+    kern_ms = sum(per_chunk_ms)
+    flops_in_order = [eff_flops_chunk[c] for c in order(w)]
+    achieved = sum(flops_in_order) / (kern_ms * 1e-3) / 1e12
+    log("chunk kernel ms (visit order): " + ", ".join(f"{x:.3f}" for x in per_chunk_ms))
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": ATTN_KERNEL,
+                "launches_per_step": w.n_chunks, "mean_launch_us": round(1e3 * kern_ms / w.n_chunks, 2),
+                "flops_per_launch_mean": sum(eff_flops_chunk) / w.n_chunks}
+    del acc, acc_lse
+
+    cpu = None
+    if not args.no_cpu:
+        log(f"timing the float64 oracle on {args.cpu_rows} sampled rows ...")
+        cpu = cpu_baseline(w, args.cpu_rows)
+        log(f"oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "Sq": w.Sq, "Skv": w.Skv,
+                   "kv_chunks": w.n_chunks, "chunk": w.chunk, "D": w.D, "causal": w.causal,
+                   "softcap": w.softcap, "sinks": w.sinks is not None, "q_shard": w.q_shard,
+                   "effective_flops": eff_flops},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

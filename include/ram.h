@@ -1,0 +1,170 @@
+/*
+ * ram.h - C ABI of the chunked (ring) attention forward for MI355X (gfx950).
+ *
+ * What it computes. The ejkernel ring-splash source page (module
+ * ejkernel.kernels._pallas.tpu.ring_attention._ring_splash) runs, once per
+ * KV chunk of a ring, a block-sparse flash-attention forward that returns the
+ * chunk output and its per-row log-sum-exp, and folds each chunk into a
+ * running (out, lse) with the sigmoid/softplus merge of _update_out_and_lse.
+ * The Kvax page ("Kvax: Flash Attention for JAX", flash_attention and
+ * create_attention_mask) fixes the tensor layouts and the position /
+ * segment-ID masking. On one GPU the ring is a sequential loop over chunks.
+ *
+ * Conventions shared by every call:
+ *  - Tensor pointers are DEVICE pointers, allocated and owned by the caller.
+ *    The library allocates nothing and keeps no state besides a thread-local
+ *    error message.
+ *  - Layouts (row-major, innermost last): q and out [B, Sq, H, D];
+ *    k and v [B, Skv, Hkv, D]; lse [B, H, Sq] float32; positions and segment
+ *    IDs [B, S] int32. Within a batch, rows are dense (row stride H*D or
+ *    Hkv*D elements); the batch stride may be larger (a chunk view of a
+ *    longer KV), given in elements, 0 meaning dense.
+ *  - Every call validates all arguments on the host before it enqueues
+ *    anything. On a non-OK status nothing was launched and no output was
+ *    written; ram_last_error() describes the failure.
+ *  - Calls are asynchronous on `stream` (0 = the null stream).
+ *  - Query head h reads KV head h / (H / Hkv) (contiguous groups; Hkv == 1
+ *    is MQA).
+ *  - Scores: s = scale * q.k; with softcap > 0, s = softcap * tanh(s / softcap).
+ *    A pair (i, j) takes part iff (!causal || kv_pos[j] <= q_pos[i]) and,
+ *    with segment IDs, q_seg[i] == kv_seg[j] != RAM_PAD_SEGMENT_ID. Excluded
+ *    pairs get weight exactly 0 (the pages' finite mask value gives the same
+ *    result on every row that attends to at least one key).
+ *  - A sink (float32 [H], raw logit, neither scaled nor capped) adds
+ *    exp(sink[h]) to the softmax normaliser with no value row.
+ *  - A row with no allowed key (and no sink) has out = 0 and lse = -inf.
+ *  - lse is the natural log of the normaliser.
+ */
+#ifndef RAM_H
+#define RAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Segment ID of padding tokens. The Kvax page names the constant without a value. */
+#define RAM_PAD_SEGMENT_ID (-1)
+
+typedef enum {
+  RAM_OK = 0,
+  RAM_ERR_INVALID = 1,     /* bad argument: null pointer, bad shape, mismatched tiles */
+  RAM_ERR_UNSUPPORTED = 2, /* valid but not built: head dim, dtype, alignment */
+  RAM_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  RAM_ERR_HIP = 4          /* a HIP launch failed; message holds hipGetErrorString */
+} ram_status;
+
+typedef enum { RAM_F32 = 0, RAM_BF16 = 1 } ram_dtype;
+
+/* Tile classes: the ring-splash page names a block mask without codes. */
+typedef enum { RAM_TILE_EMPTY = 0, RAM_TILE_PARTIAL = 1, RAM_TILE_FULL = 2 } ram_tile_class;
+
+/* WRITE stores the chunk's (out, lse); MERGE folds them into (out, lse). */
+typedef enum { RAM_OUT_WRITE = 0, RAM_OUT_MERGE = 1 } ram_out_mode;
+
+typedef struct {
+  int32_t B, Sq, Skv, H, Hkv, D; /* Skv: keys of one chunk; H % Hkv == 0; D in {64, 128} */
+  int32_t dtype;                 /* ram_dtype of q, k, v (and of the final out) */
+  int64_t q_stride_b;            /* elements between batches of q; 0 = Sq*H*D */
+  int64_t kv_stride_b;           /* elements between batches of k and v; 0 = Skv*Hkv*D */
+  float scale;                   /* score scale (Kvax default is 1.0) */
+  float softcap;                 /* <= 0: off */
+  int32_t causal;                /* 0 or 1 */
+  int32_t block_q, block_kv;     /* tile of the block mask; attention needs ram_kernel_tile() */
+} ram_attn_desc;
+
+/* Positions and segment IDs for one (q, KV-chunk) pair (Kvax flash_attention
+ * arguments). A NULL position array means sequential positions base + index.
+ * Segment arrays are both NULL (no segment masking) or both set. */
+typedef struct {
+  const int32_t* q_pos;   /* [B, Sq] or NULL => q_pos_base + i */
+  const int32_t* kv_pos;  /* [B, Skv] or NULL => kv_pos_base + j */
+  int32_t q_pos_base, kv_pos_base;
+  const int32_t* q_seg;   /* [B, Sq] or NULL */
+  const int32_t* kv_seg;  /* [B, Skv] or NULL */
+  int64_t q_meta_stride_b;  /* elements between batches of q_pos/q_seg; 0 = Sq */
+  int64_t kv_meta_stride_b; /* elements between batches of kv_pos/kv_seg; 0 = Skv */
+} ram_mask_src;
+
+/* Block mask of one (q, KV-chunk) pair at tile (block_q, block_kv), with
+ * nQb = ceil(Sq/block_q), nKb = ceil(Skv/block_kv):
+ *   tile_class uint8 [B, nQb, nKb]: ram_tile_class of each tile; pairs past
+ *              the sequence ends do not count;
+ *   row_cnt    int32 [B, nQb]: number of non-EMPTY tiles in the tile row;
+ *   col_idx    int32 [B, nQb, nKb]: the row's non-EMPTY kv-tile indices in
+ *              ascending order, then -1 in the remaining slots. */
+typedef struct {
+  uint8_t* tile_class;
+  int32_t* row_cnt;
+  int32_t* col_idx;
+} ram_block_mask;
+
+/* Tile classes and compacted non-empty tile lists from positions and segment
+ * IDs (Kvax create_attention_mask; ring-splash MaskInfo block_mask and the
+ * lists of blocks to visit). Only desc->B, Sq, Skv, causal, block_q and
+ * block_kv are read; block_q and block_kv must lie in [16, 512]. Exact for
+ * every tile. */
+ram_status build_block_mask(const ram_attn_desc* desc, const ram_mask_src* src,
+                            const ram_block_mask* out, hipStream_t stream);
+
+/* One chunk of block-sparse attention forward (ring-splash
+ * _ring_attention_forward, the per-step kernel call), visiting only the
+ * non-EMPTY tiles of `mask` (built by build_block_mask at ram_kernel_tile()).
+ *   q [B,Sq,H,D], k and v [B,Skv,Hkv,D] in desc->dtype; sinks float32 [H] or NULL.
+ *   mode RAM_OUT_WRITE: out <- chunk output (float32 [B,Sq,H,D]), lse <- chunk
+ *        lse (float32 [B,H,Sq]), for every row (empty rows get 0 / -inf).
+ *   mode RAM_OUT_MERGE: (out, lse) hold a running state and are updated in
+ *        place with the merge of _update_out_and_lse: a row whose running lse
+ *        is -inf takes the chunk's values; otherwise, with x = chunk_lse - lse,
+ *        out -= sigmoid(x) * (out - chunk_out) and lse += softplus(x).
+ * `src` gives the masking data of this chunk (it must match the one the mask
+ * was built from). */
+ram_status attn_fwd_chunk(const ram_attn_desc* desc, const void* q, const void* k, const void* v,
+                          const ram_mask_src* src, const ram_block_mask* mask, const float* sinks,
+                          int32_t mode, float* out, float* lse, hipStream_t stream);
+
+/* Standalone merge of one chunk's (out_blk, lse_blk) into (out_acc, lse_acc),
+ * in place, by _update_out_and_lse of the ring-splash page. All float32;
+ * out_* [B,Sq,H,D], lse_* [B,H,Sq]. out_blk may not alias out_acc. */
+ram_status lse_merge(int32_t B, int32_t Sq, int32_t H, int32_t D, float* out_acc, float* lse_acc,
+                     const float* out_blk, const float* lse_blk, hipStream_t stream);
+
+/* The ring of _ring_attention_forward on one GPU: n_chunks KV chunks of
+ * desc->Skv keys each, k_all and v_all [B, n_chunks*Skv, Hkv, D], visited in
+ * sequence and merged by LSE into float32 accumulators; the result is cast to
+ * the q dtype (out [B,Sq,H,D]) with lse float32 [B,H,Sq].
+ *   q_shard >= 0: this q shard is ring index r = q_shard of n_chunks; step t
+ *     visits chunk (r - t) mod n_chunks, and sequential q positions start at
+ *     r * Sq + src->q_pos_base.
+ *   q_shard == -1: chunks are visited in order 0..n_chunks-1 and sequential q
+ *     positions start at src->q_pos_base.
+ *   Sequential KV positions are global: chunk c key j is c*Skv + j +
+ *     src->kv_pos_base. Explicit kv_pos / kv_seg arrays span all
+ *     n_chunks*Skv keys and travel with their chunk.
+ *   Sinks enter on the first visited chunk only.
+ * workspace: device memory of at least ring_attn_workspace_bytes(), 256-byte
+ * aligned; it holds the float32 output accumulator (bf16 only) and the block
+ * masks of every chunk. */
+ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32_t q_shard,
+                              const void* q, const void* k_all, const void* v_all,
+                              const ram_mask_src* src, const float* sinks, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes ring_attn_fwd_1gpu needs for this shape (0 on bad input). */
+size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks);
+
+/* The tile (block_q, block_kv) the attention kernel of (dtype, D) runs at;
+ * block masks passed to attn_fwd_chunk must be built at this tile. */
+ram_status ram_kernel_tile(int32_t dtype, int32_t D, int32_t* block_q, int32_t* block_kv);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* ram_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAM_H */

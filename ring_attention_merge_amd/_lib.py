@@ -1,0 +1,267 @@
+"""ctypes binding of libram (include/ram.h): argument marshalling only.
+
+Every step of the path runs in the HIP library; this module turns torch
+tensors into device pointers and the current HIP stream, checks that each
+tensor is on the GPU with the dtype and size the call reads (so a wrong tensor
+can never reach a kernel), and raises ``RamError`` with the library's message
+on a non-OK status. It fails loudly when libram.so is missing: there is no
+CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libram.so")
+
+RAM_OK, RAM_ERR_INVALID, RAM_ERR_UNSUPPORTED, RAM_ERR_WORKSPACE, RAM_ERR_HIP = range(5)
+RAM_F32, RAM_BF16 = 0, 1
+RAM_TILE_EMPTY, RAM_TILE_PARTIAL, RAM_TILE_FULL = 0, 1, 2
+RAM_OUT_WRITE, RAM_OUT_MERGE = 0, 1
+RAM_PAD_SEGMENT_ID = -1
+
+EXPORTS = ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
+           "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_last_error")
+
+
+class RamError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libram status {status}: {message}")
+        self.status = status
+
+
+class c_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Sq", ctypes.c_int32), ("Skv", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("q_stride_b", ctypes.c_int64),
+                ("kv_stride_b", ctypes.c_int64), ("scale", ctypes.c_float),
+                ("softcap", ctypes.c_float), ("causal", ctypes.c_int32),
+                ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32)]
+
+
+class c_mask_src(ctypes.Structure):
+    _fields_ = [("q_pos", ctypes.c_void_p), ("kv_pos", ctypes.c_void_p),
+                ("q_pos_base", ctypes.c_int32), ("kv_pos_base", ctypes.c_int32),
+                ("q_seg", ctypes.c_void_p), ("kv_seg", ctypes.c_void_p),
+                ("q_meta_stride_b", ctypes.c_int64), ("kv_meta_stride_b", ctypes.c_int64)]
+
+
+class c_block_mask(ctypes.Structure):
+    _fields_ = [("tile_class", ctypes.c_void_p), ("row_cnt", ctypes.c_void_p),
+                ("col_idx", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libram.so (once). Raises ImportError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libram.so not found at {path}; build it with "
+                          "`python -m ring_attention_merge_amd.build` (there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
+    P = ctypes.POINTER
+    lib.build_block_mask.argtypes = [P(c_desc), P(c_mask_src), P(c_block_mask), vp]
+    lib.attn_fwd_chunk.argtypes = [P(c_desc), vp, vp, vp, P(c_mask_src), P(c_block_mask), f32p, i32,
+                                   f32p, f32p, vp]
+    lib.lse_merge.argtypes = [i32, i32, i32, i32, f32p, f32p, f32p, f32p, vp]
+    lib.ring_attn_fwd_1gpu.argtypes = [P(c_desc), i32, i32, vp, vp, vp, P(c_mask_src), f32p, vp, f32p,
+                                       vp, ctypes.c_size_t, vp]
+    lib.ring_attn_workspace_bytes.argtypes = [P(c_desc), i32]
+    lib.ring_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.ram_kernel_tile.argtypes = [i32, i32, P(i32), P(i32)]
+    lib.ram_last_error.argtypes = []
+    lib.ram_last_error.restype = ctypes.c_char_p
+    for name in ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu", "ram_kernel_tile"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != RAM_OK:
+        raise RamError(status, load().ram_last_error().decode())
+
+
+# ------------------------------------------------------------------------------ descriptors
+@dataclass
+class Desc:
+    """Python side of ram_attn_desc (sizes, dtype, scale, soft cap, causal, tile)."""
+    B: int
+    Sq: int
+    Skv: int
+    H: int
+    Hkv: int
+    D: int
+    dtype: int = RAM_BF16
+    scale: float = 1.0
+    softcap: float = 0.0
+    causal: bool = True
+    block_q: int = 128
+    block_kv: int = 64
+    q_stride_b: int = 0
+    kv_stride_b: int = 0
+
+    def c(self) -> c_desc:
+        return c_desc(self.B, self.Sq, self.Skv, self.H, self.Hkv, self.D, self.dtype, self.q_stride_b,
+                      self.kv_stride_b, self.scale, self.softcap if self.softcap else 0.0,
+                      int(self.causal), self.block_q, self.block_kv)
+
+
+@dataclass
+class MaskSrc:
+    """Python side of ram_mask_src: int32 CUDA tensors or None (sequential / no segments)."""
+    q_pos: Optional[torch.Tensor] = None
+    kv_pos: Optional[torch.Tensor] = None
+    q_pos_base: int = 0
+    kv_pos_base: int = 0
+    q_seg: Optional[torch.Tensor] = None
+    kv_seg: Optional[torch.Tensor] = None
+    q_meta_stride_b: int = 0
+    kv_meta_stride_b: int = 0
+
+    def c(self, B: int, Sq: int, kv_len: int) -> c_mask_src:
+        for name, t, S, st in (("q_pos", self.q_pos, Sq, self.q_meta_stride_b),
+                               ("q_seg", self.q_seg, Sq, self.q_meta_stride_b),
+                               ("kv_pos", self.kv_pos, kv_len, self.kv_meta_stride_b),
+                               ("kv_seg", self.kv_seg, kv_len, self.kv_meta_stride_b)):
+            if t is not None:
+                _need(t, name, torch.int32, (B - 1) * (st or S) + S if B > 0 else 0)
+        return c_mask_src(_ptr(self.q_pos), _ptr(self.kv_pos), self.q_pos_base, self.kv_pos_base,
+                          _ptr(self.q_seg), _ptr(self.kv_seg), self.q_meta_stride_b, self.kv_meta_stride_b)
+
+
+@dataclass
+class BlockMask:
+    """Python side of ram_block_mask: uint8 / int32 CUDA tensors."""
+    tile_class: torch.Tensor
+    row_cnt: torch.Tensor
+    col_idx: torch.Tensor
+    nQb: int = 0
+    nKb: int = 0
+
+    def c(self, B: int) -> c_block_mask:
+        _need(self.tile_class, "tile_class", torch.uint8, B * self.nQb * self.nKb)
+        _need(self.row_cnt, "row_cnt", torch.int32, B * self.nQb)
+        _need(self.col_idx, "col_idx", torch.int32, B * self.nQb * self.nKb)
+        return c_block_mask(_ptr(self.tile_class), _ptr(self.row_cnt), _ptr(self.col_idx))
+
+
+def alloc_block_mask(desc: Desc, device="cuda") -> BlockMask:
+    """Allocate the three block-mask arrays for desc's shape and tile."""
+    nQb = -(-desc.Sq // desc.block_q)
+    nKb = -(-desc.Skv // desc.block_kv)
+    n = max(1, desc.B * nQb * nKb)
+    return BlockMask(torch.empty(n, dtype=torch.uint8, device=device),
+                     torch.empty(max(1, desc.B * nQb), dtype=torch.int32, device=device),
+                     torch.empty(n, dtype=torch.int32, device=device), nQb, nKb)
+
+
+# ------------------------------------------------------------------------------ helpers
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype, numel: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (device {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, the call reads {numel}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _tdtype(dtype: int):
+    return torch.bfloat16 if dtype == RAM_BF16 else torch.float32
+
+
+def _span(B, stride, dense):
+    return 0 if B == 0 else (B - 1) * (stride or dense) + dense
+
+
+# ------------------------------------------------------------------------------ entry points
+def kernel_tile(dtype: int, D: int):
+    """ram_kernel_tile: the (block_q, block_kv) the attention kernel runs at."""
+    bq, bk = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().ram_kernel_tile(dtype, D, ctypes.byref(bq), ctypes.byref(bk)))
+    return bq.value, bk.value
+
+
+def build_block_mask(desc: Desc, src: MaskSrc, out: BlockMask, stream=None):
+    """build_block_mask: tile classes and compacted non-empty tile lists."""
+    cd, cs = desc.c(), src.c(desc.B, desc.Sq, desc.Skv)
+    cb = out.c(desc.B)
+    _check(load().build_block_mask(ctypes.byref(cd), ctypes.byref(cs), ctypes.byref(cb), _stream(stream)))
+
+
+def attn_fwd_chunk(desc: Desc, q, k, v, src: MaskSrc, mask: BlockMask, sinks, mode: int, out, lse,
+                   stream=None):
+    """attn_fwd_chunk: one KV chunk, written (mode 0) or merged (mode 1) into out / lse."""
+    dt = _tdtype(desc.dtype)
+    _need(q, "q", dt, _span(desc.B, desc.q_stride_b, desc.Sq * desc.H * desc.D))
+    if desc.Skv > 0:
+        _need(k, "k", dt, _span(desc.B, desc.kv_stride_b, desc.Skv * desc.Hkv * desc.D))
+        _need(v, "v", dt, _span(desc.B, desc.kv_stride_b, desc.Skv * desc.Hkv * desc.D))
+    _need(out, "out", torch.float32, desc.B * desc.Sq * desc.H * desc.D)
+    _need(lse, "lse", torch.float32, desc.B * desc.H * desc.Sq)
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, desc.H)
+    cd, cs, cb = desc.c(), src.c(desc.B, desc.Sq, desc.Skv), mask.c(desc.B)
+    _check(load().attn_fwd_chunk(ctypes.byref(cd), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
+                                 ctypes.byref(cb), _ptr(sinks), mode, _ptr(out), _ptr(lse),
+                                 _stream(stream)))
+
+
+def lse_merge(out_acc, lse_acc, out_blk, lse_blk, stream=None):
+    """lse_merge: fold (out_blk, lse_blk) into (out_acc, lse_acc) in place; out [B,Sq,H,D]."""
+    B, Sq, H, D = out_acc.shape
+    n = B * Sq * H * D
+    for name, t, m in (("out_acc", out_acc, n), ("out_blk", out_blk, n), ("lse_acc", lse_acc, B * H * Sq),
+                       ("lse_blk", lse_blk, B * H * Sq)):
+        _need(t, name, torch.float32, m)
+    _check(load().lse_merge(B, Sq, H, D, _ptr(out_acc), _ptr(lse_acc), _ptr(out_blk), _ptr(lse_blk),
+                            _stream(stream)))
+
+
+def ring_attn_workspace_bytes(desc: Desc, n_chunks: int) -> int:
+    cd = desc.c()
+    return int(load().ring_attn_workspace_bytes(ctypes.byref(cd), n_chunks))
+
+
+def ring_attn_fwd_1gpu(desc: Desc, n_chunks: int, q_shard: int, q, k_all, v_all, src: MaskSrc, sinks,
+                       out, lse, workspace, stream=None):
+    """ring_attn_fwd_1gpu: all KV chunks in (ring) order, merged by LSE, cast to the q dtype."""
+    dt = _tdtype(desc.dtype)
+    kv_len = n_chunks * desc.Skv
+    _need(q, "q", dt, _span(desc.B, desc.q_stride_b, desc.Sq * desc.H * desc.D))
+    if kv_len > 0:
+        _need(k_all, "k_all", dt, _span(desc.B, desc.kv_stride_b, kv_len * desc.Hkv * desc.D))
+        _need(v_all, "v_all", dt, _span(desc.B, desc.kv_stride_b, kv_len * desc.Hkv * desc.D))
+    _need(out, "out", dt, desc.B * desc.Sq * desc.H * desc.D)
+    _need(lse, "lse", torch.float32, desc.B * desc.H * desc.Sq)
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, desc.H)
+    _need(workspace, "workspace", torch.uint8, 0)
+    cd, cs = desc.c(), src.c(desc.B, desc.Sq, kv_len)
+    _check(load().ring_attn_fwd_1gpu(ctypes.byref(cd), n_chunks, q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
+                                     ctypes.byref(cs), _ptr(sinks), _ptr(out), _ptr(lse), _ptr(workspace),
+                                     workspace.numel(), _stream(stream)))

@@ -1,0 +1,534 @@
+// Block-sparse attention forward for one KV chunk, with a fused LSE-merge epilogue.
+//
+// What it computes: the per-ring-step kernel call of the ejkernel ring-splash
+// source page (_ring_attention_forward): attention of q over one KV chunk,
+// returning the chunk output and log-sum-exp, then (merge mode) the fold of
+// _update_out_and_lse into the running state. Masking follows the Kvax
+// flash_attention arguments (positions, segment IDs, padding segment).
+//
+// Design for gfx950 (CDNA4):
+//  * One workgroup = 4 waves = 128 query rows of one head; each wave owns 32
+//    rows. The workgroup walks the compacted list of non-EMPTY kv tiles of
+//    its row of tiles (64 keys each); FULL tiles skip all mask arithmetic.
+//  * Scores are computed transposed, S^T = K * Q^T, with
+//    v_mfma_f32_32x32x16_bf16: A = K tile from LDS (32 keys x 16 dims), B = Q
+//    held in registers for the whole loop. In the 32x32 accumulator layout a
+//    lane owns one query row (lane & 31) and 16 keys, so row max / row sum
+//    are in-lane plus one v_permlane32_swap with the partner lane.
+//  * O^T = V^T * P^T with the same instruction: P leaves the S accumulator as
+//    packed bf16 and feeds the B operand directly (no LDS round trip); V is
+//    stored transposed in LDS, keys permuted inside each group of 16 so one
+//    16-byte LDS read gives the A operand in the key order P arrives in.
+//  * K / V tiles are double-buffered in LDS; the next tile's global loads are
+//    issued before the current tile's math, one barrier per tile.
+//  * Online softmax in base 2 with the scale folded into one FMA; the running
+//    max is only raised when a row's max grows by more than 2^8 (the weights
+//    stay <= 256, exact in the final normalisation), so most tiles skip the
+//    O rescale.
+//  * Workgroup ids are mapped so that each XCD (ids are dealt round-robin over
+//    the 8 XCDs) gets a contiguous range of (batch, kv head) groups, keeping
+//    their K/V in that XCD's L2, and within it heavier (later) q tiles first.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "ram_internal.h"
+
+namespace ram {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Lanes l and l^32 hold the same query row. v_permlane32_swap exchanges the
+// upper half of its first operand with the lower half of its second; with x
+// passed as both, the two results of each lane are {own value, partner value}
+// (in an order that depends on the lane half), so max / sum over the pair is
+// the reduction over both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Work decode: item order is (batch*Hkv + kv head, q tile descending, head in group);
+// XCD x = id % 8 takes the contiguous item range [x*per, (x+1)*per).
+__device__ __forceinline__ bool decode_work(const AttnParams& p, int& b, int& h, int& qb) {
+  const int G = p.H / p.Hkv;
+  const int64_t T = (int64_t)p.B * p.Hkv * p.nQb * G;
+  const int64_t per = (T + 7) / 8;
+  const int64_t id = blockIdx.x;
+  const int64_t item = (id & 7) * per + (id >> 3);
+  if (item >= T) return false;
+  const int hg = (int)(item % G);
+  const int64_t r = item / G;
+  const int qrev = (int)(r % p.nQb);
+  const int64_t bg = r / p.nQb;
+  const int g = (int)(bg % p.Hkv);
+  b = (int)(bg / p.Hkv);
+  h = g * G + hg;
+  qb = p.nQb - 1 - qrev;
+  return true;
+}
+
+// Element mask for the 32 keys a lane holds of a 64-key tile starting at k0.
+// Key of accumulator register i of half kb2: k0 + kb2*32 + 8*(i>>2) + 4*lg + (i&3).
+__device__ __forceinline__ void apply_mask(f32x16 (&S)[2], const AttnParams& p, int b, int k0,
+                                           int lg, int qpos, int qseg) {
+  const int32_t* kvp = p.kv_pos ? p.kv_pos + (int64_t)b * p.kvm_stride_b : nullptr;
+  const int32_t* kvs = p.kv_seg ? p.kv_seg + (int64_t)b * p.kvm_stride_b : nullptr;
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = k0 + kb2 * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
+      bool ok = key < p.Skv;
+      if (ok && p.causal) {
+        const int kp = kvp ? kvp[key] : p.kv_pos_base + key;
+        ok = kp <= qpos;
+      }
+      if (ok && kvs) ok = (kvs[key] == qseg) && (qseg != -1);
+      if (!ok) S[kb2][i] = neg_inf();
+    }
+  }
+}
+
+// Soft cap in log2 units: u = cap*log2(e) * tanh(s*scale/cap), tanh(x) = 1 - 2/(1+e^{2x}).
+__device__ __forceinline__ float capped_log2(float s, float k2, float cap_log2) {
+  const float e = fast_exp2(s * k2);
+  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e);
+  return cap_log2 * t;
+}
+
+// Online-softmax step on the 32 scores a lane holds. Returns nothing; updates
+// m_ref / l_acc / O and leaves the weights in S.
+template <int NDB, bool CAP>
+__device__ __forceinline__ void softmax_step(f32x16 (&S)[2], f32x16 (&O)[NDB], float& m_ref,
+                                             float& l_acc, const AttnParams& p) {
+  float mx = neg_inf();
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[kb2][i]);
+  mx = pair_max(mx);
+  const float umax = CAP ? mx : mx * p.scale_log2;
+  const bool need = umax > m_ref + kRescaleThreshold;
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    const float m_new = fmaxf(m_ref, umax);
+    const float alpha = (m_new == neg_inf()) ? 1.0f : fast_exp2(m_ref - m_new);
+    l_acc *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
+    m_ref = m_new;
+  }
+  const float msub = (m_ref == neg_inf()) ? 0.0f : m_ref;
+  float ls = 0.0f;
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e = CAP ? fast_exp2(S[kb2][i] - msub)
+                          : fast_exp2(__builtin_fmaf(S[kb2][i], p.scale_log2, -msub));
+      S[kb2][i] = e;
+      ls += e;
+    }
+  l_acc += ls;
+}
+
+// Epilogue: normalise, then write (mode 0) or merge into (mode 1) the running state.
+template <int NDB>
+__device__ __forceinline__ void epilogue(const f32x16 (&O)[NDB], float m_ref, float l_acc,
+                                         const AttnParams& p, int b, int h, int q_row, int lg) {
+  constexpr int D = NDB * 32;
+  const float l_row = pair_sum(l_acc);
+  if (q_row >= p.Sq) return;
+  const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+  const float lse_c = l_row > 0.0f ? (m_ref + log2f(l_row)) * kLn2 : neg_inf();
+  float* orow = p.out + (((int64_t)b * p.Sq + q_row) * p.H + h) * D;
+  float* lptr = p.lse + ((int64_t)b * p.H + h) * p.Sq + q_row;
+  if (p.mode == 0) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        float4 o;
+        o.x = O[db][4 * i4 + 0] * inv;
+        o.y = O[db][4 * i4 + 1] * inv;
+        o.z = O[db][4 * i4 + 2] * inv;
+        o.w = O[db][4 * i4 + 3] * inv;
+        *reinterpret_cast<float4*>(orow + db * 32 + 8 * i4 + 4 * lg) = o;
+      }
+    if (lg == 0) *lptr = lse_c;
+    return;
+  }
+  // merge (ring-splash _update_out_and_lse)
+  if (lse_c == neg_inf()) return;  // nothing attended in this chunk: identity
+  const float acc_lse = *lptr;
+  float sig = 1.0f, new_lse = lse_c;
+  if (acc_lse != neg_inf()) {
+    const float x = lse_c - acc_lse;
+    sig = 1.0f / (1.0f + expf(-x));
+    new_lse = acc_lse + (fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))));
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      float4* ptr = reinterpret_cast<float4*>(orow + db * 32 + 8 * i4 + 4 * lg);
+      float4 a = (acc_lse == neg_inf()) ? make_float4(0.f, 0.f, 0.f, 0.f) : *ptr;
+      float4 o;
+      o.x = a.x - sig * (a.x - O[db][4 * i4 + 0] * inv);
+      o.y = a.y - sig * (a.y - O[db][4 * i4 + 1] * inv);
+      o.z = a.z - sig * (a.z - O[db][4 * i4 + 2] * inv);
+      o.w = a.w - sig * (a.w - O[db][4 * i4 + 3] * inv);
+      *ptr = o;
+    }
+  if (lg == 0) *lptr = new_lse;
+}
+
+// Physical slot of key k inside a V^T row: within each group of 16 keys the
+// groups of 4 are stored in the order 0, 2, 1, 3, so that lane group lg's
+// 8 keys {4lg..4lg+3, 8+4lg..8+4lg+3} are contiguous.
+__device__ __forceinline__ int vt_slot(int k) {
+  const int q4 = (k >> 2) & 3;
+  const int sw = ((q4 & 1) << 1) | (q4 >> 1);
+  return (k & ~15) | (sw << 2) | (k & 3);
+}
+
+// ------------------------------------------------------------------------------ bf16
+template <int D, bool CAP>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
+  constexpr int BK = kBlockKV;
+  constexpr int NDS = D / 16;      // k-steps of S^T = K Q^T
+  constexpr int NDB = D / 32;      // 32-row blocks of O^T
+  constexpr int KP = D + 8;        // K row pitch (elements)
+  constexpr int VP = BK + 8;       // V^T row pitch (elements)
+  constexpr int K_ELEMS = BK * KP;
+  constexpr int V_ELEMS = D * VP;
+  constexpr int CH = D / 8;               // 16-byte chunks per K row
+  constexpr int RPP = kThreads / CH;      // K rows per load pass
+  constexpr int NPK = BK / RPP;           // K load passes
+  constexpr int KG = BK * D / (8 * kThreads);  // V keys per thread (4 or 2)
+  static_assert(KG == 4 || KG == 2, "V tile split");
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (K_ELEMS + V_ELEMS)];
+
+  int b, h, qb;
+  if (!decode_work(p, b, h, qb)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int ln = lane & 31, lg = lane >> 5;
+  const int G = p.H / p.Hkv;
+  const int g = h / G;
+  const int q_row = qb * kBlockQ + w * 32 + ln;
+  const bool q_ok = q_row < p.Sq;
+
+  const int64_t mrow = (int64_t)b * p.nQb + qb;
+  const int cnt = p.row_cnt[mrow];
+  if (cnt == 0 && p.mode == 1 && p.sinks == nullptr) return;
+  const int32_t* cols = p.col_idx + mrow * p.nKb;
+  const uint8_t* cls = p.tile_class + mrow * p.nKb;
+
+  // Q fragments (B operand): lane holds row q_row, dims ds*16 + lg*8 .. +7.
+  bf16x8 qf[NDS];
+  {
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b +
+                         ((int64_t)(q_ok ? q_row : 0) * p.H + h) * D;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      bf16x8 t = *reinterpret_cast<const bf16x8*>(qrow + ds * 16 + lg * 8);
+      qf[ds] = q_ok ? t : bf16x8{};
+    }
+  }
+  const int qrow_c = q_ok ? q_row : p.Sq - 1;
+  const int qpos = p.q_pos ? p.q_pos[(int64_t)b * p.qm_stride_b + qrow_c] : p.q_pos_base + q_row;
+  const int qseg = p.q_seg ? p.q_seg[(int64_t)b * p.qm_stride_b + qrow_c] : 0;
+
+  float m_ref = neg_inf(), l_acc = 0.0f;
+  if (p.sinks) {
+    m_ref = p.sinks[h] * kLog2e;
+    l_acc = (lg == 0) ? 1.0f : 0.0f;
+  }
+  f32x16 O[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) O[db] = f32x16{};
+
+  const int64_t krs = (int64_t)p.Hkv * D;  // key row stride
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.kv_stride_b + g * D;
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.kv_stride_b + g * D;
+  const int kc = tid % CH, kr0 = tid / CH;
+  const int vc = tid % CH, vk0 = (tid / CH) * KG;
+  uint4 kreg[NPK], vreg[KG];
+
+  auto gload = [&](int kb) {
+    const int k0 = kb * BK;
+#pragma unroll
+    for (int i = 0; i < NPK; ++i) {
+      const int row = k0 + kr0 + i * RPP;
+      kreg[i] = row < p.Skv ? *reinterpret_cast<const uint4*>(kbase + row * krs + kc * 8)
+                            : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < KG; ++r) {
+      const int row = k0 + vk0 + r;
+      vreg[r] = row < p.Skv ? *reinterpret_cast<const uint4*>(vbase + row * krs + vc * 8)
+                            : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+    __bf16* Ks = smem + buf * (K_ELEMS + V_ELEMS);
+    __bf16* Vt = Ks + K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < NPK; ++i)
+      *reinterpret_cast<uint4*>(Ks + (kr0 + i * RPP) * KP + kc * 8) = kreg[i];
+    const int slot = vt_slot(vk0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {     // u32 word m holds dims 2m (low half), 2m+1 (high half)
+      uint32_t wv[KG];
+#pragma unroll
+      for (int r = 0; r < KG; ++r) wv[r] = (&vreg[r].x)[m];
+      __bf16* d0 = Vt + (vc * 8 + 2 * m) * VP + slot;
+      __bf16* d1 = d0 + VP;
+      if constexpr (KG == 4) {
+        uint2 lo, hi;
+        lo.x = (wv[0] & 0xffffu) | (wv[1] << 16);
+        lo.y = (wv[2] & 0xffffu) | (wv[3] << 16);
+        hi.x = (wv[0] >> 16) | (wv[1] & 0xffff0000u);
+        hi.y = (wv[2] >> 16) | (wv[3] & 0xffff0000u);
+        *reinterpret_cast<uint2*>(d0) = lo;
+        *reinterpret_cast<uint2*>(d1) = hi;
+      } else {
+        *reinterpret_cast<uint32_t*>(d0) = (wv[0] & 0xffffu) | (wv[1] << 16);
+        *reinterpret_cast<uint32_t*>(d1) = (wv[0] >> 16) | (wv[1] & 0xffff0000u);
+      }
+    }
+  };
+
+  if (cnt > 0) {
+    gload(cols[0]);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < cnt; ++it) {
+    const int kb = cols[it];
+    const int buf = it & 1;
+    const bool has_next = it + 1 < cnt;
+    if (has_next) gload(cols[it + 1]);
+    const __bf16* Ks = smem + buf * (K_ELEMS + V_ELEMS);
+    const __bf16* Vt = Ks + K_ELEMS;
+
+    f32x16 S[2];
+    S[0] = f32x16{};
+    S[1] = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (kb2 * 32 + ln) * KP + ds * 16 + lg * 8);
+        S[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], S[kb2], 0, 0, 0);
+      }
+    }
+    if constexpr (CAP) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
+    }
+    const bool need_mask = cls[kb] != 2 || (kb + 1) * BK > p.Skv;
+    if (need_mask) apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
+    softmax_step<NDB, CAP>(S, O, m_ref, l_acc, p);
+
+    bf16x8 P[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x2 two = {S[ks >> 1][(ks & 1) * 8 + 2 * j], S[ks >> 1][(ks & 1) * 8 + 2 * j + 1]};
+        bf16x2 pk = __builtin_convertvector(two, bf16x2);
+        P[ks][2 * j] = pk[0];
+        P[ks][2 * j + 1] = pk[1];
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vt + (db * 32 + ln) * VP + ks * 16 + lg * 8);
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[ks], O[db], 0, 0, 0);
+      }
+    }
+    if (has_next) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  epilogue<NDB>(O, m_ref, l_acc, p, b, h, q_row, lg);
+}
+
+// ------------------------------------------------------------------------------ fp32
+// Same structure with v_mfma_f32_32x32x2_f32: one fp32 per lane per operand,
+// K and V kept row-major in LDS, the fp32 weights feed PV directly.
+template <int D, bool CAP>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(AttnParams p) {
+  constexpr int BK = kBlockKV;
+  constexpr int NDB = D / 32;
+  constexpr int NDS = D / 2;
+  constexpr int KP = D + 4;                 // row pitch (floats), keeps float4 stores aligned
+  constexpr int ELEMS = BK * KP;
+  constexpr int CH = D / 4;                 // float4 chunks per row
+  constexpr int NLD = BK * CH / kThreads;   // float4 loads per thread per tensor
+  __shared__ __attribute__((aligned(16))) float smem[2 * 2 * ELEMS];
+
+  int b, h, qb;
+  if (!decode_work(p, b, h, qb)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int ln = lane & 31, lg = lane >> 5;
+  const int G = p.H / p.Hkv;
+  const int g = h / G;
+  const int q_row = qb * kBlockQ + w * 32 + ln;
+  const bool q_ok = q_row < p.Sq;
+
+  const int64_t mrow = (int64_t)b * p.nQb + qb;
+  const int cnt = p.row_cnt[mrow];
+  if (cnt == 0 && p.mode == 1 && p.sinks == nullptr) return;
+  const int32_t* cols = p.col_idx + mrow * p.nKb;
+  const uint8_t* cls = p.tile_class + mrow * p.nKb;
+
+  float qf[NDS];
+  {
+    const float* qrow = reinterpret_cast<const float*>(p.q) + (int64_t)b * p.q_stride_b +
+                        ((int64_t)(q_ok ? q_row : 0) * p.H + h) * D;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qf[ds] = q_ok ? qrow[ds * 2 + lg] : 0.0f;
+  }
+  const int qrow_c = q_ok ? q_row : p.Sq - 1;
+  const int qpos = p.q_pos ? p.q_pos[(int64_t)b * p.qm_stride_b + qrow_c] : p.q_pos_base + q_row;
+  const int qseg = p.q_seg ? p.q_seg[(int64_t)b * p.qm_stride_b + qrow_c] : 0;
+
+  float m_ref = neg_inf(), l_acc = 0.0f;
+  if (p.sinks) {
+    m_ref = p.sinks[h] * kLog2e;
+    l_acc = (lg == 0) ? 1.0f : 0.0f;
+  }
+  f32x16 O[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) O[db] = f32x16{};
+
+  const int64_t krs = (int64_t)p.Hkv * D;
+  const float* kbase = reinterpret_cast<const float*>(p.k) + (int64_t)b * p.kv_stride_b + g * D;
+  const float* vbase = reinterpret_cast<const float*>(p.v) + (int64_t)b * p.kv_stride_b + g * D;
+  float4 kreg[NLD], vreg[NLD];
+
+  auto gload = [&](int kb) {
+    const int k0 = kb * BK;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = tid + i * kThreads;
+      const int row = k0 + idx / CH, c = idx % CH;
+      const bool ok = row < p.Skv;
+      kreg[i] = ok ? *reinterpret_cast<const float4*>(kbase + row * krs + c * 4) : make_float4(0, 0, 0, 0);
+      vreg[i] = ok ? *reinterpret_cast<const float4*>(vbase + row * krs + c * 4) : make_float4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+    float* Ks = smem + buf * 2 * ELEMS;
+    float* Vs = Ks + ELEMS;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = tid + i * kThreads;
+      const int row = idx / CH, c = idx % CH;
+      *reinterpret_cast<float4*>(Ks + row * KP + c * 4) = kreg[i];
+      *reinterpret_cast<float4*>(Vs + row * KP + c * 4) = vreg[i];
+    }
+  };
+
+  if (cnt > 0) {
+    gload(cols[0]);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < cnt; ++it) {
+    const int kb = cols[it];
+    const int buf = it & 1;
+    const bool has_next = it + 1 < cnt;
+    if (has_next) gload(cols[it + 1]);
+    const float* Ks = smem + buf * 2 * ELEMS;
+    const float* Vs = Ks + ELEMS;
+
+    f32x16 S[2];
+    S[0] = f32x16{};
+    S[1] = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const float a = Ks[(kb2 * 32 + ln) * KP + ds * 2 + lg];
+        S[kb2] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[ds], S[kb2], 0, 0, 0);
+      }
+    }
+    if constexpr (CAP) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
+    }
+    const bool need_mask = cls[kb] != 2 || (kb + 1) * BK > p.Skv;
+    if (need_mask) apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
+    softmax_step<NDB, CAP>(S, O, m_ref, l_acc, p);
+
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb2 * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const float a = Vs[key * KP + db * 32 + ln];
+          O[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, S[kb2][i], O[db], 0, 0, 0);
+        }
+      }
+    }
+    if (has_next) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  epilogue<NDB>(O, m_ref, l_acc, p, b, h, q_row, lg);
+}
+
+template <typename K>
+hipError_t launch(K kernel, const AttnParams& p, hipStream_t s) {
+  const int64_t T = (int64_t)p.B * p.H * p.nQb;
+  const int64_t grid = 8 * ((T + 7) / 8);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s) {
+  const bool cap = p.softcap_on != 0;
+  if (dtype == 1) {
+    if (p.D == 128) return cap ? launch(attn_fwd_bf16<128, true>, p, s) : launch(attn_fwd_bf16<128, false>, p, s);
+    return cap ? launch(attn_fwd_bf16<64, true>, p, s) : launch(attn_fwd_bf16<64, false>, p, s);
+  }
+  if (p.D == 128) return cap ? launch(attn_fwd_f32<128, true>, p, s) : launch(attn_fwd_f32<128, false>, p, s);
+  return cap ? launch(attn_fwd_f32<64, true>, p, s) : launch(attn_fwd_f32<64, false>, p, s);
+}
+
+}  // namespace ram

@@ -1,0 +1,387 @@
+// C ABI of libram: host-side validation, launches and the one-GPU ring loop.
+//
+// Every entry point checks all of its arguments before it enqueues anything
+// (the ring-splash page likewise raises before any compute), so on a non-OK
+// status no kernel ran and no output changed.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/ram.h"
+#include "ram_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ram_status fail(ram_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+ram_status ok() {
+  g_err.clear();
+  return RAM_OK;
+}
+
+ram_status hip_fail(hipError_t e, const char* what) {
+  return fail(RAM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int64_t kMaxSeq = int64_t(1) << 30;
+
+// Checks the fields every call reads. `tile_for_attn` also requires the
+// kernel tile; otherwise the mask tile limits apply.
+ram_status check_desc(const ram_attn_desc* d, bool tile_for_attn, bool need_heads) {
+  if (!d) return fail(RAM_ERR_INVALID, "desc is null");
+  if (d->B < 0 || d->Sq < 0 || d->Skv < 0)
+    return fail(RAM_ERR_INVALID, "negative size: B=%d Sq=%d Skv=%d", d->B, d->Sq, d->Skv);
+  if (d->Sq > kMaxSeq || d->Skv > kMaxSeq)
+    return fail(RAM_ERR_INVALID, "sequence too long: Sq=%d Skv=%d", d->Sq, d->Skv);
+  if (d->causal != 0 && d->causal != 1) return fail(RAM_ERR_INVALID, "causal must be 0 or 1");
+  if (need_heads) {
+    if (d->H < 1 || d->Hkv < 1) return fail(RAM_ERR_INVALID, "H=%d Hkv=%d must be >= 1", d->H, d->Hkv);
+    if (d->H % d->Hkv) return fail(RAM_ERR_INVALID, "H=%d is not a multiple of Hkv=%d", d->H, d->Hkv);
+    if (d->D != 64 && d->D != 128) return fail(RAM_ERR_UNSUPPORTED, "head dim D=%d (built: 64, 128)", d->D);
+    if (d->dtype != RAM_F32 && d->dtype != RAM_BF16) return fail(RAM_ERR_UNSUPPORTED, "dtype %d", d->dtype);
+    if (!std::isfinite(d->scale) || !(d->scale > 0.0f))
+      return fail(RAM_ERR_INVALID, "scale must be finite and > 0");
+    if (!std::isfinite(d->softcap)) return fail(RAM_ERR_INVALID, "softcap must be finite");
+    const int64_t esz = d->dtype == RAM_BF16 ? 2 : 4;
+    const int64_t qmin = (int64_t)d->Sq * d->H * d->D;
+    if (d->q_stride_b != 0 && (d->q_stride_b < qmin || (d->q_stride_b * esz) % 16))
+      return fail(RAM_ERR_INVALID, "q_stride_b=%lld (>= %lld, 16-byte multiple)", (long long)d->q_stride_b,
+                  (long long)qmin);
+  }
+  if (tile_for_attn) {
+    if (d->block_q != ram::kBlockQ || d->block_kv != ram::kBlockKV)
+      return fail(RAM_ERR_INVALID, "block mask tile %dx%d differs from the kernel tile %dx%d", d->block_q,
+                  d->block_kv, ram::kBlockQ, ram::kBlockKV);
+  } else {
+    if (d->block_q < 16 || d->block_q > ram::kMaxMaskTile || d->block_kv < 16 || d->block_kv > ram::kMaxMaskTile)
+      return fail(RAM_ERR_INVALID, "tile %dx%d outside [16, %d]", d->block_q, d->block_kv, ram::kMaxMaskTile);
+  }
+  if (cdiv(d->Skv, d->block_kv) > ram::kMaxMaskCols)
+    return fail(RAM_ERR_UNSUPPORTED, "more than %d kv tiles in a row", ram::kMaxMaskCols);
+  return RAM_OK;
+}
+
+ram_status check_kv_stride(const ram_attn_desc* d, int64_t keys) {
+  const int64_t esz = d->dtype == RAM_BF16 ? 2 : 4;
+  const int64_t kmin = keys * d->Hkv * d->D;
+  if (d->kv_stride_b != 0 && (d->kv_stride_b < kmin || (d->kv_stride_b * esz) % 16))
+    return fail(RAM_ERR_INVALID, "kv_stride_b=%lld (>= %lld, 16-byte multiple)", (long long)d->kv_stride_b,
+                (long long)kmin);
+  return RAM_OK;
+}
+
+// Positions / segments of one call whose KV spans `kv_len` keys.
+ram_status check_src(const ram_mask_src* m, const ram_attn_desc* d, int64_t kv_len, int64_t q_base_extra) {
+  if (!m) return fail(RAM_ERR_INVALID, "mask source is null");
+  if ((m->q_seg == nullptr) != (m->kv_seg == nullptr))
+    return fail(RAM_ERR_INVALID, "q_seg and kv_seg must both be set or both be null");
+  if (m->q_meta_stride_b != 0 && m->q_meta_stride_b < d->Sq)
+    return fail(RAM_ERR_INVALID, "q_meta_stride_b=%lld < Sq", (long long)m->q_meta_stride_b);
+  if (m->kv_meta_stride_b != 0 && m->kv_meta_stride_b < kv_len)
+    return fail(RAM_ERR_INVALID, "kv_meta_stride_b=%lld < %lld", (long long)m->kv_meta_stride_b, (long long)kv_len);
+  const void* arrs[4] = {m->q_pos, m->kv_pos, m->q_seg, m->kv_seg};
+  for (const void* a : arrs)
+    if (a && !aligned(a, 4)) return fail(RAM_ERR_INVALID, "position / segment arrays must be 4-byte aligned");
+  if (!m->q_pos) {
+    const int64_t hi = (int64_t)m->q_pos_base + q_base_extra + d->Sq;
+    if (hi > INT32_MAX || (int64_t)m->q_pos_base + q_base_extra < INT32_MIN)
+      return fail(RAM_ERR_INVALID, "sequential q positions overflow int32");
+  }
+  if (!m->kv_pos) {
+    const int64_t hi = (int64_t)m->kv_pos_base + kv_len;
+    if (hi > INT32_MAX || m->kv_pos_base < INT32_MIN / 2)
+      return fail(RAM_ERR_INVALID, "sequential kv positions overflow int32");
+  }
+  return RAM_OK;
+}
+
+ram_status check_mask_arrays(const ram_block_mask* bm, const ram_attn_desc* d) {
+  if (!bm) return fail(RAM_ERR_INVALID, "block mask is null");
+  const int64_t rows = (int64_t)d->B * cdiv(d->Sq, d->block_q);
+  if (rows == 0) return RAM_OK;
+  if (!bm->row_cnt || !aligned(bm->row_cnt, 4)) return fail(RAM_ERR_INVALID, "row_cnt null or misaligned");
+  if (cdiv(d->Skv, d->block_kv) > 0) {
+    if (!bm->tile_class) return fail(RAM_ERR_INVALID, "tile_class is null");
+    if (!bm->col_idx || !aligned(bm->col_idx, 4)) return fail(RAM_ERR_INVALID, "col_idx null or misaligned");
+  }
+  return RAM_OK;
+}
+
+ram_status check_tensor(const void* p, const char* name) {
+  if (!p) return fail(RAM_ERR_INVALID, "%s is null", name);
+  if (!aligned(p, 16)) return fail(RAM_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+  return RAM_OK;
+}
+
+#define RAM_TRY(x)                      \
+  do {                                  \
+    ram_status _s = (x);                \
+    if (_s != RAM_OK) return _s;        \
+  } while (0)
+
+ram::MaskParams mask_params(const ram_attn_desc* d, const ram_mask_src* m, const ram_block_mask* bm) {
+  ram::MaskParams p{};
+  p.q_pos = m->q_pos;
+  p.kv_pos = m->kv_pos;
+  p.q_seg = m->q_seg;
+  p.kv_seg = m->kv_seg;
+  p.qm_stride_b = m->q_meta_stride_b ? m->q_meta_stride_b : d->Sq;
+  p.kvm_stride_b = m->kv_meta_stride_b ? m->kv_meta_stride_b : d->Skv;
+  p.kv_chunk_off = 0;
+  p.q_pos_base = m->q_pos_base;
+  p.kv_pos_base = m->kv_pos_base;
+  p.kv_base_step = 0;
+  p.B = d->B;
+  p.Sq = d->Sq;
+  p.Skv = d->Skv;
+  p.bq = d->block_q;
+  p.bk = d->block_kv;
+  p.nQb = (int)cdiv(d->Sq, d->block_q);
+  p.nKb = (int)cdiv(d->Skv, d->block_kv);
+  p.causal = d->causal;
+  p.tile_class = bm->tile_class;
+  p.row_cnt = bm->row_cnt;
+  p.col_idx = bm->col_idx;
+  return p;
+}
+
+ram::AttnParams attn_params(const ram_attn_desc* d, const void* q, const void* k, const void* v,
+                            const ram_mask_src* m, const ram_block_mask* bm, const float* sinks, int mode,
+                            float* out, float* lse) {
+  ram::AttnParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.sinks = sinks;
+  p.tile_class = bm->tile_class;
+  p.row_cnt = bm->row_cnt;
+  p.col_idx = bm->col_idx;
+  p.q_pos = m->q_pos;
+  p.kv_pos = m->kv_pos;
+  p.q_seg = m->q_seg;
+  p.kv_seg = m->kv_seg;
+  p.q_stride_b = d->q_stride_b ? d->q_stride_b : (int64_t)d->Sq * d->H * d->D;
+  p.kv_stride_b = d->kv_stride_b ? d->kv_stride_b : (int64_t)d->Skv * d->Hkv * d->D;
+  p.qm_stride_b = m->q_meta_stride_b ? m->q_meta_stride_b : d->Sq;
+  p.kvm_stride_b = m->kv_meta_stride_b ? m->kv_meta_stride_b : d->Skv;
+  p.q_pos_base = m->q_pos_base;
+  p.kv_pos_base = m->kv_pos_base;
+  p.B = d->B;
+  p.Sq = d->Sq;
+  p.Skv = d->Skv;
+  p.H = d->H;
+  p.Hkv = d->Hkv;
+  p.D = d->D;
+  p.nQb = (int)cdiv(d->Sq, ram::kBlockQ);
+  p.nKb = (int)cdiv(d->Skv, ram::kBlockKV);
+  const float log2e = 1.4426950408889634f;
+  p.scale_log2 = d->scale * log2e;
+  p.softcap_on = d->softcap > 0.0f;
+  p.cap_k2 = p.softcap_on ? 2.0f * d->scale * log2e / d->softcap : 0.0f;
+  p.cap_log2 = p.softcap_on ? d->softcap * log2e : 0.0f;
+  p.causal = d->causal;
+  p.mode = mode;
+  return p;
+}
+
+struct RingLayout {
+  size_t acc_off, cls_off, cnt_off, col_off, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks) {
+  RingLayout L{};
+  const int64_t nQb = cdiv(d->Sq, ram::kBlockQ), nKb = cdiv(d->Skv, ram::kBlockKV);
+  const int64_t tiles = (int64_t)n_chunks * d->B * nQb * nKb;
+  const int64_t rows = (int64_t)n_chunks * d->B * nQb;
+  size_t off = 0;
+  L.acc_off = off;
+  if (d->dtype == RAM_BF16) off += align256((size_t)d->B * d->Sq * d->H * d->D * sizeof(float));
+  L.cls_off = off;
+  off += align256((size_t)tiles);
+  L.cnt_off = off;
+  off += align256((size_t)rows * sizeof(int32_t));
+  L.col_off = off;
+  off += align256((size_t)tiles * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ram_last_error(void) { return g_err.c_str(); }
+
+ram_status ram_kernel_tile(int32_t dtype, int32_t D, int32_t* block_q, int32_t* block_kv) {
+  if (!block_q || !block_kv) return fail(RAM_ERR_INVALID, "null output pointer");
+  if (dtype != RAM_F32 && dtype != RAM_BF16) return fail(RAM_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (D != 64 && D != 128) return fail(RAM_ERR_UNSUPPORTED, "head dim D=%d (built: 64, 128)", D);
+  *block_q = ram::kBlockQ;
+  *block_kv = ram::kBlockKV;
+  return ok();
+}
+
+ram_status build_block_mask(const ram_attn_desc* desc, const ram_mask_src* src, const ram_block_mask* out,
+                            hipStream_t stream) {
+  RAM_TRY(check_desc(desc, false, false));
+  RAM_TRY(check_src(src, desc, desc->Skv, 0));
+  RAM_TRY(check_mask_arrays(out, desc));
+  if (desc->B == 0 || desc->Sq == 0) return ok();
+  ram::MaskParams p = mask_params(desc, src, out);
+  hipError_t e = ram::launch_block_mask(p, 1, stream);
+  if (e != hipSuccess) return hip_fail(e, "build_block_mask launch");
+  return ok();
+}
+
+ram_status attn_fwd_chunk(const ram_attn_desc* desc, const void* q, const void* k, const void* v,
+                          const ram_mask_src* src, const ram_block_mask* mask, const float* sinks, int32_t mode,
+                          float* out, float* lse, hipStream_t stream) {
+  RAM_TRY(check_desc(desc, true, true));
+  RAM_TRY(check_kv_stride(desc, desc->Skv));
+  RAM_TRY(check_src(src, desc, desc->Skv, 0));
+  RAM_TRY(check_mask_arrays(mask, desc));
+  if (mode != RAM_OUT_WRITE && mode != RAM_OUT_MERGE) return fail(RAM_ERR_INVALID, "mode %d", mode);
+  if (desc->B == 0 || desc->Sq == 0) return ok();
+  RAM_TRY(check_tensor(q, "q"));
+  if (desc->Skv > 0) {
+    RAM_TRY(check_tensor(k, "k"));
+    RAM_TRY(check_tensor(v, "v"));
+  }
+  RAM_TRY(check_tensor(out, "out"));
+  if (!lse || !aligned(lse, 4)) return fail(RAM_ERR_INVALID, "lse null or misaligned");
+  if (sinks && !aligned(sinks, 4)) return fail(RAM_ERR_INVALID, "sinks misaligned");
+  ram::AttnParams p = attn_params(desc, q, k, v, src, mask, sinks, mode, out, lse);
+  hipError_t e = ram::launch_attn(p, desc->dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_fwd_chunk launch");
+  return ok();
+}
+
+ram_status lse_merge(int32_t B, int32_t Sq, int32_t H, int32_t D, float* out_acc, float* lse_acc,
+                     const float* out_blk, const float* lse_blk, hipStream_t stream) {
+  if (B < 0 || Sq < 0 || H < 0) return fail(RAM_ERR_INVALID, "negative size");
+  if (D != 64 && D != 128) return fail(RAM_ERR_UNSUPPORTED, "head dim D=%d (built: 64, 128)", D);
+  if ((int64_t)B * Sq * H == 0) return ok();
+  RAM_TRY(check_tensor(out_acc, "out_acc"));
+  RAM_TRY(check_tensor(out_blk, "out_blk"));
+  if (!lse_acc || !lse_blk || !aligned(lse_acc, 4) || !aligned(lse_blk, 4))
+    return fail(RAM_ERR_INVALID, "lse null or misaligned");
+  if (out_acc == out_blk) return fail(RAM_ERR_INVALID, "out_blk aliases out_acc");
+  hipError_t e = ram::launch_merge(B, Sq, H, D, out_acc, lse_acc, out_blk, lse_blk, stream);
+  if (e != hipSuccess) return hip_fail(e, "lse_merge launch");
+  return ok();
+}
+
+size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks) {
+  if (!desc || n_chunks < 1 || desc->B < 0 || desc->Sq < 0 || desc->Skv < 0 || desc->H < 1 ||
+      (desc->D != 64 && desc->D != 128))
+    return 0;
+  ram_attn_desc dt = *desc;
+  dt.block_q = ram::kBlockQ;
+  dt.block_kv = ram::kBlockKV;
+  return ring_layout(&dt, n_chunks).total;
+}
+
+ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32_t q_shard, const void* q,
+                              const void* k_all, const void* v_all, const ram_mask_src* src, const float* sinks,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  if (!desc) return fail(RAM_ERR_INVALID, "desc is null");
+  ram_attn_desc dt = *desc;  // the ring builds its own masks at the kernel tile
+  dt.block_q = ram::kBlockQ;
+  dt.block_kv = ram::kBlockKV;
+  desc = &dt;
+  RAM_TRY(check_desc(desc, true, true));
+  if (n_chunks < 1) return fail(RAM_ERR_INVALID, "n_chunks=%d must be >= 1", n_chunks);
+  if (q_shard < -1 || q_shard >= n_chunks)
+    return fail(RAM_ERR_INVALID, "q_shard=%d outside [-1, %d)", q_shard, n_chunks);
+  const int64_t kv_total = (int64_t)n_chunks * desc->Skv;
+  if (kv_total > kMaxSeq) return fail(RAM_ERR_INVALID, "total KV too long");
+  RAM_TRY(check_kv_stride(desc, kv_total));
+  const int64_t q_extra = q_shard >= 0 ? (int64_t)q_shard * desc->Sq : 0;
+  RAM_TRY(check_src(src, desc, kv_total, q_extra));
+  if (desc->B == 0 || desc->Sq == 0) return ok();
+  RAM_TRY(check_tensor(q, "q"));
+  if (desc->Skv > 0) {
+    RAM_TRY(check_tensor(k_all, "k_all"));
+    RAM_TRY(check_tensor(v_all, "v_all"));
+  }
+  RAM_TRY(check_tensor(out, "out"));
+  if (!lse || !aligned(lse, 4)) return fail(RAM_ERR_INVALID, "lse null or misaligned");
+  if (sinks && !aligned(sinks, 4)) return fail(RAM_ERR_INVALID, "sinks misaligned");
+  const RingLayout L = ring_layout(desc, n_chunks);
+  if (!workspace || !aligned(workspace, 256))
+    return fail(RAM_ERR_WORKSPACE, "workspace null or not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(RAM_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, L.total);
+
+  char* ws = static_cast<char*>(workspace);
+  ram_block_mask bm{reinterpret_cast<uint8_t*>(ws + L.cls_off), reinterpret_cast<int32_t*>(ws + L.cnt_off),
+                    reinterpret_cast<int32_t*>(ws + L.col_off)};
+  float* acc = desc->dtype == RAM_BF16 ? reinterpret_cast<float*>(ws + L.acc_off) : static_cast<float*>(out);
+  const int64_t nQb = cdiv(desc->Sq, ram::kBlockQ), nKb = cdiv(desc->Skv, ram::kBlockKV);
+  const int64_t kv_full_stride = desc->kv_stride_b ? desc->kv_stride_b : kv_total * desc->Hkv * desc->D;
+  const int64_t kvm_full = src->kv_meta_stride_b ? src->kv_meta_stride_b : kv_total;
+  const int32_t q_base = (int32_t)(src->q_pos_base + q_extra);
+
+  // Block masks of every chunk in one launch (chunk c in blockIdx.z).
+  ram_attn_desc dm = *desc;
+  ram_mask_src sm = *src;
+  sm.q_pos_base = q_base;
+  sm.kv_meta_stride_b = kvm_full;
+  ram::MaskParams mp = mask_params(&dm, &sm, &bm);
+  mp.kv_chunk_off = desc->Skv;
+  mp.kv_base_step = desc->Skv;
+  hipError_t e = ram::launch_block_mask(mp, n_chunks, stream);
+  if (e != hipSuccess) return hip_fail(e, "ring block mask launch");
+
+  const int64_t esz = desc->dtype == RAM_BF16 ? 2 : 4;
+  for (int t = 0; t < n_chunks; ++t) {
+    const int c = q_shard >= 0 ? ((q_shard - t) % n_chunks + n_chunks) % n_chunks : t;
+    ram_attn_desc dc = *desc;
+    dc.kv_stride_b = kv_full_stride;
+    ram_mask_src sc = *src;
+    sc.q_pos_base = q_base;
+    sc.kv_meta_stride_b = kvm_full;
+    sc.kv_pos = src->kv_pos ? src->kv_pos + (int64_t)c * desc->Skv : nullptr;
+    sc.kv_seg = src->kv_seg ? src->kv_seg + (int64_t)c * desc->Skv : nullptr;
+    sc.kv_pos_base = src->kv_pos_base + c * desc->Skv;
+    const ram_block_mask bc{bm.tile_class + (int64_t)c * desc->B * nQb * nKb,
+                            bm.row_cnt + (int64_t)c * desc->B * nQb,
+                            bm.col_idx + (int64_t)c * desc->B * nQb * nKb};
+    const char* kc = static_cast<const char*>(k_all) + (int64_t)c * desc->Skv * desc->Hkv * desc->D * esz;
+    const char* vc = static_cast<const char*>(v_all) + (int64_t)c * desc->Skv * desc->Hkv * desc->D * esz;
+    ram::AttnParams p = attn_params(&dc, q, kc, vc, &sc, &bc, t == 0 ? sinks : nullptr,
+                                    t == 0 ? RAM_OUT_WRITE : RAM_OUT_MERGE, acc, lse);
+    e = ram::launch_attn(p, desc->dtype, stream);
+    if (e != hipSuccess) return hip_fail(e, "ring chunk launch");
+  }
+  if (desc->dtype == RAM_BF16) {
+    e = ram::launch_cast_bf16(acc, out, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
+    if (e != hipSuccess) return hip_fail(e, "final cast launch");
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal parameter blocks and launchers shared by the HIP sources of libram.
+// Not part of the C ABI (include/ram.h is).
+#pragma once
+
+#include <cstdint>
+#include <hip/hip_runtime_api.h>
+
+namespace ram {
+
+// Attention kernel tile: 4 waves of 32 query rows, 64 keys per step.
+constexpr int kBlockQ = 128;
+constexpr int kBlockKV = 64;
+// Largest number of kv tiles in one block-mask row (classes are staged in LDS).
+constexpr int kMaxMaskCols = 8192;
+constexpr int kMaxMaskTile = 512;
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;         // float32 [B,Sq,H,D], dense
+  float* lse;         // float32 [B,H,Sq], dense
+  const float* sinks; // [H] or null
+  const uint8_t* tile_class;
+  const int32_t* row_cnt;
+  const int32_t* col_idx;
+  const int32_t* q_pos;
+  const int32_t* kv_pos;
+  const int32_t* q_seg;
+  const int32_t* kv_seg;
+  int64_t q_stride_b, kv_stride_b;   // elements
+  int64_t qm_stride_b, kvm_stride_b; // elements of the position / segment arrays
+  int32_t q_pos_base, kv_pos_base;
+  int32_t B, Sq, Skv, H, Hkv, D;
+  int32_t nQb, nKb;
+  float scale_log2;   // scale * log2(e)
+  float cap_k2;       // 2 * scale * log2(e) / softcap   (soft cap on)
+  float cap_log2;     // softcap * log2(e)               (soft cap on)
+  int32_t softcap_on;
+  int32_t causal;
+  int32_t mode;       // 0 write, 1 merge
+};
+
+struct MaskParams {
+  const int32_t* q_pos;
+  const int32_t* kv_pos;
+  const int32_t* q_seg;
+  const int32_t* kv_seg;
+  int64_t qm_stride_b, kvm_stride_b;
+  int64_t kv_chunk_off;    // elements added to kv_pos / kv_seg per chunk (blockIdx.z)
+  int32_t q_pos_base, kv_pos_base;
+  int32_t kv_base_step;    // added to kv_pos_base per chunk
+  int32_t B, Sq, Skv, bq, bk, nQb, nKb, causal;
+  uint8_t* tile_class;     // chunk c at + c * B*nQb*nKb
+  int32_t* row_cnt;        // chunk c at + c * B*nQb
+  int32_t* col_idx;        // chunk c at + c * B*nQb*nKb
+};
+
+hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s);
+hipError_t launch_block_mask(const MaskParams& p, int n_chunks, hipStream_t s);
+hipError_t launch_merge(int B, int Sq, int H, int D, float* out_acc, float* lse_acc,
+                        const float* out_blk, const float* lse_blk, hipStream_t s);
+hipError_t launch_cast_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
+
+}  // namespace ram

@@ -1,0 +1,186 @@
+"""C ABI checks that need no GPU: exported symbols and host-side argument validation.
+
+Every call here fails validation (or is an empty no-op) before anything is
+enqueued, so no device is touched; the pointers are fake but aligned and are
+never dereferenced on these paths.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ring_attention_merge_amd as ram
+from ring_attention_merge_amd import _lib, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000            # 16-byte (and 256-byte) aligned, never dereferenced
+FAKE2 = 0x200000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        build.build()
+    return ram.load()
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "ram.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_header_symbol_is_exported(lib):
+    names = _header_functions()
+    assert set(names) == {"build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
+                          "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_last_error"}, names
+    for n in names:
+        assert hasattr(lib, n), f"libram.so does not export {n}"
+
+
+def _desc(**kw):
+    d = dict(B=1, Sq=256, Skv=256, H=4, Hkv=2, D=128, dtype=ram.RAM_BF16, scale=0.125, softcap=0.0,
+             causal=True, block_q=128, block_kv=64)
+    d.update(kw)
+    return ram.Desc(**d).c()
+
+
+def _src(**kw):
+    return _lib.c_mask_src(kw.get("q_pos", 0), kw.get("kv_pos", 0), kw.get("q_pos_base", 0),
+                           kw.get("kv_pos_base", 0), kw.get("q_seg", 0), kw.get("kv_seg", 0),
+                           kw.get("q_meta_stride_b", 0), kw.get("kv_meta_stride_b", 0))
+
+
+def _bm(**kw):
+    return _lib.c_block_mask(kw.get("tile_class", FAKE), kw.get("row_cnt", FAKE), kw.get("col_idx", FAKE))
+
+
+def _chunk(lib, d, *, q=FAKE, k=FAKE, v=FAKE, src=None, bm=None, sinks=0, mode=0, out=FAKE, lse=FAKE):
+    src = src or _src()
+    bm = bm or _bm()
+    return lib.attn_fwd_chunk(ctypes.byref(d), q, k, v, ctypes.byref(src), ctypes.byref(bm), sinks, mode,
+                              out, lse, 0)
+
+
+def _err(lib):
+    return lib.ram_last_error().decode()
+
+
+def test_kernel_tile(lib):
+    assert ram.kernel_tile(ram.RAM_BF16, 128) == (128, 64)
+    assert ram.kernel_tile(ram.RAM_F32, 64) == (128, 64)
+    with pytest.raises(ram.RamError) as e:
+        ram.kernel_tile(ram.RAM_BF16, 96)
+    assert e.value.status == _lib.RAM_ERR_UNSUPPORTED
+    with pytest.raises(ram.RamError) as e:
+        ram.kernel_tile(7, 128)
+    assert e.value.status == _lib.RAM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw, status, msg", [
+    (dict(H=6, Hkv=4), _lib.RAM_ERR_INVALID, "multiple"),
+    (dict(D=96), _lib.RAM_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=5), _lib.RAM_ERR_UNSUPPORTED, "dtype"),
+    (dict(scale=0.0), _lib.RAM_ERR_INVALID, "scale"),
+    (dict(scale=float("nan")), _lib.RAM_ERR_INVALID, "scale"),
+    (dict(softcap=float("inf")), _lib.RAM_ERR_INVALID, "softcap"),
+    (dict(causal=2), _lib.RAM_ERR_INVALID, "causal"),
+    (dict(block_q=64), _lib.RAM_ERR_INVALID, "tile"),
+    (dict(block_kv=128), _lib.RAM_ERR_INVALID, "tile"),
+    (dict(B=-1), _lib.RAM_ERR_INVALID, "negative"),
+    (dict(H=0), _lib.RAM_ERR_INVALID, ">= 1"),
+    (dict(q_stride_b=100), _lib.RAM_ERR_INVALID, "q_stride_b"),
+    (dict(kv_stride_b=256 * 2 * 128 + 3), _lib.RAM_ERR_INVALID, "kv_stride_b"),
+])
+def test_chunk_desc_validation(lib, kw, status, msg):
+    assert _chunk(lib, _desc(**kw)) == status
+    assert msg in _err(lib)
+
+
+def test_chunk_pointer_validation(lib):
+    d = _desc()
+    assert _chunk(lib, d, q=0) == _lib.RAM_ERR_INVALID and "q is null" in _err(lib)
+    assert _chunk(lib, d, k=FAKE + 2) == _lib.RAM_ERR_UNSUPPORTED and "aligned" in _err(lib)
+    assert _chunk(lib, d, out=0) == _lib.RAM_ERR_INVALID
+    assert _chunk(lib, d, lse=FAKE + 2) == _lib.RAM_ERR_INVALID
+    assert _chunk(lib, d, mode=3) == _lib.RAM_ERR_INVALID and "mode" in _err(lib)
+    assert _chunk(lib, d, src=_src(q_seg=FAKE)) == _lib.RAM_ERR_INVALID and "both" in _err(lib)
+    assert _chunk(lib, d, src=_src(q_pos=FAKE + 1)) == _lib.RAM_ERR_INVALID
+    assert _chunk(lib, d, src=_src(q_pos_base=2**31 - 10)) == _lib.RAM_ERR_INVALID and "overflow" in _err(lib)
+    assert _chunk(lib, d, bm=_bm(row_cnt=0)) == _lib.RAM_ERR_INVALID and "row_cnt" in _err(lib)
+    assert _chunk(lib, d, bm=_bm(col_idx=0)) == _lib.RAM_ERR_INVALID
+    assert _chunk(lib, d, src=_src(kv_meta_stride_b=10)) == _lib.RAM_ERR_INVALID
+    assert lib.attn_fwd_chunk(ctypes.byref(d), FAKE, FAKE, FAKE, None, ctypes.byref(_bm()), 0, 0, FAKE, FAKE,
+                              0) == _lib.RAM_ERR_INVALID
+    assert lib.attn_fwd_chunk(None, FAKE, FAKE, FAKE, None, None, 0, 0, FAKE, FAKE, 0) == _lib.RAM_ERR_INVALID
+
+
+def test_empty_inputs_are_noops(lib):
+    # B = 0 or Sq = 0: valid, nothing to do, nothing launched (works without a GPU)
+    assert _chunk(lib, _desc(B=0), q=0, out=0, lse=0) == _lib.RAM_OK
+    assert _chunk(lib, _desc(Sq=0), q=0, out=0, lse=0) == _lib.RAM_OK
+    d = _desc(Sq=0)
+    assert lib.build_block_mask(ctypes.byref(d), ctypes.byref(_src()), ctypes.byref(_bm()), 0) == _lib.RAM_OK
+    assert lib.lse_merge(0, 5, 2, 128, 0, 0, 0, 0, 0) == _lib.RAM_OK
+    assert _err(lib) == ""
+
+
+def test_mask_validation(lib):
+    bad = [dict(block_q=8), dict(block_kv=1024), dict(Skv=10_000_000, block_kv=16)]
+    for kw in bad:
+        d = _desc(**kw)
+        st = lib.build_block_mask(ctypes.byref(d), ctypes.byref(_src()), ctypes.byref(_bm()), 0)
+        assert st in (_lib.RAM_ERR_INVALID, _lib.RAM_ERR_UNSUPPORTED), kw
+    d = _desc(block_q=256, block_kv=16)
+    assert lib.build_block_mask(ctypes.byref(d), ctypes.byref(_src()), ctypes.byref(_bm(tile_class=0)),
+                                0) == _lib.RAM_ERR_INVALID
+    assert lib.build_block_mask(ctypes.byref(d), None, ctypes.byref(_bm()), 0) == _lib.RAM_ERR_INVALID
+
+
+def test_merge_validation(lib):
+    assert lib.lse_merge(1, 4, 2, 96, FAKE, FAKE, FAKE2, FAKE2, 0) == _lib.RAM_ERR_UNSUPPORTED
+    assert lib.lse_merge(1, 4, 2, 128, FAKE, FAKE, FAKE, FAKE2, 0) == _lib.RAM_ERR_INVALID
+    assert "alias" in _err(lib)
+    assert lib.lse_merge(1, 4, 2, 128, 0, FAKE, FAKE2, FAKE2, 0) == _lib.RAM_ERR_INVALID
+    assert lib.lse_merge(-1, 4, 2, 128, FAKE, FAKE, FAKE2, FAKE2, 0) == _lib.RAM_ERR_INVALID
+
+
+def _ring(lib, d, n, r, ws=FAKE, ws_bytes=1 << 40, src=None, out=FAKE, q=FAKE):
+    src = src or _src()
+    return lib.ring_attn_fwd_1gpu(ctypes.byref(d), n, r, q, FAKE, FAKE, ctypes.byref(src), 0, out, FAKE2, ws,
+                                  ws_bytes, 0)
+
+
+def test_ring_validation_and_workspace(lib):
+    d = _desc(B=1, Sq=4096, Skv=4096, H=8, Hkv=8)
+    need = lib.ring_attn_workspace_bytes(ctypes.byref(d), 4)
+    acc = 4096 * 8 * 128 * 4
+    tiles = 4 * 32 * 64
+    expect = acc + ((tiles + 255) // 256) * 256 + ((4 * 32 * 4 + 255) // 256) * 256 + tiles * 4
+    assert need == expect
+    d32 = _desc(B=1, Sq=4096, Skv=4096, H=8, Hkv=8, dtype=ram.RAM_F32)
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(d32), 4) == need - acc   # fp32 accumulates in out
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert _ring(lib, d, 0, -1) == _lib.RAM_ERR_INVALID
+    assert _ring(lib, d, 4, 4) == _lib.RAM_ERR_INVALID and "q_shard" in _err(lib)
+    assert _ring(lib, d, 4, -2) == _lib.RAM_ERR_INVALID
+    assert _ring(lib, d, 4, 3, ws_bytes=need - 1) == _lib.RAM_ERR_WORKSPACE and "need" in _err(lib)
+    assert _ring(lib, d, 4, 3, ws=FAKE + 16) == _lib.RAM_ERR_WORKSPACE
+    assert _ring(lib, d, 4, 3, ws=0) == _lib.RAM_ERR_WORKSPACE
+    assert _ring(lib, d, 4, 3, src=_src(q_pos_base=2**31 - 5000)) == _lib.RAM_ERR_INVALID  # 3*Sq overflows
+    assert _ring(lib, d, 4, 3, src=_src(kv_meta_stride_b=4096)) == _lib.RAM_ERR_INVALID    # must span 4 chunks
+    assert _ring(lib, d, 4, 3, out=0) == _lib.RAM_ERR_INVALID
+    # the ring picks its own tile: a caller's block_q/block_kv are ignored
+    dt = _desc(B=1, Sq=4096, Skv=4096, H=8, Hkv=8, block_q=32, block_kv=32)
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(dt), 4) == need
+    assert _ring(lib, _desc(B=0), 4, 3, q=0, out=0) == _lib.RAM_OK
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    import torch
+    d = ram.Desc(B=1, Sq=8, Skv=8, H=1, Hkv=1, D=64, dtype=ram.RAM_F32, scale=0.1)
+    x = torch.zeros(8 * 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ram.attn_fwd_chunk(d, x, x, x, ram.MaskSrc(), ram.alloc_block_mask(d, device="cpu"), None, 0, x,
+                           torch.zeros(8), stream=0)
