@@ -16,9 +16,13 @@
 //    lane owns one query row (lane & 31) and 16 keys, so row max / row sum
 //    are in-lane plus one v_permlane32_swap with the partner lane.
 //  * O^T = V^T * P^T with the same instruction: P leaves the S accumulator as
-//    packed bf16 and feeds the B operand directly (no LDS round trip); V is
-//    stored transposed in LDS, keys permuted inside each group of 16 so one
-//    16-byte LDS read gives the A operand in the key order P arrives in.
+//    packed bf16 and feeds the B operand directly (no LDS round trip). V is
+//    stored row-major in LDS like K and its A operand is read with gfx950's
+//    transposing LDS read (ds_read_b64_tr_b16): two reads give each lane 8
+//    keys of one head-dim column, in the key order P arrives in.
+//  * LDS pitches keep every access conflict-free: K rows are 272 B (16 lanes
+//    reading 16 B from 16 consecutive rows hit 16 distinct bank quads), V rows
+//    are 320 B (a transposing read covers 4 rows x 64 B, i.e. all 64 banks).
 //  * K / V tiles are double-buffered in LDS; the next tile's global loads are
 //    issued before the current tile's math, one barrier per tile.
 //  * Online softmax in base 2 with the scale folded into one FMA; the running
@@ -203,13 +207,12 @@ __device__ __forceinline__ void epilogue(const f32x16 (&O)[NDB], float m_ref, fl
   if (lg == 0) *lptr = new_lse;
 }
 
-// Physical slot of key k inside a V^T row: within each group of 16 keys the
-// groups of 4 are stored in the order 0, 2, 1, 3, so that lane group lg's
-// 8 keys {4lg..4lg+3, 8+4lg..8+4lg+3} are contiguous.
-__device__ __forceinline__ int vt_slot(int k) {
-  const int q4 = (k >> 2) & 3;
-  const int sw = ((q4 & 1) << 1) | (q4 >> 1);
-  return (k & ~15) | (sw << 2) | (k & 3);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read: within each group of 16 lanes, lane i receives element
+// (i % 4) of the 8-byte chunks addressed by lanes i/4, i/4+4, i/4+8, i/4+12.
+__device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
 // ------------------------------------------------------------------------------ bf16
@@ -218,15 +221,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
   constexpr int BK = kBlockKV;
   constexpr int NDS = D / 16;      // k-steps of S^T = K Q^T
   constexpr int NDB = D / 32;      // 32-row blocks of O^T
-  constexpr int KP = D + 8;        // K row pitch (elements)
-  constexpr int VP = BK + 8;       // V^T row pitch (elements)
+  constexpr int KP = D + 8;        // K row pitch (elements): 272 B for D = 128
+  constexpr int VP = D + 32;       // V row pitch (elements): 320 B for D = 128
   constexpr int K_ELEMS = BK * KP;
-  constexpr int V_ELEMS = D * VP;
-  constexpr int CH = D / 8;               // 16-byte chunks per K row
-  constexpr int RPP = kThreads / CH;      // K rows per load pass
-  constexpr int NPK = BK / RPP;           // K load passes
-  constexpr int KG = BK * D / (8 * kThreads);  // V keys per thread (4 or 2)
-  static_assert(KG == 4 || KG == 2, "V tile split");
+  constexpr int V_ELEMS = BK * VP;
+  constexpr int CH = D / 8;               // 16-byte chunks per row
+  constexpr int RPP = kThreads / CH;      // rows per load pass
+  constexpr int NPK = BK / RPP;           // load passes per tensor
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (K_ELEMS + V_ELEMS)];
 
   int b, h, qb;
@@ -273,8 +274,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.kv_stride_b + g * D;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.kv_stride_b + g * D;
   const int kc = tid % CH, kr0 = tid / CH;
-  const int vc = tid % CH, vk0 = (tid / CH) * KG;
-  uint4 kreg[NPK], vreg[KG];
+  uint4 kreg[NPK], vreg[NPK];
+  // Transposing-read address of this lane inside a V tile (see lds_read_tr16):
+  // row 4*lg + (i >> 2), column 16*half + 4*(i & 3), i = lane & 15, half = (lane >> 4) & 1.
+  const int vtr_off = (4 * lg + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   auto gload = [&](int kb) {
     const int k0 = kb * BK;
@@ -285,38 +288,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
                             : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int r = 0; r < KG; ++r) {
-      const int row = k0 + vk0 + r;
-      vreg[r] = row < p.Skv ? *reinterpret_cast<const uint4*>(vbase + row * krs + vc * 8)
+    for (int i = 0; i < NPK; ++i) {
+      const int row = k0 + kr0 + i * RPP;
+      vreg[i] = row < p.Skv ? *reinterpret_cast<const uint4*>(vbase + row * krs + kc * 8)
                             : make_uint4(0, 0, 0, 0);
     }
   };
   auto lstore = [&](int buf) {
     __bf16* Ks = smem + buf * (K_ELEMS + V_ELEMS);
-    __bf16* Vt = Ks + K_ELEMS;
+    __bf16* Vs = Ks + K_ELEMS;
 #pragma unroll
-    for (int i = 0; i < NPK; ++i)
+    for (int i = 0; i < NPK; ++i) {
       *reinterpret_cast<uint4*>(Ks + (kr0 + i * RPP) * KP + kc * 8) = kreg[i];
-    const int slot = vt_slot(vk0);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {     // u32 word m holds dims 2m (low half), 2m+1 (high half)
-      uint32_t wv[KG];
-#pragma unroll
-      for (int r = 0; r < KG; ++r) wv[r] = (&vreg[r].x)[m];
-      __bf16* d0 = Vt + (vc * 8 + 2 * m) * VP + slot;
-      __bf16* d1 = d0 + VP;
-      if constexpr (KG == 4) {
-        uint2 lo, hi;
-        lo.x = (wv[0] & 0xffffu) | (wv[1] << 16);
-        lo.y = (wv[2] & 0xffffu) | (wv[3] << 16);
-        hi.x = (wv[0] >> 16) | (wv[1] & 0xffff0000u);
-        hi.y = (wv[2] >> 16) | (wv[3] & 0xffff0000u);
-        *reinterpret_cast<uint2*>(d0) = lo;
-        *reinterpret_cast<uint2*>(d1) = hi;
-      } else {
-        *reinterpret_cast<uint32_t*>(d0) = (wv[0] & 0xffffu) | (wv[1] << 16);
-        *reinterpret_cast<uint32_t*>(d1) = (wv[0] >> 16) | (wv[1] & 0xffff0000u);
-      }
+      *reinterpret_cast<uint4*>(Vs + (kr0 + i * RPP) * VP + kc * 8) = vreg[i];
     }
   };
 
@@ -332,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
     const bool has_next = it + 1 < cnt;
     if (has_next) gload(cols[it + 1]);
     const __bf16* Ks = smem + buf * (K_ELEMS + V_ELEMS);
-    const __bf16* Vt = Ks + K_ELEMS;
+    const __bf16* Vs = Ks + K_ELEMS;
 
     f32x16 S[2];
     S[0] = f32x16{};
@@ -370,7 +354,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vt + (db * 32 + ln) * VP + ks * 16 + lg * 8);
+        // keys ks*16 + 4*lg + 0..3 and ks*16 + 8 + 4*lg + 0..3 of column db*32 + (lane & 31)
+        const __bf16* vp = Vs + ks * 16 * VP + db * 32 + vtr_off;
+        const s16x4 lo = lds_read_tr16(vp);
+        const s16x4 hi = lds_read_tr16(vp + 8 * VP);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[ks], O[db], 0, 0, 0);
       }
     }
