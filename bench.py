@@ -82,6 +82,32 @@ def tile_counts(w, desc, dev, tile_q, tile_kv):
     return counts
 
 
+def kernel_source_hash() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "ring_attention_merge_amd", "csrc", "attn_fwd.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per chunk launch from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_bf16_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        line = line.strip().strip("`")
+        if "=" in line and " " not in line.split("=", 1)[0]:
+            k, v = line.split("=", 1)
+            fields[k] = v.strip()
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, n_rows: int):
     import oracle
     from threadpoolctl import threadpool_info
@@ -112,6 +138,8 @@ def main():
     ap.add_argument("--workload", default="c5", choices=["c5", "c4", "c4mqa", "c3", "c2"])
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (to scale FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); this path has no multi-GPU "
@@ -193,10 +221,18 @@ def main():
     achieved = sum(flops_in_order) / (kern_ms * 1e-3) / 1e12
     log("chunk kernel ms (visit order): " + ", ".join(f"{x:.3f}" for x in per_chunk_ms))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": ATTN_KERNEL,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(args.workload),
+                "kernel": ATTN_KERNEL,
                 "launches_per_step": w.n_chunks, "mean_launch_us": round(1e3 * kern_ms / w.n_chunks, 2),
                 "flops_per_launch_mean": sum(eff_flops_chunk) / w.n_chunks}
     del acc, acc_lse
+    if args.copy_calibration:
+        a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        b2 = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b2.copy_(a)                     # reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
+        del a, b2
 
     cpu = None
     if not args.no_cpu:

@@ -321,6 +321,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
     f32x16 S[2];
     S[0] = f32x16{};
     S[1] = f32x16{};
+    // MFMA sections run at raised wave priority so that the other wave on
+    // this SIMD fills the matrix core's shadow with its softmax arithmetic.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
 #pragma unroll
@@ -329,6 +333,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
         S[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], S[kb2], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (CAP) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -350,6 +356,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
         P[ks][2 * j + 1] = pk[1];
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -362,6 +370,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
         O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[ks], O[db], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     if (has_next) lstore(buf ^ 1);
     __syncthreads();
   }
