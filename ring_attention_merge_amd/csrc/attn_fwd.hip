@@ -32,43 +32,15 @@
 //  * Workgroup ids are mapped so that each XCD (ids are dealt round-robin over
 //    the 8 XCDs) gets a contiguous range of (batch, kv head) groups, keeping
 //    their K/V in that XCD's L2, and within it heavier (later) q tiles first.
-#include <hip/hip_runtime.h>
+#include <cstdlib>
+#include <cstring>
 
-#include <cmath>
-
-#include "ram_internal.h"
+#include "attn_common.h"
 
 namespace ram {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-
-__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
-
-// Lanes l and l^32 hold the same query row. v_permlane32_swap exchanges the
-// upper half of its first operand with the lower half of its second; with x
-// passed as both, the two results of each lane are {own value, partner value}
-// (in an order that depends on the lane half), so max / sum over the pair is
-// the reduction over both lanes.
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+using namespace attn;
 
 // Work decode: item order is (batch*Hkv + kv head, q tile descending, head in group);
 // XCD x = id % 8 takes the contiguous item range [x*per, (x+1)*per).
@@ -88,131 +60,6 @@ __device__ __forceinline__ bool decode_work(const AttnParams& p, int& b, int& h,
   h = g * G + hg;
   qb = p.nQb - 1 - qrev;
   return true;
-}
-
-// Element mask for the 32 keys a lane holds of a 64-key tile starting at k0.
-// Key of accumulator register i of half kb2: k0 + kb2*32 + 8*(i>>2) + 4*lg + (i&3).
-__device__ __forceinline__ void apply_mask(f32x16 (&S)[2], const AttnParams& p, int b, int k0,
-                                           int lg, int qpos, int qseg) {
-  const int32_t* kvp = p.kv_pos ? p.kv_pos + (int64_t)b * p.kvm_stride_b : nullptr;
-  const int32_t* kvs = p.kv_seg ? p.kv_seg + (int64_t)b * p.kvm_stride_b : nullptr;
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = k0 + kb2 * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
-      bool ok = key < p.Skv;
-      if (ok && p.causal) {
-        const int kp = kvp ? kvp[key] : p.kv_pos_base + key;
-        ok = kp <= qpos;
-      }
-      if (ok && kvs) ok = (kvs[key] == qseg) && (qseg != -1);
-      if (!ok) S[kb2][i] = neg_inf();
-    }
-  }
-}
-
-// Soft cap in log2 units: u = cap*log2(e) * tanh(s*scale/cap), tanh(x) = 1 - 2/(1+e^{2x}).
-__device__ __forceinline__ float capped_log2(float s, float k2, float cap_log2) {
-  const float e = fast_exp2(s * k2);
-  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e);
-  return cap_log2 * t;
-}
-
-// Online-softmax step on the 32 scores a lane holds. Returns nothing; updates
-// m_ref / l_acc / O and leaves the weights in S.
-template <int NDB, bool CAP>
-__device__ __forceinline__ void softmax_step(f32x16 (&S)[2], f32x16 (&O)[NDB], float& m_ref,
-                                             float& l_acc, const AttnParams& p) {
-  float mx = neg_inf();
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[kb2][i]);
-  mx = pair_max(mx);
-  const float umax = CAP ? mx : mx * p.scale_log2;
-  const bool need = umax > m_ref + kRescaleThreshold;
-  if (__builtin_amdgcn_ballot_w64(need) != 0) {
-    const float m_new = fmaxf(m_ref, umax);
-    const float alpha = (m_new == neg_inf()) ? 1.0f : fast_exp2(m_ref - m_new);
-    l_acc *= alpha;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
-    m_ref = m_new;
-  }
-  const float msub = (m_ref == neg_inf()) ? 0.0f : m_ref;
-  float ls = 0.0f;
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = CAP ? fast_exp2(S[kb2][i] - msub)
-                          : fast_exp2(__builtin_fmaf(S[kb2][i], p.scale_log2, -msub));
-      S[kb2][i] = e;
-      ls += e;
-    }
-  l_acc += ls;
-}
-
-// Epilogue: normalise, then write (mode 0) or merge into (mode 1) the running state.
-template <int NDB>
-__device__ __forceinline__ void epilogue(const f32x16 (&O)[NDB], float m_ref, float l_acc,
-                                         const AttnParams& p, int b, int h, int q_row, int lg) {
-  constexpr int D = NDB * 32;
-  const float l_row = pair_sum(l_acc);
-  if (q_row >= p.Sq) return;
-  const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-  const float lse_c = l_row > 0.0f ? (m_ref + log2f(l_row)) * kLn2 : neg_inf();
-  float* orow = p.out + (((int64_t)b * p.Sq + q_row) * p.H + h) * D;
-  float* lptr = p.lse + ((int64_t)b * p.H + h) * p.Sq + q_row;
-  if (p.mode == 0) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        float4 o;
-        o.x = O[db][4 * i4 + 0] * inv;
-        o.y = O[db][4 * i4 + 1] * inv;
-        o.z = O[db][4 * i4 + 2] * inv;
-        o.w = O[db][4 * i4 + 3] * inv;
-        *reinterpret_cast<float4*>(orow + db * 32 + 8 * i4 + 4 * lg) = o;
-      }
-    if (lg == 0) *lptr = lse_c;
-    return;
-  }
-  // merge (ring-splash _update_out_and_lse)
-  if (lse_c == neg_inf()) return;  // nothing attended in this chunk: identity
-  const float acc_lse = *lptr;
-  float sig = 1.0f, new_lse = lse_c;
-  if (acc_lse != neg_inf()) {
-    const float x = lse_c - acc_lse;
-    sig = 1.0f / (1.0f + expf(-x));
-    new_lse = acc_lse + (fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))));
-  }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      float4* ptr = reinterpret_cast<float4*>(orow + db * 32 + 8 * i4 + 4 * lg);
-      float4 a = (acc_lse == neg_inf()) ? make_float4(0.f, 0.f, 0.f, 0.f) : *ptr;
-      float4 o;
-      o.x = a.x - sig * (a.x - O[db][4 * i4 + 0] * inv);
-      o.y = a.y - sig * (a.y - O[db][4 * i4 + 1] * inv);
-      o.z = a.z - sig * (a.z - O[db][4 * i4 + 2] * inv);
-      o.w = a.w - sig * (a.w - O[db][4 * i4 + 3] * inv);
-      *ptr = o;
-    }
-  if (lg == 0) *lptr = new_lse;
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Transposing LDS read: within each group of 16 lanes, lane i receives element
-// (i % 4) of the 8-byte chunks addressed by lanes i/4, i/4+4, i/4+8, i/4+12.
-__device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
 // ------------------------------------------------------------------------------ bf16
@@ -519,8 +366,19 @@ hipError_t launch(K kernel, const AttnParams& p, hipStream_t s) {
 
 }  // namespace
 
+// Kernel choice for bf16. The 4-wave kernel is the default; the 8-wave
+// ping-pong kernel measured slower on MI355X (its MFMA phase is bound by the
+// transposing LDS reads, ~56 B/clk/CU). RAM_ATTN_KERNEL=4wave|pingpong forces
+// one (the tests check both against the oracle).
+static int attn_variant(const AttnParams&) {
+  const char* e = getenv("RAM_ATTN_KERNEL");
+  if (e && strcmp(e, "pingpong") == 0) return 1;
+  return 0;
+}
+
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s) {
   const bool cap = p.softcap_on != 0;
+  if (dtype == 1 && attn_variant(p) == 1) return launch_attn_pp(p, s);
   if (dtype == 1) {
     if (p.D == 128) return cap ? launch(attn_fwd_bf16<128, true>, p, s) : launch(attn_fwd_bf16<128, false>, p, s);
     return cap ? launch(attn_fwd_bf16<64, true>, p, s) : launch(attn_fwd_bf16<64, false>, p, s);

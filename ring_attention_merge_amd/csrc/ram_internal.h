@@ -57,6 +57,7 @@ struct MaskParams {
 };
 
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s);
+hipError_t launch_attn_pp(const AttnParams& p, hipStream_t s);   // bf16, 8-wave ping-pong
 hipError_t launch_block_mask(const MaskParams& p, int n_chunks, hipStream_t s);
 hipError_t launch_merge(int B, int Sq, int H, int D, float* out_acc, float* lse_acc,
                         const float* out_blk, const float* lse_blk, hipStream_t s);
