@@ -79,11 +79,13 @@ __device__ __forceinline__ float capped_log2(float s, float k2, float cap_log2) 
 template <int NDB, bool CAP>
 __device__ __forceinline__ void softmax_step(f32x16 (&S)[2], f32x16 (&O)[NDB], float& m_ref,
                                              float& l_acc, const AttnParams& p) {
-  float mx = neg_inf();
+  // row max: a tree over the 32 scores (short dependency chains)
+  float t[8];
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[kb2][i]);
+  for (int u = 0; u < 8; ++u)
+    t[u] = fmaxf(fmaxf(S[u >> 2][(u & 3) * 4 + 0], S[u >> 2][(u & 3) * 4 + 1]),
+                 fmaxf(S[u >> 2][(u & 3) * 4 + 2], S[u >> 2][(u & 3) * 4 + 3]));
+  float mx = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
   mx = pair_max(mx);
   const float umax = CAP ? mx : mx * p.scale_log2;
   const bool need = umax > m_ref + kRescaleThreshold;
@@ -98,17 +100,17 @@ __device__ __forceinline__ void softmax_step(f32x16 (&S)[2], f32x16 (&O)[NDB], f
     m_ref = m_new;
   }
   const float msub = (m_ref == neg_inf()) ? 0.0f : m_ref;
-  float ls = 0.0f;
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = CAP ? fast_exp2(S[kb2][i] - msub)
-                          : fast_exp2(__builtin_fmaf(S[kb2][i], p.scale_log2, -msub));
-      S[kb2][i] = e;
-      ls += e;
-    }
-  l_acc += ls;
+    for (int i = 0; i < 16; ++i)
+      S[kb2][i] = CAP ? fast_exp2(S[kb2][i] - msub) : fast_exp2(__builtin_fmaf(S[kb2][i], p.scale_log2, -msub));
+  // row sum: a tree as well
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    t[u] = (S[u >> 2][(u & 3) * 4 + 0] + S[u >> 2][(u & 3) * 4 + 1]) +
+           (S[u >> 2][(u & 3) * 4 + 2] + S[u >> 2][(u & 3) * 4 + 3]);
+  l_acc += ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
 }
 
 // Epilogue: normalise, then write (mode 0) or merge into (mode 1) the running state.

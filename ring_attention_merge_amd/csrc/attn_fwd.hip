@@ -366,19 +366,30 @@ hipError_t launch(K kernel, const AttnParams& p, hipStream_t s) {
 
 }  // namespace
 
-// Kernel choice for bf16. The 4-wave kernel is the default; the 8-wave
-// ping-pong kernel measured slower on MI355X (its MFMA phase is bound by the
-// transposing LDS reads, ~56 B/clk/CU). RAM_ATTN_KERNEL=4wave|pingpong forces
-// one (the tests check both against the oracle).
-static int attn_variant(const AttnParams&) {
+// Kernel choice for bf16. The 4-wave kernel is the default. The other layouts
+// are kept as measured alternatives, all checked against the oracle; on the
+// 32k causal D=128 workload they ran at or below the default:
+//   pingpong  8 waves in two groups taking turns at the matrix cores
+//   wide      4 waves, 64 query rows per wave (halves LDS reads per MFMA)
+//   g8        8 waves, 32 rows each, 3-stage K/V ring filled by LDS DMA
+//   g8p       g8 with each wave's softmax interleaved between its MFMAs
+// RAM_ATTN_KERNEL=<name> forces one (D = 128 only, except pingpong).
+static int attn_variant(const AttnParams& p) {
   const char* e = getenv("RAM_ATTN_KERNEL");
   if (e && strcmp(e, "pingpong") == 0) return 1;
+  if (e && strcmp(e, "wide") == 0 && p.D == 128) return 2;
+  if (e && strcmp(e, "g8") == 0 && p.D == 128) return 3;
+  if (e && strcmp(e, "g8p") == 0 && p.D == 128) return 4;
   return 0;
 }
 
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s) {
   const bool cap = p.softcap_on != 0;
-  if (dtype == 1 && attn_variant(p) == 1) return launch_attn_pp(p, s);
+  const int variant = dtype == 1 ? attn_variant(p) : 0;
+  if (variant == 1) return launch_attn_pp(p, s);
+  if (variant == 2) return launch_attn_w64(p, s);
+  if (variant == 3) return launch_attn_g8(p, s);
+  if (variant == 4) return launch_attn_g8p(p, s);
   if (dtype == 1) {
     if (p.D == 128) return cap ? launch(attn_fwd_bf16<128, true>, p, s) : launch(attn_fwd_bf16<128, false>, p, s);
     return cap ? launch(attn_fwd_bf16<64, true>, p, s) : launch(attn_fwd_bf16<64, false>, p, s);

@@ -58,6 +58,9 @@ struct MaskParams {
 
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_attn_pp(const AttnParams& p, hipStream_t s);   // bf16, 8-wave ping-pong
+hipError_t launch_attn_w64(const AttnParams& p, hipStream_t s);  // bf16, D = 128, 64 rows per wave
+hipError_t launch_attn_g8(const AttnParams& p, hipStream_t s);   // bf16, D = 128, 8 waves, 3-stage DMA
+hipError_t launch_attn_g8p(const AttnParams& p, hipStream_t s);  // bf16, D = 128, 8 waves, pipelined
 hipError_t launch_block_mask(const MaskParams& p, int n_chunks, hipStream_t s);
 hipError_t launch_merge(int B, int Sq, int H, int D, float* out_acc, float* lse_acc,
                         const float* out_blk, const float* lse_blk, hipStream_t s);

@@ -21,9 +21,9 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.fixture(params=["4wave", "pingpong"])
+@pytest.fixture(params=["4wave", "pingpong", "wide", "g8", "g8p"])
 def variant(request, monkeypatch):
-    """Force one of the two bf16 attention kernels (fp32 inputs always use the fp32 kernel)."""
+    """Force one of the bf16 attention kernel layouts (fp32 inputs always use the fp32 kernel)."""
     monkeypatch.setenv("RAM_ATTN_KERNEL", request.param)
     return request.param
 
