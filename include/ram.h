@@ -66,7 +66,7 @@ typedef enum { RAM_TILE_EMPTY = 0, RAM_TILE_PARTIAL = 1, RAM_TILE_FULL = 2 } ram
 typedef enum { RAM_OUT_WRITE = 0, RAM_OUT_MERGE = 1 } ram_out_mode;
 
 typedef struct {
-  int32_t B, Sq, Skv, H, Hkv, D; /* Skv: keys of one chunk; H % Hkv == 0; D in {64, 128} */
+  int32_t B, Sq, Skv, H, Hkv, D; /* Skv: keys of one chunk; H % Hkv == 0, H <= 65536; D in {64, 128} */
   int32_t dtype;                 /* ram_dtype of q, k, v (and of the final out) */
   int64_t q_stride_b;            /* elements between batches of q; 0 = Sq*H*D */
   int64_t kv_stride_b;           /* elements between batches of k and v; 0 = Skv*Hkv*D */

@@ -29,6 +29,13 @@ constexpr int kThreads = 64 * kWaves;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// The tile lists are read-only for the whole launch: reading them through the
+// constant address space lets uniform loads go through the scalar cache.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* as_const_space(const T* p) {
+  return (const __attribute__((address_space(4))) T*)p;
+}
+
 // Lanes l and l^32 hold the same query row. v_permlane32_swap exchanges the
 // upper half of its first operand with the lower half of its second; with x
 // passed as both, the two results of each lane are {own value, partner value}
@@ -165,6 +172,16 @@ __device__ __forceinline__ void epilogue(const f32x16 (&O)[NDB], float m_ref, fl
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + bytes): loads at offsets >= bytes return
+// zero (raw buffer, stride 0; 0x00020000 is the gfx9 word-3 default format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load_16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 // Transposing LDS read: within each group of 16 lanes, lane i receives element
 // (i % 4) of the 8-byte chunks addressed by lanes i/4, i/4+4, i/4+8, i/4+12.

@@ -90,8 +90,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
   const int64_t mrow = (int64_t)b * p.nQb + qb;
   const int cnt = p.row_cnt[mrow];
   if (cnt == 0 && p.mode == 1 && p.sinks == nullptr) return;
-  const int32_t* cols = p.col_idx + mrow * p.nKb;
-  const uint8_t* cls = p.tile_class + mrow * p.nKb;
+  const auto cols = as_const_space(p.col_idx + mrow * p.nKb);
+  const auto cls = as_const_space(p.tile_class + mrow * p.nKb);
 
   // Q fragments (B operand): lane holds row q_row, dims ds*16 + lg*8 .. +7.
   bf16x8 qf[NDS];
@@ -126,20 +126,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
   // row 4*lg + (i >> 2), column 16*half + 4*(i & 3), i = lane & 15, half = (lane >> 4) & 1.
   const int vtr_off = (4 * lg + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
+  // K / V tiles come in through buffer loads whose resource covers exactly the
+  // tile's rows that exist: rows past Skv read as zero, with no branches.
+  const uint32_t row_bytes = (uint32_t)krs * 2;
+  uint32_t voff[NPK];
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) voff[i] = (uint32_t)(kr0 + i * RPP) * row_bytes + kc * 16;
   auto gload = [&](int kb) {
     const int k0 = kb * BK;
+    const uint32_t bytes = (uint32_t)min(p.Skv - k0, BK) * row_bytes;
+    const auto kr = tile_rsrc(kbase + (int64_t)k0 * krs, bytes);
+    const auto vr = tile_rsrc(vbase + (int64_t)k0 * krs, bytes);
 #pragma unroll
-    for (int i = 0; i < NPK; ++i) {
-      const int row = k0 + kr0 + i * RPP;
-      kreg[i] = row < p.Skv ? *reinterpret_cast<const uint4*>(kbase + row * krs + kc * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < NPK; ++i) kreg[i] = buffer_load_16(kr, voff[i]);
 #pragma unroll
-    for (int i = 0; i < NPK; ++i) {
-      const int row = k0 + kr0 + i * RPP;
-      vreg[i] = row < p.Skv ? *reinterpret_cast<const uint4*>(vbase + row * krs + kc * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < NPK; ++i) vreg[i] = buffer_load_16(vr, voff[i]);
   };
   auto lstore = [&](int buf) {
     __bf16* Ks = smem + buf * (K_ELEMS + V_ELEMS);
@@ -151,17 +152,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
     }
   };
 
+  // The tile list is read ahead: entry it+2 and the mask flag of tile it+1
+  // are loaded while tile it is processed, so no iteration waits on them.
+  auto needs_mask = [&](int kb) { return cls[kb] != 2 || (kb + 1) * BK > p.Skv; };
+  int kb_cur = cnt > 0 ? cols[0] : 0;
+  int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
+  bool mk_cur = needs_mask(kb_cur);
   if (cnt > 0) {
-    gload(cols[0]);
+    gload(kb_cur);
     lstore(0);
   }
   __syncthreads();
 
   for (int it = 0; it < cnt; ++it) {
-    const int kb = cols[it];
+    const int kb = kb_cur;
+    const bool need_mask = mk_cur;
     const int buf = it & 1;
     const bool has_next = it + 1 < cnt;
-    if (has_next) gload(cols[it + 1]);
+    const int kb_nn = cols[min(it + 2, cnt - 1)];
+    const bool mk_nxt = needs_mask(kb_nxt);
+    if (has_next) gload(kb_nxt);
     const __bf16* Ks = smem + buf * (K_ELEMS + V_ELEMS);
     const __bf16* Vs = Ks + K_ELEMS;
 
@@ -188,7 +198,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
     }
-    const bool need_mask = cls[kb] != 2 || (kb + 1) * BK > p.Skv;
     if (need_mask) apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
     softmax_step<NDB, CAP>(S, O, m_ref, l_acc, p);
 
@@ -221,6 +230,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
     __builtin_amdgcn_sched_barrier(0);
     if (has_next) lstore(buf ^ 1);
     __syncthreads();
+    kb_cur = kb_nxt;
+    kb_nxt = kb_nn;
+    mk_cur = mk_nxt;
   }
   epilogue<NDB>(O, m_ref, l_acc, p, b, h, q_row, lg);
 }
@@ -252,8 +264,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(AttnParams p) {
   const int64_t mrow = (int64_t)b * p.nQb + qb;
   const int cnt = p.row_cnt[mrow];
   if (cnt == 0 && p.mode == 1 && p.sinks == nullptr) return;
-  const int32_t* cols = p.col_idx + mrow * p.nKb;
-  const uint8_t* cls = p.tile_class + mrow * p.nKb;
+  const auto cols = as_const_space(p.col_idx + mrow * p.nKb);
+  const auto cls = as_const_space(p.tile_class + mrow * p.nKb);
 
   float qf[NDS];
   {
@@ -303,17 +315,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(AttnParams p) {
     }
   };
 
+  // The tile list is read ahead: entry it+2 and the mask flag of tile it+1
+  // are loaded while tile it is processed, so no iteration waits on them.
+  auto needs_mask = [&](int kb) { return cls[kb] != 2 || (kb + 1) * BK > p.Skv; };
+  int kb_cur = cnt > 0 ? cols[0] : 0;
+  int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
+  bool mk_cur = needs_mask(kb_cur);
   if (cnt > 0) {
-    gload(cols[0]);
+    gload(kb_cur);
     lstore(0);
   }
   __syncthreads();
 
   for (int it = 0; it < cnt; ++it) {
-    const int kb = cols[it];
+    const int kb = kb_cur;
+    const bool need_mask = mk_cur;
     const int buf = it & 1;
     const bool has_next = it + 1 < cnt;
-    if (has_next) gload(cols[it + 1]);
+    const int kb_nn = cols[min(it + 2, cnt - 1)];
+    const bool mk_nxt = needs_mask(kb_nxt);
+    if (has_next) gload(kb_nxt);
     const float* Ks = smem + buf * 2 * ELEMS;
     const float* Vs = Ks + ELEMS;
 
@@ -334,7 +355,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
     }
-    const bool need_mask = cls[kb] != 2 || (kb + 1) * BK > p.Skv;
     if (need_mask) apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
     softmax_step<NDB, CAP>(S, O, m_ref, l_acc, p);
 
@@ -352,6 +372,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(AttnParams p) {
     }
     if (has_next) lstore(buf ^ 1);
     __syncthreads();
+    kb_cur = kb_nxt;
+    kb_nxt = kb_nn;
+    mk_cur = mk_nxt;
   }
   epilogue<NDB>(O, m_ref, l_acc, p, b, h, q_row, lg);
 }

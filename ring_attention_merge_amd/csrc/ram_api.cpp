@@ -42,6 +42,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int64_t kMaxSeq = int64_t(1) << 30;
+constexpr int kMaxHeads = 1 << 16;
 
 // Checks the fields every call reads. `tile_for_attn` also requires the
 // kernel tile; otherwise the mask tile limits apply.
@@ -55,6 +56,9 @@ ram_status check_desc(const ram_attn_desc* d, bool tile_for_attn, bool need_head
   if (need_heads) {
     if (d->H < 1 || d->Hkv < 1) return fail(RAM_ERR_INVALID, "H=%d Hkv=%d must be >= 1", d->H, d->Hkv);
     if (d->H % d->Hkv) return fail(RAM_ERR_INVALID, "H=%d is not a multiple of Hkv=%d", d->H, d->Hkv);
+    // K/V tiles are read through 32-bit buffer offsets: one tile of key rows
+    // (64 x Hkv x D elements) must stay well inside 4 GiB.
+    if (d->H > kMaxHeads) return fail(RAM_ERR_UNSUPPORTED, "H=%d above %d", d->H, kMaxHeads);
     if (d->D != 64 && d->D != 128) return fail(RAM_ERR_UNSUPPORTED, "head dim D=%d (built: 64, 128)", d->D);
     if (d->dtype != RAM_F32 && d->dtype != RAM_BF16) return fail(RAM_ERR_UNSUPPORTED, "dtype %d", d->dtype);
     if (!std::isfinite(d->scale) || !(d->scale > 0.0f))

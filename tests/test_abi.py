@@ -90,6 +90,7 @@ def test_kernel_tile(lib):
     (dict(block_kv=128), _lib.RAM_ERR_INVALID, "tile"),
     (dict(B=-1), _lib.RAM_ERR_INVALID, "negative"),
     (dict(H=0), _lib.RAM_ERR_INVALID, ">= 1"),
+    (dict(H=1 << 17, Hkv=1), _lib.RAM_ERR_UNSUPPORTED, "H=131072 above"),
     (dict(q_stride_b=100), _lib.RAM_ERR_INVALID, "q_stride_b"),
     (dict(kv_stride_b=256 * 2 * 128 + 3), _lib.RAM_ERR_INVALID, "kv_stride_b"),
 ])
