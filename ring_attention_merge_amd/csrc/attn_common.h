@@ -52,17 +52,35 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Element mask for the 32 keys a lane holds of a 64-key tile starting at k0.
-// Key of accumulator register i of half kb2: k0 + kb2*32 + 8*(i>>2) + 4*lg + (i&3).
-__device__ __forceinline__ void apply_mask(f32x16 (&S)[2], const AttnParams& p, int b, int k0,
+// Element mask for the keys a lane holds of NK 32-key blocks starting at k0.
+// Key of accumulator register i of block kb2: k0 + kb2*32 + 8*(i>>2) + 4*lg + (i&3).
+template <int NK>
+__device__ __forceinline__ void apply_mask(f32x16 (&S)[NK], const AttnParams& p, int b, int k0,
                                            int lg, int qpos, int qseg) {
+  if (!p.kv_pos && !p.kv_seg) {
+    // positions kv_pos_base + key: exactly the keys below `lim` are kept
+    const int64_t reach = (int64_t)qpos - p.kv_pos_base + 1;
+    const int lim = p.causal ? (int)max<int64_t>(-1, min<int64_t>(p.Skv, reach)) : p.Skv;
+    int thr = lim - (k0 + 4 * lg);
+    // keep the per-element compares next to their use (hoisted, they pin one
+    // scalar register pair per score across the MFMA block)
+    asm volatile("" : "+v"(thr));
+#pragma unroll
+    for (int kb2 = 0; kb2 < NK; ++kb2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (kb2 * 32 + 8 * (i >> 2) + (i & 3) >= thr) S[kb2][i] = neg_inf();
+    return;
+  }
   const int32_t* kvp = p.kv_pos ? p.kv_pos + (int64_t)b * p.kvm_stride_b : nullptr;
   const int32_t* kvs = p.kv_seg ? p.kv_seg + (int64_t)b * p.kvm_stride_b : nullptr;
+  int key0 = k0 + 4 * lg;
+  asm volatile("" : "+v"(key0));   // as above: no hoisting of the compares
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
+  for (int kb2 = 0; kb2 < NK; ++kb2) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = k0 + kb2 * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
+      const int key = key0 + kb2 * 32 + 8 * (i >> 2) + (i & 3);
       bool ok = key < p.Skv;
       if (ok && p.causal) {
         const int kp = kvp ? kvp[key] : p.kv_pos_base + key;
@@ -81,19 +99,23 @@ __device__ __forceinline__ float capped_log2(float s, float k2, float cap_log2) 
   return cap_log2 * t;
 }
 
-// Online-softmax step on the 32 scores a lane holds. Returns nothing; updates
-// m_ref / l_acc / O and leaves the weights in S.
-template <int NDB, bool CAP>
-__device__ __forceinline__ void softmax_step(f32x16 (&S)[2], f32x16 (&O)[NDB], float& m_ref,
+// Online-softmax step on the NK*16 scores a lane holds. Updates m_ref / l_acc
+// / O and leaves the weights in S.
+template <int NDB, bool CAP, int NK>
+__device__ __forceinline__ void softmax_step(f32x16 (&S)[NK], f32x16 (&O)[NDB], float& m_ref,
                                              float& l_acc, const AttnParams& p) {
-  // row max: a tree over the 32 scores (short dependency chains)
-  float t[8];
+  constexpr int NG = NK * 4;
+  // row max: a tree over the scores (short dependency chains)
+  float t[NG];
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
+  for (int u = 0; u < NG; ++u)
     t[u] = fmaxf(fmaxf(S[u >> 2][(u & 3) * 4 + 0], S[u >> 2][(u & 3) * 4 + 1]),
                  fmaxf(S[u >> 2][(u & 3) * 4 + 2], S[u >> 2][(u & 3) * 4 + 3]));
-  float mx = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
-  mx = pair_max(mx);
+#pragma unroll
+  for (int w = NG / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int u = 0; u < w; ++u) t[u] = fmaxf(t[u], t[u + w]);
+  const float mx = pair_max(t[0]);
   const float umax = CAP ? mx : mx * p.scale_log2;
   const bool need = umax > m_ref + kRescaleThreshold;
   if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -108,16 +130,20 @@ __device__ __forceinline__ void softmax_step(f32x16 (&S)[2], f32x16 (&O)[NDB], f
   }
   const float msub = (m_ref == neg_inf()) ? 0.0f : m_ref;
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
+  for (int kb2 = 0; kb2 < NK; ++kb2)
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       S[kb2][i] = CAP ? fast_exp2(S[kb2][i] - msub) : fast_exp2(__builtin_fmaf(S[kb2][i], p.scale_log2, -msub));
   // row sum: a tree as well
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
+  for (int u = 0; u < NG; ++u)
     t[u] = (S[u >> 2][(u & 3) * 4 + 0] + S[u >> 2][(u & 3) * 4 + 1]) +
            (S[u >> 2][(u & 3) * 4 + 2] + S[u >> 2][(u & 3) * 4 + 3]);
-  l_acc += ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+#pragma unroll
+  for (int w = NG / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int u = 0; u < w; ++u) t[u] += t[u + w];
+  l_acc += t[0];
 }
 
 // Epilogue: normalise, then write (mode 0) or merge into (mode 1) the running state.
@@ -175,8 +201,14 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource over [base, base + bytes): loads at offsets >= bytes return
 // zero (raw buffer, stride 0; 0x00020000 is the gfx9 word-3 default format).
+// `base` and `bytes` must be wave-uniform; they are read from the first lane
+// so that the resource stays in scalar registers.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), 0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 __device__ __forceinline__ uint4 buffer_load_16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);

@@ -237,6 +237,205 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
   epilogue<NDB>(O, m_ref, l_acc, p, b, h, q_row, lg);
 }
 
+// ------------------------------------------------------------------------------ bf16, D = 128, LDS DMA
+// The 4-wave kernel with its K / V tiles moved by the LDS DMA path
+// (buffer_load_dwordx4 ... lds): no staging registers, no LDS stores in the
+// instruction stream. The DMA writes 1 KB per instruction at consecutive
+// addresses, so tiles are dense 256-byte rows whose 16-byte chunks are XOR
+// swizzled (chunk ^ (row & 15) for K, chunk ^ 4*(row & 3) for V) to keep the
+// operand reads free of bank conflicts. Rows past Skv read as zero.
+constexpr int kDmaTile = kBlockKV * 128;   // one K or V tile (elements)
+
+template <bool CAP>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_dma(AttnParams p) {
+  constexpr int D = 128;
+  constexpr int BK = kBlockKV;
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * kDmaTile];   // [stage][K, V]
+
+  int b, h, qb;
+  if (!decode_work(p, b, h, qb)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, lg = lane >> 5;
+  const int G = p.H / p.Hkv;
+  const int g = h / G;
+  const int q_row = qb * kBlockQ + w * 32 + ln;
+  const bool q_ok = q_row < p.Sq;
+
+  const int64_t mrow = (int64_t)b * p.nQb + qb;
+  const int cnt = p.row_cnt[mrow];
+  if (cnt == 0 && p.mode == 1 && p.sinks == nullptr) return;
+  const auto cols = as_const_space(p.col_idx + mrow * p.nKb);
+  const auto cls = as_const_space(p.tile_class + mrow * p.nKb);
+
+  bf16x8 qf[NDS];
+  {
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b +
+                         ((int64_t)(q_ok ? q_row : 0) * p.H + h) * D;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      bf16x8 t = *reinterpret_cast<const bf16x8*>(qrow + ds * 16 + lg * 8);
+      qf[ds] = q_ok ? t : bf16x8{};
+    }
+  }
+  const int qrow_c = q_ok ? q_row : p.Sq - 1;
+  const int qpos = p.q_pos ? p.q_pos[(int64_t)b * p.qm_stride_b + qrow_c] : p.q_pos_base + q_row;
+  const int qseg = p.q_seg ? p.q_seg[(int64_t)b * p.qm_stride_b + qrow_c] : 0;
+
+  float m_ref = neg_inf(), l_acc = 0.0f;
+  if (p.sinks) {
+    m_ref = p.sinks[h] * kLog2e;
+    l_acc = (lg == 0) ? 1.0f : 0.0f;
+  }
+  f32x16 O[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) O[db] = f32x16{};
+
+  const int64_t krs = (int64_t)p.Hkv * D;
+  const uint32_t row_bytes = (uint32_t)krs * 2;
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.kv_stride_b + g * D;
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.kv_stride_b + g * D;
+
+  // DMA: wave w fills tile rows [16w, 16w+16) in four 4-row slabs; lane l of
+  // slab i writes physical chunk l & 15 of row 16w + 4i + (l >> 4).
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * i + (lane >> 4);
+    const int phys = lane & 15;
+    koff[i] = (uint32_t)r * row_bytes + (phys ^ (r & 15)) * 16;
+    voff[i] = (uint32_t)r * row_bytes + (phys ^ (4 * (r & 3))) * 16;
+  }
+  auto dma = [&](int kb, int buf) {
+    const int k0 = kb * BK;
+    const uint32_t bytes = (uint32_t)min(p.Skv - k0, BK) * row_bytes;
+    const auto kr = tile_rsrc(kbase + (int64_t)k0 * krs, bytes);
+    const auto vr = tile_rsrc(vbase + (int64_t)k0 * krs, bytes);
+    __bf16* Ks = smem + buf * 2 * kDmaTile;
+    __bf16* Vs = Ks + kDmaTile;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(Ks + (16 * w + 4 * i) * D),
+                                               16, koff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(Vs + (16 * w + 4 * i) * D),
+                                               16, voff[i], 0, 0, 0);
+    }
+  };
+  // Operand offsets (bytes) inside a tile.
+  int k_off[2][NDS];                // K: row kb2*32 + ln, logical chunk 2*ds + lg
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) k_off[kb2][ds] = (kb2 * 32 + ln) * 256 + (((2 * ds + lg) ^ (ln & 15)) * 16);
+  // V (transposing reads): row ks*16 + 8*half + 4*lg + r4, column db*32 + 16*hs + 4*(lane&3)
+  const int r4 = (lane & 15) >> 2, hs = (lane >> 4) & 1;
+  const int v_row = 4 * lg + r4;
+  int v_col[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    v_col[db] = (((db * 4 + 2 * hs + ((lane & 3) >> 1)) ^ (4 * r4)) * 16) + (lane & 1) * 8;
+
+  if (p.Skv % BK) {
+    // a ragged last tile leaves rows unwritten: start from zeros so that those
+    // rows (masked, weight 0) hold finite values
+    for (int i = tid; i < 2 * 2 * kDmaTile / 8; i += kThreads)
+      reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  }
+
+  auto needs_mask = [&](int kb) { return cls[kb] != 2 || (kb + 1) * BK > p.Skv; };
+  int kb_cur = cnt > 0 ? cols[0] : 0;
+  int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
+  bool mk_cur = needs_mask(kb_cur);
+  if (cnt > 0) dma(kb_cur, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int it = 0; it < cnt; ++it) {
+    const int kb = kb_cur;
+    const bool need_mask = mk_cur;
+    const int buf = it & 1;
+    const bool has_next = it + 1 < cnt;
+    if (has_next) dma(kb_nxt, buf ^ 1);   // the stage tile it-1 used: every wave has passed it
+    const char* Kt = reinterpret_cast<const char*>(smem + buf * 2 * kDmaTile);
+    const char* Vt = Kt + kDmaTile * 2;
+
+    // All K operands are requested before the first MFMA (the scheduler would
+    // otherwise issue them one or two MFMAs ahead and wait on each).
+    bf16x8 kf[NDS][2];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) kf[ds][kb2] = *reinterpret_cast<const bf16x8*>(Kt + k_off[kb2][ds]);
+    f32x16 S[2];
+    S[0] = f32x16{};
+    S[1] = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) S[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][kb2], qf[ds], S[kb2], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // The first half of the V operands load while the softmax runs.
+    constexpr int NVF = 4 * NDB;   // V operands (ks, db) = (f / NDB, f % NDB)
+    bf16x8 vf[NVF];
+    auto vread = [&](int f) {
+      const char* vp = Vt + ((f / NDB) * 16 + v_row) * 256 + v_col[f % NDB];
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp + 8 * 256));
+      vf[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+#pragma unroll
+    for (int f = 0; f < NVF / 2; ++f) vread(f);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (CAP) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
+    }
+    if (need_mask) apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
+    softmax_step<NDB, CAP>(S, O, m_ref, l_acc, p);
+
+    bf16x8 P[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x2 two = {S[ks >> 1][(ks & 1) * 8 + 2 * j], S[ks >> 1][(ks & 1) * 8 + 2 * j + 1]};
+        bf16x2 pk = __builtin_convertvector(two, bf16x2);
+        P[ks][2 * j] = pk[0];
+        P[ks][2 * j + 1] = pk[1];
+      }
+    }
+#pragma unroll
+    for (int f = NVF / 2; f < NVF; ++f) vread(f);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int f = 0; f < NVF; ++f) O[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], P[f / NDB], O[f % NDB], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // List entries for the next iterations. These scalar loads share the wait
+    // counter of LDS reads but complete out of order; issued here, no LDS wait
+    // above has to cover them.
+    const int kb_nn = cols[min(it + 2, cnt - 1)];
+    const bool mk_nxt = needs_mask(kb_nxt);
+    // the next tile's DMA must have landed before any wave reads it
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    kb_cur = kb_nxt;
+    kb_nxt = kb_nn;
+    mk_cur = mk_nxt;
+  }
+  epilogue<NDB>(O, m_ref, l_acc, p, b, h, q_row, lg);
+}
+
 // ------------------------------------------------------------------------------ fp32
 // Same structure with v_mfma_f32_32x32x2_f32: one fp32 per lane per operand,
 // K and V kept row-major in LDS, the fp32 weights feed PV directly.
@@ -389,20 +588,23 @@ hipError_t launch(K kernel, const AttnParams& p, hipStream_t s) {
 
 }  // namespace
 
-// Kernel choice for bf16. The 4-wave kernel is the default. The other layouts
-// are kept as measured alternatives, all checked against the oracle; on the
-// 32k causal D=128 workload they ran at or below the default:
+// Kernel choice for bf16. The 4-wave kernel is the default (for D = 128 with
+// its tiles moved by LDS DMA; `staged` forces the register-staged version).
+// The other layouts are kept as measured alternatives, all checked against
+// the oracle; on the 32k causal D=128 workload they ran below the default:
 //   pingpong  8 waves in two groups taking turns at the matrix cores
-//   wide      4 waves, 64 query rows per wave (halves LDS reads per MFMA)
+//   wide      4 waves, 64 query rows per wave (halves LDS reads per MFMA),
+//             softmax interleaved with MFMAs; no position / segment arrays
 //   g8        8 waves, 32 rows each, 3-stage K/V ring filled by LDS DMA
 //   g8p       g8 with each wave's softmax interleaved between its MFMAs
 // RAM_ATTN_KERNEL=<name> forces one (D = 128 only, except pingpong).
 static int attn_variant(const AttnParams& p) {
   const char* e = getenv("RAM_ATTN_KERNEL");
   if (e && strcmp(e, "pingpong") == 0) return 1;
-  if (e && strcmp(e, "wide") == 0 && p.D == 128) return 2;
+  if (e && strcmp(e, "wide") == 0 && p.D == 128 && !p.kv_pos && !p.kv_seg) return 2;
   if (e && strcmp(e, "g8") == 0 && p.D == 128) return 3;
   if (e && strcmp(e, "g8p") == 0 && p.D == 128) return 4;
+  if (e && strcmp(e, "staged") == 0) return 5;
   return 0;
 }
 
@@ -414,7 +616,10 @@ hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s) {
   if (variant == 3) return launch_attn_g8(p, s);
   if (variant == 4) return launch_attn_g8p(p, s);
   if (dtype == 1) {
-    if (p.D == 128) return cap ? launch(attn_fwd_bf16<128, true>, p, s) : launch(attn_fwd_bf16<128, false>, p, s);
+    if (p.D == 128) {
+      if (variant == 5) return cap ? launch(attn_fwd_bf16<128, true>, p, s) : launch(attn_fwd_bf16<128, false>, p, s);
+      return cap ? launch(attn_fwd_bf16_dma<true>, p, s) : launch(attn_fwd_bf16_dma<false>, p, s);
+    }
     return cap ? launch(attn_fwd_bf16<64, true>, p, s) : launch(attn_fwd_bf16<64, false>, p, s);
   }
   if (p.D == 128) return cap ? launch(attn_fwd_f32<128, true>, p, s) : launch(attn_fwd_f32<128, false>, p, s);

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.fixture(params=["4wave", "pingpong", "wide", "g8", "g8p"])
+@pytest.fixture(params=["4wave", "staged", "pingpong", "wide", "g8", "g8p"])
 def variant(request, monkeypatch):
     """Force one of the bf16 attention kernel layouts (fp32 inputs always use the fp32 kernel)."""
     monkeypatch.setenv("RAM_ATTN_KERNEL", request.param)
