@@ -146,7 +146,19 @@ __device__ __forceinline__ void softmax_step(f32x16 (&S)[NK], f32x16 (&O)[NDB], 
   l_acc += t[0];
 }
 
-// Epilogue: normalise, then write (mode 0) or merge into (mode 1) the running state.
+// Four consecutive floats of a row as bf16, one 8-byte store.
+__device__ __forceinline__ void store_bf16x4(void* base, int64_t idx, float4 v) {
+  f32x2 lo = {v.x, v.y}, hi = {v.z, v.w};
+  const bf16x2 a = __builtin_convertvector(lo, bf16x2), c = __builtin_convertvector(hi, bf16x2);
+  uint2 u;
+  u.x = __builtin_bit_cast(uint32_t, a);
+  u.y = __builtin_bit_cast(uint32_t, c);
+  *reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(base) + idx) = u;
+}
+
+// Epilogue: normalise, then write (mode 0) or merge into (mode 1) the running
+// state. With p.out_final set the result goes there as bf16 instead of back
+// into p.out (rows this chunk does not reach are converted unchanged).
 template <int NDB>
 __device__ __forceinline__ void epilogue(const f32x16 (&O)[NDB], float m_ref, float l_acc,
                                          const AttnParams& p, int b, int h, int q_row, int lg) {
@@ -155,7 +167,8 @@ __device__ __forceinline__ void epilogue(const f32x16 (&O)[NDB], float m_ref, fl
   if (q_row >= p.Sq) return;
   const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
   const float lse_c = l_row > 0.0f ? (m_ref + log2f(l_row)) * kLn2 : neg_inf();
-  float* orow = p.out + (((int64_t)b * p.Sq + q_row) * p.H + h) * D;
+  const int64_t row0 = (((int64_t)b * p.Sq + q_row) * p.H + h) * D;
+  float* orow = p.out + row0;
   float* lptr = p.lse + ((int64_t)b * p.H + h) * p.Sq + q_row;
   if (p.mode == 0) {
 #pragma unroll
@@ -167,13 +180,26 @@ __device__ __forceinline__ void epilogue(const f32x16 (&O)[NDB], float m_ref, fl
         o.y = O[db][4 * i4 + 1] * inv;
         o.z = O[db][4 * i4 + 2] * inv;
         o.w = O[db][4 * i4 + 3] * inv;
-        *reinterpret_cast<float4*>(orow + db * 32 + 8 * i4 + 4 * lg) = o;
+        const int col = db * 32 + 8 * i4 + 4 * lg;
+        if (p.out_final) store_bf16x4(p.out_final, row0 + col, o);
+        else *reinterpret_cast<float4*>(orow + col) = o;
       }
     if (lg == 0) *lptr = lse_c;
     return;
   }
   // merge (ring-splash _update_out_and_lse)
-  if (lse_c == neg_inf()) return;  // nothing attended in this chunk: identity
+  if (lse_c == neg_inf()) {   // nothing attended in this chunk: identity
+    if (p.out_final) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int col = db * 32 + 8 * i4 + 4 * lg;
+          store_bf16x4(p.out_final, row0 + col, *reinterpret_cast<const float4*>(orow + col));
+        }
+    }
+    return;
+  }
   const float acc_lse = *lptr;
   float sig = 1.0f, new_lse = lse_c;
   if (acc_lse != neg_inf()) {
@@ -185,14 +211,16 @@ __device__ __forceinline__ void epilogue(const f32x16 (&O)[NDB], float m_ref, fl
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      float4* ptr = reinterpret_cast<float4*>(orow + db * 32 + 8 * i4 + 4 * lg);
+      const int col = db * 32 + 8 * i4 + 4 * lg;
+      float4* ptr = reinterpret_cast<float4*>(orow + col);
       float4 a = (acc_lse == neg_inf()) ? make_float4(0.f, 0.f, 0.f, 0.f) : *ptr;
       float4 o;
       o.x = a.x - sig * (a.x - O[db][4 * i4 + 0] * inv);
       o.y = a.y - sig * (a.y - O[db][4 * i4 + 1] * inv);
       o.z = a.z - sig * (a.z - O[db][4 * i4 + 2] * inv);
       o.w = a.w - sig * (a.w - O[db][4 * i4 + 3] * inv);
-      *ptr = o;
+      if (p.out_final) store_bf16x4(p.out_final, row0 + col, o);
+      else *ptr = o;
     }
   if (lg == 0) *lptr = new_lse;
 }

@@ -89,7 +89,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
 
   const int64_t mrow = (int64_t)b * p.nQb + qb;
   const int cnt = p.row_cnt[mrow];
-  if (cnt == 0 && p.mode == 1 && p.sinks == nullptr) return;
+  // a merge with nothing to add is the identity (unless the result must be
+  // converted to its final type, which the epilogue does for empty rows)
+  if (cnt == 0 && p.mode == 1 && p.sinks == nullptr && p.out_final == nullptr) return;
   const auto cols = as_const_space(p.col_idx + mrow * p.nKb);
   const auto cls = as_const_space(p.tile_class + mrow * p.nKb);
 
@@ -267,7 +269,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_dma(AttnParams p) {
 
   const int64_t mrow = (int64_t)b * p.nQb + qb;
   const int cnt = p.row_cnt[mrow];
-  if (cnt == 0 && p.mode == 1 && p.sinks == nullptr) return;
+  // a merge with nothing to add is the identity (unless the result must be
+  // converted to its final type, which the epilogue does for empty rows)
+  if (cnt == 0 && p.mode == 1 && p.sinks == nullptr && p.out_final == nullptr) return;
   const auto cols = as_const_space(p.col_idx + mrow * p.nKb);
   const auto cls = as_const_space(p.tile_class + mrow * p.nKb);
 
@@ -606,6 +610,12 @@ static int attn_variant(const AttnParams& p) {
   if (e && strcmp(e, "g8p") == 0 && p.D == 128) return 4;
   if (e && strcmp(e, "staged") == 0) return 5;
   return 0;
+}
+
+bool attn_writes_final(const AttnParams& p, int dtype) {
+  if (dtype != 1) return false;
+  const int v = attn_variant(p);
+  return v == 0 || v == 5;
 }
 
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s) {

@@ -361,6 +361,7 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   if (e != hipSuccess) return hip_fail(e, "ring block mask launch");
 
   const int64_t esz = desc->dtype == RAM_BF16 ? 2 : 4;
+  bool final_fused = false;
   for (int t = 0; t < n_chunks; ++t) {
     const int c = q_shard >= 0 ? ((q_shard - t) % n_chunks + n_chunks) % n_chunks : t;
     ram_attn_desc dc = *desc;
@@ -378,10 +379,15 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
     const char* vc = static_cast<const char*>(v_all) + (int64_t)c * desc->Skv * desc->Hkv * desc->D * esz;
     ram::AttnParams p = attn_params(&dc, q, kc, vc, &sc, &bc, t == 0 ? sinks : nullptr,
                                     t == 0 ? RAM_OUT_WRITE : RAM_OUT_MERGE, acc, lse);
+    // the last visit writes the bf16 result itself when its kernel can
+    if (t == n_chunks - 1 && desc->dtype == RAM_BF16 && ram::attn_writes_final(p, desc->dtype)) {
+      p.out_final = out;
+      final_fused = true;
+    }
     e = ram::launch_attn(p, desc->dtype, stream);
     if (e != hipSuccess) return hip_fail(e, "ring chunk launch");
   }
-  if (desc->dtype == RAM_BF16) {
+  if (desc->dtype == RAM_BF16 && !final_fused) {
     e = ram::launch_cast_bf16(acc, out, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
     if (e != hipSuccess) return hip_fail(e, "final cast launch");
   }

@@ -19,6 +19,8 @@ struct AttnParams {
   const void* k;
   const void* v;
   float* out;         // float32 [B,Sq,H,D], dense
+  void* out_final;    // bf16 [B,Sq,H,D] or null: when set, the final result goes
+                      // here in bf16 (the last chunk of a ring) and `out` is only read
   float* lse;         // float32 [B,H,Sq], dense
   const float* sinks; // [H] or null
   const uint8_t* tile_class;
@@ -57,6 +59,8 @@ struct MaskParams {
 };
 
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s);
+// Whether the kernel launch_attn would pick for p honours p.out_final.
+bool attn_writes_final(const AttnParams& p, int dtype);
 hipError_t launch_attn_pp(const AttnParams& p, hipStream_t s);   // bf16, 8-wave ping-pong
 hipError_t launch_attn_w64(const AttnParams& p, hipStream_t s);  // bf16, D = 128, 64 rows per wave
 hipError_t launch_attn_g8(const AttnParams& p, hipStream_t s);   // bf16, D = 128, 8 waves, 3-stage DMA
