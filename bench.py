@@ -2,8 +2,9 @@
 """Throughput of the chunked (ring) attention forward on one MI355X.
 
 A step is one ring_attn_fwd_1gpu call over one batch of synthetic input: the
-block-mask build of every chunk, eight chunk launches of the attention kernel
-(the first writes, the rest merge by LSE) and the final cast. The workload is
+block-mask build of every chunk and eight chunk launches of the attention
+kernel (the first writes, the rest merge by LSE, the last also writes the bf16
+result). The workload is
 long-context causal attention: B=1, H=32 query heads over Hkv=8 KV heads,
 32768 queries, 32768 keys in 8 sequential chunks of 4096, D=128, bf16 q, k
 ~ N(0,1) and v ~ U(-1,1). Inputs are resident in HBM before timing starts.
@@ -38,7 +39,7 @@ from ring_attention_merge_amd import workloads as wl  # noqa: E402
 METRIC = "effective attention fwd TFLOP/s (unmasked tiles) and % bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 REF_TILE = 128                  # fixed reference tiling for effective FLOPs
-ATTN_KERNEL = "attn_fwd_bf16<128, false>"
+ATTN_KERNEL = "attn_fwd_bf16_dma<false>"
 
 
 def log(*a):
@@ -82,16 +83,21 @@ def tile_counts(w, desc, dev, tile_q, tile_kv):
     return counts
 
 
+KERNEL_SOURCES = ("attn_fwd.hip", "attn_common.h")   # what the default chunk kernel is built from
+
+
 def kernel_source_hash() -> str:
     import hashlib
-    path = os.path.join(ROOT, "ring_attention_merge_amd", "csrc", "attn_fwd.hip")
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "ring_attention_merge_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def recorded_traffic(workload: str):
     """HBM bytes per chunk launch from the committed counter summary, if it was taken
     on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_bf16_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_bf16_dma_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
