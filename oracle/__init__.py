@@ -6,10 +6,11 @@ library and its Python binding) never calls it and shares no code with it.
 
 Contents:
   attention.attention    plain masked softmax attention, full score matrix
-  attention.allowed      the element mask from positions and segment IDs
+  attention.allowed      the element mask from positions, segment IDs and a dense mask
   attention.merge        the sigmoid/softplus LSE merge
   attention.chunked      attention per KV chunk folded with ``merge``
   blockmask.block_mask   tile classes and compacted non-empty tile lists
+  blockmask.partial_bits the element mask of each PARTIAL tile as bits
 
 Every function is pinned by tests under ``tests/test_oracle_*.py`` against
 closed forms, library routines, brute force and invariants; the soft-cap
@@ -17,7 +18,7 @@ formula itself is a reading (the pages give only the parameter), pinned to its
 closed form and its large-cap limit, but not to any value on the pages.
 """
 from .attention import allowed, attention, merge, chunked, DEFAULT_MASK_VALUE, PAD_SEGMENT_ID
-from .blockmask import block_mask, TILE_EMPTY, TILE_PARTIAL, TILE_FULL
+from .blockmask import block_mask, partial_bits, TILE_EMPTY, TILE_PARTIAL, TILE_FULL
 
-__all__ = ["allowed", "attention", "merge", "chunked", "block_mask", "DEFAULT_MASK_VALUE",
+__all__ = ["allowed", "attention", "merge", "chunked", "block_mask", "partial_bits", "DEFAULT_MASK_VALUE",
            "PAD_SEGMENT_ID", "TILE_EMPTY", "TILE_PARTIAL", "TILE_FULL"]

@@ -11,6 +11,9 @@ Sources (the pages):
   [kvax]  "Kvax: Flash Attention for JAX" page: flash_attention and
           create_attention_mask arguments ([B,S,H,D] layouts, positions and
           segment IDs, padding segment, scale).
+  [make]  the ring-splash page's make_ring_attention: a two-dimensional
+          boolean mask over (query, key) given by the caller, turned into the
+          block mask and partial-block contents of MaskInfo.
 
 The method reaches, up to rounding order, ordinary masked softmax attention
 over the full key set, so ``attention`` is that definition written out: it
@@ -22,6 +25,14 @@ softmax. Readings of points the pages leave open (see the project design notes):
     gives out = 0 and lse = -inf (lse = sink with a sink);
   * the soft cap is cap * tanh(s / cap) on the scaled logit s = scale * q.k;
   * causal means kv_pos <= q_pos; segments must be equal and not padding;
+  * a dense mask is one [Sq, Skv] boolean array shared by every batch row and
+    head; a pair takes part only if the dense mask, the causal test and the
+    segment test all allow it (the pages' ring uses the dense mask on its
+    non-causal path, where it and the segment IDs both apply);
+  * in the chunked fold, chunk c reads the dense mask's columns from a start
+    column of its own: the chunk's first key for one mask over the whole KV,
+    or 0 for every chunk to reuse one local mask at each step (what the
+    pages' non-causal ring does with its fixed mask info);
   * query head h reads KV head h // (H / Hkv);
   * lse is the natural log, laid out [B, H, Sq].
 """
@@ -35,17 +46,24 @@ DEFAULT_MASK_VALUE = -2.381976426469702e38
 PAD_SEGMENT_ID = -1
 
 
-def allowed(q_pos, kv_pos, q_seg=None, kv_seg=None, causal=True):
+def allowed(q_pos, kv_pos, q_seg=None, kv_seg=None, causal=True, dense=None):
     """Element mask for one batch row: [Sq, Skv] bool.
 
     [ring] _ring_attention_forward: the causal mask keeps a key when the query
     id is >= the key id, ids being positions shifted by the ring offsets.
     [kvax] flash_attention: tokens attend within their own segment; padding
     tokens carry the padding segment ID and take part in nothing.
+    [make] make_ring_attention: ``dense`` [Sq, Skv] (nonzero = allowed) is
+    the caller's two-dimensional mask; it further restricts the pairs.
     """
     q_pos = np.asarray(q_pos)
     kv_pos = np.asarray(kv_pos)
     ok = np.ones((q_pos.shape[0], kv_pos.shape[0]), dtype=bool)
+    if dense is not None:
+        dense = np.asarray(dense)
+        if dense.shape != ok.shape:
+            raise ValueError(f"dense mask of shape {dense.shape}, expected {ok.shape}")
+        ok &= dense != 0
     if causal:
         ok &= kv_pos[None, :] <= q_pos[:, None]
     if q_seg is not None:
@@ -57,11 +75,12 @@ def allowed(q_pos, kv_pos, q_seg=None, kv_seg=None, causal=True):
 
 
 def attention(q, k, v, *, scale, q_pos, kv_pos, q_seg=None, kv_seg=None, causal=True,
-              softcap=None, sinks=None, rows=None, row_block=512):
+              softcap=None, sinks=None, dense=None, rows=None, row_block=512):
     """Masked softmax attention in float64 from the full score matrix.
 
     q [B,Sq,H,D], k and v [B,Skv,Hkv,D]; positions [B,Sq] / [B,Skv]; segment
-    IDs the same or None; sinks [H] or None. ``rows`` restricts the query rows
+    IDs the same or None; sinks [H] or None; ``dense`` [Sq, Skv] or None, one
+    mask for every batch row and head. ``rows`` restricts the query rows
     computed (for sampled checks). Returns out [B,R,H,D] and lse [B,H,R] in
     float64, R = Sq or len(rows).
 
@@ -88,7 +107,8 @@ def attention(q, k, v, *, scale, q_pos, kv_pos, q_seg=None, kv_seg=None, causal=
             r = row_idx[start:start + row_block]
             ok = allowed(np.asarray(q_pos)[b, r], np.asarray(kv_pos)[b],
                          None if q_seg is None else np.asarray(q_seg)[b, r],
-                         None if kv_seg is None else np.asarray(kv_seg)[b], causal)
+                         None if kv_seg is None else np.asarray(kv_seg)[b], causal,
+                         None if dense is None else np.asarray(dense)[r])
             for h in range(H):
                 g = h // G
                 s = scale * (q[b, r, h, :] @ k[b, :, g, :].T)
@@ -138,14 +158,16 @@ def merge(out, lse, block_out, block_lse):
 
 
 def chunked(q, k, v, *, scale, q_pos, kv_pos, bounds, order, q_seg=None, kv_seg=None,
-            causal=True, softcap=None, sinks=None, rows=None):
+            causal=True, softcap=None, sinks=None, dense=None, dense_col0=None, rows=None):
     """Attention per KV chunk, folded with ``merge`` in the given chunk order.
 
     [ring] _ring_attention_forward: the running state starts at out = 0,
     lse = -inf; each step attends to one KV chunk and merges it in; sinks
     enter only on the first step. ``bounds`` lists each chunk's [start, end)
     key range; ``order`` lists chunk indices in visiting order. Chunk segment
-    IDs and positions travel with their keys.
+    IDs and positions travel with their keys. With a ``dense`` mask [Sq, n],
+    chunk c reads its columns from ``dense_col0[c]`` on (default: the chunk's
+    first key, i.e. one mask over the whole KV).
     """
     q = np.asarray(q, np.float64)
     B, Sq, H, D = q.shape
@@ -154,10 +176,14 @@ def chunked(q, k, v, *, scale, q_pos, kv_pos, bounds, order, q_seg=None, kv_seg=
     acc_lse = np.full((B, H, R), -np.inf)
     for t, c in enumerate(order):
         a, e = bounds[c]
+        dense_c = None
+        if dense is not None:
+            c0 = a if dense_col0 is None else dense_col0[c]
+            dense_c = np.asarray(dense)[:, c0:c0 + (e - a)]
         o_c, l_c = attention(q, np.asarray(k)[:, a:e], np.asarray(v)[:, a:e], scale=scale,
                              q_pos=q_pos, kv_pos=np.asarray(kv_pos)[:, a:e], q_seg=q_seg,
                              kv_seg=None if kv_seg is None else np.asarray(kv_seg)[:, a:e],
-                             causal=causal, softcap=softcap,
+                             causal=causal, softcap=softcap, dense=dense_c,
                              sinks=sinks if t == 0 else None, rows=rows)
         acc, acc_lse = merge(acc, acc_lse, o_c, l_c)
     return acc, acc_lse

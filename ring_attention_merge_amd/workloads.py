@@ -116,6 +116,42 @@ def packed_documents(rng, B: int, S: int, len_lo: int, len_hi: int, pad_frac: fl
     return seg, pos, lengths
 
 
+def dense_mask(rng, Sq: int, Skv: int, *, q_offset: int = 0, window: int = 256, n_global: int = 64,
+               block: int = 128, p_block: float = 0.15, p_keep: float = 0.5, dead_rows: int = 3):
+    """A seeded two-dimensional mask (uint8 [Sq, Skv], 1 = allowed) with the structures
+    caller-given masks have: a band, global keys, random blocks and dead rows.
+
+    Query i sits at key coordinate q_offset + i. The mask is the union of
+      * a band: keys j with |q_offset + i - j| < window;
+      * global keys: j < n_global;
+      * random blocks: each (block x block) cell is picked with probability
+        p_block; a picked cell is either all ones or, with probability 1/2,
+        elements drawn independently with probability p_keep (cells are
+        aligned to ``block`` from (0, 0), so with a tile that divides
+        ``block`` they give whole FULL and ragged PARTIAL tiles);
+    then ``dead_rows`` randomly chosen rows are cleared (rows with no key).
+    Draw order: the cell picks, the all-ones / random choice per cell, the
+    element draws of the random cells (row-major), then the dead rows.
+    """
+    i = np.arange(Sq)[:, None] + q_offset
+    j = np.arange(Skv)[None, :]
+    m = np.abs(i - j) < window
+    m |= j < n_global
+    nbq, nbk = -(-Sq // block), -(-Skv // block)
+    pick = rng.random((nbq, nbk)) < p_block
+    rand_cell = rng.random((nbq, nbk)) < 0.5
+    for bi, bj in zip(*np.nonzero(pick)):
+        r0, c0 = bi * block, bj * block
+        r1, c1 = min(Sq, r0 + block), min(Skv, c0 + block)
+        if rand_cell[bi, bj]:
+            m[r0:r1, c0:c1] |= rng.random((r1 - r0, c1 - c0)) < p_keep
+        else:
+            m[r0:r1, c0:c1] = True
+    if dead_rows and Sq:
+        m[rng.choice(Sq, size=min(dead_rows, Sq), replace=False)] = False
+    return m.astype(np.uint8)
+
+
 def make(name: str, *, B: int, H: int, Hkv: int, Sq: int, chunk: int, n_chunks: int, D: int,
          dtype: str = "bf16", causal: bool = True, softcap: Optional[float] = None,
          with_sinks: bool = False, q_shard: int = -1, seed: int = 0,

@@ -1,7 +1,8 @@
 """Pins for the float64 oracle: checks against facts that do not come from the oracle.
 
 Each ``pin_*`` takes an oracle module ``ora`` (with ``attention``, ``allowed``,
-``merge``, ``chunked``, ``block_mask`` and the tile-class constants) and raises
+``merge``, ``chunked``, ``block_mask``, ``partial_bits`` and the tile-class
+constants) and raises
 AssertionError when the oracle disagrees with:
   * the constants the pages print (tests/golden/*.json),
   * closed forms (zero queries, single allowed key, constant values, merge as
@@ -11,7 +12,10 @@ AssertionError when the oracle disagrees with:
   * brute force with math.fsum on tiny inputs,
   * invariants (chunked + merge equals the whole KV in any split and order,
     GQA equals repeated KV heads, packed documents equal separate documents,
-    ring offsets equal one offset causal mask, a sink counts once).
+    ring offsets equal one offset causal mask, a sink counts once, a
+    lower-triangular dense mask equals the causal test, a block-diagonal one
+    equals segment IDs, a reused local mask equals the tiled global one),
+  * numpy's little-endian bit unpacking for the partial-tile bits.
 ``tests/test_oracle_pins.py`` runs them on the real oracle;
 ``tests/test_oracle_mutants.py`` runs them on broken copies and expects failures.
 """
@@ -432,6 +436,134 @@ def pin_block_mask(ora):
         assert np.array_equal(cls, _classes_by_reshape(ok, 32, 16)), f"segment classes {trial}"
 
 
+# ---------------------------------------------------------------------------- dense masks
+def _brute_dense(q, k, v, scale, dense, causal, qp, kp):
+    """Brute force with a dense mask shared by all batch rows (no cap, sinks or segments)."""
+    B, Sq, H, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    out = np.zeros((B, Sq, H, D))
+    lse = np.full((B, H, Sq), -math.inf)
+    for b in range(B):
+        for h in range(H):
+            g = (h * Hkv) // H
+            for i in range(Sq):
+                ws, js = [], []
+                for j in range(Skv):
+                    if not dense[i][j] or (causal and kp[b, j] > qp[b, i]):
+                        continue
+                    s = scale * math.fsum(float(q[b, i, h, d]) * float(k[b, j, g, d]) for d in range(D))
+                    ws.append(math.exp(s))
+                    js.append(j)
+                if not ws:
+                    continue
+                Z = math.fsum(ws)
+                lse[b, h, i] = math.log(Z)
+                for d in range(D):
+                    out[b, i, h, d] = math.fsum(w * float(v[b, j, g, d]) for w, j in zip(ws, js)) / Z
+    return out, lse
+
+
+def pin_dense_mask(ora):
+    rng = np.random.default_rng(23)
+    # brute force on tiny inputs, one mask for both batch rows, Sq != Skv
+    for trial in range(12):
+        B, Hkv = 2, int(rng.choice([1, 2]))
+        H = Hkv * int(rng.choice([1, 2]))
+        Sq, Skv, D = int(rng.integers(1, 9)), int(rng.integers(1, 11)), int(rng.integers(1, 6))
+        q, k, v, qp, kp, _, _ = _rand_problem(rng, B, Sq, Skv, H, Hkv, D, shuffle_pos=True)
+        dense = (rng.random((Sq, Skv)) < 0.6).astype(np.uint8) * int(rng.choice([1, 3]))
+        causal = bool(trial % 2)
+        o1, l1 = ora.attention(q, k, v, scale=0.45, q_pos=qp, kv_pos=kp, causal=causal, dense=dense)
+        o2, l2 = _brute_dense(q, k, v, 0.45, dense, causal, qp, kp)
+        _close(o1, o2, 1e-12, f"dense brute out {trial}"); _close(l1, l2, 1e-12, f"dense brute lse {trial}")
+    # a lower-triangular mask (numpy tri, offset by the q shift) equals the causal test
+    Sq, Skv, off = 37, 53, 16
+    q, k, v, _, _, _, _ = _rand_problem(rng, 1, Sq, Skv, 2, 1, 8)
+    qp, kp = (off + np.arange(Sq))[None], np.arange(Skv)[None]
+    tri = np.tri(Sq, Skv, k=off, dtype=bool)
+    o1, l1 = ora.attention(q, k, v, scale=0.3, q_pos=qp, kv_pos=kp, causal=False, dense=tri)
+    o2, l2 = ora.attention(q, k, v, scale=0.3, q_pos=qp, kv_pos=kp, causal=True)
+    _close(o1, o2, 0.0, "tri dense = causal"); _close(l1, l2, 0.0, "tri dense = causal lse")
+    # a block-diagonal mask (scipy block_diag of documents) equals segment IDs
+    import scipy.linalg
+    S = 90
+    seg, pos, lengths = wl.packed_documents(rng, 1, S, 7, 25, 0.1)
+    bd = scipy.linalg.block_diag(*[np.ones((L, L)) for L in lengths[0]])
+    dense = np.zeros((S, S)); dense[:bd.shape[0], :bd.shape[1]] = bd
+    q, k, v, _, _, _, _ = _rand_problem(rng, 1, S, S, 2, 2, 8)
+    o1, l1 = ora.attention(q, k, v, scale=0.3, q_pos=pos, kv_pos=pos, causal=False, dense=dense)
+    o2, l2 = ora.attention(q, k, v, scale=0.3, q_pos=pos, kv_pos=pos, q_seg=seg, kv_seg=seg, causal=False)
+    _close(o1, o2, 0.0, "block-diagonal = segments"); _close(l1, l2, 0.0, "block-diagonal = segments lse")
+    # dense AND causal AND segments: the intersection of the three element masks
+    o1, l1 = ora.attention(q, k, v, scale=0.3, q_pos=pos, kv_pos=pos, q_seg=seg, kv_seg=seg,
+                           causal=True, dense=np.tri(S, S, k=-2))
+    pos2 = np.arange(S)[None]
+    both = _mask_indep(pos[0], pos[0], seg[0], seg[0], True) & np.tri(S, S, k=-2, dtype=bool)
+    o2, l2 = ora.attention(q, k, v, scale=0.3, q_pos=pos2, kv_pos=pos2, causal=False, dense=both)
+    _close(o1, o2, 0.0, "intersection"); _close(l1, l2, 0.0, "intersection lse")
+    # a cleared row gives (0, -inf); with a sink, lse = sink
+    dense = np.ones((S, S), np.uint8); dense[5] = 0
+    sinks = np.array([0.5, -2.0])
+    o, l = ora.attention(q, k, v, scale=0.3, q_pos=pos2, kv_pos=pos2, dense=dense)
+    assert np.all(o[0, 5] == 0) and np.all(l[0, :, 5] == -np.inf)
+    o, l = ora.attention(q, k, v, scale=0.3, q_pos=pos2, kv_pos=pos2, dense=dense, sinks=sinks)
+    assert np.all(o[0, 5] == 0) and np.array_equal(l[0, :, 5], sinks)
+
+
+def pin_dense_chunked(ora):
+    rng = np.random.default_rng(24)
+    N, C, Sq, H, D = 4, 13, 21, 2, 8
+    q, k, v, _, _, _, _ = _rand_problem(rng, 1, Sq, N * C, H, H, D)
+    qp, kp = (3 * C + np.arange(Sq))[None], np.arange(N * C)[None]
+    bounds = [(c * C, (c + 1) * C) for c in range(N)]
+    for causal in (False, True):
+        # one mask over the whole KV: each chunk reads its own columns
+        dense = rng.random((Sq, N * C)) < 0.5
+        ref_o, ref_l = ora.attention(q, k, v, scale=0.3, q_pos=qp, kv_pos=kp, causal=causal, dense=dense)
+        for order in ([0, 1, 2, 3], [3, 2, 1, 0], [1, 3, 0, 2]):
+            o, l = ora.chunked(q, k, v, scale=0.3, q_pos=qp, kv_pos=kp, bounds=bounds, order=order,
+                               causal=causal, dense=dense)
+            _close(o, ref_o, 1e-12, f"global dense {order}"); _close(l, ref_l, 1e-12, f"global dense lse {order}")
+        # one local mask reused at every step equals that mask tiled along the keys
+        local = rng.random((Sq, C)) < 0.5
+        ref_o, ref_l = ora.attention(q, k, v, scale=0.3, q_pos=qp, kv_pos=kp, causal=causal,
+                                     dense=np.tile(local, (1, N)))
+        o, l = ora.chunked(q, k, v, scale=0.3, q_pos=qp, kv_pos=kp, bounds=bounds, order=[3, 2, 1, 0],
+                           causal=causal, dense=local, dense_col0=[0] * N)
+        _close(o, ref_o, 1e-12, "reused local dense"); _close(l, ref_l, 1e-12, "reused local dense lse")
+
+
+def pin_partial_bits(ora):
+    rng = np.random.default_rng(25)
+    for trial in range(16):
+        Sq, Skv = (int(x) for x in rng.integers(1, 160, size=2))
+        bq, bk = int(rng.choice([16, 32, 48])), int(rng.choice([16, 32, 48, 64, 100]))
+        ok = rng.random((Sq, Skv)) < rng.choice([0.05, 0.5, 0.97])
+        ok[: Sq // 3, : Skv // 3] = True                                   # some FULL tiles
+        ok[Sq // 2:, Skv // 2:] = False                                    # some EMPTY tiles
+        bits = ora.partial_bits(ok, bq, bk)
+        cls = _classes_by_reshape(ok, bq, bk)
+        nQb, nKb = cls.shape
+        W = -(-bk // 32)
+        assert bits.shape == (nQb, nKb, bq, W) and bits.dtype == np.uint32
+        # numpy's little-endian unpacking: bit j of the row is key j of the tile
+        unp = np.unpackbits(bits.astype("<u4").view(np.uint8), axis=-1, bitorder="little")
+        unp = unp.reshape(nQb, nKb, bq, W * 32).astype(bool)
+        padded = np.zeros((nQb * bq, nKb * bk), bool); padded[:Sq, :Skv] = ok
+        tiles = padded.reshape(nQb, bq, nKb, bk).transpose(0, 2, 1, 3)
+        part = cls == 1
+        assert part.any(), f"trial {trial} has no PARTIAL tile"
+        assert np.array_equal(unp[..., :bk][part], tiles[part]), f"partial bits {trial}"
+        assert not unp[..., bk:].any(), f"bits past the tile width {trial}"
+        assert not unp[~part].any(), f"bits on a non-PARTIAL tile {trial}"
+    # one allowed pair: exactly one word holds exactly one bit
+    ok = np.zeros((70, 90), bool); ok[37, 77] = True
+    bits = ora.partial_bits(ok, 32, 64)
+    want = np.zeros_like(bits); want[1, 1, 5, 0] = np.uint32(1 << 13)
+    assert np.array_equal(bits, want), "single pair bit"
+
+
 ALL_PINS = [pin_mask_value_constant, pin_finite_mask_equivalence, pin_bruteforce, pin_sdpa,
             pin_closed_forms, pin_softcap, pin_merge, pin_chunked_equals_full, pin_sink_once,
-            pin_gqa_repeat, pin_packed_docs, pin_ring_offsets, pin_block_mask]
+            pin_gqa_repeat, pin_packed_docs, pin_ring_offsets, pin_block_mask, pin_dense_mask,
+            pin_dense_chunked, pin_partial_bits]

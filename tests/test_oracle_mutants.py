@@ -30,11 +30,19 @@ ATTN_MUTANTS = {
     "merge_is_first_ignored": ("new_out = np.where(first4, block_out, new_out)", "pass"),
     "lse_log2": ("m_safe + np.log(np.where", "m_safe + np.log2(np.where"),
     "normaliser_off": ("o[nz] = num[nz] / z[nz, None]", "o[nz] = num[nz] / (z[nz, None] + 1e-3)"),
+    "dense_ignored": ("ok &= dense != 0", "pass"),
+    "dense_inverted": ("ok &= dense != 0", "ok &= dense == 0"),
+    "dense_col0_ignored": ("c0 = a if dense_col0 is None else dense_col0[c]", "c0 = a"),
+    "dense_from_first_column": ("c0 = a if dense_col0 is None else dense_col0[c]",
+                                "c0 = 0 if dense_col0 is None else dense_col0[c]"),
 }
 MASK_MUTANTS = {
     "no_empty_tiles": ("elif tile.any():", "elif True:"),
     "full_from_first_row": ("if tile.all():", "if tile[0].all():"),
     "col_idx_unsorted": ("col_idx[qb, :len(nz)] = nz", "col_idx[qb, :len(nz)] = nz[::-1]"),
+    "bits_msb_first": ("np.uint32(1 << (j % 32))", "np.uint32(1 << (31 - j % 32))"),
+    "bits_on_full_tiles": ("if cls[qb, kb] != TILE_PARTIAL:", "if cls[qb, kb] == TILE_EMPTY:"),
+    "bits_word_index": ("bits[qb, kb, i, j // 32]", "bits[qb, kb, i, j % W]"),
 }
 
 
@@ -58,7 +66,7 @@ def _mutant(which, key):
         m = _load(mask_path, "mut_blockmask", *MASK_MUTANTS[key])
     return types.SimpleNamespace(
         attention=a.attention, allowed=a.allowed, merge=a.merge, chunked=a.chunked,
-        DEFAULT_MASK_VALUE=a.DEFAULT_MASK_VALUE, block_mask=m.block_mask,
+        DEFAULT_MASK_VALUE=a.DEFAULT_MASK_VALUE, block_mask=m.block_mask, partial_bits=m.partial_bits,
         TILE_EMPTY=m.TILE_EMPTY, TILE_PARTIAL=m.TILE_PARTIAL, TILE_FULL=m.TILE_FULL)
 
 
