@@ -39,7 +39,7 @@ from ring_attention_merge_amd import workloads as wl  # noqa: E402
 METRIC = "effective attention fwd TFLOP/s (unmasked tiles) and % bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 REF_TILE = 128                  # fixed reference tiling for effective FLOPs
-ATTN_KERNEL = "attn_fwd_bf16_dma<false>"
+ATTN_KERNEL = "attn_fwd_bf16_dma<false, false>"
 
 
 def log(*a):

@@ -8,7 +8,9 @@
  * running (out, lse) with the sigmoid/softplus merge of _update_out_and_lse.
  * The Kvax page ("Kvax: Flash Attention for JAX", flash_attention and
  * create_attention_mask) fixes the tensor layouts and the position /
- * segment-ID masking. On one GPU the ring is a sequential loop over chunks.
+ * segment-ID masking; the ring-splash page's make_ring_attention adds a
+ * caller-given two-dimensional mask. On one GPU the ring is a sequential
+ * loop over chunks.
  *
  * Conventions shared by every call:
  *  - Tensor pointers are DEVICE pointers, allocated and owned by the caller.
@@ -27,7 +29,8 @@
  *    is MQA).
  *  - Scores: s = scale * q.k; with softcap > 0, s = softcap * tanh(s / softcap).
  *    A pair (i, j) takes part iff (!causal || kv_pos[j] <= q_pos[i]) and,
- *    with segment IDs, q_seg[i] == kv_seg[j] != RAM_PAD_SEGMENT_ID. Excluded
+ *    with segment IDs, q_seg[i] == kv_seg[j] != RAM_PAD_SEGMENT_ID and, with
+ *    a dense mask, its byte for (i, j) is nonzero. Excluded
  *    pairs get weight exactly 0 (the pages' finite mask value gives the same
  *    result on every row that attends to at least one key).
  *  - A sink (float32 [H], raw logit, neither scaled nor capped) adds
@@ -76,9 +79,20 @@ typedef struct {
   int32_t block_q, block_kv;     /* tile of the block mask; attention needs ram_kernel_tile() */
 } ram_attn_desc;
 
-/* Positions and segment IDs for one (q, KV-chunk) pair (Kvax flash_attention
- * arguments). A NULL position array means sequential positions base + index.
- * Segment arrays are both NULL (no segment masking) or both set. */
+/* Positions, segment IDs and an optional dense mask for one (q, KV-chunk)
+ * pair (Kvax flash_attention arguments; the two-dimensional mask of the
+ * ring-splash make_ring_attention). A NULL position array means sequential
+ * positions base + index. Segment arrays are both NULL (no segment masking)
+ * or both set.
+ *
+ * Dense mask: uint8 [Sq, dense_ld], row i for query row i of this call, one
+ * mask for every batch row and head; nonzero allows the pair. Key j of a
+ * single-chunk call reads column j. In ring_attn_fwd_1gpu key j of chunk c
+ * reads column c * dense_chunk_step + j: dense_chunk_step = Skv gives one mask
+ * over all n_chunks*Skv keys, 0 reuses one [Sq, Skv] mask for every chunk (the
+ * non-causal ring of the ring-splash page keeps one mask info for all steps).
+ * dense_ld 0 means the columns the call reads: Skv, or Skv + (n_chunks - 1) *
+ * dense_chunk_step in the ring. A dense mask needs tile bits (ram_block_mask). */
 typedef struct {
   const int32_t* q_pos;   /* [B, Sq] or NULL => q_pos_base + i */
   const int32_t* kv_pos;  /* [B, Skv] or NULL => kv_pos_base + j */
@@ -87,6 +101,9 @@ typedef struct {
   const int32_t* kv_seg;  /* [B, Skv] or NULL */
   int64_t q_meta_stride_b;  /* elements between batches of q_pos/q_seg; 0 = Sq */
   int64_t kv_meta_stride_b; /* elements between batches of kv_pos/kv_seg; 0 = Skv */
+  const uint8_t* dense;     /* [Sq, dense_ld] or NULL */
+  int64_t dense_ld;         /* bytes between dense rows; 0 = the columns the call reads */
+  int64_t dense_chunk_step; /* ring only: dense columns per chunk index, >= 0 */
 } ram_mask_src;
 
 /* Block mask of one (q, KV-chunk) pair at tile (block_q, block_kv), with
@@ -95,24 +112,33 @@ typedef struct {
  *              the sequence ends do not count;
  *   row_cnt    int32 [B, nQb]: number of non-EMPTY tiles in the tile row;
  *   col_idx    int32 [B, nQb, nKb]: the row's non-EMPTY kv-tile indices in
- *              ascending order, then -1 in the remaining slots. */
+ *              ascending order, then -1 in the remaining slots;
+ *   bits       uint32 [B, nQb, nKb, block_q, ceil(block_kv/32)] or NULL: the
+ *              element mask of each PARTIAL tile (MaskInfo partial_mask_blocks
+ *              of the ring-splash page), one row of words per query row, key
+ *              j of the tile at bit j % 32 of word j / 32, 0 past the
+ *              sequence ends. Only PARTIAL tiles are written; the words of
+ *              other tiles are left as they were. 8-byte aligned. */
 typedef struct {
   uint8_t* tile_class;
   int32_t* row_cnt;
   int32_t* col_idx;
+  uint32_t* bits;
 } ram_block_mask;
 
-/* Tile classes and compacted non-empty tile lists from positions and segment
- * IDs (Kvax create_attention_mask; ring-splash MaskInfo block_mask and the
- * lists of blocks to visit). Only desc->B, Sq, Skv, causal, block_q and
- * block_kv are read; block_q and block_kv must lie in [16, 512]. Exact for
- * every tile. */
+/* Tile classes and compacted non-empty tile lists from positions, segment
+ * IDs and the dense mask (Kvax create_attention_mask; ring-splash MaskInfo
+ * block_mask, the lists of blocks to visit and, when out->bits is set, the
+ * partial blocks). Only desc->B, Sq, Skv, causal, block_q and block_kv are
+ * read; block_q and block_kv must lie in [16, 512]. Exact for every tile. */
 ram_status build_block_mask(const ram_attn_desc* desc, const ram_mask_src* src,
                             const ram_block_mask* out, hipStream_t stream);
 
 /* One chunk of block-sparse attention forward (ring-splash
  * _ring_attention_forward, the per-step kernel call), visiting only the
  * non-EMPTY tiles of `mask` (built by build_block_mask at ram_kernel_tile()).
+ * With mask->bits set, PARTIAL tiles are masked by their bits (required
+ * when src->dense is set); otherwise by positions and segment IDs.
  *   q [B,Sq,H,D], k and v [B,Skv,Hkv,D] in desc->dtype; sinks float32 [H] or NULL.
  *   mode RAM_OUT_WRITE: out <- chunk output (float32 [B,Sq,H,D]), lse <- chunk
  *        lse (float32 [B,H,Sq]), for every row (empty rows get 0 / -inf).
@@ -145,16 +171,18 @@ ram_status lse_merge(int32_t B, int32_t Sq, int32_t H, int32_t D, float* out_acc
  *     src->kv_pos_base. Explicit kv_pos / kv_seg arrays span all
  *     n_chunks*Skv keys and travel with their chunk.
  *   Sinks enter on the first visited chunk only.
+ *   A dense mask (src->dense) is read per chunk as ram_mask_src describes.
  * workspace: device memory of at least ring_attn_workspace_bytes(), 256-byte
  * aligned; it holds the float32 output accumulator (bf16 only) and the block
- * masks of every chunk. */
+ * masks of every chunk (with their tile bits when src->dense is set). */
 ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32_t q_shard,
                               const void* q, const void* k_all, const void* v_all,
                               const ram_mask_src* src, const float* sinks, void* out, float* lse,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes ring_attn_fwd_1gpu needs for this shape (0 on bad input). */
-size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks);
+/* Workspace bytes ring_attn_fwd_1gpu needs for this shape (0 on bad input).
+ * src may be NULL; a source with a dense mask needs room for tile bits. */
+size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src);
 
 /* The tile (block_q, block_kv) the attention kernel of (dtype, D) runs at;
  * block masks passed to attn_fwd_chunk must be built at this tile. */

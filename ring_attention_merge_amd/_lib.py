@@ -48,12 +48,14 @@ class c_mask_src(ctypes.Structure):
     _fields_ = [("q_pos", ctypes.c_void_p), ("kv_pos", ctypes.c_void_p),
                 ("q_pos_base", ctypes.c_int32), ("kv_pos_base", ctypes.c_int32),
                 ("q_seg", ctypes.c_void_p), ("kv_seg", ctypes.c_void_p),
-                ("q_meta_stride_b", ctypes.c_int64), ("kv_meta_stride_b", ctypes.c_int64)]
+                ("q_meta_stride_b", ctypes.c_int64), ("kv_meta_stride_b", ctypes.c_int64),
+                ("dense", ctypes.c_void_p), ("dense_ld", ctypes.c_int64),
+                ("dense_chunk_step", ctypes.c_int64)]
 
 
 class c_block_mask(ctypes.Structure):
     _fields_ = [("tile_class", ctypes.c_void_p), ("row_cnt", ctypes.c_void_p),
-                ("col_idx", ctypes.c_void_p)]
+                ("col_idx", ctypes.c_void_p), ("bits", ctypes.c_void_p)]
 
 
 _lib = None
@@ -76,7 +78,7 @@ def load(path: str = LIB_PATH):
     lib.lse_merge.argtypes = [i32, i32, i32, i32, f32p, f32p, f32p, f32p, vp]
     lib.ring_attn_fwd_1gpu.argtypes = [P(c_desc), i32, i32, vp, vp, vp, P(c_mask_src), f32p, vp, f32p,
                                        vp, ctypes.c_size_t, vp]
-    lib.ring_attn_workspace_bytes.argtypes = [P(c_desc), i32]
+    lib.ring_attn_workspace_bytes.argtypes = [P(c_desc), i32, P(c_mask_src)]
     lib.ring_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.ram_kernel_tile.argtypes = [i32, i32, P(i32), P(i32)]
     lib.ram_last_error.argtypes = []
@@ -119,7 +121,8 @@ class Desc:
 
 @dataclass
 class MaskSrc:
-    """Python side of ram_mask_src: int32 CUDA tensors or None (sequential / no segments)."""
+    """Python side of ram_mask_src: int32 CUDA tensors or None (sequential / no segments),
+    and an optional dense uint8 [Sq, dense_ld] mask (nonzero = allowed)."""
     q_pos: Optional[torch.Tensor] = None
     kv_pos: Optional[torch.Tensor] = None
     q_pos_base: int = 0
@@ -128,42 +131,57 @@ class MaskSrc:
     kv_seg: Optional[torch.Tensor] = None
     q_meta_stride_b: int = 0
     kv_meta_stride_b: int = 0
+    dense: Optional[torch.Tensor] = None
+    dense_ld: int = 0
+    dense_chunk_step: int = 0
 
-    def c(self, B: int, Sq: int, kv_len: int) -> c_mask_src:
+    def c(self, B: int, Sq: int, kv_len: int, dense_cols: Optional[int] = None) -> c_mask_src:
         for name, t, S, st in (("q_pos", self.q_pos, Sq, self.q_meta_stride_b),
                                ("q_seg", self.q_seg, Sq, self.q_meta_stride_b),
                                ("kv_pos", self.kv_pos, kv_len, self.kv_meta_stride_b),
                                ("kv_seg", self.kv_seg, kv_len, self.kv_meta_stride_b)):
             if t is not None:
                 _need(t, name, torch.int32, (B - 1) * (st or S) + S if B > 0 else 0)
+        if self.dense is not None:
+            cols = kv_len if dense_cols is None else dense_cols
+            ld = self.dense_ld or cols
+            _need(self.dense, "dense", torch.uint8, (Sq - 1) * ld + cols if Sq > 0 and ld >= cols else 0)
         return c_mask_src(_ptr(self.q_pos), _ptr(self.kv_pos), self.q_pos_base, self.kv_pos_base,
-                          _ptr(self.q_seg), _ptr(self.kv_seg), self.q_meta_stride_b, self.kv_meta_stride_b)
+                          _ptr(self.q_seg), _ptr(self.kv_seg), self.q_meta_stride_b, self.kv_meta_stride_b,
+                          _ptr(self.dense), self.dense_ld, self.dense_chunk_step)
 
 
 @dataclass
 class BlockMask:
-    """Python side of ram_block_mask: uint8 / int32 CUDA tensors."""
+    """Python side of ram_block_mask: uint8 / int32 CUDA tensors, plus the optional
+    int32 tile bits (uint32 words in the C ABI) of PARTIAL tiles."""
     tile_class: torch.Tensor
     row_cnt: torch.Tensor
     col_idx: torch.Tensor
     nQb: int = 0
     nKb: int = 0
+    bits: Optional[torch.Tensor] = None
+    tile_words: int = 0   # block_q * ceil(block_kv / 32)
 
     def c(self, B: int) -> c_block_mask:
         _need(self.tile_class, "tile_class", torch.uint8, B * self.nQb * self.nKb)
         _need(self.row_cnt, "row_cnt", torch.int32, B * self.nQb)
         _need(self.col_idx, "col_idx", torch.int32, B * self.nQb * self.nKb)
-        return c_block_mask(_ptr(self.tile_class), _ptr(self.row_cnt), _ptr(self.col_idx))
+        if self.bits is not None:
+            _need(self.bits, "bits", torch.int32, B * self.nQb * self.nKb * self.tile_words)
+        return c_block_mask(_ptr(self.tile_class), _ptr(self.row_cnt), _ptr(self.col_idx), _ptr(self.bits))
 
 
-def alloc_block_mask(desc: Desc, device="cuda") -> BlockMask:
-    """Allocate the three block-mask arrays for desc's shape and tile."""
+def alloc_block_mask(desc: Desc, device="cuda", with_bits: bool = False) -> BlockMask:
+    """Allocate the block-mask arrays for desc's shape and tile (and the tile bits)."""
     nQb = -(-desc.Sq // desc.block_q)
     nKb = -(-desc.Skv // desc.block_kv)
     n = max(1, desc.B * nQb * nKb)
+    tw = desc.block_q * (-(-desc.block_kv // 32))
+    bits = torch.zeros(n * tw, dtype=torch.int32, device=device) if with_bits else None
     return BlockMask(torch.empty(n, dtype=torch.uint8, device=device),
                      torch.empty(max(1, desc.B * nQb), dtype=torch.int32, device=device),
-                     torch.empty(n, dtype=torch.int32, device=device), nQb, nKb)
+                     torch.empty(n, dtype=torch.int32, device=device), nQb, nKb, bits, tw)
 
 
 # ------------------------------------------------------------------------------ helpers
@@ -242,9 +260,12 @@ def lse_merge(out_acc, lse_acc, out_blk, lse_blk, stream=None):
                             _stream(stream)))
 
 
-def ring_attn_workspace_bytes(desc: Desc, n_chunks: int) -> int:
+def ring_attn_workspace_bytes(desc: Desc, n_chunks: int, src: Optional[MaskSrc] = None) -> int:
     cd = desc.c()
-    return int(load().ring_attn_workspace_bytes(ctypes.byref(cd), n_chunks))
+    if src is None:
+        return int(load().ring_attn_workspace_bytes(ctypes.byref(cd), n_chunks, None))
+    cs = c_mask_src(0, 0, 0, 0, 0, 0, 0, 0, _ptr(src.dense), src.dense_ld, src.dense_chunk_step)
+    return int(load().ring_attn_workspace_bytes(ctypes.byref(cd), n_chunks, ctypes.byref(cs)))
 
 
 def ring_attn_fwd_1gpu(desc: Desc, n_chunks: int, q_shard: int, q, k_all, v_all, src: MaskSrc, sinks,
@@ -261,7 +282,8 @@ def ring_attn_fwd_1gpu(desc: Desc, n_chunks: int, q_shard: int, q, k_all, v_all,
     if sinks is not None:
         _need(sinks, "sinks", torch.float32, desc.H)
     _need(workspace, "workspace", torch.uint8, 0)
-    cd, cs = desc.c(), src.c(desc.B, desc.Sq, kv_len)
+    dense_cols = desc.Skv + (n_chunks - 1) * src.dense_chunk_step
+    cd, cs = desc.c(), src.c(desc.B, desc.Sq, kv_len, dense_cols)
     _check(load().ring_attn_fwd_1gpu(ctypes.byref(cd), n_chunks, q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
                                      ctypes.byref(cs), _ptr(sinks), _ptr(out), _ptr(lse), _ptr(workspace),
                                      workspace.numel(), _stream(stream)))

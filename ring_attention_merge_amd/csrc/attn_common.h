@@ -92,6 +92,28 @@ __device__ __forceinline__ void apply_mask(f32x16 (&S)[NK], const AttnParams& p,
   }
 }
 
+// Element mask of a PARTIAL tile from its stored bits: `row` holds NK words
+// for this lane's query row, key j of the tile at bit j % 32 of word j / 32.
+template <int NK>
+__device__ __forceinline__ void apply_bits(f32x16 (&S)[NK], const uint32_t* row, int lg) {
+  uint32_t wv[NK];
+  if constexpr (NK == 2) {
+    const uint2 t = *reinterpret_cast<const uint2*>(row);
+    wv[0] = t.x;
+    wv[1] = t.y;
+  } else {
+#pragma unroll
+    for (int kb2 = 0; kb2 < NK; ++kb2) wv[kb2] = row[kb2];
+  }
+#pragma unroll
+  for (int kb2 = 0; kb2 < NK; ++kb2) {
+    const uint32_t x = wv[kb2] >> (4 * lg);   // key 8*(i>>2) + 4*lg + (i&3) of the block
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (((x >> (8 * (i >> 2) + (i & 3))) & 1u) == 0u) S[kb2][i] = neg_inf();
+  }
+}
+
 // Soft cap in log2 units: u = cap*log2(e) * tanh(s*scale/cap), tanh(x) = 1 - 2/(1+e^{2x}).
 __device__ __forceinline__ float capped_log2(float s, float k2, float cap_log2) {
   const float e = fast_exp2(s * k2);

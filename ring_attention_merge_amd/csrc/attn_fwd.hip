@@ -63,7 +63,7 @@ __device__ __forceinline__ bool decode_work(const AttnParams& p, int& b, int& h,
 }
 
 // ------------------------------------------------------------------------------ bf16
-template <int D, bool CAP>
+template <int D, bool CAP, bool BITS>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
   constexpr int BK = kBlockKV;
   constexpr int NDS = D / 16;      // k-steps of S^T = K Q^T
@@ -156,10 +156,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
 
   // The tile list is read ahead: entry it+2 and the mask flag of tile it+1
   // are loaded while tile it is processed, so no iteration waits on them.
-  auto needs_mask = [&](int kb) { return cls[kb] != 2 || (kb + 1) * BK > p.Skv; };
+  // mask kind of a tile: 0 none, 1 from positions / segments, 2 from its stored bits
+  auto needs_mask = [&](int kb) {
+    const int c = cls[kb];
+    if constexpr (BITS)
+      if (c == 1) return 2;
+    return (c != 2 || (kb + 1) * BK > p.Skv) ? 1 : 0;
+  };
   int kb_cur = cnt > 0 ? cols[0] : 0;
   int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
-  bool mk_cur = needs_mask(kb_cur);
+  int mk_cur = needs_mask(kb_cur);
   if (cnt > 0) {
     gload(kb_cur);
     lstore(0);
@@ -168,11 +174,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
 
   for (int it = 0; it < cnt; ++it) {
     const int kb = kb_cur;
-    const bool need_mask = mk_cur;
+    const int need_mask = mk_cur;
     const int buf = it & 1;
     const bool has_next = it + 1 < cnt;
     const int kb_nn = cols[min(it + 2, cnt - 1)];
-    const bool mk_nxt = needs_mask(kb_nxt);
+    const int mk_nxt = needs_mask(kb_nxt);
     if (has_next) gload(kb_nxt);
     const __bf16* Ks = smem + buf * (K_ELEMS + V_ELEMS);
     const __bf16* Vs = Ks + K_ELEMS;
@@ -200,7 +206,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
     }
-    if (need_mask) apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
+    if (BITS && need_mask == 2)
+      apply_bits(S, p.mask_bits + ((mrow * p.nKb + kb) * kBlockQ + w * 32 + ln) * 2, lg);
+    else if (need_mask)
+      apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
     softmax_step<NDB, CAP>(S, O, m_ref, l_acc, p);
 
     bf16x8 P[4];
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
 // operand reads free of bank conflicts. Rows past Skv read as zero.
 constexpr int kDmaTile = kBlockKV * 128;   // one K or V tile (elements)
 
-template <bool CAP>
+template <bool CAP, bool BITS>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_dma(AttnParams p) {
   constexpr int D = 128;
   constexpr int BK = kBlockKV;
@@ -350,17 +359,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_dma(AttnParams p) {
     __syncthreads();
   }
 
-  auto needs_mask = [&](int kb) { return cls[kb] != 2 || (kb + 1) * BK > p.Skv; };
+  // mask kind of a tile: 0 none, 1 from positions / segments, 2 from its stored bits
+  auto needs_mask = [&](int kb) {
+    const int c = cls[kb];
+    if constexpr (BITS)
+      if (c == 1) return 2;
+    return (c != 2 || (kb + 1) * BK > p.Skv) ? 1 : 0;
+  };
   int kb_cur = cnt > 0 ? cols[0] : 0;
   int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
-  bool mk_cur = needs_mask(kb_cur);
+  int mk_cur = needs_mask(kb_cur);
   if (cnt > 0) dma(kb_cur, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int it = 0; it < cnt; ++it) {
     const int kb = kb_cur;
-    const bool need_mask = mk_cur;
+    const int need_mask = mk_cur;
     const int buf = it & 1;
     const bool has_next = it + 1 < cnt;
     if (has_next) dma(kb_nxt, buf ^ 1);   // the stage tile it-1 used: every wave has passed it
@@ -403,7 +418,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_dma(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
     }
-    if (need_mask) apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
+    if (BITS && need_mask == 2)
+      apply_bits(S, p.mask_bits + ((mrow * p.nKb + kb) * kBlockQ + w * 32 + ln) * 2, lg);
+    else if (need_mask)
+      apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
     softmax_step<NDB, CAP>(S, O, m_ref, l_acc, p);
 
     bf16x8 P[4];
@@ -429,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_dma(AttnParams p) {
     // counter of LDS reads but complete out of order; issued here, no LDS wait
     // above has to cover them.
     const int kb_nn = cols[min(it + 2, cnt - 1)];
-    const bool mk_nxt = needs_mask(kb_nxt);
+    const int mk_nxt = needs_mask(kb_nxt);
     // the next tile's DMA must have landed before any wave reads it
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -443,7 +461,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_dma(AttnParams p) {
 // ------------------------------------------------------------------------------ fp32
 // Same structure with v_mfma_f32_32x32x2_f32: one fp32 per lane per operand,
 // K and V kept row-major in LDS, the fp32 weights feed PV directly.
-template <int D, bool CAP>
+template <int D, bool CAP, bool BITS>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(AttnParams p) {
   constexpr int BK = kBlockKV;
   constexpr int NDB = D / 32;
@@ -520,10 +538,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(AttnParams p) {
 
   // The tile list is read ahead: entry it+2 and the mask flag of tile it+1
   // are loaded while tile it is processed, so no iteration waits on them.
-  auto needs_mask = [&](int kb) { return cls[kb] != 2 || (kb + 1) * BK > p.Skv; };
+  // mask kind of a tile: 0 none, 1 from positions / segments, 2 from its stored bits
+  auto needs_mask = [&](int kb) {
+    const int c = cls[kb];
+    if constexpr (BITS)
+      if (c == 1) return 2;
+    return (c != 2 || (kb + 1) * BK > p.Skv) ? 1 : 0;
+  };
   int kb_cur = cnt > 0 ? cols[0] : 0;
   int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
-  bool mk_cur = needs_mask(kb_cur);
+  int mk_cur = needs_mask(kb_cur);
   if (cnt > 0) {
     gload(kb_cur);
     lstore(0);
@@ -532,11 +556,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(AttnParams p) {
 
   for (int it = 0; it < cnt; ++it) {
     const int kb = kb_cur;
-    const bool need_mask = mk_cur;
+    const int need_mask = mk_cur;
     const int buf = it & 1;
     const bool has_next = it + 1 < cnt;
     const int kb_nn = cols[min(it + 2, cnt - 1)];
-    const bool mk_nxt = needs_mask(kb_nxt);
+    const int mk_nxt = needs_mask(kb_nxt);
     if (has_next) gload(kb_nxt);
     const float* Ks = smem + buf * 2 * ELEMS;
     const float* Vs = Ks + ELEMS;
@@ -558,7 +582,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
     }
-    if (need_mask) apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
+    if (BITS && need_mask == 2)
+      apply_bits(S, p.mask_bits + ((mrow * p.nKb + kb) * kBlockQ + w * 32 + ln) * 2, lg);
+    else if (need_mask)
+      apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
     softmax_step<NDB, CAP>(S, O, m_ref, l_acc, p);
 
 #pragma unroll
@@ -604,6 +631,7 @@ hipError_t launch(K kernel, const AttnParams& p, hipStream_t s) {
 // RAM_ATTN_KERNEL=<name> forces one (D = 128 only, except pingpong).
 static int attn_variant(const AttnParams& p) {
   const char* e = getenv("RAM_ATTN_KERNEL");
+  if (p.mask_bits) return (e && strcmp(e, "staged") == 0) ? 5 : 0;   // the others read no tile bits
   if (e && strcmp(e, "pingpong") == 0) return 1;
   if (e && strcmp(e, "wide") == 0 && p.D == 128 && !p.kv_pos && !p.kv_seg) return 2;
   if (e && strcmp(e, "g8") == 0 && p.D == 128) return 3;
@@ -618,22 +646,44 @@ bool attn_writes_final(const AttnParams& p, int dtype) {
   return v == 0 || v == 5;
 }
 
+// Instantiations by (soft cap, tile bits); BITS kernels mask PARTIAL tiles by their stored bits.
+template <template <bool, bool> class K>
+hipError_t launch_cb(const AttnParams& p, hipStream_t s) {
+  const bool cap = p.softcap_on != 0, bits = p.mask_bits != nullptr;
+  if (cap) return bits ? launch(K<true, true>::fn, p, s) : launch(K<true, false>::fn, p, s);
+  return bits ? launch(K<false, true>::fn, p, s) : launch(K<false, false>::fn, p, s);
+}
+template <int D>
+struct Bf16Staged {
+  template <bool CAP, bool BITS>
+  struct K {
+    static constexpr auto fn = attn_fwd_bf16<D, CAP, BITS>;
+  };
+};
+template <int D>
+struct F32 {
+  template <bool CAP, bool BITS>
+  struct K {
+    static constexpr auto fn = attn_fwd_f32<D, CAP, BITS>;
+  };
+};
+template <bool CAP, bool BITS>
+struct Bf16Dma {
+  static constexpr auto fn = attn_fwd_bf16_dma<CAP, BITS>;
+};
+
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s) {
-  const bool cap = p.softcap_on != 0;
   const int variant = dtype == 1 ? attn_variant(p) : 0;
   if (variant == 1) return launch_attn_pp(p, s);
   if (variant == 2) return launch_attn_w64(p, s);
   if (variant == 3) return launch_attn_g8(p, s);
   if (variant == 4) return launch_attn_g8p(p, s);
   if (dtype == 1) {
-    if (p.D == 128) {
-      if (variant == 5) return cap ? launch(attn_fwd_bf16<128, true>, p, s) : launch(attn_fwd_bf16<128, false>, p, s);
-      return cap ? launch(attn_fwd_bf16_dma<true>, p, s) : launch(attn_fwd_bf16_dma<false>, p, s);
-    }
-    return cap ? launch(attn_fwd_bf16<64, true>, p, s) : launch(attn_fwd_bf16<64, false>, p, s);
+    if (p.D == 128) return variant == 5 ? launch_cb<Bf16Staged<128>::K>(p, s) : launch_cb<Bf16Dma>(p, s);
+    return launch_cb<Bf16Staged<64>::K>(p, s);
   }
-  if (p.D == 128) return cap ? launch(attn_fwd_f32<128, true>, p, s) : launch(attn_fwd_f32<128, false>, p, s);
-  return cap ? launch(attn_fwd_f32<64, true>, p, s) : launch(attn_fwd_f32<64, false>, p, s);
+  if (p.D == 128) return launch_cb<F32<128>::K>(p, s);
+  return launch_cb<F32<64>::K>(p, s);
 }
 
 }  // namespace ram

@@ -1,21 +1,27 @@
-// Block-mask builder: tile classes (EMPTY / PARTIAL / FULL) and, per row of
-// tiles, the compacted ascending list of non-EMPTY kv tiles.
+// Block-mask builder: tile classes (EMPTY / PARTIAL / FULL), per row of tiles
+// the compacted ascending list of non-EMPTY kv tiles, and optionally the
+// element mask of every PARTIAL tile as bits.
 //
 // What it computes: the block-sparse metadata the ejkernel ring-splash page
-// passes to its kernel (MaskInfo: a block mask plus the lists of blocks to
-// visit), built the way the Kvax page's create_attention_mask builds its
+// passes to its kernel (MaskInfo: a block mask, the lists of blocks to visit
+// and, for a caller-given two-dimensional mask, the contents of the partial
+// blocks), built the way the Kvax page's create_attention_mask builds its
 // block-wise masks: from positions and segment IDs, skipping blocks with
 // nothing to attend. A tile is EMPTY when none of its (query, key) pairs is
 // allowed, FULL when all are, else PARTIAL; pairs past the sequence ends do
 // not count.
 //
-// One workgroup per (row of tiles, batch, chunk). With sequential positions
-// and no segments a tile's class follows from its position ranges alone:
-// FULL iff min q_pos >= max kv_pos, EMPTY iff max q_pos < min kv_pos. With
-// explicit positions but no segments the same test runs on the tile's
-// position minima and maxima. With segments every pair of the tile is
-// checked. Classes are staged in LDS, then compacted in order with wave
-// ballots and a running offset.
+// One workgroup per (row of tiles, batch, chunk). With sequential positions,
+// no segments, no dense mask and no bits requested, a tile's class follows
+// from its position ranges alone: FULL iff min q_pos >= max kv_pos, EMPTY iff
+// max q_pos < min kv_pos; with explicit positions the same test runs on the
+// tile's position minima and maxima. Otherwise every pair is checked, a
+// group of tiles per round: each thread builds 32-pair words of the tiles' bit
+// rows (key j of a tile at bit j % 32 of word j / 32) from a closed-form causal
+// prefix (sequential keys), the segment IDs and 16-byte reads of the dense
+// mask, skipping the reads for words the other tests already cleared; the
+// words are staged in LDS and stored for PARTIAL tiles. Classes are staged in
+// LDS, then compacted in order with wave ballots and a running offset.
 #include <hip/hip_runtime.h>
 
 #include "ram_internal.h"
@@ -25,6 +31,34 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+// Pairwise rounds cover up to kGroupKeys keys and kGroupWords bit words.
+constexpr int kGroupKeys = 1024;
+constexpr int kGroupWords = 8192;
+
+// One bit per byte of 4 bytes (nonzero -> 1), byte k to bit k: OR-fold each
+// byte onto its lowest bit, then one multiply moves the four bits next to each
+// other at bits 21..24 (the 16 partial products land on distinct bits).
+__device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t x) {
+  uint32_t y = x | (x >> 4);
+  y |= y >> 2;
+  y |= y >> 1;
+  y &= 0x01010101u;
+  return ((y * 0x00204081u) >> 21) & 0xFu;
+}
+
+// Bits of `n` (<= 32) consecutive dense-mask bytes, byte j at bit j.
+__device__ __forceinline__ uint32_t dense_word(const uint8_t* d, int n) {
+  if (n == 32 && (reinterpret_cast<uintptr_t>(d) & 15) == 0) {
+    const uint4 a = *reinterpret_cast<const uint4*>(d);
+    const uint4 b = *reinterpret_cast<const uint4*>(d + 16);
+    return nonzero_bytes4(a.x) | nonzero_bytes4(a.y) << 4 | nonzero_bytes4(a.z) << 8 |
+           nonzero_bytes4(a.w) << 12 | nonzero_bytes4(b.x) << 16 | nonzero_bytes4(b.y) << 20 |
+           nonzero_bytes4(b.z) << 24 | nonzero_bytes4(b.w) << 28;
+  }
+  uint32_t m = 0;
+  for (int j = 0; j < n; ++j) m |= (uint32_t)(d[j] != 0) << j;
+  return m;
+}
 
 __device__ __forceinline__ int wave_min(int v) {
   for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
@@ -57,9 +91,11 @@ __device__ __forceinline__ void block_minmax(int vmin, int vmax, int* red, int& 
 __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
   __shared__ uint8_t cls_s[kMaxMaskCols];
   __shared__ int qpos_s[kMaxMaskTile], qseg_s[kMaxMaskTile];
-  __shared__ int kpos_s[kMaxMaskTile], kseg_s[kMaxMaskTile];
+  __shared__ int kpos_s[kGroupKeys], kseg_s[kGroupKeys];
   __shared__ int red[2 * kWaves];
   __shared__ int wsum[kWaves];
+  __shared__ uint32_t bits_s[kGroupWords];
+  __shared__ int flag_s[kGroupKeys / 16];
 
   const int qb = blockIdx.x, b = blockIdx.y, c = blockIdx.z;
   const int tid = threadIdx.x;
@@ -73,8 +109,8 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
   const int32_t* kvseg = p.kv_seg ? p.kv_seg + kvoff : nullptr;
   const int64_t crow = ((int64_t)c * p.B + b) * p.nQb + qb;   // row index over (chunk, batch, q tile)
 
-  if (qseg == nullptr) {
-    // No segments: classes from position ranges (exact: all pairs allowed iff
+  if (qseg == nullptr && p.dense == nullptr && p.bits == nullptr) {
+    // No segments or dense mask: classes from position ranges (exact: all pairs allowed iff
     // max kv <= min q; none iff max q < min kv).
     int qmin, qmax;
     if (qpos) {
@@ -116,31 +152,74 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
       }
     }
   } else {
-    // Segments: check every pair of each tile.
+    // Pairwise: positions, segments and the dense mask of every pair, a group
+    // of tiles per round. Each thread builds 32-pair words of the tiles' bit
+    // rows; per-tile flags (bit 0: a pair allowed, bit 1: a pair excluded)
+    // give the classes.
     for (int i = tid; i < nq; i += kThreads) {
       qpos_s[i] = qpos ? qpos[i] : p.q_pos_base + q0 + i;
-      qseg_s[i] = qseg[i];
+      qseg_s[i] = qseg ? qseg[i] : 0;
     }
-    for (int kb = 0; kb < p.nKb; ++kb) {
-      const int k0 = kb * p.bk;
-      const int nk = min(p.Skv, k0 + p.bk) - k0;
-      for (int j = tid; j < nk; j += kThreads) {
-        kpos_s[j] = kvpos ? kvpos[k0 + j] : kv_base + k0 + j;
-        kseg_s[j] = kvseg[k0 + j];
+    const int W = (p.bk + 31) >> 5;   // words per tile row
+    const int tw = p.bq * W;          // words per tile
+    const int tg = max(1, min(kGroupKeys / p.bk, kGroupWords / tw));
+    const uint8_t* drow0 = p.dense ? p.dense + (int64_t)q0 * p.dense_ld + (int64_t)c * p.dense_col_step : nullptr;
+    for (int kbg = 0; kbg < p.nKb; kbg += tg) {
+      const int ng = min(tg, p.nKb - kbg);
+      const int g0 = kbg * p.bk;                           // first key of the group
+      const int gk = min(p.Skv, (kbg + ng) * p.bk) - g0;   // keys of the group
+      for (int j = tid; j < gk; j += kThreads) {
+        kpos_s[j] = kvpos ? kvpos[g0 + j] : kv_base + g0 + j;
+        kseg_s[j] = kvseg ? kvseg[g0 + j] : 0;
+      }
+      for (int t = tid; t < ng; t += kThreads) flag_s[t] = 0;
+      __syncthreads();
+      const int nw = ng * tw;
+      for (int t = tid; t < nw; t += kThreads) {
+        const int tl = t / tw, r = t - tl * tw;
+        const int i = r / W;
+        const int j0 = tl * p.bk + (r - i * W) * 32;       // first key of the word within the group
+        const int jn = min(min(32, gk - j0), (tl + 1) * p.bk - j0);
+        uint32_t word = 0;
+        if (i < nq && jn > 0) {
+          const uint32_t valid = jn == 32 ? ~0u : ((1u << jn) - 1u);
+          uint32_t w = valid;
+          if (p.causal) {
+            if (!kvpos) {
+              // sequential keys: the allowed ones are a prefix of the word
+              const int64_t lim = (int64_t)qpos_s[i] - ((int64_t)kv_base + g0 + j0);
+              w &= lim < 0 ? 0u : (lim >= 31 ? ~0u : ((2u << lim) - 1u));
+            } else {
+              uint32_t cm = 0;
+              for (int jj = 0; jj < jn; ++jj) cm |= (uint32_t)(kpos_s[j0 + jj] <= qpos_s[i]) << jj;
+              w &= cm;
+            }
+          }
+          if (qseg && w) {
+            const int qs = qseg_s[i];
+            uint32_t sm = 0;
+            if (qs != -1)
+              for (int jj = 0; jj < jn; ++jj) sm |= (uint32_t)(kseg_s[j0 + jj] == qs) << jj;
+            w &= sm;
+          }
+          if (drow0 && w) w &= dense_word(drow0 + (int64_t)i * p.dense_ld + g0 + j0, jn);
+          word = w;
+          const int f = (w != 0 ? 1 : 0) | (w != valid ? 2 : 0);
+          if (f) atomicOr(&flag_s[tl], f);
+        }
+        bits_s[t] = word;
       }
       __syncthreads();
-      int any_ok = 0, any_bad = 0;
-      const int npair = nq * nk;
-      for (int t = tid; t < npair; t += kThreads) {
-        const int i = t / nk, j = t - (t / nk) * nk;
-        bool ok = qseg_s[i] != -1 && qseg_s[i] == kseg_s[j];
-        if (p.causal) ok = ok && kpos_s[j] <= qpos_s[i];
-        any_ok |= ok;
-        any_bad |= !ok;
+      for (int t = tid; t < ng; t += kThreads) {
+        const int f = flag_s[t];
+        cls_s[kbg + t] = (f & 1) ? ((f & 2) ? 1 : 2) : 0;
       }
-      any_ok = __syncthreads_or(any_ok);
-      any_bad = __syncthreads_or(any_bad);
-      if (tid == 0) cls_s[kb] = any_ok ? (any_bad ? 1 : 2) : 0;
+      if (p.bits) {
+        uint32_t* dst = p.bits + ((size_t)crow * p.nKb + kbg) * tw;
+        for (int t = tid; t < nw; t += kThreads)
+          if (flag_s[t / tw] == 3) dst[t] = bits_s[t];
+      }
+      __syncthreads();   // the next group rewrites kpos_s / kseg_s / bits_s / flag_s
     }
   }
   __syncthreads();

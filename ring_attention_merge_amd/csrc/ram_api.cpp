@@ -92,9 +92,16 @@ ram_status check_kv_stride(const ram_attn_desc* d, int64_t keys) {
   return RAM_OK;
 }
 
-// Positions / segments of one call whose KV spans `kv_len` keys.
-ram_status check_src(const ram_mask_src* m, const ram_attn_desc* d, int64_t kv_len, int64_t q_base_extra) {
+// Positions / segments of one call whose KV spans `kv_len` keys; a dense mask
+// is read over `dense_cols` columns per row.
+ram_status check_src(const ram_mask_src* m, const ram_attn_desc* d, int64_t kv_len, int64_t q_base_extra,
+                     int64_t dense_cols) {
   if (!m) return fail(RAM_ERR_INVALID, "mask source is null");
+  if (m->dense) {
+    if (m->dense_chunk_step < 0) return fail(RAM_ERR_INVALID, "dense_chunk_step=%lld < 0", (long long)m->dense_chunk_step);
+    if (m->dense_ld != 0 && m->dense_ld < dense_cols)
+      return fail(RAM_ERR_INVALID, "dense_ld=%lld < %lld columns read", (long long)m->dense_ld, (long long)dense_cols);
+  }
   if ((m->q_seg == nullptr) != (m->kv_seg == nullptr))
     return fail(RAM_ERR_INVALID, "q_seg and kv_seg must both be set or both be null");
   if (m->q_meta_stride_b != 0 && m->q_meta_stride_b < d->Sq)
@@ -117,8 +124,11 @@ ram_status check_src(const ram_mask_src* m, const ram_attn_desc* d, int64_t kv_l
   return RAM_OK;
 }
 
-ram_status check_mask_arrays(const ram_block_mask* bm, const ram_attn_desc* d) {
+ram_status check_mask_arrays(const ram_block_mask* bm, const ram_attn_desc* d, bool need_bits) {
   if (!bm) return fail(RAM_ERR_INVALID, "block mask is null");
+  if (bm->bits && !aligned(bm->bits, 8)) return fail(RAM_ERR_INVALID, "bits not 8-byte aligned");
+  if (need_bits && !bm->bits && cdiv(d->Skv, d->block_kv) > 0)
+    return fail(RAM_ERR_INVALID, "a dense mask needs the tile bits (block mask bits is null)");
   const int64_t rows = (int64_t)d->B * cdiv(d->Sq, d->block_q);
   if (rows == 0) return RAM_OK;
   if (!bm->row_cnt || !aligned(bm->row_cnt, 4)) return fail(RAM_ERR_INVALID, "row_cnt null or misaligned");
@@ -141,8 +151,13 @@ ram_status check_tensor(const void* p, const char* name) {
     if (_s != RAM_OK) return _s;        \
   } while (0)
 
-ram::MaskParams mask_params(const ram_attn_desc* d, const ram_mask_src* m, const ram_block_mask* bm) {
+ram::MaskParams mask_params(const ram_attn_desc* d, const ram_mask_src* m, const ram_block_mask* bm,
+                            int64_t dense_cols) {
   ram::MaskParams p{};
+  p.dense = m->dense;
+  p.dense_ld = m->dense_ld ? m->dense_ld : dense_cols;
+  p.dense_col_step = 0;
+  p.bits = bm->bits;
   p.q_pos = m->q_pos;
   p.kv_pos = m->kv_pos;
   p.q_seg = m->q_seg;
@@ -180,6 +195,7 @@ ram::AttnParams attn_params(const ram_attn_desc* d, const void* q, const void* k
   p.tile_class = bm->tile_class;
   p.row_cnt = bm->row_cnt;
   p.col_idx = bm->col_idx;
+  p.mask_bits = bm->bits;
   p.q_pos = m->q_pos;
   p.kv_pos = m->kv_pos;
   p.q_seg = m->q_seg;
@@ -209,12 +225,15 @@ ram::AttnParams attn_params(const ram_attn_desc* d, const void* q, const void* k
 }
 
 struct RingLayout {
-  size_t acc_off, cls_off, cnt_off, col_off, total;
+  size_t acc_off, cls_off, cnt_off, col_off, bits_off, total;
 };
+
+// Words of tile bits per kernel tile (block_q rows of block_kv / 32 words).
+constexpr int64_t kTileWords = (int64_t)ram::kBlockQ * (ram::kBlockKV / 32);
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks) {
+RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits) {
   RingLayout L{};
   const int64_t nQb = cdiv(d->Sq, ram::kBlockQ), nKb = cdiv(d->Skv, ram::kBlockKV);
   const int64_t tiles = (int64_t)n_chunks * d->B * nQb * nKb;
@@ -228,6 +247,8 @@ RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks) {
   off += align256((size_t)rows * sizeof(int32_t));
   L.col_off = off;
   off += align256((size_t)tiles * sizeof(int32_t));
+  L.bits_off = off;
+  if (with_bits) off += align256((size_t)tiles * kTileWords * sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -250,10 +271,10 @@ ram_status ram_kernel_tile(int32_t dtype, int32_t D, int32_t* block_q, int32_t* 
 ram_status build_block_mask(const ram_attn_desc* desc, const ram_mask_src* src, const ram_block_mask* out,
                             hipStream_t stream) {
   RAM_TRY(check_desc(desc, false, false));
-  RAM_TRY(check_src(src, desc, desc->Skv, 0));
-  RAM_TRY(check_mask_arrays(out, desc));
+  RAM_TRY(check_src(src, desc, desc->Skv, 0, desc->Skv));
+  RAM_TRY(check_mask_arrays(out, desc, false));
   if (desc->B == 0 || desc->Sq == 0) return ok();
-  ram::MaskParams p = mask_params(desc, src, out);
+  ram::MaskParams p = mask_params(desc, src, out, desc->Skv);
   hipError_t e = ram::launch_block_mask(p, 1, stream);
   if (e != hipSuccess) return hip_fail(e, "build_block_mask launch");
   return ok();
@@ -264,8 +285,8 @@ ram_status attn_fwd_chunk(const ram_attn_desc* desc, const void* q, const void* 
                           float* out, float* lse, hipStream_t stream) {
   RAM_TRY(check_desc(desc, true, true));
   RAM_TRY(check_kv_stride(desc, desc->Skv));
-  RAM_TRY(check_src(src, desc, desc->Skv, 0));
-  RAM_TRY(check_mask_arrays(mask, desc));
+  RAM_TRY(check_src(src, desc, desc->Skv, 0, desc->Skv));
+  RAM_TRY(check_mask_arrays(mask, desc, src->dense != nullptr));
   if (mode != RAM_OUT_WRITE && mode != RAM_OUT_MERGE) return fail(RAM_ERR_INVALID, "mode %d", mode);
   if (desc->B == 0 || desc->Sq == 0) return ok();
   RAM_TRY(check_tensor(q, "q"));
@@ -297,14 +318,14 @@ ram_status lse_merge(int32_t B, int32_t Sq, int32_t H, int32_t D, float* out_acc
   return ok();
 }
 
-size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks) {
+size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src) {
   if (!desc || n_chunks < 1 || desc->B < 0 || desc->Sq < 0 || desc->Skv < 0 || desc->H < 1 ||
       (desc->D != 64 && desc->D != 128))
     return 0;
   ram_attn_desc dt = *desc;
   dt.block_q = ram::kBlockQ;
   dt.block_kv = ram::kBlockKV;
-  return ring_layout(&dt, n_chunks).total;
+  return ring_layout(&dt, n_chunks, src && src->dense).total;
 }
 
 ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32_t q_shard, const void* q,
@@ -324,7 +345,9 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   if (kv_total > kMaxSeq) return fail(RAM_ERR_INVALID, "total KV too long");
   RAM_TRY(check_kv_stride(desc, kv_total));
   const int64_t q_extra = q_shard >= 0 ? (int64_t)q_shard * desc->Sq : 0;
-  RAM_TRY(check_src(src, desc, kv_total, q_extra));
+  if (!src) return fail(RAM_ERR_INVALID, "mask source is null");
+  const int64_t dense_cols = desc->Skv + (int64_t)(n_chunks - 1) * (src->dense ? src->dense_chunk_step : 0);
+  RAM_TRY(check_src(src, desc, kv_total, q_extra, dense_cols));
   if (desc->B == 0 || desc->Sq == 0) return ok();
   RAM_TRY(check_tensor(q, "q"));
   if (desc->Skv > 0) {
@@ -334,7 +357,8 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   RAM_TRY(check_tensor(out, "out"));
   if (!lse || !aligned(lse, 4)) return fail(RAM_ERR_INVALID, "lse null or misaligned");
   if (sinks && !aligned(sinks, 4)) return fail(RAM_ERR_INVALID, "sinks misaligned");
-  const RingLayout L = ring_layout(desc, n_chunks);
+  const bool with_bits = src->dense != nullptr;
+  const RingLayout L = ring_layout(desc, n_chunks, with_bits);
   if (!workspace || !aligned(workspace, 256))
     return fail(RAM_ERR_WORKSPACE, "workspace null or not 256-byte aligned");
   if (workspace_bytes < L.total)
@@ -342,7 +366,8 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
 
   char* ws = static_cast<char*>(workspace);
   ram_block_mask bm{reinterpret_cast<uint8_t*>(ws + L.cls_off), reinterpret_cast<int32_t*>(ws + L.cnt_off),
-                    reinterpret_cast<int32_t*>(ws + L.col_off)};
+                    reinterpret_cast<int32_t*>(ws + L.col_off),
+                    with_bits ? reinterpret_cast<uint32_t*>(ws + L.bits_off) : nullptr};
   float* acc = desc->dtype == RAM_BF16 ? reinterpret_cast<float*>(ws + L.acc_off) : static_cast<float*>(out);
   const int64_t nQb = cdiv(desc->Sq, ram::kBlockQ), nKb = cdiv(desc->Skv, ram::kBlockKV);
   const int64_t kv_full_stride = desc->kv_stride_b ? desc->kv_stride_b : kv_total * desc->Hkv * desc->D;
@@ -354,9 +379,10 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   ram_mask_src sm = *src;
   sm.q_pos_base = q_base;
   sm.kv_meta_stride_b = kvm_full;
-  ram::MaskParams mp = mask_params(&dm, &sm, &bm);
+  ram::MaskParams mp = mask_params(&dm, &sm, &bm, dense_cols);
   mp.kv_chunk_off = desc->Skv;
   mp.kv_base_step = desc->Skv;
+  mp.dense_col_step = src->dense_chunk_step;
   hipError_t e = ram::launch_block_mask(mp, n_chunks, stream);
   if (e != hipSuccess) return hip_fail(e, "ring block mask launch");
 
@@ -372,9 +398,9 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
     sc.kv_pos = src->kv_pos ? src->kv_pos + (int64_t)c * desc->Skv : nullptr;
     sc.kv_seg = src->kv_seg ? src->kv_seg + (int64_t)c * desc->Skv : nullptr;
     sc.kv_pos_base = src->kv_pos_base + c * desc->Skv;
-    const ram_block_mask bc{bm.tile_class + (int64_t)c * desc->B * nQb * nKb,
-                            bm.row_cnt + (int64_t)c * desc->B * nQb,
-                            bm.col_idx + (int64_t)c * desc->B * nQb * nKb};
+    const int64_t tiles_c = (int64_t)c * desc->B * nQb * nKb;
+    const ram_block_mask bc{bm.tile_class + tiles_c, bm.row_cnt + (int64_t)c * desc->B * nQb,
+                            bm.col_idx + tiles_c, with_bits ? bm.bits + tiles_c * kTileWords : nullptr};
     const char* kc = static_cast<const char*>(k_all) + (int64_t)c * desc->Skv * desc->Hkv * desc->D * esz;
     const char* vc = static_cast<const char*>(v_all) + (int64_t)c * desc->Skv * desc->Hkv * desc->D * esz;
     ram::AttnParams p = attn_params(&dc, q, kc, vc, &sc, &bc, t == 0 ? sinks : nullptr,

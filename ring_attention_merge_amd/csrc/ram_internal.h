@@ -30,6 +30,7 @@ struct AttnParams {
   const int32_t* kv_pos;
   const int32_t* q_seg;
   const int32_t* kv_seg;
+  const uint32_t* mask_bits;  // bits of the PARTIAL tiles (128 rows x 2 words per tile) or null
   int64_t q_stride_b, kv_stride_b;   // elements
   int64_t qm_stride_b, kvm_stride_b; // elements of the position / segment arrays
   int32_t q_pos_base, kv_pos_base;
@@ -52,10 +53,13 @@ struct MaskParams {
   int64_t kv_chunk_off;    // elements added to kv_pos / kv_seg per chunk (blockIdx.z)
   int32_t q_pos_base, kv_pos_base;
   int32_t kv_base_step;    // added to kv_pos_base per chunk
+  const uint8_t* dense;    // [Sq, dense_ld] or null; chunk c reads from column c * dense_col_step
+  int64_t dense_ld, dense_col_step;
   int32_t B, Sq, Skv, bq, bk, nQb, nKb, causal;
   uint8_t* tile_class;     // chunk c at + c * B*nQb*nKb
   int32_t* row_cnt;        // chunk c at + c * B*nQb
   int32_t* col_idx;        // chunk c at + c * B*nQb*nKb
+  uint32_t* bits;          // or null; tile t at + t * bq*ceil(bk/32), t counted like tile_class
 };
 
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s);

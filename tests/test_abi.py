@@ -49,11 +49,13 @@ def _desc(**kw):
 def _src(**kw):
     return _lib.c_mask_src(kw.get("q_pos", 0), kw.get("kv_pos", 0), kw.get("q_pos_base", 0),
                            kw.get("kv_pos_base", 0), kw.get("q_seg", 0), kw.get("kv_seg", 0),
-                           kw.get("q_meta_stride_b", 0), kw.get("kv_meta_stride_b", 0))
+                           kw.get("q_meta_stride_b", 0), kw.get("kv_meta_stride_b", 0),
+                           kw.get("dense", 0), kw.get("dense_ld", 0), kw.get("dense_chunk_step", 0))
 
 
 def _bm(**kw):
-    return _lib.c_block_mask(kw.get("tile_class", FAKE), kw.get("row_cnt", FAKE), kw.get("col_idx", FAKE))
+    return _lib.c_block_mask(kw.get("tile_class", FAKE), kw.get("row_cnt", FAKE), kw.get("col_idx", FAKE),
+                             kw.get("bits", 0))
 
 
 def _chunk(lib, d, *, q=FAKE, k=FAKE, v=FAKE, src=None, bm=None, sinks=0, mode=0, out=FAKE, lse=FAKE):
@@ -117,6 +119,32 @@ def test_chunk_pointer_validation(lib):
     assert lib.attn_fwd_chunk(None, FAKE, FAKE, FAKE, None, None, 0, 0, FAKE, FAKE, 0) == _lib.RAM_ERR_INVALID
 
 
+def test_dense_mask_validation(lib):
+    d = _desc()
+    # a dense mask is applied through the tile bits: attention needs them
+    assert _chunk(lib, d, src=_src(dense=FAKE2)) == _lib.RAM_ERR_INVALID and "tile bits" in _err(lib)
+    assert _chunk(lib, d, src=_src(dense=FAKE2), bm=_bm(bits=FAKE + 4)) == _lib.RAM_ERR_INVALID
+    assert "8-byte" in _err(lib)
+    assert _chunk(lib, d, src=_src(dense=FAKE2, dense_ld=255), bm=_bm(bits=FAKE2)) == _lib.RAM_ERR_INVALID
+    assert "dense_ld" in _err(lib)
+    assert _chunk(lib, d, src=_src(dense=FAKE2, dense_chunk_step=-1), bm=_bm(bits=FAKE2)) == _lib.RAM_ERR_INVALID
+    dm = _desc(block_q=64, block_kv=48)
+    assert lib.build_block_mask(ctypes.byref(dm), ctypes.byref(_src(dense=FAKE2, dense_ld=100)),
+                                ctypes.byref(_bm()), 0) == _lib.RAM_ERR_INVALID
+    # the ring reads Skv + (n - 1) * step columns per row
+    dr = _desc(B=1, Sq=512, Skv=512, H=4, Hkv=4)
+    src = _src(dense=FAKE2, dense_chunk_step=512, dense_ld=4 * 512 - 1)
+    assert _ring(lib, dr, 4, 3, src=src) == _lib.RAM_ERR_INVALID and "dense_ld" in _err(lib)
+    src = _src(dense=FAKE2, dense_chunk_step=0, dense_ld=511)
+    assert _ring(lib, dr, 4, 3, src=src) == _lib.RAM_ERR_INVALID
+    # with a dense mask the ring workspace also holds one 1 KiB bit tile per kernel tile
+    base = lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, None)
+    plain = lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src()))
+    dense = lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src(dense=FAKE2)))
+    assert base == plain and dense == base + 4 * 4 * 8 * 1024
+    assert _ring(lib, dr, 4, 3, src=_src(dense=FAKE2), ws_bytes=dense - 1) == _lib.RAM_ERR_WORKSPACE
+
+
 def test_empty_inputs_are_noops(lib):
     # B = 0 or Sq = 0: valid, nothing to do, nothing launched (works without a GPU)
     assert _chunk(lib, _desc(B=0), q=0, out=0, lse=0) == _lib.RAM_OK
@@ -155,14 +183,14 @@ def _ring(lib, d, n, r, ws=FAKE, ws_bytes=1 << 40, src=None, out=FAKE, q=FAKE):
 
 def test_ring_validation_and_workspace(lib):
     d = _desc(B=1, Sq=4096, Skv=4096, H=8, Hkv=8)
-    need = lib.ring_attn_workspace_bytes(ctypes.byref(d), 4)
+    need = lib.ring_attn_workspace_bytes(ctypes.byref(d), 4, None)
     acc = 4096 * 8 * 128 * 4
     tiles = 4 * 32 * 64
     expect = acc + ((tiles + 255) // 256) * 256 + ((4 * 32 * 4 + 255) // 256) * 256 + tiles * 4
     assert need == expect
     d32 = _desc(B=1, Sq=4096, Skv=4096, H=8, Hkv=8, dtype=ram.RAM_F32)
-    assert lib.ring_attn_workspace_bytes(ctypes.byref(d32), 4) == need - acc   # fp32 accumulates in out
-    assert lib.ring_attn_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(d32), 4, None) == need - acc   # fp32 accumulates in out
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(d), 0, None) == 0
     assert _ring(lib, d, 0, -1) == _lib.RAM_ERR_INVALID
     assert _ring(lib, d, 4, 4) == _lib.RAM_ERR_INVALID and "q_shard" in _err(lib)
     assert _ring(lib, d, 4, -2) == _lib.RAM_ERR_INVALID
@@ -174,7 +202,7 @@ def test_ring_validation_and_workspace(lib):
     assert _ring(lib, d, 4, 3, out=0) == _lib.RAM_ERR_INVALID
     # the ring picks its own tile: a caller's block_q/block_kv are ignored
     dt = _desc(B=1, Sq=4096, Skv=4096, H=8, Hkv=8, block_q=32, block_kv=32)
-    assert lib.ring_attn_workspace_bytes(ctypes.byref(dt), 4) == need
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(dt), 4, None) == need
     assert _ring(lib, _desc(B=0), 4, 3, q=0, out=0) == _lib.RAM_OK
 
 
