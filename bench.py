@@ -17,6 +17,12 @@ roofline: the attention chunk kernel alone, timed launch by launch with HIP
 cpu_baseline: the float64 oracle on a bounded sample of query rows of the
        same workload (all heads, all keys), in pair FLOPs per second.
 
+--workload c5dense runs the same shape with a dense two-dimensional mask over
+all keys (ANDed with the causal test): the step then also classifies every
+pair of the mask, the chunk kernel masks PARTIAL tiles from their stored bits,
+and the line carries a `mask_builder` object (the builder alone over the whole
+mask, against HBM bandwidth).
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -39,7 +45,9 @@ from ring_attention_merge_amd import workloads as wl  # noqa: E402
 METRIC = "effective attention fwd TFLOP/s (unmasked tiles) and % bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 REF_TILE = 128                  # fixed reference tiling for effective FLOPs
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
 ATTN_KERNEL = "attn_fwd_bf16_dma<false, false>"
+ATTN_KERNEL_BITS = "attn_fwd_bf16_dma<false, true>"
 
 
 def log(*a):
@@ -53,17 +61,24 @@ def workload(name: str):
         "c4mqa": lambda: wl.c4_gqa_cap_sinks(Hkv=1),
         "c3": wl.c3_packed_docs,
         "c2": wl.c2_ring_shard,
+        "c5dense": wl.c5_dense,
     }[name]()
 
 
-def ring_chunk_src(w, c, dev):
-    """Mask source of chunk c of the ring (positions and segments travel with the chunk)."""
+def dense_tensor(w, dev):
+    return None if w.dense is None else torch.from_numpy(w.dense).to(dev)
+
+
+def ring_chunk_src(w, c, dev, dense=None):
+    """Mask source of chunk c of the ring (positions, segments and dense-mask columns travel
+    with the chunk)."""
     t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
     q_base = (w.q_shard * w.Sq if w.q_shard >= 0 else 0)
     kp = None if w.kv_pos is None else t(w.kv_pos[:, c * w.chunk:(c + 1) * w.chunk])
     ks = None if w.kv_seg is None else t(w.kv_seg[:, c * w.chunk:(c + 1) * w.chunk])
+    dv = None if dense is None else dense.view(-1)[c * w.chunk:]   # column c*chunk, row stride Skv
     return ram.MaskSrc(q_pos=t(w.q_pos), kv_pos=kp, q_pos_base=q_base, kv_pos_base=c * w.chunk,
-                       q_seg=t(w.q_seg), kv_seg=ks)
+                       q_seg=t(w.q_seg), kv_seg=ks, dense=dv, dense_ld=w.Skv if dense is not None else 0)
 
 
 def order(w):
@@ -71,13 +86,13 @@ def order(w):
     return [((w.q_shard - t) % N) if w.q_shard >= 0 else t for t in range(N)]
 
 
-def tile_counts(w, desc, dev, tile_q, tile_kv):
+def tile_counts(w, desc, dev, tile_q, tile_kv, dense=None):
     """Non-EMPTY tiles per chunk at (tile_q, tile_kv), from the library's block-mask builder."""
     counts = []
     for c in range(w.n_chunks):
         d = ram.Desc(**{**desc.__dict__, "block_q": tile_q, "block_kv": tile_kv})
         bm = ram.alloc_block_mask(d, device=dev)
-        ram.build_block_mask(d, ring_chunk_src(w, c, dev), bm)
+        ram.build_block_mask(d, ring_chunk_src(w, c, dev, dense), bm)
         torch.cuda.synchronize()
         counts.append(int(bm.row_cnt[: d.B * bm.nQb].sum().item()))
     return counts
@@ -114,6 +129,35 @@ def recorded_traffic(workload: str):
         return None
 
 
+def mask_builder_rate(w, desc, dense, bq, bk, dev, stream, reps):
+    """The block-mask builder alone over the whole dense mask (one launch, all Sq x Skv pairs,
+    at the kernel tile, bits stored), timed with HIP events on the stream it runs on.
+    Algorithmic bytes: the mask bytes of every 32-key word the causal test does not clear
+    (the builder reads no others), the bits of the PARTIAL tiles, and the classes and lists."""
+    d = ram.Desc(**{**desc.__dict__, "Skv": w.Skv, "block_q": bq, "block_kv": bk})
+    src = ram.MaskSrc(q_pos_base=w.q_shard * w.Sq if w.q_shard >= 0 else 0, dense=dense)
+    bm = ram.alloc_block_mask(d, device=dev, with_bits=True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ram.build_block_mask(d, src, bm, stream=stream)
+    a.record(stream)
+    for _ in range(reps):
+        ram.build_block_mask(d, src, bm, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / reps
+    q0 = src.q_pos_base
+    rows = np.arange(w.Sq, dtype=np.int64) + q0
+    read = int(np.minimum(w.Skv, ((rows + 1 + 31) // 32) * 32).clip(min=0).sum()) if w.causal else w.Sq * w.Skv
+    n_tiles = bm.nQb * bm.nKb
+    n_partial = int((bm.tile_class[:n_tiles] == ram.RAM_TILE_PARTIAL).sum().item())
+    nbytes = read + n_partial * bm.tile_words * 4 + n_tiles * 5 + bm.nQb * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"mask builder over [{w.Sq}, {w.Skv}]: {us:.1f} us, {gbs:.0f} GB/s of {nbytes / 1e6:.1f} MB")
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "block_mask_kernel", "launch_us": round(us, 1),
+            "bytes_per_launch": nbytes, "partial_tiles": n_partial, "tiles": n_tiles}
+
+
 def cpu_baseline(w, n_rows: int):
     import oracle
     from threadpoolctl import threadpool_info
@@ -122,12 +166,13 @@ def cpu_baseline(w, n_rows: int):
     qp, kp = w.positions()
     t0 = time.perf_counter()
     oracle.attention(q, k, v, scale=w.scale, q_pos=qp, kv_pos=kp, q_seg=w.q_seg, kv_seg=w.kv_seg,
-                     causal=w.causal, softcap=w.softcap, sinks=sinks, rows=rows)
+                     causal=w.causal, softcap=w.softcap, sinks=sinks, dense=w.dense, rows=rows)
     dt = time.perf_counter() - t0
     pairs = 0
     for b in range(w.B):
         ok = oracle.allowed(qp[b, rows], kp[b], None if w.q_seg is None else w.q_seg[b, rows],
-                            None if w.kv_seg is None else w.kv_seg[b], w.causal)
+                            None if w.kv_seg is None else w.kv_seg[b], w.causal,
+                            None if w.dense is None else w.dense[rows])
         pairs += int(ok.sum())
     flops = 4.0 * w.D * w.H * pairs
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -141,7 +186,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c5", choices=["c5", "c4", "c4mqa", "c3", "c2"])
+    ap.add_argument("--workload", default="c5", choices=["c5", "c4", "c4mqa", "c3", "c2", "c5dense"])
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -165,13 +210,15 @@ def main():
     q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
     sinks = None if w.sinks is None else w.sinks.to(dev)
     t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
-    src = ram.MaskSrc(q_pos=t(w.q_pos), kv_pos=t(w.kv_pos), q_seg=t(w.q_seg), kv_seg=t(w.kv_seg))
+    dense = dense_tensor(w, dev)
+    src = ram.MaskSrc(q_pos=t(w.q_pos), kv_pos=t(w.kv_pos), q_seg=t(w.q_seg), kv_seg=t(w.kv_seg),
+                      dense=dense, dense_chunk_step=w.chunk if dense is not None else 0)
     out = torch.empty_like(q)
     lse = torch.empty(w.B, w.H, w.Sq, dtype=torch.float32, device=dev)
-    ws = torch.empty(ram.ring_attn_workspace_bytes(desc, w.n_chunks), dtype=torch.uint8, device=dev)
+    ws = torch.empty(ram.ring_attn_workspace_bytes(desc, w.n_chunks, src), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    ref_tiles = tile_counts(w, desc, dev, REF_TILE, REF_TILE)
+    ref_tiles = tile_counts(w, desc, dev, REF_TILE, REF_TILE, dense)
     eff_flops_chunk = [4.0 * w.D * w.H * n * REF_TILE * REF_TILE for n in ref_tiles]
     eff_flops = sum(eff_flops_chunk)
     log(f"non-empty {REF_TILE}x{REF_TILE} tiles per chunk: {ref_tiles}; effective FLOPs {eff_flops:.4e}")
@@ -198,8 +245,8 @@ def main():
     dk = ram.Desc(**{**desc.__dict__, "block_q": bq, "block_kv": bk, "kv_stride_b": w.Skv * w.Hkv * w.D})
     masks, srcs = [], []
     for c in range(w.n_chunks):
-        srcs.append(ring_chunk_src(w, c, dev))
-        bm = ram.alloc_block_mask(dk, device=dev)
+        srcs.append(ring_chunk_src(w, c, dev, dense))
+        bm = ram.alloc_block_mask(dk, device=dev, with_bits=dense is not None)
         ram.build_block_mask(dk, srcs[c], bm)
         masks.append(bm)
     acc = torch.empty(w.B, w.Sq, w.H, w.D, dtype=torch.float32, device=dev)
@@ -228,10 +275,11 @@ def main():
     log("chunk kernel ms (visit order): " + ", ".join(f"{x:.3f}" for x in per_chunk_ms))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(args.workload),
-                "kernel": ATTN_KERNEL,
+                "kernel": ATTN_KERNEL if dense is None else ATTN_KERNEL_BITS,
                 "launches_per_step": w.n_chunks, "mean_launch_us": round(1e3 * kern_ms / w.n_chunks, 2),
                 "flops_per_launch_mean": sum(eff_flops_chunk) / w.n_chunks}
-    del acc, acc_lse
+    del acc, acc_lse, masks
+    builder = None if dense is None else mask_builder_rate(w, desc, dense, bq, bk, dev, stream, reps)
     if args.copy_calibration:
         a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
         b2 = torch.empty_like(a)
@@ -258,6 +306,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if builder is not None:
+        line["mask_builder"] = builder
     print(json.dumps(line), flush=True)
 
 

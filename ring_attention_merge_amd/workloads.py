@@ -61,6 +61,7 @@ class Workload:
     kv_pos: Optional[np.ndarray] = None
     q_seg: Optional[np.ndarray] = None
     kv_seg: Optional[np.ndarray] = None
+    dense: Optional[np.ndarray] = None   # uint8 [Sq, n_chunks*chunk], one mask over all keys
     meta: dict = field(default_factory=dict)
 
     @property
@@ -133,10 +134,13 @@ def dense_mask(rng, Sq: int, Skv: int, *, q_offset: int = 0, window: int = 256, 
     Draw order: the cell picks, the all-ones / random choice per cell, the
     element draws of the random cells (row-major), then the dead rows.
     """
-    i = np.arange(Sq)[:, None] + q_offset
-    j = np.arange(Skv)[None, :]
-    m = np.abs(i - j) < window
-    m |= j < n_global
+    m = np.zeros((Sq, Skv), dtype=bool)
+    for i in range(Sq):                       # band, row by row (no [Sq, Skv] temporaries)
+        c = q_offset + i
+        lo, hi = max(0, c - window + 1), min(Skv, c + window)
+        if lo < hi:
+            m[i, lo:hi] = True
+    m[:, :min(n_global, Skv)] = True
     nbq, nbk = -(-Sq // block), -(-Skv // block)
     pick = rng.random((nbq, nbk)) < p_block
     rand_cell = rng.random((nbq, nbk)) < 0.5
@@ -149,7 +153,7 @@ def dense_mask(rng, Sq: int, Skv: int, *, q_offset: int = 0, window: int = 256, 
             m[r0:r1, c0:c1] = True
     if dead_rows and Sq:
         m[rng.choice(Sq, size=min(dead_rows, Sq), replace=False)] = False
-    return m.astype(np.uint8)
+    return m.view(np.uint8)
 
 
 def make(name: str, *, B: int, H: int, Hkv: int, Sq: int, chunk: int, n_chunks: int, D: int,
@@ -225,6 +229,19 @@ def c5_long_causal(S: int = 32768, H: int = 32, Hkv: int = 8, n_chunks: int = 8,
     """Long-context causal, 8 sequential chunks merged by LSE, v ~ U(-1, 1)."""
     return make(f"c5_long_causal_h{H}_hkv{Hkv}_s{S}", B=1, H=H, Hkv=Hkv, Sq=S,
                 chunk=S // n_chunks, n_chunks=n_chunks, D=128, v_uniform=True, seed=seed)
+
+
+def c5_dense(S: int = 32768, H: int = 32, Hkv: int = 8, n_chunks: int = 8, seed: int = 1006) -> Workload:
+    """The long-context causal workload with a dense two-dimensional mask over all keys:
+    a band of 2048 around the diagonal, 256 global keys, 10% of the 512x512 cells picked
+    (half of them all ones, half with elements kept at p = 1/2) and 3 cleared rows, ANDed
+    with the causal test. The mask is drawn after q, k, v from the same generator."""
+    w = make(f"c5_dense_h{H}_hkv{Hkv}_s{S}", B=1, H=H, Hkv=Hkv, Sq=S, chunk=S // n_chunks,
+             n_chunks=n_chunks, D=128, v_uniform=True, seed=seed)
+    rng = np.random.default_rng(seed + 1_000_000)
+    w.dense = dense_mask(rng, S, S, window=2048, n_global=256, block=512, p_block=0.1, p_keep=0.5,
+                         dead_rows=3)
+    return w
 
 
 def sampled_rows(Sq: int, chunk: int, n: int = 256, seed: int = 1005) -> np.ndarray:

@@ -151,7 +151,7 @@ def test_chunk_dense(name, variant):
                               q_pos=qp, kv_pos=kp, q_seg=qs, kv_seg=ks, causal=causal, softcap=cap,
                               sinks=None if sinks is None else sinks.double().numpy(), dense=dense)
     assert (~dense.any(axis=1)).any(), "no cleared row exercised"
-    compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, dt, name)
+    compare(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, dt, "dense chunk " + name)
 
 
 # ------------------------------------------------------------------------------ ring
@@ -194,7 +194,7 @@ def test_ring_dense(name):
     ro, rl = oracle.chunked(q, k, v, scale=w.scale, q_pos=qp, kv_pos=kp,
                             bounds=[(c * C, (c + 1) * C) for c in range(n)], order=order, causal=causal,
                             softcap=cap, sinks=s64, dense=dense, dense_col0=[c * step for c in range(n)])
-    compare(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, dt, name)
+    compare(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, dt, "dense ring " + name)
 
 
 def test_ring_dense_c2_shape_sampled():
