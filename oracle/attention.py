@@ -11,6 +11,8 @@ Sources (the pages):
   [kvax]  "Kvax: Flash Attention for JAX" page: flash_attention and
           create_attention_mask arguments ([B,S,H,D] layouts, positions and
           segment IDs, padding segment, scale).
+  [bwd]   the same page's _ring_attention_backward: the chunk backward per ring
+          step against the final out and logsumexp, gradients summed.
   [make]  the ring-splash page's make_ring_attention: a two-dimensional
           boolean mask over (query, key) given by the caller, turned into the
           block mask and partial-block contents of MaskInfo.
@@ -187,3 +189,113 @@ def chunked(q, k, v, *, scale, q_pos, kv_pos, bounds, order, q_seg=None, kv_seg=
                              sinks=sinks if t == 0 else None, rows=rows)
         acc, acc_lse = merge(acc, acc_lse, o_c, l_c)
     return acc, acc_lse
+
+
+def attention_bwd(q, k, v, dout, *, scale, q_pos, kv_pos, q_seg=None, kv_seg=None, causal=True,
+                  softcap=None, sinks=None, dense=None, out=None, lse=None, row_block=512):
+    """Gradients of ``attention`` with respect to q, k, v and the sinks, in float64.
+
+    [ring] _ring_attention_backward runs the chunk kernel's backward once per ring
+    step with the final ``out`` and ``logsumexp`` as residuals and sums the chunk
+    gradients. This function is the gradient of the forward defined above, written
+    out from the full score matrix (no tiling): for query row i of head h and an
+    allowed key j (KV head g),
+        t_ij = tanh(s_ij / cap) with s_ij = scale * q_i.k_j;  u_ij = cap * t_ij  (u = s uncapped)
+        p_ij = exp(u_ij - lse_i),      p_sink,i = exp(sink_h - lse_i)
+        dp_ij = dout_i . v_j,          D_i = dout_i . out_i
+        du_ij = p_ij (dp_ij - D_i),    ds_ij = du_ij (1 - t_ij^2)   (ds = du uncapped)
+        dq_i  = scale * sum_j ds_ij k_j
+        dk_j += scale * sum_i ds_ij q_i      (summed over the heads sharing KV head g)
+        dv_j += sum_i p_ij dout_i            (likewise)
+        dsink_h = - sum over batch rows and queries of p_sink,i * D_i
+    ``out`` / ``lse`` default to this module's forward on the same inputs; passing
+    the forward's stored results reproduces the pages' use of residuals. Rows with
+    lse = -inf contribute nothing. Returns (dq, dk, dv, dsinks) with dsinks None
+    when there are no sinks.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    dout = np.asarray(dout, np.float64)
+    B, Sq, H, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    G = H // Hkv
+    if out is None or lse is None:
+        out, lse = attention(q, k, v, scale=scale, q_pos=q_pos, kv_pos=kv_pos, q_seg=q_seg,
+                             kv_seg=kv_seg, causal=causal, softcap=softcap, sinks=sinks, dense=dense)
+    out = np.asarray(out, np.float64)
+    lse = np.asarray(lse, np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dsinks = None if sinks is None else np.zeros(H)
+    for b in range(B):
+        for start in range(0, Sq, row_block):
+            r = np.arange(start, min(Sq, start + row_block))
+            ok = allowed(np.asarray(q_pos)[b, r], np.asarray(kv_pos)[b],
+                         None if q_seg is None else np.asarray(q_seg)[b, r],
+                         None if kv_seg is None else np.asarray(kv_seg)[b], causal,
+                         None if dense is None else np.asarray(dense)[r])
+            for h in range(H):
+                g = h // G
+                l = lse[b, h, r]
+                live = np.isfinite(l)
+                l_safe = np.where(live, l, 0.0)
+                s = scale * (q[b, r, h, :] @ k[b, :, g, :].T)
+                if softcap is not None:
+                    t = np.tanh(s / softcap)
+                    u = softcap * t
+                else:
+                    u = s
+                p = np.where(ok & live[:, None], np.exp(u - l_safe[:, None]), 0.0)
+                do = dout[b, r, h, :]
+                dp = do @ v[b, :, g, :].T
+                Drow = np.sum(do * out[b, r, h, :], axis=1)
+                du = p * (dp - Drow[:, None])
+                ds = du * (1.0 - t * t) if softcap is not None else du
+                dq[b, r, h, :] = scale * (ds @ k[b, :, g, :])
+                dk[b, :, g, :] += scale * (ds.T @ q[b, r, h, :])
+                dv[b, :, g, :] += p.T @ do
+                if sinks is not None:
+                    ps = np.where(live, np.exp(float(sinks[h]) - l_safe), 0.0)
+                    dsinks[h] -= float(np.sum(ps * Drow))
+    return dq, dk, dv, dsinks
+
+
+def chunked_bwd(q, k, v, dout, *, scale, q_pos, kv_pos, bounds, q_seg=None, kv_seg=None, causal=True,
+                softcap=None, sinks=None, dense=None, dense_col0=None):
+    """The ring backward: per-chunk gradients against the final (out, lse), summed.
+
+    [ring] _ring_attention_backward: every step runs the chunk backward with the
+    final ``out`` and ``logsumexp`` of the whole ring as residuals; dq sums over the
+    steps, dk and dv belong to the chunk they were computed on. The chunk terms
+    are ``attention_bwd`` restricted to the chunk's keys with those residuals. The
+    sink term does not depend on the keys and is taken once (reading: the gradient
+    of a forward in which the sink enters once).
+    """
+    out, lse = chunked(q, k, v, scale=scale, q_pos=q_pos, kv_pos=kv_pos, bounds=bounds,
+                       order=list(range(len(bounds))), q_seg=q_seg, kv_seg=kv_seg, causal=causal,
+                       softcap=softcap, sinks=sinks, dense=dense, dense_col0=dense_col0)
+    q = np.asarray(q, np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros(np.shape(k))
+    dv = np.zeros(np.shape(v))
+    dsinks = None
+    for c, (a, e) in enumerate(bounds):
+        dense_c = None
+        if dense is not None:
+            c0 = a if dense_col0 is None else dense_col0[c]
+            dense_c = np.asarray(dense)[:, c0:c0 + (e - a)]
+        dq_c, dk_c, dv_c, ds_c = attention_bwd(
+            q, np.asarray(k)[:, a:e], np.asarray(v)[:, a:e], dout, scale=scale, q_pos=q_pos,
+            kv_pos=np.asarray(kv_pos)[:, a:e], q_seg=q_seg,
+            kv_seg=None if kv_seg is None else np.asarray(kv_seg)[:, a:e], causal=causal,
+            softcap=softcap, sinks=sinks if c == 0 else None, dense=dense_c, out=out, lse=lse)
+        dq += dq_c
+        dk[:, a:e] = dk_c
+        dv[:, a:e] = dv_c
+        if ds_c is not None:
+            dsinks = ds_c if dsinks is None else dsinks + ds_c
+    return dq, dk, dv, dsinks

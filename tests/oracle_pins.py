@@ -567,3 +567,117 @@ ALL_PINS = [pin_mask_value_constant, pin_finite_mask_equivalence, pin_bruteforce
             pin_closed_forms, pin_softcap, pin_merge, pin_chunked_equals_full, pin_sink_once,
             pin_gqa_repeat, pin_packed_docs, pin_ring_offsets, pin_block_mask, pin_dense_mask,
             pin_dense_chunked, pin_partial_bits]
+
+
+# ---------------------------------------------------------------------------- backward
+def _torch_forward(q, k, v, scale, ok, cap, sinks):
+    """The forward written in torch (float64) for autograd: [B,Sq,H,D] layouts, ok [B,Sq,Skv].
+    Masked pairs are dropped with torch.where (no -inf enters exp), so rows with nothing
+    allowed give zeros without NaN."""
+    H, Hkv = q.shape[2], k.shape[2]
+    kr = k.repeat_interleave(H // Hkv, dim=2)
+    vr = v.repeat_interleave(H // Hkv, dim=2)
+    s = scale * torch.matmul(q.permute(0, 2, 1, 3), kr.permute(0, 2, 3, 1))      # [B,H,Sq,Skv]
+    if cap is not None:
+        s = cap * torch.tanh(s / cap)
+    okb = ok[:, None].expand_as(s)
+    m = torch.where(okb, s, torch.full_like(s, -math.inf)).amax(dim=-1, keepdim=True)
+    if sinks is not None:
+        m = torch.maximum(m, sinks[None, :, None, None].expand_as(m))
+    m = torch.where(torch.isfinite(m), m, torch.zeros_like(m)).detach()
+    e = torch.where(okb, torch.exp(s - m), torch.zeros_like(s))
+    z = e.sum(dim=-1, keepdim=True)
+    if sinks is not None:
+        z = z + torch.exp(sinks[None, :, None, None] - m)
+    p = e / torch.where(z > 0, z, torch.ones_like(z))
+    return torch.matmul(p, vr.permute(0, 2, 1, 3)).permute(0, 2, 1, 3)
+
+
+def pin_bwd_autograd(ora):
+    """Backward = torch autograd of an independent torch forward (float64), with GQA, caps,
+    sinks, segments with padding, shuffled positions, dense masks and empty rows."""
+    rng = np.random.default_rng(26)
+    for trial in range(10):
+        B, Hkv = 1 + trial % 2, int(rng.choice([1, 2]))
+        H = Hkv * int(rng.choice([1, 2, 3]))
+        Sq, Skv, D = int(rng.integers(5, 40)), int(rng.integers(5, 40)), int(rng.choice([4, 8]))
+        segs = trial >= 5
+        q, k, v, qp, kp, qs, ks = _rand_problem(rng, B, Sq, Skv, H, Hkv, D, segs=segs,
+                                                shuffle_pos=trial % 3 == 1, pad=segs)
+        causal = trial % 4 != 3
+        cap = 2.5 if trial % 2 else None
+        sinks = rng.standard_normal(H) if trial % 3 != 2 else None
+        dense = (rng.random((Sq, Skv)) < 0.7) if trial in (2, 5, 6, 9) else None
+        if dense is not None:
+            dense[Sq // 2] = False                               # an empty row
+        ok = np.stack([ora.allowed(qp[b], kp[b], None if qs is None else qs[b], None if ks is None else ks[b],
+                                   causal, dense) for b in range(B)])
+        dout = rng.standard_normal(q.shape)
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+        ts = None if sinks is None else torch.from_numpy(sinks).requires_grad_()
+        o = _torch_forward(tq, tk, tv, 0.4, torch.from_numpy(ok), cap, ts)
+        (o * torch.from_numpy(dout)).sum().backward()
+        dq, dk, dv, dsk = ora.attention_bwd(q, k, v, dout, scale=0.4, q_pos=qp, kv_pos=kp, q_seg=qs,
+                                            kv_seg=ks, causal=causal, softcap=cap, sinks=sinks, dense=dense)
+        _close(dq, tq.grad.numpy(), 1e-10, f"autograd dq {trial}")
+        _close(dk, tk.grad.numpy(), 1e-10, f"autograd dk {trial}")
+        _close(dv, tv.grad.numpy(), 1e-10, f"autograd dv {trial}")
+        if sinks is not None:
+            _close(dsk, ts.grad.numpy(), 1e-10, f"autograd dsinks {trial}")
+        assert np.abs(dq).max() > 0 and np.abs(dk).max() > 0
+
+
+def pin_bwd_finite_differences(ora):
+    """Central differences of L = sum(out * dout) through the oracle's own (pinned) forward."""
+    rng = np.random.default_rng(27)
+    B, Sq, Skv, H, Hkv, D = 1, 4, 5, 2, 1, 3
+    q, k, v, qp, kp, _, _ = _rand_problem(rng, B, Sq, Skv, H, Hkv, D, shuffle_pos=True)
+    sinks = rng.standard_normal(H)
+    dout = rng.standard_normal(q.shape)
+    kw = dict(scale=0.6, q_pos=qp, kv_pos=kp, causal=True, softcap=1.5)
+    loss = lambda q_, k_, v_, s_: float(np.sum(ora.attention(q_, k_, v_, sinks=s_, **kw)[0] * dout))
+    dq, dk, dv, dsk = ora.attention_bwd(q, k, v, dout, sinks=sinks, **kw)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv), ("sinks", sinks, dsk)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps; xm[idx] -= eps
+            args_p = [q, k, v, sinks]; args_m = [q, k, v, sinks]
+            pos = ("q", "k", "v", "sinks").index(name)
+            args_p[pos], args_m[pos] = xp, xm
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        _close(g, num, 1e-7, f"finite differences d{name}")
+
+
+def pin_bwd_chunked_and_gqa(ora):
+    """Ring backward (chunk terms against the final out / lse, summed) = whole-KV backward, the
+    sink counted once; GQA gradients = repeated-KV gradients summed over each group."""
+    rng = np.random.default_rng(28)
+    for trial in range(4):
+        B, Sq, H, Hkv, D = 1 + trial % 2, 18 + trial, 4, 2, 6
+        Skv = int(rng.integers(30, 50))
+        q, k, v, qp, kp, qs, ks = _rand_problem(rng, B, Sq, Skv, H, Hkv, D, segs=trial >= 2, pad=trial >= 2)
+        cap = 3.0 if trial % 2 else None
+        sinks = rng.standard_normal(H)
+        dense = rng.random((Sq, Skv)) < 0.8 if trial == 3 else None
+        dout = rng.standard_normal(q.shape)
+        cuts = np.sort(rng.choice(np.arange(1, Skv), size=2, replace=False))
+        bounds = [(0, int(cuts[0])), (int(cuts[0]), int(cuts[1])), (int(cuts[1]), Skv)]
+        kw = dict(scale=0.5, q_pos=qp, kv_pos=kp, q_seg=qs, kv_seg=ks, softcap=cap, sinks=sinks, dense=dense)
+        ref = ora.attention_bwd(q, k, v, dout, **kw)
+        got = ora.chunked_bwd(q, k, v, dout, bounds=bounds, **kw)
+        for name, a, b_ in zip(("dq", "dk", "dv", "dsinks"), got, ref):
+            _close(a, b_, 1e-11, f"chunked {name} {trial}")
+    q, k, v, qp, kp, qs, ks = _rand_problem(rng, 1, 20, 26, 6, 2, 4, segs=True, pad=True)
+    dout = rng.standard_normal(q.shape)
+    kw = dict(scale=0.5, q_pos=qp, kv_pos=kp, q_seg=qs, kv_seg=ks, softcap=2.0, sinks=rng.standard_normal(6))
+    g1 = ora.attention_bwd(q, k, v, dout, **kw)
+    g2 = ora.attention_bwd(q, np.repeat(k, 3, axis=2), np.repeat(v, 3, axis=2), dout, **kw)
+    _close(g1[0], g2[0], 1e-12, "gqa dq")
+    _close(g1[1], g2[1].reshape(1, 26, 2, 3, 4).sum(axis=3), 1e-12, "gqa dk")
+    _close(g1[2], g2[2].reshape(1, 26, 2, 3, 4).sum(axis=3), 1e-12, "gqa dv")
+    _close(g1[3], g2[3], 1e-12, "gqa dsinks")
+
+
+ALL_PINS += [pin_bwd_autograd, pin_bwd_finite_differences, pin_bwd_chunked_and_gqa]

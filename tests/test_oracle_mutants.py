@@ -14,13 +14,15 @@ import oracle_pins
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 ATTN_MUTANTS = {
-    "gqa_modulo": ("g = h // G", "g = h % Hkv"),
+    "gqa_modulo": ("g = h // G\n                s = scale", "g = h % Hkv\n                s = scale"),
     "causal_strict": ("kv_pos[None, :] <= q_pos[:, None]", "kv_pos[None, :] < q_pos[:, None]"),
     "causal_reversed": ("kv_pos[None, :] <= q_pos[:, None]", "kv_pos[None, :] >= q_pos[:, None]"),
     "pad_attended": ("ok &= (q_seg != PAD_SEGMENT_ID)[:, None]", "pass"),
     "segment_compare": ("q_seg[:, None] == kv_seg[None, :]", "q_seg[:, None] >= kv_seg[None, :]"),
-    "scale_dropped": ("s = scale * (", "s = ("),
-    "k_v_swapped": ("@ k[b, :, g, :].T", "@ v[b, :, g, :].T"),
+    "scale_dropped": ("s = scale * (q[b, r, h, :] @ k[b, :, g, :].T)\n                if softcap is not None:\n                    s = softcap",
+                      "s = (q[b, r, h, :] @ k[b, :, g, :].T)\n                if softcap is not None:\n                    s = softcap"),
+    "k_v_swapped": ("@ k[b, :, g, :].T)\n                if softcap is not None:\n                    s = softcap",
+                    "@ v[b, :, g, :].T)\n                if softcap is not None:\n                    s = softcap"),
     "cap_factor_dropped": ("s = softcap * np.tanh(s / softcap)", "s = np.tanh(s / softcap)"),
     "sink_every_chunk": ("sinks=sinks if t == 0 else None", "sinks=sinks"),
     "sink_ignored": ("if sinks is not None:\n                    s = np.concatenate",
@@ -32,9 +34,19 @@ ATTN_MUTANTS = {
     "normaliser_off": ("o[nz] = num[nz] / z[nz, None]", "o[nz] = num[nz] / (z[nz, None] + 1e-3)"),
     "dense_ignored": ("ok &= dense != 0", "pass"),
     "dense_inverted": ("ok &= dense != 0", "ok &= dense == 0"),
-    "dense_col0_ignored": ("c0 = a if dense_col0 is None else dense_col0[c]", "c0 = a"),
-    "dense_from_first_column": ("c0 = a if dense_col0 is None else dense_col0[c]",
-                                "c0 = 0 if dense_col0 is None else dense_col0[c]"),
+    "dense_col0_ignored": ("c0 = a if dense_col0 is None else dense_col0[c]\n            dense_c = np.asarray(dense)[:, c0:c0 + (e - a)]\n        o_c",
+                           "c0 = a\n            dense_c = np.asarray(dense)[:, c0:c0 + (e - a)]\n        o_c"),
+    "dense_from_first_column": ("c0 = a if dense_col0 is None else dense_col0[c]\n            dense_c = np.asarray(dense)[:, c0:c0 + (e - a)]\n        o_c",
+                                "c0 = 0 if dense_col0 is None else dense_col0[c]\n            dense_c = np.asarray(dense)[:, c0:c0 + (e - a)]\n        o_c"),
+    "bwd_delta_dropped": ("du = p * (dp - Drow[:, None])", "du = p * dp"),
+    "bwd_cap_chain_dropped": ("ds = du * (1.0 - t * t) if softcap is not None else du", "ds = du"),
+    "bwd_dk_scale_dropped": ("dk[b, :, g, :] += scale * (ds.T @ q[b, r, h, :])", "dk[b, :, g, :] += ds.T @ q[b, r, h, :]"),
+    "bwd_dv_from_ds": ("dv[b, :, g, :] += p.T @ do", "dv[b, :, g, :] += ds.T @ do"),
+    "bwd_gqa_overwrite": ("dv[b, :, g, :] += p.T @ do", "dv[b, :, g, :] = p.T @ do"),
+    "bwd_sink_sign": ("dsinks[h] -= float(np.sum(ps * Drow))", "dsinks[h] += float(np.sum(ps * Drow))"),
+    "bwd_sink_every_chunk": ("sinks=sinks if c == 0 else None, dense=dense_c, out=out, lse=lse)",
+                             "sinks=sinks, dense=dense_c, out=out, lse=lse)"),
+    "bwd_chunk_local_lse": ("dense=dense_c, out=out, lse=lse)", "dense=dense_c, out=None, lse=None)"),
 }
 MASK_MUTANTS = {
     "no_empty_tiles": ("elif tile.any():", "elif True:"),
@@ -66,6 +78,7 @@ def _mutant(which, key):
         m = _load(mask_path, "mut_blockmask", *MASK_MUTANTS[key])
     return types.SimpleNamespace(
         attention=a.attention, allowed=a.allowed, merge=a.merge, chunked=a.chunked,
+        attention_bwd=a.attention_bwd, chunked_bwd=a.chunked_bwd,
         DEFAULT_MASK_VALUE=a.DEFAULT_MASK_VALUE, block_mask=m.block_mask, partial_bits=m.partial_bits,
         TILE_EMPTY=m.TILE_EMPTY, TILE_PARTIAL=m.TILE_PARTIAL, TILE_FULL=m.TILE_FULL)
 
