@@ -17,6 +17,12 @@ roofline: the attention chunk kernel alone, timed launch by launch with HIP
 cpu_baseline: the float64 oracle on a bounded sample of query rows of the
        same workload (all heads, all keys), in pair FLOPs per second.
 
+--backward times ring_attn_bwd_1gpu instead (out and lse from one forward
+call before timing, dout ~ N(0,1) in bf16): value = 2.5x the forward's
+effective FLOPs (five products per pair: S, dP, dV, dK, dQ) per second; the
+roofline leg times each chunk's attn_bwd_chunk call (its dq and dk/dv
+kernels) with HIP events, against the same FLOPs.
+
 --workload c5dense runs the same shape with a dense two-dimensional mask over
 all keys (ANDed with the causal test): the step then also classifies every
 pair of the mask, the chunk kernel masks PARTIAL tiles from their stored bits,
@@ -43,6 +49,8 @@ import ring_attention_merge_amd as ram  # noqa: E402
 from ring_attention_merge_amd import workloads as wl  # noqa: E402
 
 METRIC = "effective attention fwd TFLOP/s (unmasked tiles) and % bf16 MFMA peak, 1 GPU"
+METRIC_BWD = "effective attention bwd TFLOP/s (unmasked tiles, 2.5x fwd FLOPs) and % bf16 MFMA peak, 1 GPU"
+BWD_FLOP_FACTOR = 2.5
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 REF_TILE = 128                  # fixed reference tiling for effective FLOPs
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
@@ -129,6 +137,115 @@ def recorded_traffic(workload: str):
         return None
 
 
+def backward(args, w, desc, q, k, v, src, sinks, out, lse, ws, stream, dense, eff_flops_chunk, fwd_step):
+    """The --backward leg: ring_attn_bwd_1gpu steps, then each chunk's attn_bwd_chunk timed alone."""
+    dev = q.device
+    fwd_step()
+    dout = torch.from_numpy(np.random.default_rng(4242).standard_normal(tuple(q.shape), dtype=np.float32)).to(
+        torch.bfloat16).to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsinks = None if sinks is None else torch.empty(w.H, dtype=torch.float32, device=dev)
+    del ws
+    wsb = torch.empty(ram.ring_attn_bwd_workspace_bytes(desc, w.n_chunks, src), dtype=torch.uint8, device=dev)
+    eff = BWD_FLOP_FACTOR * sum(eff_flops_chunk)
+
+    def bstep():
+        ram.ring_attn_bwd_1gpu(desc, w.n_chunks, w.q_shard, q, k, v, out, lse, dout, src, sinks, dq, dk, dv, dsinks,
+                               wsb, stream=stream)
+
+    for _ in range(args.warmup):
+        bstep()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        bstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = eff / (ms * 1e-3) / 1e12
+    log(f"backward step {ms:.3f} ms, {tflops:.1f} effective TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak)")
+    del wsb
+
+    # roofline leg: each chunk's backward call alone (dq written on the first visit, added after)
+    bq, bk = ram.kernel_tile(ram.RAM_BF16, w.D)
+    dkd = ram.Desc(**{**desc.__dict__, "block_q": bq, "block_kv": bk, "kv_stride_b": w.Skv * w.Hkv * w.D})
+    delta = torch.empty(w.B, w.H, w.Sq, dtype=torch.float32, device=dev)
+    ram.attn_bwd_prep(dkd, out, dout, lse, sinks, delta, dsinks, stream=stream)
+    dq32 = torch.empty(w.B, w.Sq, w.H, w.D, dtype=torch.float32, device=dev)
+    dk32 = torch.empty(w.B, w.Skv, w.Hkv, w.D, dtype=torch.float32, device=dev)
+    dv32 = torch.empty_like(dk32)
+    kv_elems = w.chunk * w.Hkv * w.D
+    masks, srcs = [], []
+    for c in range(w.n_chunks):
+        srcs.append(ring_chunk_src(w, c, dev, dense))
+        bm = ram.alloc_block_mask(dkd, device=dev, with_bits=dense is not None, with_cols=True)
+        ram.build_block_mask(dkd, srcs[c], bm, stream=stream)
+        masks.append(bm)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.n_chunks)]
+    reps = max(1, args.steps // 2)
+    per_chunk_ms = [0.0] * w.n_chunks
+    for rep in range(reps + 1):
+        for t_, c in enumerate(order(w)):
+            a, b = evs[t_]
+            a.record(stream)
+            ram.attn_bwd_chunk(dkd, q, k.view(-1)[c * kv_elems:], v.view(-1)[c * kv_elems:], dout, lse, delta, srcs[c],
+                               masks[c], 0 if t_ == 0 else 1, dq32, dk32.view(-1)[c * kv_elems:],
+                               dv32.view(-1)[c * kv_elems:], stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        if rep > 0:
+            for t_ in range(w.n_chunks):
+                per_chunk_ms[t_] += evs[t_][0].elapsed_time(evs[t_][1]) / reps
+    kern_ms = sum(per_chunk_ms)
+    achieved = eff / (kern_ms * 1e-3) / 1e12
+    log("chunk backward ms (visit order): " + ", ".join(f"{x:.3f}" for x in per_chunk_ms))
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "attn_bwd_dq + attn_bwd_dkv (one attn_bwd_chunk call)",
+                "launches_per_step": w.n_chunks, "mean_launch_us": round(1e3 * kern_ms / w.n_chunks, 2),
+                "flops_per_launch_mean": eff / w.n_chunks}
+    line = {
+        "metric": METRIC_BWD, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "Hkv": w.Hkv, "Sq": w.Sq,
+                   "Skv": w.Skv, "kv_chunks": w.n_chunks, "chunk": w.chunk, "D": w.D, "causal": w.causal,
+                   "softcap": w.softcap, "sinks": w.sinks is not None, "q_shard": w.q_shard, "effective_flops": eff},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": None if args.no_cpu else cpu_baseline_bwd(w, min(args.cpu_rows, 256)),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_bwd(w, n_rows):
+    """The float64 oracle backward over n_rows sampled query rows (all heads, all keys): the gradients of
+    those rows' outputs, in the same 10*D FLOPs per allowed pair as the GPU's effective count."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    q, k, v, sinks = w.as_f64()
+    qp, kp = w.positions()
+    rows = wl.sampled_rows(w.Sq, w.chunk, n=n_rows, seed=2024)
+    dout = np.random.default_rng(4243).standard_normal((w.B, n_rows, w.H, w.D))
+    t0 = time.perf_counter()
+    oracle.attention_bwd(q[:, rows], k, v, dout, scale=w.scale, q_pos=qp[:, rows], kv_pos=kp,
+                         q_seg=None if w.q_seg is None else w.q_seg[:, rows], kv_seg=w.kv_seg, causal=w.causal,
+                         softcap=w.softcap, sinks=sinks, dense=None if w.dense is None else w.dense[rows])
+    dt = time.perf_counter() - t0
+    pairs = 0
+    for b in range(w.B):
+        ok = oracle.allowed(qp[b, rows], kp[b], None if w.q_seg is None else w.q_seg[b, rows],
+                            None if w.kv_seg is None else w.kv_seg[b], w.causal,
+                            None if w.dense is None else w.dense[rows])
+        pairs += int(ok.sum())
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    flops = 10.0 * w.D * w.H * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_rows} sampled of {w.Sq} query rows x all {w.H} heads x all {w.Skv} keys: float64 numpy "
+                      f"oracle backward (its forward included), {dt:.2f} s"}
+
+
 def mask_builder_rate(w, desc, dense, bq, bk, dev, stream, reps):
     """The block-mask builder alone over the whole dense mask (one launch, all Sq x Skv pairs,
     at the kernel tile, bits stored), timed with HIP events on the stream it runs on.
@@ -189,6 +306,7 @@ def main():
     ap.add_argument("--workload", default="c5", choices=["c5", "c4", "c4mqa", "c3", "c2", "c5dense"])
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--backward", action="store_true", help="time the ring backward instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (to scale FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -225,6 +343,9 @@ def main():
 
     def step():
         ram.ring_attn_fwd_1gpu(desc, w.n_chunks, w.q_shard, q, k, v, src, sinks, out, lse, ws, stream=stream)
+
+    if args.backward:
+        return backward(args, w, desc, q, k, v, src, sinks, out, lse, ws, stream, dense, eff_flops_chunk, step)
 
     for _ in range(args.warmup):
         step()

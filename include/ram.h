@@ -118,12 +118,18 @@ typedef struct {
  *              of the ring-splash page), one row of words per query row, key
  *              j of the tile at bit j % 32 of word j / 32, 0 past the
  *              sequence ends. Only PARTIAL tiles are written; the words of
- *              other tiles are left as they were. 8-byte aligned. */
+ *              other tiles are left as they were. 8-byte aligned;
+ *   col_cnt    int32 [B, nKb] or NULL, and
+ *   row_idx    int32 [B, nKb, nQb] or NULL (both or neither): the transposed
+ *              lists the backward walks (the ring-splash dkv MaskInfo): for
+ *              each kv tile, its non-EMPTY q tiles ascending, then -1. */
 typedef struct {
   uint8_t* tile_class;
   int32_t* row_cnt;
   int32_t* col_idx;
   uint32_t* bits;
+  int32_t* col_cnt;
+  int32_t* row_idx;
 } ram_block_mask;
 
 /* Tile classes and compacted non-empty tile lists from positions, segment
@@ -179,6 +185,51 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
                               const void* q, const void* k_all, const void* v_all,
                               const ram_mask_src* src, const float* sinks, void* out, float* lse,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- backward
+ * The ring-splash page's _ring_attention_backward: every ring step runs the
+ * chunk backward with the final out and logsumexp of the whole ring as
+ * residuals and sums the chunk gradients. For query row i and allowed key j:
+ *   p_ij = exp(s'_ij - lse_i) (s' the scaled, capped logit), D_i = dout_i . out_i,
+ *   ds_ij = p_ij (dout_i . v_j - D_i) (1 - t_ij^2 with a soft cap, t = s' / cap),
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,  dv_j = sum_i p_ij dout_i
+ * (dk, dv summed over the query heads sharing a KV head), and for a sink
+ *   dsink_h = - sum over batch rows and queries of exp(sink_h - lse_i) D_i,
+ * counted once (the sink enters the forward once). Built for bf16 with
+ * D = 128; other dtypes and head dims return RAM_ERR_UNSUPPORTED.
+ * out, dout: [B, Sq, H, D] dense in desc->dtype; lse: float32 [B, H, Sq] (as
+ * the forward wrote them). */
+
+/* delta[b,h,i] = dout[b,i,h,:] . out[b,i,h,:] (float32 [B, H, Sq]) and, when
+ * sinks is not NULL, dsinks (float32 [H]) as above. */
+ram_status attn_bwd_prep(const ram_attn_desc* desc, const void* out, const void* dout, const float* lse,
+                         const float* sinks, float* delta, float* dsinks, hipStream_t stream);
+
+/* Gradients of one chunk (the per-step call of _ring_attention_backward) with
+ * mask built by build_block_mask at ram_kernel_tile() including the transposed
+ * lists (and the bits when src->dense is set).
+ *   dq: float32 [B, Sq, H, D] dense; dq_mode RAM_OUT_WRITE stores the chunk's
+ *       dq, RAM_OUT_MERGE adds it to dq.
+ *   dk, dv: float32 with the layout and strides of k and v; written.
+ * Deterministic: no atomics. */
+ram_status attn_bwd_chunk(const ram_attn_desc* desc, const void* q, const void* k, const void* v,
+                          const void* dout, const float* lse, const float* delta, const ram_mask_src* src,
+                          const ram_block_mask* mask, int32_t dq_mode, float* dq, float* dk, float* dv,
+                          hipStream_t stream);
+
+/* The backward of ring_attn_fwd_1gpu with the same desc, n_chunks, q_shard,
+ * src and sinks: dq [B, Sq, H, D] dense, dk_all and dv_all with the layout of
+ * k_all and v_all, all in desc->dtype; dsinks float32 [H] (NULL when sinks is
+ * NULL). workspace: at least ring_attn_bwd_workspace_bytes(), 256-byte
+ * aligned (float32 accumulators, delta, and the block masks of every chunk). */
+ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32_t q_shard, const void* q,
+                              const void* k_all, const void* v_all, const void* out, const float* lse,
+                              const void* dout, const ram_mask_src* src, const float* sinks, void* dq,
+                              void* dk_all, void* dv_all, float* dsinks, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Workspace bytes ring_attn_bwd_1gpu needs (0 on bad input); src may be NULL. */
+size_t ring_attn_bwd_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src);
 
 /* Workspace bytes ring_attn_fwd_1gpu needs for this shape (0 on bad input).
  * src may be NULL; a source with a dense mask needs room for tile bits. */

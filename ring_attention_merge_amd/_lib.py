@@ -26,7 +26,8 @@ RAM_OUT_WRITE, RAM_OUT_MERGE = 0, 1
 RAM_PAD_SEGMENT_ID = -1
 
 EXPORTS = ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
-           "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_last_error")
+           "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_last_error", "attn_bwd_prep",
+           "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes")
 
 
 class RamError(RuntimeError):
@@ -55,7 +56,8 @@ class c_mask_src(ctypes.Structure):
 
 class c_block_mask(ctypes.Structure):
     _fields_ = [("tile_class", ctypes.c_void_p), ("row_cnt", ctypes.c_void_p),
-                ("col_idx", ctypes.c_void_p), ("bits", ctypes.c_void_p)]
+                ("col_idx", ctypes.c_void_p), ("bits", ctypes.c_void_p),
+                ("col_cnt", ctypes.c_void_p), ("row_idx", ctypes.c_void_p)]
 
 
 _lib = None
@@ -81,9 +83,17 @@ def load(path: str = LIB_PATH):
     lib.ring_attn_workspace_bytes.argtypes = [P(c_desc), i32, P(c_mask_src)]
     lib.ring_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.ram_kernel_tile.argtypes = [i32, i32, P(i32), P(i32)]
+    lib.attn_bwd_prep.argtypes = [P(c_desc), vp, vp, f32p, f32p, f32p, f32p, vp]
+    lib.attn_bwd_chunk.argtypes = [P(c_desc), vp, vp, vp, vp, f32p, f32p, P(c_mask_src), P(c_block_mask), i32,
+                                   f32p, f32p, f32p, vp]
+    lib.ring_attn_bwd_1gpu.argtypes = [P(c_desc), i32, i32, vp, vp, vp, vp, f32p, vp, P(c_mask_src), f32p, vp,
+                                       vp, vp, f32p, vp, ctypes.c_size_t, vp]
+    lib.ring_attn_bwd_workspace_bytes.argtypes = [P(c_desc), i32, P(c_mask_src)]
+    lib.ring_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ram_last_error.argtypes = []
     lib.ram_last_error.restype = ctypes.c_char_p
-    for name in ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu", "ram_kernel_tile"):
+    for name in ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu", "ram_kernel_tile",
+                 "attn_bwd_prep", "attn_bwd_chunk", "ring_attn_bwd_1gpu"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -162,6 +172,8 @@ class BlockMask:
     nKb: int = 0
     bits: Optional[torch.Tensor] = None
     tile_words: int = 0   # block_q * ceil(block_kv / 32)
+    col_cnt: Optional[torch.Tensor] = None
+    row_idx: Optional[torch.Tensor] = None
 
     def c(self, B: int) -> c_block_mask:
         _need(self.tile_class, "tile_class", torch.uint8, B * self.nQb * self.nKb)
@@ -169,19 +181,26 @@ class BlockMask:
         _need(self.col_idx, "col_idx", torch.int32, B * self.nQb * self.nKb)
         if self.bits is not None:
             _need(self.bits, "bits", torch.int32, B * self.nQb * self.nKb * self.tile_words)
-        return c_block_mask(_ptr(self.tile_class), _ptr(self.row_cnt), _ptr(self.col_idx), _ptr(self.bits))
+        if self.col_cnt is not None:
+            _need(self.col_cnt, "col_cnt", torch.int32, B * self.nKb)
+            _need(self.row_idx, "row_idx", torch.int32, B * self.nKb * self.nQb)
+        return c_block_mask(_ptr(self.tile_class), _ptr(self.row_cnt), _ptr(self.col_idx), _ptr(self.bits),
+                            _ptr(self.col_cnt), _ptr(self.row_idx))
 
 
-def alloc_block_mask(desc: Desc, device="cuda", with_bits: bool = False) -> BlockMask:
-    """Allocate the block-mask arrays for desc's shape and tile (and the tile bits)."""
+def alloc_block_mask(desc: Desc, device="cuda", with_bits: bool = False, with_cols: bool = False) -> BlockMask:
+    """Allocate the block-mask arrays for desc's shape and tile (and the tile bits, and the
+    transposed lists the backward walks)."""
     nQb = -(-desc.Sq // desc.block_q)
     nKb = -(-desc.Skv // desc.block_kv)
     n = max(1, desc.B * nQb * nKb)
     tw = desc.block_q * (-(-desc.block_kv // 32))
     bits = torch.zeros(n * tw, dtype=torch.int32, device=device) if with_bits else None
+    cc = torch.empty(max(1, desc.B * nKb), dtype=torch.int32, device=device) if with_cols else None
+    ri = torch.empty(n, dtype=torch.int32, device=device) if with_cols else None
     return BlockMask(torch.empty(n, dtype=torch.uint8, device=device),
                      torch.empty(max(1, desc.B * nQb), dtype=torch.int32, device=device),
-                     torch.empty(n, dtype=torch.int32, device=device), nQb, nKb, bits, tw)
+                     torch.empty(n, dtype=torch.int32, device=device), nQb, nKb, bits, tw, cc, ri)
 
 
 # ------------------------------------------------------------------------------ helpers
@@ -287,3 +306,73 @@ def ring_attn_fwd_1gpu(desc: Desc, n_chunks: int, q_shard: int, q, k_all, v_all,
     _check(load().ring_attn_fwd_1gpu(ctypes.byref(cd), n_chunks, q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
                                      ctypes.byref(cs), _ptr(sinks), _ptr(out), _ptr(lse), _ptr(workspace),
                                      workspace.numel(), _stream(stream)))
+
+
+# ------------------------------------------------------------------------------ backward
+def attn_bwd_prep(desc: Desc, out, dout, lse, sinks, delta, dsinks, stream=None):
+    """attn_bwd_prep: delta = rowsum(dout * out) [B,H,Sq] and, with sinks, dsinks [H]."""
+    dt = _tdtype(desc.dtype)
+    n = desc.B * desc.Sq * desc.H * desc.D
+    _need(out, "out", dt, n)
+    _need(dout, "dout", dt, n)
+    _need(lse, "lse", torch.float32, desc.B * desc.H * desc.Sq)
+    _need(delta, "delta", torch.float32, desc.B * desc.H * desc.Sq)
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, desc.H)
+        _need(dsinks, "dsinks", torch.float32, desc.H)
+    cd = desc.c()
+    _check(load().attn_bwd_prep(ctypes.byref(cd), _ptr(out), _ptr(dout), _ptr(lse), _ptr(sinks), _ptr(delta),
+                                _ptr(dsinks), _stream(stream)))
+
+
+def attn_bwd_chunk(desc: Desc, q, k, v, dout, lse, delta, src: MaskSrc, mask: BlockMask, dq_mode: int, dq, dk, dv,
+                   stream=None):
+    """attn_bwd_chunk: float32 dq written (mode 0) or added (mode 1); float32 dk, dv written."""
+    dt = _tdtype(desc.dtype)
+    _need(q, "q", dt, _span(desc.B, desc.q_stride_b, desc.Sq * desc.H * desc.D))
+    _need(dout, "dout", dt, desc.B * desc.Sq * desc.H * desc.D)
+    _need(lse, "lse", torch.float32, desc.B * desc.H * desc.Sq)
+    _need(delta, "delta", torch.float32, desc.B * desc.H * desc.Sq)
+    _need(dq, "dq", torch.float32, desc.B * desc.Sq * desc.H * desc.D)
+    kvn = _span(desc.B, desc.kv_stride_b, desc.Skv * desc.Hkv * desc.D)
+    if desc.Skv > 0:
+        for name, t, tt in (("k", k, dt), ("v", v, dt), ("dk", dk, torch.float32), ("dv", dv, torch.float32)):
+            _need(t, name, tt, kvn)
+    cd, cs, cb = desc.c(), src.c(desc.B, desc.Sq, desc.Skv), mask.c(desc.B)
+    _check(load().attn_bwd_chunk(ctypes.byref(cd), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
+                                 ctypes.byref(cs), ctypes.byref(cb), dq_mode, _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _stream(stream)))
+
+
+def ring_attn_bwd_workspace_bytes(desc: Desc, n_chunks: int, src: Optional[MaskSrc] = None) -> int:
+    cd = desc.c()
+    if src is None:
+        return int(load().ring_attn_bwd_workspace_bytes(ctypes.byref(cd), n_chunks, None))
+    cs = c_mask_src(0, 0, 0, 0, 0, 0, 0, 0, _ptr(src.dense), src.dense_ld, src.dense_chunk_step)
+    return int(load().ring_attn_bwd_workspace_bytes(ctypes.byref(cd), n_chunks, ctypes.byref(cs)))
+
+
+def ring_attn_bwd_1gpu(desc: Desc, n_chunks: int, q_shard: int, q, k_all, v_all, out, lse, dout, src: MaskSrc,
+                       sinks, dq, dk_all, dv_all, dsinks, workspace, stream=None):
+    """ring_attn_bwd_1gpu: gradients of ring_attn_fwd_1gpu (dq, dk_all, dv_all in the q dtype; dsinks float32)."""
+    dt = _tdtype(desc.dtype)
+    kv_len = n_chunks * desc.Skv
+    n = desc.B * desc.Sq * desc.H * desc.D
+    _need(q, "q", dt, _span(desc.B, desc.q_stride_b, desc.Sq * desc.H * desc.D))
+    for name, t in (("out", out), ("dout", dout), ("dq", dq)):
+        _need(t, name, dt, n)
+    _need(lse, "lse", torch.float32, desc.B * desc.H * desc.Sq)
+    if kv_len > 0:
+        kvn = _span(desc.B, desc.kv_stride_b, kv_len * desc.Hkv * desc.D)
+        for name, t in (("k_all", k_all), ("v_all", v_all), ("dk_all", dk_all), ("dv_all", dv_all)):
+            _need(t, name, dt, kvn)
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, desc.H)
+        _need(dsinks, "dsinks", torch.float32, desc.H)
+    _need(workspace, "workspace", torch.uint8, 0)
+    dense_cols = desc.Skv + (n_chunks - 1) * src.dense_chunk_step
+    cd, cs = desc.c(), src.c(desc.B, desc.Sq, kv_len, dense_cols)
+    _check(load().ring_attn_bwd_1gpu(ctypes.byref(cd), n_chunks, q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
+                                     _ptr(out), _ptr(lse), _ptr(dout), ctypes.byref(cs), _ptr(sinks), _ptr(dq),
+                                     _ptr(dk_all), _ptr(dv_all), _ptr(dsinks), _ptr(workspace), workspace.numel(),
+                                     _stream(stream)))

@@ -1,0 +1,697 @@
+// Block-sparse attention backward for one KV chunk, and its helpers.
+//
+// What it computes: the per-step call of the ejkernel ring-splash page's
+// _ring_attention_backward: the gradients of one chunk's attention given the
+// final out and logsumexp of the whole ring (so the chunk's weights are its
+// share of the global softmax). For query row i, allowed key j:
+//   p_ij = exp(u_ij - lse_i),  dp_ij = dout_i . v_j,  D_i = dout_i . out_i,
+//   ds_ij = p_ij (dp_ij - D_i) (1 - t_ij^2 with the soft cap, t = u / cap),
+//   dq_i += scale * sum_j ds_ij k_j,  dk_j = scale * sum_i ds_ij q_i,
+//   dv_j = sum_i p_ij dout_i   (dk, dv summed over the heads sharing a KV head).
+//
+// Design for gfx950 (bf16, D = 128; v_mfma_f32_32x32x16_bf16 throughout):
+//  * dq: one workgroup per (batch, head, 128-row q tile), the forward's layout:
+//    S^T = K Q^T and dP^T = V dO^T with Q and dO held in registers as B
+//    operands (a lane owns one query row), then dQ^T += K^T dS^T with dS^T
+//    going from the accumulator to the B operand in registers and K^T read
+//    from LDS with the transposing read. Walks the row's non-EMPTY kv tiles.
+//  * dk / dv: one workgroup per (batch, kv head, 64-key tile); a wave owns 32
+//    keys and one half of every 64-row q step, with K and V held in registers
+//    as B operands (a lane owns one key): S = Q K^T, dP = dO V^T, then
+//    dV^T += dO^T P and dK^T += Q^T dS with Q^T and dO^T read transposed from
+//    LDS. Walks the kv tile's non-EMPTY q tiles (the transposed tile lists)
+//    and every head of the KV group; the two waves of a key block add their
+//    halves through LDS at the end. No atomics anywhere: results are
+//    deterministic.
+//  * Tiles move HBM -> LDS by DMA. Every tile is read both row-wise and with
+//    the transposing read, so 16-byte chunks are swizzled by
+//    chunk ^ (4*(row & 3) + ((row >> 2) & 3)): 16 consecutive rows put one
+//    logical chunk in 16 distinct bank groups, and the 4 rows x 64 bytes of a
+//    transposing read cover all 64 banks.
+//  * Row values (lse, D) of rows past Sq or with lse = -inf become +inf / 0,
+//    so their weights are exactly 0.
+#include <cstdlib>
+#include <cstring>
+
+#include "attn_common.h"
+
+namespace ram {
+namespace {
+
+using namespace attn;
+
+constexpr int D = 128;
+constexpr int NDS = D / 16;
+constexpr int NDB = D / 32;
+constexpr int kTileElems = 64 * D;   // one 64-row tile (elements)
+
+__device__ __forceinline__ int swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+
+// Byte offsets of this lane's DMA chunks: wave w fills rows [16w, 16w + 16) of
+// a 64-row tile in four 4-row slabs; lane l of slab i writes physical chunk
+// l & 15 of row 16w + 4i + (l >> 4), fetched from the logical chunk at that
+// position. `row_bytes` is the global row stride.
+__device__ __forceinline__ void dma_offsets(uint32_t (&off)[4], int w, int lane, uint32_t row_bytes) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * i + (lane >> 4);
+    off[i] = (uint32_t)r * row_bytes + ((lane & 15) ^ swz(r)) * 16;
+  }
+}
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, __bf16* tile, const uint32_t (&off)[4], int w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(tile + (16 * w + 4 * i) * D),
+                                             16, off[i], 0, 0, 0);
+}
+
+// Row read (16 bytes): row `row`, logical chunk c.
+__device__ __forceinline__ bf16x8 lds_row(const char* tile, int row, int c) {
+  return *reinterpret_cast<const bf16x8*>(tile + row * 256 + ((c ^ swz(row)) * 16));
+}
+// Transposed operand of 32 columns x 16 rows starting at row r0, column block db:
+// lane receives column db*32 + (lane & 31) at rows r0 + 4*lg + 0..3 and r0 + 8 + 4*lg + 0..3.
+__device__ __forceinline__ bf16x8 lds_tr(const char* tile, int r0, int db, int lane) {
+  const int lg = lane >> 5, r4 = (lane & 15) >> 2, hs = (lane >> 4) & 1;
+  const int c = 4 * db + 2 * hs + ((lane & 3) >> 1);
+  const int ra = r0 + 4 * lg + r4, rb = ra + 8;
+  const char* pa = tile + ra * 256 + ((c ^ swz(ra)) * 16) + (lane & 1) * 8;
+  const char* pb = tile + rb * 256 + ((c ^ swz(rb)) * 16) + (lane & 1) * 8;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pa));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pb));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// The 16 accumulator values of a 32x32 block as two 16-deep bf16 B operands
+// (K index order matching lds_tr: 4*lg + 0..3, then 8 + 4*lg + 0..3).
+__device__ __forceinline__ void pack_b(const f32x16& S, bf16x8 (&P)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x2 two = {S[ks * 8 + 2 * j], S[ks * 8 + 2 * j + 1]};
+      bf16x2 pk = __builtin_convertvector(two, bf16x2);
+      P[ks][2 * j] = pk[0];
+      P[ks][2 * j + 1] = pk[1];
+    }
+}
+
+// Weights and score gradients of one 32x32 block in place: S (raw q.k, masked
+// entries -inf after capping) becomes dS = P (dP - D) (1 - t^2), and P is
+// returned in Pout. lse2 / dl per element (log2 units / D of the element's row).
+template <bool CAP>
+__device__ __forceinline__ void weights_and_grads(f32x16& S, const f32x16& dP, f32x16& Pout, const float (&lse2)[16],
+                                                  const float (&dl)[16], const AttnParams& p) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float pw, g = 1.0f;
+    if constexpr (CAP) {
+      pw = fast_exp2(S[i] - lse2[i]);
+      const float t = fmaxf(S[i], -p.cap_log2) * (1.0f / p.cap_log2);
+      g = __builtin_fmaf(-t, t, 1.0f);
+    } else {
+      pw = fast_exp2(__builtin_fmaf(S[i], p.scale_log2, -lse2[i]));
+    }
+    Pout[i] = pw;
+    S[i] = pw * (dP[i] - dl[i]) * g;
+  }
+}
+
+// ------------------------------------------------------------------------------ dq
+template <bool CAP, bool BITS>
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
+  const AttnParams& p = bp.a;
+  constexpr int BK = kBlockKV;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * kTileElems];   // [stage][K, V]
+
+  int b, h, qb;
+  if (!decode_work(p, b, h, qb)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, lg = lane >> 5;
+  const int G = p.H / p.Hkv;
+  const int g = h / G;
+  const int q_row = qb * kBlockQ + w * 32 + ln;
+  const bool q_ok = q_row < p.Sq;
+
+  const int64_t mrow = (int64_t)b * p.nQb + qb;
+  const int cnt = p.row_cnt[mrow];
+  if (cnt == 0 && bp.dq_mode == 1) return;   // adds nothing
+  const auto cols = as_const_space(p.col_idx + mrow * p.nKb);
+  const auto cls = as_const_space(p.tile_class + mrow * p.nKb);
+
+  // q and dout rows as B operands: lane holds row q_row, dims ds*16 + lg*8 .. +7
+  bf16x8 qf[NDS], dof[NDS];
+  {
+    const int64_t rq = (q_ok ? q_row : 0) * (int64_t)p.H + h;
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b + rq * D;
+    const __bf16* drow = reinterpret_cast<const __bf16*>(bp.dout) + ((int64_t)b * p.Sq * p.H + rq) * D;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(qrow + ds * 16 + lg * 8);
+      const bf16x8 c = *reinterpret_cast<const bf16x8*>(drow + ds * 16 + lg * 8);
+      qf[ds] = q_ok ? a : bf16x8{};
+      dof[ds] = q_ok ? c : bf16x8{};
+    }
+  }
+  const int qrow_c = q_ok ? q_row : p.Sq - 1;
+  const int qpos = p.q_pos ? p.q_pos[(int64_t)b * p.qm_stride_b + qrow_c] : p.q_pos_base + q_row;
+  const int qseg = p.q_seg ? p.q_seg[(int64_t)b * p.qm_stride_b + qrow_c] : 0;
+  float lse2 = __builtin_inff(), dl = 0.0f;
+  if (q_ok) {
+    const int64_t li = ((int64_t)b * p.H + h) * p.Sq + q_row;
+    const float l = p.lse[li];
+    if (l != neg_inf()) {
+      lse2 = l * kLog2e;
+      dl = bp.delta[li];
+    }
+  }
+  float lse2v[16], dlv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    lse2v[i] = lse2;
+    dlv[i] = dl;
+  }
+
+  f32x16 dQ[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dQ[db] = f32x16{};
+
+  const int64_t krs = (int64_t)p.Hkv * D;
+  const uint32_t row_bytes = (uint32_t)krs * 2;
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.kv_stride_b + g * D;
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.kv_stride_b + g * D;
+  uint32_t off[4];
+  dma_offsets(off, w, lane, row_bytes);
+  auto dma = [&](int kb, int buf) {
+    const int k0 = kb * BK;
+    const uint32_t bytes = (uint32_t)min(p.Skv - k0, BK) * row_bytes;
+    __bf16* Ks = smem + buf * 2 * kTileElems;
+    dma_tile(tile_rsrc(kbase + (int64_t)k0 * krs, bytes), Ks, off, w);
+    dma_tile(tile_rsrc(vbase + (int64_t)k0 * krs, bytes), Ks + kTileElems, off, w);
+  };
+  if (p.Skv % BK) {
+    // a ragged last tile leaves rows unwritten: start from zeros (finite, masked)
+    for (int i = tid; i < 2 * 2 * kTileElems / 8; i += kThreads)
+      reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  }
+
+  auto needs_mask = [&](int kb) {
+    const int c = cls[kb];
+    if constexpr (BITS)
+      if (c == 1) return 2;
+    return (c != 2 || (kb + 1) * BK > p.Skv) ? 1 : 0;
+  };
+  int kb_cur = cnt > 0 ? cols[0] : 0;
+  int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
+  int mk_cur = needs_mask(kb_cur);
+  if (cnt > 0) dma(kb_cur, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int it = 0; it < cnt; ++it) {
+    const int kb = kb_cur;
+    const int need_mask = mk_cur;
+    const int buf = it & 1;
+    if (it + 1 < cnt) dma(kb_nxt, buf ^ 1);
+    const char* Kt = reinterpret_cast<const char*>(smem + buf * 2 * kTileElems);
+    const char* Vt = Kt + kTileElems * 2;
+
+    // S^T = K Q^T and dP^T = V dO^T: A = key rows of K / V, B = q / dout in registers
+    f32x16 S[2], dP[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      S[kb2] = f32x16{};
+      dP[kb2] = f32x16{};
+    }
+    // in four phases of 8 operands each, so that few operands are live at once
+#pragma unroll
+    for (int ph = 0; ph < 4; ++ph) {
+      const char* T = (ph < 2) ? Kt : Vt;
+      bf16x8 a[4][2];
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) a[d4][kb2] = lds_row(T, kb2 * 32 + ln, 2 * ((ph & 1) * 4 + d4) + lg);
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const int ds = (ph & 1) * 4 + d4;
+          if (ph < 2) S[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4][kb2], qf[ds], S[kb2], 0, 0, 0);
+          else dP[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4][kb2], dof[ds], dP[kb2], 0, 0, 0);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (CAP) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
+    }
+    if (BITS && need_mask == 2)
+      apply_bits(S, p.mask_bits + ((mrow * p.nKb + kb) * kBlockQ + w * 32 + ln) * 2, lg);
+    else if (need_mask)
+      apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
+    bf16x8 DS[4];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      f32x16 Pw;
+      weights_and_grads<CAP>(S[kb2], dP[kb2], Pw, lse2v, dlv, p);
+      bf16x8 two[2];
+      pack_b(S[kb2], two);
+      DS[2 * kb2] = two[0];
+      DS[2 * kb2 + 1] = two[1];
+    }
+    // dQ^T += K^T dS^T: A = K read transposed (lane = dim), B = dS^T (lane = query)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr(Kt, ks * 16, db, lane), DS[ks], dQ[db], 0, 0, 0);
+
+    const int kb_nn = cols[min(it + 2, cnt - 1)];
+    const int mk_nxt = needs_mask(kb_nxt);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    kb_cur = kb_nxt;
+    kb_nxt = kb_nn;
+    mk_cur = mk_nxt;
+  }
+
+  if (!q_ok) return;
+  const float sc = p.scale_log2 * kLn2;   // the score scale
+  float* dq = bp.dq + (((int64_t)b * p.Sq + q_row) * p.H + h) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int col = db * 32 + 8 * i4 + 4 * lg;
+      float4 v = make_float4(dQ[db][4 * i4] * sc, dQ[db][4 * i4 + 1] * sc, dQ[db][4 * i4 + 2] * sc,
+                             dQ[db][4 * i4 + 3] * sc);
+      float4* ptr = reinterpret_cast<float4*>(dq + col);
+      if (bp.dq_mode == 1) {
+        const float4 a = *ptr;
+        v.x += a.x;
+        v.y += a.y;
+        v.z += a.z;
+        v.w += a.w;
+      }
+      *ptr = v;
+    }
+}
+
+// ------------------------------------------------------------------------------ dk, dv
+// Work decode: item order (batch * Hkv + kv head, kv tile ascending); XCD x =
+// id % 8 takes the contiguous item range [x*per, (x+1)*per).
+__device__ __forceinline__ bool decode_kv_work(const AttnParams& p, int& b, int& g, int& kb) {
+  const int64_t T = (int64_t)p.B * p.Hkv * p.nKb;
+  const int64_t per = (T + 7) / 8;
+  const int64_t id = blockIdx.x;
+  const int64_t item = (id & 7) * per + (id >> 3);
+  if (item >= T) return false;
+  kb = (int)(item % p.nKb);
+  const int64_t bg = item / p.nKb;
+  g = (int)(bg % p.Hkv);
+  b = (int)(bg / p.Hkv);
+  return true;
+}
+
+// Element mask of a 32-query x 32-key block with the key per lane: query of
+// register i is row q0 + 8*(i>>2) + 4*lg + (i&3) of the step (rows of the
+// step at qrow0 in the sequence). Positions / segments of the step's rows are
+// in LDS (qpos_s, qseg_s) when the call has such arrays.
+__device__ __forceinline__ void mask_kv(f32x16& S, const AttnParams& p, int key, int kpos, int kseg, int qrow0,
+                                        int q0, int lg, const int* qpos_s, const int* qseg_s) {
+  if (!p.q_pos && !p.kv_pos && !p.q_seg) {
+    // sequential positions: a query row r keeps the key iff r >= key + kv_base - q_base
+    const int64_t t64 = (int64_t)key + p.kv_pos_base - p.q_pos_base - (qrow0 + q0 + 4 * lg);
+    int thr = key < p.Skv ? (p.causal ? (int)max<int64_t>(-64, min<int64_t>(64, t64)) : -64) : 64;
+    asm volatile("" : "+v"(thr));
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (8 * (i >> 2) + (i & 3) < thr) S[i] = neg_inf();
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = q0 + 8 * (i >> 2) + 4 * lg + (i & 3);
+    bool ok = key < p.Skv;
+    if (p.causal) {
+      const int qp = p.q_pos ? qpos_s[r] : p.q_pos_base + qrow0 + r;
+      ok = ok && kpos <= qp;
+    }
+    if (p.q_seg) ok = ok && qseg_s[r] == kseg && kseg != -1;
+    if (!ok) S[i] = neg_inf();
+  }
+}
+
+// One workgroup per CU slot per SIMD: K, V (64 registers), the dK / dV
+// accumulators (128) and a step's products do not fit the 256 registers of
+// two waves per SIMD.
+template <bool CAP, bool BITS>
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkv(BwdParams bp) {
+  const AttnParams& p = bp.a;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * kTileElems];   // [stage][Q, dO]
+  __shared__ __attribute__((aligned(16))) float row_s[2][4][64];             // [stage][lse2, D, pos, seg]
+
+  int b, g, kb;
+  if (!decode_kv_work(p, b, g, kb)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, lg = lane >> 5;
+  const int kbw = w & 1, qh = w >> 1;        // key block and query half of this wave
+  const int G = p.H / p.Hkv;
+  const int key = kb * kBlockKV + 32 * kbw + ln;
+  const bool key_ok = key < p.Skv;
+
+  // K and V rows as B operands: lane holds key `key`, dims ds*16 + lg*8 .. +7
+  bf16x8 kt[NDS], vt[NDS];
+  {
+    const int64_t ro = (int64_t)b * p.kv_stride_b + ((int64_t)(key_ok ? key : 0) * p.Hkv + g) * D;
+    const __bf16* krow = reinterpret_cast<const __bf16*>(p.k) + ro;
+    const __bf16* vrow = reinterpret_cast<const __bf16*>(p.v) + ro;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + ds * 16 + lg * 8);
+      const bf16x8 c = *reinterpret_cast<const bf16x8*>(vrow + ds * 16 + lg * 8);
+      kt[ds] = key_ok ? a : bf16x8{};
+      vt[ds] = key_ok ? c : bf16x8{};
+    }
+  }
+  const int key_c = key_ok ? key : 0;
+  const int kpos = p.kv_pos ? p.kv_pos[(int64_t)b * p.kvm_stride_b + key_c] : p.kv_pos_base + key;
+  const int kseg = p.kv_seg ? p.kv_seg[(int64_t)b * p.kvm_stride_b + key_c] : 0;
+
+  f32x16 dK[NDB], dV[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dK[db] = f32x16{};
+    dV[db] = f32x16{};
+  }
+
+  const int64_t kcol = (int64_t)b * p.nKb + kb;
+  const int ccnt = bp.col_cnt[kcol];
+  const auto rows = as_const_space(bp.row_idx + kcol * p.nQb);
+  const int n_steps = ccnt * 2 * G;          // (q tile, 64-row half, head in group)
+
+  const uint32_t row_bytes = (uint32_t)p.H * D * 2;
+  uint32_t off[4];
+  dma_offsets(off, w, lane, row_bytes);
+  // Step t: q tile rows[t / (2G)], half (t / G) & 1, head g*G + t % G.
+  auto step_rows = [&](int t, int& qb, int& r0, int& h) {
+    qb = rows[t / (2 * G)];
+    r0 = qb * kBlockQ + ((t / G) & 1) * 64;
+    h = g * G + t % G;
+  };
+  auto stage = [&](int t, int buf) {
+    int qb, r0, h;
+    step_rows(t, qb, r0, h);
+    const int nrows = min(64, p.Sq - r0);
+    const uint32_t bytes = nrows > 0 ? (uint32_t)(nrows - 1) * row_bytes + D * 2 : 0u;
+    const int64_t rq = (int64_t)r0 * p.H + h;
+    __bf16* Qs = smem + buf * 2 * kTileElems;
+    dma_tile(tile_rsrc(reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b + rq * D, bytes), Qs, off, w);
+    dma_tile(tile_rsrc(reinterpret_cast<const __bf16*>(bp.dout) + ((int64_t)b * p.Sq * p.H + rq) * D, bytes),
+             Qs + kTileElems, off, w);
+  };
+  // Per-row values of a step (threads 0..63): lse in log2 units (+inf where the
+  // row has no weight), D, and positions / segments when the call has them.
+  auto row_values = [&](int t, float (&v)[4]) {
+    int qb, r0, h;
+    step_rows(t, qb, r0, h);
+    const int r = r0 + tid;
+    v[0] = __builtin_inff();
+    v[1] = 0.0f;
+    v[2] = 0.0f;
+    v[3] = 0.0f;
+    if (r < p.Sq) {
+      const int64_t li = ((int64_t)b * p.H + h) * p.Sq + r;
+      const float l = p.lse[li];
+      if (l != neg_inf()) {
+        v[0] = l * kLog2e;
+        v[1] = bp.delta[li];
+      }
+      if (p.q_pos) v[2] = __int_as_float(p.q_pos[(int64_t)b * p.qm_stride_b + r]);
+      if (p.q_seg) v[3] = __int_as_float(p.q_seg[(int64_t)b * p.qm_stride_b + r]);
+    }
+  };
+
+  if (n_steps > 0) {
+    stage(0, 0);
+    if (tid < 64) {
+      float v[4];
+      row_values(0, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) row_s[0][j][tid] = v[j];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_steps; ++t) {
+    const int buf = t & 1;
+    const bool has_next = t + 1 < n_steps;
+    float nv[4];
+    if (has_next) {
+      stage(t + 1, buf ^ 1);
+      if (tid < 64) row_values(t + 1, nv);
+    }
+    int qb, r0, h;
+    step_rows(t, qb, r0, h);
+    const int cl = p.tile_class[((int64_t)b * p.nQb + qb) * p.nKb + kb];
+    const int need_mask = (BITS && cl == 1) ? 2 : ((cl != 2 || (kb + 1) * kBlockKV > p.Skv) ? 1 : 0);
+    const char* Qt = reinterpret_cast<const char*>(smem + buf * 2 * kTileElems);
+    const char* Ot = Qt + kTileElems * 2;
+    const int q0 = 32 * qh;                  // this wave's first row in the step
+
+    // S = Q K^T and dP = dO V^T for 32 queries x 32 keys: A = query rows from LDS
+    f32x16 S = f32x16{}, dP = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(Qt, q0 + ln, 2 * ds + lg), kt[ds], S, 0, 0, 0);
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(Ot, q0 + ln, 2 * ds + lg), vt[ds], dP, 0, 0, 0);
+    }
+    if constexpr (CAP) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[i] = capped_log2(S[i], p.cap_k2, p.cap_log2);
+    }
+    const int* qpos_s = reinterpret_cast<const int*>(row_s[buf][2]);
+    const int* qseg_s = reinterpret_cast<const int*>(row_s[buf][3]);
+    if (BITS && need_mask == 2) {
+      // bits of the tile: row (step half * 64 + q0 + r), word kbw, bit ln
+      const uint32_t* tb = p.mask_bits + (((int64_t)b * p.nQb + qb) * p.nKb + kb) * kBlockQ * 2 +
+                           (int64_t)((r0 - qb * kBlockQ) + q0 + 4 * lg) * 2 + kbw;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (((tb[(8 * (i >> 2) + (i & 3)) * 2] >> ln) & 1u) == 0u) S[i] = neg_inf();
+    } else if (need_mask) {
+      mask_kv(S, p, key, kpos, kseg, r0, q0, lg, qpos_s, qseg_s);
+    }
+    float lse2v[16], dlv[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 a = *reinterpret_cast<const float4*>(&row_s[buf][0][q0 + 8 * j + 4 * lg]);
+      const float4 c = *reinterpret_cast<const float4*>(&row_s[buf][1][q0 + 8 * j + 4 * lg]);
+      lse2v[4 * j] = a.x;
+      lse2v[4 * j + 1] = a.y;
+      lse2v[4 * j + 2] = a.z;
+      lse2v[4 * j + 3] = a.w;
+      dlv[4 * j] = c.x;
+      dlv[4 * j + 1] = c.y;
+      dlv[4 * j + 2] = c.z;
+      dlv[4 * j + 3] = c.w;
+    }
+    f32x16 Pw;
+    weights_and_grads<CAP>(S, dP, Pw, lse2v, dlv, p);
+    bf16x8 Pb[2], DSb[2];
+    pack_b(Pw, Pb);
+    pack_b(S, DSb);
+    __builtin_amdgcn_sched_barrier(0);
+    // dV^T += dO^T P and dK^T += Q^T dS: A = dO / Q read transposed (lane = dim)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr(Ot, q0 + ks * 16, db, lane), Pb[ks], dV[db], 0, 0, 0);
+        dK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr(Qt, q0 + ks * 16, db, lane), DSb[ks], dK[db], 0, 0, 0);
+      }
+    if (has_next && tid < 64) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) row_s[buf ^ 1][j][tid] = nv[j];
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // The two query halves of each key block: waves 2, 3 hand theirs to waves 0, 1.
+  float* red = reinterpret_cast<float*>(smem);   // [key block][2 tensors][NDB][16][64 lanes]
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        red[(((kbw * 2 + 0) * NDB + db) * 16 + i) * 64 + lane] = dK[db][i];
+        red[(((kbw * 2 + 1) * NDB + db) * 16 + i) * 64 + lane] = dV[db][i];
+      }
+  }
+  __syncthreads();
+  if (qh == 1 || !key_ok) return;
+  const float sc = p.scale_log2 * kLn2;
+  const int64_t ro = (int64_t)b * bp.dkv_stride_b + ((int64_t)key * p.Hkv + g) * D;
+  float* dk = bp.dk + ro;
+  float* dv = bp.dv + ro;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int col = db * 32 + 8 * i4 + 4 * lg;
+      float a[4], c[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * i4 + e;
+        a[e] = (dK[db][i] + red[(((kbw * 2 + 0) * NDB + db) * 16 + i) * 64 + lane]) * sc;
+        c[e] = dV[db][i] + red[(((kbw * 2 + 1) * NDB + db) * 16 + i) * 64 + lane];
+      }
+      *reinterpret_cast<float4*>(dk + col) = make_float4(a[0], a[1], a[2], a[3]);
+      *reinterpret_cast<float4*>(dv + col) = make_float4(c[0], c[1], c[2], c[3]);
+    }
+}
+
+// ------------------------------------------------------------------------------ helpers
+// delta[b,h,i] = dout[b,i,h,:] . out[b,i,h,:]; 16 lanes per (row, head), 8 elements each.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(int64_t n_rows, int H, int Sq, int Dd, const T* out,
+                                                        const T* dout, const float* lse, float* delta) {
+  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int part = threadIdx.x & 15;
+  float acc = 0.0f;
+  if (pair < n_rows) {
+    const T* o = out + pair * Dd;
+    const T* d = dout + pair * Dd;
+    for (int e = part * 8; e < Dd; e += 128)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += (float)o[e + j] * (float)d[e + j];
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 16);
+  if (pair < n_rows && part == 0) {
+    // pair = (b*Sq + i)*H + h  ->  [b, h, i]
+    const int h = (int)(pair % H);
+    const int64_t bi = pair / H;
+    const int i = (int)(bi % Sq);
+    const int64_t bb = bi / Sq;
+    delta[(bb * H + h) * Sq + i] = acc;
+  }
+}
+
+// dsinks[h] = -sum over (b, i) of exp(sink_h - lse[b,h,i]) * delta[b,h,i] (rows
+// with lse = -inf have no weight); one workgroup per head, a fixed-order tree.
+__global__ __launch_bounds__(256) void bwd_dsinks_kernel(int B, int H, int Sq, const float* sinks, const float* lse,
+                                                         const float* delta, float* dsinks) {
+  __shared__ float red[256];
+  const int h = blockIdx.x;
+  const float s = sinks[h];
+  float acc = 0.0f;
+  for (int b = 0; b < B; ++b) {
+    const int64_t base = ((int64_t)b * H + h) * Sq;
+    for (int i = threadIdx.x; i < Sq; i += 256) {
+      const float l = lse[base + i];
+      if (l != neg_inf()) acc += expf(s - l) * delta[base + i];
+    }
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dsinks[h] = -red[0];
+}
+
+// Transposed tile lists: for every kv tile, the q tiles whose class is not
+// EMPTY, ascending, then -1. One workgroup per (kv tile, batch, chunk).
+__global__ __launch_bounds__(256) void col_lists_kernel(MaskParams p, int32_t* col_cnt, int32_t* row_idx) {
+  __shared__ int wsum[4];
+  const int kb = blockIdx.x, b = blockIdx.y, c = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t chunk_tiles = (int64_t)p.B * p.nQb * p.nKb;
+  const uint8_t* cls = p.tile_class + c * chunk_tiles + (int64_t)b * p.nQb * p.nKb + kb;
+  const int64_t col = ((int64_t)c * p.B + b) * p.nKb + kb;
+  int32_t* out = row_idx + col * p.nQb;
+  int running = 0;
+  for (int base = 0; base < p.nQb; base += 256) {
+    const int qb = base + tid;
+    const bool f = qb < p.nQb && cls[(int64_t)qb * p.nKb] != 0;
+    const uint64_t bal = __ballot(f);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[w] = __popcll(bal);
+    __syncthreads();
+    int o = running, total = 0;
+    for (int i = 0; i < 4; ++i) {
+      if (i < w) o += wsum[i];
+      total += wsum[i];
+    }
+    if (f) out[o + before] = qb;
+    running += total;
+    __syncthreads();
+  }
+  for (int j = running + tid; j < p.nQb; j += 256) out[j] = -1;
+  if (tid == 0) col_cnt[col] = running;
+}
+
+template <typename K>
+hipError_t launch_grid(K kernel, int64_t items, const BwdParams& p, hipStream_t s) {
+  const int64_t grid = 8 * ((items + 7) / 8);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s) {
+  const AttnParams& a = p.a;
+  const bool cap = a.softcap_on != 0, bits = a.mask_bits != nullptr;
+  const int64_t q_items = (int64_t)a.B * a.H * a.nQb;
+  const int64_t kv_items = (int64_t)a.B * a.Hkv * a.nKb;
+  hipError_t e;
+  if (q_items > 0) {
+    if (cap) e = bits ? launch_grid(attn_bwd_dq<true, true>, q_items, p, s) : launch_grid(attn_bwd_dq<true, false>, q_items, p, s);
+    else e = bits ? launch_grid(attn_bwd_dq<false, true>, q_items, p, s) : launch_grid(attn_bwd_dq<false, false>, q_items, p, s);
+    if (e != hipSuccess) return e;
+  }
+  if (kv_items > 0) {
+    if (cap) e = bits ? launch_grid(attn_bwd_dkv<true, true>, kv_items, p, s) : launch_grid(attn_bwd_dkv<true, false>, kv_items, p, s);
+    else e = bits ? launch_grid(attn_bwd_dkv<false, true>, kv_items, p, s) : launch_grid(attn_bwd_dkv<false, false>, kv_items, p, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_prep(int B, int Sq, int H, int Dd, const void* out, const void* dout, const float* lse,
+                           const float* sinks, float* delta, float* dsinks, hipStream_t s) {
+  const int64_t n_rows = (int64_t)B * Sq * H;
+  if (n_rows > 0) {
+    const int64_t grid = (n_rows * 16 + 255) / 256;
+    hipLaunchKernelGGL(bwd_delta_kernel<__bf16>, dim3((unsigned)grid), dim3(256), 0, s, n_rows, H, Sq, Dd,
+                       reinterpret_cast<const __bf16*>(out), reinterpret_cast<const __bf16*>(dout), lse, delta);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (sinks && H > 0) {
+    hipLaunchKernelGGL(bwd_dsinks_kernel, dim3(H), dim3(256), 0, s, B, H, Sq, sinks, lse, delta, dsinks);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_col_lists(const MaskParams& p, int n_chunks, int32_t* col_cnt, int32_t* row_idx, hipStream_t s) {
+  if (p.B == 0 || p.nKb == 0 || n_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(col_lists_kernel, dim3(p.nKb, p.B, n_chunks), dim3(256), 0, s, p, col_cnt, row_idx);
+  return hipGetLastError();
+}
+
+}  // namespace ram

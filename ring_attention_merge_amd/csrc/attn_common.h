@@ -36,6 +36,26 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T* as_const_s
   return (const __attribute__((address_space(4))) T*)p;
 }
 
+// Work decode: item order is (batch*Hkv + kv head, q tile descending, head in group);
+// XCD x = id % 8 takes the contiguous item range [x*per, (x+1)*per).
+__device__ __forceinline__ bool decode_work(const AttnParams& p, int& b, int& h, int& qb) {
+  const int G = p.H / p.Hkv;
+  const int64_t T = (int64_t)p.B * p.Hkv * p.nQb * G;
+  const int64_t per = (T + 7) / 8;
+  const int64_t id = blockIdx.x;
+  const int64_t item = (id & 7) * per + (id >> 3);
+  if (item >= T) return false;
+  const int hg = (int)(item % G);
+  const int64_t r = item / G;
+  const int qrev = (int)(r % p.nQb);
+  const int64_t bg = r / p.nQb;
+  const int g = (int)(bg % p.Hkv);
+  b = (int)(bg / p.Hkv);
+  h = g * G + hg;
+  qb = p.nQb - 1 - qrev;
+  return true;
+}
+
 // Lanes l and l^32 hold the same query row. v_permlane32_swap exchanges the
 // upper half of its first operand with the lower half of its second; with x
 // passed as both, the two results of each lane are {own value, partner value}

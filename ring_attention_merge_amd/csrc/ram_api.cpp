@@ -139,6 +139,23 @@ ram_status check_mask_arrays(const ram_block_mask* bm, const ram_attn_desc* d, b
   return RAM_OK;
 }
 
+ram_status check_col_lists(const ram_block_mask* bm, const ram_attn_desc* d, bool need) {
+  if ((bm->col_cnt == nullptr) != (bm->row_idx == nullptr))
+    return fail(RAM_ERR_INVALID, "col_cnt and row_idx must both be set or both be null");
+  if (bm->col_cnt && (!aligned(bm->col_cnt, 4) || !aligned(bm->row_idx, 4)))
+    return fail(RAM_ERR_INVALID, "col_cnt / row_idx misaligned");
+  if (need && !bm->col_cnt && (int64_t)d->B * cdiv(d->Skv, d->block_kv) > 0)
+    return fail(RAM_ERR_INVALID, "the backward needs the transposed lists (col_cnt, row_idx)");
+  return RAM_OK;
+}
+
+// What the backward kernels are built for.
+ram_status check_bwd_support(const ram_attn_desc* d) {
+  if (d->dtype != RAM_BF16) return fail(RAM_ERR_UNSUPPORTED, "backward dtype %d (built: bf16)", d->dtype);
+  if (d->D != 128) return fail(RAM_ERR_UNSUPPORTED, "backward head dim D=%d (built: 128)", d->D);
+  return RAM_OK;
+}
+
 ram_status check_tensor(const void* p, const char* name) {
   if (!p) return fail(RAM_ERR_INVALID, "%s is null", name);
   if (!aligned(p, 16)) return fail(RAM_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
@@ -253,6 +270,33 @@ RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits)
   return L;
 }
 
+struct BwdLayout {
+  size_t dq_off, dk_off, dv_off, delta_off, cls_off, cnt_off, col_off, bits_off, ccnt_off, ridx_off, total;
+};
+BwdLayout bwd_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits) {
+  BwdLayout L{};
+  const int64_t nQb = cdiv(d->Sq, ram::kBlockQ), nKb = cdiv(d->Skv, ram::kBlockKV);
+  const int64_t tiles = (int64_t)n_chunks * d->B * nQb * nKb;
+  const int64_t kv_elems = (int64_t)d->B * n_chunks * d->Skv * d->Hkv * d->D;
+  size_t off = 0;
+  auto take = [&](size_t& at, size_t bytes) {
+    at = off;
+    off += align256(bytes);
+  };
+  take(L.dq_off, (size_t)d->B * d->Sq * d->H * d->D * sizeof(float));
+  take(L.dk_off, (size_t)kv_elems * sizeof(float));
+  take(L.dv_off, (size_t)kv_elems * sizeof(float));
+  take(L.delta_off, (size_t)d->B * d->H * d->Sq * sizeof(float));
+  take(L.cls_off, (size_t)tiles);
+  take(L.cnt_off, (size_t)n_chunks * d->B * nQb * sizeof(int32_t));
+  take(L.col_off, (size_t)tiles * sizeof(int32_t));
+  take(L.bits_off, with_bits ? (size_t)tiles * kTileWords * sizeof(uint32_t) : 0);
+  take(L.ccnt_off, (size_t)n_chunks * d->B * nKb * sizeof(int32_t));
+  take(L.ridx_off, (size_t)tiles * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -273,10 +317,15 @@ ram_status build_block_mask(const ram_attn_desc* desc, const ram_mask_src* src, 
   RAM_TRY(check_desc(desc, false, false));
   RAM_TRY(check_src(src, desc, desc->Skv, 0, desc->Skv));
   RAM_TRY(check_mask_arrays(out, desc, false));
+  RAM_TRY(check_col_lists(out, desc, false));
   if (desc->B == 0 || desc->Sq == 0) return ok();
   ram::MaskParams p = mask_params(desc, src, out, desc->Skv);
   hipError_t e = ram::launch_block_mask(p, 1, stream);
   if (e != hipSuccess) return hip_fail(e, "build_block_mask launch");
+  if (out->col_cnt) {
+    e = ram::launch_col_lists(p, 1, out->col_cnt, out->row_idx, stream);
+    if (e != hipSuccess) return hip_fail(e, "build_block_mask transposed lists launch");
+  }
   return ok();
 }
 
@@ -416,6 +465,203 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   if (desc->dtype == RAM_BF16 && !final_fused) {
     e = ram::launch_cast_bf16(acc, out, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
     if (e != hipSuccess) return hip_fail(e, "final cast launch");
+  }
+  return ok();
+}
+
+// ------------------------------------------------------------------------------ backward
+ram_status attn_bwd_prep(const ram_attn_desc* desc, const void* out, const void* dout, const float* lse,
+                         const float* sinks, float* delta, float* dsinks, hipStream_t stream) {
+  if (!desc) return fail(RAM_ERR_INVALID, "desc is null");
+  if (desc->B < 0 || desc->Sq < 0) return fail(RAM_ERR_INVALID, "negative size: B=%d Sq=%d", desc->B, desc->Sq);
+  if (desc->H < 1 || desc->H > kMaxHeads) return fail(RAM_ERR_INVALID, "H=%d outside [1, %d]", desc->H, kMaxHeads);
+  RAM_TRY(check_bwd_support(desc));
+  if (desc->B == 0 || desc->Sq == 0) {
+    if (!sinks) return ok();
+  } else {
+    RAM_TRY(check_tensor(out, "out"));
+    RAM_TRY(check_tensor(dout, "dout"));
+    if (!delta || !aligned(delta, 4)) return fail(RAM_ERR_INVALID, "delta null or misaligned");
+  }
+  if (!lse && desc->B * (int64_t)desc->Sq > 0) return fail(RAM_ERR_INVALID, "lse is null");
+  if (lse && !aligned(lse, 4)) return fail(RAM_ERR_INVALID, "lse misaligned");
+  if (sinks && (!aligned(sinks, 4) || !dsinks || !aligned(dsinks, 4)))
+    return fail(RAM_ERR_INVALID, "sinks given: dsinks must be set, both 4-byte aligned");
+  hipError_t e = ram::launch_bwd_prep(desc->B, desc->Sq, desc->H, desc->D, out, dout, lse, sinks, delta, dsinks,
+                                      stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_bwd_prep launch");
+  return ok();
+}
+
+ram_status attn_bwd_chunk(const ram_attn_desc* desc, const void* q, const void* k, const void* v,
+                          const void* dout, const float* lse, const float* delta, const ram_mask_src* src,
+                          const ram_block_mask* mask, int32_t dq_mode, float* dq, float* dk, float* dv,
+                          hipStream_t stream) {
+  RAM_TRY(check_desc(desc, true, true));
+  RAM_TRY(check_bwd_support(desc));
+  RAM_TRY(check_kv_stride(desc, desc->Skv));
+  RAM_TRY(check_src(src, desc, desc->Skv, 0, desc->Skv));
+  RAM_TRY(check_mask_arrays(mask, desc, src->dense != nullptr));
+  RAM_TRY(check_col_lists(mask, desc, true));
+  if (dq_mode != RAM_OUT_WRITE && dq_mode != RAM_OUT_MERGE) return fail(RAM_ERR_INVALID, "dq_mode %d", dq_mode);
+  if (desc->B == 0) return ok();
+  if (desc->Sq > 0) {
+    RAM_TRY(check_tensor(q, "q"));
+    RAM_TRY(check_tensor(dout, "dout"));
+    RAM_TRY(check_tensor(dq, "dq"));
+    if (!lse || !aligned(lse, 4) || !delta || !aligned(delta, 4))
+      return fail(RAM_ERR_INVALID, "lse / delta null or misaligned");
+  }
+  if (desc->Skv > 0) {
+    RAM_TRY(check_tensor(k, "k"));
+    RAM_TRY(check_tensor(v, "v"));
+    RAM_TRY(check_tensor(dk, "dk"));
+    RAM_TRY(check_tensor(dv, "dv"));
+  }
+  if (desc->Sq == 0 && desc->Skv == 0) return ok();
+  ram::BwdParams bp{};
+  bp.a = attn_params(desc, q, k, v, src, mask, nullptr, 0, nullptr, const_cast<float*>(lse));
+  bp.dout = dout;
+  bp.delta = delta;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.dkv_stride_b = bp.a.kv_stride_b;
+  bp.col_cnt = mask->col_cnt;
+  bp.row_idx = mask->row_idx;
+  bp.dq_mode = dq_mode;
+  hipError_t e = ram::launch_attn_bwd(bp, stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_bwd_chunk launch");
+  return ok();
+}
+
+
+size_t ring_attn_bwd_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src) {
+  if (!desc || n_chunks < 1 || desc->B < 0 || desc->Sq < 0 || desc->Skv < 0 || desc->H < 1 || desc->Hkv < 1 ||
+      desc->D != 128)
+    return 0;
+  ram_attn_desc dt = *desc;
+  dt.block_q = ram::kBlockQ;
+  dt.block_kv = ram::kBlockKV;
+  return bwd_layout(&dt, n_chunks, src && src->dense).total;
+}
+
+ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32_t q_shard, const void* q,
+                              const void* k_all, const void* v_all, const void* out, const float* lse,
+                              const void* dout, const ram_mask_src* src, const float* sinks, void* dq,
+                              void* dk_all, void* dv_all, float* dsinks, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  if (!desc) return fail(RAM_ERR_INVALID, "desc is null");
+  ram_attn_desc dt = *desc;
+  dt.block_q = ram::kBlockQ;
+  dt.block_kv = ram::kBlockKV;
+  desc = &dt;
+  RAM_TRY(check_desc(desc, true, true));
+  RAM_TRY(check_bwd_support(desc));
+  if (n_chunks < 1) return fail(RAM_ERR_INVALID, "n_chunks=%d must be >= 1", n_chunks);
+  if (q_shard < -1 || q_shard >= n_chunks)
+    return fail(RAM_ERR_INVALID, "q_shard=%d outside [-1, %d)", q_shard, n_chunks);
+  const int64_t kv_total = (int64_t)n_chunks * desc->Skv;
+  if (kv_total > kMaxSeq) return fail(RAM_ERR_INVALID, "total KV too long");
+  RAM_TRY(check_kv_stride(desc, kv_total));
+  const int64_t q_extra = q_shard >= 0 ? (int64_t)q_shard * desc->Sq : 0;
+  if (!src) return fail(RAM_ERR_INVALID, "mask source is null");
+  const int64_t dense_cols = desc->Skv + (int64_t)(n_chunks - 1) * (src->dense ? src->dense_chunk_step : 0);
+  RAM_TRY(check_src(src, desc, kv_total, q_extra, dense_cols));
+  if (sinks && (!aligned(sinks, 4) || !dsinks || !aligned(dsinks, 4)))
+    return fail(RAM_ERR_INVALID, "sinks given: dsinks must be set, both 4-byte aligned");
+  if (desc->B == 0) return ok();
+  if (desc->Sq > 0) {
+    RAM_TRY(check_tensor(q, "q"));
+    RAM_TRY(check_tensor(out, "out"));
+    RAM_TRY(check_tensor(dout, "dout"));
+    RAM_TRY(check_tensor(dq, "dq"));
+    if (!lse || !aligned(lse, 4)) return fail(RAM_ERR_INVALID, "lse null or misaligned");
+  }
+  if (desc->Skv > 0) {
+    RAM_TRY(check_tensor(k_all, "k_all"));
+    RAM_TRY(check_tensor(v_all, "v_all"));
+    RAM_TRY(check_tensor(dk_all, "dk_all"));
+    RAM_TRY(check_tensor(dv_all, "dv_all"));
+  }
+  const bool with_bits = src->dense != nullptr;
+  const BwdLayout L = bwd_layout(desc, n_chunks, with_bits);
+  if (!workspace || !aligned(workspace, 256))
+    return fail(RAM_ERR_WORKSPACE, "workspace null or not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(RAM_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, L.total);
+
+  char* ws = static_cast<char*>(workspace);
+  float* dq_acc = reinterpret_cast<float*>(ws + L.dq_off);
+  float* dk_acc = reinterpret_cast<float*>(ws + L.dk_off);
+  float* dv_acc = reinterpret_cast<float*>(ws + L.dv_off);
+  float* delta = reinterpret_cast<float*>(ws + L.delta_off);
+  ram_block_mask bm{reinterpret_cast<uint8_t*>(ws + L.cls_off), reinterpret_cast<int32_t*>(ws + L.cnt_off),
+                    reinterpret_cast<int32_t*>(ws + L.col_off),
+                    with_bits ? reinterpret_cast<uint32_t*>(ws + L.bits_off) : nullptr,
+                    reinterpret_cast<int32_t*>(ws + L.ccnt_off), reinterpret_cast<int32_t*>(ws + L.ridx_off)};
+  const int64_t nQb = cdiv(desc->Sq, ram::kBlockQ), nKb = cdiv(desc->Skv, ram::kBlockKV);
+  const int64_t kv_full_stride = desc->kv_stride_b ? desc->kv_stride_b : kv_total * desc->Hkv * desc->D;
+  const int64_t kv_acc_stride = kv_total * desc->Hkv * desc->D;
+  const int64_t kvm_full = src->kv_meta_stride_b ? src->kv_meta_stride_b : kv_total;
+  const int32_t q_base = (int32_t)(src->q_pos_base + q_extra);
+
+  hipError_t e = ram::launch_bwd_prep(desc->B, desc->Sq, desc->H, desc->D, out, dout, lse, sinks, delta, dsinks,
+                                      stream);
+  if (e != hipSuccess) return hip_fail(e, "ring backward prep launch");
+  ram_mask_src sm = *src;
+  sm.q_pos_base = q_base;
+  sm.kv_meta_stride_b = kvm_full;
+  ram::MaskParams mp = mask_params(desc, &sm, &bm, dense_cols);
+  mp.kv_chunk_off = desc->Skv;
+  mp.kv_base_step = desc->Skv;
+  mp.dense_col_step = src->dense_chunk_step;
+  e = ram::launch_block_mask(mp, n_chunks, stream);
+  if (e != hipSuccess) return hip_fail(e, "ring backward block mask launch");
+  e = ram::launch_col_lists(mp, n_chunks, bm.col_cnt, bm.row_idx, stream);
+  if (e != hipSuccess) return hip_fail(e, "ring backward transposed lists launch");
+
+  const int64_t esz = 2;
+  for (int t = 0; t < n_chunks; ++t) {
+    const int c = q_shard >= 0 ? ((q_shard - t) % n_chunks + n_chunks) % n_chunks : t;
+    ram_attn_desc dc = *desc;
+    dc.kv_stride_b = kv_full_stride;
+    ram_mask_src sc = *src;
+    sc.q_pos_base = q_base;
+    sc.kv_meta_stride_b = kvm_full;
+    sc.kv_pos = src->kv_pos ? src->kv_pos + (int64_t)c * desc->Skv : nullptr;
+    sc.kv_seg = src->kv_seg ? src->kv_seg + (int64_t)c * desc->Skv : nullptr;
+    sc.kv_pos_base = src->kv_pos_base + c * desc->Skv;
+    const int64_t tiles_c = (int64_t)c * desc->B * nQb * nKb;
+    const ram_block_mask bc{bm.tile_class + tiles_c, bm.row_cnt + (int64_t)c * desc->B * nQb, bm.col_idx + tiles_c,
+                            with_bits ? bm.bits + tiles_c * kTileWords : nullptr,
+                            bm.col_cnt + (int64_t)c * desc->B * nKb, bm.row_idx + tiles_c};
+    const int64_t kv_off = (int64_t)c * desc->Skv * desc->Hkv * desc->D;
+    ram::BwdParams bp{};
+    bp.a = attn_params(&dc, q, static_cast<const char*>(k_all) + kv_off * esz,
+                       static_cast<const char*>(v_all) + kv_off * esz, &sc, &bc, nullptr, 0, nullptr,
+                       const_cast<float*>(lse));
+    bp.dout = dout;
+    bp.delta = delta;
+    bp.dq = dq_acc;
+    bp.dk = dk_acc + kv_off;
+    bp.dv = dv_acc + kv_off;
+    bp.dkv_stride_b = kv_acc_stride;
+    bp.col_cnt = bc.col_cnt;
+    bp.row_idx = bc.row_idx;
+    bp.dq_mode = t == 0 ? RAM_OUT_WRITE : RAM_OUT_MERGE;
+    e = ram::launch_attn_bwd(bp, stream);
+    if (e != hipSuccess) return hip_fail(e, "ring backward chunk launch");
+  }
+  e = ram::launch_cast_bf16(dq_acc, dq, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
+  if (e != hipSuccess) return hip_fail(e, "dq cast launch");
+  for (int b = 0; b < desc->B; ++b) {
+    e = ram::launch_cast_bf16(dk_acc + b * kv_acc_stride, static_cast<char*>(dk_all) + b * kv_full_stride * esz,
+                              kv_acc_stride, stream);
+    if (e == hipSuccess)
+      e = ram::launch_cast_bf16(dv_acc + b * kv_acc_stride, static_cast<char*>(dv_all) + b * kv_full_stride * esz,
+                                kv_acc_stride, stream);
+    if (e != hipSuccess) return hip_fail(e, "dk / dv cast launch");
   }
   return ok();
 }

@@ -62,7 +62,27 @@ struct MaskParams {
   uint32_t* bits;          // or null; tile t at + t * bq*ceil(bk/32), t counted like tile_class
 };
 
+// Backward of one chunk: `a` carries q, k, v, lse, the masks and sizes of the
+// forward call (a.out, a.out_final, a.sinks and a.mode are not read).
+struct BwdParams {
+  AttnParams a;
+  const void* dout;        // [B,Sq,H,D] in the q dtype
+  const float* delta;      // [B,H,Sq]: rowsum(dout * out)
+  float* dq;               // float32 [B,Sq,H,D], written (dq_mode 0) or added to (1)
+  float* dk;               // float32 [B, Skv, Hkv, D] rows, batch stride dkv_stride_b
+  float* dv;
+  int64_t dkv_stride_b;    // elements
+  const int32_t* col_cnt;  // [B, nKb]: non-EMPTY q tiles per kv tile
+  const int32_t* row_idx;  // [B, nKb, nQb]: those q tiles, ascending
+  int32_t dq_mode;
+};
+
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s);
+hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s);   // bf16, D = 128: dq, then dk / dv
+hipError_t launch_bwd_prep(int B, int Sq, int H, int D, const void* out, const void* dout, const float* lse,
+                           const float* sinks, float* delta, float* dsinks, hipStream_t s);
+hipError_t launch_col_lists(const MaskParams& p, int n_chunks, int32_t* col_cnt, int32_t* row_idx,
+                            hipStream_t s);
 // Whether the kernel launch_attn would pick for p honours p.out_final.
 bool attn_writes_final(const AttnParams& p, int dtype);
 hipError_t launch_attn_pp(const AttnParams& p, hipStream_t s);   // bf16, 8-wave ping-pong

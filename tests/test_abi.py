@@ -34,7 +34,8 @@ def _header_functions():
 def test_every_header_symbol_is_exported(lib):
     names = _header_functions()
     assert set(names) == {"build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
-                          "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_last_error"}, names
+                          "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_last_error", "attn_bwd_prep",
+                          "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes"}, names
     for n in names:
         assert hasattr(lib, n), f"libram.so does not export {n}"
 
@@ -55,7 +56,7 @@ def _src(**kw):
 
 def _bm(**kw):
     return _lib.c_block_mask(kw.get("tile_class", FAKE), kw.get("row_cnt", FAKE), kw.get("col_idx", FAKE),
-                             kw.get("bits", 0))
+                             kw.get("bits", 0), kw.get("col_cnt", 0), kw.get("row_idx", 0))
 
 
 def _chunk(lib, d, *, q=FAKE, k=FAKE, v=FAKE, src=None, bm=None, sinks=0, mode=0, out=FAKE, lse=FAKE):
@@ -213,3 +214,43 @@ def test_binding_rejects_cpu_tensors(lib):
     with pytest.raises(ValueError, match="GPU tensor"):
         ram.attn_fwd_chunk(d, x, x, x, ram.MaskSrc(), ram.alloc_block_mask(d, device="cpu"), None, 0, x,
                            torch.zeros(8), stream=0)
+
+
+def test_backward_validation(lib):
+    d = _desc()
+    z = ctypes.c_void_p(0)
+    args = lambda **kw: (ctypes.byref(kw.get("d", d)), kw.get("q", FAKE), kw.get("k", FAKE), kw.get("v", FAKE),
+                         kw.get("dout", FAKE), kw.get("lse", FAKE2), kw.get("delta", FAKE2),
+                         ctypes.byref(kw.get("src", _src())), ctypes.byref(kw.get("bm", _bm(col_cnt=FAKE, row_idx=FAKE))),
+                         kw.get("mode", 0), kw.get("dq", FAKE), kw.get("dk", FAKE), kw.get("dv", FAKE), 0)
+    # built for bf16, D = 128 only
+    assert lib.attn_bwd_chunk(*args(d=_desc(D=64))) == _lib.RAM_ERR_UNSUPPORTED and "128" in _err(lib)
+    assert lib.attn_bwd_chunk(*args(d=_desc(dtype=ram.RAM_F32))) == _lib.RAM_ERR_UNSUPPORTED
+    # the transposed lists are required, both or neither
+    assert lib.attn_bwd_chunk(*args(bm=_bm())) == _lib.RAM_ERR_INVALID and "transposed" in _err(lib)
+    assert lib.attn_bwd_chunk(*args(bm=_bm(col_cnt=FAKE))) == _lib.RAM_ERR_INVALID and "both" in _err(lib)
+    assert lib.attn_bwd_chunk(*args(mode=2)) == _lib.RAM_ERR_INVALID and "dq_mode" in _err(lib)
+    assert lib.attn_bwd_chunk(*args(dout=FAKE + 2)) == _lib.RAM_ERR_UNSUPPORTED
+    assert lib.attn_bwd_chunk(*args(delta=0)) == _lib.RAM_ERR_INVALID
+    assert lib.attn_bwd_chunk(*args(dk=0)) == _lib.RAM_ERR_INVALID
+    assert lib.attn_bwd_chunk(*args(src=_src(dense=FAKE2))) == _lib.RAM_ERR_INVALID and "bits" in _err(lib)
+    # prep: sinks need dsinks
+    assert lib.attn_bwd_prep(ctypes.byref(d), FAKE, FAKE, FAKE2, FAKE2, FAKE2, z, 0) == _lib.RAM_ERR_INVALID
+    assert lib.attn_bwd_prep(ctypes.byref(_desc(D=64)), FAKE, FAKE, FAKE2, 0, FAKE2, 0, 0) == _lib.RAM_ERR_UNSUPPORTED
+    # the ring: workspace holds float32 dq, dk, dv, delta and the masks with transposed lists
+    dr = _desc(B=1, Sq=512, Skv=512, H=4, Hkv=2)
+    need = lib.ring_attn_bwd_workspace_bytes(ctypes.byref(dr), 4, None)
+    al = lambda x: (x + 255) // 256 * 256
+    tiles = 4 * 4 * 8
+    expect = (al(512 * 4 * 128 * 4) + 2 * al(4 * 512 * 2 * 128 * 4) + al(4 * 512 * 4) + al(tiles)
+              + al(4 * 4 * 4) + al(tiles * 4) + al(4 * 8 * 4) + al(tiles * 4))
+    assert need == expect
+    dense = lib.ring_attn_bwd_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src(dense=FAKE2)))
+    assert dense == need + tiles * 1024
+    assert lib.ring_attn_bwd_workspace_bytes(ctypes.byref(_desc(D=64)), 4, None) == 0
+    ring = lambda ws_bytes, **kw: lib.ring_attn_bwd_1gpu(
+        ctypes.byref(kw.get("d", dr)), 4, kw.get("r", 3), FAKE, FAKE, FAKE, FAKE, FAKE2, FAKE,
+        ctypes.byref(_src()), kw.get("sinks", 0), FAKE, FAKE, FAKE, kw.get("dsinks", 0), FAKE, ws_bytes, 0)
+    assert ring(need - 1) == _lib.RAM_ERR_WORKSPACE and "need" in _err(lib)
+    assert ring(need, r=4) == _lib.RAM_ERR_INVALID
+    assert ring(need, sinks=FAKE2) == _lib.RAM_ERR_INVALID and "dsinks" in _err(lib)
