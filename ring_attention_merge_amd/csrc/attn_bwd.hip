@@ -71,15 +71,37 @@ __device__ __forceinline__ bf16x8 lds_row(const char* tile, int row, int c) {
 }
 // Transposed operand of 32 columns x 16 rows starting at row r0, column block db:
 // lane receives column db*32 + (lane & 31) at rows r0 + 4*lg + 0..3 and r0 + 8 + 4*lg + 0..3.
-__device__ __forceinline__ bf16x8 lds_tr(const char* tile, int r0, int db, int lane) {
+// Issued from assembly (see lds_tr_pair_issue): the value must pass lds_settle().
+__device__ __forceinline__ TrPair lds_tr(const char* tile, int r0, int db, int lane) {
   const int lg = lane >> 5, r4 = (lane & 15) >> 2, hs = (lane >> 4) & 1;
   const int c = 4 * db + 2 * hs + ((lane & 3) >> 1);
   const int ra = r0 + 4 * lg + r4, rb = ra + 8;
   const char* pa = tile + ra * 256 + ((c ^ swz(ra)) * 16) + (lane & 1) * 8;
   const char* pb = tile + rb * 256 + ((c ^ swz(rb)) * 16) + (lane & 1) * 8;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pa));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pb));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return lds_tr_pair_issue2(pa, pb);
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Four 16-byte LDS reads at a, a+32, a+64, a+96 from each of two bases, and the
+// wait for them. Written out so that the compiler, which cannot tell these rows
+// from LDS written by an outstanding DMA, adds no wait on that DMA here (the
+// loop waits for the data of a step explicitly before its barrier).
+__device__ __forceinline__ void lds_rows8(const char* a, const char* b, f32x4 (&x)[4], f32x4 (&y)[4]) {
+  const uint32_t pa = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)a;
+  const uint32_t pb = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)b;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:32\n\t"
+      "ds_read_b128 %2, %8 offset:64\n\t"
+      "ds_read_b128 %3, %8 offset:96\n\t"
+      "ds_read_b128 %4, %9\n\t"
+      "ds_read_b128 %5, %9 offset:32\n\t"
+      "ds_read_b128 %6, %9 offset:64\n\t"
+      "ds_read_b128 %7, %9 offset:96\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3])
+      : "v"(pa), "v"(pb));
 }
 
 // The 16 accumulator values of a 32x32 block as two 16-deep bf16 B operands
@@ -267,10 +289,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
     }
     // dQ^T += K^T dS^T: A = K read transposed (lane = dim), B = dS^T (lane = query)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int half = 0; half < 2; ++half) {
+      TrPair kt8[8];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr(Kt, ks * 16, db, lane), DS[ks], dQ[db], 0, 0, 0);
+      for (int f = 0; f < 8; ++f) kt8[f] = lds_tr(Kt, (half * 2 + f / NDB) * 16, f % NDB, lane);
+      lds_settle(kt8);
+#pragma unroll
+      for (int f = 0; f < 8; ++f) {
+        const int ks = half * 2 + f / NDB, db = f % NDB;
+        dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(kt8[f]), DS[ks], dQ[db], 0, 0, 0);
+      }
+    }
 
     const int kb_nn = cols[min(it + 2, cnt - 1)];
     const int mk_nxt = needs_mask(kb_nxt);
@@ -321,10 +350,10 @@ __device__ __forceinline__ bool decode_kv_work(const AttnParams& p, int& b, int&
 
 // Element mask of a 32-query x 32-key block with the key per lane: query of
 // register i is row q0 + 8*(i>>2) + 4*lg + (i&3) of the step (rows of the
-// step at qrow0 in the sequence). Positions / segments of the step's rows are
-// in LDS (qpos_s, qseg_s) when the call has such arrays.
+// step at qrow0 in the sequence); qposv / qsegv hold that row's position and
+// segment when the call has such arrays.
 __device__ __forceinline__ void mask_kv(f32x16& S, const AttnParams& p, int key, int kpos, int kseg, int qrow0,
-                                        int q0, int lg, const int* qpos_s, const int* qseg_s) {
+                                        int q0, int lg, const int (&qposv)[16], const int (&qsegv)[16]) {
   if (!p.q_pos && !p.kv_pos && !p.q_seg) {
     // sequential positions: a query row r keeps the key iff r >= key + kv_base - q_base
     const int64_t t64 = (int64_t)key + p.kv_pos_base - p.q_pos_base - (qrow0 + q0 + 4 * lg);
@@ -340,22 +369,33 @@ __device__ __forceinline__ void mask_kv(f32x16& S, const AttnParams& p, int key,
     const int r = q0 + 8 * (i >> 2) + 4 * lg + (i & 3);
     bool ok = key < p.Skv;
     if (p.causal) {
-      const int qp = p.q_pos ? qpos_s[r] : p.q_pos_base + qrow0 + r;
+      const int qp = p.q_pos ? qposv[i] : p.q_pos_base + qrow0 + r;
       ok = ok && kpos <= qp;
     }
-    if (p.q_seg) ok = ok && qseg_s[r] == kseg && kseg != -1;
+    if (p.q_seg) ok = ok && qsegv[i] == kseg && kseg != -1;
     if (!ok) S[i] = neg_inf();
   }
 }
 
-// One workgroup per CU slot per SIMD: K, V (64 registers), the dK / dV
-// accumulators (128) and a step's products do not fit the 256 registers of
-// two waves per SIMD.
+// One wave per SIMD: K, V (64 registers), the dK / dV accumulators (128) and
+// a step's products do not fit the 256 registers of two waves per SIMD. With
+// no second workgroup to cover load latency, the step data (Q, dO and the
+// rows' lse, D, positions, segments) comes through a 4-stage DMA ring: the
+// loads of step t+3 are issued at the top of step t. Every wave issues exactly
+// kDmaPerStep loads per step (steps past the end load nothing from empty
+// resources), so one fixed vmcnt wait per step covers the next step.
+constexpr int kStages = 4;
+constexpr int kDmaPerStep = 9;
+// s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt not waited on (gfx9 encoding).
+constexpr int vmcnt_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 template <bool CAP, bool BITS>
 __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkv(BwdParams bp) {
   const AttnParams& p = bp.a;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * kTileElems];   // [stage][Q, dO]
-  __shared__ __attribute__((aligned(16))) float row_s[2][4][64];             // [stage][lse2, D, pos, seg]
+  // [stage][Q, dO] tiles, then [stage][lse, D, pos, seg] rows: one LDS object for every DMA target
+  __shared__ __attribute__((aligned(16))) __bf16 smem[kStages * 2 * kTileElems + kStages * 4 * 64 * 2];
+  char* const rows_lds = reinterpret_cast<char*>(smem + kStages * 2 * kTileElems);   // [stage][4][64] floats
+  auto row_at = [&](int buf, int arr, int r) { return rows_lds + ((buf * 4 + arr) * 64 + r) * 4; };
 
   int b, g, kb;
   if (!decode_kv_work(p, b, g, kb)) return;
@@ -396,6 +436,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkv(BwdParams bp) {
   const int64_t kcol = (int64_t)b * p.nKb + kb;
   const int ccnt = bp.col_cnt[kcol];
   const auto rows = as_const_space(bp.row_idx + kcol * p.nQb);
+  // tile classes are bytes; read the aligned dword that holds one (a scalar load)
+  auto tile_class_of = [&](int qb) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p.tile_class + ((int64_t)b * p.nQb + qb) * p.nKb + kb);
+    const uint32_t word = *as_const_space(reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3)));
+    return (int)((word >> (8 * (a & 3))) & 0xffu);
+  };
   const int n_steps = ccnt * 2 * G;          // (q tile, 64-row half, head in group)
 
   const uint32_t row_bytes = (uint32_t)p.H * D * 2;
@@ -407,80 +453,65 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkv(BwdParams bp) {
     r0 = qb * kBlockQ + ((t / G) & 1) * 64;
     h = g * G + t % G;
   };
+  // The row array this wave moves: 0 lse, 1 D, 2 positions, 3 segments (empty when absent).
+  const float* row_src = w == 0 ? p.lse : (w == 1 ? bp.delta : reinterpret_cast<const float*>(w == 2 ? p.q_pos : p.q_seg));
+  const bool row_per_head = w < 2;
   auto stage = [&](int t, int buf) {
-    int qb, r0, h;
-    step_rows(t, qb, r0, h);
-    const int nrows = min(64, p.Sq - r0);
+    int qb = 0, r0 = p.Sq, h = g * G;
+    if (t < n_steps) step_rows(t, qb, r0, h);
+    const int nrows = max(0, min(64, p.Sq - r0));
     const uint32_t bytes = nrows > 0 ? (uint32_t)(nrows - 1) * row_bytes + D * 2 : 0u;
-    const int64_t rq = (int64_t)r0 * p.H + h;
+    const int64_t rq = (int64_t)min(r0, p.Sq) * p.H + h;
     __bf16* Qs = smem + buf * 2 * kTileElems;
     dma_tile(tile_rsrc(reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b + rq * D, bytes), Qs, off, w);
     dma_tile(tile_rsrc(reinterpret_cast<const __bf16*>(bp.dout) + ((int64_t)b * p.Sq * p.H + rq) * D, bytes),
              Qs + kTileElems, off, w);
-  };
-  // Per-row values of a step (threads 0..63): lse in log2 units (+inf where the
-  // row has no weight), D, and positions / segments when the call has them.
-  auto row_values = [&](int t, float (&v)[4]) {
-    int qb, r0, h;
-    step_rows(t, qb, r0, h);
-    const int r = r0 + tid;
-    v[0] = __builtin_inff();
-    v[1] = 0.0f;
-    v[2] = 0.0f;
-    v[3] = 0.0f;
-    if (r < p.Sq) {
-      const int64_t li = ((int64_t)b * p.H + h) * p.Sq + r;
-      const float l = p.lse[li];
-      if (l != neg_inf()) {
-        v[0] = l * kLog2e;
-        v[1] = bp.delta[li];
-      }
-      if (p.q_pos) v[2] = __int_as_float(p.q_pos[(int64_t)b * p.qm_stride_b + r]);
-      if (p.q_seg) v[3] = __int_as_float(p.q_seg[(int64_t)b * p.qm_stride_b + r]);
-    }
+    const int64_t rbase = row_per_head ? ((int64_t)b * p.H + h) * p.Sq : (int64_t)b * p.qm_stride_b;
+    const uint32_t rbytes = row_src ? (uint32_t)nrows * 4u : 0u;
+    const float* rs = row_src ? row_src + rbase + min(r0, p.Sq) : p.lse;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tile_rsrc(rs, rbytes),
+                                             (__attribute__((address_space(3))) void*)(row_at(buf, w, 0)), 4,
+                                             (uint32_t)lane * 4u, 0, 0, 0);
   };
 
-  if (n_steps > 0) {
-    stage(0, 0);
-    if (tid < 64) {
-      float v[4];
-      row_values(0, v);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) row_s[0][j][tid] = v[j];
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
+  for (int t = 0; t < kStages - 1; ++t) stage(t, t);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kStages - 2)));
   __syncthreads();
 
   for (int t = 0; t < n_steps; ++t) {
-    const int buf = t & 1;
-    const bool has_next = t + 1 < n_steps;
-    float nv[4];
-    if (has_next) {
-      stage(t + 1, buf ^ 1);
-      if (tid < 64) row_values(t + 1, nv);
-    }
+    const int buf = t & (kStages - 1);
+    stage(t + kStages - 1, (t + kStages - 1) & (kStages - 1));   // the buffer step t-1 read
     int qb, r0, h;
     step_rows(t, qb, r0, h);
-    const int cl = p.tile_class[((int64_t)b * p.nQb + qb) * p.nKb + kb];
+    const int cl = tile_class_of(qb);
     const int need_mask = (BITS && cl == 1) ? 2 : ((cl != 2 || (kb + 1) * kBlockKV > p.Skv) ? 1 : 0);
     const char* Qt = reinterpret_cast<const char*>(smem + buf * 2 * kTileElems);
     const char* Ot = Qt + kTileElems * 2;
     const int q0 = 32 * qh;                  // this wave's first row in the step
 
     // S = Q K^T and dP = dO V^T for 32 queries x 32 keys: A = query rows from LDS
+    // (issued from assembly, like every LDS read of DMA-filled data in this loop)
     f32x16 S = f32x16{}, dP = f32x16{};
+    {
+      bf16x8 a[16];
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(Qt, q0 + ln, 2 * ds + lg), kt[ds], S, 0, 0, 0);
-      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(Ot, q0 + ln, 2 * ds + lg), vt[ds], dP, 0, 0, 0);
+      for (int ds = 0; ds < NDS; ++ds) {
+        const int r = q0 + ln, c = 2 * ds + lg;
+        a[ds] = lds_b128_issue(Qt + r * 256 + ((c ^ swz(r)) * 16));
+        a[NDS + ds] = lds_b128_issue(Ot + r * 256 + ((c ^ swz(r)) * 16));
+      }
+      lds_settle16(a);
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds], kt[ds], S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[NDS + ds], vt[ds], dP, 0, 0, 0);
+      }
     }
     if constexpr (CAP) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) S[i] = capped_log2(S[i], p.cap_k2, p.cap_log2);
     }
-    const int* qpos_s = reinterpret_cast<const int*>(row_s[buf][2]);
-    const int* qseg_s = reinterpret_cast<const int*>(row_s[buf][3]);
     if (BITS && need_mask == 2) {
       // bits of the tile: row (step half * 64 + q0 + r), word kbw, bit ln
       const uint32_t* tb = p.mask_bits + (((int64_t)b * p.nQb + qb) * p.nKb + kb) * kBlockQ * 2 +
@@ -489,21 +520,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkv(BwdParams bp) {
       for (int i = 0; i < 16; ++i)
         if (((tb[(8 * (i >> 2) + (i & 3)) * 2] >> ln) & 1u) == 0u) S[i] = neg_inf();
     } else if (need_mask) {
-      mask_kv(S, p, key, kpos, kseg, r0, q0, lg, qpos_s, qseg_s);
-    }
-    float lse2v[16], dlv[16];
+      int qposv[16], qsegv[16];
+      if (p.q_pos || p.q_seg) {
+        f32x4 a[4], c[4];
+        lds_rows8(row_at(buf, 2, q0 + 4 * lg), row_at(buf, 3, q0 + 4 * lg), a, c);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 a = *reinterpret_cast<const float4*>(&row_s[buf][0][q0 + 8 * j + 4 * lg]);
-      const float4 c = *reinterpret_cast<const float4*>(&row_s[buf][1][q0 + 8 * j + 4 * lg]);
-      lse2v[4 * j] = a.x;
-      lse2v[4 * j + 1] = a.y;
-      lse2v[4 * j + 2] = a.z;
-      lse2v[4 * j + 3] = a.w;
-      dlv[4 * j] = c.x;
-      dlv[4 * j + 1] = c.y;
-      dlv[4 * j + 2] = c.z;
-      dlv[4 * j + 3] = c.w;
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            qposv[4 * j + e] = __float_as_int(a[j][e]);
+            qsegv[4 * j + e] = __float_as_int(c[j][e]);
+          }
+      }
+      mask_kv(S, p, key, kpos, kseg, r0, q0, lg, qposv, qsegv);
+    }
+    // Row values: lse in log2 units, +inf where the row has no weight (lse = -inf);
+    // rows past Sq read 0 and have zero Q / dO rows, so they add nothing.
+    float lse2v[16], dlv[16];
+    {
+      f32x4 la[4], da[4];   // rows q0 + 8j + 4*lg + 0..3, j = 0..3
+      lds_rows8(row_at(buf, 0, q0 + 4 * lg), row_at(buf, 1, q0 + 4 * lg), la, da);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lse2v[4 * j + e] = la[j][e] == neg_inf() ? __builtin_inff() : la[j][e] * kLog2e;
+          dlv[4 * j + e] = da[j][e];
+        }
     }
     f32x16 Pw;
     weights_and_grads<CAP>(S, dP, Pw, lse2v, dlv, p);
@@ -512,20 +555,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkv(BwdParams bp) {
     pack_b(S, DSb);
     __builtin_amdgcn_sched_barrier(0);
     // dV^T += dO^T P and dK^T += Q^T dS: A = dO / Q read transposed (lane = dim)
+    {
+      TrPair ot8[8], qt8[8];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int f = 0; f < 8; ++f) ot8[f] = lds_tr(Ot, q0 + (f / NDB) * 16, f % NDB, lane);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr(Ot, q0 + ks * 16, db, lane), Pb[ks], dV[db], 0, 0, 0);
-        dK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr(Qt, q0 + ks * 16, db, lane), DSb[ks], dK[db], 0, 0, 0);
+      for (int f = 0; f < 8; ++f) qt8[f] = lds_tr(Qt, q0 + (f / NDB) * 16, f % NDB, lane);
+      lds_settle(ot8);
+      lds_settle(qt8);
+#pragma unroll
+      for (int f = 0; f < 8; ++f) {
+        const int ks = f / NDB, db = f % NDB;
+        dV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(ot8[f]), Pb[ks], dV[db], 0, 0, 0);
+        dK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(qt8[f]), DSb[ks], dK[db], 0, 0, 0);
       }
-    if (has_next && tid < 64) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) row_s[buf ^ 1][j][tid] = nv[j];
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // Step t+1 has landed once at most the loads of steps t+2, t+3 are
+    // outstanding. A bare barrier: every LDS read in this loop is issued from
+    // assembly and has completed, and the fences of __syncthreads would wait
+    // for the loads still in flight.
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kStages - 2)));
+    __builtin_amdgcn_s_barrier();
   }
+  __builtin_amdgcn_s_waitcnt(0);   // the empty loads of the last stages
+  __syncthreads();
 
   // The two query halves of each key block: waves 2, 3 hand theirs to waves 0, 1.
   float* red = reinterpret_cast<float*>(smem);   // [key block][2 tensors][NDB][16][64 lanes]

@@ -291,5 +291,57 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
+// Transposing LDS reads issued from inline assembly. The compiler cannot tell
+// a ds_read_b64_tr_b16 address from LDS that an LDS-DMA in flight is writing,
+// so its own form waits for every outstanding DMA first, including the one
+// filling the next tile. Kernels that prefetch by DMA issue these instead and
+// wait for the next tile explicitly. A value read this way may not be touched
+// (not even moved) before lds_settle(): the hardware does not interlock LDS
+// results, so the wait ties every pending register.
+struct TrPair {
+  s16x4 lo, hi;
+};
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+// reads at p and p + OFF bytes
+template <int OFF>
+__device__ __forceinline__ TrPair lds_tr_pair_issue(const void* p) {
+  TrPair r;
+  asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:%3"
+               : "=&v"(r.lo), "=&v"(r.hi)
+               : "v"(lds_addr(p)), "i"(OFF));
+  return r;
+}
+// reads at two addresses
+__device__ __forceinline__ TrPair lds_tr_pair_issue2(const void* pa, const void* pb) {
+  TrPair r;
+  asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %3"
+               : "=&v"(r.lo), "=&v"(r.hi)
+               : "v"(lds_addr(pa)), "v"(lds_addr(pb)));
+  return r;
+}
+// A 16-byte LDS read issued from assembly, for the same reason; settle with lds_settle16.
+__device__ __forceinline__ bf16x8 lds_b128_issue(const void* p) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+  return r;
+}
+__device__ __forceinline__ void lds_settle16(bf16x8 (&t)[16]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7]),
+                 "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15]));
+}
+// Waits for all LDS reads of this wave (lgkmcnt(0)) and ties eight pairs.
+__device__ __forceinline__ void lds_settle(TrPair (&t)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(t[0].lo), "+v"(t[0].hi), "+v"(t[1].lo), "+v"(t[1].hi), "+v"(t[2].lo), "+v"(t[2].hi),
+                 "+v"(t[3].lo), "+v"(t[3].hi), "+v"(t[4].lo), "+v"(t[4].hi), "+v"(t[5].lo), "+v"(t[5].hi),
+                 "+v"(t[6].lo), "+v"(t[6].hi), "+v"(t[7].lo), "+v"(t[7].hi));
+}
+__device__ __forceinline__ bf16x8 tr_join(const TrPair& t) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t.lo, t.hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 }  // namespace attn
 }  // namespace ram
