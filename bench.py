@@ -117,6 +117,30 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def recorded_traffic_bwd(workload: str):
+    """HBM bytes per chunk backward call (dq + dk/dv kernels) from the committed counter summary, if
+    it was taken on the current backward source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_bwd_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        line = line.strip().strip("`")
+        if "=" in line and " " not in line.split("=", 1)[0]:
+            k, v = line.split("=", 1)
+            fields[k] = v.strip()
+    h = hashlib.sha256()
+    for f in ("attn_bwd.hip", "attn_common.h"):
+        h.update(open(os.path.join(ROOT, "ring_attention_merge_amd", "csrc", f), "rb").read())
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_call_dq"]) + int(fields["traffic_bytes_per_call_dkv"])
+    except (KeyError, ValueError):
+        return None
+
+
 def recorded_traffic(workload: str):
     """HBM bytes per chunk launch from the committed counter summary, if it was taken
     on the current kernel source (else None)."""
@@ -200,8 +224,10 @@ def backward(args, w, desc, q, k, v, src, sinks, out, lse, ws, stream, dense, ef
     kern_ms = sum(per_chunk_ms)
     achieved = eff / (kern_ms * 1e-3) / 1e12
     log("chunk backward ms (visit order): " + ", ".join(f"{x:.3f}" for x in per_chunk_ms))
+    if args.copy_calibration:
+        copy_calibration(dev)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic_bwd(args.workload),
                 "kernel": "attn_bwd_dq + attn_bwd_dkv (one attn_bwd_chunk call)",
                 "launches_per_step": w.n_chunks, "mean_launch_us": round(1e3 * kern_ms / w.n_chunks, 2),
                 "flops_per_launch_mean": eff / w.n_chunks}
@@ -217,6 +243,16 @@ def backward(args, w, desc, q, k, v, src, sinks, out, lse, ws, stream, dense, ef
         "cpu_baseline": None if args.no_cpu else cpu_baseline_bwd(w, min(args.cpu_rows, 256)),
     }
     print(json.dumps(line), flush=True)
+
+
+def copy_calibration(dev):
+    """A plain 256 MiB device copy, to scale the FETCH_SIZE / WRITE_SIZE counters."""
+    a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+    b2 = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b2.copy_(a)                     # reads 256 MiB, writes 256 MiB
+    torch.cuda.synchronize()
+    del a, b2
 
 
 def cpu_baseline_bwd(w, n_rows):
@@ -402,12 +438,7 @@ def main():
     del acc, acc_lse, masks
     builder = None if dense is None else mask_builder_rate(w, desc, dense, bq, bk, dev, stream, reps)
     if args.copy_calibration:
-        a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
-        b2 = torch.empty_like(a)
-        torch.cuda.synchronize()
-        b2.copy_(a)                     # reads 256 MiB, writes 256 MiB
-        torch.cuda.synchronize()
-        del a, b2
+        copy_calibration(dev)
 
     cpu = None
     if not args.no_cpu:
