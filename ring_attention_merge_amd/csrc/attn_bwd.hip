@@ -83,27 +83,6 @@ __device__ __forceinline__ TrPair lds_tr(const char* tile, int r0, int db, int l
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Four 16-byte LDS reads at a, a+32, a+64, a+96 from each of two bases, and the
-// wait for them. Written out so that the compiler, which cannot tell these rows
-// from LDS written by an outstanding DMA, adds no wait on that DMA here (the
-// loop waits for the data of a step explicitly before its barrier).
-__device__ __forceinline__ void lds_rows8(const char* a, const char* b, f32x4 (&x)[4], f32x4 (&y)[4]) {
-  const uint32_t pa = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)a;
-  const uint32_t pb = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)b;
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:32\n\t"
-      "ds_read_b128 %2, %8 offset:64\n\t"
-      "ds_read_b128 %3, %8 offset:96\n\t"
-      "ds_read_b128 %4, %9\n\t"
-      "ds_read_b128 %5, %9 offset:32\n\t"
-      "ds_read_b128 %6, %9 offset:64\n\t"
-      "ds_read_b128 %7, %9 offset:96\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3])
-      : "v"(pa), "v"(pb));
-}
-
 // The 16 accumulator values of a 32x32 block as two 16-deep bf16 B operands
 // (K index order matching lds_tr: 4*lg + 0..3, then 8 + 4*lg + 0..3).
 __device__ __forceinline__ void pack_b(const f32x16& S, bf16x8 (&P)[2]) {
@@ -348,13 +327,11 @@ __device__ __forceinline__ bool decode_kv_work(const AttnParams& p, int& b, int&
   return true;
 }
 
-// Element mask of a 32-query x 32-key block with the key per lane: query of
-// register i is row q0 + 8*(i>>2) + 4*lg + (i&3) of the step (rows of the
-// step at qrow0 in the sequence); qposv / qsegv hold that row's position and
-// segment when the call has such arrays.
-__device__ __forceinline__ void mask_kv(f32x16& S, const AttnParams& p, int key, int kpos, int kseg, int qrow0,
-                                        int q0, int lg, const int (&qposv)[16], const int (&qsegv)[16]) {
-  if (!p.q_pos && !p.kv_pos && !p.q_seg) {
+// Element mask of a 32-query x 32-key block with the key per lane and
+// sequential positions: query of register i is row q0 + 8*(i>>2) + 4*lg + (i&3)
+// of the step (rows of the step at qrow0 in the sequence).
+__device__ __forceinline__ void mask_kv_seq(f32x16& S, const AttnParams& p, int key, int qrow0, int q0, int lg) {
+  {
     // sequential positions: a query row r keeps the key iff r >= key + kv_base - q_base
     const int64_t t64 = (int64_t)key + p.kv_pos_base - p.q_pos_base - (qrow0 + q0 + 4 * lg);
     int thr = key < p.Skv ? (p.causal ? (int)max<int64_t>(-64, min<int64_t>(64, t64)) : -64) : 64;
@@ -362,40 +339,74 @@ __device__ __forceinline__ void mask_kv(f32x16& S, const AttnParams& p, int key,
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (8 * (i >> 2) + (i & 3) < thr) S[i] = neg_inf();
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = q0 + 8 * (i >> 2) + 4 * lg + (i & 3);
-    bool ok = key < p.Skv;
-    if (p.causal) {
-      const int qp = p.q_pos ? qposv[i] : p.q_pos_base + qrow0 + r;
-      ok = ok && kpos <= qp;
-    }
-    if (p.q_seg) ok = ok && qsegv[i] == kseg && kseg != -1;
-    if (!ok) S[i] = neg_inf();
   }
 }
 
-// One wave per SIMD: K, V (64 registers), the dK / dV accumulators (128) and
-// a step's products do not fit the 256 registers of two waves per SIMD. With
-// no second workgroup to cover load latency, the step data (Q, dO and the
-// rows' lse, D, positions, segments) comes through a 4-stage DMA ring: the
-// loads of step t+3 are issued at the top of step t. Every wave issues exactly
-// kDmaPerStep loads per step (steps past the end load nothing from empty
-// resources), so one fixed vmcnt wait per step covers the next step.
+// Eight waves in two roles, two waves per SIMD. For key block kbw (32 keys)
+// and query half qh (32 rows of the 64-row step):
+//   P wave  (waves 0-3), step t:   S = Q K^T, mask, P = exp2(S' - lse),
+//                                  hands G = P (1 - t^2) (G = P without a cap)
+//                                  to its partner, then dV^T += dO^T P
+//   dS wave (waves 4-7), step t-1: dP = dO V^T, dS = G (dP - D), dK^T += Q^T dS
+// Each wave runs 16 products per step and holds one accumulator (64
+// registers) and one of K / V (32), so two waves fit a SIMD and each hides
+// the other's latency. The dS waves trail by one step, so the hand-off
+// (bf16, 32 bytes per lane, double-buffered in LDS) needs no barrier of its
+// own: one barrier per step. The step data (Q, dO tiles and the rows' lse, D,
+// positions, segments) comes through a 4-stage LDS-DMA ring filled two steps
+// ahead (the dS waves still read the previous stage), 5 loads per wave and
+// step, with one fixed vmcnt wait per step. Every LDS access in the loop is
+// issued from assembly (see lds_tr_pair_issue), and the loop's barrier is a
+// bare s_barrier for the same reason.
+constexpr int kDkvWaves = 8;
+constexpr int kDkvThreads = 64 * kDkvWaves;
 constexpr int kStages = 4;
-constexpr int kDmaPerStep = 9;
+constexpr int kDmaPerStep = 5;
 // s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt not waited on (gfx9 encoding).
 constexpr int vmcnt_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
+__device__ __forceinline__ void lds_settle8v(bf16x8 (&t)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7]));
+}
+// Four 16-byte reads at a, a+32, a+64, a+96 (the 16 row values of a lane), and their wait.
+__device__ __forceinline__ void lds_rows4(const char* a, f32x4 (&x)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:32\n\t"
+      "ds_read_b128 %2, %4 offset:64\n\t"
+      "ds_read_b128 %3, %4 offset:96\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "v"(lds_addr(a)));
+}
+// Hand-off of 16 bf16 values per lane: two 16-byte halves, 1 KB apart.
+__device__ __forceinline__ void lds_put32(char* a, const bf16x8& lo, const bf16x8& hi) {
+  asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024" : : "v"(lds_addr(a)), "v"(lo), "v"(hi));
+}
+__device__ __forceinline__ void lds_get32(const char* a, bf16x8& lo, bf16x8& hi) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(lo), "=&v"(hi)
+               : "v"(lds_addr(a)));
+}
+// Two 16-byte reads (a and b) and their wait.
+__device__ __forceinline__ void lds_pair4(const char* a, const char* b, f32x4& x, f32x4& y) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(x), "=&v"(y)
+               : "v"(lds_addr(a)), "v"(lds_addr(b)));
+}
+
 template <bool CAP, bool BITS>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkv(BwdParams bp) {
+__global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
   const AttnParams& p = bp.a;
-  // [stage][Q, dO] tiles, then [stage][lse, D, pos, seg] rows: one LDS object for every DMA target
-  __shared__ __attribute__((aligned(16))) __bf16 smem[kStages * 2 * kTileElems + kStages * 4 * 64 * 2];
-  char* const rows_lds = reinterpret_cast<char*>(smem + kStages * 2 * kTileElems);   // [stage][4][64] floats
-  auto row_at = [&](int buf, int arr, int r) { return rows_lds + ((buf * 4 + arr) * 64 + r) * 4; };
+  // [stage][Q, dO] tiles, then [stage][8][64] row floats (lse, D, pos, seg, 4 unused),
+  // then the hand-off: [step parity][kbw*2 + qh][half][64 lanes][16 bytes]
+  constexpr int kRowsBytes = kStages * 8 * 64 * 4;
+  constexpr int kXBytes = 2 * 4 * 2 * 64 * 16;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[kStages * 2 * kTileElems + (kRowsBytes + kXBytes) / 2];
+  char* const rows_lds = reinterpret_cast<char*>(smem + kStages * 2 * kTileElems);
+  char* const xch = rows_lds + kRowsBytes;
+  auto row_at = [&](int buf, int arr, int r) { return rows_lds + ((buf * 8 + arr) * 64 + r) * 4; };
 
   int b, g, kb;
   if (!decode_kv_work(p, b, g, kb)) return;
@@ -403,58 +414,60 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkv(BwdParams bp) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, lg = lane >> 5;
-  const int kbw = w & 1, qh = w >> 1;        // key block and query half of this wave
+  const bool pw = w < 4;                     // P wave (else dS wave)
+  const int kbw = w & 1, qh = (w >> 1) & 1;  // key block and query half
   const int G = p.H / p.Hkv;
   const int key = kb * kBlockKV + 32 * kbw + ln;
   const bool key_ok = key < p.Skv;
+  char* const my_x = xch + (kbw * 2 + qh) * 2 * 1024 + lane * 16;   // parity 0; parity 1 at + 8 KB
 
-  // K and V rows as B operands: lane holds key `key`, dims ds*16 + lg*8 .. +7
-  bf16x8 kt[NDS], vt[NDS];
+  // K (P waves) or V (dS waves) rows as B operands: lane holds key `key`, dims ds*16 + lg*8 .. +7
+  bf16x8 kv[NDS];
   {
     const int64_t ro = (int64_t)b * p.kv_stride_b + ((int64_t)(key_ok ? key : 0) * p.Hkv + g) * D;
-    const __bf16* krow = reinterpret_cast<const __bf16*>(p.k) + ro;
-    const __bf16* vrow = reinterpret_cast<const __bf16*>(p.v) + ro;
+    const __bf16* row = reinterpret_cast<const __bf16*>(pw ? p.k : p.v) + ro;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + ds * 16 + lg * 8);
-      const bf16x8 c = *reinterpret_cast<const bf16x8*>(vrow + ds * 16 + lg * 8);
-      kt[ds] = key_ok ? a : bf16x8{};
-      vt[ds] = key_ok ? c : bf16x8{};
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(row + ds * 16 + lg * 8);
+      kv[ds] = key_ok ? a : bf16x8{};
     }
   }
   const int key_c = key_ok ? key : 0;
   const int kpos = p.kv_pos ? p.kv_pos[(int64_t)b * p.kvm_stride_b + key_c] : p.kv_pos_base + key;
   const int kseg = p.kv_seg ? p.kv_seg[(int64_t)b * p.kvm_stride_b + key_c] : 0;
 
-  f32x16 dK[NDB], dV[NDB];
+  f32x16 acc[NDB];   // dV^T (P waves) or dK^T (dS waves): [dim][key]
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dK[db] = f32x16{};
-    dV[db] = f32x16{};
-  }
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
   const int64_t kcol = (int64_t)b * p.nKb + kb;
   const int ccnt = bp.col_cnt[kcol];
   const auto rows = as_const_space(bp.row_idx + kcol * p.nQb);
-  // tile classes are bytes; read the aligned dword that holds one (a scalar load)
+  const int n_steps = ccnt * 2 * G;          // (q tile, 64-row half, head in group)
   auto tile_class_of = [&](int qb) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p.tile_class + ((int64_t)b * p.nQb + qb) * p.nKb + kb);
     const uint32_t word = *as_const_space(reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3)));
     return (int)((word >> (8 * (a & 3))) & 0xffu);
   };
-  const int n_steps = ccnt * 2 * G;          // (q tile, 64-row half, head in group)
 
   const uint32_t row_bytes = (uint32_t)p.H * D * 2;
-  uint32_t off[4];
-  dma_offsets(off, w, lane, row_bytes);
-  // Step t: q tile rows[t / (2G)], half (t / G) & 1, head g*G + t % G.
+  // DMA: wave w fills rows [8w, 8w + 8) of the Q and dO tiles (two 4-row slabs each)
+  uint32_t off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * w + 4 * i + (lane >> 4);
+    off[i] = (uint32_t)r * row_bytes + ((lane & 15) ^ swz(r)) * 16;
+  }
   auto step_rows = [&](int t, int& qb, int& r0, int& h) {
     qb = rows[t / (2 * G)];
     r0 = qb * kBlockQ + ((t / G) & 1) * 64;
     h = g * G + t % G;
   };
-  // The row array this wave moves: 0 lse, 1 D, 2 positions, 3 segments (empty when absent).
-  const float* row_src = w == 0 ? p.lse : (w == 1 ? bp.delta : reinterpret_cast<const float*>(w == 2 ? p.q_pos : p.q_seg));
+  // The row array this wave moves: waves 0-3 lse, D, positions, segments (empty when
+  // absent); waves 4-7 an empty load into an unused array, so every wave issues the same count.
+  const float* row_src =
+      w == 0 ? p.lse : (w == 1 ? bp.delta : (w == 2 ? reinterpret_cast<const float*>(p.q_pos)
+                                                   : (w == 3 ? reinterpret_cast<const float*>(p.q_seg) : nullptr)));
   const bool row_per_head = w < 2;
   auto stage = [&](int t, int buf) {
     int qb = 0, r0 = p.Sq, h = g * G;
@@ -463,9 +476,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkv(BwdParams bp) {
     const uint32_t bytes = nrows > 0 ? (uint32_t)(nrows - 1) * row_bytes + D * 2 : 0u;
     const int64_t rq = (int64_t)min(r0, p.Sq) * p.H + h;
     __bf16* Qs = smem + buf * 2 * kTileElems;
-    dma_tile(tile_rsrc(reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b + rq * D, bytes), Qs, off, w);
-    dma_tile(tile_rsrc(reinterpret_cast<const __bf16*>(bp.dout) + ((int64_t)b * p.Sq * p.H + rq) * D, bytes),
-             Qs + kTileElems, off, w);
+    const auto qr = tile_rsrc(reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b + rq * D, bytes);
+    const auto orr = tile_rsrc(reinterpret_cast<const __bf16*>(bp.dout) + ((int64_t)b * p.Sq * p.H + rq) * D, bytes);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (__attribute__((address_space(3))) void*)(Qs + (8 * w + 4 * i) * D),
+                                               16, off[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          orr, (__attribute__((address_space(3))) void*)(Qs + kTileElems + (8 * w + 4 * i) * D), 16, off[i], 0, 0, 0);
+    }
     const int64_t rbase = row_per_head ? ((int64_t)b * p.H + h) * p.Sq : (int64_t)b * p.qm_stride_b;
     const uint32_t rbytes = row_src ? (uint32_t)nrows * 4u : 0u;
     const float* rs = row_src ? row_src + rbase + min(r0, p.Sq) : p.lse;
@@ -474,143 +493,162 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkv(BwdParams bp) {
                                              (uint32_t)lane * 4u, 0, 0, 0);
   };
 
-#pragma unroll
-  for (int t = 0; t < kStages - 1; ++t) stage(t, t);
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kStages - 2)));
+  constexpr int kAhead = 2;   // stages in flight beyond the next one
+  stage(0, 0);
+  stage(1, 1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kAhead - 1)));
   __syncthreads();
 
-  for (int t = 0; t < n_steps; ++t) {
-    const int buf = t & (kStages - 1);
-    stage(t + kStages - 1, (t + kStages - 1) & (kStages - 1));   // the buffer step t-1 read
-    int qb, r0, h;
-    step_rows(t, qb, r0, h);
-    const int cl = tile_class_of(qb);
-    const int need_mask = (BITS && cl == 1) ? 2 : ((cl != 2 || (kb + 1) * kBlockKV > p.Skv) ? 1 : 0);
+  const int q0 = 32 * qh;                    // this wave's first row in a step
+  for (int t = 0; t <= n_steps; ++t) {
+    // the buffer of step t+2 was last read by the dS waves in step t-1 (for step t-2)
+    stage(t + kAhead, (t + kAhead) & (kStages - 1));
+    // P waves work on step t, dS waves on step t-1
+    const int u = pw ? t : t - 1;
+    if (u < 0 || u >= n_steps) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kAhead - 1)));
+      __builtin_amdgcn_s_barrier();
+      continue;
+    }
+    const int buf = u & (kStages - 1);
     const char* Qt = reinterpret_cast<const char*>(smem + buf * 2 * kTileElems);
     const char* Ot = Qt + kTileElems * 2;
-    const int q0 = 32 * qh;                  // this wave's first row in the step
+    char* const x_u = my_x + (u & 1) * 8192;
 
-    // S = Q K^T and dP = dO V^T for 32 queries x 32 keys: A = query rows from LDS
-    // (issued from assembly, like every LDS read of DMA-filled data in this loop)
-    f32x16 S = f32x16{}, dP = f32x16{};
+    f32x16 X = f32x16{};   // S (P waves) or dP (dS waves)
     {
-      bf16x8 a[16];
+      const char* T = pw ? Qt : Ot;
+      bf16x8 a[8];
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         const int r = q0 + ln, c = 2 * ds + lg;
-        a[ds] = lds_b128_issue(Qt + r * 256 + ((c ^ swz(r)) * 16));
-        a[NDS + ds] = lds_b128_issue(Ot + r * 256 + ((c ^ swz(r)) * 16));
+        a[ds] = lds_b128_issue(T + r * 256 + ((c ^ swz(r)) * 16));
       }
-      lds_settle16(a);
+      lds_settle8v(a);
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds], kt[ds], S, 0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[NDS + ds], vt[ds], dP, 0, 0, 0);
+      for (int ds = 0; ds < NDS; ++ds) X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds], kv[ds], X, 0, 0, 0);
+    }
+    if (pw) {
+      int qb, r0, h;
+      step_rows(u, qb, r0, h);
+      const int cl = tile_class_of(qb);
+      const int need_mask = (BITS && cl == 1) ? 2 : ((cl != 2 || (kb + 1) * kBlockKV > p.Skv) ? 1 : 0);
+      if constexpr (CAP) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) X[i] = capped_log2(X[i], p.cap_k2, p.cap_log2);
       }
-    }
-    if constexpr (CAP) {
+      if (BITS && need_mask == 2) {
+        // bits of the tile: row (step half * 64 + q0 + r), word kbw, bit ln
+        const uint32_t* tb = p.mask_bits + (((int64_t)b * p.nQb + qb) * p.nKb + kb) * kBlockQ * 2 +
+                             (int64_t)((r0 - qb * kBlockQ) + q0 + 4 * lg) * 2 + kbw;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) S[i] = capped_log2(S[i], p.cap_k2, p.cap_log2);
-    }
-    if (BITS && need_mask == 2) {
-      // bits of the tile: row (step half * 64 + q0 + r), word kbw, bit ln
-      const uint32_t* tb = p.mask_bits + (((int64_t)b * p.nQb + qb) * p.nKb + kb) * kBlockQ * 2 +
-                           (int64_t)((r0 - qb * kBlockQ) + q0 + 4 * lg) * 2 + kbw;
+        for (int i = 0; i < 16; ++i)
+          if (((tb[(8 * (i >> 2) + (i & 3)) * 2] >> ln) & 1u) == 0u) X[i] = neg_inf();
+      } else if (need_mask) {
+        if (!p.q_pos && !p.kv_pos && !p.q_seg) {
+          mask_kv_seq(X, p, key, r0, q0, lg);
+        } else {
+          // explicit positions / segments: the rows' values four at a time
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (((tb[(8 * (i >> 2) + (i & 3)) * 2] >> ln) & 1u) == 0u) S[i] = neg_inf();
-    } else if (need_mask) {
-      int qposv[16], qsegv[16];
-      if (p.q_pos || p.q_seg) {
-        f32x4 a[4], c[4];
-        lds_rows8(row_at(buf, 2, q0 + 4 * lg), row_at(buf, 3, q0 + 4 * lg), a, c);
+          for (int j = 0; j < 4; ++j) {
+            f32x4 qpv, qsv;
+            lds_pair4(row_at(buf, 2, q0 + 8 * j + 4 * lg), row_at(buf, 3, q0 + 8 * j + 4 * lg), qpv, qsv);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            qposv[4 * j + e] = __float_as_int(a[j][e]);
-            qsegv[4 * j + e] = __float_as_int(c[j][e]);
+            for (int e = 0; e < 4; ++e) {
+              const int r = q0 + 8 * j + 4 * lg + e;
+              bool ok = key < p.Skv;
+              if (p.causal) ok = ok && kpos <= (p.q_pos ? __float_as_int(qpv[e]) : p.q_pos_base + r0 + r);
+              if (p.q_seg) ok = ok && __float_as_int(qsv[e]) == kseg && kseg != -1;
+              if (!ok) X[4 * j + e] = neg_inf();
+            }
           }
-      }
-      mask_kv(S, p, key, kpos, kseg, r0, q0, lg, qposv, qsegv);
-    }
-    // Row values: lse in log2 units, +inf where the row has no weight (lse = -inf);
-    // rows past Sq read 0 and have zero Q / dO rows, so they add nothing.
-    float lse2v[16], dlv[16];
-    {
-      f32x4 la[4], da[4];   // rows q0 + 8j + 4*lg + 0..3, j = 0..3
-      lds_rows8(row_at(buf, 0, q0 + 4 * lg), row_at(buf, 1, q0 + 4 * lg), la, da);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lse2v[4 * j + e] = la[j][e] == neg_inf() ? __builtin_inff() : la[j][e] * kLog2e;
-          dlv[4 * j + e] = da[j][e];
         }
-    }
-    f32x16 Pw;
-    weights_and_grads<CAP>(S, dP, Pw, lse2v, dlv, p);
-    bf16x8 Pb[2], DSb[2];
-    pack_b(Pw, Pb);
-    pack_b(S, DSb);
-    __builtin_amdgcn_sched_barrier(0);
-    // dV^T += dO^T P and dK^T += Q^T dS: A = dO / Q read transposed (lane = dim)
-    {
-      TrPair ot8[8], qt8[8];
-#pragma unroll
-      for (int f = 0; f < 8; ++f) ot8[f] = lds_tr(Ot, q0 + (f / NDB) * 16, f % NDB, lane);
-#pragma unroll
-      for (int f = 0; f < 8; ++f) qt8[f] = lds_tr(Qt, q0 + (f / NDB) * 16, f % NDB, lane);
-      lds_settle(ot8);
-      lds_settle(qt8);
-#pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const int ks = f / NDB, db = f % NDB;
-        dV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(ot8[f]), Pb[ks], dV[db], 0, 0, 0);
-        dK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(qt8[f]), DSb[ks], dK[db], 0, 0, 0);
       }
+      f32x4 la[4];   // lse of rows q0 + 8j + 4*lg + 0..3
+      lds_rows4(row_at(buf, 0, q0 + 4 * lg), la);
+      // P in place of S; G = P (1 - t^2) goes to the partner (G = P without a cap)
+      f32x16 Gw;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float l = la[i >> 2][i & 3];
+        const float l2 = l == neg_inf() ? __builtin_inff() : l * kLog2e;
+        if constexpr (CAP) {
+          const float tt = fmaxf(X[i], -p.cap_log2) * (1.0f / p.cap_log2);
+          X[i] = fast_exp2(X[i] - l2);
+          Gw[i] = X[i] * __builtin_fmaf(-tt, tt, 1.0f);
+        } else {
+          X[i] = fast_exp2(__builtin_fmaf(X[i], p.scale_log2, -l2));
+        }
+      }
+      bf16x8 Pb[2];
+      pack_b(X, Pb);
+      if constexpr (CAP) {
+        bf16x8 Gb[2];
+        pack_b(Gw, Gb);
+        lds_put32(x_u, Gb[0], Gb[1]);
+      } else {
+        lds_put32(x_u, Pb[0], Pb[1]);
+      }
+      // dV^T += dO^T P
+      TrPair tr[8];
+#pragma unroll
+      for (int f = 0; f < 8; ++f) tr[f] = lds_tr(Ot, q0 + (f / NDB) * 16, f % NDB, lane);
+      lds_settle(tr);
+#pragma unroll
+      for (int f = 0; f < 8; ++f)
+        acc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(tr[f]), Pb[f / NDB], acc[f % NDB], 0, 0, 0);
+    } else {
+      // dS = G (dP - D), dK^T += Q^T dS (the partner wrote G in the previous step)
+      bf16x8 gb[2];
+      lds_get32(x_u, gb[0], gb[1]);
+      f32x4 da[4];   // D of rows q0 + 8j + 4*lg + 0..3
+      lds_rows4(row_at(buf, 1, q0 + 4 * lg), da);
+      f32x16 dS;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dS[i] = (float)gb[i >> 3][i & 7] * (X[i] - da[i >> 2][i & 3]);
+      bf16x8 DSb[2];
+      pack_b(dS, DSb);
+      TrPair tr[8];
+#pragma unroll
+      for (int f = 0; f < 8; ++f) tr[f] = lds_tr(Qt, q0 + (f / NDB) * 16, f % NDB, lane);
+      lds_settle(tr);
+#pragma unroll
+      for (int f = 0; f < 8; ++f)
+        acc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(tr[f]), DSb[f / NDB], acc[f % NDB], 0, 0, 0);
     }
-    // Step t+1 has landed once at most the loads of steps t+2, t+3 are
-    // outstanding. A bare barrier: every LDS read in this loop is issued from
-    // assembly and has completed, and the fences of __syncthreads would wait
-    // for the loads still in flight.
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kStages - 2)));
+    // Step t+1 has landed once at most the loads of step t+2 are outstanding
+    // (the LDS stores and reads above have all been waited for).
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kAhead - 1)));
     __builtin_amdgcn_s_barrier();
   }
   __builtin_amdgcn_s_waitcnt(0);   // the empty loads of the last stages
   __syncthreads();
 
-  // The two query halves of each key block: waves 2, 3 hand theirs to waves 0, 1.
-  float* red = reinterpret_cast<float*>(smem);   // [key block][2 tensors][NDB][16][64 lanes]
+  // The two query halves of each (role, key block): qh = 1 hands its sum to qh = 0.
+  float* red = reinterpret_cast<float*>(smem);   // [role][key block][NDB][16][64 lanes]
+  const int slot = (pw ? 0 : 2) + kbw;
   if (qh == 1) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        red[(((kbw * 2 + 0) * NDB + db) * 16 + i) * 64 + lane] = dK[db][i];
-        red[(((kbw * 2 + 1) * NDB + db) * 16 + i) * 64 + lane] = dV[db][i];
-      }
+      for (int i = 0; i < 16; ++i) red[((slot * NDB + db) * 16 + i) * 64 + lane] = acc[db][i];
   }
   __syncthreads();
   if (qh == 1 || !key_ok) return;
-  const float sc = p.scale_log2 * kLn2;
-  const int64_t ro = (int64_t)b * bp.dkv_stride_b + ((int64_t)key * p.Hkv + g) * D;
-  float* dk = bp.dk + ro;
-  float* dv = bp.dv + ro;
+  const float sc = pw ? 1.0f : p.scale_log2 * kLn2;   // dk carries the score scale
+  float* dst = (pw ? bp.dv : bp.dk) + (int64_t)b * bp.dkv_stride_b + ((int64_t)key * p.Hkv + g) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int col = db * 32 + 8 * i4 + 4 * lg;
-      float a[4], c[4];
+      float a[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * i4 + e;
-        a[e] = (dK[db][i] + red[(((kbw * 2 + 0) * NDB + db) * 16 + i) * 64 + lane]) * sc;
-        c[e] = dV[db][i] + red[(((kbw * 2 + 1) * NDB + db) * 16 + i) * 64 + lane];
+        a[e] = (acc[db][i] + red[((slot * NDB + db) * 16 + i) * 64 + lane]) * sc;
       }
-      *reinterpret_cast<float4*>(dk + col) = make_float4(a[0], a[1], a[2], a[3]);
-      *reinterpret_cast<float4*>(dv + col) = make_float4(c[0], c[1], c[2], c[3]);
+      *reinterpret_cast<float4*>(dst + col) = make_float4(a[0], a[1], a[2], a[3]);
     }
 }
 
@@ -697,9 +735,9 @@ __global__ __launch_bounds__(256) void col_lists_kernel(MaskParams p, int32_t* c
 }
 
 template <typename K>
-hipError_t launch_grid(K kernel, int64_t items, const BwdParams& p, hipStream_t s) {
+hipError_t launch_grid(K kernel, int64_t items, int threads, const BwdParams& p, hipStream_t s) {
   const int64_t grid = 8 * ((items + 7) / 8);
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -712,13 +750,15 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s) {
   const int64_t kv_items = (int64_t)a.B * a.Hkv * a.nKb;
   hipError_t e;
   if (q_items > 0) {
-    if (cap) e = bits ? launch_grid(attn_bwd_dq<true, true>, q_items, p, s) : launch_grid(attn_bwd_dq<true, false>, q_items, p, s);
-    else e = bits ? launch_grid(attn_bwd_dq<false, true>, q_items, p, s) : launch_grid(attn_bwd_dq<false, false>, q_items, p, s);
+    const int t = kThreads;
+    if (cap) e = bits ? launch_grid(attn_bwd_dq<true, true>, q_items, t, p, s) : launch_grid(attn_bwd_dq<true, false>, q_items, t, p, s);
+    else e = bits ? launch_grid(attn_bwd_dq<false, true>, q_items, t, p, s) : launch_grid(attn_bwd_dq<false, false>, q_items, t, p, s);
     if (e != hipSuccess) return e;
   }
   if (kv_items > 0) {
-    if (cap) e = bits ? launch_grid(attn_bwd_dkv<true, true>, kv_items, p, s) : launch_grid(attn_bwd_dkv<true, false>, kv_items, p, s);
-    else e = bits ? launch_grid(attn_bwd_dkv<false, true>, kv_items, p, s) : launch_grid(attn_bwd_dkv<false, false>, kv_items, p, s);
+    const int t = kDkvThreads;
+    if (cap) e = bits ? launch_grid(attn_bwd_dkv<true, true>, kv_items, t, p, s) : launch_grid(attn_bwd_dkv<true, false>, kv_items, t, p, s);
+    else e = bits ? launch_grid(attn_bwd_dkv<false, true>, kv_items, t, p, s) : launch_grid(attn_bwd_dkv<false, false>, kv_items, t, p, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
