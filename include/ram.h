@@ -196,7 +196,7 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
  * (dk, dv summed over the query heads sharing a KV head), and for a sink
  *   dsink_h = - sum over batch rows and queries of exp(sink_h - lse_i) D_i,
  * counted once (the sink enters the forward once). Built for bf16 with
- * D = 128; other dtypes and head dims return RAM_ERR_UNSUPPORTED.
+ * D = 64 or 128; other dtypes and head dims return RAM_ERR_UNSUPPORTED.
  * out, dout: [B, Sq, H, D] dense in desc->dtype; lse: float32 [B, H, Sq] (as
  * the forward wrote them). */
 

@@ -9,7 +9,7 @@
 //   dq_i += scale * sum_j ds_ij k_j,  dk_j = scale * sum_i ds_ij q_i,
 //   dv_j = sum_i p_ij dout_i   (dk, dv summed over the heads sharing a KV head).
 //
-// Design for gfx950 (bf16, D = 128; v_mfma_f32_32x32x16_bf16 throughout):
+// Design for gfx950 (bf16, D = 128 or 64; v_mfma_f32_32x32x16_bf16 throughout):
 //  * dq: one workgroup per (batch, head, 128-row q tile), the forward's layout:
 //    S^T = K Q^T and dP^T = V dO^T with Q and dO held in registers as B
 //    operands (a lane owns one query row), then dQ^T += K^T dS^T with dS^T
@@ -24,10 +24,11 @@
 //    halves through LDS at the end. No atomics anywhere: results are
 //    deterministic.
 //  * Tiles move HBM -> LDS by DMA. Every tile is read both row-wise and with
-//    the transposing read, so 16-byte chunks are swizzled by
-//    chunk ^ (4*(row & 3) + ((row >> 2) & 3)): 16 consecutive rows put one
-//    logical chunk in 16 distinct bank groups, and the 4 rows x 64 bytes of a
-//    transposing read cover all 64 banks.
+//    the transposing read, so 16-byte chunks are swizzled: with 256-byte rows
+//    (D = 128) by chunk ^ (4*(row & 3) + ((row >> 2) & 3)), with 128-byte rows
+//    (D = 64) by chunk ^ (4*((row >> 1) & 1) + ((row >> 2) & 3)). Either way
+//    16 consecutive rows put one logical chunk in 16 distinct bank groups,
+//    and the 4 rows x 64 bytes of a transposing read cover all 64 banks.
 //  * Row values (lse, D) of rows past Sq or with lse = -inf become +inf / 0,
 //    so their weights are exactly 0.
 #include <cstdlib>
@@ -40,44 +41,69 @@ namespace {
 
 using namespace attn;
 
-constexpr int D = 128;
-constexpr int NDS = D / 16;
-constexpr int NDB = D / 32;
-constexpr int kTileElems = 64 * D;   // one 64-row tile (elements)
+// Tile geometry for head dim D: 64-row tiles of D bf16 (2D-byte rows, D/8 chunks of 16 bytes).
+template <int D>
+struct Geo {
+  static constexpr int NDS = D / 16;            // 16-deep MFMA steps over D
+  static constexpr int NDB = D / 32;            // 32-wide blocks of D
+  static constexpr int kTileElems = 64 * D;     // one 64-row tile (elements)
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = D / 8;         // 16-byte chunks per row
+  static constexpr int kSlabRows = 64 / kChunks;  // rows one 16-byte DMA of a wave fills
+};
 
-__device__ __forceinline__ int swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
+  else return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
 
 // Byte offsets of this lane's DMA chunks: wave w fills rows [16w, 16w + 16) of
-// a 64-row tile in four 4-row slabs; lane l of slab i writes physical chunk
-// l & 15 of row 16w + 4i + (l >> 4), fetched from the logical chunk at that
-// position. `row_bytes` is the global row stride.
-__device__ __forceinline__ void dma_offsets(uint32_t (&off)[4], int w, int lane, uint32_t row_bytes) {
+// a 64-row tile in slabs of kSlabRows rows; lane l of slab i writes physical
+// chunk l % kChunks of row 16w + kSlabRows*i + l / kChunks, fetched from the
+// logical chunk at that position. `row_bytes` is the global row stride.
+template <int D, int N>
+__device__ __forceinline__ void dma_offsets(uint32_t (&off)[N], int w, int lane, uint32_t row_bytes) {
+  using Gm = Geo<D>;
+  static_assert(N == 16 / Gm::kSlabRows, "one offset per slab");
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * w + 4 * i + (lane >> 4);
-    off[i] = (uint32_t)r * row_bytes + ((lane & 15) ^ swz(r)) * 16;
+  for (int i = 0; i < N; ++i) {
+    const int r = 16 * w + Gm::kSlabRows * i + lane / Gm::kChunks;
+    off[i] = (uint32_t)r * row_bytes + ((lane % Gm::kChunks) ^ swz<D>(r)) * 16;
   }
 }
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, __bf16* tile, const uint32_t (&off)[4], int w) {
+// LDS-DMA of 16 / 4 bytes per lane. Kernel lambdas reach the builtin only
+// through these plain functions: a builtin call whose arguments depend on a
+// template parameter inside a lambda (which the host pass also compiles) makes
+// the host pass drop the kernel's launch stub without a diagnostic.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, 0);
+}
+// (D is a constant once inlined)
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, __bf16* tile, const uint32_t* off, int w, int D) {
+  const int slab_rows = 512 / D, n = 16 / slab_rows;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(tile + (16 * w + 4 * i) * D),
-                                             16, off[i], 0, 0, 0);
+  for (int i = 0; i < n; ++i) dma16(r, tile + (16 * w + slab_rows * i) * D, off[i]);
 }
 
 // Row read (16 bytes): row `row`, logical chunk c.
+template <int D>
 __device__ __forceinline__ bf16x8 lds_row(const char* tile, int row, int c) {
-  return *reinterpret_cast<const bf16x8*>(tile + row * 256 + ((c ^ swz(row)) * 16));
+  return *reinterpret_cast<const bf16x8*>(tile + row * (2 * D) + ((c ^ swz<D>(row)) * 16));
 }
 // Transposed operand of 32 columns x 16 rows starting at row r0, column block db:
 // lane receives column db*32 + (lane & 31) at rows r0 + 4*lg + 0..3 and r0 + 8 + 4*lg + 0..3.
 // Issued from assembly (see lds_tr_pair_issue): the value must pass lds_settle().
+template <int D>
 __device__ __forceinline__ TrPair lds_tr(const char* tile, int r0, int db, int lane) {
   const int lg = lane >> 5, r4 = (lane & 15) >> 2, hs = (lane >> 4) & 1;
   const int c = 4 * db + 2 * hs + ((lane & 3) >> 1);
   const int ra = r0 + 4 * lg + r4, rb = ra + 8;
-  const char* pa = tile + ra * 256 + ((c ^ swz(ra)) * 16) + (lane & 1) * 8;
-  const char* pb = tile + rb * 256 + ((c ^ swz(rb)) * 16) + (lane & 1) * 8;
+  const char* pa = tile + ra * (2 * D) + ((c ^ swz<D>(ra)) * 16) + (lane & 1) * 8;
+  const char* pb = tile + rb * (2 * D) + ((c ^ swz<D>(rb)) * 16) + (lane & 1) * 8;
   return lds_tr_pair_issue2(pa, pb);
 }
 
@@ -119,9 +145,11 @@ __device__ __forceinline__ void weights_and_grads(f32x16& S, const f32x16& dP, f
 }
 
 // ------------------------------------------------------------------------------ dq
-template <bool CAP, bool BITS>
+template <int D, bool CAP, bool BITS>
 __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
   const AttnParams& p = bp.a;
+  using Gm = Geo<D>;
+  constexpr int NDS = Gm::NDS, NDB = Gm::NDB, kTileElems = Gm::kTileElems;
   constexpr int BK = kBlockKV;
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * kTileElems];   // [stage][K, V]
 
@@ -183,14 +211,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
   const uint32_t row_bytes = (uint32_t)krs * 2;
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.kv_stride_b + g * D;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.kv_stride_b + g * D;
-  uint32_t off[4];
-  dma_offsets(off, w, lane, row_bytes);
+  uint32_t off[16 / Gm::kSlabRows];
+  dma_offsets<D>(off, w, lane, row_bytes);
   auto dma = [&](int kb, int buf) {
     const int k0 = kb * BK;
     const uint32_t bytes = (uint32_t)min(p.Skv - k0, BK) * row_bytes;
     __bf16* Ks = smem + buf * 2 * kTileElems;
-    dma_tile(tile_rsrc(kbase + (int64_t)k0 * krs, bytes), Ks, off, w);
-    dma_tile(tile_rsrc(vbase + (int64_t)k0 * krs, bytes), Ks + kTileElems, off, w);
+    dma_tile(tile_rsrc(kbase + (int64_t)k0 * krs, bytes), Ks, off, w, D);
+    dma_tile(tile_rsrc(vbase + (int64_t)k0 * krs, bytes), Ks + kTileElems, off, w, D);
   };
   if (p.Skv % BK) {
     // a ragged last tile leaves rows unwritten: start from zeros (finite, masked)
@@ -227,21 +255,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
       S[kb2] = f32x16{};
       dP[kb2] = f32x16{};
     }
-    // in four phases of 8 operands each, so that few operands are live at once
+    // in phases of 8 operands each (NDS / 4 per product), so that few operands are live at once
+    constexpr int kPh = NDS / 4;
 #pragma unroll
-    for (int ph = 0; ph < 4; ++ph) {
-      const char* T = (ph < 2) ? Kt : Vt;
+    for (int ph = 0; ph < 2 * kPh; ++ph) {
+      const char* T = (ph < kPh) ? Kt : Vt;
       bf16x8 a[4][2];
 #pragma unroll
       for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) a[d4][kb2] = lds_row(T, kb2 * 32 + ln, 2 * ((ph & 1) * 4 + d4) + lg);
+        for (int kb2 = 0; kb2 < 2; ++kb2) a[d4][kb2] = lds_row<D>(T, kb2 * 32 + ln, 2 * ((ph % kPh) * 4 + d4) + lg);
 #pragma unroll
       for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const int ds = (ph & 1) * 4 + d4;
-          if (ph < 2) S[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4][kb2], qf[ds], S[kb2], 0, 0, 0);
+          const int ds = (ph % kPh) * 4 + d4;
+          if (ph < kPh) S[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4][kb2], qf[ds], S[kb2], 0, 0, 0);
           else dP[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4][kb2], dof[ds], dP[kb2], 0, 0, 0);
         }
       __builtin_amdgcn_sched_barrier(0);
@@ -266,16 +295,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
       DS[2 * kb2] = two[0];
       DS[2 * kb2 + 1] = two[1];
     }
-    // dQ^T += K^T dS^T: A = K read transposed (lane = dim), B = dS^T (lane = query)
+    // dQ^T += K^T dS^T: A = K read transposed (lane = dim), B = dS^T (lane = query);
+    // 4 * NDB products in batches of 8
+    constexpr int kKsPer = 8 / NDB;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < 4 / kKsPer; ++half) {
       TrPair kt8[8];
 #pragma unroll
-      for (int f = 0; f < 8; ++f) kt8[f] = lds_tr(Kt, (half * 2 + f / NDB) * 16, f % NDB, lane);
+      for (int f = 0; f < 8; ++f) kt8[f] = lds_tr<D>(Kt, (half * kKsPer + f / NDB) * 16, f % NDB, lane);
       lds_settle(kt8);
 #pragma unroll
       for (int f = 0; f < 8; ++f) {
-        const int ks = half * 2 + f / NDB, db = f % NDB;
+        const int ks = half * kKsPer + f / NDB, db = f % NDB;
         dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(kt8[f]), DS[ks], dQ[db], 0, 0, 0);
       }
     }
@@ -355,19 +386,26 @@ __device__ __forceinline__ void mask_kv_seq(f32x16& S, const AttnParams& p, int 
 // own: one barrier per step. The step data (Q, dO tiles and the rows' lse, D,
 // positions, segments) comes through a 4-stage LDS-DMA ring filled two steps
 // ahead (the dS waves still read the previous stage), 5 loads per wave and
-// step, with one fixed vmcnt wait per step. Every LDS access in the loop is
+// step (3 at D = 64), with one fixed vmcnt wait per step. Every LDS access in the loop is
 // issued from assembly (see lds_tr_pair_issue), and the loop's barrier is a
 // bare s_barrier for the same reason.
 constexpr int kDkvWaves = 8;
 constexpr int kDkvThreads = 64 * kDkvWaves;
 constexpr int kStages = 4;
-constexpr int kDmaPerStep = 5;
 // s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt not waited on (gfx9 encoding).
 constexpr int vmcnt_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-__device__ __forceinline__ void lds_settle8v(bf16x8 (&t)[8]) {
+__device__ __forceinline__ void lds_settle_v(bf16x8 (&t)[8]) {
   asm volatile("s_waitcnt lgkmcnt(0)"
                : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7]));
+}
+__device__ __forceinline__ void lds_settle(TrPair (&t)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(t[0].lo), "+v"(t[0].hi), "+v"(t[1].lo), "+v"(t[1].hi), "+v"(t[2].lo), "+v"(t[2].hi),
+                 "+v"(t[3].lo), "+v"(t[3].hi));
+}
+__device__ __forceinline__ void lds_settle_v(bf16x8 (&t)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
 }
 // Four 16-byte reads at a, a+32, a+64, a+96 (the 16 row values of a lane), and their wait.
 __device__ __forceinline__ void lds_rows4(const char* a, f32x4 (&x)[4]) {
@@ -396,9 +434,13 @@ __device__ __forceinline__ void lds_pair4(const char* a, const char* b, f32x4& x
                : "v"(lds_addr(a)), "v"(lds_addr(b)));
 }
 
-template <bool CAP, bool BITS>
+template <int D, bool CAP, bool BITS>
 __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
   const AttnParams& p = bp.a;
+  using Gm = Geo<D>;
+  constexpr int NDS = Gm::NDS, NDB = Gm::NDB, kTileElems = Gm::kTileElems;
+  constexpr int kSlabs = 8 / Gm::kSlabRows;        // DMA slabs per wave and tile (8 rows)
+  constexpr int kDmaPerStep = 2 * kSlabs + 1;      // Q, dO slabs and one row array
   // [stage][Q, dO] tiles, then [stage][8][64] row floats (lse, D, pos, seg, 4 unused),
   // then the hand-off: [step parity][kbw*2 + qh][half][64 lanes][16 bytes]
   constexpr int kRowsBytes = kStages * 8 * 64 * 4;
@@ -451,12 +493,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
   };
 
   const uint32_t row_bytes = (uint32_t)p.H * D * 2;
-  // DMA: wave w fills rows [8w, 8w + 8) of the Q and dO tiles (two 4-row slabs each)
-  uint32_t off[2];
+  // DMA: wave w fills rows [8w, 8w + 8) of the Q and dO tiles (kSlabs slabs each)
+  uint32_t off[kSlabs];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 8 * w + 4 * i + (lane >> 4);
-    off[i] = (uint32_t)r * row_bytes + ((lane & 15) ^ swz(r)) * 16;
+  for (int i = 0; i < kSlabs; ++i) {
+    const int r = 8 * w + Gm::kSlabRows * i + lane / Gm::kChunks;
+    off[i] = (uint32_t)r * row_bytes + ((lane % Gm::kChunks) ^ swz<D>(r)) * 16;
   }
   auto step_rows = [&](int t, int& qb, int& r0, int& h) {
     qb = rows[t / (2 * G)];
@@ -479,18 +521,15 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
     const auto qr = tile_rsrc(reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b + rq * D, bytes);
     const auto orr = tile_rsrc(reinterpret_cast<const __bf16*>(bp.dout) + ((int64_t)b * p.Sq * p.H + rq) * D, bytes);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (__attribute__((address_space(3))) void*)(Qs + (8 * w + 4 * i) * D),
-                                               16, off[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          orr, (__attribute__((address_space(3))) void*)(Qs + kTileElems + (8 * w + 4 * i) * D), 16, off[i], 0, 0, 0);
+    for (int i = 0; i < kSlabs; ++i) {
+      const int r = 8 * w + Gm::kSlabRows * i;
+      dma16(qr, Qs + r * D, off[i]);
+      dma16(orr, Qs + kTileElems + r * D, off[i]);
     }
     const int64_t rbase = row_per_head ? ((int64_t)b * p.H + h) * p.Sq : (int64_t)b * p.qm_stride_b;
     const uint32_t rbytes = row_src ? (uint32_t)nrows * 4u : 0u;
     const float* rs = row_src ? row_src + rbase + min(r0, p.Sq) : p.lse;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(tile_rsrc(rs, rbytes),
-                                             (__attribute__((address_space(3))) void*)(row_at(buf, w, 0)), 4,
-                                             (uint32_t)lane * 4u, 0, 0, 0);
+    dma4(tile_rsrc(rs, rbytes), row_at(buf, w, 0), (uint32_t)lane * 4u);
   };
 
   constexpr int kAhead = 2;   // stages in flight beyond the next one
@@ -518,13 +557,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
     f32x16 X = f32x16{};   // S (P waves) or dP (dS waves)
     {
       const char* T = pw ? Qt : Ot;
-      bf16x8 a[8];
+      bf16x8 a[NDS];
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         const int r = q0 + ln, c = 2 * ds + lg;
-        a[ds] = lds_b128_issue(T + r * 256 + ((c ^ swz(r)) * 16));
+        a[ds] = lds_b128_issue(T + r * (2 * D) + ((c ^ swz<D>(r)) * 16));
       }
-      lds_settle8v(a);
+      lds_settle_v(a);
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds], kv[ds], X, 0, 0, 0);
     }
@@ -590,12 +629,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
         lds_put32(x_u, Pb[0], Pb[1]);
       }
       // dV^T += dO^T P
-      TrPair tr[8];
+      TrPair tr[2 * NDB];
 #pragma unroll
-      for (int f = 0; f < 8; ++f) tr[f] = lds_tr(Ot, q0 + (f / NDB) * 16, f % NDB, lane);
+      for (int f = 0; f < 2 * NDB; ++f) tr[f] = lds_tr<D>(Ot, q0 + (f / NDB) * 16, f % NDB, lane);
       lds_settle(tr);
 #pragma unroll
-      for (int f = 0; f < 8; ++f)
+      for (int f = 0; f < 2 * NDB; ++f)
         acc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(tr[f]), Pb[f / NDB], acc[f % NDB], 0, 0, 0);
     } else {
       // dS = G (dP - D), dK^T += Q^T dS (the partner wrote G in the previous step)
@@ -608,12 +647,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
       for (int i = 0; i < 16; ++i) dS[i] = (float)gb[i >> 3][i & 7] * (X[i] - da[i >> 2][i & 3]);
       bf16x8 DSb[2];
       pack_b(dS, DSb);
-      TrPair tr[8];
+      TrPair tr[2 * NDB];
 #pragma unroll
-      for (int f = 0; f < 8; ++f) tr[f] = lds_tr(Qt, q0 + (f / NDB) * 16, f % NDB, lane);
+      for (int f = 0; f < 2 * NDB; ++f) tr[f] = lds_tr<D>(Qt, q0 + (f / NDB) * 16, f % NDB, lane);
       lds_settle(tr);
 #pragma unroll
-      for (int f = 0; f < 8; ++f)
+      for (int f = 0; f < 2 * NDB; ++f)
         acc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(tr[f]), DSb[f / NDB], acc[f % NDB], 0, 0, 0);
     }
     // Step t+1 has landed once at most the loads of step t+2 are outstanding
@@ -741,9 +780,8 @@ hipError_t launch_grid(K kernel, int64_t items, int threads, const BwdParams& p,
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s) {
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
   const AttnParams& a = p.a;
   const bool cap = a.softcap_on != 0, bits = a.mask_bits != nullptr;
   const int64_t q_items = (int64_t)a.B * a.H * a.nQb;
@@ -751,17 +789,23 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s) {
   hipError_t e;
   if (q_items > 0) {
     const int t = kThreads;
-    if (cap) e = bits ? launch_grid(attn_bwd_dq<true, true>, q_items, t, p, s) : launch_grid(attn_bwd_dq<true, false>, q_items, t, p, s);
-    else e = bits ? launch_grid(attn_bwd_dq<false, true>, q_items, t, p, s) : launch_grid(attn_bwd_dq<false, false>, q_items, t, p, s);
+    if (cap) e = bits ? launch_grid(attn_bwd_dq<D, true, true>, q_items, t, p, s) : launch_grid(attn_bwd_dq<D, true, false>, q_items, t, p, s);
+    else e = bits ? launch_grid(attn_bwd_dq<D, false, true>, q_items, t, p, s) : launch_grid(attn_bwd_dq<D, false, false>, q_items, t, p, s);
     if (e != hipSuccess) return e;
   }
   if (kv_items > 0) {
     const int t = kDkvThreads;
-    if (cap) e = bits ? launch_grid(attn_bwd_dkv<true, true>, kv_items, t, p, s) : launch_grid(attn_bwd_dkv<true, false>, kv_items, t, p, s);
-    else e = bits ? launch_grid(attn_bwd_dkv<false, true>, kv_items, t, p, s) : launch_grid(attn_bwd_dkv<false, false>, kv_items, t, p, s);
+    if (cap) e = bits ? launch_grid(attn_bwd_dkv<D, true, true>, kv_items, t, p, s) : launch_grid(attn_bwd_dkv<D, true, false>, kv_items, t, p, s);
+    else e = bits ? launch_grid(attn_bwd_dkv<D, false, true>, kv_items, t, p, s) : launch_grid(attn_bwd_dkv<D, false, false>, kv_items, t, p, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s) {
+  return p.a.D == 64 ? launch_bwd_d<64>(p, s) : launch_bwd_d<128>(p, s);
 }
 
 hipError_t launch_bwd_prep(int B, int Sq, int H, int Dd, const void* out, const void* dout, const float* lse,

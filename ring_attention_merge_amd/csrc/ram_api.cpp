@@ -152,7 +152,7 @@ ram_status check_col_lists(const ram_block_mask* bm, const ram_attn_desc* d, boo
 // What the backward kernels are built for.
 ram_status check_bwd_support(const ram_attn_desc* d) {
   if (d->dtype != RAM_BF16) return fail(RAM_ERR_UNSUPPORTED, "backward dtype %d (built: bf16)", d->dtype);
-  if (d->D != 128) return fail(RAM_ERR_UNSUPPORTED, "backward head dim D=%d (built: 128)", d->D);
+  if (d->D != 128 && d->D != 64) return fail(RAM_ERR_UNSUPPORTED, "backward head dim D=%d (built: 64, 128)", d->D);
   return RAM_OK;
 }
 
@@ -538,7 +538,7 @@ ram_status attn_bwd_chunk(const ram_attn_desc* desc, const void* q, const void* 
 
 size_t ring_attn_bwd_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src) {
   if (!desc || n_chunks < 1 || desc->B < 0 || desc->Sq < 0 || desc->Skv < 0 || desc->H < 1 || desc->Hkv < 1 ||
-      desc->D != 128)
+      (desc->D != 64 && desc->D != 128))
     return 0;
   ram_attn_desc dt = *desc;
   dt.block_q = ram::kBlockQ;

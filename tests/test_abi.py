@@ -223,8 +223,9 @@ def test_backward_validation(lib):
                          kw.get("dout", FAKE), kw.get("lse", FAKE2), kw.get("delta", FAKE2),
                          ctypes.byref(kw.get("src", _src())), ctypes.byref(kw.get("bm", _bm(col_cnt=FAKE, row_idx=FAKE))),
                          kw.get("mode", 0), kw.get("dq", FAKE), kw.get("dk", FAKE), kw.get("dv", FAKE), 0)
-    # built for bf16, D = 128 only
-    assert lib.attn_bwd_chunk(*args(d=_desc(D=64))) == _lib.RAM_ERR_UNSUPPORTED and "128" in _err(lib)
+    # built for bf16, D = 64 and 128 only
+    assert lib.attn_bwd_chunk(*args(d=_desc(D=32))) == _lib.RAM_ERR_UNSUPPORTED
+    assert lib.attn_bwd_chunk(*args(d=_desc(D=96))) == _lib.RAM_ERR_UNSUPPORTED
     assert lib.attn_bwd_chunk(*args(d=_desc(dtype=ram.RAM_F32))) == _lib.RAM_ERR_UNSUPPORTED
     # the transposed lists are required, both or neither
     assert lib.attn_bwd_chunk(*args(bm=_bm())) == _lib.RAM_ERR_INVALID and "transposed" in _err(lib)
@@ -236,7 +237,9 @@ def test_backward_validation(lib):
     assert lib.attn_bwd_chunk(*args(src=_src(dense=FAKE2))) == _lib.RAM_ERR_INVALID and "bits" in _err(lib)
     # prep: sinks need dsinks
     assert lib.attn_bwd_prep(ctypes.byref(d), FAKE, FAKE, FAKE2, FAKE2, FAKE2, z, 0) == _lib.RAM_ERR_INVALID
-    assert lib.attn_bwd_prep(ctypes.byref(_desc(D=64)), FAKE, FAKE, FAKE2, 0, FAKE2, 0, 0) == _lib.RAM_ERR_UNSUPPORTED
+    assert lib.attn_bwd_prep(ctypes.byref(_desc(D=96)), FAKE, FAKE, FAKE2, 0, FAKE2, 0, 0) == _lib.RAM_ERR_UNSUPPORTED
+    assert lib.attn_bwd_prep(ctypes.byref(_desc(dtype=ram.RAM_F32)), FAKE, FAKE, FAKE2, 0, FAKE2, 0,
+                             0) == _lib.RAM_ERR_UNSUPPORTED
     # the ring: workspace holds float32 dq, dk, dv, delta and the masks with transposed lists
     dr = _desc(B=1, Sq=512, Skv=512, H=4, Hkv=2)
     need = lib.ring_attn_bwd_workspace_bytes(ctypes.byref(dr), 4, None)
@@ -247,7 +250,10 @@ def test_backward_validation(lib):
     assert need == expect
     dense = lib.ring_attn_bwd_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src(dense=FAKE2)))
     assert dense == need + tiles * 1024
-    assert lib.ring_attn_bwd_workspace_bytes(ctypes.byref(_desc(D=64)), 4, None) == 0
+    assert lib.ring_attn_bwd_workspace_bytes(ctypes.byref(_desc(D=96)), 4, None) == 0
+    d64 = _desc(B=1, Sq=512, Skv=512, H=4, Hkv=2, D=64)
+    assert lib.ring_attn_bwd_workspace_bytes(ctypes.byref(d64), 4, None) == expect - (
+        al(512 * 4 * 128 * 4) + 2 * al(4 * 512 * 2 * 128 * 4)) + al(512 * 4 * 64 * 4) + 2 * al(4 * 512 * 2 * 64 * 4)
     ring = lambda ws_bytes, **kw: lib.ring_attn_bwd_1gpu(
         ctypes.byref(kw.get("d", dr)), 4, kw.get("r", 3), FAKE, FAKE, FAKE, FAKE, FAKE2, FAKE,
         ctypes.byref(_src()), kw.get("sinks", 0), FAKE, FAKE, FAKE, kw.get("dsinks", 0), FAKE, ws_bytes, 0)
