@@ -141,23 +141,37 @@ __device__ __forceinline__ float capped_log2(float s, float k2, float cap_log2) 
   return cap_log2 * t;
 }
 
+// Maximum of N values by a tree of three-input maxima (v_max3_f32).
+template <int N>
+__device__ __forceinline__ float max_tree3(const float (&v)[N]) {
+  if constexpr (N == 1) {
+    return v[0];
+  } else if constexpr (N == 2) {
+    return fmaxf(v[0], v[1]);
+  } else {
+    constexpr int M = (N + 2) / 3;
+    float u[M];
+#pragma unroll
+    for (int j = 0; j < N / 3; ++j) u[j] = fmaxf(fmaxf(v[3 * j], v[3 * j + 1]), v[3 * j + 2]);
+    if constexpr (N % 3 == 1) u[M - 1] = v[N - 1];
+    if constexpr (N % 3 == 2) u[M - 1] = fmaxf(v[N - 2], v[N - 1]);
+    return max_tree3<M>(u);
+  }
+}
+
 // Online-softmax step on the NK*16 scores a lane holds. Updates m_ref / l_acc
 // / O and leaves the weights in S.
 template <int NDB, bool CAP, int NK>
 __device__ __forceinline__ void softmax_step(f32x16 (&S)[NK], f32x16 (&O)[NDB], float& m_ref,
                                              float& l_acc, const AttnParams& p) {
   constexpr int NG = NK * 4;
-  // row max: a tree over the scores (short dependency chains)
   float t[NG];
+  float all[NK * 16];
 #pragma unroll
-  for (int u = 0; u < NG; ++u)
-    t[u] = fmaxf(fmaxf(S[u >> 2][(u & 3) * 4 + 0], S[u >> 2][(u & 3) * 4 + 1]),
-                 fmaxf(S[u >> 2][(u & 3) * 4 + 2], S[u >> 2][(u & 3) * 4 + 3]));
+  for (int kb2 = 0; kb2 < NK; ++kb2)
 #pragma unroll
-  for (int w = NG / 2; w >= 1; w /= 2)
-#pragma unroll
-    for (int u = 0; u < w; ++u) t[u] = fmaxf(t[u], t[u + w]);
-  const float mx = pair_max(t[0]);
+    for (int i = 0; i < 16; ++i) all[kb2 * 16 + i] = S[kb2][i];
+  const float mx = pair_max(max_tree3(all));
   const float umax = CAP ? mx : mx * p.scale_log2;
   const bool need = umax > m_ref + kRescaleThreshold;
   if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -176,7 +190,8 @@ __device__ __forceinline__ void softmax_step(f32x16 (&S)[NK], f32x16 (&O)[NDB], 
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       S[kb2][i] = CAP ? fast_exp2(S[kb2][i] - msub) : fast_exp2(__builtin_fmaf(S[kb2][i], p.scale_log2, -msub));
-  // row sum: a tree as well
+  // row sum: a tree (short dependency chains), in fp32: the weights' bf16
+  // rounding would put up to 2^-9 into the logsumexp of a row with few keys
 #pragma unroll
   for (int u = 0; u < NG; ++u)
     t[u] = (S[u >> 2][(u & 3) * 4 + 0] + S[u >> 2][(u & 3) * 4 + 1]) +
