@@ -334,6 +334,28 @@ def cpu_baseline(w, n_rows: int):
                       f"numpy oracle (full score rows, BLAS dgemm), {dt:.2f} s"}
 
 
+def mfma_rates(dev, stream) -> dict:
+    """The dense bf16 MFMA rate this GPU sustains from registers (ram_mfma_probe), with all-zero and
+    with pseudo-random operands: the clock of the matrix cores follows the operands' switching activity,
+    so the published peak is reached only with the former."""
+    n_blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(n_blocks * 512, dtype=torch.float32, device=dev)
+    iters = 2000
+    flops = 32768.0 * 32 * iters * 8 * n_blocks       # 32 MFMAs per wave and iteration, 8 waves per block
+    res = {}
+    for name, kind in (("zeros", 0), ("random", 1)):
+        ram.mfma_probe(n_blocks, 50, kind, out, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ram.mfma_probe(n_blocks, iters, kind, out, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = round(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    res["unit"] = "TFLOP/s"
+    res["probe"] = f"ram_mfma_probe, {n_blocks} workgroups x 8 waves, 32x32x16 bf16 MFMAs from registers"
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -436,6 +458,10 @@ def main():
                 "launches_per_step": w.n_chunks, "mean_launch_us": round(1e3 * kern_ms / w.n_chunks, 2),
                 "flops_per_launch_mean": sum(eff_flops_chunk) / w.n_chunks}
     del acc, acc_lse, masks
+    measured = mfma_rates(dev, stream)
+    roofline["measured_peak_random"] = measured["random"]
+    roofline["frac_of_measured_random"] = round(achieved / measured["random"], 4)
+    log(f"MFMA probe: {measured['zeros']} TFLOP/s with zero operands, {measured['random']} with random ones")
     builder = None if dense is None else mask_builder_rate(w, desc, dense, bq, bk, dev, stream, reps)
     if args.copy_calibration:
         copy_calibration(dev)
@@ -457,6 +483,7 @@ def main():
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "mfma_measured": measured,
     }
     if builder is not None:
         line["mask_builder"] = builder

@@ -242,6 +242,16 @@ ram_status ram_kernel_tile(int32_t dtype, int32_t D, int32_t* block_q, int32_t* 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ram_last_error(void);
 
+/* Measurement aid, not part of the attention path: n_blocks workgroups of 8
+ * waves, each wave running iters x 32 v_mfma_f32_32x32x16_bf16 (32768 FLOP
+ * each) from operands held in registers, all zero
+ * (operands = 0) or pseudo-random in [-1, 1) (operands = 1): the dense bf16
+ * MFMA rate the chip sustains, which depends on the operands' values. out:
+ * device float32 [n_blocks * 512], written (a checksum per thread). Returns
+ * RAM_ERR_INVALID for bad arguments (nothing launched), RAM_ERR_HIP if the
+ * launch fails; ram_last_error() is not set by this call. */
+ram_status ram_mfma_probe(int32_t n_blocks, int32_t iters, int32_t operands, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

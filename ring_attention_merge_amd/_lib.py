@@ -27,7 +27,7 @@ RAM_PAD_SEGMENT_ID = -1
 
 EXPORTS = ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
            "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_last_error", "attn_bwd_prep",
-           "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes")
+           "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes", "ram_mfma_probe")
 
 
 class RamError(RuntimeError):
@@ -92,8 +92,9 @@ def load(path: str = LIB_PATH):
     lib.ring_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ram_last_error.argtypes = []
     lib.ram_last_error.restype = ctypes.c_char_p
+    lib.ram_mfma_probe.argtypes = [i32, i32, i32, f32p, vp]
     for name in ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu", "ram_kernel_tile",
-                 "attn_bwd_prep", "attn_bwd_chunk", "ring_attn_bwd_1gpu"):
+                 "attn_bwd_prep", "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ram_mfma_probe"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -266,6 +267,15 @@ def attn_fwd_chunk(desc: Desc, q, k, v, src: MaskSrc, mask: BlockMask, sinks, mo
     _check(load().attn_fwd_chunk(ctypes.byref(cd), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
                                  ctypes.byref(cb), _ptr(sinks), mode, _ptr(out), _ptr(lse),
                                  _stream(stream)))
+
+
+def mfma_probe(n_blocks: int, iters: int, operands: int, out, stream=None):
+    """ram_mfma_probe: n_blocks x 8 waves of register-fed bf16 MFMAs (operands 0: zeros, 1: random);
+    out float32 [n_blocks * 512] receives a checksum per thread."""
+    _need(out, "out", torch.float32, n_blocks * 512)
+    st = load().ram_mfma_probe(n_blocks, iters, operands, _ptr(out), _stream(stream))
+    if st != RAM_OK:
+        raise RamError(st, f"ram_mfma_probe(n_blocks={n_blocks}, iters={iters}, operands={operands})")
 
 
 def lse_merge(out_acc, lse_acc, out_blk, lse_blk, stream=None):

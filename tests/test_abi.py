@@ -35,9 +35,18 @@ def test_every_header_symbol_is_exported(lib):
     names = _header_functions()
     assert set(names) == {"build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
                           "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_last_error", "attn_bwd_prep",
-                          "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes"}, names
+                          "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes",
+                          "ram_mfma_probe"}, names
     for n in names:
         assert hasattr(lib, n), f"libram.so does not export {n}"
+
+
+def test_mfma_probe_validation(lib):
+    # rejected before any launch (no GPU needed)
+    assert lib.ram_mfma_probe(0, 10, 1, FAKE2, 0) == _lib.RAM_ERR_INVALID
+    assert lib.ram_mfma_probe(4, 0, 1, FAKE2, 0) == _lib.RAM_ERR_INVALID
+    assert lib.ram_mfma_probe(4, 10, 2, FAKE2, 0) == _lib.RAM_ERR_INVALID
+    assert lib.ram_mfma_probe(4, 10, 0, 0, 0) == _lib.RAM_ERR_INVALID
 
 
 def _desc(**kw):
