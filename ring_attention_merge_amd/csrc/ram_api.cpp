@@ -436,6 +436,27 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   if (e != hipSuccess) return hip_fail(e, "ring block mask launch");
 
   const int64_t esz = desc->dtype == RAM_BF16 ? 2 : 4;
+  {
+    // The whole ring as one launch where the kernel supports it: every visit
+    // runs exactly as a per-chunk launch would (same tiles, epilogue and merge).
+    ram_attn_desc dc = *desc;
+    dc.kv_stride_b = kv_full_stride;
+    ram_mask_src sc = *src;
+    sc.q_pos_base = q_base;
+    sc.kv_meta_stride_b = kvm_full;
+    ram::AttnParams p = attn_params(&dc, q, k_all, v_all, &sc, &bm, sinks, RAM_OUT_WRITE, acc, lse);
+    if (ram::attn_ring_fused(p, desc->dtype)) {
+      p.n_chunks = n_chunks;
+      p.ring_shard = q_shard;
+      p.kv_chunk_elems = (int64_t)desc->Skv * desc->Hkv * desc->D;
+      p.mask_chunk_tiles = (int64_t)desc->B * nQb * nKb;
+      p.mask_chunk_rows = (int64_t)desc->B * nQb;
+      p.out_final = out;   // bf16: the last visit writes the result
+      e = ram::launch_attn_ring(p, stream);
+      if (e != hipSuccess) return hip_fail(e, "ring launch");
+      return ok();
+    }
+  }
   bool final_fused = false;
   for (int t = 0; t < n_chunks; ++t) {
     const int c = q_shard >= 0 ? ((q_shard - t) % n_chunks + n_chunks) % n_chunks : t;

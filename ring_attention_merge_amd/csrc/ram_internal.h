@@ -42,6 +42,17 @@ struct AttnParams {
   int32_t softcap_on;
   int32_t causal;
   int32_t mode;       // 0 write, 1 merge
+  // One launch for a whole ring (launch_attn_ring): k, v, the mask arrays and
+  // kv_pos / kv_seg / kv_pos_base describe chunk 0, chunk c lies kv_chunk_elems
+  // elements (k, v), mask_chunk_tiles tiles and mask_chunk_rows rows (masks)
+  // and c*Skv keys (kv arrays, kv_pos_base) further. Visit t takes chunk
+  // (ring_shard - t) mod n_chunks, or t when ring_shard < 0; sinks and `mode`
+  // apply to visit 0, out_final to the last.
+  int32_t n_chunks;
+  int32_t ring_shard;
+  int64_t kv_chunk_elems;
+  int64_t mask_chunk_tiles;
+  int64_t mask_chunk_rows;
 };
 
 struct MaskParams {
@@ -78,6 +89,9 @@ struct BwdParams {
 };
 
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s);
+// Whether a ring of this kernel choice runs as one launch (launch_attn_ring).
+bool attn_ring_fused(const AttnParams& p, int dtype);
+hipError_t launch_attn_ring(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s);   // bf16, D = 128: dq, then dk / dv
 hipError_t launch_bwd_prep(int B, int Sq, int H, int D, const void* out, const void* dout, const float* lse,
                            const float* sinks, float* delta, float* dsinks, hipStream_t s);
