@@ -54,8 +54,8 @@ BWD_FLOP_FACTOR = 2.5
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 REF_TILE = 128                  # fixed reference tiling for effective FLOPs
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
-ATTN_KERNEL = "attn_fwd_bf16_dma<false, false>"
-ATTN_KERNEL_BITS = "attn_fwd_bf16_dma<false, true>"
+ATTN_KERNEL = "attn_fwd_bf16_dma_ring<false, false>"
+ATTN_KERNEL_BITS = "attn_fwd_bf16_dma_ring<false, true>"
 
 
 def log(*a):
@@ -142,9 +142,9 @@ def recorded_traffic_bwd(workload: str):
 
 
 def recorded_traffic(workload: str):
-    """HBM bytes per chunk launch from the committed counter summary, if it was taken
+    """HBM bytes per ring launch from the committed counter summary, if it was taken
     on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_bf16_dma_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_bf16_dma_ring_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -419,45 +419,27 @@ def main():
     tflops = eff_flops / (ms * 1e-3) / 1e12
     log(f"step {ms:.3f} ms, {tflops:.1f} effective TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak)")
 
-    # Roofline of the dominant kernel: each chunk launch timed alone on the same stream.
+    # Roofline of the dominant kernel: the ring's attention launch (one per step), timed with HIP
+    # events the library records on the step's stream right around it (ram_set_kernel_events).
     bq, bk = ram.kernel_tile(dcode, w.D)
-    dk = ram.Desc(**{**desc.__dict__, "block_q": bq, "block_kv": bk, "kv_stride_b": w.Skv * w.Hkv * w.D})
-    masks, srcs = [], []
-    for c in range(w.n_chunks):
-        srcs.append(ring_chunk_src(w, c, dev, dense))
-        bm = ram.alloc_block_mask(dk, device=dev, with_bits=dense is not None)
-        ram.build_block_mask(dk, srcs[c], bm)
-        masks.append(bm)
-    acc = torch.empty(w.B, w.Sq, w.H, w.D, dtype=torch.float32, device=dev)
-    acc_lse = torch.empty(w.B, w.H, w.Sq, dtype=torch.float32, device=dev)
-    kv_elems = w.chunk * w.Hkv * w.D
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(w.n_chunks)]
+    fused = os.environ.get("RAM_RING") != "per_chunk" and not os.environ.get("RAM_ATTN_KERNEL")
     reps = max(1, args.steps // 2)
-    per_chunk_ms = [0.0] * w.n_chunks
-    for rep in range(reps + 1):
-        for t_, c in enumerate(order(w)):
-            kc = k.view(-1)[c * kv_elems:]
-            vc = v.view(-1)[c * kv_elems:]
-            a, b = evs[t_]
-            a.record(stream)
-            ram.attn_fwd_chunk(dk, q, kc, vc, srcs[c], masks[c],
-                               sinks if t_ == 0 else None, 0 if t_ == 0 else 1, acc, acc_lse, stream=stream)
-            b.record(stream)
-        torch.cuda.synchronize()
-        if rep > 0:                      # first pass is a warm-up
-            for t_ in range(w.n_chunks):
-                per_chunk_ms[t_] += evs[t_][0].elapsed_time(evs[t_][1]) / reps
-    kern_ms = sum(per_chunk_ms)
-    flops_in_order = [eff_flops_chunk[c] for c in order(w)]
-    achieved = sum(flops_in_order) / (kern_ms * 1e-3) / 1e12
-    log("chunk kernel ms (visit order): " + ", ".join(f"{x:.3f}" for x in per_chunk_ms))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        ram.set_kernel_events(a, b, stream=stream)
+        step()
+    ram.set_kernel_events()
+    torch.cuda.synchronize()
+    kern_ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+    launches = 1 if fused else w.n_chunks
+    achieved = eff_flops / (kern_ms * 1e-3) / 1e12
+    log(f"attention kernel {kern_ms:.3f} ms per step ({launches} launch(es)), {achieved:.1f} TFLOP/s")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(args.workload),
-                "kernel": ATTN_KERNEL if dense is None else ATTN_KERNEL_BITS,
-                "launches_per_step": w.n_chunks, "mean_launch_us": round(1e3 * kern_ms / w.n_chunks, 2),
-                "flops_per_launch_mean": sum(eff_flops_chunk) / w.n_chunks}
-    del acc, acc_lse, masks
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": recorded_traffic(args.workload) if fused else None,
+                "kernel": (ATTN_KERNEL if dense is None else ATTN_KERNEL_BITS) if fused else "per-chunk launches",
+                "launches_per_step": launches, "mean_launch_us": round(1e3 * kern_ms / launches, 2),
+                "flops_per_launch_mean": eff_flops / launches}
     measured = mfma_rates(dev, stream)
     roofline["measured_peak_random"] = measured["random"]
     roofline["frac_of_measured_random"] = round(achieved / measured["random"], 4)

@@ -27,7 +27,8 @@ RAM_PAD_SEGMENT_ID = -1
 
 EXPORTS = ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
            "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_last_error", "attn_bwd_prep",
-           "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes", "ram_mfma_probe")
+           "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes", "ram_mfma_probe",
+           "ram_set_kernel_events")
 
 
 class RamError(RuntimeError):
@@ -93,8 +94,10 @@ def load(path: str = LIB_PATH):
     lib.ram_last_error.argtypes = []
     lib.ram_last_error.restype = ctypes.c_char_p
     lib.ram_mfma_probe.argtypes = [i32, i32, i32, f32p, vp]
+    lib.ram_set_kernel_events.argtypes = [vp, vp]
     for name in ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu", "ram_kernel_tile",
-                 "attn_bwd_prep", "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ram_mfma_probe"):
+                 "attn_bwd_prep", "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ram_mfma_probe",
+                 "ram_set_kernel_events"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -267,6 +270,21 @@ def attn_fwd_chunk(desc: Desc, q, k, v, src: MaskSrc, mask: BlockMask, sinks, mo
     _check(load().attn_fwd_chunk(ctypes.byref(cd), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
                                  ctypes.byref(cb), _ptr(sinks), mode, _ptr(out), _ptr(lse),
                                  _stream(stream)))
+
+
+def set_kernel_events(start=None, stop=None, stream=None):
+    """ram_set_kernel_events: torch.cuda.Event pair (enable_timing) that this thread's ring forward
+    calls record around their attention launches; no arguments to stop. Both events are recorded
+    once here on `stream` (torch measures only events it has seen recorded); the ring calls record
+    them again at their launches, and elapsed_time reads those last records."""
+    if (start is None) != (stop is None):
+        raise ValueError("set both events or neither")
+    if start is not None:
+        st = torch.cuda.current_stream() if stream is None else stream
+        start.record(st)
+        stop.record(st)
+    h = lambda e: None if e is None else e.cuda_event
+    _check(load().ram_set_kernel_events(h(start), h(stop)))
 
 
 def mfma_probe(n_blocks: int, iters: int, operands: int, out, stream=None):

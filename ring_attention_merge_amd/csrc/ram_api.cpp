@@ -17,6 +17,8 @@
 namespace {
 
 thread_local std::string g_err;
+// Events ring_attn_fwd_1gpu records around its attention launches (ram_set_kernel_events).
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 ram_status fail(ram_status s, const char* fmt, ...) {
   char buf[512];
@@ -303,6 +305,13 @@ extern "C" {
 
 const char* ram_last_error(void) { return g_err.c_str(); }
 
+ram_status ram_set_kernel_events(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr)) return fail(RAM_ERR_INVALID, "set both events or neither");
+  g_ev_start = start;
+  g_ev_stop = stop;
+  return ok();
+}
+
 ram_status ram_kernel_tile(int32_t dtype, int32_t D, int32_t* block_q, int32_t* block_kv) {
   if (!block_q || !block_kv) return fail(RAM_ERR_INVALID, "null output pointer");
   if (dtype != RAM_F32 && dtype != RAM_BF16) return fail(RAM_ERR_UNSUPPORTED, "dtype %d", dtype);
@@ -452,12 +461,15 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
       p.mask_chunk_tiles = (int64_t)desc->B * nQb * nKb;
       p.mask_chunk_rows = (int64_t)desc->B * nQb;
       p.out_final = out;   // bf16: the last visit writes the result
+      if (g_ev_start && (e = hipEventRecord(g_ev_start, stream)) != hipSuccess) return hip_fail(e, "event record");
       e = ram::launch_attn_ring(p, stream);
       if (e != hipSuccess) return hip_fail(e, "ring launch");
+      if (g_ev_stop && (e = hipEventRecord(g_ev_stop, stream)) != hipSuccess) return hip_fail(e, "event record");
       return ok();
     }
   }
   bool final_fused = false;
+  if (g_ev_start && (e = hipEventRecord(g_ev_start, stream)) != hipSuccess) return hip_fail(e, "event record");
   for (int t = 0; t < n_chunks; ++t) {
     const int c = q_shard >= 0 ? ((q_shard - t) % n_chunks + n_chunks) % n_chunks : t;
     ram_attn_desc dc = *desc;
@@ -483,6 +495,7 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
     e = ram::launch_attn(p, desc->dtype, stream);
     if (e != hipSuccess) return hip_fail(e, "ring chunk launch");
   }
+  if (g_ev_stop && (e = hipEventRecord(g_ev_stop, stream)) != hipSuccess) return hip_fail(e, "event record");
   if (desc->dtype == RAM_BF16 && !final_fused) {
     e = ram::launch_cast_bf16(acc, out, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
     if (e != hipSuccess) return hip_fail(e, "final cast launch");

@@ -36,9 +36,15 @@ def test_every_header_symbol_is_exported(lib):
     assert set(names) == {"build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
                           "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_last_error", "attn_bwd_prep",
                           "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes",
-                          "ram_mfma_probe"}, names
+                          "ram_mfma_probe", "ram_set_kernel_events"}, names
     for n in names:
         assert hasattr(lib, n), f"libram.so does not export {n}"
+
+
+def test_kernel_events_validation(lib):
+    assert lib.ram_set_kernel_events(FAKE, 0) == _lib.RAM_ERR_INVALID and "both" in _err(lib)
+    assert lib.ram_set_kernel_events(0, FAKE) == _lib.RAM_ERR_INVALID
+    assert lib.ram_set_kernel_events(0, 0) == _lib.RAM_OK
 
 
 def test_mfma_probe_validation(lib):
