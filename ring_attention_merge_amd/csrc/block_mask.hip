@@ -46,15 +46,16 @@ __device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t x) {
   return ((y * 0x00204081u) >> 21) & 0xFu;
 }
 
+// Bits of 32 dense-mask bytes held in two 16-byte values, byte j at bit j.
+__device__ __forceinline__ uint32_t bits_of_bytes32(const uint4& a, const uint4& b) {
+  return nonzero_bytes4(a.x) | nonzero_bytes4(a.y) << 4 | nonzero_bytes4(a.z) << 8 | nonzero_bytes4(a.w) << 12 |
+         nonzero_bytes4(b.x) << 16 | nonzero_bytes4(b.y) << 20 | nonzero_bytes4(b.z) << 24 | nonzero_bytes4(b.w) << 28;
+}
+
 // Bits of `n` (<= 32) consecutive dense-mask bytes, byte j at bit j.
 __device__ __forceinline__ uint32_t dense_word(const uint8_t* d, int n) {
-  if (n == 32 && (reinterpret_cast<uintptr_t>(d) & 15) == 0) {
-    const uint4 a = *reinterpret_cast<const uint4*>(d);
-    const uint4 b = *reinterpret_cast<const uint4*>(d + 16);
-    return nonzero_bytes4(a.x) | nonzero_bytes4(a.y) << 4 | nonzero_bytes4(a.z) << 8 |
-           nonzero_bytes4(a.w) << 12 | nonzero_bytes4(b.x) << 16 | nonzero_bytes4(b.y) << 20 |
-           nonzero_bytes4(b.z) << 24 | nonzero_bytes4(b.w) << 28;
-  }
+  if (n == 32 && (reinterpret_cast<uintptr_t>(d) & 15) == 0)
+    return bits_of_bytes32(*reinterpret_cast<const uint4*>(d), *reinterpret_cast<const uint4*>(d + 16));
   uint32_t m = 0;
   for (int j = 0; j < n; ++j) m |= (uint32_t)(d[j] != 0) << j;
   return m;
@@ -175,39 +176,81 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
       for (int t = tid; t < ng; t += kThreads) flag_s[t] = 0;
       __syncthreads();
       const int nw = ng * tw;
-      for (int t = tid; t < nw; t += kThreads) {
-        const int tl = t / tw, r = t - tl * tw;
-        const int i = r / W;
-        const int j0 = tl * p.bk + (r - i * W) * 32;       // first key of the word within the group
-        const int jn = min(min(32, gk - j0), (tl + 1) * p.bk - j0);
-        uint32_t word = 0;
-        if (i < nq && jn > 0) {
-          const uint32_t valid = jn == 32 ? ~0u : ((1u << jn) - 1u);
-          uint32_t w = valid;
-          if (p.causal) {
-            if (!kvpos) {
-              // sequential keys: the allowed ones are a prefix of the word
-              const int64_t lim = (int64_t)qpos_s[i] - ((int64_t)kv_base + g0 + j0);
-              w &= lim < 0 ? 0u : (lim >= 31 ? ~0u : ((2u << lim) - 1u));
-            } else {
-              uint32_t cm = 0;
-              for (int jj = 0; jj < jn; ++jj) cm |= (uint32_t)(kpos_s[j0 + jj] <= qpos_s[i]) << jj;
-              w &= cm;
+      const int gw = ng * W;   // words per tile row across the round
+      // Words are taken row by row (consecutive threads: consecutive 32-key words
+      // of one query row), so the dense mask is read in long contiguous runs, and
+      // kBatch words per thread at a time: their positions and segments first,
+      // then all their dense-mask loads together (latency, not bandwidth, bounds
+      // a thread that waits for each word's bytes before loading the next).
+      constexpr int kBatch = 4;
+      for (int u0 = tid; u0 < nw; u0 += kBatch * kThreads) {
+        uint32_t wv[kBatch], valv[kBatch];
+        int tv[kBatch], tlv[kBatch], iv[kBatch], j0v[kBatch], jnv[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int u = u0 + k * kThreads;
+          const int i = u / gw, jw = u - i * gw;
+          const int tl = jw / W, wi = jw - tl * W;
+          const int j0 = tl * p.bk + wi * 32;                // first key of the word within the group
+          const int jn = u < nw ? min(min(32, gk - j0), (tl + 1) * p.bk - j0) : 0;
+          tv[k] = tl * tw + i * W + wi;                      // the word's place in bits_s (tile-major)
+          tlv[k] = tl;
+          iv[k] = i;
+          j0v[k] = j0;
+          jnv[k] = jn;
+          uint32_t w = 0, valid = 0;
+          if (u < nw && i < nq && jn > 0) {
+            valid = jn == 32 ? ~0u : ((1u << jn) - 1u);
+            w = valid;
+            if (p.causal) {
+              if (!kvpos) {
+                // sequential keys: the allowed ones are a prefix of the word
+                const int64_t lim = (int64_t)qpos_s[i] - ((int64_t)kv_base + g0 + j0);
+                w &= lim < 0 ? 0u : (lim >= 31 ? ~0u : ((2u << lim) - 1u));
+              } else {
+                uint32_t cm = 0;
+                for (int jj = 0; jj < jn; ++jj) cm |= (uint32_t)(kpos_s[j0 + jj] <= qpos_s[i]) << jj;
+                w &= cm;
+              }
+            }
+            if (qseg && w) {
+              const int qs = qseg_s[i];
+              uint32_t sm = 0;
+              if (qs != -1)
+                for (int jj = 0; jj < jn; ++jj) sm |= (uint32_t)(kseg_s[j0 + jj] == qs) << jj;
+              w &= sm;
             }
           }
-          if (qseg && w) {
-            const int qs = qseg_s[i];
-            uint32_t sm = 0;
-            if (qs != -1)
-              for (int jj = 0; jj < jn; ++jj) sm |= (uint32_t)(kseg_s[j0 + jj] == qs) << jj;
-            w &= sm;
-          }
-          if (drow0 && w) w &= dense_word(drow0 + (int64_t)i * p.dense_ld + g0 + j0, jn);
-          word = w;
-          const int f = (w != 0 ? 1 : 0) | (w != valid ? 2 : 0);
-          if (f) atomicOr(&flag_s[tl], f);
+          wv[k] = w;
+          valv[k] = valid;
         }
-        bits_s[t] = word;
+        if (drow0) {
+          uint4 lo[kBatch], hi[kBatch];
+#pragma unroll
+          for (int k = 0; k < kBatch; ++k) {
+            const uint8_t* d = drow0 + (int64_t)iv[k] * p.dense_ld + g0 + j0v[k];
+            lo[k] = hi[k] = make_uint4(0, 0, 0, 0);
+            if (wv[k] && jnv[k] == 32 && (reinterpret_cast<uintptr_t>(d) & 15) == 0) {
+              lo[k] = *reinterpret_cast<const uint4*>(d);
+              hi[k] = *reinterpret_cast<const uint4*>(d + 16);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < kBatch; ++k) {
+            if (!wv[k]) continue;
+            const uint8_t* d = drow0 + (int64_t)iv[k] * p.dense_ld + g0 + j0v[k];
+            wv[k] &= (jnv[k] == 32 && (reinterpret_cast<uintptr_t>(d) & 15) == 0) ? bits_of_bytes32(lo[k], hi[k])
+                                                                                   : dense_word(d, jnv[k]);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          if (u0 + k * kThreads >= nw) continue;
+          const uint32_t w = wv[k];
+          const int f = valv[k] ? ((w != 0 ? 1 : 0) | (w != valv[k] ? 2 : 0)) : 0;
+          if (f) atomicOr(&flag_s[tlv[k]], f);
+          bits_s[tv[k]] = w;
+        }
       }
       __syncthreads();
       for (int t = tid; t < ng; t += kThreads) {
