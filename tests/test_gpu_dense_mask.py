@@ -166,7 +166,7 @@ RING_CASES = {
 
 
 @pytest.mark.parametrize("name", sorted(RING_CASES))
-def test_ring_dense(name):
+def test_ring_dense(name, monkeypatch):
     dt, D, B, H, Hkv, Sq, C, n, r, causal, kind, pad, cap, with_sinks = RING_CASES[name]
     rng = np.random.default_rng(zlib.crc32(name.encode()))
     w = wl.make(name, B=B, H=H, Hkv=Hkv, Sq=Sq, chunk=C, n_chunks=n, D=D, dtype=dt, causal=causal,
@@ -187,7 +187,12 @@ def test_ring_dense(name):
     ws = torch.empty(ram.ring_attn_workspace_bytes(d, n, src), dtype=torch.uint8, device=DEV)
     sinks = None if w.sinks is None else w.sinks.to(DEV)
     ram.ring_attn_fwd_1gpu(d, n, r, w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), src, sinks, out, lse, ws)
+    # the same ring as chunk-by-chunk launches: bit-identical
+    monkeypatch.setenv("RAM_RING", "per_chunk")
+    out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+    ram.ring_attn_fwd_1gpu(d, n, r, w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), src, sinks, out2, lse2, ws)
     torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), "one-launch ring differs from chunk launches"
     q, k, v, s64 = w.as_f64()
     qp, kp = w.positions()
     order = [(r - t) % n for t in range(n)] if r >= 0 else list(range(n))

@@ -249,6 +249,18 @@ def test_ring_small(name, variant):
     compare(out.numpy(), lse.numpy(), ro, rl, w.dtype, name)
 
 
+@pytest.mark.parametrize("name", ["ring_shard3of4", "ring_shard1of3_ragged", "docs_small", "gqa_cap_sinks_small"])
+def test_ring_one_launch_equals_chunk_launches(name, monkeypatch):
+    """The one-launch ring runs every chunk visit as a chunk launch does (same tiles, same merge):
+    its results are bit-identical to the chunk-by-chunk ring."""
+    w = SMALL_RING[name]()
+    say(f"ring one launch vs chunk launches {name}")
+    o1, l1 = run_ring(w)
+    monkeypatch.setenv("RAM_RING", "per_chunk")
+    o2, l2 = run_ring(w)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 # ------------------------------------------------------------------------------ full sizes
 def test_c1_full():
     w = wl.c1_causal_f32()
