@@ -500,10 +500,23 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
     const int r = 8 * w + Gm::kSlabRows * i + lane / Gm::kChunks;
     off[i] = (uint32_t)r * row_bytes + ((lane % Gm::kChunks) ^ swz<D>(r)) * 16;
   }
-  auto step_rows = [&](int t, int& qb, int& r0, int& h) {
-    qb = rows[t / (2 * G)];
-    r0 = qb * kBlockQ + ((t / G) & 1) * 64;
-    h = g * G + t % G;
+  // Step t covers q tile rows[t / 2G], 64-row half (t / G) & 1 and head g*G + t % G. Both
+  // the DMA stage and the work step advance one step at a time, so each keeps a cursor
+  // (tile index, half, head in group) instead of dividing by G every step.
+  struct Cursor {
+    int qi, half, hi;
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.hi == G) {
+      c.hi = 0;
+      c.half ^= 1;
+      c.qi += c.half == 0;
+    }
+  };
+  auto step_rows = [&](const Cursor& c, int& qb, int& r0, int& h) {
+    qb = rows[c.qi];
+    r0 = qb * kBlockQ + c.half * 64;
+    h = g * G + c.hi;
   };
   // The row array this wave moves: waves 0-3 lse, D, positions, segments (empty when
   // absent); waves 4-7 an empty load into an unused array, so every wave issues the same count.
@@ -511,9 +524,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
       w == 0 ? p.lse : (w == 1 ? bp.delta : (w == 2 ? reinterpret_cast<const float*>(p.q_pos)
                                                    : (w == 3 ? reinterpret_cast<const float*>(p.q_seg) : nullptr)));
   const bool row_per_head = w < 2;
+  Cursor stc{0, 0, 0};   // the next step to stage
   auto stage = [&](int t, int buf) {
     int qb = 0, r0 = p.Sq, h = g * G;
-    if (t < n_steps) step_rows(t, qb, r0, h);
+    if (t < n_steps) step_rows(stc, qb, r0, h);
+    advance(stc);
     const int nrows = max(0, min(64, p.Sq - r0));
     const uint32_t bytes = nrows > 0 ? (uint32_t)(nrows - 1) * row_bytes + D * 2 : 0u;
     const int64_t rq = (int64_t)min(r0, p.Sq) * p.H + h;
@@ -539,6 +554,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
   __syncthreads();
 
   const int q0 = 32 * qh;                    // this wave's first row in a step
+  Cursor wc{0, 0, 0};                        // the step this wave works on next
   for (int t = 0; t <= n_steps; ++t) {
     // the buffer of step t+2 was last read by the dS waves in step t-1 (for step t-2)
     stage(t + kAhead, (t + kAhead) & (kStages - 1));
@@ -569,7 +585,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
     }
     if (pw) {
       int qb, r0, h;
-      step_rows(u, qb, r0, h);
+      step_rows(wc, qb, r0, h);
       const int cl = tile_class_of(qb);
       const int need_mask = (BITS && cl == 1) ? 2 : ((cl != 2 || (kb + 1) * kBlockKV > p.Skv) ? 1 : 0);
       if constexpr (CAP) {
@@ -655,6 +671,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
       for (int f = 0; f < 2 * NDB; ++f)
         acc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(tr[f]), DSb[f / NDB], acc[f % NDB], 0, 0, 0);
     }
+    advance(wc);
     // Step t+1 has landed once at most the loads of step t+2 are outstanding
     // (the LDS stores and reads above have all been waited for).
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kAhead - 1)));
