@@ -524,32 +524,51 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
       w == 0 ? p.lse : (w == 1 ? bp.delta : (w == 2 ? reinterpret_cast<const float*>(p.q_pos)
                                                    : (w == 3 ? reinterpret_cast<const float*>(p.q_seg) : nullptr)));
   const bool row_per_head = w < 2;
-  Cursor stc{0, 0, 0};   // the next step to stage
-  auto stage = [&](int t, int buf) {
-    int qb = 0, r0 = p.Sq, h = g * G;
-    if (t < n_steps) step_rows(stc, qb, r0, h);
-    advance(stc);
+  // Staging: bases at head g*G of this workgroup's batch; the values that change only with
+  // the staged q tile or half (first row, byte counts, row offset) are recomputed only then,
+  // and a step adds its head's stride (steps past the last stage empty loads).
+  const __bf16* q_wg = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b + (int64_t)g * G * D;
+  const __bf16* o_wg = reinterpret_cast<const __bf16*>(bp.dout) + ((int64_t)b * p.Sq * p.H + (int64_t)g * G) * D;
+  const float* r_wg =
+      row_src ? row_src + (row_per_head ? ((int64_t)b * p.H + g * G) * p.Sq : (int64_t)b * p.qm_stride_b) : p.lse;
+  const int r_step = row_per_head ? p.Sq : 0;   // row-array elements per head
+  Cursor stc{0, 0, 0};                          // the next step to stage
+  int64_t st_off = 0;                           // elements to its first row at head g*G
+  int st_r0 = 0;
+  uint32_t st_bytes = 0, st_rbytes = 0;
+  auto stage_rows = [&]() {
+    const int r0 = stc.qi < ccnt ? rows[stc.qi] * kBlockQ + stc.half * 64 : p.Sq;
     const int nrows = max(0, min(64, p.Sq - r0));
-    const uint32_t bytes = nrows > 0 ? (uint32_t)(nrows - 1) * row_bytes + D * 2 : 0u;
-    const int64_t rq = (int64_t)min(r0, p.Sq) * p.H + h;
+    st_r0 = min(r0, p.Sq);
+    st_off = (int64_t)st_r0 * p.H * D;
+    st_bytes = nrows > 0 ? (uint32_t)(nrows - 1) * row_bytes + D * 2 : 0u;
+    st_rbytes = row_src ? (uint32_t)nrows * 4u : 0u;
+  };
+  stage_rows();
+  auto stage = [&](int buf) {
+    const int64_t eoff = st_off + (int64_t)stc.hi * D;
     __bf16* Qs = smem + buf * 2 * kTileElems;
-    const auto qr = tile_rsrc(reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b + rq * D, bytes);
-    const auto orr = tile_rsrc(reinterpret_cast<const __bf16*>(bp.dout) + ((int64_t)b * p.Sq * p.H + rq) * D, bytes);
+    const auto qr = tile_rsrc(q_wg + eoff, st_bytes);
+    const auto orr = tile_rsrc(o_wg + eoff, st_bytes);
 #pragma unroll
     for (int i = 0; i < kSlabs; ++i) {
       const int r = 8 * w + Gm::kSlabRows * i;
       dma16(qr, Qs + r * D, off[i]);
       dma16(orr, Qs + kTileElems + r * D, off[i]);
     }
-    const int64_t rbase = row_per_head ? ((int64_t)b * p.H + h) * p.Sq : (int64_t)b * p.qm_stride_b;
-    const uint32_t rbytes = row_src ? (uint32_t)nrows * 4u : 0u;
-    const float* rs = row_src ? row_src + rbase + min(r0, p.Sq) : p.lse;
-    dma4(tile_rsrc(rs, rbytes), row_at(buf, w, 0), (uint32_t)lane * 4u);
+    const float* rs = row_src ? r_wg + stc.hi * r_step + st_r0 : p.lse;
+    dma4(tile_rsrc(rs, st_rbytes), row_at(buf, w, 0), (uint32_t)lane * 4u);
+    if (++stc.hi == G) {
+      stc.hi = 0;
+      stc.half ^= 1;
+      stc.qi += stc.half == 0;
+      stage_rows();
+    }
   };
 
   constexpr int kAhead = 2;   // stages in flight beyond the next one
-  stage(0, 0);
-  stage(1, 1);
+  stage(0);
+  stage(1);
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kAhead - 1)));
   __syncthreads();
 
@@ -557,7 +576,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
   Cursor wc{0, 0, 0};                        // the step this wave works on next
   for (int t = 0; t <= n_steps; ++t) {
     // the buffer of step t+2 was last read by the dS waves in step t-1 (for step t-2)
-    stage(t + kAhead, (t + kAhead) & (kStages - 1));
+    stage((t + kAhead) & (kStages - 1));
     // P waves work on step t, dS waves on step t-1
     const int u = pw ? t : t - 1;
     if (u < 0 || u >= n_steps) {
