@@ -644,8 +644,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
       f32x16 Gw;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float l = la[i >> 2][i & 3];
-        const float l2 = l == neg_inf() ? __builtin_inff() : l * kLog2e;
+        // l * log2(e); a row with lse = -inf has no allowed key anywhere, so all its scores
+        // are masked (-inf) and clamping its l2 to the lowest finite float keeps its
+        // weights exactly 0 without a compare per score
+        const float l2 = fmaxf(la[i >> 2][i & 3] * kLog2e, -__FLT_MAX__);
         if constexpr (CAP) {
           const float tt = fmaxf(X[i], -p.cap_log2) * (1.0f / p.cap_log2);
           X[i] = fast_exp2(X[i] - l2);
