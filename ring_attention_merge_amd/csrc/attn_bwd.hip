@@ -513,11 +513,6 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
       c.qi += c.half == 0;
     }
   };
-  auto step_rows = [&](const Cursor& c, int& qb, int& r0, int& h) {
-    qb = rows[c.qi];
-    r0 = qb * kBlockQ + c.half * 64;
-    h = g * G + c.hi;
-  };
   // The row array this wave moves: waves 0-3 lse, D, positions, segments (empty when
   // absent); waves 4-7 an empty load into an unused array, so every wave issues the same count.
   const float* row_src =
@@ -574,6 +569,17 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
 
   const int q0 = 32 * qh;                    // this wave's first row in a step
   Cursor wc{0, 0, 0};                        // the step this wave works on next
+  // The P waves' q tile of that step and its mask kind (0 none, 1 positions / segments,
+  // 2 stored bits), looked up when the cursor enters a q tile (every 2G steps).
+  auto tile_mask_kind = [&](int qb) {
+    const int cl = tile_class_of(qb);
+    return (BITS && cl == 1) ? 2 : ((cl != 2 || (kb + 1) * kBlockKV > p.Skv) ? 1 : 0);
+  };
+  int w_qb = 0, w_mask = 0;
+  if (pw && ccnt > 0) {
+    w_qb = rows[0];
+    w_mask = tile_mask_kind(w_qb);
+  }
   for (int t = 0; t <= n_steps; ++t) {
     // the buffer of step t+2 was last read by the dS waves in step t-1 (for step t-2)
     stage((t + kAhead) & (kStages - 1));
@@ -603,10 +609,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
       for (int ds = 0; ds < NDS; ++ds) X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds], kv[ds], X, 0, 0, 0);
     }
     if (pw) {
-      int qb, r0, h;
-      step_rows(wc, qb, r0, h);
-      const int cl = tile_class_of(qb);
-      const int need_mask = (BITS && cl == 1) ? 2 : ((cl != 2 || (kb + 1) * kBlockKV > p.Skv) ? 1 : 0);
+      const int qb = w_qb;
+      const int r0 = qb * kBlockQ + wc.half * 64;
+      const int need_mask = w_mask;
       if constexpr (CAP) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) X[i] = capped_log2(X[i], p.cap_k2, p.cap_log2);
@@ -693,6 +698,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
         acc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(tr[f]), DSb[f / NDB], acc[f % NDB], 0, 0, 0);
     }
     advance(wc);
+    if (pw && wc.hi == 0 && wc.half == 0 && wc.qi < ccnt) {
+      w_qb = rows[wc.qi];
+      w_mask = tile_mask_kind(w_qb);
+    }
     // Step t+1 has landed once at most the loads of step t+2 are outstanding
     // (the LDS stores and reads above have all been waited for).
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kAhead - 1)));
