@@ -195,8 +195,9 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
  *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,  dv_j = sum_i p_ij dout_i
  * (dk, dv summed over the query heads sharing a KV head), and for a sink
  *   dsink_h = - sum over batch rows and queries of exp(sink_h - lse_i) D_i,
- * counted once (the sink enters the forward once). Built for bf16 with
- * D = 64 or 128; other dtypes and head dims return RAM_ERR_UNSUPPORTED.
+ * counted once (the sink enters the forward once). Built for bf16 and
+ * float32 with D = 64 or 128; other dtypes and head dims return
+ * RAM_ERR_UNSUPPORTED.
  * out, dout: [B, Sq, H, D] dense in desc->dtype; lse: float32 [B, H, Sq] (as
  * the forward wrote them). */
 

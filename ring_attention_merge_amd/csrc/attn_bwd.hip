@@ -855,13 +855,17 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s) {
   return p.a.D == 64 ? launch_bwd_d<64>(p, s) : launch_bwd_d<128>(p, s);
 }
 
-hipError_t launch_bwd_prep(int B, int Sq, int H, int Dd, const void* out, const void* dout, const float* lse,
-                           const float* sinks, float* delta, float* dsinks, hipStream_t s) {
+hipError_t launch_bwd_prep(int dtype, int B, int Sq, int H, int Dd, const void* out, const void* dout,
+                           const float* lse, const float* sinks, float* delta, float* dsinks, hipStream_t s) {
   const int64_t n_rows = (int64_t)B * Sq * H;
   if (n_rows > 0) {
     const int64_t grid = (n_rows * 16 + 255) / 256;
-    hipLaunchKernelGGL(bwd_delta_kernel<__bf16>, dim3((unsigned)grid), dim3(256), 0, s, n_rows, H, Sq, Dd,
-                       reinterpret_cast<const __bf16*>(out), reinterpret_cast<const __bf16*>(dout), lse, delta);
+    if (dtype == 1)
+      hipLaunchKernelGGL(bwd_delta_kernel<__bf16>, dim3((unsigned)grid), dim3(256), 0, s, n_rows, H, Sq, Dd,
+                         reinterpret_cast<const __bf16*>(out), reinterpret_cast<const __bf16*>(dout), lse, delta);
+    else
+      hipLaunchKernelGGL(bwd_delta_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s, n_rows, H, Sq, Dd,
+                         reinterpret_cast<const float*>(out), reinterpret_cast<const float*>(dout), lse, delta);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

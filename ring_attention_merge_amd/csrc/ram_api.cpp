@@ -153,7 +153,8 @@ ram_status check_col_lists(const ram_block_mask* bm, const ram_attn_desc* d, boo
 
 // What the backward kernels are built for.
 ram_status check_bwd_support(const ram_attn_desc* d) {
-  if (d->dtype != RAM_BF16) return fail(RAM_ERR_UNSUPPORTED, "backward dtype %d (built: bf16)", d->dtype);
+  if (d->dtype != RAM_BF16 && d->dtype != RAM_F32)
+    return fail(RAM_ERR_UNSUPPORTED, "backward dtype %d (built: bf16, float32)", d->dtype);
   if (d->D != 128 && d->D != 64) return fail(RAM_ERR_UNSUPPORTED, "backward head dim D=%d (built: 64, 128)", d->D);
   return RAM_OK;
 }
@@ -521,7 +522,7 @@ ram_status attn_bwd_prep(const ram_attn_desc* desc, const void* out, const void*
   if (lse && !aligned(lse, 4)) return fail(RAM_ERR_INVALID, "lse misaligned");
   if (sinks && (!aligned(sinks, 4) || !dsinks || !aligned(dsinks, 4)))
     return fail(RAM_ERR_INVALID, "sinks given: dsinks must be set, both 4-byte aligned");
-  hipError_t e = ram::launch_bwd_prep(desc->B, desc->Sq, desc->H, desc->D, out, dout, lse, sinks, delta, dsinks,
+  hipError_t e = ram::launch_bwd_prep(desc->dtype, desc->B, desc->Sq, desc->H, desc->D, out, dout, lse, sinks, delta, dsinks,
                                       stream);
   if (e != hipSuccess) return hip_fail(e, "attn_bwd_prep launch");
   return ok();
@@ -564,7 +565,7 @@ ram_status attn_bwd_chunk(const ram_attn_desc* desc, const void* q, const void* 
   bp.col_cnt = mask->col_cnt;
   bp.row_idx = mask->row_idx;
   bp.dq_mode = dq_mode;
-  hipError_t e = ram::launch_attn_bwd(bp, stream);
+  hipError_t e = desc->dtype == RAM_F32 ? ram::launch_attn_bwd_f32(bp, stream) : ram::launch_attn_bwd(bp, stream);
   if (e != hipSuccess) return hip_fail(e, "attn_bwd_chunk launch");
   return ok();
 }
@@ -640,7 +641,7 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   const int64_t kvm_full = src->kv_meta_stride_b ? src->kv_meta_stride_b : kv_total;
   const int32_t q_base = (int32_t)(src->q_pos_base + q_extra);
 
-  hipError_t e = ram::launch_bwd_prep(desc->B, desc->Sq, desc->H, desc->D, out, dout, lse, sinks, delta, dsinks,
+  hipError_t e = ram::launch_bwd_prep(desc->dtype, desc->B, desc->Sq, desc->H, desc->D, out, dout, lse, sinks, delta, dsinks,
                                       stream);
   if (e != hipSuccess) return hip_fail(e, "ring backward prep launch");
   ram_mask_src sm = *src;
@@ -655,7 +656,7 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   e = ram::launch_col_lists(mp, n_chunks, bm.col_cnt, bm.row_idx, stream);
   if (e != hipSuccess) return hip_fail(e, "ring backward transposed lists launch");
 
-  const int64_t esz = 2;
+  const int64_t esz = desc->dtype == RAM_BF16 ? 2 : 4;
   for (int t = 0; t < n_chunks; ++t) {
     const int c = q_shard >= 0 ? ((q_shard - t) % n_chunks + n_chunks) % n_chunks : t;
     ram_attn_desc dc = *desc;
@@ -684,8 +685,22 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
     bp.col_cnt = bc.col_cnt;
     bp.row_idx = bc.row_idx;
     bp.dq_mode = t == 0 ? RAM_OUT_WRITE : RAM_OUT_MERGE;
-    e = ram::launch_attn_bwd(bp, stream);
+    e = desc->dtype == RAM_F32 ? ram::launch_attn_bwd_f32(bp, stream) : ram::launch_attn_bwd(bp, stream);
     if (e != hipSuccess) return hip_fail(e, "ring backward chunk launch");
+  }
+  if (desc->dtype == RAM_F32) {
+    // float32 results: the accumulators are the answer, copied into the caller's layout
+    const size_t dq_bytes = (size_t)desc->B * desc->Sq * desc->H * desc->D * 4;
+    e = hipMemcpyAsync(dq, dq_acc, dq_bytes, hipMemcpyDeviceToDevice, stream);
+    for (int b = 0; b < desc->B && e == hipSuccess; ++b) {
+      e = hipMemcpyAsync(static_cast<char*>(dk_all) + b * kv_full_stride * esz, dk_acc + b * kv_acc_stride,
+                         kv_acc_stride * 4, hipMemcpyDeviceToDevice, stream);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(static_cast<char*>(dv_all) + b * kv_full_stride * esz, dv_acc + b * kv_acc_stride,
+                           kv_acc_stride * 4, hipMemcpyDeviceToDevice, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "dq / dk / dv copy");
+    return ok();
   }
   e = ram::launch_cast_bf16(dq_acc, dq, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
   if (e != hipSuccess) return hip_fail(e, "dq cast launch");

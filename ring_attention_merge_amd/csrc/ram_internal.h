@@ -92,9 +92,11 @@ hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s);
 // Whether a ring of this kernel choice runs as one launch (launch_attn_ring).
 bool attn_ring_fused(const AttnParams& p, int dtype);
 hipError_t launch_attn_ring(const AttnParams& p, hipStream_t s);
-hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s);   // bf16, D = 128: dq, then dk / dv
-hipError_t launch_bwd_prep(int B, int Sq, int H, int D, const void* out, const void* dout, const float* lse,
-                           const float* sinks, float* delta, float* dsinks, hipStream_t s);
+hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s);       // bf16, D = 64 / 128: dq, then dk / dv
+hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s);   // float32, D = 64 / 128
+// delta (and dsinks) from out and dout in `dtype` (RAM_BF16 / RAM_F32 codes)
+hipError_t launch_bwd_prep(int dtype, int B, int Sq, int H, int D, const void* out, const void* dout,
+                           const float* lse, const float* sinks, float* delta, float* dsinks, hipStream_t s);
 hipError_t launch_col_lists(const MaskParams& p, int n_chunks, int32_t* col_cnt, int32_t* row_idx,
                             hipStream_t s);
 // Whether the kernel launch_attn would pick for p honours p.out_final.

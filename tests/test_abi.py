@@ -238,10 +238,10 @@ def test_backward_validation(lib):
                          kw.get("dout", FAKE), kw.get("lse", FAKE2), kw.get("delta", FAKE2),
                          ctypes.byref(kw.get("src", _src())), ctypes.byref(kw.get("bm", _bm(col_cnt=FAKE, row_idx=FAKE))),
                          kw.get("mode", 0), kw.get("dq", FAKE), kw.get("dk", FAKE), kw.get("dv", FAKE), 0)
-    # built for bf16, D = 64 and 128 only
+    # built for bf16 and float32, D = 64 and 128 only
     assert lib.attn_bwd_chunk(*args(d=_desc(D=32))) == _lib.RAM_ERR_UNSUPPORTED
     assert lib.attn_bwd_chunk(*args(d=_desc(D=96))) == _lib.RAM_ERR_UNSUPPORTED
-    assert lib.attn_bwd_chunk(*args(d=_desc(dtype=ram.RAM_F32))) == _lib.RAM_ERR_UNSUPPORTED
+    assert lib.attn_bwd_chunk(*args(d=_desc(dtype=5))) == _lib.RAM_ERR_UNSUPPORTED
     # the transposed lists are required, both or neither
     assert lib.attn_bwd_chunk(*args(bm=_bm())) == _lib.RAM_ERR_INVALID and "transposed" in _err(lib)
     assert lib.attn_bwd_chunk(*args(bm=_bm(col_cnt=FAKE))) == _lib.RAM_ERR_INVALID and "both" in _err(lib)
@@ -253,7 +253,7 @@ def test_backward_validation(lib):
     # prep: sinks need dsinks
     assert lib.attn_bwd_prep(ctypes.byref(d), FAKE, FAKE, FAKE2, FAKE2, FAKE2, z, 0) == _lib.RAM_ERR_INVALID
     assert lib.attn_bwd_prep(ctypes.byref(_desc(D=96)), FAKE, FAKE, FAKE2, 0, FAKE2, 0, 0) == _lib.RAM_ERR_UNSUPPORTED
-    assert lib.attn_bwd_prep(ctypes.byref(_desc(dtype=ram.RAM_F32)), FAKE, FAKE, FAKE2, 0, FAKE2, 0,
+    assert lib.attn_bwd_prep(ctypes.byref(_desc(dtype=5)), FAKE, FAKE, FAKE2, 0, FAKE2, 0,
                              0) == _lib.RAM_ERR_UNSUPPORTED
     # the ring: workspace holds float32 dq, dk, dv, delta and the masks with transposed lists
     dr = _desc(B=1, Sq=512, Skv=512, H=4, Hkv=2)

@@ -24,6 +24,7 @@ from gpu_util import say
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 GRAD_TOL = 2e-2
+GRAD_TOL_F32 = 1e-5   # float32 inputs: float32 rounding over a few thousand terms is ~1e-6
 SINK_TOL = 1e-2   # dsinks error over sum_i exp(sink - lse_i) |D_i| (see _sinks_check)
 
 
@@ -43,7 +44,7 @@ def _rel(name, got, ref, tol, what):
     assert rel <= tol, f"{what} {name}: normalised error {rel:.3e} > {tol}"
 
 
-def _sinks_check(got, ref, out, lse, dout, sinks, what):
+def _sinks_check(got, ref, out, lse, dout, sinks, what, tol=SINK_TOL):
     """dsinks_h = -sum_i w_i D_i (w_i = exp(sink_h - lse_i), D_i = dout_i . out_i) is a signed
     sum that can cancel to far below its terms, so its error is measured against the sum of the
     terms' magnitudes, sum_i w_i |D_i|, from the oracle's float64 out and lse. Per term the
@@ -57,8 +58,8 @@ def _sinks_check(got, ref, out, lse, dout, sinks, what):
     err = np.abs(got - ref)
     rel = float(np.max(err / np.maximum(mag, 1e-30)))
     say(f"{what} dsinks: max err {float(err.max()):.3e}, max |ref| {float(np.abs(ref).max()):.3e}, "
-        f"err / sum w|D| {rel:.3e} (tol {SINK_TOL:.0e})")
-    assert rel <= SINK_TOL, f"{what} dsinks: error {rel:.3e} of sum w|D| > {SINK_TOL}"
+        f"err / sum w|D| {rel:.3e} (tol {tol:.0e})")
+    assert rel <= tol, f"{what} dsinks: error {rel:.3e} of sum w|D| > {tol}"
 
 
 # ------------------------------------------------------------------------------ transposed lists
@@ -115,14 +116,19 @@ CASES = {
     "d64_segs_cap": (1, 260, 300, 2, 2, False, 0, "segs", 10.0, False, 64),
     "d64_docs": (1, 384, 384, 2, 1, True, 0, "docs", None, False, 64),
     "d64_dense_cap_sinks": (1, 257, 270, 4, 4, True, 20, "dense", 30.0, True, 64),
+    # float32 inputs (the exact-reference dtype)
+    "f32_d64_causal": (1, 256, 256, 2, 2, True, 0, None, None, False, 64, "f32"),
+    "f32_d128_gqa_segs_cap_sinks": (2, 200, 230, 4, 2, False, 0, "segs", 8.0, True, 128, "f32"),
+    "f32_d64_dense_ragged": (1, 130, 200, 2, 1, True, 30, "dense", None, False, 64, "f32"),
 }
 
 
 def _inputs(name):
     B, Sq, Skv, H, Hkv, causal, qb, extra, cap, with_sinks = CASES[name][:10]
     D = CASES[name][10] if len(CASES[name]) > 10 else 128
+    f32 = len(CASES[name]) > 11 and CASES[name][11] == "f32"
     rng = np.random.default_rng(zlib.crc32(name.encode()))
-    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.float32 if f32 else torch.bfloat16)
     q = bf(rng.standard_normal((B, Sq, H, D)))
     k = bf(rng.standard_normal((B, Skv, Hkv, D)))
     v = bf(rng.standard_normal((B, Skv, Hkv, D)))
@@ -148,8 +154,8 @@ def _inputs(name):
     src = ram.MaskSrc(q_pos=_i32(qp) if explicit else None, kv_pos=_i32(kp) if explicit else None,
                       q_pos_base=0 if explicit else qb, q_seg=_i32(qs), kv_seg=_i32(ks),
                       dense=None if dense is None else torch.from_numpy(dense).to(DEV))
-    d = ram.Desc(B=B, Sq=Sq, Skv=Skv, H=H, Hkv=Hkv, D=D, scale=1.0 / math.sqrt(D), softcap=cap or 0.0,
-                 causal=causal)
+    d = ram.Desc(B=B, Sq=Sq, Skv=Skv, H=H, Hkv=Hkv, D=D, dtype=ram.RAM_F32 if f32 else ram.RAM_BF16,
+                 scale=1.0 / math.sqrt(D), softcap=cap or 0.0, causal=causal)
     ref_kw = dict(scale=d.scale, q_pos=qp, kv_pos=kp, q_seg=qs, kv_seg=ks, causal=causal, softcap=cap, dense=dense,
                   sinks=None if sinks is None else sinks.double().numpy())
     return d, q, k, v, dout, sinks, src, ref_kw
@@ -163,7 +169,7 @@ def test_chunk_backward(name):
     qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV)
     sd = None if sinks is None else sinks.to(DEV)
     # forward through the library (one chunk, bf16 result)
-    out = torch.full((B, Sq, H, D), float("nan"), device=DEV).to(torch.bfloat16)
+    out = torch.full((B, Sq, H, D), float("nan"), device=DEV).to(q.dtype)
     lse = torch.full((B, H, Sq), float("nan"), device=DEV)
     ws = torch.empty(max(1, ram.ring_attn_workspace_bytes(d, 1, src)), dtype=torch.uint8, device=DEV)
     ram.ring_attn_fwd_1gpu(d, 1, -1, qd, kd, vd, src, sd, out, lse, ws)
@@ -180,12 +186,13 @@ def test_chunk_backward(name):
     torch.cuda.synchronize()
     q64, k64, v64, do64 = (x.double().numpy() for x in (q, k, v, dout))
     rq, rk, rv, rs = oracle.attention_bwd(q64, k64, v64, do64, **ref_kw)
-    _rel("dq", dq.cpu().numpy(), rq, GRAD_TOL, name)
-    _rel("dk", dk.cpu().numpy(), rk, GRAD_TOL, name)
-    _rel("dv", dv.cpu().numpy(), rv, GRAD_TOL, name)
+    tol = GRAD_TOL_F32 if d.dtype == ram.RAM_F32 else GRAD_TOL
+    _rel("dq", dq.cpu().numpy(), rq, tol, name)
+    _rel("dk", dk.cpu().numpy(), rk, tol, name)
+    _rel("dv", dv.cpu().numpy(), rv, tol, name)
     if sinks is not None:
         ro, rl = oracle.attention(q64, k64, v64, **ref_kw)
-        _sinks_check(dsinks.cpu().numpy(), rs, ro, rl, do64, ref_kw["sinks"], name)
+        _sinks_check(dsinks.cpu().numpy(), rs, ro, rl, do64, ref_kw["sinks"], name, tol)
 
 
 def test_chunk_backward_add_mode():
@@ -225,11 +232,16 @@ RING = {
                                                    q_shard=2, softcap=20.0, with_sinks=True, seed=38),
     "d64_docs": lambda: wl.make("r64d", B=1, H=2, Hkv=1, Sq=768, chunk=256, n_chunks=3, D=64, docs=(32, 200, 0.05),
                                 seed=39),
+    "f32_c1_shape": lambda: wl.make("rf32", B=1, H=2, Hkv=2, Sq=256, chunk=128, n_chunks=2, D=64, dtype="f32",
+                                    seed=40),
+    "f32_shard1of3_gqa_cap_sinks": lambda: wl.make("rf32s", B=2, H=4, Hkv=2, Sq=150, chunk=150, n_chunks=3, D=128,
+                                                   dtype="f32", q_shard=1, softcap=10.0, with_sinks=True, seed=41),
 }
 
 
 def _run_ring_bwd(w, dout, src=None):
-    d = ram.Desc(B=w.B, Sq=w.Sq, Skv=w.chunk, H=w.H, Hkv=w.Hkv, D=w.D, scale=w.scale, softcap=w.softcap or 0.0,
+    d = ram.Desc(B=w.B, Sq=w.Sq, Skv=w.chunk, H=w.H, Hkv=w.Hkv, D=w.D,
+                 dtype=ram.RAM_F32 if w.dtype == "f32" else ram.RAM_BF16, scale=w.scale, softcap=w.softcap or 0.0,
                  causal=w.causal)
     if src is None:
         src = ram.MaskSrc(q_pos=_i32(w.q_pos), kv_pos=_i32(w.kv_pos), q_seg=_i32(w.q_seg), kv_seg=_i32(w.kv_seg))
@@ -261,23 +273,24 @@ def _ring_ref(w, dout, dense=None, dense_col0=None):
 
 
 def _ring_sinks_check(w, dout, got, ref, what, dense=None):
+    tol = GRAD_TOL_F32 if w.dtype == "f32" else SINK_TOL
     q, k, v, s64 = w.as_f64()
     qp, kp = w.positions()
     ro, rl = oracle.attention(q, k, v, scale=w.scale, q_pos=qp, kv_pos=kp, q_seg=w.q_seg, kv_seg=w.kv_seg,
                               causal=w.causal, softcap=w.softcap, sinks=s64, dense=dense)
-    _sinks_check(got, ref, ro, rl, dout.double().numpy(), s64, what)
+    _sinks_check(got, ref, ro, rl, dout.double().numpy(), s64, what, tol)
 
 
 @pytest.mark.parametrize("name", sorted(RING))
 def test_ring_backward(name):
     w = RING[name]()
     dout = torch.from_numpy(np.random.default_rng(zlib.crc32(name.encode())).standard_normal(
-        (w.B, w.Sq, w.H, w.D)).astype(np.float32)).to(torch.bfloat16)
+        (w.B, w.Sq, w.H, w.D)).astype(np.float32)).to(w.q.dtype)
     say(f"ring_attn_bwd_1gpu {name}: B={w.B} H={w.H}/{w.Hkv} Sq={w.Sq} chunks={w.n_chunks}x{w.chunk}")
     got = _run_ring_bwd(w, dout)
     ref = _ring_ref(w, dout)
     for nm, g, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
-        _rel(nm, g, r, GRAD_TOL, name)
+        _rel(nm, g, r, GRAD_TOL_F32 if w.dtype == "f32" else GRAD_TOL, name)
     if w.sinks is not None:
         _ring_sinks_check(w, dout, got[3], ref[3], name)
 
