@@ -407,26 +407,26 @@ __device__ __forceinline__ void lds_settle(TrPair (&t)[4]) {
 __device__ __forceinline__ void lds_settle_v(bf16x8 (&t)[4]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
 }
-// Four 16-byte reads at a, a+32, a+64, a+96 (the 16 row values of a lane), and their wait.
-__device__ __forceinline__ void lds_rows4(const char* a, f32x4 (&x)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %4 offset:32\n\t"
-      "ds_read_b128 %2, %4 offset:64\n\t"
-      "ds_read_b128 %3, %4 offset:96\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
-      : "v"(lds_addr(a)));
-}
 // Hand-off of 16 bf16 values per lane: two 16-byte halves, 1 KB apart.
 __device__ __forceinline__ void lds_put32(char* a, const bf16x8& lo, const bf16x8& hi) {
   asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024" : : "v"(lds_addr(a)), "v"(lo), "v"(hi));
 }
-__device__ __forceinline__ void lds_get32(const char* a, bf16x8& lo, bf16x8& hi) {
-  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(lo), "=&v"(hi)
-               : "v"(lds_addr(a)));
+// Reads issued without a wait; the values must pass lds_tie() after a later wait.
+__device__ __forceinline__ void lds_rows4_issue(const char* a, f32x4 (&x)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:32\n\t"
+      "ds_read_b128 %2, %4 offset:64\n\t"
+      "ds_read_b128 %3, %4 offset:96"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "v"(lds_addr(a)));
 }
+__device__ __forceinline__ void lds_get32_issue(const char* a, bf16x8& lo, bf16x8& hi) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024" : "=&v"(lo), "=&v"(hi) : "v"(lds_addr(a)));
+}
+// Ties values read without a wait to the point after an `s_waitcnt lgkmcnt(0)` issued before it.
+__device__ __forceinline__ void lds_tie(f32x4 (&x)[4]) { asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])); }
+__device__ __forceinline__ void lds_tie(bf16x8& lo, bf16x8& hi) { asm volatile("" : "+v"(lo), "+v"(hi)); }
 // Two 16-byte reads (a and b) and their wait.
 __device__ __forceinline__ void lds_pair4(const char* a, const char* b, f32x4& x, f32x4& y) {
   asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
@@ -595,6 +595,14 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
     const char* Ot = Qt + kTileElems * 2;
     char* const x_u = my_x + (u & 1) * 8192;
 
+    // The step's first LDS reads go out together: the first product's A operands and the
+    // row values (P waves: lse; dS waves: the partner's hand-off and D), one wait for all.
+    // Both roles issue the same reads (P waves ignore the hand-off slot they read): reads
+    // under a branch would leave their results to be joined by copies before the wait.
+    f32x4 rv[4];   // lse (P waves) or D (dS waves) of rows q0 + 8j + 4*lg + 0..3
+    bf16x8 gb[2];  // dS waves: G from the partner
+    lds_get32_issue(x_u, gb[0], gb[1]);
+    lds_rows4_issue(row_at(buf, pw ? 0 : 1, q0 + 4 * lg), rv);
     f32x16 X = f32x16{};   // S (P waves) or dP (dS waves)
     {
       const char* T = pw ? Qt : Ot;
@@ -605,9 +613,17 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
         a[ds] = lds_b128_issue(T + r * (2 * D) + ((c ^ swz<D>(r)) * 16));
       }
       lds_settle_v(a);
+      lds_tie(rv);
+      lds_tie(gb[0], gb[1]);
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds], kv[ds], X, 0, 0, 0);
     }
+    // The second product's A operands (dO^T for P waves, Q^T for dS waves) load while the
+    // weights or the score gradients are computed.
+    TrPair tr[2 * NDB];
+#pragma unroll
+    for (int f = 0; f < 2 * NDB; ++f) tr[f] = lds_tr<D>(pw ? Ot : Qt, q0 + (f / NDB) * 16, f % NDB, lane);
+    bf16x8 Bop[2];   // P (P waves) or dS (dS waves) as the second product's B operand
     if (pw) {
       const int qb = w_qb;
       const int r0 = qb * kBlockQ + wc.half * 64;
@@ -643,8 +659,6 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
           }
         }
       }
-      f32x4 la[4];   // lse of rows q0 + 8j + 4*lg + 0..3
-      lds_rows4(row_at(buf, 0, q0 + 4 * lg), la);
       // P in place of S; G = P (1 - t^2) goes to the partner (G = P without a cap)
       f32x16 Gw;
 #pragma unroll
@@ -652,7 +666,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
         // l * log2(e); a row with lse = -inf has no allowed key anywhere, so all its scores
         // are masked (-inf) and clamping its l2 to the lowest finite float keeps its
         // weights exactly 0 without a compare per score
-        const float l2 = fmaxf(la[i >> 2][i & 3] * kLog2e, -__FLT_MAX__);
+        const float l2 = fmaxf(rv[i >> 2][i & 3] * kLog2e, -__FLT_MAX__);
         if constexpr (CAP) {
           const float tt = fmaxf(X[i], -p.cap_log2) * (1.0f / p.cap_log2);
           X[i] = fast_exp2(X[i] - l2);
@@ -661,42 +675,26 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
           X[i] = fast_exp2(__builtin_fmaf(X[i], p.scale_log2, -l2));
         }
       }
-      bf16x8 Pb[2];
-      pack_b(X, Pb);
+      pack_b(X, Bop);
       if constexpr (CAP) {
         bf16x8 Gb[2];
         pack_b(Gw, Gb);
         lds_put32(x_u, Gb[0], Gb[1]);
       } else {
-        lds_put32(x_u, Pb[0], Pb[1]);
+        lds_put32(x_u, Bop[0], Bop[1]);
       }
-      // dV^T += dO^T P
-      TrPair tr[2 * NDB];
-#pragma unroll
-      for (int f = 0; f < 2 * NDB; ++f) tr[f] = lds_tr<D>(Ot, q0 + (f / NDB) * 16, f % NDB, lane);
-      lds_settle(tr);
-#pragma unroll
-      for (int f = 0; f < 2 * NDB; ++f)
-        acc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(tr[f]), Pb[f / NDB], acc[f % NDB], 0, 0, 0);
     } else {
-      // dS = G (dP - D), dK^T += Q^T dS (the partner wrote G in the previous step)
-      bf16x8 gb[2];
-      lds_get32(x_u, gb[0], gb[1]);
-      f32x4 da[4];   // D of rows q0 + 8j + 4*lg + 0..3
-      lds_rows4(row_at(buf, 1, q0 + 4 * lg), da);
+      // dS = G (dP - D)
       f32x16 dS;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dS[i] = (float)gb[i >> 3][i & 7] * (X[i] - da[i >> 2][i & 3]);
-      bf16x8 DSb[2];
-      pack_b(dS, DSb);
-      TrPair tr[2 * NDB];
-#pragma unroll
-      for (int f = 0; f < 2 * NDB; ++f) tr[f] = lds_tr<D>(Qt, q0 + (f / NDB) * 16, f % NDB, lane);
-      lds_settle(tr);
-#pragma unroll
-      for (int f = 0; f < 2 * NDB; ++f)
-        acc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(tr[f]), DSb[f / NDB], acc[f % NDB], 0, 0, 0);
+      for (int i = 0; i < 16; ++i) dS[i] = (float)gb[i >> 3][i & 7] * (X[i] - rv[i >> 2][i & 3]);
+      pack_b(dS, Bop);
     }
+    // dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves)
+    lds_settle(tr);
+#pragma unroll
+    for (int f = 0; f < 2 * NDB; ++f)
+      acc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(tr[f]), Bop[f / NDB], acc[f % NDB], 0, 0, 0);
     advance(wc);
     if (pw && wc.hi == 0 && wc.half == 0 && wc.qi < ccnt) {
       w_qb = rows[wc.qi];
