@@ -194,7 +194,7 @@ def backward(args, w, desc, q, k, v, src, sinks, out, lse, ws, stream, dense, ef
     # roofline leg: each chunk's backward call alone (dq written on the first visit, added after)
     bq, bk = ram.kernel_tile(ram.RAM_BF16, w.D)
     dkd = ram.Desc(**{**desc.__dict__, "block_q": bq, "block_kv": bk, "kv_stride_b": w.Skv * w.Hkv * w.D})
-    delta = torch.empty(w.B, w.H, w.Sq, dtype=torch.float32, device=dev)
+    delta = torch.empty(2, w.B, w.H, w.Sq, dtype=torch.float32, device=dev)
     ram.attn_bwd_prep(dkd, out, dout, lse, sinks, delta, dsinks, stream=stream)
     dq32 = torch.empty(w.B, w.Sq, w.H, w.D, dtype=torch.float32, device=dev)
     dk32 = torch.empty(w.B, w.Skv, w.Hkv, w.D, dtype=torch.float32, device=dev)

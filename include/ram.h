@@ -201,8 +201,10 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
  * out, dout: [B, Sq, H, D] dense in desc->dtype; lse: float32 [B, H, Sq] (as
  * the forward wrote them). */
 
-/* delta[b,h,i] = dout[b,i,h,:] . out[b,i,h,:] (float32 [B, H, Sq]) and, when
- * sinks is not NULL, dsinks (float32 [H]) as above. */
+/* delta: float32 [2, B, H, Sq], the row values the chunk backward reads:
+ * delta[0,b,h,i] = dout[b,i,h,:] . out[b,i,h,:] and delta[1,b,h,i] =
+ * lse[b,h,i] * log2(e) (+inf where lse is -inf); and, when sinks is not NULL,
+ * dsinks (float32 [H]) as above. */
 ram_status attn_bwd_prep(const ram_attn_desc* desc, const void* out, const void* dout, const float* lse,
                          const float* sinks, float* delta, float* dsinks, hipStream_t stream);
 

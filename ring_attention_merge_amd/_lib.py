@@ -338,13 +338,13 @@ def ring_attn_fwd_1gpu(desc: Desc, n_chunks: int, q_shard: int, q, k_all, v_all,
 
 # ------------------------------------------------------------------------------ backward
 def attn_bwd_prep(desc: Desc, out, dout, lse, sinks, delta, dsinks, stream=None):
-    """attn_bwd_prep: delta = rowsum(dout * out) [B,H,Sq] and, with sinks, dsinks [H]."""
+    """attn_bwd_prep: delta [2,B,H,Sq] (rowsum(dout * out), then the base-2 lse) and, with sinks, dsinks [H]."""
     dt = _tdtype(desc.dtype)
     n = desc.B * desc.Sq * desc.H * desc.D
     _need(out, "out", dt, n)
     _need(dout, "dout", dt, n)
     _need(lse, "lse", torch.float32, desc.B * desc.H * desc.Sq)
-    _need(delta, "delta", torch.float32, desc.B * desc.H * desc.Sq)
+    _need(delta, "delta", torch.float32, 2 * desc.B * desc.H * desc.Sq)
     if sinks is not None:
         _need(sinks, "sinks", torch.float32, desc.H)
         _need(dsinks, "dsinks", torch.float32, desc.H)
@@ -360,7 +360,7 @@ def attn_bwd_chunk(desc: Desc, q, k, v, dout, lse, delta, src: MaskSrc, mask: Bl
     _need(q, "q", dt, _span(desc.B, desc.q_stride_b, desc.Sq * desc.H * desc.D))
     _need(dout, "dout", dt, desc.B * desc.Sq * desc.H * desc.D)
     _need(lse, "lse", torch.float32, desc.B * desc.H * desc.Sq)
-    _need(delta, "delta", torch.float32, desc.B * desc.H * desc.Sq)
+    _need(delta, "delta", torch.float32, 2 * desc.B * desc.H * desc.Sq)
     _need(dq, "dq", torch.float32, desc.B * desc.Sq * desc.H * desc.D)
     kvn = _span(desc.B, desc.kv_stride_b, desc.Skv * desc.Hkv * desc.D)
     if desc.Skv > 0:

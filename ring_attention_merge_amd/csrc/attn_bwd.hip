@@ -513,10 +513,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
       c.qi += c.half == 0;
     }
   };
-  // The row array this wave moves: waves 0-3 lse, D, positions, segments (empty when
-  // absent); waves 4-7 an empty load into an unused array, so every wave issues the same count.
+  // The row array this wave moves: waves 0-3 the base-2 lse and D (both written by the
+  // prep kernel), positions, segments (empty when absent); waves 4-7 an empty load into
+  // an unused array, so every wave issues the same count.
   const float* row_src =
-      w == 0 ? p.lse : (w == 1 ? bp.delta : (w == 2 ? reinterpret_cast<const float*>(p.q_pos)
+      w == 0 ? bp.delta + (int64_t)p.B * p.H * p.Sq : (w == 1 ? bp.delta : (w == 2 ? reinterpret_cast<const float*>(p.q_pos)
                                                    : (w == 3 ? reinterpret_cast<const float*>(p.q_seg) : nullptr)));
   const bool row_per_head = w < 2;
   // Staging: bases at head g*G of this workgroup's batch; the values that change only with
@@ -599,7 +600,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
     // row values (P waves: lse; dS waves: the partner's hand-off and D), one wait for all.
     // Both roles issue the same reads (P waves ignore the hand-off slot they read): reads
     // under a branch would leave their results to be joined by copies before the wait.
-    f32x4 rv[4];   // lse (P waves) or D (dS waves) of rows q0 + 8j + 4*lg + 0..3
+    f32x4 rv[4];   // base-2 lse (P waves) or D (dS waves) of rows q0 + 8j + 4*lg + 0..3
     bf16x8 gb[2];  // dS waves: G from the partner
     lds_get32_issue(x_u, gb[0], gb[1]);
     lds_rows4_issue(row_at(buf, pw ? 0 : 1, q0 + 4 * lg), rv);
@@ -663,10 +664,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
       f32x16 Gw;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        // l * log2(e); a row with lse = -inf has no allowed key anywhere, so all its scores
-        // are masked (-inf) and clamping its l2 to the lowest finite float keeps its
-        // weights exactly 0 without a compare per score
-        const float l2 = fmaxf(rv[i >> 2][i & 3] * kLog2e, -__FLT_MAX__);
+        const float l2 = rv[i >> 2][i & 3];   // lse * log2(e), +inf for a row with no allowed key
         if constexpr (CAP) {
           const float tt = fmaxf(X[i], -p.cap_log2) * (1.0f / p.cap_log2);
           X[i] = fast_exp2(X[i] - l2);
@@ -759,7 +757,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(int64_t n_rows, int H, i
     const int64_t bi = pair / H;
     const int i = (int)(bi % Sq);
     const int64_t bb = bi / Sq;
-    delta[(bb * H + h) * Sq + i] = acc;
+    const int64_t at = (bb * H + h) * Sq + i;
+    delta[at] = acc;
+    // the row's logsumexp in base 2; +inf for a row with no allowed key, whose weights
+    // exp2(s * scale * log2(e) - that) are then exactly 0
+    const float l = lse[at];
+    delta[n_rows + at] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
   }
 }
 

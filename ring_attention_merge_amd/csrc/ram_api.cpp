@@ -289,7 +289,7 @@ BwdLayout bwd_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits) {
   take(L.dq_off, (size_t)d->B * d->Sq * d->H * d->D * sizeof(float));
   take(L.dk_off, (size_t)kv_elems * sizeof(float));
   take(L.dv_off, (size_t)kv_elems * sizeof(float));
-  take(L.delta_off, (size_t)d->B * d->H * d->Sq * sizeof(float));
+  take(L.delta_off, (size_t)2 * d->B * d->H * d->Sq * sizeof(float));
   take(L.cls_off, (size_t)tiles);
   take(L.cnt_off, (size_t)n_chunks * d->B * nQb * sizeof(int32_t));
   take(L.col_off, (size_t)tiles * sizeof(int32_t));

@@ -260,7 +260,7 @@ def test_backward_validation(lib):
     need = lib.ring_attn_bwd_workspace_bytes(ctypes.byref(dr), 4, None)
     al = lambda x: (x + 255) // 256 * 256
     tiles = 4 * 4 * 8
-    expect = (al(512 * 4 * 128 * 4) + 2 * al(4 * 512 * 2 * 128 * 4) + al(4 * 512 * 4) + al(tiles)
+    expect = (al(512 * 4 * 128 * 4) + 2 * al(4 * 512 * 2 * 128 * 4) + al(2 * 4 * 512 * 4) + al(tiles)
               + al(4 * 4 * 4) + al(tiles * 4) + al(4 * 8 * 4) + al(tiles * 4))
     assert need == expect
     dense = lib.ring_attn_bwd_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src(dense=FAKE2)))

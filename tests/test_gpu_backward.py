@@ -176,9 +176,15 @@ def test_chunk_backward(name):
     # backward of the chunk
     bm = ram.alloc_block_mask(d, with_bits=src.dense is not None, with_cols=True)
     ram.build_block_mask(d, src, bm)
-    delta = torch.full((B, H, Sq), float("nan"), device=DEV)
+    delta = torch.full((2, B, H, Sq), float("nan"), device=DEV)
     dsinks = None if sinks is None else torch.full((H,), float("nan"), device=DEV)
     ram.attn_bwd_prep(d, out, dod, lse, sd, delta, dsinks)
+    # the prep's second row array: the forward's lse in base 2, +inf for rows with no key
+    l32 = lse.cpu().numpy()
+    want = np.where(np.isneginf(l32), np.float32(np.inf), l32 * np.float32(1.4426950408889634))
+    got = delta[1].cpu().numpy()
+    assert np.array_equal(np.isinf(got), np.isinf(want)) and np.allclose(got[np.isfinite(want)], want[np.isfinite(want)],
+                                                                         rtol=1e-6, atol=0), name
     dq = torch.full((B, Sq, H, D), float("nan"), device=DEV)
     dk = torch.full((B, Skv, Hkv, D), float("nan"), device=DEV)
     dv = torch.full((B, Skv, Hkv, D), float("nan"), device=DEV)
@@ -205,7 +211,7 @@ def test_chunk_backward_add_mode():
     ram.ring_attn_fwd_1gpu(d, 1, -1, qd, kd, vd, src, None, out, lse, ws)
     bm = ram.alloc_block_mask(d, with_cols=True)
     ram.build_block_mask(d, src, bm)
-    delta = torch.empty(d.B, d.H, d.Sq, device=DEV)
+    delta = torch.empty(2, d.B, d.H, d.Sq, device=DEV)
     ram.attn_bwd_prep(d, out, dod, lse, None, delta, None)
     dq1 = torch.empty(d.B, d.Sq, d.H, 128, device=DEV)
     dq2 = torch.empty_like(dq1)
