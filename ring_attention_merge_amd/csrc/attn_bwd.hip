@@ -582,11 +582,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
     w_mask = tile_mask_kind(w_qb);
   }
   for (int t = 0; t <= n_steps; ++t) {
-    // the buffer of step t+2 was last read by the dS waves in step t-1 (for step t-2)
-    stage((t + kAhead) & (kStages - 1));
-    // P waves work on step t, dS waves on step t-1
+    // Each step stages step t+2, into the buffer the dS waves last read in step t-1 (for
+    // step t-2). P waves work on step t, dS waves on step t-1.
     const int u = pw ? t : t - 1;
     if (u < 0 || u >= n_steps) {
+      stage((t + kAhead) & (kStages - 1));
       __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kAhead - 1)));
       __builtin_amdgcn_s_barrier();
       continue;
@@ -613,6 +613,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
         const int r = q0 + ln, c = 2 * ds + lg;
         a[ds] = lds_b128_issue(T + r * (2 * D) + ((c ^ swz<D>(r)) * 16));
       }
+      // the stage's loads issue while these reads are served
+      stage((t + kAhead) & (kStages - 1));
       lds_settle_v(a);
       lds_tie(rv);
       lds_tie(gb[0], gb[1]);
