@@ -581,129 +581,166 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
     w_qb = rows[0];
     w_mask = tile_mask_kind(w_qb);
   }
-  for (int t = 0; t <= n_steps; ++t) {
-    // Each step stages step t+2, into the buffer the dS waves last read in step t-1 (for
-    // step t-2). P waves work on step t, dS waves on step t-1.
-    const int u = pw ? t : t - 1;
-    if (u < 0 || u >= n_steps) {
-      stage((t + kAhead) & (kStages - 1));
-      __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kAhead - 1)));
-      __builtin_amdgcn_s_barrier();
-      continue;
-    }
-    const int buf = u & (kStages - 1);
-    const char* Qt = reinterpret_cast<const char*>(smem + buf * 2 * kTileElems);
-    const char* Ot = Qt + kTileElems * 2;
-    char* const x_u = my_x + (u & 1) * 8192;
-
-    // The step's first LDS reads go out together: the first product's A operands and the
-    // row values (P waves: lse; dS waves: the partner's hand-off and D), one wait for all.
-    // Both roles issue the same reads (P waves ignore the hand-off slot they read): reads
-    // under a branch would leave their results to be joined by copies before the wait.
-    f32x4 rv[4];   // base-2 lse (P waves) or D (dS waves) of rows q0 + 8j + 4*lg + 0..3
-    bf16x8 gb[2];  // dS waves: G from the partner
-    lds_get32_issue(x_u, gb[0], gb[1]);
-    lds_rows4_issue(row_at(buf, pw ? 0 : 1, q0 + 4 * lg), rv);
-    f32x16 X = f32x16{};   // S (P waves) or dP (dS waves)
-    {
-      const char* T = pw ? Qt : Ot;
-      bf16x8 a[NDS];
+  // The dS waves run half a step behind the P waves: in step t a dS wave first finishes
+  // step t-1 (dS from the dP it computed at the end of step t-1 and the partner's G, then
+  // dK^T += Q^T dS) and then computes dP of step t, which it keeps in registers. Its
+  // products thus fall in the P wave's softmax phase, and its VALU work in the P wave's
+  // wait for its first operands. Step t reads buffers t (P waves, and dO for the dS
+  // waves' dP) and t-1 (the dS waves' Q^T, D and G); the stage writes buffer t+2.
+  // The two roles run separate loops (the same number of barriers), so that neither
+  // role's registers count against the other's.
+  // Step t+1 has landed once at most the loads of step t+2 are outstanding (every LDS
+  // access of a step has been waited for before its barrier).
+  auto step_end = [&]() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kAhead - 1)));
+    __builtin_amdgcn_s_barrier();
+  };
+  if (pw) {
+    for (int t = 0; t <= n_steps; ++t) {
+      const int buf = t & (kStages - 1);
+      const char* Qt = reinterpret_cast<const char*>(smem + buf * 2 * kTileElems);
+      const char* Ot = Qt + kTileElems * 2;
+      if (t == n_steps) {
+        stage((t + kAhead) & (kStages - 1));
+      } else {
+        char* const x_t = my_x + (t & 1) * 8192;
+        // the first product's A operands (Q rows) and the rows' base-2 lse, one wait for both
+        f32x4 rv[4];
+        lds_rows4_issue(row_at(buf, 0, q0 + 4 * lg), rv);
+        f32x16 X = f32x16{};
+        {
+          bf16x8 a[NDS];
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const int r = q0 + ln, c = 2 * ds + lg;
-        a[ds] = lds_b128_issue(T + r * (2 * D) + ((c ^ swz<D>(r)) * 16));
-      }
-      // the stage's loads issue while these reads are served
-      stage((t + kAhead) & (kStages - 1));
-      lds_settle_v(a);
-      lds_tie(rv);
-      lds_tie(gb[0], gb[1]);
+          for (int ds = 0; ds < NDS; ++ds) {
+            const int r = q0 + ln, c = 2 * ds + lg;
+            a[ds] = lds_b128_issue(Qt + r * (2 * D) + ((c ^ swz<D>(r)) * 16));
+          }
+          // the stage's loads issue while these reads are served
+          stage((t + kAhead) & (kStages - 1));
+          lds_settle_v(a);
+          lds_tie(rv);
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds], kv[ds], X, 0, 0, 0);
-    }
-    // The second product's A operands (dO^T for P waves, Q^T for dS waves) load while the
-    // weights or the score gradients are computed.
-    TrPair tr[2 * NDB];
+          for (int ds = 0; ds < NDS; ++ds) X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds], kv[ds], X, 0, 0, 0);
+        }
+        // dO^T operands of dV load while the weights are computed
+        TrPair tr[2 * NDB];
 #pragma unroll
-    for (int f = 0; f < 2 * NDB; ++f) tr[f] = lds_tr<D>(pw ? Ot : Qt, q0 + (f / NDB) * 16, f % NDB, lane);
-    bf16x8 Bop[2];   // P (P waves) or dS (dS waves) as the second product's B operand
-    if (pw) {
-      const int qb = w_qb;
-      const int r0 = qb * kBlockQ + wc.half * 64;
-      const int need_mask = w_mask;
-      if constexpr (CAP) {
+        for (int f = 0; f < 2 * NDB; ++f) tr[f] = lds_tr<D>(Ot, q0 + (f / NDB) * 16, f % NDB, lane);
+        const int qb = w_qb;
+        const int r0 = qb * kBlockQ + wc.half * 64;
+        const int need_mask = w_mask;
+        if constexpr (CAP) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) X[i] = capped_log2(X[i], p.cap_k2, p.cap_log2);
-      }
-      if (BITS && need_mask == 2) {
-        // bits of the tile: row (step half * 64 + q0 + r), word kbw, bit ln
-        const uint32_t* tb = p.mask_bits + (((int64_t)b * p.nQb + qb) * p.nKb + kb) * kBlockQ * 2 +
-                             (int64_t)((r0 - qb * kBlockQ) + q0 + 4 * lg) * 2 + kbw;
+          for (int i = 0; i < 16; ++i) X[i] = capped_log2(X[i], p.cap_k2, p.cap_log2);
+        }
+        if (BITS && need_mask == 2) {
+          // bits of the tile: row (step half * 64 + q0 + r), word kbw, bit ln
+          const uint32_t* tb = p.mask_bits + (((int64_t)b * p.nQb + qb) * p.nKb + kb) * kBlockQ * 2 +
+                               (int64_t)((r0 - qb * kBlockQ) + q0 + 4 * lg) * 2 + kbw;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (((tb[(8 * (i >> 2) + (i & 3)) * 2] >> ln) & 1u) == 0u) X[i] = neg_inf();
-      } else if (need_mask) {
-        if (!p.q_pos && !p.kv_pos && !p.q_seg) {
-          mask_kv_seq(X, p, key, r0, q0, lg);
-        } else {
-          // explicit positions / segments: the rows' values four at a time
+          for (int i = 0; i < 16; ++i)
+            if (((tb[(8 * (i >> 2) + (i & 3)) * 2] >> ln) & 1u) == 0u) X[i] = neg_inf();
+        } else if (need_mask) {
+          if (!p.q_pos && !p.kv_pos && !p.q_seg) {
+            mask_kv_seq(X, p, key, r0, q0, lg);
+          } else {
+            // explicit positions / segments: the rows' values four at a time
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            f32x4 qpv, qsv;
-            lds_pair4(row_at(buf, 2, q0 + 8 * j + 4 * lg), row_at(buf, 3, q0 + 8 * j + 4 * lg), qpv, qsv);
+            for (int j = 0; j < 4; ++j) {
+              f32x4 qpv, qsv;
+              lds_pair4(row_at(buf, 2, q0 + 8 * j + 4 * lg), row_at(buf, 3, q0 + 8 * j + 4 * lg), qpv, qsv);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = q0 + 8 * j + 4 * lg + e;
-              bool ok = key < p.Skv;
-              if (p.causal) ok = ok && kpos <= (p.q_pos ? __float_as_int(qpv[e]) : p.q_pos_base + r0 + r);
-              if (p.q_seg) ok = ok && __float_as_int(qsv[e]) == kseg && kseg != -1;
-              if (!ok) X[4 * j + e] = neg_inf();
+              for (int e = 0; e < 4; ++e) {
+                const int r = q0 + 8 * j + 4 * lg + e;
+                bool ok = key < p.Skv;
+                if (p.causal) ok = ok && kpos <= (p.q_pos ? __float_as_int(qpv[e]) : p.q_pos_base + r0 + r);
+                if (p.q_seg) ok = ok && __float_as_int(qsv[e]) == kseg && kseg != -1;
+                if (!ok) X[4 * j + e] = neg_inf();
+              }
             }
           }
         }
-      }
-      // P in place of S; G = P (1 - t^2) goes to the partner (G = P without a cap)
-      f32x16 Gw;
+        // P in place of S; G = P (1 - t^2) goes to the partner (G = P without a cap)
+        f32x16 Gw;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float l2 = rv[i >> 2][i & 3];   // lse * log2(e), +inf for a row with no allowed key
+        for (int i = 0; i < 16; ++i) {
+          const float l2 = rv[i >> 2][i & 3];   // lse * log2(e), +inf for a row with no allowed key
+          if constexpr (CAP) {
+            const float tt = fmaxf(X[i], -p.cap_log2) * (1.0f / p.cap_log2);
+            X[i] = fast_exp2(X[i] - l2);
+            Gw[i] = X[i] * __builtin_fmaf(-tt, tt, 1.0f);
+          } else {
+            X[i] = fast_exp2(__builtin_fmaf(X[i], p.scale_log2, -l2));
+          }
+        }
+        bf16x8 Pb[2];
+        pack_b(X, Pb);
         if constexpr (CAP) {
-          const float tt = fmaxf(X[i], -p.cap_log2) * (1.0f / p.cap_log2);
-          X[i] = fast_exp2(X[i] - l2);
-          Gw[i] = X[i] * __builtin_fmaf(-tt, tt, 1.0f);
+          bf16x8 Gb[2];
+          pack_b(Gw, Gb);
+          lds_put32(x_t, Gb[0], Gb[1]);
         } else {
-          X[i] = fast_exp2(__builtin_fmaf(X[i], p.scale_log2, -l2));
+          lds_put32(x_t, Pb[0], Pb[1]);
+        }
+        // dV^T += dO^T P
+        lds_settle(tr);
+#pragma unroll
+        for (int f = 0; f < 2 * NDB; ++f)
+          acc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(tr[f]), Pb[f / NDB], acc[f % NDB], 0, 0, 0);
+        advance(wc);
+        if (wc.hi == 0 && wc.half == 0 && wc.qi < ccnt) {
+          w_qb = rows[wc.qi];
+          w_mask = tile_mask_kind(w_qb);
         }
       }
-      pack_b(X, Bop);
-      if constexpr (CAP) {
-        bf16x8 Gb[2];
-        pack_b(Gw, Gb);
-        lds_put32(x_u, Gb[0], Gb[1]);
-      } else {
-        lds_put32(x_u, Bop[0], Bop[1]);
+      step_end();
+    }
+  } else {
+    f32x16 dp_keep = f32x16{};   // dP of the step the wave finishes next
+    for (int t = 0; t <= n_steps; ++t) {
+      const char* Ot = reinterpret_cast<const char*>(smem + (t & (kStages - 1)) * 2 * kTileElems) + kTileElems * 2;
+      if (t > 0) {
+        // finish step t-1: dS = G (dP - D), dK^T += Q^T dS
+        const int pb = (t - 1) & (kStages - 1);
+        const char* Qp = reinterpret_cast<const char*>(smem + pb * 2 * kTileElems);
+        char* const x_p = my_x + ((t - 1) & 1) * 8192;
+        TrPair tr[2 * NDB];
+#pragma unroll
+        for (int f = 0; f < 2 * NDB; ++f) tr[f] = lds_tr<D>(Qp, q0 + (f / NDB) * 16, f % NDB, lane);
+        bf16x8 gb[2];
+        f32x4 rv[4];   // D of rows q0 + 8j + 4*lg + 0..3
+        lds_get32_issue(x_p, gb[0], gb[1]);
+        lds_rows4_issue(row_at(pb, 1, q0 + 4 * lg), rv);
+        if (t == n_steps) stage((t + kAhead) & (kStages - 1));
+        lds_settle(tr);
+        lds_tie(rv);
+        lds_tie(gb[0], gb[1]);
+        f32x16 dS;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dS[i] = (float)gb[i >> 3][i & 7] * (dp_keep[i] - rv[i >> 2][i & 3]);
+        bf16x8 DSb[2];
+        pack_b(dS, DSb);
+#pragma unroll
+        for (int f = 0; f < 2 * NDB; ++f)
+          acc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(tr[f]), DSb[f / NDB], acc[f % NDB], 0, 0, 0);
       }
-    } else {
-      // dS = G (dP - D)
-      f32x16 dS;
+      if (t < n_steps) {
+        // dP of step t = dO V^T
+        bf16x8 a[NDS];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dS[i] = (float)gb[i >> 3][i & 7] * (X[i] - rv[i >> 2][i & 3]);
-      pack_b(dS, Bop);
-    }
-    // dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves)
-    lds_settle(tr);
+        for (int ds = 0; ds < NDS; ++ds) {
+          const int r = q0 + ln, c = 2 * ds + lg;
+          a[ds] = lds_b128_issue(Ot + r * (2 * D) + ((c ^ swz<D>(r)) * 16));
+        }
+        stage((t + kAhead) & (kStages - 1));
+        lds_settle_v(a);
+        f32x16 X = f32x16{};
 #pragma unroll
-    for (int f = 0; f < 2 * NDB; ++f)
-      acc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(tr[f]), Bop[f / NDB], acc[f % NDB], 0, 0, 0);
-    advance(wc);
-    if (pw && wc.hi == 0 && wc.half == 0 && wc.qi < ccnt) {
-      w_qb = rows[wc.qi];
-      w_mask = tile_mask_kind(w_qb);
+        for (int ds = 0; ds < NDS; ++ds) X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds], kv[ds], X, 0, 0, 0);
+        dp_keep = X;
+      }
+      step_end();
     }
-    // Step t+1 has landed once at most the loads of step t+2 are outstanding
-    // (the LDS stores and reads above have all been waited for).
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kDmaPerStep * (kAhead - 1)));
-    __builtin_amdgcn_s_barrier();
   }
   __builtin_amdgcn_s_waitcnt(0);   // the empty loads of the last stages
   __syncthreads();
