@@ -375,15 +375,17 @@ __device__ __forceinline__ void mask_kv_seq(f32x16& S, const AttnParams& p, int 
 
 // Eight waves in two roles, two waves per SIMD. For key block kbw (32 keys)
 // and query half qh (32 rows of the 64-row step):
-//   P wave  (waves 0-3), step t:   S = Q K^T, mask, P = exp2(S' - lse),
-//                                  hands G = P (1 - t^2) (G = P without a cap)
-//                                  to its partner, then dV^T += dO^T P
-//   dS wave (waves 4-7), step t-1: dP = dO V^T, dS = G (dP - D), dK^T += Q^T dS
+//   P wave  (waves 0-3), step t: S = Q K^T, mask, P = exp2(S' - lse), hands
+//                                G = P (1 - t^2) (G = P without a cap) to its
+//                                partner, then dV^T += dO^T P
+//   dS wave (waves 4-7), step t: dS = G (dP - D) and dK^T += Q^T dS of step
+//                                t-1, then dP = dO V^T of step t (kept in
+//                                registers for the next step)
 // Each wave runs 16 products per step and holds one accumulator (64
 // registers) and one of K / V (32), so two waves fit a SIMD and each hides
-// the other's latency. The dS waves trail by one step, so the hand-off
-// (bf16, 32 bytes per lane, double-buffered in LDS) needs no barrier of its
-// own: one barrier per step. The step data (Q, dO tiles and the rows' lse, D,
+// the other's latency. The dS waves use the hand-off one step after it is
+// written (bf16, 32 bytes per lane, double-buffered in LDS), so it needs no
+// barrier of its own: one barrier per step. The step data (Q, dO tiles and the rows' lse, D,
 // positions, segments) comes through a 4-stage LDS-DMA ring filled two steps
 // ahead (the dS waves still read the previous stage), 5 loads per wave and
 // step (3 at D = 64), with one fixed vmcnt wait per step. Every LDS access in the loop is
