@@ -161,6 +161,27 @@ def recorded_traffic(workload: str):
         return None
 
 
+def recorded_mfma_busy(workload: str):
+    """Fraction of the ring launch's cycles with the matrix cores busy, from the committed counter
+    summary (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x GRBM_GUI_ACTIVE per XCD), if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_bf16_dma_ring_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        line = line.strip().strip("`")
+        if "=" in line and " " not in line.split("=", 1)[0]:
+            k, v = line.split("=", 1)
+            fields[k] = v.strip()
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["mfma_busy_frac"])
+    except (KeyError, ValueError):
+        return None
+
+
 def backward(args, w, desc, q, k, v, src, sinks, out, lse, ws, stream, dense, eff_flops_chunk, fwd_step):
     """The --backward leg: ring_attn_bwd_1gpu steps, then each chunk's attn_bwd_chunk timed alone."""
     dev = q.device
@@ -443,6 +464,10 @@ def main():
     measured = mfma_rates(dev, stream)
     roofline["measured_peak_random"] = measured["random"]
     roofline["frac_of_measured_random"] = round(achieved / measured["random"], 4)
+    # rocprofv3 counters of the same launch, recorded in profiles/ (null once the kernel changed)
+    roofline["mfma_busy"] = recorded_mfma_busy(args.workload) if fused else None
+    roofline["hbm_gbs"] = (round(roofline["traffic"] / (kern_ms * 1e-3 / launches) / 1e9, 1)
+                           if roofline["traffic"] else None)
     log(f"MFMA probe: {measured['zeros']} TFLOP/s with zero operands, {measured['random']} with random ones")
     builder = None if dense is None else mask_builder_rate(w, desc, dense, bq, bk, dev, stream, reps)
     if args.copy_calibration:
