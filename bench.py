@@ -54,8 +54,9 @@ BWD_FLOP_FACTOR = 2.5
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 REF_TILE = 128                  # fixed reference tiling for effective FLOPs
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
-ATTN_KERNEL = "attn_fwd_bf16_dma_ring<false, false>"
-ATTN_KERNEL_BITS = "attn_fwd_bf16_dma_ring<false, true>"
+def ring_kernel_name(cap: bool, bits: bool) -> str:
+    """The ring kernel instantiation a launch runs (soft cap, stored mask bits)."""
+    return f"attn_fwd_bf16_dma_ring<{str(bool(cap)).lower()}, {str(bool(bits)).lower()}>"
 
 
 def log(*a):
@@ -458,7 +459,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": recorded_traffic(args.workload) if fused else None,
-                "kernel": (ATTN_KERNEL if dense is None else ATTN_KERNEL_BITS) if fused else "per-chunk launches",
+                "kernel": ring_kernel_name(w.softcap, dense is not None) if fused else "per-chunk launches",
                 "launches_per_step": launches, "mean_launch_us": round(1e3 * kern_ms / launches, 2),
                 "flops_per_launch_mean": eff_flops / launches}
     measured = mfma_rates(dev, stream)

@@ -347,9 +347,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
 // id % 8 takes the contiguous item range [x*per, (x+1)*per).
 __device__ __forceinline__ bool decode_kv_work(const AttnParams& p, int& b, int& g, int& kb) {
   const int64_t T = (int64_t)p.B * p.Hkv * p.nKb;
-  const int64_t per = (T + 7) / 8;
   const int64_t id = blockIdx.x;
-  const int64_t item = (id & 7) * per + (id >> 3);
+  // as decode_work: whole (batch, kv head) groups per XCD when they divide evenly, else round
+  // robin (causal kv tiles differ in work)
+  int64_t item = id;
+  if (((int64_t)p.B * p.Hkv) % 8 == 0) item = (id & 7) * (T / 8) + (id >> 3);
   if (item >= T) return false;
   kb = (int)(item % p.nKb);
   const int64_t bg = item / p.nKb;

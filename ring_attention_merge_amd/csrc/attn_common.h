@@ -41,9 +41,13 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T* as_const_s
 __device__ __forceinline__ bool decode_work(const AttnParams& p, int& b, int& h, int& qb) {
   const int G = p.H / p.Hkv;
   const int64_t T = (int64_t)p.B * p.Hkv * p.nQb * G;
-  const int64_t per = (T + 7) / 8;
   const int64_t id = blockIdx.x;
-  const int64_t item = (id & 7) * per + (id >> 3);
+  // Workgroups go to the 8 XCDs round robin (block id mod 8). With whole (batch, kv head)
+  // groups per XCD, a group's K / V stay in one XCD's L2. With fewer groups than that (MQA,
+  // small batches) a contiguous share would give one XCD the heaviest causal rows: there
+  // the items go round robin too, so that each XCD gets some heads of every q tile.
+  int64_t item = id;
+  if (((int64_t)p.B * p.Hkv) % 8 == 0) item = (id & 7) * (T / 8) + (id >> 3);
   if (item >= T) return false;
   const int hg = (int)(item % G);
   const int64_t r = item / G;
