@@ -345,16 +345,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
 // ------------------------------------------------------------------------------ dk, dv
 // Work decode: item order (batch * Hkv + kv head, kv tile ascending); XCD x =
 // id % 8 takes the contiguous item range [x*per, (x+1)*per).
-__device__ __forceinline__ bool decode_kv_work(const AttnParams& p, int& b, int& g, int& kb) {
-  const int64_t T = (int64_t)p.B * p.Hkv * p.nKb;
+__device__ __forceinline__ bool decode_kv_work(const AttnParams& p, int S, int& b, int& g, int& kb, int& s) {
+  const int64_t T = (int64_t)p.B * p.Hkv * p.nKb * S;
   const int64_t id = blockIdx.x;
   // as decode_work: whole (batch, kv head) groups per XCD when they divide evenly, else round
   // robin (causal kv tiles differ in work)
   int64_t item = id;
   if (((int64_t)p.B * p.Hkv) % 8 == 0) item = (id & 7) * (T / 8) + (id >> 3);
   if (item >= T) return false;
-  kb = (int)(item % p.nKb);
-  const int64_t bg = item / p.nKb;
+  s = (int)(item % S);
+  kb = (int)((item / S) % p.nKb);
+  const int64_t bg = item / S / p.nKb;
   g = (int)(bg % p.Hkv);
   b = (int)(bg / p.Hkv);
   return true;
@@ -454,15 +455,17 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
   char* const xch = rows_lds + kRowsBytes;
   auto row_at = [&](int buf, int arr, int r) { return rows_lds + ((buf * 8 + arr) * 64 + r) * 4; };
 
-  int b, g, kb;
-  if (!decode_kv_work(p, b, g, kb)) return;
+  int b, g, kb, hs;
+  const int S = bp.head_split;
+  if (!decode_kv_work(p, S, b, g, kb, hs)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, lg = lane >> 5;
   const bool pw = w < 4;                     // P wave (else dS wave)
   const int kbw = w & 1, qh = (w >> 1) & 1;  // key block and query half
-  const int G = p.H / p.Hkv;
+  const int G = p.H / p.Hkv / S;   // heads of the group this workgroup walks
+  const int h0 = g * (p.H / p.Hkv) + hs * G;   // the first of them
   const int key = kb * kBlockKV + 32 * kbw + ln;
   const bool key_ok = key < p.Skv;
   char* const my_x = xch + (kbw * 2 + qh) * 2 * 1024 + lane * 16;   // parity 0; parity 1 at + 8 KB
@@ -527,10 +530,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
   // Staging: bases at head g*G of this workgroup's batch; the values that change only with
   // the staged q tile or half (first row, byte counts, row offset) are recomputed only then,
   // and a step adds its head's stride (steps past the last stage empty loads).
-  const __bf16* q_wg = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b + (int64_t)g * G * D;
-  const __bf16* o_wg = reinterpret_cast<const __bf16*>(bp.dout) + ((int64_t)b * p.Sq * p.H + (int64_t)g * G) * D;
+  const __bf16* q_wg = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b + (int64_t)h0 * D;
+  const __bf16* o_wg = reinterpret_cast<const __bf16*>(bp.dout) + ((int64_t)b * p.Sq * p.H + h0) * D;
   const float* r_wg =
-      row_src ? row_src + (row_per_head ? ((int64_t)b * p.H + g * G) * p.Sq : (int64_t)b * p.qm_stride_b) : p.lse;
+      row_src ? row_src + (row_per_head ? ((int64_t)b * p.H + h0) * p.Sq : (int64_t)b * p.qm_stride_b) : p.lse;
   const int r_step = row_per_head ? p.Sq : 0;   // row-array elements per head
   Cursor stc{0, 0, 0};                          // the next step to stage
   int64_t st_off = 0;                           // elements to its first row at head g*G
@@ -761,7 +764,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkv(BwdParams bp) {
   __syncthreads();
   if (qh == 1 || !key_ok) return;
   const float sc = pw ? 1.0f : p.scale_log2 * kLn2;   // dk carries the score scale
-  float* dst = (pw ? bp.dv : bp.dk) + (int64_t)b * bp.dkv_stride_b + ((int64_t)key * p.Hkv + g) * D;
+  float* dst = (pw ? bp.dv : bp.dk) + hs * bp.part_stride + (int64_t)b * bp.dkv_stride_b + ((int64_t)key * p.Hkv + g) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -807,6 +810,24 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(int64_t n_rows, int H, i
     const float l = lse[at];
     delta[n_rows + at] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
   }
+}
+
+// dst[b * dst_stride + i] = sum over s of src[s * part_stride + b * n + i], four floats per thread.
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float* src, int S, int64_t part_stride, int64_t n4,
+                                                        float* dst, int64_t dst_stride) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  if (i >= n4) return;
+  const float4* sp = reinterpret_cast<const float4*>(src + (int64_t)b * n4 * 4) + i;
+  float4 a = sp[0];
+  for (int s = 1; s < S; ++s) {
+    const float4 c = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sp) + s * part_stride);
+    a.x += c.x;
+    a.y += c.y;
+    a.z += c.z;
+    a.w += c.w;
+  }
+  reinterpret_cast<float4*>(dst + (int64_t)b * dst_stride)[i] = a;
 }
 
 // dsinks[h] = -sum over (b, i) of exp(sink_h - lse[b,h,i]) * delta[b,h,i] (rows
@@ -876,7 +897,7 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
   const AttnParams& a = p.a;
   const bool cap = a.softcap_on != 0, bits = a.mask_bits != nullptr;
   const int64_t q_items = (int64_t)a.B * a.H * a.nQb;
-  const int64_t kv_items = (int64_t)a.B * a.Hkv * a.nKb;
+  const int64_t kv_items = (int64_t)a.B * a.Hkv * a.nKb * p.head_split;
   hipError_t e;
   if (q_items > 0) {
     const int t = kThreads;
@@ -918,6 +939,15 @@ hipError_t launch_bwd_prep(int dtype, int B, int Sq, int H, int Dd, const void* 
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+hipError_t launch_sum_parts(const float* src, int S, int64_t part_stride, int B, int64_t n, float* dst,
+                            int64_t dst_stride, hipStream_t s) {
+  const int64_t n4 = n / 4;   // n is a multiple of 4 (rows of D floats)
+  if (n4 == 0 || B == 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((n4 + 255) / 256), (unsigned)B), dim3(256), 0, s, src, S,
+                     part_stride, n4, dst, dst_stride);
+  return hipGetLastError();
 }
 
 hipError_t launch_col_lists(const MaskParams& p, int n_chunks, int32_t* col_cnt, int32_t* row_idx, hipStream_t s) {

@@ -273,8 +273,20 @@ RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits)
   return L;
 }
 
+// How many workgroups share the heads of a KV group in the ring's dk / dv launches: enough that a
+// chunk's launch has 512 of them (two per CU), within the group size. Only the bf16 kernels split.
+int bwd_head_split(const ram_attn_desc* d) {
+  if (d->dtype != RAM_BF16) return 1;
+  const int G = d->H / d->Hkv;
+  const int64_t items = (int64_t)d->B * d->Hkv * cdiv(d->Skv, ram::kBlockKV);
+  int S = 1;
+  while (items * S < 512 && G % (2 * S) == 0) S *= 2;
+  return S;
+}
+
 struct BwdLayout {
-  size_t dq_off, dk_off, dv_off, delta_off, cls_off, cnt_off, col_off, bits_off, ccnt_off, ridx_off, total;
+  size_t dq_off, dk_off, dv_off, delta_off, cls_off, cnt_off, col_off, bits_off, ccnt_off, ridx_off, kpart_off,
+      vpart_off, total;
 };
 BwdLayout bwd_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits) {
   BwdLayout L{};
@@ -296,6 +308,11 @@ BwdLayout bwd_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits) {
   take(L.bits_off, with_bits ? (size_t)tiles * kTileWords * sizeof(uint32_t) : 0);
   take(L.ccnt_off, (size_t)n_chunks * d->B * nKb * sizeof(int32_t));
   take(L.ridx_off, (size_t)tiles * sizeof(int32_t));
+  // one chunk's partial dk / dv per head split (reused by every chunk)
+  const int S = bwd_head_split(d);
+  const size_t part = S > 1 ? (size_t)S * d->B * d->Skv * d->Hkv * d->D * sizeof(float) : 0;
+  take(L.kpart_off, part);
+  take(L.vpart_off, part);
   L.total = off;
   return L;
 }
@@ -565,6 +582,7 @@ ram_status attn_bwd_chunk(const ram_attn_desc* desc, const void* q, const void* 
   bp.col_cnt = mask->col_cnt;
   bp.row_idx = mask->row_idx;
   bp.dq_mode = dq_mode;
+  bp.head_split = 1;
   hipError_t e = desc->dtype == RAM_F32 ? ram::launch_attn_bwd_f32(bp, stream) : ram::launch_attn_bwd(bp, stream);
   if (e != hipSuccess) return hip_fail(e, "attn_bwd_chunk launch");
   return ok();
@@ -631,6 +649,9 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   float* dk_acc = reinterpret_cast<float*>(ws + L.dk_off);
   float* dv_acc = reinterpret_cast<float*>(ws + L.dv_off);
   float* delta = reinterpret_cast<float*>(ws + L.delta_off);
+  const int head_split = bwd_head_split(desc);
+  float* k_part = reinterpret_cast<float*>(ws + L.kpart_off);
+  float* v_part = reinterpret_cast<float*>(ws + L.vpart_off);
   ram_block_mask bm{reinterpret_cast<uint8_t*>(ws + L.cls_off), reinterpret_cast<int32_t*>(ws + L.cnt_off),
                     reinterpret_cast<int32_t*>(ws + L.col_off),
                     with_bits ? reinterpret_cast<uint32_t*>(ws + L.bits_off) : nullptr,
@@ -685,8 +706,24 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
     bp.col_cnt = bc.col_cnt;
     bp.row_idx = bc.row_idx;
     bp.dq_mode = t == 0 ? RAM_OUT_WRITE : RAM_OUT_MERGE;
+    bp.head_split = head_split;
+    if (head_split > 1) {
+      // partial sums per head split, [S][B][Skv][Hkv][D], added into the chunk's accumulators below
+      bp.dk = k_part;
+      bp.dv = v_part;
+      bp.dkv_stride_b = (int64_t)desc->Skv * desc->Hkv * desc->D;
+      bp.part_stride = (int64_t)desc->B * bp.dkv_stride_b;
+    }
     e = desc->dtype == RAM_F32 ? ram::launch_attn_bwd_f32(bp, stream) : ram::launch_attn_bwd(bp, stream);
     if (e != hipSuccess) return hip_fail(e, "ring backward chunk launch");
+    if (head_split > 1) {
+      const int64_t n = (int64_t)desc->Skv * desc->Hkv * desc->D;
+      e = ram::launch_sum_parts(k_part, head_split, bp.part_stride, desc->B, n, dk_acc + kv_off, kv_acc_stride, stream);
+      if (e == hipSuccess)
+        e = ram::launch_sum_parts(v_part, head_split, bp.part_stride, desc->B, n, dv_acc + kv_off, kv_acc_stride,
+                                  stream);
+      if (e != hipSuccess) return hip_fail(e, "ring backward partial sums launch");
+    }
   }
   if (desc->dtype == RAM_F32) {
     // float32 results: the accumulators are the answer, copied into the caller's layout

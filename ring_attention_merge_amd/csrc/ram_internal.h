@@ -86,6 +86,11 @@ struct BwdParams {
   const int32_t* col_cnt;  // [B, nKb]: non-EMPTY q tiles per kv tile
   const int32_t* row_idx;  // [B, nKb, nQb]: those q tiles, ascending
   int32_t dq_mode;
+  // dk / dv over the heads of a KV group split into head_split workgroups (a divisor of the
+  // group size; 1 = one workgroup per kv tile): split s writes its partial sums at
+  // dk / dv + s * part_stride, to be added up by launch_sum_parts.
+  int32_t head_split;
+  int64_t part_stride;     // elements
 };
 
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s);
@@ -109,5 +114,9 @@ hipError_t launch_block_mask(const MaskParams& p, int n_chunks, hipStream_t s);
 hipError_t launch_merge(int B, int Sq, int H, int D, float* out_acc, float* lse_acc,
                         const float* out_blk, const float* lse_blk, hipStream_t s);
 hipError_t launch_cast_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
+// dst[b * dst_stride + i] = sum over s < S of src[s * part_stride + b * n + i], i < n, b < B
+// (a fixed order: deterministic).
+hipError_t launch_sum_parts(const float* src, int S, int64_t part_stride, int B, int64_t n, float* dst,
+                            int64_t dst_stride, hipStream_t s);
 
 }  // namespace ram

@@ -260,15 +260,23 @@ def test_backward_validation(lib):
     need = lib.ring_attn_bwd_workspace_bytes(ctypes.byref(dr), 4, None)
     al = lambda x: (x + 255) // 256 * 256
     tiles = 4 * 4 * 8
+    # the dk / dv launch of a chunk has 2 kv heads x 8 kv tiles = 16 workgroups: the 2 heads of
+    # each group go to 2 workgroups, whose partial dk and dv for one chunk take 2 x 2 x 512 x 2 x 128 floats
+    parts = 2 * al(2 * 512 * 2 * 128 * 4)
     expect = (al(512 * 4 * 128 * 4) + 2 * al(4 * 512 * 2 * 128 * 4) + al(2 * 4 * 512 * 4) + al(tiles)
-              + al(4 * 4 * 4) + al(tiles * 4) + al(4 * 8 * 4) + al(tiles * 4))
+              + al(4 * 4 * 4) + al(tiles * 4) + al(4 * 8 * 4) + al(tiles * 4) + parts)
     assert need == expect
+    # float32 runs one workgroup per kv tile: no partial sums
+    f32 = lib.ring_attn_bwd_workspace_bytes(ctypes.byref(_desc(B=1, Sq=512, Skv=512, H=4, Hkv=2, dtype=ram.RAM_F32)), 4,
+                                            None)
+    assert f32 == expect - parts
     dense = lib.ring_attn_bwd_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src(dense=FAKE2)))
     assert dense == need + tiles * 1024
     assert lib.ring_attn_bwd_workspace_bytes(ctypes.byref(_desc(D=96)), 4, None) == 0
     d64 = _desc(B=1, Sq=512, Skv=512, H=4, Hkv=2, D=64)
-    assert lib.ring_attn_bwd_workspace_bytes(ctypes.byref(d64), 4, None) == expect - (
-        al(512 * 4 * 128 * 4) + 2 * al(4 * 512 * 2 * 128 * 4)) + al(512 * 4 * 64 * 4) + 2 * al(4 * 512 * 2 * 64 * 4)
+    assert lib.ring_attn_bwd_workspace_bytes(ctypes.byref(d64), 4, None) == expect - parts - (
+        al(512 * 4 * 128 * 4) + 2 * al(4 * 512 * 2 * 128 * 4)) + al(512 * 4 * 64 * 4) + 2 * al(4 * 512 * 2 * 64 * 4) + (
+        2 * al(2 * 512 * 2 * 64 * 4))
     ring = lambda ws_bytes, **kw: lib.ring_attn_bwd_1gpu(
         ctypes.byref(kw.get("d", dr)), 4, kw.get("r", 3), FAKE, FAKE, FAKE, FAKE, FAKE2, FAKE,
         ctypes.byref(_src()), kw.get("sinks", 0), FAKE, FAKE, FAKE, kw.get("dsinks", 0), FAKE, ws_bytes, 0)

@@ -232,6 +232,9 @@ RING = {
     "docs": lambda: wl.c3_packed_docs(S=1024, B=2, H=2, len_lo=32, len_hi=256, seed=33),
     "gqa_cap_sinks": lambda: wl.c4_gqa_cap_sinks(S=1024, H=8, Hkv=2, seed=34),
     "mqa_cap_sinks": lambda: wl.c4_gqa_cap_sinks(S=768, H=4, Hkv=1, seed=35),
+    # 16 heads on one kv head, 4 kv tiles per chunk: the dk / dv launch splits the group's heads
+    # over 16 workgroups and adds their partial sums
+    "mqa16_ragged": lambda: wl.make("mq16", B=1, H=16, Hkv=1, Sq=250, chunk=250, n_chunks=2, D=128, seed=42),
     "noncausal_sinks": lambda: wl.make("nc", B=1, H=2, Hkv=2, Sq=100, chunk=70, n_chunks=3, D=128, causal=False,
                                        seed=36, with_sinks=True),
     "d64_shard2of4_gqa_cap_sinks": lambda: wl.make("r64", B=2, H=4, Hkv=2, Sq=320, chunk=320, n_chunks=4, D=64,
