@@ -89,10 +89,33 @@ __device__ __forceinline__ void block_minmax(int vmin, int vmax, int* red, int& 
   __syncthreads();
 }
 
+// Bit jj of the result: keys[j0 + jj] <= v (EQ false) or == v (EQ true), jj < n. A full,
+// 16-byte aligned word reads its 32 values with eight 16-byte LDS reads issued together.
+template <bool EQ>
+__device__ __forceinline__ uint32_t key_bits(const int* keys, int j0, int n, int v) {
+  uint32_t m = 0;
+  if (n == 32 && (j0 & 3) == 0) {
+    const int4* k4 = reinterpret_cast<const int4*>(keys + j0);
+    int4 a[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = k4[q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e[4] = {a[q].x, a[q].y, a[q].z, a[q].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m |= (uint32_t)(EQ ? e[r] == v : e[r] <= v) << (4 * q + r);
+    }
+    return m;
+  }
+  for (int jj = 0; jj < n; ++jj) m |= (uint32_t)(EQ ? keys[j0 + jj] == v : keys[j0 + jj] <= v) << jj;
+  return m;
+}
+
 __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
   __shared__ uint8_t cls_s[kMaxMaskCols];
   __shared__ int qpos_s[kMaxMaskTile], qseg_s[kMaxMaskTile];
-  __shared__ int kpos_s[kGroupKeys], kseg_s[kGroupKeys];
+  __shared__ __attribute__((aligned(16))) int kpos_s[kGroupKeys];
+  __shared__ __attribute__((aligned(16))) int kseg_s[kGroupKeys];
   __shared__ int red[2 * kWaves];
   __shared__ int wsum[kWaves];
   __shared__ uint32_t bits_s[kGroupWords];
@@ -157,10 +180,32 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
     // of tiles per round. Each thread builds 32-pair words of the tiles' bit
     // rows; per-tile flags (bit 0: a pair allowed, bit 1: a pair excluded)
     // give the classes.
+    // ranges over the rows that can have an allowed key (padding rows have none)
+    int qpl = 0x7fffffff, qph = -0x7fffffff - 1, qsl = 0x7fffffff, qsh = -0x7fffffff - 1;
+    bool qpad = false;
     for (int i = tid; i < nq; i += kThreads) {
       qpos_s[i] = qpos ? qpos[i] : p.q_pos_base + q0 + i;
       qseg_s[i] = qseg ? qseg[i] : 0;
+      if (qseg_s[i] == -1 && qseg) {
+        qpad = true;
+        continue;
+      }
+      qpl = min(qpl, qpos_s[i]);
+      qph = max(qph, qpos_s[i]);
+      qsl = min(qsl, qseg_s[i]);
+      qsh = max(qsh, qseg_s[i]);
     }
+    // Tiles whose class follows from the rows' and keys' position and segment ranges are
+    // decided before their pairs are checked (exactly: these are sufficient conditions); the
+    // rest (class 3 until then) go through the pairwise words. Ranges leave out padding rows
+    // and keys (segment -1), which have no allowed pair. EMPTY: every key after every row
+    // (causal), disjoint segment ranges, or all rows or all keys padding. FULL (without a
+    // dense mask, which can clear any pair): every key at or before every row, no padding,
+    // and one segment on both sides.
+    int qpmin, qpmax, qsmin, qsmax;
+    block_minmax(qpl, qph, red, qpmin, qpmax);
+    block_minmax(qsl, qsh, red, qsmin, qsmax);
+    const bool any_qpad = __syncthreads_or(qpad);
     const int W = (p.bk + 31) >> 5;   // words per tile row
     const int tw = p.bq * W;          // words per tile
     const int tg = max(1, min(kGroupKeys / p.bk, kGroupWords / tw));
@@ -175,6 +220,44 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
       }
       for (int t = tid; t < ng; t += kThreads) flag_s[t] = 0;
       __syncthreads();
+      // the group's tiles by their ranges, 16 threads per tile
+      bool open = false;
+      for (int t0 = 0; t0 < ng; t0 += kThreads / 16) {
+        const int t = t0 + (tid >> 4), l = tid & 15;
+        const int nk = t < ng ? min(p.bk, gk - t * p.bk) : 0;
+        int kpl = 0x7fffffff, kph = -0x7fffffff - 1, ksl = 0x7fffffff, ksh = -0x7fffffff - 1, kpad = 0;
+        for (int j = l; j < nk; j += 16) {
+          const int sg = kseg_s[t * p.bk + j];
+          if (sg == -1 && qseg) {
+            kpad = 1;
+            continue;
+          }
+          kpl = min(kpl, kpos_s[t * p.bk + j]);
+          kph = max(kph, kpos_s[t * p.bk + j]);
+          ksl = min(ksl, sg);
+          ksh = max(ksh, sg);
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+          kpl = min(kpl, __shfl_xor(kpl, o, 16));
+          kph = max(kph, __shfl_xor(kph, o, 16));
+          ksl = min(ksl, __shfl_xor(ksl, o, 16));
+          ksh = max(ksh, __shfl_xor(ksh, o, 16));
+          kpad |= __shfl_xor(kpad, o, 16);
+        }
+        if (t < ng) {
+          const bool segs = qseg != nullptr;
+          // (with no non-padding rows or keys the ranges are empty: min > max)
+          const bool empty = nk <= 0 || qpmin > qpmax || kpl > kph || (p.causal && kpl > qpmax) ||
+                             (segs && (ksh < qsmin || ksl > qsmax));
+          const bool full = p.dense == nullptr && !any_qpad && !kpad && (!p.causal || kph <= qpmin) &&
+                            (!segs || (qsmin == qsmax && ksl == ksh && qsmin == ksl));
+          const uint8_t cl = empty ? 0 : (full ? 2 : 3);
+          if (l == 0) cls_s[kbg + t] = cl;
+          open = open || cl == 3;
+        }
+      }
+      if (!__syncthreads_or(open)) continue;   // every tile of the group decided
       const int nw = ng * tw;
       const int gw = ng * W;   // words per tile row across the round
       // Words are taken row by row (consecutive threads: consecutive 32-key words
@@ -199,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
           j0v[k] = j0;
           jnv[k] = jn;
           uint32_t w = 0, valid = 0;
-          if (u < nw && i < nq && jn > 0) {
+          if (u < nw && i < nq && jn > 0 && cls_s[kbg + tl] == 3) {
             valid = jn == 32 ? ~0u : ((1u << jn) - 1u);
             w = valid;
             if (p.causal) {
@@ -208,17 +291,12 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
                 const int64_t lim = (int64_t)qpos_s[i] - ((int64_t)kv_base + g0 + j0);
                 w &= lim < 0 ? 0u : (lim >= 31 ? ~0u : ((2u << lim) - 1u));
               } else {
-                uint32_t cm = 0;
-                for (int jj = 0; jj < jn; ++jj) cm |= (uint32_t)(kpos_s[j0 + jj] <= qpos_s[i]) << jj;
-                w &= cm;
+                w &= key_bits<false>(kpos_s, j0, jn, qpos_s[i]);
               }
             }
             if (qseg && w) {
               const int qs = qseg_s[i];
-              uint32_t sm = 0;
-              if (qs != -1)
-                for (int jj = 0; jj < jn; ++jj) sm |= (uint32_t)(kseg_s[j0 + jj] == qs) << jj;
-              w &= sm;
+              w &= qs != -1 ? key_bits<true>(kseg_s, j0, jn, qs) : 0u;
             }
           }
           wv[k] = w;
@@ -255,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
       __syncthreads();
       for (int t = tid; t < ng; t += kThreads) {
         const int f = flag_s[t];
-        cls_s[kbg + t] = (f & 1) ? ((f & 2) ? 1 : 2) : 0;
+        if (cls_s[kbg + t] == 3) cls_s[kbg + t] = (f & 1) ? ((f & 2) ? 1 : 2) : 0;
       }
       if (p.bits) {
         uint32_t* dst = p.bits + ((size_t)crow * p.nKb + kbg) * tw;
