@@ -38,9 +38,11 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T* as_const_s
 
 // Work decode: item order is (batch*Hkv + kv head, q tile descending, head in group);
 // XCD x = id % 8 takes the contiguous item range [x*per, (x+1)*per).
-__device__ __forceinline__ bool decode_work(const AttnParams& p, int& b, int& h, int& qb) {
+// With S > 1 each (batch, head, q tile) is S items, *s_out the index among them.
+__device__ __forceinline__ bool decode_work(const AttnParams& p, int& b, int& h, int& qb, int S = 1,
+                                            int* s_out = nullptr) {
   const int G = p.H / p.Hkv;
-  const int64_t T = (int64_t)p.B * p.Hkv * p.nQb * G;
+  const int64_t T = (int64_t)p.B * p.Hkv * p.nQb * G * S;
   const int64_t id = blockIdx.x;
   // Workgroups go to the 8 XCDs round robin (block id mod 8). With whole (batch, kv head)
   // groups per XCD, a group's K / V stay in one XCD's L2. With fewer groups than that (MQA,
@@ -49,6 +51,8 @@ __device__ __forceinline__ bool decode_work(const AttnParams& p, int& b, int& h,
   int64_t item = id;
   if (((int64_t)p.B * p.Hkv) % 8 == 0) item = (id & 7) * (T / 8) + (id >> 3);
   if (item >= T) return false;
+  if (s_out) *s_out = (int)(item % S);
+  item /= S;
   const int hg = (int)(item % G);
   const int64_t r = item / G;
   const int qrev = (int)(r % p.nQb);

@@ -467,16 +467,18 @@ __device__ __forceinline__ void ring_chunk_view(AttnParams& pc, const AttnParams
   pc.out_final = t == n - 1 ? p.out_final : nullptr;
 }
 
-template <bool CAP, bool BITS>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_dma_ring(AttnParams p) {
+template <bool CAP, bool BITS, bool SPLIT>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_dma_ring(AttnParams p, RingSplit rs) {
   constexpr int D = 128;
   constexpr int BK = kBlockKV;
   constexpr int NDS = D / 16;
   constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * kDmaTile];   // [stage][K, V]
 
-  int b, h, qb;
-  if (!decode_work(p, b, h, qb)) return;
+  // SPLIT: two workgroups per row (an instantiation of its own, so that the other keeps its
+  // registers)
+  int b, h, qb, sp = 0;
+  if (!decode_work(p, b, h, qb, SPLIT ? 2 : 1, SPLIT ? &sp : nullptr)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -537,9 +539,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_dma_ring(AttnParams
     __syncthreads();
   }
 
-  for (int t = 0; t < p.n_chunks; ++t) {
+  // this workgroup's visits (all of them, or one of the two halves of a split ring)
+  const int t_half = (p.n_chunks + 1) / 2;
+  const int t_begin = (SPLIT && sp == 1) ? t_half : 0;
+  const int t_end = (SPLIT && sp == 0) ? t_half : p.n_chunks;
+  for (int t = t_begin; t < t_end; ++t) {
     AttnParams pc = p;   // this visit's chunk
     ring_chunk_view(pc, p, t);
+    if (SPLIT && sp == 1) {
+      // the second half runs its own ring into out2 / lse2, starting as a first visit does
+      pc.out = rs.out2;
+      pc.lse = rs.lse2;
+      if (t == t_begin) pc.mode = p.mode;
+    }
     const int cnt = pc.row_cnt[mrow];
     // a merge with nothing to add is the identity (unless the result must be
     // converted to its final type, which the epilogue does for empty rows)
@@ -890,7 +902,11 @@ struct Bf16Dma {
 };
 template <bool CAP, bool BITS>
 struct Bf16DmaRing {
-  static constexpr auto fn = attn_fwd_bf16_dma_ring<CAP, BITS>;
+  static constexpr auto fn = attn_fwd_bf16_dma_ring<CAP, BITS, false>;
+};
+template <bool CAP, bool BITS>
+struct Bf16DmaRingSplit {
+  static constexpr auto fn = attn_fwd_bf16_dma_ring<CAP, BITS, true>;
 };
 
 bool attn_ring_fused(const AttnParams& p, int dtype) {
@@ -899,9 +915,19 @@ bool attn_ring_fused(const AttnParams& p, int dtype) {
   return !(e && strcmp(e, "per_chunk") == 0);
 }
 
-hipError_t launch_attn_ring(const AttnParams& p, hipStream_t s) {
+template <template <bool, bool> class K>
+hipError_t launch_ring_cb(const AttnParams& p, const RingSplit& rs, int S, hipStream_t s) {
+  const bool cap = p.softcap_on != 0, bits = p.mask_bits != nullptr;
+  const auto fn = cap ? (bits ? K<true, true>::fn : K<true, false>::fn) : (bits ? K<false, true>::fn : K<false, false>::fn);
+  const int64_t T = (int64_t)p.B * p.H * p.nQb * S;
+  hipLaunchKernelGGL(fn, dim3((unsigned)(8 * ((T + 7) / 8))), dim3(kThreads), 0, s, p, rs);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_ring(const AttnParams& p, const RingSplit* split, hipStream_t s) {
   if (p.n_chunks < 1) return hipErrorInvalidValue;
-  return launch_cb<Bf16DmaRing>(p, s);
+  if (split) return launch_ring_cb<Bf16DmaRingSplit>(p, *split, 2, s);
+  return launch_ring_cb<Bf16DmaRing>(p, RingSplit{nullptr, nullptr}, 1, s);
 }
 
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s) {

@@ -245,8 +245,18 @@ ram::AttnParams attn_params(const ram_attn_desc* d, const void* q, const void* k
 }
 
 struct RingLayout {
-  size_t acc_off, cls_off, cnt_off, col_off, bits_off, total;
+  size_t acc_off, cls_off, cnt_off, col_off, bits_off, acc2_off, lse2_off, total;
 };
+
+// Whether the one-launch ring splits each q tile row's visits over two workgroups: when its
+// rows give fewer than two workgroups per CU (the kernel is built for two waves per SIMD),
+// two halves of the ring run side by side and are merged afterwards. The workspace always
+// has room for the second half's result when the shape could split; `RAM_RING_SPLIT=0` keeps
+// one workgroup per row (then the ring is bit-identical to chunk-by-chunk launches).
+bool ring_split_shape(const ram_attn_desc* d, int32_t n_chunks) {
+  return d->dtype == RAM_BF16 && d->D == 128 && n_chunks >= 2 &&
+         (int64_t)d->B * d->H * cdiv(d->Sq, ram::kBlockQ) < 512;
+}
 
 // Words of tile bits per kernel tile (block_q rows of block_kv / 32 words).
 constexpr int64_t kTileWords = (int64_t)ram::kBlockQ * (ram::kBlockKV / 32);
@@ -269,6 +279,11 @@ RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits)
   off += align256((size_t)tiles * sizeof(int32_t));
   L.bits_off = off;
   if (with_bits) off += align256((size_t)tiles * kTileWords * sizeof(uint32_t));
+  const bool split = ring_split_shape(d, n_chunks);
+  L.acc2_off = off;
+  if (split) off += align256((size_t)d->B * d->Sq * d->H * d->D * sizeof(float));
+  L.lse2_off = off;
+  if (split) off += align256((size_t)d->B * d->H * d->Sq * sizeof(float));
   L.total = off;
   return L;
 }
@@ -478,11 +493,22 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
       p.kv_chunk_elems = (int64_t)desc->Skv * desc->Hkv * desc->D;
       p.mask_chunk_tiles = (int64_t)desc->B * nQb * nKb;
       p.mask_chunk_rows = (int64_t)desc->B * nQb;
-      p.out_final = out;   // bf16: the last visit writes the result
+      const char* no_split = getenv("RAM_RING_SPLIT");
+      const bool split = ring_split_shape(desc, n_chunks) && !(no_split && strcmp(no_split, "0") == 0);
+      float* acc2 = reinterpret_cast<float*>(ws + L.acc2_off);
+      float* lse2 = reinterpret_cast<float*>(ws + L.lse2_off);
+      const ram::RingSplit halves{acc2, lse2};
+      if (!split) p.out_final = out;   // bf16: the last visit writes the result
       if (g_ev_start && (e = hipEventRecord(g_ev_start, stream)) != hipSuccess) return hip_fail(e, "event record");
-      e = ram::launch_attn_ring(p, stream);
+      e = ram::launch_attn_ring(p, split ? &halves : nullptr, stream);
       if (e != hipSuccess) return hip_fail(e, "ring launch");
       if (g_ev_stop && (e = hipEventRecord(g_ev_stop, stream)) != hipSuccess) return hip_fail(e, "event record");
+      if (split) {
+        // the second half's running result merged into the first's, then the bf16 result
+        e = ram::launch_merge(desc->B, desc->Sq, desc->H, desc->D, acc, lse, acc2, lse2, stream);
+        if (e == hipSuccess) e = ram::launch_cast_bf16(acc, out, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
+        if (e != hipSuccess) return hip_fail(e, "split ring merge launch");
+      }
       return ok();
     }
   }

@@ -55,6 +55,15 @@ struct AttnParams {
   int64_t mask_chunk_rows;
 };
 
+// A split ring (launch_attn_ring with this given): each q tile row's visits go to two
+// workgroups, visits [0, h) and [h, n_chunks) with h = (n_chunks + 1) / 2; the second writes
+// its own running result to out2 / lse2 (its first visit in `mode`), to be merged into
+// out / lse afterwards.
+struct RingSplit {
+  float* out2;
+  float* lse2;
+};
+
 struct MaskParams {
   const int32_t* q_pos;
   const int32_t* kv_pos;
@@ -96,7 +105,7 @@ struct BwdParams {
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s);
 // Whether a ring of this kernel choice runs as one launch (launch_attn_ring).
 bool attn_ring_fused(const AttnParams& p, int dtype);
-hipError_t launch_attn_ring(const AttnParams& p, hipStream_t s);
+hipError_t launch_attn_ring(const AttnParams& p, const RingSplit* split, hipStream_t s);
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s);       // bf16, D = 64 / 128: dq, then dk / dv
 hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s);   // float32, D = 64 / 128
 // delta (and dsinks) from out and dout in `dtype` (RAM_BF16 / RAM_F32 codes)

@@ -202,10 +202,18 @@ def test_ring_validation_and_workspace(lib):
     need = lib.ring_attn_workspace_bytes(ctypes.byref(d), 4, None)
     acc = 4096 * 8 * 128 * 4
     tiles = 4 * 32 * 64
-    expect = acc + ((tiles + 255) // 256) * 256 + ((4 * 32 * 4 + 255) // 256) * 256 + tiles * 4
+    # 32 q tiles x 8 heads = 256 workgroups, under two per CU: room for the second half of a
+    # split ring (its float32 result and lse)
+    split = acc + 8 * 4096 * 4
+    expect = acc + ((tiles + 255) // 256) * 256 + ((4 * 32 * 4 + 255) // 256) * 256 + tiles * 4 + split
     assert need == expect
     d32 = _desc(B=1, Sq=4096, Skv=4096, H=8, Hkv=8, dtype=ram.RAM_F32)
-    assert lib.ring_attn_workspace_bytes(ctypes.byref(d32), 4, None) == need - acc   # fp32 accumulates in out
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(d32), 4, None) == need - acc - split   # fp32: in out, no split
+    # 64 q tiles x 8 heads = 512 workgroups: no split
+    d2 = _desc(B=2, Sq=4096, Skv=4096, H=8, Hkv=8)
+    tiles2 = 4 * 64 * 64
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(d2), 4, None) == (
+        2 * acc + ((tiles2 + 255) // 256) * 256 + ((4 * 64 * 4 + 255) // 256) * 256 + tiles2 * 4)
     assert lib.ring_attn_workspace_bytes(ctypes.byref(d), 0, None) == 0
     assert _ring(lib, d, 0, -1) == _lib.RAM_ERR_INVALID
     assert _ring(lib, d, 4, 4) == _lib.RAM_ERR_INVALID and "q_shard" in _err(lib)

@@ -187,12 +187,16 @@ def test_ring_dense(name, monkeypatch):
     ws = torch.empty(ram.ring_attn_workspace_bytes(d, n, src), dtype=torch.uint8, device=DEV)
     sinks = None if w.sinks is None else w.sinks.to(DEV)
     ram.ring_attn_fwd_1gpu(d, n, r, w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), src, sinks, out, lse, ws)
-    # the same ring as chunk-by-chunk launches: bit-identical
+    # with one workgroup per row (no split of the visits), the one-launch ring and the same ring
+    # as chunk-by-chunk launches are bit-identical
+    monkeypatch.setenv("RAM_RING_SPLIT", "0")
+    out3, lse3 = torch.empty_like(out), torch.empty_like(lse)
+    ram.ring_attn_fwd_1gpu(d, n, r, w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), src, sinks, out3, lse3, ws)
     monkeypatch.setenv("RAM_RING", "per_chunk")
     out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
     ram.ring_attn_fwd_1gpu(d, n, r, w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), src, sinks, out2, lse2, ws)
     torch.cuda.synchronize()
-    assert torch.equal(out, out2) and torch.equal(lse, lse2), "one-launch ring differs from chunk launches"
+    assert torch.equal(out3, out2) and torch.equal(lse3, lse2), "one-launch ring differs from chunk launches"
     q, k, v, s64 = w.as_f64()
     qp, kp = w.positions()
     order = [(r - t) % n for t in range(n)] if r >= 0 else list(range(n))

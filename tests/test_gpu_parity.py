@@ -252,13 +252,33 @@ def test_ring_small(name, variant):
 @pytest.mark.parametrize("name", ["ring_shard3of4", "ring_shard1of3_ragged", "docs_small", "gqa_cap_sinks_small"])
 def test_ring_one_launch_equals_chunk_launches(name, monkeypatch):
     """The one-launch ring runs every chunk visit as a chunk launch does (same tiles, same merge):
-    its results are bit-identical to the chunk-by-chunk ring."""
+    with one workgroup per row (RAM_RING_SPLIT=0) its results are bit-identical to the
+    chunk-by-chunk ring."""
     w = SMALL_RING[name]()
     say(f"ring one launch vs chunk launches {name}")
+    monkeypatch.setenv("RAM_RING_SPLIT", "0")
     o1, l1 = run_ring(w)
     monkeypatch.setenv("RAM_RING", "per_chunk")
     o2, l2 = run_ring(w)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", ["ring_shard3of4", "gqa_cap_sinks_small"])
+def test_ring_split_matches_unsplit(name, monkeypatch):
+    """These small rings have fewer than two workgroups per CU, so the one-launch ring splits
+    each row's visits over two workgroups and merges the halves by their lse: the same result
+    up to the rounding of the merge order (the oracle tests check both against the float64
+    reference). Both halves of these rings have keys to add, so the results differ in rounding."""
+    w = SMALL_RING[name]()
+    say(f"split ring vs one workgroup per row {name}")
+    o1, l1 = run_ring(w)
+    monkeypatch.setenv("RAM_RING_SPLIT", "0")
+    o2, l2 = run_ring(w)
+    assert not (torch.equal(o1, o2) and torch.equal(l1, l2)), "the split did not engage"
+    torch.testing.assert_close(o1.float(), o2.float(), rtol=0, atol=2e-2)
+    fin = torch.isfinite(l2)
+    assert torch.equal(fin, torch.isfinite(l1))
+    torch.testing.assert_close(l1[fin], l2[fin], rtol=0, atol=1e-4)
 
 
 # ------------------------------------------------------------------------------ full sizes
