@@ -179,8 +179,12 @@ ram_status lse_merge(int32_t B, int32_t Sq, int32_t H, int32_t D, float* out_acc
  *   Sinks enter on the first visited chunk only.
  *   A dense mask (src->dense) is read per chunk as ram_mask_src describes.
  * workspace: device memory of at least ring_attn_workspace_bytes(), 256-byte
- * aligned; it holds the float32 output accumulator (bf16 only) and the block
- * masks of every chunk (with their tile bits when src->dense is set). */
+ * aligned; it holds the float32 output accumulator (bf16 only), the block
+ * masks of every chunk (with their tile bits when src->dense is set) and, for
+ * bf16 rings too small to give two workgroups per CU, the running result of
+ * the second half of the visits, which then run beside the first half and are
+ * merged into it by lse (the environment variable RAM_RING_SPLIT=0 turns this
+ * off). */
 ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32_t q_shard,
                               const void* q, const void* k_all, const void* v_all,
                               const ram_mask_src* src, const float* sinks, void* out, float* lse,
