@@ -76,7 +76,8 @@ typedef struct {
   float scale;                   /* score scale (Kvax default is 1.0) */
   float softcap;                 /* <= 0: off */
   int32_t causal;                /* 0 or 1 */
-  int32_t block_q, block_kv;     /* tile of the block mask; attention needs ram_kernel_tile() */
+  int32_t block_q, block_kv;     /* tile of the block mask; attention needs ram_kernel_tile() (forward)
+                                    or ram_bwd_kernel_tile() (backward) */
 } ram_attn_desc;
 
 /* Positions, segment IDs and an optional dense mask for one (q, KV-chunk)
@@ -143,8 +144,11 @@ ram_status build_block_mask(const ram_attn_desc* desc, const ram_mask_src* src,
 /* One chunk of block-sparse attention forward (ring-splash
  * _ring_attention_forward, the per-step kernel call), visiting only the
  * non-EMPTY tiles of `mask` (built by build_block_mask at ram_kernel_tile()).
- * With mask->bits set, PARTIAL tiles are masked by their bits (required
- * when src->dense is set); otherwise by positions and segment IDs.
+ * PARTIAL tiles are masked from mask->bits when they are needed: with a dense
+ * mask, and for bf16 with D = 128 also with kv positions or segment IDs (that
+ * kernel's only other mask is the positional one); mask->bits must then be
+ * set, else the call returns RAM_ERR_INVALID. Otherwise they are masked by
+ * positions and segment IDs (and bits, if given, by them).
  *   q [B,Sq,H,D], k and v [B,Skv,Hkv,D] in desc->dtype; sinks float32 [H] or NULL.
  *   mode RAM_OUT_WRITE: out <- chunk output (float32 [B,Sq,H,D]), lse <- chunk
  *        lse (float32 [B,H,Sq]), for every row (empty rows get 0 / -inf).
@@ -178,13 +182,17 @@ ram_status lse_merge(int32_t B, int32_t Sq, int32_t H, int32_t D, float* out_acc
  *     n_chunks*Skv keys and travel with their chunk.
  *   Sinks enter on the first visited chunk only.
  *   A dense mask (src->dense) is read per chunk as ram_mask_src describes.
+ * bf16 with D = 128 runs the whole ring as one launch in which each workgroup
+ * keeps its q tile and visits every chunk; when the rows of q tiles are fewer
+ * than the GPU's compute units, each row's visits are split over two
+ * workgroups (the first and second half of the ring order) whose running
+ * results are merged by lse afterwards: the same result up to the rounding of
+ * the merge order.
  * workspace: device memory of at least ring_attn_workspace_bytes(), 256-byte
  * aligned; it holds the float32 output accumulator (bf16 only), the block
- * masks of every chunk (with their tile bits when src->dense is set) and, for
- * bf16 rings too small to give two workgroups per CU, the running result of
- * the second half of the visits, which then run beside the first half and are
- * merged into it by lse (the environment variable RAM_RING_SPLIT=0 turns this
- * off). */
+ * masks of every chunk (with their tile bits when the forward call would need
+ * them, see attn_fwd_chunk) and, for a split ring, the second half's running
+ * result. */
 ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32_t q_shard,
                               const void* q, const void* k_all, const void* v_all,
                               const ram_mask_src* src, const float* sinks, void* out, float* lse,
@@ -213,7 +221,7 @@ ram_status attn_bwd_prep(const ram_attn_desc* desc, const void* out, const void*
                          const float* sinks, float* delta, float* dsinks, hipStream_t stream);
 
 /* Gradients of one chunk (the per-step call of _ring_attention_backward) with
- * mask built by build_block_mask at ram_kernel_tile() including the transposed
+ * mask built by build_block_mask at ram_bwd_kernel_tile() including the transposed
  * lists (and the bits when src->dense is set).
  *   dq: float32 [B, Sq, H, D] dense; dq_mode RAM_OUT_WRITE stores the chunk's
  *       dq, RAM_OUT_MERGE adds it to dq.
@@ -239,12 +247,17 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
 size_t ring_attn_bwd_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src);
 
 /* Workspace bytes ring_attn_fwd_1gpu needs for this shape (0 on bad input).
- * src may be NULL; a source with a dense mask needs room for tile bits. */
+ * src may be NULL; a source whose forward needs tile bits needs room for them. */
 size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src);
 
-/* The tile (block_q, block_kv) the attention kernel of (dtype, D) runs at;
- * block masks passed to attn_fwd_chunk must be built at this tile. */
+/* The tile (block_q, block_kv) the forward kernel of (dtype, D) walks: block
+ * masks passed to attn_fwd_chunk must be built at this tile (256 x 64 for bf16
+ * with D = 128, 128 x 64 otherwise). */
 ram_status ram_kernel_tile(int32_t dtype, int32_t D, int32_t* block_q, int32_t* block_kv);
+
+/* The tile the backward kernels walk (128 x 64): block masks passed to
+ * attn_bwd_chunk must be built at this tile. */
+ram_status ram_bwd_kernel_tile(int32_t dtype, int32_t D, int32_t* block_q, int32_t* block_kv);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ram_last_error(void);

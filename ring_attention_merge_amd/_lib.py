@@ -26,7 +26,7 @@ RAM_OUT_WRITE, RAM_OUT_MERGE = 0, 1
 RAM_PAD_SEGMENT_ID = -1
 
 EXPORTS = ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
-           "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_last_error", "attn_bwd_prep",
+           "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_bwd_kernel_tile", "ram_last_error", "attn_bwd_prep",
            "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes", "ram_mfma_probe",
            "ram_set_kernel_events")
 
@@ -84,6 +84,7 @@ def load(path: str = LIB_PATH):
     lib.ring_attn_workspace_bytes.argtypes = [P(c_desc), i32, P(c_mask_src)]
     lib.ring_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.ram_kernel_tile.argtypes = [i32, i32, P(i32), P(i32)]
+    lib.ram_bwd_kernel_tile.argtypes = [i32, i32, P(i32), P(i32)]
     lib.attn_bwd_prep.argtypes = [P(c_desc), vp, vp, f32p, f32p, f32p, f32p, vp]
     lib.attn_bwd_chunk.argtypes = [P(c_desc), vp, vp, vp, vp, f32p, f32p, P(c_mask_src), P(c_block_mask), i32,
                                    f32p, f32p, f32p, vp]
@@ -96,6 +97,7 @@ def load(path: str = LIB_PATH):
     lib.ram_mfma_probe.argtypes = [i32, i32, i32, f32p, vp]
     lib.ram_set_kernel_events.argtypes = [vp, vp]
     for name in ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu", "ram_kernel_tile",
+                 "ram_bwd_kernel_tile",
                  "attn_bwd_prep", "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ram_mfma_probe",
                  "ram_set_kernel_events"):
         getattr(lib, name).restype = ctypes.c_int
@@ -241,9 +243,16 @@ def _span(B, stride, dense):
 
 # ------------------------------------------------------------------------------ entry points
 def kernel_tile(dtype: int, D: int):
-    """ram_kernel_tile: the (block_q, block_kv) the attention kernel runs at."""
+    """ram_kernel_tile: the (block_q, block_kv) mask tile attn_fwd_chunk needs."""
     bq, bk = ctypes.c_int32(), ctypes.c_int32()
     _check(load().ram_kernel_tile(dtype, D, ctypes.byref(bq), ctypes.byref(bk)))
+    return bq.value, bk.value
+
+
+def bwd_kernel_tile(dtype: int, D: int):
+    """ram_bwd_kernel_tile: the (block_q, block_kv) mask tile attn_bwd_chunk needs."""
+    bq, bk = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().ram_bwd_kernel_tile(dtype, D, ctypes.byref(bq), ctypes.byref(bk)))
     return bq.value, bk.value
 
 
@@ -311,7 +320,9 @@ def ring_attn_workspace_bytes(desc: Desc, n_chunks: int, src: Optional[MaskSrc] 
     cd = desc.c()
     if src is None:
         return int(load().ring_attn_workspace_bytes(ctypes.byref(cd), n_chunks, None))
-    cs = c_mask_src(0, 0, 0, 0, 0, 0, 0, 0, _ptr(src.dense), src.dense_ld, src.dense_chunk_step)
+    # only which arrays are given matters for the size (they may live anywhere)
+    cs = c_mask_src(_ptr(src.q_pos), _ptr(src.kv_pos), 0, 0, _ptr(src.q_seg), _ptr(src.kv_seg), 0, 0,
+                    _ptr(src.dense), src.dense_ld, src.dense_chunk_step)
     return int(load().ring_attn_workspace_bytes(ctypes.byref(cd), n_chunks, ctypes.byref(cs)))
 
 

@@ -1,9 +1,12 @@
 """Build libram.so (HIP kernels + C ABI) for gfx950 with hipcc, in place.
 
+Each source compiles to an object of its own (in parallel, under _build/), then one link.
+
 Usage: python -m ring_attention_merge_amd.build   (or build() from Python)
 """
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
@@ -12,10 +15,13 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libram.so")
+OBJ_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+# Device sources. The feature switch below reaches the host pass of each .hip file too, where
+# it is ignored with a notice; the host-only ram_api.cpp is built without it.
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 ops (v_pk_*_f32) anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # device code never sees NaN inputs it must preserve (masked scores are
@@ -23,6 +29,8 @@ FLAGS = [
     "-Xarch_device", "-fno-honor-nans",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]
+LINK_FLAGS = ["--offload-arch=gfx950", "-shared", "-fPIC"]
 
 
 def sources():
@@ -30,15 +38,35 @@ def sources():
         [os.path.join(HERE, "csrc", "ram_api.cpp")]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into ring_attention_merge_amd/libram.so; return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+    inc = ["-I", os.path.join(ROOT, "include")]
+    if src.endswith(".cpp"):
+        cmd = ["g++", *HOST_FLAGS, *inc, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *HIP_FLAGS, *inc, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"compile of {os.path.basename(src)} failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into ring_attention_merge_amd/libram.so; return its path."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = sources()
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *LINK_FLAGS, *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     return LIB
 

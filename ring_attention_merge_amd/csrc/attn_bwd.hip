@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
   };
   int kb_cur = cnt > 0 ? cols[0] : 0;
   int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
-  int mk_cur = needs_mask(kb_cur);
+  int mk_cur = cnt > 0 ? needs_mask(kb_cur) : 0;   // no class array to read when the row is empty
   if (cnt > 0) dma(kb_cur, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();

@@ -290,6 +290,27 @@ __device__ __forceinline__ void epilogue(const f32x16 (&O)[NDB], float m_ref, fl
   if (lg == 0) *lptr = new_lse;
 }
 
+// The chunk of visit t of a one-launch ring: a copy of the launch's parameters pointing at
+// chunk c = (ring_shard - t) mod n_chunks (or t for natural order), its K / V, masks, key
+// positions and segments; sinks and the launch's `mode` belong to the first visit, out_final
+// to the last.
+__device__ __forceinline__ void ring_chunk_view(AttnParams& pc, const AttnParams& p, int t) {
+  const int n = p.n_chunks;
+  const int c = p.ring_shard >= 0 ? ((p.ring_shard - t) % n + n) % n : t;
+  pc.k = reinterpret_cast<const __bf16*>(p.k) + c * p.kv_chunk_elems;
+  pc.v = reinterpret_cast<const __bf16*>(p.v) + c * p.kv_chunk_elems;
+  pc.tile_class = p.tile_class + c * p.mask_chunk_tiles;
+  pc.col_idx = p.col_idx + c * p.mask_chunk_tiles;
+  pc.row_cnt = p.row_cnt + c * p.mask_chunk_rows;
+  pc.mask_bits = p.mask_bits ? p.mask_bits + c * p.mask_chunk_tiles * p.tile_words : nullptr;
+  pc.kv_pos = p.kv_pos ? p.kv_pos + (int64_t)c * p.Skv : nullptr;
+  pc.kv_seg = p.kv_seg ? p.kv_seg + (int64_t)c * p.Skv : nullptr;
+  pc.kv_pos_base = p.kv_pos_base + c * p.Skv;
+  pc.sinks = t == 0 ? p.sinks : nullptr;
+  pc.mode = t == 0 ? p.mode : 1;
+  pc.out_final = t == n - 1 ? p.out_final : nullptr;
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource over [base, base + bytes): loads at offsets >= bytes return

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
   };
   int kb_cur = cnt > 0 ? cols[0] : 0;
   int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
-  int mk_cur = needs_mask(kb_cur);
+  int mk_cur = cnt > 0 ? needs_mask(kb_cur) : 0;   // no class array to read when the row is empty
   if (cnt > 0) {
     gload(kb_cur);
     lstore(0);
@@ -226,465 +226,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(AttnParams p) {
     mk_cur = mk_nxt;
   }
   epilogue<NDB>(O, m_ref, l_acc, p, b, h, q_row, lg);
-}
-
-// ------------------------------------------------------------------------------ bf16, D = 128, LDS DMA
-// The 4-wave kernel with its K / V tiles moved by the LDS DMA path
-// (buffer_load_dwordx4 ... lds): no staging registers, no LDS stores in the
-// instruction stream. The DMA writes 1 KB per instruction at consecutive
-// addresses, so tiles are dense 256-byte rows whose 16-byte chunks are XOR
-// swizzled (chunk ^ (row & 15) for K, chunk ^ 4*(row & 3) for V) to keep the
-// operand reads free of bank conflicts. Rows past Skv read as zero.
-constexpr int kDmaTile = kBlockKV * 128;   // one K or V tile (elements)
-
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
-}
-
-template <bool CAP, bool BITS>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_dma(AttnParams p) {
-  constexpr int D = 128;
-  constexpr int BK = kBlockKV;
-  constexpr int NDS = D / 16;
-  constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * kDmaTile];   // [stage][K, V]
-
-  int b, h, qb;
-  if (!decode_work(p, b, h, qb)) return;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ln = lane & 31, lg = lane >> 5;
-  const int G = p.H / p.Hkv;
-  const int g = h / G;
-  const int q_row = qb * kBlockQ + w * 32 + ln;
-  const bool q_ok = q_row < p.Sq;
-
-  const int64_t mrow = (int64_t)b * p.nQb + qb;
-  const int cnt = p.row_cnt[mrow];
-  // a merge with nothing to add is the identity (unless the result must be
-  // converted to its final type, which the epilogue does for empty rows)
-  if (cnt == 0 && p.mode == 1 && p.sinks == nullptr && p.out_final == nullptr) return;
-  const auto cols = as_const_space(p.col_idx + mrow * p.nKb);
-  const auto cls = as_const_space(p.tile_class + mrow * p.nKb);
-
-  bf16x8 qf[NDS];
-  {
-    const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b +
-                         ((int64_t)(q_ok ? q_row : 0) * p.H + h) * D;
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      bf16x8 t = *reinterpret_cast<const bf16x8*>(qrow + ds * 16 + lg * 8);
-      qf[ds] = q_ok ? t : bf16x8{};
-    }
-  }
-  const int qrow_c = q_ok ? q_row : p.Sq - 1;
-  const int qpos = p.q_pos ? p.q_pos[(int64_t)b * p.qm_stride_b + qrow_c] : p.q_pos_base + q_row;
-  const int qseg = p.q_seg ? p.q_seg[(int64_t)b * p.qm_stride_b + qrow_c] : 0;
-
-  float m_ref = neg_inf(), l_acc = 0.0f;
-  if (p.sinks) {
-    m_ref = p.sinks[h] * kLog2e;
-    l_acc = (lg == 0) ? 1.0f : 0.0f;
-  }
-  f32x16 O[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) O[db] = f32x16{};
-
-  const int64_t krs = (int64_t)p.Hkv * D;
-  const uint32_t row_bytes = (uint32_t)krs * 2;
-  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.kv_stride_b + g * D;
-  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.kv_stride_b + g * D;
-
-  // DMA: wave w fills tile rows [16w, 16w+16) in four 4-row slabs; lane l of
-  // slab i writes physical chunk l & 15 of row 16w + 4i + (l >> 4).
-  uint32_t koff[4], voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * w + 4 * i + (lane >> 4);
-    const int phys = lane & 15;
-    koff[i] = (uint32_t)r * row_bytes + (phys ^ (r & 15)) * 16;
-    voff[i] = (uint32_t)r * row_bytes + (phys ^ (4 * (r & 3))) * 16;
-  }
-  auto dma = [&](int kb, int buf) {
-    const int k0 = kb * BK;
-    const uint32_t bytes = (uint32_t)min(p.Skv - k0, BK) * row_bytes;
-    const auto kr = tile_rsrc(kbase + (int64_t)k0 * krs, bytes);
-    const auto vr = tile_rsrc(vbase + (int64_t)k0 * krs, bytes);
-    __bf16* Ks = smem + buf * 2 * kDmaTile;
-    __bf16* Vs = Ks + kDmaTile;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(Ks + (16 * w + 4 * i) * D),
-                                               16, koff[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(Vs + (16 * w + 4 * i) * D),
-                                               16, voff[i], 0, 0, 0);
-    }
-  };
-  // Operand offsets (bytes) inside a tile.
-  int k_off[2][NDS];                // K: row kb2*32 + ln, logical chunk 2*ds + lg
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) k_off[kb2][ds] = (kb2 * 32 + ln) * 256 + (((2 * ds + lg) ^ (ln & 15)) * 16);
-  // V (transposing reads): row ks*16 + 8*half + 4*lg + r4, column db*32 + 16*hs + 4*(lane&3)
-  const int r4 = (lane & 15) >> 2, hs = (lane >> 4) & 1;
-  const int v_row = 4 * lg + r4;
-  int v_col[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-    v_col[db] = (((db * 4 + 2 * hs + ((lane & 3) >> 1)) ^ (4 * r4)) * 16) + (lane & 1) * 8;
-
-  if (p.Skv % BK) {
-    // a ragged last tile leaves rows unwritten: start from zeros so that those
-    // rows (masked, weight 0) hold finite values
-    for (int i = tid; i < 2 * 2 * kDmaTile / 8; i += kThreads)
-      reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
-    __syncthreads();
-  }
-
-  // mask kind of a tile: 0 none, 1 from positions / segments, 2 from its stored bits
-  auto needs_mask = [&](int kb) {
-    const int c = cls[kb];
-    if constexpr (BITS)
-      if (c == 1) return 2;
-    return (c != 2 || (kb + 1) * BK > p.Skv) ? 1 : 0;
-  };
-  int kb_cur = cnt > 0 ? cols[0] : 0;
-  int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
-  int mk_cur = needs_mask(kb_cur);
-  if (cnt > 0) dma(kb_cur, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int it = 0; it < cnt; ++it) {
-    const int kb = kb_cur;
-    const int need_mask = mk_cur;
-    const int buf = it & 1;
-    const bool has_next = it + 1 < cnt;
-    if (has_next) dma(kb_nxt, buf ^ 1);   // the stage tile it-1 used: every wave has passed it
-    const char* Kt = reinterpret_cast<const char*>(smem + buf * 2 * kDmaTile);
-    const char* Vt = Kt + kDmaTile * 2;
-
-    // All K operands are requested before the first MFMA (the scheduler would
-    // otherwise issue them one or two MFMAs ahead and wait on each).
-    bf16x8 kf[NDS][2];
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds)
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) kf[ds][kb2] = *reinterpret_cast<const bf16x8*>(Kt + k_off[kb2][ds]);
-    f32x16 S[2];
-    S[0] = f32x16{};
-    S[1] = f32x16{};
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds)
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) S[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][kb2], qf[ds], S[kb2], 0, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_sched_barrier(0);
-    // The first half of the V operands load while the softmax runs.
-    constexpr int NVF = 4 * NDB;   // V operands (ks, db) = (f / NDB, f % NDB)
-    bf16x8 vf[NVF];
-    auto vread = [&](int f) {
-      const char* vp = Vt + ((f / NDB) * 16 + v_row) * 256 + v_col[f % NDB];
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp + 8 * 256));
-      vf[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-#pragma unroll
-    for (int f = 0; f < NVF / 2; ++f) vread(f);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (CAP) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
-    }
-    if (BITS && need_mask == 2)
-      apply_bits(S, p.mask_bits + ((mrow * p.nKb + kb) * kBlockQ + w * 32 + ln) * 2, lg);
-    else if (need_mask)
-      apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
-    softmax_step<NDB, CAP>(S, O, m_ref, l_acc, p);
-
-    bf16x8 P[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x2 two = {S[ks >> 1][(ks & 1) * 8 + 2 * j], S[ks >> 1][(ks & 1) * 8 + 2 * j + 1]};
-        bf16x2 pk = __builtin_convertvector(two, bf16x2);
-        P[ks][2 * j] = pk[0];
-        P[ks][2 * j + 1] = pk[1];
-      }
-    }
-#pragma unroll
-    for (int f = NVF / 2; f < NVF; ++f) vread(f);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int f = 0; f < NVF; ++f) O[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], P[f / NDB], O[f % NDB], 0, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_sched_barrier(0);
-    // List entries for the next iterations. These scalar loads share the wait
-    // counter of LDS reads but complete out of order; issued here, no LDS wait
-    // above has to cover them.
-    const int kb_nn = cols[min(it + 2, cnt - 1)];
-    const int mk_nxt = needs_mask(kb_nxt);
-    // the next tile's DMA must have landed before any wave reads it
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    kb_cur = kb_nxt;
-    kb_nxt = kb_nn;
-    mk_cur = mk_nxt;
-  }
-  epilogue<NDB>(O, m_ref, l_acc, p, b, h, q_row, lg);
-}
-
-// attn_fwd_bf16_dma_ring: the kernel above for a whole ring in one launch. A
-// workgroup keeps its q tile and visits every chunk in ring order, each
-// exactly as a launch of its own would:
-// fresh online-softmax state, the chunk's tile list, positions and sinks (first
-// visit only), then the epilogue's WRITE (first visit) or sigmoid / softplus
-// MERGE into the fp32 running state, the last visit writing the bf16 result.
-// Q, its positions and the operand offsets are loaded once, and no launch ends
-// with a tail of idle compute units between chunks.
-__device__ __forceinline__ void ring_chunk_view(AttnParams& pc, const AttnParams& p, int t) {
-  const int n = p.n_chunks;
-  const int c = p.ring_shard >= 0 ? ((p.ring_shard - t) % n + n) % n : t;
-  pc.k = reinterpret_cast<const __bf16*>(p.k) + c * p.kv_chunk_elems;
-  pc.v = reinterpret_cast<const __bf16*>(p.v) + c * p.kv_chunk_elems;
-  pc.tile_class = p.tile_class + c * p.mask_chunk_tiles;
-  pc.col_idx = p.col_idx + c * p.mask_chunk_tiles;
-  pc.row_cnt = p.row_cnt + c * p.mask_chunk_rows;
-  pc.mask_bits = p.mask_bits ? p.mask_bits + c * p.mask_chunk_tiles * (kBlockQ * (kBlockKV / 32)) : nullptr;
-  pc.kv_pos = p.kv_pos ? p.kv_pos + (int64_t)c * p.Skv : nullptr;
-  pc.kv_seg = p.kv_seg ? p.kv_seg + (int64_t)c * p.Skv : nullptr;
-  pc.kv_pos_base = p.kv_pos_base + c * p.Skv;
-  pc.sinks = t == 0 ? p.sinks : nullptr;
-  pc.mode = t == 0 ? p.mode : 1;
-  pc.out_final = t == n - 1 ? p.out_final : nullptr;
-}
-
-template <bool CAP, bool BITS, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_dma_ring(AttnParams p, RingSplit rs) {
-  constexpr int D = 128;
-  constexpr int BK = kBlockKV;
-  constexpr int NDS = D / 16;
-  constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * kDmaTile];   // [stage][K, V]
-
-  // SPLIT: two workgroups per row (an instantiation of its own, so that the other keeps its
-  // registers)
-  int b, h, qb, sp = 0;
-  if (!decode_work(p, b, h, qb, SPLIT ? 2 : 1, SPLIT ? &sp : nullptr)) return;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ln = lane & 31, lg = lane >> 5;
-  const int G = p.H / p.Hkv;
-  const int g = h / G;
-  const int q_row = qb * kBlockQ + w * 32 + ln;
-  const bool q_ok = q_row < p.Sq;
-  const int64_t mrow = (int64_t)b * p.nQb + qb;
-
-  bf16x8 qf[NDS];
-  {
-    const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b +
-                         ((int64_t)(q_ok ? q_row : 0) * p.H + h) * D;
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      bf16x8 t = *reinterpret_cast<const bf16x8*>(qrow + ds * 16 + lg * 8);
-      qf[ds] = q_ok ? t : bf16x8{};
-    }
-  }
-  const int qrow_c = q_ok ? q_row : p.Sq - 1;
-  const int qpos = p.q_pos ? p.q_pos[(int64_t)b * p.qm_stride_b + qrow_c] : p.q_pos_base + q_row;
-  const int qseg = p.q_seg ? p.q_seg[(int64_t)b * p.qm_stride_b + qrow_c] : 0;
-
-  const int64_t krs = (int64_t)p.Hkv * D;
-  const uint32_t row_bytes = (uint32_t)krs * 2;
-
-  // DMA: wave w fills tile rows [16w, 16w+16) in four 4-row slabs; lane l of
-  // slab i writes physical chunk l & 15 of row 16w + 4i + (l >> 4).
-  uint32_t koff[4], voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * w + 4 * i + (lane >> 4);
-    const int phys = lane & 15;
-    koff[i] = (uint32_t)r * row_bytes + (phys ^ (r & 15)) * 16;
-    voff[i] = (uint32_t)r * row_bytes + (phys ^ (4 * (r & 3))) * 16;
-  }
-  // Operand offsets (bytes) inside a tile.
-  int k_off[2][NDS];                // K: row kb2*32 + ln, logical chunk 2*ds + lg
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) k_off[kb2][ds] = (kb2 * 32 + ln) * 256 + (((2 * ds + lg) ^ (ln & 15)) * 16);
-  // V (transposing reads): row ks*16 + 8*half + 4*lg + r4, column db*32 + 16*hs + 4*(lane&3)
-  const int r4 = (lane & 15) >> 2, hs = (lane >> 4) & 1;
-  const int v_row = 4 * lg + r4;
-  int v_col[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-    v_col[db] = (((db * 4 + 2 * hs + ((lane & 3) >> 1)) ^ (4 * r4)) * 16) + (lane & 1) * 8;
-
-  if (p.Skv % BK) {
-    // a ragged last tile leaves rows unwritten: start from zeros so that those
-    // rows (masked, weight 0) hold finite values (later visits leave earlier
-    // tiles' finite data there)
-    for (int i = tid; i < 2 * 2 * kDmaTile / 8; i += kThreads)
-      reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
-    __syncthreads();
-  }
-
-  // this workgroup's visits (all of them, or one of the two halves of a split ring)
-  const int t_half = (p.n_chunks + 1) / 2;
-  const int t_begin = (SPLIT && sp == 1) ? t_half : 0;
-  const int t_end = (SPLIT && sp == 0) ? t_half : p.n_chunks;
-  for (int t = t_begin; t < t_end; ++t) {
-    AttnParams pc = p;   // this visit's chunk
-    ring_chunk_view(pc, p, t);
-    if (SPLIT && sp == 1) {
-      // the second half runs its own ring into out2 / lse2, starting as a first visit does
-      pc.out = rs.out2;
-      pc.lse = rs.lse2;
-      if (t == t_begin) pc.mode = p.mode;
-    }
-    const int cnt = pc.row_cnt[mrow];
-    // a merge with nothing to add is the identity (unless the result must be
-    // converted to its final type, which the epilogue does for empty rows)
-    if (cnt == 0 && pc.mode == 1 && pc.sinks == nullptr && pc.out_final == nullptr) continue;
-    const auto cols = as_const_space(pc.col_idx + mrow * p.nKb);
-    const auto cls = as_const_space(pc.tile_class + mrow * p.nKb);
-
-    float m_ref = neg_inf(), l_acc = 0.0f;
-    if (pc.sinks) {
-      m_ref = pc.sinks[h] * kLog2e;
-      l_acc = (lg == 0) ? 1.0f : 0.0f;
-    }
-    f32x16 O[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) O[db] = f32x16{};
-
-    const __bf16* kbase = reinterpret_cast<const __bf16*>(pc.k) + (int64_t)b * p.kv_stride_b + g * D;
-    const __bf16* vbase = reinterpret_cast<const __bf16*>(pc.v) + (int64_t)b * p.kv_stride_b + g * D;
-    auto dma = [&](int kb, int buf) {
-      const int k0 = kb * BK;
-      const uint32_t bytes = (uint32_t)min(p.Skv - k0, BK) * row_bytes;
-      const auto kr = tile_rsrc(kbase + (int64_t)k0 * krs, bytes);
-      const auto vr = tile_rsrc(vbase + (int64_t)k0 * krs, bytes);
-      __bf16* Ks = smem + buf * 2 * kDmaTile;
-      __bf16* Vs = Ks + kDmaTile;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dma16(kr, Ks + (16 * w + 4 * i) * D, koff[i]);
-        dma16(vr, Vs + (16 * w + 4 * i) * D, voff[i]);
-      }
-    };
-
-    // mask kind of a tile: 0 none, 1 from positions / segments, 2 from its stored bits
-    auto needs_mask = [&](int kb) {
-      const int c = cls[kb];
-      if constexpr (BITS)
-        if (c == 1) return 2;
-      return (c != 2 || (kb + 1) * BK > p.Skv) ? 1 : 0;
-    };
-    int kb_cur = cnt > 0 ? cols[0] : 0;
-    int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
-    int mk_cur = needs_mask(kb_cur);
-    if (cnt > 0) dma(kb_cur, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int it = 0; it < cnt; ++it) {
-      const int kb = kb_cur;
-      const int need_mask = mk_cur;
-      const int buf = it & 1;
-      const bool has_next = it + 1 < cnt;
-      if (has_next) dma(kb_nxt, buf ^ 1);   // the stage tile it-1 used: every wave has passed it
-      const char* Kt = reinterpret_cast<const char*>(smem + buf * 2 * kDmaTile);
-      const char* Vt = Kt + kDmaTile * 2;
-
-      // All K operands are requested before the first MFMA (the scheduler would
-      // otherwise issue them one or two MFMAs ahead and wait on each).
-      bf16x8 kf[NDS][2];
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds)
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) kf[ds][kb2] = *reinterpret_cast<const bf16x8*>(Kt + k_off[kb2][ds]);
-      f32x16 S[2];
-      S[0] = f32x16{};
-      S[1] = f32x16{};
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds)
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-          S[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][kb2], qf[ds], S[kb2], 0, 0, 0);
-      __builtin_amdgcn_s_setprio(0);
-      __builtin_amdgcn_sched_barrier(0);
-      // The first half of the V operands load while the softmax runs.
-      constexpr int NVF = 4 * NDB;   // V operands (ks, db) = (f / NDB, f % NDB)
-      bf16x8 vf[NVF];
-      auto vread = [&](int f) {
-        const char* vp = Vt + ((f / NDB) * 16 + v_row) * 256 + v_col[f % NDB];
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp));
-        const s16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp + 8 * 256));
-        vf[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-#pragma unroll
-      for (int f = 0; f < NVF / 2; ++f) vread(f);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (CAP) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
-      }
-      if (BITS && need_mask == 2)
-        apply_bits(S, pc.mask_bits + ((mrow * p.nKb + kb) * kBlockQ + w * 32 + ln) * 2, lg);
-      else if (need_mask)
-        apply_mask(S, pc, b, kb * BK, lg, qpos, qseg);
-      softmax_step<NDB, CAP>(S, O, m_ref, l_acc, p);
-
-      bf16x8 P[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x2 two = {S[ks >> 1][(ks & 1) * 8 + 2 * j], S[ks >> 1][(ks & 1) * 8 + 2 * j + 1]};
-          bf16x2 pk = __builtin_convertvector(two, bf16x2);
-          P[ks][2 * j] = pk[0];
-          P[ks][2 * j + 1] = pk[1];
-        }
-      }
-#pragma unroll
-      for (int f = NVF / 2; f < NVF; ++f) vread(f);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int f = 0; f < NVF; ++f)
-        O[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], P[f / NDB], O[f % NDB], 0, 0, 0);
-      __builtin_amdgcn_s_setprio(0);
-      __builtin_amdgcn_sched_barrier(0);
-      // List entries for the next iterations. These scalar loads share the wait
-      // counter of LDS reads but complete out of order; issued here, no LDS wait
-      // above has to cover them.
-      const int kb_nn = cols[min(it + 2, cnt - 1)];
-      const int mk_nxt = needs_mask(kb_nxt);
-      // the next tile's DMA must have landed before any wave reads it
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      kb_cur = kb_nxt;
-      kb_nxt = kb_nn;
-      mk_cur = mk_nxt;
-    }
-    epilogue<NDB>(O, m_ref, l_acc, pc, b, h, q_row, lg);
-  }
 }
 
 // ------------------------------------------------------------------------------ fp32
@@ -776,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(AttnParams p) {
   };
   int kb_cur = cnt > 0 ? cols[0] : 0;
   int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
-  int mk_cur = needs_mask(kb_cur);
+  int mk_cur = cnt > 0 ? needs_mask(kb_cur) : 0;   // no class array to read when the row is empty
   if (cnt > 0) {
     gload(kb_cur);
     lstore(0);
@@ -846,35 +387,6 @@ hipError_t launch(K kernel, const AttnParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-// Kernel choice for bf16. The 4-wave kernel is the default (for D = 128 with
-// its tiles moved by LDS DMA; `staged` forces the register-staged version).
-// The other layouts are kept as measured alternatives, all checked against
-// the oracle; on the 32k causal D=128 workload they ran below the default:
-//   pingpong  8 waves in two groups taking turns at the matrix cores
-//   wide      4 waves, 64 query rows per wave (halves LDS reads per MFMA),
-//             softmax interleaved with MFMAs; no position / segment arrays
-//   g8        8 waves, 32 rows each, 3-stage K/V ring filled by LDS DMA
-//   g8p       g8 with each wave's softmax interleaved between its MFMAs
-// RAM_ATTN_KERNEL=<name> forces one (D = 128 only, except pingpong).
-static int attn_variant(const AttnParams& p) {
-  const char* e = getenv("RAM_ATTN_KERNEL");
-  if (p.mask_bits) return (e && strcmp(e, "staged") == 0) ? 5 : 0;   // the others read no tile bits
-  if (e && strcmp(e, "pingpong") == 0) return 1;
-  if (e && strcmp(e, "wide") == 0 && p.D == 128 && !p.kv_pos && !p.kv_seg) return 2;
-  if (e && strcmp(e, "g8") == 0 && p.D == 128) return 3;
-  if (e && strcmp(e, "g8p") == 0 && p.D == 128) return 4;
-  if (e && strcmp(e, "staged") == 0) return 5;
-  return 0;
-}
-
-bool attn_writes_final(const AttnParams& p, int dtype) {
-  if (dtype != 1) return false;
-  const int v = attn_variant(p);
-  return v == 0 || v == 5;
-}
-
 // Instantiations by (soft cap, tile bits); BITS kernels mask PARTIAL tiles by their stored bits.
 template <template <bool, bool> class K>
 hipError_t launch_cb(const AttnParams& p, hipStream_t s) {
@@ -896,48 +408,12 @@ struct F32 {
     static constexpr auto fn = attn_fwd_f32<D, CAP, BITS>;
   };
 };
-template <bool CAP, bool BITS>
-struct Bf16Dma {
-  static constexpr auto fn = attn_fwd_bf16_dma<CAP, BITS>;
-};
-template <bool CAP, bool BITS>
-struct Bf16DmaRing {
-  static constexpr auto fn = attn_fwd_bf16_dma_ring<CAP, BITS, false>;
-};
-template <bool CAP, bool BITS>
-struct Bf16DmaRingSplit {
-  static constexpr auto fn = attn_fwd_bf16_dma_ring<CAP, BITS, true>;
-};
 
-bool attn_ring_fused(const AttnParams& p, int dtype) {
-  if (dtype != 1 || p.D != 128 || attn_variant(p) != 0) return false;
-  const char* e = getenv("RAM_RING");
-  return !(e && strcmp(e, "per_chunk") == 0);
-}
-
-template <template <bool, bool> class K>
-hipError_t launch_ring_cb(const AttnParams& p, const RingSplit& rs, int S, hipStream_t s) {
-  const bool cap = p.softcap_on != 0, bits = p.mask_bits != nullptr;
-  const auto fn = cap ? (bits ? K<true, true>::fn : K<true, false>::fn) : (bits ? K<false, true>::fn : K<false, false>::fn);
-  const int64_t T = (int64_t)p.B * p.H * p.nQb * S;
-  hipLaunchKernelGGL(fn, dim3((unsigned)(8 * ((T + 7) / 8))), dim3(kThreads), 0, s, p, rs);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_ring(const AttnParams& p, const RingSplit* split, hipStream_t s) {
-  if (p.n_chunks < 1) return hipErrorInvalidValue;
-  if (split) return launch_ring_cb<Bf16DmaRingSplit>(p, *split, 2, s);
-  return launch_ring_cb<Bf16DmaRing>(p, RingSplit{nullptr, nullptr}, 1, s);
-}
+}  // namespace
 
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s) {
-  const int variant = dtype == 1 ? attn_variant(p) : 0;
-  if (variant == 1) return launch_attn_pp(p, s);
-  if (variant == 2) return launch_attn_w64(p, s);
-  if (variant == 3) return launch_attn_g8(p, s);
-  if (variant == 4) return launch_attn_g8p(p, s);
   if (dtype == 1) {
-    if (p.D == 128) return variant == 5 ? launch_cb<Bf16Staged<128>::K>(p, s) : launch_cb<Bf16Dma>(p, s);
+    if (p.D != 64) return hipErrorInvalidValue;   // bf16 D = 128 runs launch_attn_alt
     return launch_cb<Bf16Staged<64>::K>(p, s);
   }
   if (p.D == 128) return launch_cb<F32<128>::K>(p, s);

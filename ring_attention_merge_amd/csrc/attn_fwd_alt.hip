@@ -1,0 +1,483 @@
+// Block-sparse attention forward for bf16, D = 128, with a deep DMA pipeline and operands read a
+// step ahead into registers. Serves attn_fwd_chunk (one visit) and the one-launch ring of
+// ring_attn_fwd_1gpu (one visit per KV chunk).
+//
+// What it computes: the per-ring-step kernel call of the ejkernel ring-splash source page
+// (_ring_attention_forward): attention of q over one KV chunk, returning the chunk output and
+// log-sum-exp, folded into the running state with _update_out_and_lse (sigmoid weight,
+// softplus lse) on every visit after the first. Masking follows the Kvax flash_attention
+// arguments.
+//
+// Design for gfx950 (CDNA4):
+//  * One workgroup = 4 waves = 128 query rows of one head, wave w owning rows 32w..32w+31; two
+//    workgroups per CU, so each SIMD holds two waves of different workgroups that run freely
+//    past each other: one wave's softmax arithmetic issues in the other's matrix-product
+//    shadow.
+//  * The workgroup walks the compacted list of its row of 128x64 mask tiles in steps of 32
+//    keys. Step j of a wave: S(j+1) = K(j+1) Q^T (v_mfma_f32_32x32x16_bf16, K from registers,
+//    Q held for the whole launch) in fenced groups of one product beside two exponentials of
+//    S(j); then O^T += V(j)^T P(j)^T beside the bf16 packing and row sum of S(j); one barrier;
+//    then the DMA of step j+kAltStages, the LDS reads of the next operands (K(j+2), V(j+1)),
+//    and the mask and row max of S(j+1). The loop is unrolled by the ring depth, so stage
+//    offsets are immediates of the reads and the two score register sets alternate. Scores are transposed, so a lane owns one query row:
+//    row max and row sum are in-lane plus one v_permlane32_swap with the partner lane.
+//  * K / V step tiles (32 keys x 256 B each, 16-byte chunks XOR-swizzled so the operand reads
+//    are free of bank conflicts) come into a ring of kAltStages LDS stages by LDS DMA. The DMA
+//    is issued from inline assembly, so the compiler does not see its LDS writes and places
+//    its own waits only for the LDS reads it issues; the kernel orders the DMA with vmcnt waits
+//    (only for the tile the next reads need) and barriers, both compiler memory barriers.
+//  * Masks: FULL tiles run no mask code. PARTIAL tiles are masked either by one compare per
+//    score against a per-row key limit (sequential key positions, no segments, no dense mask)
+//    or, in the BITS instantiations, from the tile's stored element bits, which come into LDS
+//    with the step's DMA. A FULL tile cut by the end of the chunk masks the keys past it.
+//  * Online softmax in base 2 with the scale folded into one FMA; the running max is raised
+//    only when a row's max grows by more than 2^8.
+#include <type_traits>
+
+#include "attn_common.h"
+
+namespace ram {
+namespace {
+
+using namespace attn;
+
+constexpr int kAltWaves = kAltRows / 32;                    // one wave per 32 query rows
+constexpr int kAltThreads = 64 * kAltWaves;
+constexpr int kAltKeys = 32;                                // keys per step
+constexpr int kAltStages = 4;                               // LDS ring depth (steps)
+constexpr int kAltTile = kAltKeys * 256;                    // bytes of one K or V step tile
+constexpr int kDmaPerTile = kAltKeys / (4 * kAltWaves);     // 1 KiB DMA instructions per wave and tile
+constexpr int kAltBitsBytes = kAltWaves * 256;              // one step's tile bits: 32 rows x 2 words per wave
+
+template <bool BITS>
+constexpr int alt_stage_bytes() {
+  return 2 * kAltTile + (BITS ? kAltBitsBytes : 0);
+}
+
+// LDS DMA issued from inline assembly: 16 bytes per lane (4 for dma4) from the buffer at byte
+// offset `voff` into LDS at m0 + 16 * lane (4 * lane). The compiler does not see these writes to
+// LDS, so it never waits for them before its own LDS reads; the kernel orders them itself with
+// vmcnt waits and barriers that are also compiler memory barriers (the "memory" clobber). m0 is
+// set by every DMA statement and read by nothing else in this kernel.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_byte, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_byte), "v"(voff), "s"(r)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds_byte, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_byte), "v"(voff), "s"(r)
+               : "memory");
+}
+
+// Wait until at most N vector-memory loads of this wave (the DMA included) are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// Wait until at most PER * k vector loads are outstanding, k in [0, K] (a runtime value picks
+// among compile-time immediates).
+template <int PER, int K>
+__device__ __forceinline__ void wait_vm_steps(int k) {
+  if constexpr (K == 0) {
+    wait_vm<0>();
+  } else {
+    if (k >= K) wait_vm<PER * K>();
+    else wait_vm_steps<PER, K - 1>(k);
+  }
+}
+// Workgroup barrier that is also a compiler memory barrier (LDS written by DMA is read after it).
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" : : : "memory"); }
+
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t byte) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>((uintptr_t)byte);
+}
+__device__ __forceinline__ uint32_t lds_b32(uint32_t byte) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>((uintptr_t)byte);
+}
+// One V operand: two transposing reads, 8 rows (2048 bytes) apart, joined.
+__device__ __forceinline__ bf16x8 lds_v_operand(uint32_t byte) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>((uintptr_t)byte));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>((uintptr_t)(byte + 2048)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Mask of one step's scores. kind: 0 no mask, 1 keys at or past `thr` (lane-relative key
+// offset) masked, 2 from bits `bw` (key 8*(i>>2) + 4*lg + (i&3) at bit 8*(i>>2) + 4*lg + (i&3)).
+template <bool BITS>
+__device__ __forceinline__ void step_mask(f32x16& S, int kind, int thr, uint32_t bw, int lg) {
+  if (kind == 1) {
+    asm volatile("" : "+v"(thr));   // keep the compares next to their use
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (8 * (i >> 2) + (i & 3) >= thr) S[i] = neg_inf();
+  } else if (BITS && kind == 2) {
+    const uint32_t x = bw >> (4 * lg);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (((x >> (8 * (i >> 2) + (i & 3))) & 1u) == 0u) S[i] = neg_inf();
+  }
+}
+
+// Row max of one step's (capped, masked) scores in the running max's units: whether some row
+// grew by more than 2^8 over m_ref (wave-uniform), and the new max and the factor for O and l.
+template <bool CAP>
+__device__ __forceinline__ bool step_max(const f32x16& S, float m_ref, float& m_new, float& alpha,
+                                         const AttnParams& p) {
+  float all[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) all[i] = S[i];
+  const float mx = pair_max(max_tree3(all));
+  const float umax = CAP ? mx : mx * p.scale_log2;
+  m_new = fmaxf(m_ref, umax);
+  alpha = (m_new == neg_inf()) ? 1.0f : fast_exp2(m_ref - m_new);
+  return __builtin_amdgcn_ballot_w64(umax > m_ref + kRescaleThreshold) != 0;
+}
+
+template <bool CAP>
+__device__ __forceinline__ void step_cap(f32x16& S, const AttnParams& p) {
+  if constexpr (CAP) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[i] = capped_log2(S[i], p.cap_k2, p.cap_log2);
+  }
+}
+
+template <bool CAP, bool BITS, bool SPLIT>
+__global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p, RingSplit rs) {
+  constexpr int D = 128;
+  constexpr int NS = kAltStages;
+  constexpr int SB = alt_stage_bytes<BITS>();
+  constexpr int NDMA = 2 * kDmaPerTile + (BITS ? 1 : 0);   // DMA instructions per wave and step
+  // NS stages of SB bytes, then the visit's tile list with each tile's class (kb | class << 16),
+  // staged once per visit so that the loop reads it from LDS instead of waiting on scalar
+  // loads (p.nKb words).
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  uint32_t* tinfo = reinterpret_cast<uint32_t*>(smem + NS * SB);
+
+  // SPLIT: two workgroups per row, each with half the visits (an instantiation of its own)
+  int b, h, qb, sp = 0;
+  if (!decode_work(p, b, h, qb, SPLIT ? 2 : 1, SPLIT ? &sp : nullptr)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, lg = lane >> 5;
+  const int G = p.H / p.Hkv;
+  const int g = h / G;
+  const int q_row = qb * kAltRows + w * 32 + ln;
+  const bool q_ok = q_row < p.Sq;
+  const int64_t mrow = (int64_t)b * p.nQb + qb;
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds row q_row, dims 16*ds + 8*lg .. +7.
+  bf16x8 qf[8];
+  {
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_stride_b +
+                         ((int64_t)(q_ok ? q_row : 0) * p.H + h) * D;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) {
+      const bf16x8 t = *reinterpret_cast<const bf16x8*>(qrow + ds * 16 + lg * 8);
+      qf[ds] = q_ok ? t : bf16x8{};
+    }
+  }
+  const int qrow_c = q_ok ? q_row : p.Sq - 1;
+  const int qpos = p.q_pos ? p.q_pos[(int64_t)b * p.qm_stride_b + qrow_c] : p.q_pos_base + q_row;
+
+  const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;   // bytes between key rows
+  // DMA: wave w fills rows 4*(w + kAltWaves*i) .. +3 of a step tile (i < kDmaPerTile); lane l
+  // writes physical 16-byte chunk l & 15 of row 4*(w + kAltWaves*i) + (l >> 4), i.e. 1 KiB of
+  // consecutive LDS bytes per instruction.
+  uint32_t koff[kDmaPerTile], voff[kDmaPerTile];
+#pragma unroll
+  for (int i = 0; i < kDmaPerTile; ++i) {
+    const int dr = 4 * (w + kAltWaves * i) + (lane >> 4), phys = lane & 15;
+    koff[i] = (uint32_t)dr * row_bytes + (uint32_t)((phys ^ (dr & 15)) * 16);
+    voff[i] = (uint32_t)dr * row_bytes + (uint32_t)((phys ^ (4 * (dr & 3))) * 16);
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  // Operand read offsets inside a stage. K: row ln, logical chunk 2*ds + lg.
+  uint32_t k_rd[8];
+#pragma unroll
+  for (int ds = 0; ds < 8; ++ds) k_rd[ds] = ln * 256 + (((2 * ds + lg) ^ (ln & 15)) * 16);
+  // V (transposing reads, see lds_read_tr16): row 4*lg + r4 (+8, +16, +24), head dims
+  // db*32 + 16*hs + 4*(lane&3) .. +3, r4 = (lane&15)>>2, hs = (lane>>4)&1.
+  const int r4 = (lane & 15) >> 2, hs = (lane >> 4) & 1;
+  uint32_t v_rd[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    v_rd[db] = kAltTile + (4 * lg + r4) * 256 + ((((db * 4 + 2 * hs + ((lane & 3) >> 1)) ^ (4 * r4)) * 16) +
+                                                 (lane & 1) * 8);
+  const uint32_t b_rd = 2 * kAltTile + w * 256 + ln * 8;   // + 4 * (step parity)
+
+  // this workgroup's visits (all of them, or one of the two halves of a split ring)
+  const int t_half = (p.n_chunks + 1) / 2;
+  const int t_begin = (SPLIT && sp == 1) ? t_half : 0;
+  const int t_end = (SPLIT && sp == 0) ? t_half : p.n_chunks;
+  for (int t = t_begin; t < t_end; ++t) {
+    AttnParams pc = p;   // this visit's chunk
+    ring_chunk_view(pc, p, t);
+    if (SPLIT && sp == 1) {
+      // the second half runs its own ring into out2 / lse2, starting as a first visit does
+      pc.out = rs.out2;
+      pc.lse = rs.lse2;
+      if (t == t_begin) pc.mode = p.mode;
+    }
+    const int cnt = pc.row_cnt[mrow];
+    // a merge with nothing to add is the identity (unless the result must be converted to its
+    // final type, which the epilogue does for empty rows)
+    if (cnt == 0 && pc.mode == 1 && pc.sinks == nullptr && pc.out_final == nullptr) continue;
+    const int n = 2 * cnt;   // steps of 32 keys
+    const int32_t* cols = pc.col_idx + mrow * p.nKb;
+    const uint8_t* cls = pc.tile_class + mrow * p.nKb;
+
+    float m_ref = neg_inf(), l_acc = 0.0f;
+    if (pc.sinks) {
+      m_ref = pc.sinks[h] * kLog2e;
+      l_acc = (lg == 0) ? 1.0f : 0.0f;
+    }
+    f32x16 O[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) O[db] = f32x16{};
+    // keys at or past lim (chunk-relative) are masked in PARTIAL tiles of the positional kernels,
+    // keys at or past Skv in FULL tiles cut by the chunk end
+    int lim = p.Skv;
+    if (!BITS && p.causal) {
+      const int64_t reach = (int64_t)qpos - pc.kv_pos_base + 1;
+      lim = (int)max<int64_t>(-1, min<int64_t>(p.Skv, reach));
+    }
+
+    // K / V of this (batch, kv head) in this chunk, as wave-uniform byte addresses
+    const uint64_t kbase = (uint64_t)reinterpret_cast<uintptr_t>(
+        reinterpret_cast<const __bf16*>(pc.k) + (int64_t)b * p.kv_stride_b + g * D);
+    const uint64_t vbase = (uint64_t)reinterpret_cast<uintptr_t>(
+        reinterpret_cast<const __bf16*>(pc.v) + (int64_t)b * p.kv_stride_b + g * D);
+    // DMA of step s (32 keys of the tile in info word `inf`) into stage st: this wave's rows of K
+    // and V and (BITS) its 32 rows' bit words of the tile when it is PARTIAL.
+    auto dma_step = [&](int s, int st, uint32_t inf) {
+      const int kb = (int)(inf & 0xffffu);
+      const int k0 = kb * kBlockKV + (s & 1) * kAltKeys;
+      const uint32_t bytes = (uint32_t)max(0, min(p.Skv - k0, kAltKeys)) * row_bytes;
+      const uint64_t off = (uint64_t)(uint32_t)k0 * row_bytes;
+      const auto kr = tile_rsrc(reinterpret_cast<const void*>(kbase + off), bytes);
+      const auto vr = tile_rsrc(reinterpret_cast<const void*>(vbase + off), bytes);
+      const uint32_t sb = lds0 + st * SB;
+#pragma unroll
+      for (int i = 0; i < kDmaPerTile; ++i) {
+        dma16(kr, sb + 4 * (w + kAltWaves * i) * 256, koff[i]);
+        dma16(vr, sb + kAltTile + 4 * (w + kAltWaves * i) * 256, voff[i]);
+      }
+      if constexpr (BITS) {
+        const bool partial = (inf >> 16) == 1u;
+        const uint32_t* words = pc.mask_bits + ((mrow * p.nKb + kb) * kAltRows + w * 32) * 2;
+        const auto br = tile_rsrc(words, partial ? 256u : 0u);
+        dma4(br, sb + 2 * kAltTile + w * 256, (uint32_t)lane * 4);
+      }
+    };
+    // mask kind and lane-relative key limit of step s
+    auto step_info = [&](int s, uint32_t inf, int& kind, int& thr) {
+      const int kb = (int)(inf & 0xffffu);
+      const int c = (int)(inf >> 16);
+      const int k0 = kb * kBlockKV + (s & 1) * kAltKeys;
+      const bool cut = k0 + kAltKeys > p.Skv;
+      kind = (BITS && c == 1) ? 2 : ((c != 2 || cut) ? 1 : 0);
+      thr = lim - (k0 + 4 * lg);
+    };
+    // info word of step s (clamped to the list), read from LDS
+    auto info = [&](int s) { return tinfo[min(s >> 1, cnt - 1)]; };
+
+    // Every wave is done with the previous visit's stages and list; then this visit's list.
+    __syncthreads();
+    for (int i = tid; i < cnt; i += kAltThreads) {
+      const int kb = cols[i];
+      tinfo[i] = (uint32_t)kb | ((uint32_t)cls[kb] << 16);
+    }
+    __syncthreads();
+    if (n > 0) {
+      const int pre = min(NS, n);
+      {
+        uint32_t inf[(NS + 1) / 2];
+#pragma unroll
+        for (int e = 0; e < (NS + 1) / 2; ++e) inf[e] = __builtin_amdgcn_readfirstlane(tinfo[min(e, cnt - 1)]);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          if (s < pre) dma_step(s, s, inf[s >> 1]);
+      }
+      // steps 0 and 1 must have landed (n is even, so n >= 2)
+      wait_vm_steps<NDMA, NS - 2>(pre - 2);
+      barrier();
+
+      bf16x8 kf[8], vf[8];
+      bf16x8 P[2];
+      // scores of the step being exponentiated and of the next one, alternating between the two
+      // registers sets with the step's parity (the loop is unrolled by NS, which is even)
+      f32x16 S2[2];
+      // S(0), its mask and row max
+      S2[0] = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds)
+        S2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(lds0 + k_rd[ds]), qf[ds], S2[0], 0, 0, 0);
+      {
+        int kind, thr;
+        step_info(0, __builtin_amdgcn_readfirstlane(info(0)), kind, thr);
+        step_cap<CAP>(S2[0], p);
+        step_mask<BITS>(S2[0], kind, thr, BITS ? lds_b32(lds0 + b_rd) : 0u, lg);
+        float m_new, alpha;
+        if (step_max<CAP>(S2[0], m_ref, m_new, alpha, p)) {
+          l_acc *= alpha;
+          m_ref = m_new;
+        }
+      }
+      // operands of step 1 (K) and step 0 (V); list entries a step ahead. Operand addresses are
+      // a per-lane base plus compile-time offsets (stage, key block), folded into the reads.
+      uint32_t kad[8], vad[4];
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds) kad[ds] = lds0 + k_rd[ds];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) vad[db] = lds0 + v_rd[db];
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds) kf[ds] = lds_b128(kad[ds] + SB);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vf[i] = lds_v_operand(vad[i & 3] + (i >> 2) * 4096);
+      uint32_t inf_dma = info(NS), inf_msk = info(1);
+
+      // Step j (stage j % NS == JS): products, barrier, loads.
+      auto step = [&](auto JS_, int j) {
+        constexpr int JS = decltype(JS_)::value;
+        constexpr int CUR = JS & 1, NXT = CUR ^ 1;
+        constexpr int ST1 = (JS + 1) % NS, ST2 = (JS + 2) % NS;
+        f32x16& Sc = S2[CUR];
+        f32x16& Sn = S2[NXT];
+        // ---------------------------------------------------------------- products of step j
+        // S(j+1) = K(j+1) Q^T in fenced groups of one product and two exponentials of S(j), then
+        // O^T += V(j)^T P(j)^T beside the bf16 packing. On the last step the first product runs
+        // on stale operands and its result is not used.
+        Sn = f32x16{};
+        {
+          const float msub = (m_ref == neg_inf()) ? 0.0f : m_ref;
+          const float sc = CAP ? 1.0f : p.scale_log2;
+#pragma unroll
+          for (int ds = 0; ds < 8; ++ds) {
+            Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[ds], Sn, 0, 0, 0);
+            float e0 = fast_exp2(__builtin_fmaf(Sc[2 * ds], sc, -msub));
+            float e1 = fast_exp2(__builtin_fmaf(Sc[2 * ds + 1], sc, -msub));
+            // pin the product and the two exponentials to this group (the compiler would
+            // otherwise move the products next to their use)
+            asm volatile("" : "+v"(Sn), "+v"(e0), "+v"(e1));
+            Sc[2 * ds] = e0;
+            Sc[2 * ds + 1] = e1;
+          }
+        }
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2) {
+          f32x2 two = {Sc[2 * j2], Sc[2 * j2 + 1]};
+          const bf16x2 pk = __builtin_convertvector(two, bf16x2);
+          P[0][2 * j2] = pk[0];
+          P[0][2 * j2 + 1] = pk[1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          O[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], P[0], O[i], 0, 0, 0);
+          if (i == 0) {
+#pragma unroll
+            for (int j2 = 0; j2 < 4; ++j2) {
+              f32x2 two = {Sc[8 + 2 * j2], Sc[8 + 2 * j2 + 1]};
+              const bf16x2 pk = __builtin_convertvector(two, bf16x2);
+              P[1][2 * j2] = pk[0];
+              P[1][2 * j2 + 1] = pk[1];
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 + i], P[1], O[i], 0, 0, 0);
+        {
+          // row sum as a tree, in fp32 (bf16 weights would put up to 2^-9 into the lse of a row
+          // with few keys)
+          const float t0 = (Sc[0] + Sc[1]) + (Sc[2] + Sc[3]);
+          const float t1 = (Sc[4] + Sc[5]) + (Sc[6] + Sc[7]);
+          const float t2 = (Sc[8] + Sc[9]) + (Sc[10] + Sc[11]);
+          const float t3 = (Sc[12] + Sc[13]) + (Sc[14] + Sc[15]);
+          l_acc += (t0 + t1) + (t2 + t3);
+        }
+        // step j+2's tile (read below) has landed: this wave issued its DMA through step
+        // min(n, j+NS)-1, the tile's being at most NS-3 steps before the newest; the barrier
+        // makes every wave's share visible and shows that every wave is done with step j's
+        // stage (its last reads fed this step's products)
+        if (j + 2 < n) wait_vm_steps<NDMA, NS - 3>(min(n, j + NS) - 1 - (j + 2));
+        barrier();
+
+        // ---------------------------------------------------------------- loads of step j
+        // The DMA into step j's stage, the operand and list reads for the next products, then
+        // the mask and row max of S(j+1) and, when a row's max grew by more than 2^8, the
+        // rescale of O and l.
+        const bool has_next = j + 1 < n;
+        const uint32_t inf_d = __builtin_amdgcn_readfirstlane(inf_dma);
+        const uint32_t inf_m = __builtin_amdgcn_readfirstlane(inf_msk);
+        if (j + NS < n) dma_step(j + NS, JS, inf_d);
+        if (j + 2 < n) {
+#pragma unroll
+          for (int ds = 0; ds < 8; ++ds) kf[ds] = lds_b128(kad[ds] + ST2 * SB);
+        }
+        if (has_next) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) vf[i] = lds_v_operand(vad[i & 3] + ST1 * SB + (i >> 2) * 4096);
+          inf_dma = info(j + 1 + NS);
+          inf_msk = info(j + 2);
+          int kind, thr;
+          step_info(j + 1, inf_m, kind, thr);
+          step_cap<CAP>(Sn, p);
+          step_mask<BITS>(Sn, kind, thr, BITS ? lds_b32(lds0 + ST1 * SB + b_rd + 4 * ((JS + 1) & 1)) : 0u, lg);
+          float m_new, alpha;
+          if (step_max<CAP>(Sn, m_ref, m_new, alpha, p)) {
+            l_acc *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
+            m_ref = m_new;
+          }
+        }
+      };
+      static_assert(NS == 4, "the step loop is unrolled by the ring depth");
+      // n is even: groups of four steps, then possibly two
+      for (int j = 0; j < n; j += 4) {
+        step(std::integral_constant<int, 0>{}, j);
+        step(std::integral_constant<int, 1>{}, j + 1);
+        if (j + 2 >= n) break;
+        step(std::integral_constant<int, 2>{}, j + 2);
+        step(std::integral_constant<int, 3>{}, j + 3);
+      }
+    }
+    epilogue<4>(O, m_ref, l_acc, pc, b, h, q_row, lg);
+  }
+}
+
+template <bool CAP, bool BITS, bool SPLIT>
+hipError_t launch_alt(const AttnParams& p, const RingSplit& rs, hipStream_t s) {
+  const int S = SPLIT ? 2 : 1;
+  const int64_t T = (int64_t)p.B * p.H * p.nQb * S;
+  const size_t lds = (size_t)kAltStages * alt_stage_bytes<BITS>() + 4 * (size_t)max(1, p.nKb);
+  hipLaunchKernelGGL((attn_fwd_bf16_alt<CAP, BITS, SPLIT>), dim3((unsigned)(8 * ((T + 7) / 8))), dim3(kAltThreads),
+                     lds, s, p, rs);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_alt(const AttnParams& p, const RingSplit* split, hipStream_t s) {
+  if (p.n_chunks < 1) return hipErrorInvalidValue;
+  const bool cap = p.softcap_on != 0, bits = p.mask_bits != nullptr;
+  const RingSplit rs = split ? *split : RingSplit{nullptr, nullptr};
+  if (split) {
+    if (cap) return bits ? launch_alt<true, true, true>(p, rs, s) : launch_alt<true, false, true>(p, rs, s);
+    return bits ? launch_alt<false, true, true>(p, rs, s) : launch_alt<false, false, true>(p, rs, s);
+  }
+  if (cap) return bits ? launch_alt<true, true, false>(p, rs, s) : launch_alt<true, false, false>(p, rs, s);
+  return bits ? launch_alt<false, true, false>(p, rs, s) : launch_alt<false, false, false>(p, rs, s);
+}
+
+}  // namespace ram

@@ -46,9 +46,12 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int64_t kMaxSeq = int64_t(1) << 30;
 constexpr int kMaxHeads = 1 << 16;
 
-// Checks the fields every call reads. `tile_for_attn` also requires the
-// kernel tile; otherwise the mask tile limits apply.
-ram_status check_desc(const ram_attn_desc* d, bool tile_for_attn, bool need_heads) {
+// Which tile a call needs its block masks at.
+enum TileUse { kMaskTile = 0, kFwdTile = 1, kBwdTile = 2 };
+
+// Checks the fields every call reads. kFwdTile / kBwdTile also require the
+// forward / backward kernels' mask tile; kMaskTile only the builder's limits.
+ram_status check_desc(const ram_attn_desc* d, TileUse tile, bool need_heads) {
   if (!d) return fail(RAM_ERR_INVALID, "desc is null");
   if (d->B < 0 || d->Sq < 0 || d->Skv < 0)
     return fail(RAM_ERR_INVALID, "negative size: B=%d Sq=%d Skv=%d", d->B, d->Sq, d->Skv);
@@ -72,10 +75,11 @@ ram_status check_desc(const ram_attn_desc* d, bool tile_for_attn, bool need_head
       return fail(RAM_ERR_INVALID, "q_stride_b=%lld (>= %lld, 16-byte multiple)", (long long)d->q_stride_b,
                   (long long)qmin);
   }
-  if (tile_for_attn) {
-    if (d->block_q != ram::kBlockQ || d->block_kv != ram::kBlockKV)
+  if (tile != kMaskTile) {
+    const int bq = tile == kFwdTile ? ram::fwd_block_q(d->dtype, d->D) : ram::kBlockQ;
+    if (d->block_q != bq || d->block_kv != ram::kBlockKV)
       return fail(RAM_ERR_INVALID, "block mask tile %dx%d differs from the kernel tile %dx%d", d->block_q,
-                  d->block_kv, ram::kBlockQ, ram::kBlockKV);
+                  d->block_kv, bq, ram::kBlockKV);
   } else {
     if (d->block_q < 16 || d->block_q > ram::kMaxMaskTile || d->block_kv < 16 || d->block_kv > ram::kMaxMaskTile)
       return fail(RAM_ERR_INVALID, "tile %dx%d outside [16, %d]", d->block_q, d->block_kv, ram::kMaxMaskTile);
@@ -204,7 +208,7 @@ ram::MaskParams mask_params(const ram_attn_desc* d, const ram_mask_src* m, const
 
 ram::AttnParams attn_params(const ram_attn_desc* d, const void* q, const void* k, const void* v,
                             const ram_mask_src* m, const ram_block_mask* bm, const float* sinks, int mode,
-                            float* out, float* lse) {
+                            float* out, float* lse, int block_q) {
   ram::AttnParams p{};
   p.q = q;
   p.k = k;
@@ -232,8 +236,9 @@ ram::AttnParams attn_params(const ram_attn_desc* d, const void* q, const void* k
   p.H = d->H;
   p.Hkv = d->Hkv;
   p.D = d->D;
-  p.nQb = (int)cdiv(d->Sq, ram::kBlockQ);
+  p.nQb = (int)cdiv(d->Sq, block_q);
   p.nKb = (int)cdiv(d->Skv, ram::kBlockKV);
+  p.tile_words = block_q * (ram::kBlockKV / 32);
   const float log2e = 1.4426950408889634f;
   p.scale_log2 = d->scale * log2e;
   p.softcap_on = d->softcap > 0.0f;
@@ -248,24 +253,36 @@ struct RingLayout {
   size_t acc_off, cls_off, cnt_off, col_off, bits_off, acc2_off, lse2_off, total;
 };
 
-// Whether the one-launch ring splits each q tile row's visits over two workgroups: when its
-// rows give fewer than two workgroups per CU (the kernel is built for two waves per SIMD),
-// two halves of the ring run side by side and are merged afterwards. The workspace always
-// has room for the second half's result when the shape could split; `RAM_RING_SPLIT=0` keeps
-// one workgroup per row (then the ring is bit-identical to chunk-by-chunk launches).
-bool ring_split_shape(const ram_attn_desc* d, int32_t n_chunks) {
-  return d->dtype == RAM_BF16 && d->D == 128 && n_chunks >= 2 &&
-         (int64_t)d->B * d->H * cdiv(d->Sq, ram::kBlockQ) < 512;
+// The bf16 kernel for D = 128 runs a whole ring in one launch; the others run one chunk per launch.
+bool alt_kernel(const ram_attn_desc* d) { return d->dtype == RAM_BF16 && d->D == 128; }
+
+// Whether a forward call's PARTIAL tiles are masked from tile bits: always with a dense mask,
+// and in the bf16 D = 128 kernel also with key positions or segment IDs (its only other mask is
+// the positional one).
+bool fwd_needs_bits(const ram_attn_desc* d, const ram_mask_src* m) {
+  return m && (m->dense || (alt_kernel(d) && (m->kv_pos || m->kv_seg || m->q_seg)));
 }
 
-// Words of tile bits per kernel tile (block_q rows of block_kv / 32 words).
-constexpr int64_t kTileWords = (int64_t)ram::kBlockQ * (ram::kBlockKV / 32);
+// Workgroups of the bf16 D = 128 kernel one launch should have: two per CU (256 CUs).
+constexpr int64_t kAltFill = 512;
+
+// Whether the one-launch ring splits each row of q tiles' visits over two workgroups: when its
+// rows give fewer workgroups than CUs, two halves of the ring run side by side and their
+// results are merged afterwards (this changes the merge order, so the result differs from
+// chunk-by-chunk calls in rounding).
+bool ring_split_shape(const ram_attn_desc* d, int32_t n_chunks) {
+  return alt_kernel(d) && n_chunks >= 2 && (int64_t)d->B * d->H * cdiv(d->Sq, ram::kAltRows) < kAltFill;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Words of tile bits per backward mask tile (block_q rows of block_kv / 32 words).
+constexpr int64_t kBwdTileWords = (int64_t)ram::kBlockQ * (ram::kBlockKV / 32);
+
 RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits) {
   RingLayout L{};
-  const int64_t nQb = cdiv(d->Sq, ram::kBlockQ), nKb = cdiv(d->Skv, ram::kBlockKV);
+  const int bq = ram::fwd_block_q(d->dtype, d->D);
+  const int64_t nQb = cdiv(d->Sq, bq), nKb = cdiv(d->Skv, ram::kBlockKV);
   const int64_t tiles = (int64_t)n_chunks * d->B * nQb * nKb;
   const int64_t rows = (int64_t)n_chunks * d->B * nQb;
   size_t off = 0;
@@ -278,7 +295,7 @@ RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits)
   L.col_off = off;
   off += align256((size_t)tiles * sizeof(int32_t));
   L.bits_off = off;
-  if (with_bits) off += align256((size_t)tiles * kTileWords * sizeof(uint32_t));
+  if (with_bits) off += align256((size_t)tiles * bq * (ram::kBlockKV / 32) * sizeof(uint32_t));
   const bool split = ring_split_shape(d, n_chunks);
   L.acc2_off = off;
   if (split) off += align256((size_t)d->B * d->Sq * d->H * d->D * sizeof(float));
@@ -320,7 +337,7 @@ BwdLayout bwd_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits) {
   take(L.cls_off, (size_t)tiles);
   take(L.cnt_off, (size_t)n_chunks * d->B * nQb * sizeof(int32_t));
   take(L.col_off, (size_t)tiles * sizeof(int32_t));
-  take(L.bits_off, with_bits ? (size_t)tiles * kTileWords * sizeof(uint32_t) : 0);
+  take(L.bits_off, with_bits ? (size_t)tiles * kBwdTileWords * sizeof(uint32_t) : 0);
   take(L.ccnt_off, (size_t)n_chunks * d->B * nKb * sizeof(int32_t));
   take(L.ridx_off, (size_t)tiles * sizeof(int32_t));
   // one chunk's partial dk / dv per head split (reused by every chunk)
@@ -349,6 +366,15 @@ ram_status ram_kernel_tile(int32_t dtype, int32_t D, int32_t* block_q, int32_t* 
   if (!block_q || !block_kv) return fail(RAM_ERR_INVALID, "null output pointer");
   if (dtype != RAM_F32 && dtype != RAM_BF16) return fail(RAM_ERR_UNSUPPORTED, "dtype %d", dtype);
   if (D != 64 && D != 128) return fail(RAM_ERR_UNSUPPORTED, "head dim D=%d (built: 64, 128)", D);
+  *block_q = ram::fwd_block_q(dtype, D);
+  *block_kv = ram::kBlockKV;
+  return ok();
+}
+
+ram_status ram_bwd_kernel_tile(int32_t dtype, int32_t D, int32_t* block_q, int32_t* block_kv) {
+  if (!block_q || !block_kv) return fail(RAM_ERR_INVALID, "null output pointer");
+  if (dtype != RAM_F32 && dtype != RAM_BF16) return fail(RAM_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (D != 64 && D != 128) return fail(RAM_ERR_UNSUPPORTED, "head dim D=%d (built: 64, 128)", D);
   *block_q = ram::kBlockQ;
   *block_kv = ram::kBlockKV;
   return ok();
@@ -356,7 +382,7 @@ ram_status ram_kernel_tile(int32_t dtype, int32_t D, int32_t* block_q, int32_t* 
 
 ram_status build_block_mask(const ram_attn_desc* desc, const ram_mask_src* src, const ram_block_mask* out,
                             hipStream_t stream) {
-  RAM_TRY(check_desc(desc, false, false));
+  RAM_TRY(check_desc(desc, kMaskTile, false));
   RAM_TRY(check_src(src, desc, desc->Skv, 0, desc->Skv));
   RAM_TRY(check_mask_arrays(out, desc, false));
   RAM_TRY(check_col_lists(out, desc, false));
@@ -374,10 +400,14 @@ ram_status build_block_mask(const ram_attn_desc* desc, const ram_mask_src* src, 
 ram_status attn_fwd_chunk(const ram_attn_desc* desc, const void* q, const void* k, const void* v,
                           const ram_mask_src* src, const ram_block_mask* mask, const float* sinks, int32_t mode,
                           float* out, float* lse, hipStream_t stream) {
-  RAM_TRY(check_desc(desc, true, true));
+  RAM_TRY(check_desc(desc, kFwdTile, true));
   RAM_TRY(check_kv_stride(desc, desc->Skv));
   RAM_TRY(check_src(src, desc, desc->Skv, 0, desc->Skv));
-  RAM_TRY(check_mask_arrays(mask, desc, src->dense != nullptr));
+  const bool need_bits = fwd_needs_bits(desc, src);
+  if (need_bits && !mask->bits && cdiv(desc->Skv, desc->block_kv) > 0 && !src->dense)
+    return fail(RAM_ERR_INVALID, "with key positions or segment IDs this kernel masks PARTIAL tiles from their bits: "
+                                 "build the block mask with bits");
+  RAM_TRY(check_mask_arrays(mask, desc, need_bits));
   if (mode != RAM_OUT_WRITE && mode != RAM_OUT_MERGE) return fail(RAM_ERR_INVALID, "mode %d", mode);
   if (desc->B == 0 || desc->Sq == 0) return ok();
   RAM_TRY(check_tensor(q, "q"));
@@ -388,8 +418,16 @@ ram_status attn_fwd_chunk(const ram_attn_desc* desc, const void* q, const void* 
   RAM_TRY(check_tensor(out, "out"));
   if (!lse || !aligned(lse, 4)) return fail(RAM_ERR_INVALID, "lse null or misaligned");
   if (sinks && !aligned(sinks, 4)) return fail(RAM_ERR_INVALID, "sinks misaligned");
-  ram::AttnParams p = attn_params(desc, q, k, v, src, mask, sinks, mode, out, lse);
-  hipError_t e = ram::launch_attn(p, desc->dtype, stream);
+  ram::AttnParams p = attn_params(desc, q, k, v, src, mask, sinks, mode, out, lse, desc->block_q);
+  hipError_t e;
+  if (alt_kernel(desc)) {
+    p.n_chunks = 1;
+    p.ring_shard = -1;
+    if (!need_bits) p.mask_bits = nullptr;
+    e = ram::launch_attn_alt(p, nullptr, stream);
+  } else {
+    e = ram::launch_attn(p, desc->dtype, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "attn_fwd_chunk launch");
   return ok();
 }
@@ -414,9 +452,9 @@ size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, co
       (desc->D != 64 && desc->D != 128))
     return 0;
   ram_attn_desc dt = *desc;
-  dt.block_q = ram::kBlockQ;
+  dt.block_q = ram::fwd_block_q(desc->dtype, desc->D);
   dt.block_kv = ram::kBlockKV;
-  return ring_layout(&dt, n_chunks, src && src->dense).total;
+  return ring_layout(&dt, n_chunks, fwd_needs_bits(&dt, src)).total;
 }
 
 ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32_t q_shard, const void* q,
@@ -425,10 +463,10 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
                               hipStream_t stream) {
   if (!desc) return fail(RAM_ERR_INVALID, "desc is null");
   ram_attn_desc dt = *desc;  // the ring builds its own masks at the kernel tile
-  dt.block_q = ram::kBlockQ;
+  dt.block_q = ram::fwd_block_q(desc->dtype, desc->D);
   dt.block_kv = ram::kBlockKV;
   desc = &dt;
-  RAM_TRY(check_desc(desc, true, true));
+  RAM_TRY(check_desc(desc, kFwdTile, true));
   if (n_chunks < 1) return fail(RAM_ERR_INVALID, "n_chunks=%d must be >= 1", n_chunks);
   if (q_shard < -1 || q_shard >= n_chunks)
     return fail(RAM_ERR_INVALID, "q_shard=%d outside [-1, %d)", q_shard, n_chunks);
@@ -448,7 +486,7 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   RAM_TRY(check_tensor(out, "out"));
   if (!lse || !aligned(lse, 4)) return fail(RAM_ERR_INVALID, "lse null or misaligned");
   if (sinks && !aligned(sinks, 4)) return fail(RAM_ERR_INVALID, "sinks misaligned");
-  const bool with_bits = src->dense != nullptr;
+  const bool with_bits = fwd_needs_bits(desc, src);
   const RingLayout L = ring_layout(desc, n_chunks, with_bits);
   if (!workspace || !aligned(workspace, 256))
     return fail(RAM_ERR_WORKSPACE, "workspace null or not 256-byte aligned");
@@ -460,7 +498,8 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
                     reinterpret_cast<int32_t*>(ws + L.col_off),
                     with_bits ? reinterpret_cast<uint32_t*>(ws + L.bits_off) : nullptr};
   float* acc = desc->dtype == RAM_BF16 ? reinterpret_cast<float*>(ws + L.acc_off) : static_cast<float*>(out);
-  const int64_t nQb = cdiv(desc->Sq, ram::kBlockQ), nKb = cdiv(desc->Skv, ram::kBlockKV);
+  const int64_t nQb = cdiv(desc->Sq, desc->block_q), nKb = cdiv(desc->Skv, ram::kBlockKV);
+  const int64_t tile_words = (int64_t)desc->block_q * (ram::kBlockKV / 32);
   const int64_t kv_full_stride = desc->kv_stride_b ? desc->kv_stride_b : kv_total * desc->Hkv * desc->D;
   const int64_t kvm_full = src->kv_meta_stride_b ? src->kv_meta_stride_b : kv_total;
   const int32_t q_base = (int32_t)(src->q_pos_base + q_extra);
@@ -478,41 +517,38 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   if (e != hipSuccess) return hip_fail(e, "ring block mask launch");
 
   const int64_t esz = desc->dtype == RAM_BF16 ? 2 : 4;
-  {
-    // The whole ring as one launch where the kernel supports it: every visit
-    // runs exactly as a per-chunk launch would (same tiles, epilogue and merge).
+  if (alt_kernel(desc)) {
+    // The whole ring as one launch: a workgroup visits every chunk in ring order, each visit
+    // exactly a chunk call's work (same tiles, epilogue and merge).
     ram_attn_desc dc = *desc;
     dc.kv_stride_b = kv_full_stride;
     ram_mask_src sc = *src;
     sc.q_pos_base = q_base;
     sc.kv_meta_stride_b = kvm_full;
-    ram::AttnParams p = attn_params(&dc, q, k_all, v_all, &sc, &bm, sinks, RAM_OUT_WRITE, acc, lse);
-    if (ram::attn_ring_fused(p, desc->dtype)) {
-      p.n_chunks = n_chunks;
-      p.ring_shard = q_shard;
-      p.kv_chunk_elems = (int64_t)desc->Skv * desc->Hkv * desc->D;
-      p.mask_chunk_tiles = (int64_t)desc->B * nQb * nKb;
-      p.mask_chunk_rows = (int64_t)desc->B * nQb;
-      const char* no_split = getenv("RAM_RING_SPLIT");
-      const bool split = ring_split_shape(desc, n_chunks) && !(no_split && strcmp(no_split, "0") == 0);
-      float* acc2 = reinterpret_cast<float*>(ws + L.acc2_off);
-      float* lse2 = reinterpret_cast<float*>(ws + L.lse2_off);
-      const ram::RingSplit halves{acc2, lse2};
-      if (!split) p.out_final = out;   // bf16: the last visit writes the result
-      if (g_ev_start && (e = hipEventRecord(g_ev_start, stream)) != hipSuccess) return hip_fail(e, "event record");
-      e = ram::launch_attn_ring(p, split ? &halves : nullptr, stream);
-      if (e != hipSuccess) return hip_fail(e, "ring launch");
-      if (g_ev_stop && (e = hipEventRecord(g_ev_stop, stream)) != hipSuccess) return hip_fail(e, "event record");
-      if (split) {
-        // the second half's running result merged into the first's, then the bf16 result
-        e = ram::launch_merge(desc->B, desc->Sq, desc->H, desc->D, acc, lse, acc2, lse2, stream);
-        if (e == hipSuccess) e = ram::launch_cast_bf16(acc, out, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
-        if (e != hipSuccess) return hip_fail(e, "split ring merge launch");
-      }
-      return ok();
+    ram::AttnParams p = attn_params(&dc, q, k_all, v_all, &sc, &bm, sinks, RAM_OUT_WRITE, acc, lse, desc->block_q);
+    p.n_chunks = n_chunks;
+    p.ring_shard = q_shard;
+    p.kv_chunk_elems = (int64_t)desc->Skv * desc->Hkv * desc->D;
+    p.mask_chunk_tiles = (int64_t)desc->B * nQb * nKb;
+    p.mask_chunk_rows = (int64_t)desc->B * nQb;
+    const bool split = ring_split_shape(desc, n_chunks);
+    float* acc2 = reinterpret_cast<float*>(ws + L.acc2_off);
+    float* lse2 = reinterpret_cast<float*>(ws + L.lse2_off);
+    const ram::RingSplit halves{acc2, lse2};
+    if (!split) p.out_final = out;   // the last visit writes the bf16 result
+    if (g_ev_start && (e = hipEventRecord(g_ev_start, stream)) != hipSuccess) return hip_fail(e, "event record");
+    e = ram::launch_attn_alt(p, split ? &halves : nullptr, stream);
+    if (e != hipSuccess) return hip_fail(e, "ring launch");
+    if (g_ev_stop && (e = hipEventRecord(g_ev_stop, stream)) != hipSuccess) return hip_fail(e, "event record");
+    if (split) {
+      // the second half's running result merged into the first's, then the bf16 result
+      e = ram::launch_merge(desc->B, desc->Sq, desc->H, desc->D, acc, lse, acc2, lse2, stream);
+      if (e == hipSuccess) e = ram::launch_cast_bf16(acc, out, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
+      if (e != hipSuccess) return hip_fail(e, "split ring merge launch");
     }
+    return ok();
   }
-  bool final_fused = false;
+  // The four-wave kernels: one launch per chunk, in ring order.
   if (g_ev_start && (e = hipEventRecord(g_ev_start, stream)) != hipSuccess) return hip_fail(e, "event record");
   for (int t = 0; t < n_chunks; ++t) {
     const int c = q_shard >= 0 ? ((q_shard - t) % n_chunks + n_chunks) % n_chunks : t;
@@ -526,24 +562,17 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
     sc.kv_pos_base = src->kv_pos_base + c * desc->Skv;
     const int64_t tiles_c = (int64_t)c * desc->B * nQb * nKb;
     const ram_block_mask bc{bm.tile_class + tiles_c, bm.row_cnt + (int64_t)c * desc->B * nQb,
-                            bm.col_idx + tiles_c, with_bits ? bm.bits + tiles_c * kTileWords : nullptr};
+                            bm.col_idx + tiles_c, with_bits ? bm.bits + tiles_c * tile_words : nullptr};
     const char* kc = static_cast<const char*>(k_all) + (int64_t)c * desc->Skv * desc->Hkv * desc->D * esz;
     const char* vc = static_cast<const char*>(v_all) + (int64_t)c * desc->Skv * desc->Hkv * desc->D * esz;
     ram::AttnParams p = attn_params(&dc, q, kc, vc, &sc, &bc, t == 0 ? sinks : nullptr,
-                                    t == 0 ? RAM_OUT_WRITE : RAM_OUT_MERGE, acc, lse);
-    // the last visit writes the bf16 result itself when its kernel can
-    if (t == n_chunks - 1 && desc->dtype == RAM_BF16 && ram::attn_writes_final(p, desc->dtype)) {
-      p.out_final = out;
-      final_fused = true;
-    }
+                                    t == 0 ? RAM_OUT_WRITE : RAM_OUT_MERGE, acc, lse, desc->block_q);
+    // the last visit writes the bf16 result itself
+    if (t == n_chunks - 1 && desc->dtype == RAM_BF16) p.out_final = out;
     e = ram::launch_attn(p, desc->dtype, stream);
     if (e != hipSuccess) return hip_fail(e, "ring chunk launch");
   }
   if (g_ev_stop && (e = hipEventRecord(g_ev_stop, stream)) != hipSuccess) return hip_fail(e, "event record");
-  if (desc->dtype == RAM_BF16 && !final_fused) {
-    e = ram::launch_cast_bf16(acc, out, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
-    if (e != hipSuccess) return hip_fail(e, "final cast launch");
-  }
   return ok();
 }
 
@@ -575,7 +604,7 @@ ram_status attn_bwd_chunk(const ram_attn_desc* desc, const void* q, const void* 
                           const void* dout, const float* lse, const float* delta, const ram_mask_src* src,
                           const ram_block_mask* mask, int32_t dq_mode, float* dq, float* dk, float* dv,
                           hipStream_t stream) {
-  RAM_TRY(check_desc(desc, true, true));
+  RAM_TRY(check_desc(desc, kBwdTile, true));
   RAM_TRY(check_bwd_support(desc));
   RAM_TRY(check_kv_stride(desc, desc->Skv));
   RAM_TRY(check_src(src, desc, desc->Skv, 0, desc->Skv));
@@ -598,7 +627,7 @@ ram_status attn_bwd_chunk(const ram_attn_desc* desc, const void* q, const void* 
   }
   if (desc->Sq == 0 && desc->Skv == 0) return ok();
   ram::BwdParams bp{};
-  bp.a = attn_params(desc, q, k, v, src, mask, nullptr, 0, nullptr, const_cast<float*>(lse));
+  bp.a = attn_params(desc, q, k, v, src, mask, nullptr, 0, nullptr, const_cast<float*>(lse), ram::kBlockQ);
   bp.dout = dout;
   bp.delta = delta;
   bp.dq = dq;
@@ -635,7 +664,7 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   dt.block_q = ram::kBlockQ;
   dt.block_kv = ram::kBlockKV;
   desc = &dt;
-  RAM_TRY(check_desc(desc, true, true));
+  RAM_TRY(check_desc(desc, kBwdTile, true));
   RAM_TRY(check_bwd_support(desc));
   if (n_chunks < 1) return fail(RAM_ERR_INVALID, "n_chunks=%d must be >= 1", n_chunks);
   if (q_shard < -1 || q_shard >= n_chunks)
@@ -716,13 +745,13 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
     sc.kv_pos_base = src->kv_pos_base + c * desc->Skv;
     const int64_t tiles_c = (int64_t)c * desc->B * nQb * nKb;
     const ram_block_mask bc{bm.tile_class + tiles_c, bm.row_cnt + (int64_t)c * desc->B * nQb, bm.col_idx + tiles_c,
-                            with_bits ? bm.bits + tiles_c * kTileWords : nullptr,
+                            with_bits ? bm.bits + tiles_c * kBwdTileWords : nullptr,
                             bm.col_cnt + (int64_t)c * desc->B * nKb, bm.row_idx + tiles_c};
     const int64_t kv_off = (int64_t)c * desc->Skv * desc->Hkv * desc->D;
     ram::BwdParams bp{};
     bp.a = attn_params(&dc, q, static_cast<const char*>(k_all) + kv_off * esz,
                        static_cast<const char*>(v_all) + kv_off * esz, &sc, &bc, nullptr, 0, nullptr,
-                       const_cast<float*>(lse));
+                       const_cast<float*>(lse), ram::kBlockQ);
     bp.dout = dout;
     bp.delta = delta;
     bp.dq = dq_acc;

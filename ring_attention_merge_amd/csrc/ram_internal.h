@@ -7,9 +7,12 @@
 
 namespace ram {
 
-// Attention kernel tile: 4 waves of 32 query rows, 64 keys per step.
+// Mask tiles the kernels walk: 128 query rows by 64 keys (the forward kernels, the backward).
 constexpr int kBlockQ = 128;
+constexpr int kAltRows = 128;
 constexpr int kBlockKV = 64;
+// Query rows of the forward mask tile for a dtype code (1 = bf16) and head dim.
+constexpr int fwd_block_q(int dtype, int D) { return (dtype == 1 && D == 128) ? kAltRows : kBlockQ; }
 // Largest number of kv tiles in one block-mask row (classes are staged in LDS).
 constexpr int kMaxMaskCols = 8192;
 constexpr int kMaxMaskTile = 512;
@@ -30,19 +33,20 @@ struct AttnParams {
   const int32_t* kv_pos;
   const int32_t* q_seg;
   const int32_t* kv_seg;
-  const uint32_t* mask_bits;  // bits of the PARTIAL tiles (128 rows x 2 words per tile) or null
+  const uint32_t* mask_bits;  // bits of the PARTIAL tiles (tile rows x 2 words per tile) or null
   int64_t q_stride_b, kv_stride_b;   // elements
   int64_t qm_stride_b, kvm_stride_b; // elements of the position / segment arrays
   int32_t q_pos_base, kv_pos_base;
   int32_t B, Sq, Skv, H, Hkv, D;
-  int32_t nQb, nKb;
+  int32_t nQb, nKb;       // mask tiles of the call
+  int32_t tile_words;     // bit words per mask tile: rows x (block_kv / 32)
   float scale_log2;   // scale * log2(e)
   float cap_k2;       // 2 * scale * log2(e) / softcap   (soft cap on)
   float cap_log2;     // softcap * log2(e)               (soft cap on)
   int32_t softcap_on;
   int32_t causal;
   int32_t mode;       // 0 write, 1 merge
-  // One launch for a whole ring (launch_attn_ring): k, v, the mask arrays and
+  // One launch for a whole ring (launch_attn_alt): k, v, the mask arrays and
   // kv_pos / kv_seg / kv_pos_base describe chunk 0, chunk c lies kv_chunk_elems
   // elements (k, v), mask_chunk_tiles tiles and mask_chunk_rows rows (masks)
   // and c*Skv keys (kv arrays, kv_pos_base) further. Visit t takes chunk
@@ -55,7 +59,7 @@ struct AttnParams {
   int64_t mask_chunk_rows;
 };
 
-// A split ring (launch_attn_ring with this given): each q tile row's visits go to two
+// A split ring (launch_attn_alt with this given): each q tile row's visits go to two
 // workgroups, visits [0, h) and [h, n_chunks) with h = (n_chunks + 1) / 2; the second writes
 // its own running result to out2 / lse2 (its first visit in `mode`), to be merged into
 // out / lse afterwards.
@@ -102,10 +106,8 @@ struct BwdParams {
   int64_t part_stride;     // elements
 };
 
+// float32 (D = 64 / 128) and bf16 D = 64: the four-wave kernels, one chunk per launch.
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s);
-// Whether a ring of this kernel choice runs as one launch (launch_attn_ring).
-bool attn_ring_fused(const AttnParams& p, int dtype);
-hipError_t launch_attn_ring(const AttnParams& p, const RingSplit* split, hipStream_t s);
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s);       // bf16, D = 64 / 128: dq, then dk / dv
 hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s);   // float32, D = 64 / 128
 // delta (and dsinks) from out and dout in `dtype` (RAM_BF16 / RAM_F32 codes)
@@ -113,12 +115,10 @@ hipError_t launch_bwd_prep(int dtype, int B, int Sq, int H, int D, const void* o
                            const float* lse, const float* sinks, float* delta, float* dsinks, hipStream_t s);
 hipError_t launch_col_lists(const MaskParams& p, int n_chunks, int32_t* col_cnt, int32_t* row_idx,
                             hipStream_t s);
-// Whether the kernel launch_attn would pick for p honours p.out_final.
-bool attn_writes_final(const AttnParams& p, int dtype);
-hipError_t launch_attn_pp(const AttnParams& p, hipStream_t s);   // bf16, 8-wave ping-pong
-hipError_t launch_attn_w64(const AttnParams& p, hipStream_t s);  // bf16, D = 128, 64 rows per wave
-hipError_t launch_attn_g8(const AttnParams& p, hipStream_t s);   // bf16, D = 128, 8 waves, 3-stage DMA
-hipError_t launch_attn_g8p(const AttnParams& p, hipStream_t s);  // bf16, D = 128, 8 waves, pipelined
+// bf16, D = 128, 256-row mask tiles: one visit per chunk (n_chunks = 1 for a single chunk).
+// Kernels without kv positions, kv segments or tile bits mask PARTIAL tiles by positions;
+// with any of them, PARTIAL tiles are masked from mask_bits, which must then be set.
+hipError_t launch_attn_alt(const AttnParams& p, const RingSplit* split, hipStream_t s);
 hipError_t launch_block_mask(const MaskParams& p, int n_chunks, hipStream_t s);
 hipError_t launch_merge(int B, int Sq, int H, int D, float* out_acc, float* lse_acc,
                         const float* out_blk, const float* lse_blk, hipStream_t s);

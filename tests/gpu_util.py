@@ -44,8 +44,9 @@ def run_ring(wl, dev="cuda", poison=True):
     if poison:
         out.fill_(float("nan"))
         lse.fill_(float("nan"))
-    ws = torch.empty(max(1, ram.ring_attn_workspace_bytes(d, wl.n_chunks)), dtype=torch.uint8, device=dev)
-    ram.ring_attn_fwd_1gpu(d, wl.n_chunks, wl.q_shard, q, k, v, mask_src(wl, dev), sinks, out, lse, ws)
+    src = mask_src(wl, dev)
+    ws = torch.empty(max(1, ram.ring_attn_workspace_bytes(d, wl.n_chunks, src)), dtype=torch.uint8, device=dev)
+    ram.ring_attn_fwd_1gpu(d, wl.n_chunks, wl.q_shard, q, k, v, src, sinks, out, lse, ws)
     torch.cuda.synchronize()
     return out.float().cpu(), lse.cpu()
 
@@ -78,3 +79,44 @@ def compare(out, lse, ref_out, ref_lse, dtype, what, rows=None):
     assert err_o <= OUT_TOL[dtype], f"{what}: out err {err_o}"
     assert err_l <= LSE_TOL, f"{what}: lse err {err_l}"
     return err_o, err_l
+
+
+def ring_by_chunks(d, n, r, q, k, v, src, sinks, dev="cuda"):
+    """The ring of ring_attn_fwd_1gpu(d, n, r, ...) as a loop of attn_fwd_chunk calls in ring
+    order (WRITE on the first visit with the sinks, MERGE after), each chunk's block mask built
+    on its own; returns the float32 (out, lse) on the device. Key positions, segment IDs and the
+    dense-mask columns travel with their chunk."""
+    C = d.Skv
+    bq, bk = ram.kernel_tile(d.dtype, d.D)
+    kv_total = n * C
+    out = torch.empty(d.B, d.Sq, d.H, d.D, dtype=torch.float32, device=dev)
+    lse = torch.empty(d.B, d.H, d.Sq, dtype=torch.float32, device=dev)
+    q_base = src.q_pos_base + (r * d.Sq if r >= 0 else 0)
+    kvm = src.kv_meta_stride_b or kv_total
+    step = src.dense_chunk_step
+    ld = src.dense_ld or (C + (n - 1) * step)
+    esz = k.element_size()
+    for t in range(n):
+        c = (r - t) % n if r >= 0 else t
+        dc = ram.Desc(**{**d.__dict__, "block_q": bq, "block_kv": bk, "kv_stride_b": kv_total * d.Hkv * d.D})
+        sc = ram.MaskSrc(q_pos=src.q_pos, q_pos_base=q_base, q_seg=src.q_seg, q_meta_stride_b=src.q_meta_stride_b,
+                         kv_pos=None if src.kv_pos is None else src.kv_pos.view(-1)[c * C:],
+                         kv_pos_base=src.kv_pos_base + c * C,
+                         kv_seg=None if src.kv_seg is None else src.kv_seg.view(-1)[c * C:],
+                         kv_meta_stride_b=kvm,
+                         dense=None if src.dense is None else src.dense.view(-1)[c * step:],
+                         dense_ld=ld if src.dense is not None else 0)
+        bm = ram.alloc_block_mask(dc, device=dev, with_bits=True)
+        ram.build_block_mask(dc, sc, bm)
+        kc = k.view(-1)[c * C * d.Hkv * d.D:]
+        vc = v.view(-1)[c * C * d.Hkv * d.D:]
+        ram.attn_fwd_chunk(dc, q, kc, vc, sc, bm, sinks if t == 0 else None, 0 if t == 0 else 1, out, lse)
+    assert esz in (2, 4)
+    return out, lse
+
+
+def ring_splits(d, n) -> bool:
+    """Whether ring_attn_fwd_1gpu splits each row of q tiles' visits over two workgroups (the
+    bf16 D = 128 kernel with fewer rows than compute units)."""
+    bq, _ = ram.kernel_tile(d.dtype, d.D)
+    return d.dtype == ram.RAM_BF16 and d.D == 128 and n >= 2 and d.B * d.H * (-(-d.Sq // bq)) < 512

@@ -34,7 +34,7 @@ def _header_functions():
 def test_every_header_symbol_is_exported(lib):
     names = _header_functions()
     assert set(names) == {"build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
-                          "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_last_error", "attn_bwd_prep",
+                          "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_bwd_kernel_tile", "ram_last_error", "attn_bwd_prep",
                           "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes",
                           "ram_mfma_probe", "ram_set_kernel_events"}, names
     for n in names:
@@ -62,6 +62,11 @@ def _desc(**kw):
     return ram.Desc(**d).c()
 
 
+def _fdesc(**kw):
+    """A descriptor at the forward tile of bf16 with D = 128 (128 x 64)."""
+    return _desc(**kw)
+
+
 def _src(**kw):
     return _lib.c_mask_src(kw.get("q_pos", 0), kw.get("kv_pos", 0), kw.get("q_pos_base", 0),
                            kw.get("kv_pos_base", 0), kw.get("q_seg", 0), kw.get("kv_seg", 0),
@@ -87,7 +92,11 @@ def _err(lib):
 
 def test_kernel_tile(lib):
     assert ram.kernel_tile(ram.RAM_BF16, 128) == (128, 64)
+    assert ram.kernel_tile(ram.RAM_BF16, 64) == (128, 64)
     assert ram.kernel_tile(ram.RAM_F32, 64) == (128, 64)
+    assert ram.kernel_tile(ram.RAM_F32, 128) == (128, 64)
+    assert ram.bwd_kernel_tile(ram.RAM_BF16, 128) == (128, 64)
+    assert ram.bwd_kernel_tile(ram.RAM_F32, 64) == (128, 64)
     with pytest.raises(ram.RamError) as e:
         ram.kernel_tile(ram.RAM_BF16, 96)
     assert e.value.status == _lib.RAM_ERR_UNSUPPORTED
@@ -113,12 +122,12 @@ def test_kernel_tile(lib):
     (dict(kv_stride_b=256 * 2 * 128 + 3), _lib.RAM_ERR_INVALID, "kv_stride_b"),
 ])
 def test_chunk_desc_validation(lib, kw, status, msg):
-    assert _chunk(lib, _desc(**kw)) == status
+    assert _chunk(lib, _fdesc(**kw)) == status
     assert msg in _err(lib)
 
 
 def test_chunk_pointer_validation(lib):
-    d = _desc()
+    d = _fdesc()
     assert _chunk(lib, d, q=0) == _lib.RAM_ERR_INVALID and "q is null" in _err(lib)
     assert _chunk(lib, d, k=FAKE + 2) == _lib.RAM_ERR_UNSUPPORTED and "aligned" in _err(lib)
     assert _chunk(lib, d, out=0) == _lib.RAM_ERR_INVALID
@@ -136,7 +145,7 @@ def test_chunk_pointer_validation(lib):
 
 
 def test_dense_mask_validation(lib):
-    d = _desc()
+    d = _fdesc()
     # a dense mask is applied through the tile bits: attention needs them
     assert _chunk(lib, d, src=_src(dense=FAKE2)) == _lib.RAM_ERR_INVALID and "tile bits" in _err(lib)
     assert _chunk(lib, d, src=_src(dense=FAKE2), bm=_bm(bits=FAKE + 4)) == _lib.RAM_ERR_INVALID
@@ -153,18 +162,25 @@ def test_dense_mask_validation(lib):
     assert _ring(lib, dr, 4, 3, src=src) == _lib.RAM_ERR_INVALID and "dense_ld" in _err(lib)
     src = _src(dense=FAKE2, dense_chunk_step=0, dense_ld=511)
     assert _ring(lib, dr, 4, 3, src=src) == _lib.RAM_ERR_INVALID
-    # with a dense mask the ring workspace also holds one 1 KiB bit tile per kernel tile
+    # with a dense mask the ring workspace also holds the bits of every 128 x 64 tile (1 KiB each);
+    # the bf16 D = 128 kernel needs them with key positions or segment IDs as well
     base = lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, None)
     plain = lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src()))
     dense = lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src(dense=FAKE2)))
     assert base == plain and dense == base + 4 * 4 * 8 * 1024
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src(kv_pos=FAKE2))) == dense
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src(q_pos=FAKE2))) == base
+    d64 = _desc(B=1, Sq=512, Skv=512, H=4, Hkv=4, D=64)
+    b64 = lib.ring_attn_workspace_bytes(ctypes.byref(d64), 4, None)
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(d64), 4, ctypes.byref(_src(kv_pos=FAKE2))) == b64
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(d64), 4, ctypes.byref(_src(dense=FAKE2))) == b64 + 4 * 4 * 8 * 1024
     assert _ring(lib, dr, 4, 3, src=_src(dense=FAKE2), ws_bytes=dense - 1) == _lib.RAM_ERR_WORKSPACE
 
 
 def test_empty_inputs_are_noops(lib):
     # B = 0 or Sq = 0: valid, nothing to do, nothing launched (works without a GPU)
-    assert _chunk(lib, _desc(B=0), q=0, out=0, lse=0) == _lib.RAM_OK
-    assert _chunk(lib, _desc(Sq=0), q=0, out=0, lse=0) == _lib.RAM_OK
+    assert _chunk(lib, _fdesc(B=0), q=0, out=0, lse=0) == _lib.RAM_OK
+    assert _chunk(lib, _fdesc(Sq=0), q=0, out=0, lse=0) == _lib.RAM_OK
     d = _desc(Sq=0)
     assert lib.build_block_mask(ctypes.byref(d), ctypes.byref(_src()), ctypes.byref(_bm()), 0) == _lib.RAM_OK
     assert lib.lse_merge(0, 5, 2, 128, 0, 0, 0, 0, 0) == _lib.RAM_OK
@@ -198,22 +214,24 @@ def _ring(lib, d, n, r, ws=FAKE, ws_bytes=1 << 40, src=None, out=FAKE, q=FAKE):
 
 
 def test_ring_validation_and_workspace(lib):
+    al = lambda x: (x + 255) // 256 * 256
     d = _desc(B=1, Sq=4096, Skv=4096, H=8, Hkv=8)
     need = lib.ring_attn_workspace_bytes(ctypes.byref(d), 4, None)
     acc = 4096 * 8 * 128 * 4
-    tiles = 4 * 32 * 64
+    tiles = 4 * 32 * 64   # 4 chunks x 128-row tiles x 64-key tiles
     # 32 q tiles x 8 heads = 256 workgroups, under two per CU: room for the second half of a
     # split ring (its float32 result and lse)
     split = acc + 8 * 4096 * 4
-    expect = acc + ((tiles + 255) // 256) * 256 + ((4 * 32 * 4 + 255) // 256) * 256 + tiles * 4 + split
+    expect = acc + al(tiles) + al(4 * 32 * 4) + tiles * 4 + split
     assert need == expect
+    # float32: accumulated in out, no split
     d32 = _desc(B=1, Sq=4096, Skv=4096, H=8, Hkv=8, dtype=ram.RAM_F32)
-    assert lib.ring_attn_workspace_bytes(ctypes.byref(d32), 4, None) == need - acc - split   # fp32: in out, no split
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(d32), 4, None) == need - acc - split
     # 64 q tiles x 8 heads = 512 workgroups: no split
     d2 = _desc(B=2, Sq=4096, Skv=4096, H=8, Hkv=8)
     tiles2 = 4 * 64 * 64
     assert lib.ring_attn_workspace_bytes(ctypes.byref(d2), 4, None) == (
-        2 * acc + ((tiles2 + 255) // 256) * 256 + ((4 * 64 * 4 + 255) // 256) * 256 + tiles2 * 4)
+        2 * acc + al(tiles2) + al(4 * 64 * 4) + tiles2 * 4)
     assert lib.ring_attn_workspace_bytes(ctypes.byref(d), 0, None) == 0
     assert _ring(lib, d, 0, -1) == _lib.RAM_ERR_INVALID
     assert _ring(lib, d, 4, 4) == _lib.RAM_ERR_INVALID and "q_shard" in _err(lib)

@@ -207,7 +207,7 @@ def test_chunk_backward_add_mode():
     qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV)
     out = torch.empty_like(qd)
     lse = torch.empty(d.B, d.H, d.Sq, device=DEV)
-    ws = torch.empty(ram.ring_attn_workspace_bytes(d, 1), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(ram.ring_attn_workspace_bytes(d, 1, src), dtype=torch.uint8, device=DEV)
     ram.ring_attn_fwd_1gpu(d, 1, -1, qd, kd, vd, src, None, out, lse, ws)
     bm = ram.alloc_block_mask(d, with_cols=True)
     ram.build_block_mask(d, src, bm)

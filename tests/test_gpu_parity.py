@@ -15,17 +15,10 @@ import torch
 import oracle
 import ring_attention_merge_amd as ram
 from ring_attention_merge_amd import workloads as wl
-from gpu_util import compare, mask_src, oracle_ref, run_ring, say
+from gpu_util import compare, mask_src, oracle_ref, ring_by_chunks, ring_desc, ring_splits, run_ring, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-
-
-@pytest.fixture(params=["4wave", "staged", "pingpong", "wide", "g8", "g8p"])
-def variant(request, monkeypatch):
-    """Force one of the bf16 attention kernel layouts (fp32 inputs always use the fp32 kernel)."""
-    monkeypatch.setenv("RAM_ATTN_KERNEL", request.param)
-    return request.param
 
 
 def _i32(a):
@@ -104,7 +97,7 @@ def _chunk_ref(q, k, v, scale, qp, kp, qs, ks, causal, cap, sinks):
 def _run_chunk(d, q, k, v, src, sinks, mode, out, lse):
     bq, bk = ram.kernel_tile(d.dtype, d.D)
     dm = ram.Desc(**{**d.__dict__, "block_q": bq, "block_kv": bk})
-    bm = ram.alloc_block_mask(dm)
+    bm = ram.alloc_block_mask(dm, with_bits=True)
     ram.build_block_mask(dm, src, bm)
     ram.attn_fwd_chunk(dm, q, k, v, src, bm, sinks, mode, out, lse)
 
@@ -158,9 +151,9 @@ def _make_chunk_inputs(name):
 
 
 @pytest.mark.parametrize("name", sorted(CHUNK_CASES))
-def test_chunk_write(name, variant):
+def test_chunk_write(name):
     dt, d, q, k, v, sinks, src, (qp, kp, qs, ks, causal, cap) = _make_chunk_inputs(name)
-    say(f"attn_fwd_chunk WRITE {name} [{variant}]")
+    say(f"attn_fwd_chunk WRITE {name}")
     out = torch.full((d.B, d.Sq, d.H, d.D), float("nan"), device=DEV)
     lse = torch.full((d.B, d.H, d.Sq), float("nan"), device=DEV)
     _run_chunk(d, q.to(DEV), k.to(DEV), v.to(DEV), src, None if sinks is None else sinks.to(DEV), 0, out, lse)
@@ -171,10 +164,10 @@ def test_chunk_write(name, variant):
 
 @pytest.mark.parametrize("name", ["bf16_d128_causal_gqa", "bf16_d128_docs_cap_sinks", "f32_d128_segs_cap_sinks",
                                   "bf16_d128_empty_rows", "f32_d64_ragged_gqa"])
-def test_chunk_merge_three_chunks(name, variant):
+def test_chunk_merge_three_chunks(name):
     """WRITE on the first chunk (with sinks), MERGE on the next two == attention over all keys."""
     dt, d, q, k, v, sinks, src, (qp, kp, qs, ks, causal, cap) = _make_chunk_inputs(name)
-    say(f"attn_fwd_chunk WRITE+MERGE {name} [{variant}]")
+    say(f"attn_fwd_chunk WRITE+MERGE {name}")
     Skv = d.Skv
     cuts = [0, Skv // 3, (2 * Skv) // 3, Skv]
     out = torch.full((d.B, d.Sq, d.H, d.D), float("nan"), device=DEV)
@@ -241,41 +234,59 @@ SMALL_RING = {
 
 
 @pytest.mark.parametrize("name", sorted(SMALL_RING))
-def test_ring_small(name, variant):
+def test_ring_small(name):
     w = SMALL_RING[name]()
-    say(f"ring_attn_fwd_1gpu {name} [{variant}]: B={w.B} H={w.H}/{w.Hkv} Sq={w.Sq} chunks={w.n_chunks}x{w.chunk}")
+    say(f"ring_attn_fwd_1gpu {name}: B={w.B} H={w.H}/{w.Hkv} Sq={w.Sq} chunks={w.n_chunks}x{w.chunk}")
     out, lse = run_ring(w)
     ro, rl = oracle_ref(w)
     compare(out.numpy(), lse.numpy(), ro, rl, w.dtype, name)
 
 
-@pytest.mark.parametrize("name", ["ring_shard3of4", "ring_shard1of3_ragged", "docs_small", "gqa_cap_sinks_small"])
-def test_ring_one_launch_equals_chunk_launches(name, monkeypatch):
-    """The one-launch ring runs every chunk visit as a chunk launch does (same tiles, same merge):
-    with one workgroup per row (RAM_RING_SPLIT=0) its results are bit-identical to the
-    chunk-by-chunk ring."""
-    w = SMALL_RING[name]()
-    say(f"ring one launch vs chunk launches {name}")
-    monkeypatch.setenv("RAM_RING_SPLIT", "0")
+# Rings with enough rows of q tiles for one workgroup per row (no split of the visits).
+UNSPLIT_RING = {
+    "shard1of4_h64": lambda: wl.make("u1", B=1, H=64, Hkv=8, Sq=1024, chunk=512, n_chunks=4, D=128, q_shard=1,
+                                     seed=31),
+    "docs_h64": lambda: wl.make("u2", B=2, H=64, Hkv=16, Sq=2048, chunk=512, n_chunks=4, D=128,
+                                docs=(64, 700, 0.05), seed=32),
+    "cap_sinks_h64": lambda: wl.make("u3", B=1, H=64, Hkv=4, Sq=1024, chunk=384, n_chunks=3, D=128, softcap=30.0,
+                                     with_sinks=True, seed=33),
+}
+
+
+@pytest.mark.parametrize("name", sorted(UNSPLIT_RING))
+def test_ring_one_launch_equals_chunk_launches(name):
+    """The one-launch ring runs every chunk visit as a chunk call does (same tiles, same merge):
+    with one workgroup per row its results are bit-identical to attn_fwd_chunk calls in ring
+    order (the last merge's float32 output rounded to bf16)."""
+    w = UNSPLIT_RING[name]()
+    d = ring_desc(w)
+    assert not ring_splits(d, w.n_chunks)
+    say(f"ring one launch vs chunk calls {name}")
     o1, l1 = run_ring(w)
-    monkeypatch.setenv("RAM_RING", "per_chunk")
-    o2, l2 = run_ring(w)
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    sinks = None if w.sinks is None else w.sinks.to(DEV)
+    o2, l2 = ring_by_chunks(d, w.n_chunks, w.q_shard, w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), mask_src(w), sinks)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2.to(torch.bfloat16).float().cpu())
+    assert torch.equal(l1, l2.cpu())
 
 
 @pytest.mark.parametrize("name", ["ring_shard3of4", "gqa_cap_sinks_small"])
-def test_ring_split_matches_unsplit(name, monkeypatch):
-    """These small rings have fewer than two workgroups per CU, so the one-launch ring splits
-    each row's visits over two workgroups and merges the halves by their lse: the same result
-    up to the rounding of the merge order (the oracle tests check both against the float64
-    reference). Both halves of these rings have keys to add, so the results differ in rounding."""
+def test_ring_split_matches_chunk_launches(name):
+    """These small rings have fewer rows of q tiles than compute units, so the one-launch ring
+    splits each row's visits over two workgroups and merges the halves by their lse: the same
+    result as chunk calls in ring order up to the rounding of the merge order (the oracle tests
+    check both against the float64 reference)."""
     w = SMALL_RING[name]()
-    say(f"split ring vs one workgroup per row {name}")
+    d = ring_desc(w)
+    assert ring_splits(d, w.n_chunks)
+    say(f"split ring vs chunk calls {name}")
     o1, l1 = run_ring(w)
-    monkeypatch.setenv("RAM_RING_SPLIT", "0")
-    o2, l2 = run_ring(w)
-    assert not (torch.equal(o1, o2) and torch.equal(l1, l2)), "the split did not engage"
-    torch.testing.assert_close(o1.float(), o2.float(), rtol=0, atol=2e-2)
+    sinks = None if w.sinks is None else w.sinks.to(DEV)
+    o2, l2 = ring_by_chunks(d, w.n_chunks, w.q_shard, w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), mask_src(w), sinks)
+    torch.cuda.synchronize()
+    o2 = o2.to(torch.bfloat16).float().cpu()
+    l2 = l2.cpu()
+    torch.testing.assert_close(o1, o2, rtol=0, atol=2e-2)
     fin = torch.isfinite(l2)
     assert torch.equal(fin, torch.isfinite(l1))
     torch.testing.assert_close(l1[fin], l2[fin], rtol=0, atol=1e-4)
@@ -293,9 +304,9 @@ def test_c1_full():
 _C2_REF = {}
 
 
-def test_c2_full_all_rows(variant):
+def test_c2_full_all_rows():
     w = wl.c2_ring_shard()
-    say(f"C2 {w.name} [{variant}]")
+    say(f"C2 {w.name}")
     out, lse = run_ring(w)
     if "ref" not in _C2_REF:
         _C2_REF["ref"] = oracle_ref(w)
@@ -324,7 +335,7 @@ def test_c4_full_sampled(Hkv):
     compare(out.numpy(), lse.numpy(), ro, rl, "bf16", w.name, rows=rows)
 
 
-def test_c5_full_sampled(variant):
+def test_c5_full_sampled():
     w = wl.c5_long_causal()
     rows = wl.sampled_rows(w.Sq, w.chunk, n=256, seed=1005)
     say(f"C5 {w.name}: {len(rows)} sampled rows")
