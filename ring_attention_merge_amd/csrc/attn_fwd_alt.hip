@@ -53,6 +53,8 @@ template <bool BITS>
 constexpr int alt_stage_bytes() {
   return 2 * kAltTile + (BITS ? kAltBitsBytes : 0);
 }
+// the stages and the longest tile list (one 8-byte record per tile) fit a CU's 160 KiB of LDS
+static_assert(kAltStages * alt_stage_bytes<true>() + 8 * kMaxMaskCols <= 160 * 1024, "LDS budget");
 
 // LDS DMA issued from inline assembly: 16 bytes per lane (4 for dma4) from the buffer at byte
 // offset `voff` into LDS at m0 + 16 * lane (4 * lane). The compiler does not see these writes to
@@ -153,15 +155,19 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
   constexpr int NS = kAltStages;
   constexpr int SB = alt_stage_bytes<BITS>();
   constexpr int NDMA = 2 * kDmaPerTile + (BITS ? 1 : 0);   // DMA instructions per wave and step
-  // NS stages of SB bytes, then the visit's tile list with each tile's class (kb | class << 16),
-  // staged once per visit so that the loop reads it from LDS instead of waiting on scalar
-  // loads (p.nKb words).
+  // NS stages of SB bytes, then the visit's tile list (AltTile records, p.nKb of them), staged
+  // once per visit so that the loop reads it from LDS instead of waiting on scalar loads
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  uint32_t* tinfo = reinterpret_cast<uint32_t*>(smem + NS * SB);
+  uint2* tinfo = reinterpret_cast<uint2*>(smem + NS * SB);
 
   // SPLIT: two workgroups per row, each with half the visits (an instantiation of its own)
   int b, h, qb, sp = 0;
   if (!decode_work(p, b, h, qb, SPLIT ? 2 : 1, SPLIT ? &sp : nullptr)) return;
+  // wave-uniform: keep them (and the addresses made from them) in scalar registers
+  b = __builtin_amdgcn_readfirstlane(b);
+  h = __builtin_amdgcn_readfirstlane(h);
+  qb = __builtin_amdgcn_readfirstlane(qb);
+  sp = __builtin_amdgcn_readfirstlane(sp);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -187,6 +193,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
   const int qpos = p.q_pos ? p.q_pos[(int64_t)b * p.qm_stride_b + qrow_c] : p.q_pos_base + q_row;
 
   const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;   // bytes between key rows
+  const uint32_t half_bytes = kAltKeys * row_bytes;      // second step of a 64-key tile
   // DMA: wave w fills rows 4*(w + kAltWaves*i) .. +3 of a step tile (i < kDmaPerTile); lane l
   // writes physical 16-byte chunk l & 15 of row 4*(w + kAltWaves*i) + (l >> 4), i.e. 1 KiB of
   // consecutive LDS bytes per instruction.
@@ -249,61 +256,75 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
       lim = (int)max<int64_t>(-1, min<int64_t>(p.Skv, reach));
     }
 
-    // K / V of this (batch, kv head) in this chunk, as wave-uniform byte addresses
-    const uint64_t kbase = (uint64_t)reinterpret_cast<uintptr_t>(
-        reinterpret_cast<const __bf16*>(pc.k) + (int64_t)b * p.kv_stride_b + g * D);
-    const uint64_t vbase = (uint64_t)reinterpret_cast<uintptr_t>(
-        reinterpret_cast<const __bf16*>(pc.v) + (int64_t)b * p.kv_stride_b + g * D);
-    // DMA of step s (32 keys of the tile in info word `inf`) into stage st: this wave's rows of K
-    // and V and (BITS) its 32 rows' bit words of the tile when it is PARTIAL.
-    auto dma_step = [&](int s, int st, uint32_t inf) {
-      const int kb = (int)(inf & 0xffffu);
-      const int k0 = kb * kBlockKV + (s & 1) * kAltKeys;
-      const uint32_t bytes = (uint32_t)max(0, min(p.Skv - k0, kAltKeys)) * row_bytes;
-      const uint64_t off = (uint64_t)(uint32_t)k0 * row_bytes;
-      const auto kr = tile_rsrc(reinterpret_cast<const void*>(kbase + off), bytes);
-      const auto vr = tile_rsrc(reinterpret_cast<const void*>(vbase + off), bytes);
+    // K / V of this (batch, kv head) in this chunk: one buffer resource each, spanning the
+    // chunk's Skv key rows, so that rows past the chunk end read as zeros (their scores are
+    // masked). Byte offsets into it fit 32 bits (the host checks Skv * row_bytes).
+    const auto krs = tile_rsrc(reinterpret_cast<const __bf16*>(pc.k) + (int64_t)b * p.kv_stride_b + g * D,
+                               (uint32_t)p.Skv * row_bytes);
+    const auto vrs = tile_rsrc(reinterpret_cast<const __bf16*>(pc.v) + (int64_t)b * p.kv_stride_b + g * D,
+                               (uint32_t)p.Skv * row_bytes);
+    // DMA of step s (parity PAR, tile record `tr`) into stage st: this wave's rows of K and V and
+    // (BITS) its 32 rows' bit words of the tile when it is PARTIAL.
+    auto dma_step = [&](auto PAR_, int st, uint2 tr) {
+      constexpr int PAR = decltype(PAR_)::value;
+      const uint32_t soff = (tr.x & ~63u) + (PAR ? half_bytes : 0u);
       const uint32_t sb = lds0 + st * SB;
 #pragma unroll
       for (int i = 0; i < kDmaPerTile; ++i) {
-        dma16(kr, sb + 4 * (w + kAltWaves * i) * 256, koff[i]);
-        dma16(vr, sb + kAltTile + 4 * (w + kAltWaves * i) * 256, voff[i]);
+        dma16(krs, sb + 4 * (w + kAltWaves * i) * 256, koff[i] + soff);
+        dma16(vrs, sb + kAltTile + 4 * (w + kAltWaves * i) * 256, voff[i] + soff);
       }
       if constexpr (BITS) {
-        const bool partial = (inf >> 16) == 1u;
+        const int kb = (int)(tr.y >> 6);
+        const bool partial = ((tr.x >> (2 * PAR)) & 3u) == 2u;
         const uint32_t* words = pc.mask_bits + ((mrow * p.nKb + kb) * kAltRows + w * 32) * 2;
         const auto br = tile_rsrc(words, partial ? 256u : 0u);
         dma4(br, sb + 2 * kAltTile + w * 256, (uint32_t)lane * 4);
       }
     };
-    // mask kind and lane-relative key limit of step s
-    auto step_info = [&](int s, uint32_t inf, int& kind, int& thr) {
-      const int kb = (int)(inf & 0xffffu);
-      const int c = (int)(inf >> 16);
-      const int k0 = kb * kBlockKV + (s & 1) * kAltKeys;
-      const bool cut = k0 + kAltKeys > p.Skv;
-      kind = (BITS && c == 1) ? 2 : ((c != 2 || cut) ? 1 : 0);
-      thr = lim - (k0 + 4 * lg);
+    // mask kind (0 none, 1 key limit, 2 bits) and lane-relative key limit of a step of parity PAR
+    auto step_info = [&](auto PAR_, uint2 tr, int& kind, int& thr) {
+      constexpr int PAR = decltype(PAR_)::value;
+      kind = (int)((tr.x >> (2 * PAR)) & 3u);
+      thr = lim - ((int)tr.y + PAR * kAltKeys + 4 * lg);
     };
-    // info word of step s (clamped to the list), read from LDS
+    // tile record of step s (clamped to the list), read from LDS
     auto info = [&](int s) { return tinfo[min(s >> 1, cnt - 1)]; };
+    auto uniform = [](uint2 t) {
+      return make_uint2(__builtin_amdgcn_readfirstlane(t.x), __builtin_amdgcn_readfirstlane(t.y));
+    };
 
-    // Every wave is done with the previous visit's stages and list; then this visit's list.
+    // Every wave is done with the previous visit's stages and list; then this visit's list. A
+    // tile's record: x = byte offset of its first key row, with the mask kinds of its two steps
+    // in bits 0-1 and 2-3 (the offset is a multiple of 64); y = its first key.
     __syncthreads();
     for (int i = tid; i < cnt; i += kAltThreads) {
       const int kb = cols[i];
-      tinfo[i] = (uint32_t)kb | ((uint32_t)cls[kb] << 16);
+      const int c = cls[kb];
+      const int k0 = kb * kBlockKV;
+      uint32_t kinds = 0;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const bool cut = k0 + (hf + 1) * kAltKeys > p.Skv;
+        const uint32_t kind = (BITS && c == 1) ? 2u : ((c != 2 || cut) ? 1u : 0u);
+        kinds |= kind << (2 * hf);
+      }
+      tinfo[i] = make_uint2((uint32_t)k0 * row_bytes | kinds, (uint32_t)k0);
     }
     __syncthreads();
     if (n > 0) {
       const int pre = min(NS, n);
       {
-        uint32_t inf[(NS + 1) / 2];
+        uint2 inf[(NS + 1) / 2];
 #pragma unroll
-        for (int e = 0; e < (NS + 1) / 2; ++e) inf[e] = __builtin_amdgcn_readfirstlane(tinfo[min(e, cnt - 1)]);
+        for (int e = 0; e < (NS + 1) / 2; ++e) inf[e] = uniform(tinfo[min(e, cnt - 1)]);
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-          if (s < pre) dma_step(s, s, inf[s >> 1]);
+        for (int s = 0; s < NS; ++s) {
+          if (s < pre) {
+            if (s & 1) dma_step(std::integral_constant<int, 1>{}, s, inf[s >> 1]);
+            else dma_step(std::integral_constant<int, 0>{}, s, inf[s >> 1]);
+          }
+        }
       }
       // steps 0 and 1 must have landed (n is even, so n >= 2)
       wait_vm_steps<NDMA, NS - 2>(pre - 2);
@@ -321,7 +342,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         S2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(lds0 + k_rd[ds]), qf[ds], S2[0], 0, 0, 0);
       {
         int kind, thr;
-        step_info(0, __builtin_amdgcn_readfirstlane(info(0)), kind, thr);
+        step_info(std::integral_constant<int, 0>{}, uniform(info(0)), kind, thr);
         step_cap<CAP>(S2[0], p);
         step_mask<BITS>(S2[0], kind, thr, BITS ? lds_b32(lds0 + b_rd) : 0u, lg);
         float m_new, alpha;
@@ -341,11 +362,14 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
       for (int ds = 0; ds < 8; ++ds) kf[ds] = lds_b128(kad[ds] + SB);
 #pragma unroll
       for (int i = 0; i < 8; ++i) vf[i] = lds_v_operand(vad[i & 3] + (i >> 2) * 4096);
-      uint32_t inf_dma = info(NS), inf_msk = info(1);
+      uint2 inf_dma = info(NS), inf_msk = info(1);
 
-      // Step j (stage j % NS == JS): products, barrier, loads.
-      auto step = [&](auto JS_, int j) {
+      // Step j (stage j % NS == JS): products, barrier, loads. STEADY: a step at least 2 NS - 1
+      // steps before the end, which issues its DMA and reads the next operands unconditionally
+      // and waits for a fixed number of DMA steps.
+      auto step = [&](auto JS_, auto STEADY_, int j) {
         constexpr int JS = decltype(JS_)::value;
+        constexpr bool STEADY = decltype(STEADY_)::value;
         constexpr int CUR = JS & 1, NXT = CUR ^ 1;
         constexpr int ST1 = (JS + 1) % NS, ST2 = (JS + 2) % NS;
         f32x16& Sc = S2[CUR];
@@ -407,18 +431,19 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         // min(n, j+NS)-1, the tile's being at most NS-3 steps before the newest; the barrier
         // makes every wave's share visible and shows that every wave is done with step j's
         // stage (its last reads fed this step's products)
-        if (j + 2 < n) wait_vm_steps<NDMA, NS - 3>(min(n, j + NS) - 1 - (j + 2));
+        if (STEADY) wait_vm<NDMA * (NS - 3)>();
+        else if (j + 2 < n) wait_vm_steps<NDMA, NS - 3>(min(n, j + NS) - 1 - (j + 2));
         barrier();
 
         // ---------------------------------------------------------------- loads of step j
         // The DMA into step j's stage, the operand and list reads for the next products, then
         // the mask and row max of S(j+1) and, when a row's max grew by more than 2^8, the
         // rescale of O and l.
-        const bool has_next = j + 1 < n;
-        const uint32_t inf_d = __builtin_amdgcn_readfirstlane(inf_dma);
-        const uint32_t inf_m = __builtin_amdgcn_readfirstlane(inf_msk);
-        if (j + NS < n) dma_step(j + NS, JS, inf_d);
-        if (j + 2 < n) {
+        const bool has_next = STEADY || j + 1 < n;
+        const uint2 inf_d = uniform(inf_dma);
+        const uint2 inf_m = uniform(inf_msk);
+        if (STEADY || j + NS < n) dma_step(std::integral_constant<int, JS & 1>{}, JS, inf_d);
+        if (STEADY || j + 2 < n) {
 #pragma unroll
           for (int ds = 0; ds < 8; ++ds) kf[ds] = lds_b128(kad[ds] + ST2 * SB);
         }
@@ -428,7 +453,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
           inf_dma = info(j + 1 + NS);
           inf_msk = info(j + 2);
           int kind, thr;
-          step_info(j + 1, inf_m, kind, thr);
+          step_info(std::integral_constant<int, NXT>{}, inf_m, kind, thr);
           step_cap<CAP>(Sn, p);
           step_mask<BITS>(Sn, kind, thr, BITS ? lds_b32(lds0 + ST1 * SB + b_rd + 4 * ((JS + 1) & 1)) : 0u, lg);
           float m_new, alpha;
@@ -443,13 +468,26 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         }
       };
       static_assert(NS == 4, "the step loop is unrolled by the ring depth");
-      // n is even: groups of four steps, then possibly two
-      for (int j = 0; j < n; j += 4) {
-        step(std::integral_constant<int, 0>{}, j);
-        step(std::integral_constant<int, 1>{}, j + 1);
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;
+      using Steady = std::true_type;
+      using Tail = std::false_type;
+      int j = 0;
+      for (; j + 2 * NS <= n; j += NS) {
+        step(I0{}, Steady{}, j);
+        step(I1{}, Steady{}, j + 1);
+        step(I2{}, Steady{}, j + 2);
+        step(I3{}, Steady{}, j + 3);
+      }
+      // the last 2 NS - 1 steps or fewer; n is even: groups of four steps, then possibly two
+      for (; j < n; j += NS) {
+        step(I0{}, Tail{}, j);
+        step(I1{}, Tail{}, j + 1);
         if (j + 2 >= n) break;
-        step(std::integral_constant<int, 2>{}, j + 2);
-        step(std::integral_constant<int, 3>{}, j + 3);
+        step(I2{}, Tail{}, j + 2);
+        step(I3{}, Tail{}, j + 3);
       }
     }
     epilogue<4>(O, m_ref, l_acc, pc, b, h, q_row, lg);
@@ -460,7 +498,7 @@ template <bool CAP, bool BITS, bool SPLIT>
 hipError_t launch_alt(const AttnParams& p, const RingSplit& rs, hipStream_t s) {
   const int S = SPLIT ? 2 : 1;
   const int64_t T = (int64_t)p.B * p.H * p.nQb * S;
-  const size_t lds = (size_t)kAltStages * alt_stage_bytes<BITS>() + 4 * (size_t)max(1, p.nKb);
+  const size_t lds = (size_t)kAltStages * alt_stage_bytes<BITS>() + sizeof(uint2) * (size_t)max(1, p.nKb);
   hipLaunchKernelGGL((attn_fwd_bf16_alt<CAP, BITS, SPLIT>), dim3((unsigned)(8 * ((T + 7) / 8))), dim3(kAltThreads),
                      lds, s, p, rs);
   return hipGetLastError();

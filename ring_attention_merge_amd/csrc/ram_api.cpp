@@ -86,6 +86,10 @@ ram_status check_desc(const ram_attn_desc* d, TileUse tile, bool need_heads) {
   }
   if (cdiv(d->Skv, d->block_kv) > ram::kMaxMaskCols)
     return fail(RAM_ERR_UNSUPPORTED, "more than %d kv tiles in a row", ram::kMaxMaskCols);
+  // the bf16 D = 128 forward reads a chunk's key rows (of one batch) through 32-bit byte offsets
+  if (tile == kFwdTile && need_heads && d->dtype == RAM_BF16 && d->D == 128 &&
+      (int64_t)d->Skv * d->Hkv * d->D * 2 > (int64_t)UINT32_MAX)
+    return fail(RAM_ERR_UNSUPPORTED, "one KV chunk of Skv=%d x Hkv=%d rows spans 4 GiB or more", d->Skv, d->Hkv);
   return RAM_OK;
 }
 

@@ -242,6 +242,10 @@ def test_ring_validation_and_workspace(lib):
     assert _ring(lib, d, 4, 3, src=_src(q_pos_base=2**31 - 5000)) == _lib.RAM_ERR_INVALID  # 3*Sq overflows
     assert _ring(lib, d, 4, 3, src=_src(kv_meta_stride_b=4096)) == _lib.RAM_ERR_INVALID    # must span 4 chunks
     assert _ring(lib, d, 4, 3, out=0) == _lib.RAM_ERR_INVALID
+    # the bf16 D = 128 forward addresses one chunk's key rows with 32-bit byte offsets
+    big = _desc(B=1, Sq=4096, Skv=524288, H=32, Hkv=32)
+    assert _ring(lib, big, 2, 1) == _lib.RAM_ERR_UNSUPPORTED and "4 GiB" in _err(lib)
+    assert _chunk(lib, _fdesc(Skv=524288, H=32, Hkv=32, block_q=128)) == _lib.RAM_ERR_UNSUPPORTED
     # the ring picks its own tile: a caller's block_q/block_kv are ignored
     dt = _desc(B=1, Sq=4096, Skv=4096, H=8, Hkv=8, block_q=32, block_kv=32)
     assert lib.ring_attn_workspace_bytes(ctypes.byref(dt), 4, None) == need
