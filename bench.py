@@ -10,12 +10,17 @@ long-context causal attention: B=1, H=32 query heads over Hkv=8 KV heads,
 ~ N(0,1) and v ~ U(-1,1). Inputs are resident in HBM before timing starts.
 
 value: effective TFLOP/s = 4*D*H*(non-EMPTY 128x128 tiles over all chunks)*128^2
-       divided by the step time.
-roofline: the attention chunk kernel alone, timed launch by launch with HIP
-       events on the stream it runs on; achieved = its effective FLOPs per
-       launch / its mean launch time, against the dense bf16 MFMA peak.
+       divided by the step time. The tiles are counted here in numpy from the
+       workload's positions, segment IDs and dense mask (not by the library);
+       the line also says whether the library's own count agrees.
+roofline: the attention kernel alone: the library records HIP events on the
+       step's stream around its one attention launch in every timed step (the
+       same window as the step time); achieved = its effective FLOPs / the
+       median launch time, against the dense bf16 MFMA peak.
 cpu_baseline: the float64 oracle on a bounded sample of query rows of the
-       same workload (all heads, all keys), in pair FLOPs per second.
+       same workload (all heads, all keys), in pair FLOPs per second, with the
+       host's cores and CPU model, and the full-size time extrapolated from
+       the sample (labelled as such).
 
 --backward times ring_attn_bwd_1gpu instead (out and lse from one forward
 call before timing, dout ~ N(0,1) in bf16): value = 2.5x the forward's
@@ -54,9 +59,19 @@ BWD_FLOP_FACTOR = 2.5
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 REF_TILE = 128                  # fixed reference tiling for effective FLOPs
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
-def ring_kernel_name(cap: bool, bits: bool) -> str:
-    """The ring kernel instantiation a launch runs (soft cap, stored mask bits)."""
-    return f"attn_fwd_bf16_dma_ring<{str(bool(cap)).lower()}, {str(bool(bits)).lower()}>"
+KERNEL = "attn_fwd_bf16_alt"    # the bf16 D = 128 forward kernel the ring launches
+
+
+def ring_kernel_name(cap: bool, bits: bool, split: bool) -> str:
+    """The kernel instantiation a ring launch runs (soft cap, stored mask bits, split ring)."""
+    f = lambda x: str(bool(x)).lower()
+    return f"{KERNEL}<{f(cap)}, {f(bits)}, {f(split)}>"
+
+
+def ring_splits(w, bq: int) -> bool:
+    """Whether the ring runs each row of q tiles as two half rings (the library does so when its
+    rows of 128-row tiles give fewer than 512 workgroups)."""
+    return w.n_chunks >= 2 and w.B * w.H * -(-w.Sq // bq) < 512
 
 
 def log(*a):
@@ -107,7 +122,51 @@ def tile_counts(w, desc, dev, tile_q, tile_kv, dense=None):
     return counts
 
 
-KERNEL_SOURCES = ("attn_fwd.hip", "attn_common.h")   # what the default chunk kernel is built from
+KERNEL_SOURCES = ("attn_fwd_alt.hip", "attn_common.h")   # what the ring's attention kernel is built from
+
+
+def independent_tiles(w, T: int = REF_TILE):
+    """Non-EMPTY TxT tiles per chunk, counted here in numpy from the workload's own arrays (no
+    library code): a tile is non-EMPTY when one of its (query, key) pairs is allowed, i.e. the
+    key's position is not past the query's (causal), both carry the same segment ID and it is not
+    the padding ID, and the dense mask keeps the pair."""
+    qp, kp = w.positions()
+    nK = -(-w.chunk // T)
+    rows = 8 * T
+    counts = []
+    for c in range(w.n_chunks):
+        ks = slice(c * w.chunk, (c + 1) * w.chunk)
+        n = 0
+        for b in range(w.B):
+            for r0 in range(0, w.Sq, rows):
+                r1 = min(w.Sq, r0 + rows)
+                ok = np.ones((r1 - r0, w.chunk), dtype=bool)
+                if w.causal:
+                    ok &= kp[b, ks][None, :] <= qp[b, r0:r1][:, None]
+                if w.q_seg is not None:
+                    qs = w.q_seg[b, r0:r1]
+                    ok &= (qs[:, None] == w.kv_seg[b, ks][None, :]) & (qs != wl.PAD_SEGMENT_ID)[:, None]
+                if w.dense is not None:
+                    ok &= w.dense[r0:r1, ks] != 0
+                rq = -(-(r1 - r0) // T) * T
+                full = np.zeros((rq, nK * T), dtype=bool)
+                full[: r1 - r0, : w.chunk] = ok
+                n += int(full.reshape(rq // T, T, nK, T).any(axis=(1, 3)).sum())
+        counts.append(n)
+    return counts
+
+
+def host_cpu():
+    """Cores this process may run on and the CPU model (from /proc/cpuinfo)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return len(os.sched_getaffinity(0)), model
 
 
 def kernel_source_hash() -> str:
@@ -145,7 +204,7 @@ def recorded_traffic_bwd(workload: str):
 def recorded_traffic(workload: str):
     """HBM bytes per ring launch from the committed counter summary, if it was taken
     on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_bf16_dma_ring_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{KERNEL}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -166,7 +225,7 @@ def recorded_mfma_busy(workload: str):
     """Fraction of the ring launch's cycles with the matrix cores busy, from the committed counter
     summary (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x GRBM_GUI_ACTIVE per XCD), if it was taken
     on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_bf16_dma_ring_{workload}_counters.md")
+    path = os.path.join(ROOT, "profiles", f"{KERNEL}_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -299,9 +358,14 @@ def cpu_baseline_bwd(w, n_rows):
         pairs += int(ok.sum())
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     flops = 10.0 * w.D * w.H * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    cores, model = host_cpu()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "cpu_model": model,
+            "blas_threads": int(threads), "kind": "oracle",
             "sample": f"{n_rows} sampled of {w.Sq} query rows x all {w.H} heads x all {w.Skv} keys: float64 numpy "
-                      f"oracle backward (its forward included), {dt:.2f} s"}
+                      f"oracle backward (its forward included), {dt:.2f} s",
+            "sample_s": round(dt, 3), "extrapolated_full_s": round(dt * w.Sq / n_rows, 1),
+            "extrapolation": "sample time x Sq / sampled rows (the oracle computes whole score rows, so its "
+                             "time is linear in the rows); an estimate, not a measurement"}
 
 
 def mask_builder_rate(w, desc, dense, bq, bk, dev, stream, reps):
@@ -351,9 +415,14 @@ def cpu_baseline(w, n_rows: int):
         pairs += int(ok.sum())
     flops = 4.0 * w.D * w.H * pairs
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    cores, model = host_cpu()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "cpu_model": model,
+            "blas_threads": int(threads), "kind": "oracle",
             "sample": f"{len(rows)} of {w.Sq} query rows x all {w.H} heads x all {w.Skv} keys, float64 "
-                      f"numpy oracle (full score rows, BLAS dgemm), {dt:.2f} s"}
+                      f"numpy oracle (full score rows, BLAS dgemm), {dt:.2f} s",
+            "sample_s": round(dt, 3), "extrapolated_full_s": round(dt * w.Sq / len(rows), 1),
+            "extrapolation": "sample time x Sq / sampled rows (the oracle computes whole score rows, so its "
+                             "time is linear in the rows); an estimate, not a measurement"}
 
 
 def mfma_rates(dev, stream) -> dict:
@@ -416,10 +485,13 @@ def main():
     ws = torch.empty(ram.ring_attn_workspace_bytes(desc, w.n_chunks, src), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    ref_tiles = tile_counts(w, desc, dev, REF_TILE, REF_TILE, dense)
+    ref_tiles = independent_tiles(w)
+    lib_tiles = tile_counts(w, desc, dev, REF_TILE, REF_TILE, dense)
     eff_flops_chunk = [4.0 * w.D * w.H * n * REF_TILE * REF_TILE for n in ref_tiles]
     eff_flops = sum(eff_flops_chunk)
-    log(f"non-empty {REF_TILE}x{REF_TILE} tiles per chunk: {ref_tiles}; effective FLOPs {eff_flops:.4e}")
+    log(f"non-empty {REF_TILE}x{REF_TILE} tiles per chunk: {ref_tiles} (library: "
+        f"{'agrees' if lib_tiles == ref_tiles else lib_tiles}); effective FLOPs {eff_flops:.4e}")
+    tiles_info = {"nonempty_tiles_128": sum(ref_tiles), "library_count_agrees": lib_tiles == ref_tiles}
 
     def step():
         ram.ring_attn_fwd_1gpu(desc, w.n_chunks, w.q_shard, q, k, v, src, sinks, out, lse, ws, stream=stream)
@@ -427,50 +499,53 @@ def main():
     if args.backward:
         return backward(args, w, desc, q, k, v, src, sinks, out, lse, ws, stream, dense, eff_flops_chunk, step)
 
+    bq, bk = ram.kernel_tile(dcode, w.D)
+    alt = dcode == ram.RAM_BF16 and w.D == 128    # one attention launch per step; else one per chunk
+    launches = 1 if alt else w.n_chunks
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # The timed window: every step also has the library record HIP events on its stream right
+    # around the attention launch(es), so the kernel's time comes from the same steps.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(args.steps):
+    for a, b in evs:
+        ram.set_kernel_events(a, b, stream=stream)
         step()
     e1.record(stream)
+    ram.set_kernel_events()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     tflops = eff_flops / (ms * 1e-3) / 1e12
     log(f"step {ms:.3f} ms, {tflops:.1f} effective TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak)")
-
-    # Roofline of the dominant kernel: the ring's attention launch (one per step), timed with HIP
-    # events the library records on the step's stream right around it (ram_set_kernel_events).
-    bq, bk = ram.kernel_tile(dcode, w.D)
-    fused = os.environ.get("RAM_RING") != "per_chunk" and not os.environ.get("RAM_ATTN_KERNEL")
-    reps = max(1, args.steps // 2)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in evs:
-        ram.set_kernel_events(a, b, stream=stream)
-        step()
-    ram.set_kernel_events()
-    torch.cuda.synchronize()
-    kern_ms = sum(a.elapsed_time(b) for a, b in evs) / reps
-    launches = 1 if fused else w.n_chunks
+    kern = sorted(a.elapsed_time(b) for a, b in evs)
+    kern_ms = float(np.median(kern))
+    if kern_ms > ms:
+        log(f"warning: median kernel time {kern_ms:.3f} ms above the mean step time {ms:.3f} ms")
     achieved = eff_flops / (kern_ms * 1e-3) / 1e12
-    log(f"attention kernel {kern_ms:.3f} ms per step ({launches} launch(es)), {achieved:.1f} TFLOP/s")
+    log(f"attention kernel median {kern_ms:.3f} ms per step (min {kern[0]:.3f}, max {kern[-1]:.3f}; "
+        f"{launches} launch(es)), {achieved:.1f} TFLOP/s")
+    split = alt and ring_splits(w, bq)
+    bits = any(x is not None for x in (dense, w.kv_pos, w.q_seg, w.kv_seg))   # masked from stored bits
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": recorded_traffic(args.workload) if fused else None,
-                "kernel": ring_kernel_name(w.softcap, dense is not None) if fused else "per-chunk launches",
-                "launches_per_step": launches, "mean_launch_us": round(1e3 * kern_ms / launches, 2),
+                "traffic": recorded_traffic(args.workload) if alt else None,
+                "kernel": ring_kernel_name(w.softcap, bits, split) if alt else "per-chunk launches",
+                "launches_per_step": launches, "median_step_kernel_us": round(1e3 * kern_ms, 1),
+                "mean_launch_us": round(1e3 * kern_ms / launches, 2),
+                "timing": "HIP events around the attention launch in each of the timed steps; median",
                 "flops_per_launch_mean": eff_flops / launches}
     measured = mfma_rates(dev, stream)
     roofline["measured_peak_random"] = measured["random"]
     roofline["frac_of_measured_random"] = round(achieved / measured["random"], 4)
     # rocprofv3 counters of the same launch, recorded in profiles/ (null once the kernel changed)
-    roofline["mfma_busy"] = recorded_mfma_busy(args.workload) if fused else None
+    roofline["mfma_busy"] = recorded_mfma_busy(args.workload) if alt else None
     roofline["hbm_gbs"] = (round(roofline["traffic"] / (kern_ms * 1e-3 / launches) / 1e9, 1)
                            if roofline["traffic"] else None)
     log(f"MFMA probe: {measured['zeros']} TFLOP/s with zero operands, {measured['random']} with random ones")
-    builder = None if dense is None else mask_builder_rate(w, desc, dense, bq, bk, dev, stream, reps)
+    builder = None if dense is None else mask_builder_rate(w, desc, dense, bq, bk, dev, stream,
+                                                            max(1, args.steps // 2))
     if args.copy_calibration:
         copy_calibration(dev)
 
@@ -478,7 +553,8 @@ def main():
     if not args.no_cpu:
         log(f"timing the float64 oracle on {args.cpu_rows} sampled rows ...")
         cpu = cpu_baseline(w, args.cpu_rows)
-        log(f"oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+        log(f"oracle: {cpu['value'] * 1e3:.3f} GFLOP/s ({cpu['cores']} cores, {cpu['blas_threads']} BLAS "
+            f"threads, {cpu['cpu_model']}); full size extrapolated {cpu['extrapolated_full_s']} s")
 
     line = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -487,7 +563,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "Sq": w.Sq, "Skv": w.Skv,
                    "kv_chunks": w.n_chunks, "chunk": w.chunk, "D": w.D, "causal": w.causal,
                    "softcap": w.softcap, "sinks": w.sinks is not None, "q_shard": w.q_shard,
-                   "effective_flops": eff_flops},
+                   "effective_flops": eff_flops, **tiles_info},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,

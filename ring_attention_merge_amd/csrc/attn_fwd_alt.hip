@@ -378,6 +378,9 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         // S(j+1) = K(j+1) Q^T in fenced groups of one product and two exponentials of S(j), then
         // O^T += V(j)^T P(j)^T beside the bf16 packing. On the last step the first product runs
         // on stale operands and its result is not used.
+        // The products run at raised wave priority: with two workgroups per CU, the wave whose
+        // matrix products are ready issues first and the other fills the slots between them.
+        __builtin_amdgcn_s_setprio(1);
         Sn = f32x16{};
         {
           const float msub = (m_ref == neg_inf()) ? 0.0f : m_ref;
@@ -418,6 +421,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 + i], P[1], O[i], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
         {
           // row sum as a tree, in fp32 (bf16 weights would put up to 2^-9 into the lse of a row
           // with few keys)
