@@ -252,20 +252,24 @@ __device__ __forceinline__ void epilogue(const f32x16 (&O)[NDB], float m_ref, fl
     if (lg == 0) *lptr = lse_c;
     return;
   }
-  // merge (ring-splash _update_out_and_lse)
+  // merge (ring-splash _update_out_and_lse). The running row is read whole, before any store
+  // (one round trip to memory, not one per 16 bytes).
+  float4 run[NDB * 4];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      run[4 * db + i4] = *reinterpret_cast<const float4*>(orow + db * 32 + 8 * i4 + 4 * lg);
+  const float acc_lse = *lptr;
   if (lse_c == neg_inf()) {   // nothing attended in this chunk: identity
     if (p.out_final) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int col = db * 32 + 8 * i4 + 4 * lg;
-          store_bf16x4(p.out_final, row0 + col, *reinterpret_cast<const float4*>(orow + col));
-        }
+        for (int i4 = 0; i4 < 4; ++i4) store_bf16x4(p.out_final, row0 + db * 32 + 8 * i4 + 4 * lg, run[4 * db + i4]);
     }
     return;
   }
-  const float acc_lse = *lptr;
   float sig = 1.0f, new_lse = lse_c;
   if (acc_lse != neg_inf()) {
     const float x = lse_c - acc_lse;
@@ -278,7 +282,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&O)[NDB], float m_ref, fl
     for (int i4 = 0; i4 < 4; ++i4) {
       const int col = db * 32 + 8 * i4 + 4 * lg;
       float4* ptr = reinterpret_cast<float4*>(orow + col);
-      float4 a = (acc_lse == neg_inf()) ? make_float4(0.f, 0.f, 0.f, 0.f) : *ptr;
+      const float4 a = (acc_lse == neg_inf()) ? make_float4(0.f, 0.f, 0.f, 0.f) : run[4 * db + i4];
       float4 o;
       o.x = a.x - sig * (a.x - O[db][4 * i4 + 0] * inv);
       o.y = a.y - sig * (a.y - O[db][4 * i4 + 1] * inv);
