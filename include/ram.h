@@ -250,6 +250,28 @@ size_t ring_attn_bwd_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks
  * src may be NULL; a source whose forward needs tile bits needs room for them. */
 size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src);
 
+/* Where ring_attn_fwd_1gpu (ring_attn_fwd_masks) and ring_attn_bwd_1gpu
+ * (ring_attn_bwd_masks) keep, inside their workspace, the block masks they
+ * build for every chunk (at the tile their kernels walk), so that a caller can
+ * read them back after a call: byte offsets of
+ *   tile classes  uint8 [n_chunks][B][nQb][nKb] (RAM_TILE_*),
+ *   tile counts   int32 [n_chunks][B][nQb],
+ *   tile lists    int32 [n_chunks][B][nQb][nKb] (ascending, -1 padded),
+ *   tile bits     uint32 [n_chunks][B][nQb][nKb][tile_words] as in
+ *                 ram_block_mask, or -1 when the call stores none,
+ * chunk c being the chunk at index c of k_all (not the visit order). The mask
+ * of a chunk is what build_block_mask makes for that chunk's keys (see
+ * ring_attn_fwd_1gpu for their positions and dense-mask columns). Same
+ * arguments as the workspace-size calls; RAM_ERR_INVALID on bad input. */
+typedef struct ram_ring_masks {
+  int64_t cls_off, cnt_off, col_off, bits_off;
+  int32_t block_q, block_kv, nQb, nKb, tile_words;
+} ram_ring_masks;
+ram_status ring_attn_fwd_masks(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src,
+                               ram_ring_masks* out);
+ram_status ring_attn_bwd_masks(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src,
+                               ram_ring_masks* out);
+
 /* The tile (block_q, block_kv) the forward kernel of (dtype, D) walks: block
  * masks passed to attn_fwd_chunk must be built at this tile (256 x 64 for bf16
  * with D = 128, 128 x 64 otherwise). */

@@ -27,8 +27,8 @@ RAM_PAD_SEGMENT_ID = -1
 
 EXPORTS = ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
            "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_bwd_kernel_tile", "ram_last_error", "attn_bwd_prep",
-           "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes", "ram_mfma_probe",
-           "ram_set_kernel_events")
+           "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes", "ring_attn_fwd_masks",
+           "ring_attn_bwd_masks", "ram_mfma_probe", "ram_set_kernel_events")
 
 
 class RamError(RuntimeError):
@@ -44,6 +44,12 @@ class c_desc(ctypes.Structure):
                 ("kv_stride_b", ctypes.c_int64), ("scale", ctypes.c_float),
                 ("softcap", ctypes.c_float), ("causal", ctypes.c_int32),
                 ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32)]
+
+
+class c_ring_masks(ctypes.Structure):
+    _fields_ = [("cls_off", ctypes.c_int64), ("cnt_off", ctypes.c_int64), ("col_off", ctypes.c_int64),
+                ("bits_off", ctypes.c_int64), ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32),
+                ("nQb", ctypes.c_int32), ("nKb", ctypes.c_int32), ("tile_words", ctypes.c_int32)]
 
 
 class c_mask_src(ctypes.Structure):
@@ -91,6 +97,8 @@ def load(path: str = LIB_PATH):
     lib.ring_attn_bwd_1gpu.argtypes = [P(c_desc), i32, i32, vp, vp, vp, vp, f32p, vp, P(c_mask_src), f32p, vp,
                                        vp, vp, f32p, vp, ctypes.c_size_t, vp]
     lib.ring_attn_bwd_workspace_bytes.argtypes = [P(c_desc), i32, P(c_mask_src)]
+    lib.ring_attn_fwd_masks.argtypes = [P(c_desc), i32, P(c_mask_src), P(c_ring_masks)]
+    lib.ring_attn_bwd_masks.argtypes = [P(c_desc), i32, P(c_mask_src), P(c_ring_masks)]
     lib.ring_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ram_last_error.argtypes = []
     lib.ram_last_error.restype = ctypes.c_char_p
@@ -99,7 +107,7 @@ def load(path: str = LIB_PATH):
     for name in ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu", "ram_kernel_tile",
                  "ram_bwd_kernel_tile",
                  "attn_bwd_prep", "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ram_mfma_probe",
-                 "ram_set_kernel_events"):
+                 "ram_set_kernel_events", "ring_attn_fwd_masks", "ring_attn_bwd_masks"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -389,6 +397,28 @@ def ring_attn_bwd_workspace_bytes(desc: Desc, n_chunks: int, src: Optional[MaskS
         return int(load().ring_attn_bwd_workspace_bytes(ctypes.byref(cd), n_chunks, None))
     cs = c_mask_src(0, 0, 0, 0, 0, 0, 0, 0, _ptr(src.dense), src.dense_ld, src.dense_chunk_step)
     return int(load().ring_attn_bwd_workspace_bytes(ctypes.byref(cd), n_chunks, ctypes.byref(cs)))
+
+
+def _ring_masks(fn, desc: Desc, n_chunks: int, src: Optional[MaskSrc]) -> dict:
+    cd = desc.c()
+    cs = None if src is None else c_mask_src(_ptr(src.q_pos), _ptr(src.kv_pos), 0, 0, _ptr(src.q_seg),
+                                            _ptr(src.kv_seg), 0, 0, _ptr(src.dense), src.dense_ld,
+                                            src.dense_chunk_step)
+    m = c_ring_masks()
+    _check(fn(ctypes.byref(cd), n_chunks, None if cs is None else ctypes.byref(cs), ctypes.byref(m)))
+    return {f: getattr(m, f) for f, _ in c_ring_masks._fields_}
+
+
+def ring_attn_fwd_masks(desc: Desc, n_chunks: int, src: Optional[MaskSrc] = None) -> dict:
+    """ring_attn_fwd_masks: where ring_attn_fwd_1gpu's workspace holds each chunk's block mask
+    (byte offsets cls_off, cnt_off, col_off, bits_off (-1: none); block_q, block_kv, nQb, nKb,
+    tile_words)."""
+    return _ring_masks(load().ring_attn_fwd_masks, desc, n_chunks, src)
+
+
+def ring_attn_bwd_masks(desc: Desc, n_chunks: int, src: Optional[MaskSrc] = None) -> dict:
+    """ring_attn_bwd_masks: the same for ring_attn_bwd_1gpu's workspace."""
+    return _ring_masks(load().ring_attn_bwd_masks, desc, n_chunks, src)
 
 
 def ring_attn_bwd_1gpu(desc: Desc, n_chunks: int, q_shard: int, q, k_all, v_all, out, lse, dout, src: MaskSrc,

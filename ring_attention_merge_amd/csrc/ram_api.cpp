@@ -461,6 +461,50 @@ size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, co
   return ring_layout(&dt, n_chunks, fwd_needs_bits(&dt, src)).total;
 }
 
+ram_status ring_attn_fwd_masks(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src,
+                               ram_ring_masks* out) {
+  if (!desc || !out) return fail(RAM_ERR_INVALID, "desc or out is null");
+  ram_attn_desc dt = *desc;
+  dt.block_q = ram::fwd_block_q(desc->dtype, desc->D);
+  dt.block_kv = ram::kBlockKV;
+  RAM_TRY(check_desc(&dt, kFwdTile, true));
+  if (n_chunks < 1) return fail(RAM_ERR_INVALID, "n_chunks=%d must be >= 1", n_chunks);
+  const bool with_bits = fwd_needs_bits(&dt, src);
+  const RingLayout L = ring_layout(&dt, n_chunks, with_bits);
+  out->cls_off = (int64_t)L.cls_off;
+  out->cnt_off = (int64_t)L.cnt_off;
+  out->col_off = (int64_t)L.col_off;
+  out->bits_off = with_bits ? (int64_t)L.bits_off : -1;
+  out->block_q = dt.block_q;
+  out->block_kv = dt.block_kv;
+  out->nQb = (int32_t)cdiv(dt.Sq, dt.block_q);
+  out->nKb = (int32_t)cdiv(dt.Skv, dt.block_kv);
+  out->tile_words = dt.block_q * (dt.block_kv / 32);
+  return ok();
+}
+
+ram_status ring_attn_bwd_masks(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src,
+                               ram_ring_masks* out) {
+  if (!desc || !out) return fail(RAM_ERR_INVALID, "desc or out is null");
+  ram_attn_desc dt = *desc;
+  dt.block_q = ram::kBlockQ;
+  dt.block_kv = ram::kBlockKV;
+  RAM_TRY(check_desc(&dt, kBwdTile, true));
+  if (n_chunks < 1) return fail(RAM_ERR_INVALID, "n_chunks=%d must be >= 1", n_chunks);
+  const bool with_bits = src && src->dense;
+  const BwdLayout L = bwd_layout(&dt, n_chunks, with_bits);
+  out->cls_off = (int64_t)L.cls_off;
+  out->cnt_off = (int64_t)L.cnt_off;
+  out->col_off = (int64_t)L.col_off;
+  out->bits_off = with_bits ? (int64_t)L.bits_off : -1;
+  out->block_q = dt.block_q;
+  out->block_kv = dt.block_kv;
+  out->nQb = (int32_t)cdiv(dt.Sq, dt.block_q);
+  out->nKb = (int32_t)cdiv(dt.Skv, dt.block_kv);
+  out->tile_words = (int32_t)kBwdTileWords;
+  return ok();
+}
+
 ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32_t q_shard, const void* q,
                               const void* k_all, const void* v_all, const ram_mask_src* src, const float* sinks,
                               void* out, float* lse, void* workspace, size_t workspace_bytes,

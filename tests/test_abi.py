@@ -9,6 +9,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import ring_attention_merge_amd as ram
 from ring_attention_merge_amd import _lib, build
@@ -36,6 +37,7 @@ def test_every_header_symbol_is_exported(lib):
     assert set(names) == {"build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
                           "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_bwd_kernel_tile", "ram_last_error", "attn_bwd_prep",
                           "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes",
+                          "ring_attn_fwd_masks", "ring_attn_bwd_masks",
                           "ram_mfma_probe", "ram_set_kernel_events"}, names
     for n in names:
         assert hasattr(lib, n), f"libram.so does not export {n}"
@@ -142,6 +144,37 @@ def test_chunk_pointer_validation(lib):
     assert lib.attn_fwd_chunk(ctypes.byref(d), FAKE, FAKE, FAKE, None, ctypes.byref(_bm()), 0, 0, FAKE, FAKE,
                               0) == _lib.RAM_ERR_INVALID
     assert lib.attn_fwd_chunk(None, FAKE, FAKE, FAKE, None, None, 0, 0, FAKE, FAKE, 0) == _lib.RAM_ERR_INVALID
+
+
+def test_ring_mask_layout(lib):
+    # the ring's block masks sit at the offsets the workspace sizing lays out: classes, counts,
+    # lists, then the bits when the forward needs them
+    al = lambda x: (x + 255) // 256 * 256
+    d = ram.Desc(B=1, Sq=4096, Skv=4096, H=8, Hkv=8, D=128)
+    m = ram.ring_attn_fwd_masks(d, 4)
+    acc = 4096 * 8 * 128 * 4
+    tiles = 4 * 32 * 64
+    assert (m["cls_off"], m["cnt_off"], m["col_off"], m["bits_off"]) == (acc, acc + al(tiles),
+                                                                         acc + al(tiles) + al(4 * 32 * 4), -1)
+    assert (m["block_q"], m["block_kv"], m["nQb"], m["nKb"], m["tile_words"]) == (128, 64, 32, 64, 256)
+    mb = ram.ring_attn_fwd_masks(d, 4, ram.MaskSrc(dense=torch.zeros(1, dtype=torch.uint8)))
+    assert mb["bits_off"] == m["col_off"] + tiles * 4
+    b = ram.ring_attn_bwd_masks(d, 4)
+    assert b["bits_off"] == -1 and (b["block_q"], b["block_kv"], b["tile_words"]) == (128, 64, 256)
+    assert b["cls_off"] > 0 and b["cnt_off"] == b["cls_off"] + al(tiles)
+    with pytest.raises(ram.RamError):
+        ram.ring_attn_fwd_masks(d, 0)
+    with pytest.raises(ram.RamError):
+        ram.ring_attn_bwd_masks(ram.Desc(B=1, Sq=64, Skv=64, H=3, Hkv=2, D=128), 2)
+
+
+def test_mask_arrays_needed_only_with_kv_tiles(lib):
+    # with key tiles, the classes and lists must be given; with Skv = 0 they may be null (the
+    # kernels then read neither: covered on the GPU by test_empty_kv_null_mask_arrays)
+    d = _fdesc()
+    assert _chunk(lib, d, bm=_bm(tile_class=0)) == _lib.RAM_ERR_INVALID and "tile_class" in _err(lib)
+    assert _chunk(lib, d, bm=_bm(col_idx=0)) == _lib.RAM_ERR_INVALID and "col_idx" in _err(lib)
+    assert _chunk(lib, d, bm=_bm(row_cnt=0)) == _lib.RAM_ERR_INVALID and "row_cnt" in _err(lib)
 
 
 def test_dense_mask_validation(lib):

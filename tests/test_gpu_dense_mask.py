@@ -225,3 +225,24 @@ def test_ring_dense_c2_shape_sampled():
     qp, kp = w.positions()
     ro, rl = oracle.attention(q, k, v, scale=w.scale, q_pos=qp, kv_pos=kp, causal=True, dense=dense, rows=rows)
     compare(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", "c2 shape dense", rows=rows)
+
+
+def test_c5dense_full_sampled():
+    """The long-context causal workload with its dense mask over all 32768 keys (the bench's
+    c5dense: 8 chunks of 4096, H=32 over Hkv=8, D=128, bf16), at full size, checked on sampled
+    rows plus the mask's dead rows."""
+    w = wl.c5_dense()
+    say(f"ring dense {w.name}: dense [{w.Sq}, {w.Skv}], {w.n_chunks} chunks")
+    d = ram.Desc(B=1, Sq=w.Sq, Skv=w.chunk, H=w.H, Hkv=w.Hkv, D=128, scale=w.scale, causal=True)
+    src = ram.MaskSrc(dense=_u8(w.dense), dense_chunk_step=w.chunk)
+    out = torch.full((1, w.Sq, w.H, 128), float("nan"), device=DEV).to(torch.bfloat16)
+    lse = torch.full((1, w.H, w.Sq), float("nan"), device=DEV)
+    ws = torch.empty(ram.ring_attn_workspace_bytes(d, w.n_chunks, src), dtype=torch.uint8, device=DEV)
+    ram.ring_attn_fwd_1gpu(d, w.n_chunks, w.q_shard, w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), src, None, out, lse, ws)
+    torch.cuda.synchronize()
+    dead = np.nonzero(~w.dense.any(axis=1))[0]
+    rows = np.unique(np.concatenate([wl.sampled_rows(w.Sq, w.chunk, n=128, seed=2006), dead]))
+    q, k, v, _ = w.as_f64()
+    qp, kp = w.positions()
+    ro, rl = oracle.attention(q, k, v, scale=w.scale, q_pos=qp, kv_pos=kp, causal=True, dense=w.dense, rows=rows)
+    compare(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", "c5dense full", rows=rows)

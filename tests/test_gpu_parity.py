@@ -15,7 +15,7 @@ import torch
 import oracle
 import ring_attention_merge_amd as ram
 from ring_attention_merge_amd import workloads as wl
-from gpu_util import compare, mask_src, oracle_ref, ring_by_chunks, ring_desc, ring_splits, run_ring, say
+from gpu_util import OUT_TOL, compare, mask_src, oracle_ref, ring_by_chunks, ring_desc, ring_splits, run_ring, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -335,6 +335,37 @@ def test_c4_full_sampled(Hkv):
     compare(out.numpy(), lse.numpy(), ro, rl, "bf16", w.name, rows=rows)
 
 
+def test_c4_error_split():
+    """Where C4's output error comes from (GQA with soft cap and sinks, full size, sampled rows):
+    the kernel's float32 result (the same ring as attn_fwd_chunk calls, which leave the running
+    output in float32) against the oracle, the bf16 rounding of the oracle's own output, and the
+    bf16 result against the oracle. The kernel's arithmetic error is bounded by its bf16
+    probabilities: each weight p is rounded with relative error <= 2^-9, so the normalised output,
+    a convex combination of v rows, moves by at most 2^-9 * max|v| (plus float32 sums)."""
+    w = wl.c4_gqa_cap_sinks()
+    rows = wl.sampled_rows(w.Sq, w.chunk, n=256, seed=1004)
+    d = ring_desc(w)
+    src = mask_src(w, DEV)
+    q, k, v = w.q.to(DEV), w.k.to(DEV), w.v.to(DEV)
+    sinks = w.sinks.to(DEV)
+    o32, l32 = ring_by_chunks(d, w.n_chunks, w.q_shard, q, k, v, src, sinks)
+    out, lse = run_ring(w)
+    torch.cuda.synchronize()
+    ro, rl = oracle_ref(w, rows=rows)
+    o32 = o32.cpu().numpy().astype(np.float64)[:, rows]
+    o16 = out.numpy().astype(np.float64)[:, rows]
+    r16 = torch.from_numpy(ro).to(torch.bfloat16).double().numpy()
+    e_kernel = float(np.max(np.abs(o32 - ro)))
+    e_round = float(np.max(np.abs(r16 - ro)))
+    e_total = float(np.max(np.abs(o16 - ro)))
+    e_vs_rounded = float(np.max(np.abs(o16 - r16)))
+    bound = 2.0 ** -9 * float(w.v.abs().max()) + 1e-4
+    say(f"C4 error split: kernel (float32) {e_kernel:.3e} (bound {bound:.3e}), bf16 rounding of the oracle "
+        f"{e_round:.3e}, bf16 result {e_total:.3e} (vs the rounded oracle {e_vs_rounded:.3e})")
+    assert e_kernel <= bound
+    assert e_total <= OUT_TOL["bf16"]
+
+
 def test_c5_full_sampled():
     w = wl.c5_long_causal()
     rows = wl.sampled_rows(w.Sq, w.chunk, n=256, seed=1005)
@@ -342,6 +373,48 @@ def test_c5_full_sampled():
     out, lse = run_ring(w)
     ro, rl = oracle_ref(w, rows=rows)
     compare(out.numpy(), lse.numpy(), ro, rl, "bf16", w.name, rows=rows)
+
+
+@pytest.mark.parametrize("dtype,D", [(ram.RAM_BF16, 128), (ram.RAM_F32, 64), (ram.RAM_BF16, 64)])
+def test_empty_kv_null_mask_arrays(dtype, D):
+    """A chunk of no keys with null tile_class and col_idx (allowed when Skv = 0): every row is
+    empty, (0, -inf), and the backward writes dq = 0; no kernel reads the null arrays."""
+    import ctypes
+    from ring_attention_merge_amd import _lib
+    say(f"empty KV, null mask arrays: dtype {dtype} D {D}")
+    lib = ram.load()
+    B, Sq, H = 2, 300, 2
+    tq = torch.bfloat16 if dtype == ram.RAM_BF16 else torch.float32
+    bq, bk = ram.kernel_tile(dtype, D)
+    d = ram.Desc(B=B, Sq=Sq, Skv=0, H=H, Hkv=H, D=D, dtype=dtype, scale=0.1, causal=False, block_q=bq, block_kv=bk)
+    q = torch.randn(B, Sq, H, D, device=DEV).to(tq)
+    kv = torch.zeros(16, dtype=tq, device=DEV)
+    out = torch.full((B, Sq, H, D), float("nan"), device=DEV)
+    lse = torch.full((B, H, Sq), float("nan"), device=DEV)
+    row_cnt = torch.zeros(B * (-(-Sq // bq)), dtype=torch.int32, device=DEV)
+    bm = _lib.c_block_mask(0, row_cnt.data_ptr(), 0, 0, 0, 0)
+    cs = _lib.c_mask_src(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0)
+    cd = d.c()
+    st = lib.attn_fwd_chunk(ctypes.byref(cd), q.data_ptr(), kv.data_ptr(), kv.data_ptr(), ctypes.byref(cs),
+                            ctypes.byref(bm), None, ram.RAM_OUT_WRITE, out.data_ptr(), lse.data_ptr(), None)
+    assert st == _lib.RAM_OK, lib.ram_last_error().decode()
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(lse == float("-inf"))
+    # the backward of the same chunk: dq of an empty chunk is zero
+    bbq, bbk = ram.bwd_kernel_tile(dtype, D)
+    db = ram.Desc(**{**d.__dict__, "block_q": bbq, "block_kv": bbk})
+    cdb = db.c()
+    rcb = torch.zeros(B * (-(-Sq // bbq)), dtype=torch.int32, device=DEV)
+    bmb = _lib.c_block_mask(0, rcb.data_ptr(), 0, 0, 0, 0)
+    dout = torch.randn(B, Sq, H, D, device=DEV).to(tq)
+    delta = torch.zeros(2, B, H, Sq, device=DEV)
+    dq = torch.full((B, Sq, H, D), float("nan"), device=DEV)
+    st = lib.attn_bwd_chunk(ctypes.byref(cdb), q.data_ptr(), kv.data_ptr(), kv.data_ptr(), dout.data_ptr(),
+                            lse.data_ptr(), delta.data_ptr(), ctypes.byref(cs), ctypes.byref(bmb), ram.RAM_OUT_WRITE,
+                            dq.data_ptr(), kv.data_ptr(), kv.data_ptr(), None)
+    assert st == _lib.RAM_OK, lib.ram_last_error().decode()
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0)
 
 
 # ------------------------------------------------------------------------------ invariants
