@@ -115,7 +115,7 @@ hipError_t launch_bwd_prep(int dtype, int B, int Sq, int H, int D, const void* o
                            const float* lse, const float* sinks, float* delta, float* dsinks, hipStream_t s);
 hipError_t launch_col_lists(const MaskParams& p, int n_chunks, int32_t* col_cnt, int32_t* row_idx,
                             hipStream_t s);
-// bf16, D = 128, 256-row mask tiles: one visit per chunk (n_chunks = 1 for a single chunk).
+// bf16, D = 128, mask tiles of kAltRows rows: one visit per chunk (n_chunks = 1 for a single chunk).
 // Kernels without kv positions, kv segments or tile bits mask PARTIAL tiles by positions;
 // with any of them, PARTIAL tiles are masked from mask_bits, which must then be set.
 hipError_t launch_attn_alt(const AttnParams& p, const RingSplit* split, hipStream_t s);
