@@ -246,6 +246,18 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
 /* Workspace bytes ring_attn_bwd_1gpu needs (0 on bad input); src may be NULL. */
 size_t ring_attn_bwd_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src);
 
+/* ring_attn_fwd_1gpu for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, results and errors without the workspace. Its scratch is a
+ * static device array of 64 MiB that each GPU the library runs on holds until
+ * the process ends (looked up on the first call on a device); shapes whose
+ * ring_attn_workspace_bytes() exceeds it fail with RAM_ERR_UNSUPPORTED before
+ * anything runs. All calls on one GPU share that GPU's array: calls that
+ * overlap on a GPU (on different streams or threads) race. Allocates nothing. */
+ram_status ring_attn_fwd_1gpu_noalloc(const ram_attn_desc* desc, int32_t n_chunks, int32_t q_shard, const void* q,
+                                      const void* k_all, const void* v_all, const ram_mask_src* src,
+                                      const float* sinks, void* out, float* lse, hipStream_t stream);
+
 /* Workspace bytes ring_attn_fwd_1gpu needs for this shape (0 on bad input).
  * src may be NULL; a source whose forward needs tile bits needs room for them. */
 size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src);

@@ -28,7 +28,7 @@ RAM_PAD_SEGMENT_ID = -1
 EXPORTS = ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
            "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_bwd_kernel_tile", "ram_last_error", "attn_bwd_prep",
            "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes", "ring_attn_fwd_masks",
-           "ring_attn_bwd_masks", "ram_mfma_probe", "ram_set_kernel_events")
+           "ring_attn_bwd_masks", "ring_attn_fwd_1gpu_noalloc", "ram_mfma_probe", "ram_set_kernel_events")
 
 
 class RamError(RuntimeError):
@@ -88,6 +88,7 @@ def load(path: str = LIB_PATH):
     lib.ring_attn_fwd_1gpu.argtypes = [P(c_desc), i32, i32, vp, vp, vp, P(c_mask_src), f32p, vp, f32p,
                                        vp, ctypes.c_size_t, vp]
     lib.ring_attn_workspace_bytes.argtypes = [P(c_desc), i32, P(c_mask_src)]
+    lib.ring_attn_fwd_1gpu_noalloc.argtypes = [P(c_desc), i32, i32, vp, vp, vp, P(c_mask_src), f32p, vp, f32p, vp]
     lib.ring_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.ram_kernel_tile.argtypes = [i32, i32, P(i32), P(i32)]
     lib.ram_bwd_kernel_tile.argtypes = [i32, i32, P(i32), P(i32)]
@@ -107,7 +108,7 @@ def load(path: str = LIB_PATH):
     for name in ("build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu", "ram_kernel_tile",
                  "ram_bwd_kernel_tile",
                  "attn_bwd_prep", "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ram_mfma_probe",
-                 "ram_set_kernel_events", "ring_attn_fwd_masks", "ring_attn_bwd_masks"):
+                 "ram_set_kernel_events", "ring_attn_fwd_masks", "ring_attn_bwd_masks", "ring_attn_fwd_1gpu_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -353,6 +354,26 @@ def ring_attn_fwd_1gpu(desc: Desc, n_chunks: int, q_shard: int, q, k_all, v_all,
     _check(load().ring_attn_fwd_1gpu(ctypes.byref(cd), n_chunks, q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
                                      ctypes.byref(cs), _ptr(sinks), _ptr(out), _ptr(lse), _ptr(workspace),
                                      workspace.numel(), _stream(stream)))
+
+
+def ring_attn_fwd_1gpu_noalloc(desc: Desc, n_chunks: int, q_shard: int, q, k_all, v_all, src: MaskSrc, sinks,
+                               out, lse, stream=None):
+    """ring_attn_fwd_1gpu_noalloc: ring_attn_fwd_1gpu with the library's static per-GPU scratch
+    instead of a workspace (no device allocation; calls that overlap on one GPU race)."""
+    dt = _tdtype(desc.dtype)
+    kv_len = n_chunks * desc.Skv
+    _need(q, "q", dt, _span(desc.B, desc.q_stride_b, desc.Sq * desc.H * desc.D))
+    if kv_len > 0:
+        _need(k_all, "k_all", dt, _span(desc.B, desc.kv_stride_b, kv_len * desc.Hkv * desc.D))
+        _need(v_all, "v_all", dt, _span(desc.B, desc.kv_stride_b, kv_len * desc.Hkv * desc.D))
+    _need(out, "out", dt, desc.B * desc.Sq * desc.H * desc.D)
+    _need(lse, "lse", torch.float32, desc.B * desc.H * desc.Sq)
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, desc.H)
+    dense_cols = desc.Skv + (n_chunks - 1) * src.dense_chunk_step
+    cd, cs = desc.c(), src.c(desc.B, desc.Sq, kv_len, dense_cols)
+    _check(load().ring_attn_fwd_1gpu_noalloc(ctypes.byref(cd), n_chunks, q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
+                                             ctypes.byref(cs), _ptr(sinks), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 # ------------------------------------------------------------------------------ backward

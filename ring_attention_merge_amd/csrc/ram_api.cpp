@@ -355,6 +355,10 @@ BwdLayout bwd_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits) {
 
 }  // namespace
 
+namespace ram {
+ram_status api_fail(ram_status s, const char* msg) { return fail(s, "%s", msg); }
+}  // namespace ram
+
 extern "C" {
 
 const char* ram_last_error(void) { return g_err.c_str(); }

@@ -5,6 +5,8 @@
 #include <cstdint>
 #include <hip/hip_runtime_api.h>
 
+#include "../../include/ram.h"
+
 namespace ram {
 
 // Mask tiles the kernels walk: 128 query rows by 64 keys (the forward kernels, the backward).
@@ -125,6 +127,8 @@ hipError_t launch_merge(int B, int Sq, int H, int D, float* out_acc, float* lse_
 hipError_t launch_cast_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
 // dst[b * dst_stride + i] = sum over s < S of src[s * part_stride + b * n + i], i < n, b < B
 // (a fixed order: deterministic).
+// Sets the message ram_last_error() returns and returns s (for entry points outside ram_api.cpp).
+ram_status api_fail(ram_status s, const char* msg);
 hipError_t launch_sum_parts(const float* src, int S, int64_t part_stride, int B, int64_t n, float* dst,
                             int64_t dst_stride, hipStream_t s);
 

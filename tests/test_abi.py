@@ -37,7 +37,7 @@ def test_every_header_symbol_is_exported(lib):
     assert set(names) == {"build_block_mask", "attn_fwd_chunk", "lse_merge", "ring_attn_fwd_1gpu",
                           "ring_attn_workspace_bytes", "ram_kernel_tile", "ram_bwd_kernel_tile", "ram_last_error", "attn_bwd_prep",
                           "attn_bwd_chunk", "ring_attn_bwd_1gpu", "ring_attn_bwd_workspace_bytes",
-                          "ring_attn_fwd_masks", "ring_attn_bwd_masks",
+                          "ring_attn_fwd_masks", "ring_attn_bwd_masks", "ring_attn_fwd_1gpu_noalloc",
                           "ram_mfma_probe", "ram_set_kernel_events"}, names
     for n in names:
         assert hasattr(lib, n), f"libram.so does not export {n}"
@@ -166,6 +166,19 @@ def test_ring_mask_layout(lib):
         ram.ring_attn_fwd_masks(d, 0)
     with pytest.raises(ram.RamError):
         ram.ring_attn_bwd_masks(ram.Desc(B=1, Sq=64, Skv=64, H=3, Hkv=2, D=128), 2)
+
+
+def test_noalloc_ring_rejects_shapes_past_its_scratch(lib):
+    # the static scratch holds 64 MiB: a ring needing more is refused before anything runs
+    big = _desc(B=1, Sq=32768, Skv=4096, H=32, Hkv=8)
+    need = lib.ring_attn_workspace_bytes(ctypes.byref(big), 8, None)
+    assert need > 64 << 20
+    src = _src()
+    st = lib.ring_attn_fwd_1gpu_noalloc(ctypes.byref(big), 8, -1, FAKE, FAKE, FAKE, ctypes.byref(src), 0, FAKE, FAKE2,
+                                        0)
+    assert st == _lib.RAM_ERR_UNSUPPORTED and "static scratch" in _err(lib) and str(need) in _err(lib)
+    assert lib.ring_attn_fwd_1gpu_noalloc(None, 8, -1, FAKE, FAKE, FAKE, ctypes.byref(src), 0, FAKE, FAKE2,
+                                          0) == _lib.RAM_ERR_INVALID
 
 
 def test_mask_arrays_needed_only_with_kv_tiles(lib):
