@@ -38,8 +38,8 @@ def lds_hazards(asm: str):
     """(function, instruction, LDS read) triples where the instruction reads or overwrites the
     read's destination before a wait covers it."""
     found = []
-    for fn in re.findall(r"^(_Z\w+):", asm, re.M):
-        body = asm[asm.index(fn + ":"):]
+    for fn in re.findall(r"^\s*\.type\s+(_Z\w+),@function", asm, re.M):
+        body = asm[asm.index("\n" + fn + ":") + 1:]
         body = body[: body.index(".Lfunc_end")]
         lines = [l.split(";")[0].strip() for l in body.split("\n")]
         lines = [l for l in lines if l and not l.startswith(".")]
@@ -79,14 +79,16 @@ def _compile(src, out_dir):
 
 def test_checker_flags_an_early_copy():
     """A copy of an LDS result before its wait is reported; after the wait it is not."""
-    early = """_Zfoo:
+    early = """\t.type\t_Zfoo,@function
+_Zfoo:
 \tds_read_b128 v[4:7], v1
 \tv_mov_b32_e32 v9, v5
 \ts_waitcnt lgkmcnt(0)
 .Lfunc_end0:
 """
     late = early.replace("\tv_mov_b32_e32 v9, v5\n\ts_waitcnt lgkmcnt(0)\n", "\ts_waitcnt lgkmcnt(0)\n\tv_mov_b32_e32 v9, v5\n")
-    partial = """_Zfoo:
+    partial = """\t.type\t_Zfoo,@function
+_Zfoo:
 \tds_read_b128 v[4:7], v1
 \tds_read_b128 v[8:11], v1 offset:16
 \ts_waitcnt lgkmcnt(1)
