@@ -18,8 +18,10 @@ LIB = os.path.join(HERE, "libram.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Device sources. The feature switch below reaches the host pass of each .hip file too, where
-# it is ignored with a notice; the host-only ram_api.cpp is built without it.
+# Device sources. The packed-fp32 switch is a cc1 option, which -Xarch_device cannot forward
+# (clang: "options requiring arguments are unsupported"), so it reaches the host pass of each
+# .hip file too, where it is ignored with a notice; the host-only ram_api.cpp is built without
+# it. tests/test_lds_waits.py checks the device assembly for packed fp32 instructions.
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 ops (v_pk_*_f32) anywhere in the device code

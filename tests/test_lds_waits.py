@@ -21,6 +21,8 @@ import tempfile
 
 import pytest
 
+from ring_attention_merge_amd import build
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "ring_attention_merge_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -69,9 +71,9 @@ def lds_hazards(asm: str):
 
 def _compile(src, out_dir):
     out = os.path.join(out_dir, os.path.basename(src) + ".s")
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-Xarch_device", "-fno-honor-nans", "-I", os.path.join(ROOT, "include"),
-           "--cuda-device-only", "-S", src, "-o", out]
+    # the flags libram.so is built with
+    flags = [f for f in build.HIP_FLAGS if f not in ("-fPIC",)]
+    cmd = [HIPCC, *flags, "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S", src, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, f"{src}: {r.stderr[-2000:]}"
     return src, open(out).read()
@@ -101,13 +103,33 @@ _Zfoo:
     assert [h[1] for h in lds_hazards(partial)] == ["v_mov_b32_e32 v21, v8"]
 
 
+_ASM = {}
+
+
+def _all_asm():
+    """gfx950 assembly of every kernel source (compiled once per test session)."""
+    if not _ASM:
+        sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+        assert sources
+        with tempfile.TemporaryDirectory() as d:
+            with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+                _ASM.update(ex.map(lambda s: _compile(s, d), sources))
+    return sorted(_ASM.items())
+
+
+@pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="hipcc not available")
+def test_no_packed_fp32_instructions():
+    """The device code holds no packed fp32 arithmetic (v_pk_add_f32, v_pk_mul_f32, v_pk_fma_f32):
+    the build turns the feature off for every kernel source."""
+    bad = []
+    for src, asm in _all_asm():
+        bad += [f"{os.path.basename(src)}: {m}" for m in re.findall(r"\bv_pk_(?:add|mul|fma)_f32\b[^\n]*", asm)]
+    assert not bad, "\n".join(bad[:20])
+
+
 @pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="hipcc not available")
 def test_no_lds_result_read_before_its_wait():
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    assert sources
-    with tempfile.TemporaryDirectory() as d:
-        with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
-            results = list(ex.map(lambda s: _compile(s, d), sources))
+    results = _all_asm()
     bad = []
     for src, asm in results:
         bad += [f"{os.path.basename(src)}: {fn[:60]}: '{ins}' before the wait of '{rd}'"
