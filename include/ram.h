@@ -271,12 +271,16 @@ size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, co
  *   tile lists    int32 [n_chunks][B][nQb][nKb] (ascending, -1 padded),
  *   tile bits     uint32 [n_chunks][B][nQb][nKb][tile_words] as in
  *                 ram_block_mask, or -1 when the call stores none,
+ *   row order     int32 [B * nQb] (forward only, else -1): the rows of q tiles
+ *                 (b * nQb + qb) in the order the one-launch ring takes them,
+ *                 most non-EMPTY tiles over all chunks first (made when
+ *                 positions, segment IDs or a dense mask are given),
  * chunk c being the chunk at index c of k_all (not the visit order). The mask
  * of a chunk is what build_block_mask makes for that chunk's keys (see
  * ring_attn_fwd_1gpu for their positions and dense-mask columns). Same
  * arguments as the workspace-size calls; RAM_ERR_INVALID on bad input. */
 typedef struct ram_ring_masks {
-  int64_t cls_off, cnt_off, col_off, bits_off;
+  int64_t cls_off, cnt_off, col_off, bits_off, order_off;
   int32_t block_q, block_kv, nQb, nKb, tile_words;
 } ram_ring_masks;
 ram_status ring_attn_fwd_masks(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src,

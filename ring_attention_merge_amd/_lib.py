@@ -48,7 +48,8 @@ class c_desc(ctypes.Structure):
 
 class c_ring_masks(ctypes.Structure):
     _fields_ = [("cls_off", ctypes.c_int64), ("cnt_off", ctypes.c_int64), ("col_off", ctypes.c_int64),
-                ("bits_off", ctypes.c_int64), ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32),
+                ("bits_off", ctypes.c_int64), ("order_off", ctypes.c_int64), ("block_q", ctypes.c_int32),
+                ("block_kv", ctypes.c_int32),
                 ("nQb", ctypes.c_int32), ("nKb", ctypes.c_int32), ("tile_words", ctypes.c_int32)]
 
 
@@ -432,8 +433,8 @@ def _ring_masks(fn, desc: Desc, n_chunks: int, src: Optional[MaskSrc]) -> dict:
 
 def ring_attn_fwd_masks(desc: Desc, n_chunks: int, src: Optional[MaskSrc] = None) -> dict:
     """ring_attn_fwd_masks: where ring_attn_fwd_1gpu's workspace holds each chunk's block mask
-    (byte offsets cls_off, cnt_off, col_off, bits_off (-1: none); block_q, block_kv, nQb, nKb,
-    tile_words)."""
+    (byte offsets cls_off, cnt_off, col_off, bits_off (-1: none), and order_off, the rows' order
+    (-1: none); block_q, block_kv, nQb, nKb, tile_words)."""
     return _ring_masks(load().ring_attn_fwd_masks, desc, n_chunks, src)
 
 

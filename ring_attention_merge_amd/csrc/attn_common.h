@@ -49,6 +49,17 @@ __device__ __forceinline__ bool decode_work(const AttnParams& p, int& b, int& h,
   // small batches) a contiguous share would give one XCD the heaviest causal rows: there
   // the items go round robin too, so that each XCD gets some heads of every q tile.
   int64_t item = id;
+  if (p.row_order) {
+    // rows most tiles first, every head of a row before the next row, round robin over XCDs
+    if (item >= T) return false;
+    if (s_out) *s_out = (int)(item % S);
+    item /= S;
+    h = (int)(item % p.H);
+    const int row = p.row_order[item / p.H];
+    b = row / p.nQb;
+    qb = row - b * p.nQb;
+    return true;
+  }
   if (((int64_t)p.B * p.Hkv) % 8 == 0) item = (id & 7) * (T / 8) + (id >> 3);
   if (item >= T) return false;
   if (s_out) *s_out = (int)(item % S);

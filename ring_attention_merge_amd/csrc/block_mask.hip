@@ -11,7 +11,9 @@
 // allowed, FULL when all are, else PARTIAL; pairs past the sequence ends do
 // not count.
 //
-// One workgroup per (row of tiles, batch, chunk). With sequential positions,
+// One workgroup per (row of tiles, batch, chunk), or, where the pairs are checked, one per group
+// of key tiles of a row, which then leave the compaction of the row's list to a second kernel
+// (block_mask_compact). With sequential positions,
 // no segments, no dense mask and no bits requested, a tile's class follows
 // from its position ranges alone: FULL iff min q_pos >= max kv_pos, EMPTY iff
 // max q_pos < min kv_pos; with explicit positions the same test runs on the
@@ -22,6 +24,8 @@
 // mask, skipping the reads for words the other tests already cleared; the
 // words are staged in LDS and stored for PARTIAL tiles. Classes are staged in
 // LDS, then compacted in order with wave ballots and a running offset.
+#include <algorithm>
+
 #include <hip/hip_runtime.h>
 
 #include "ram_internal.h"
@@ -34,6 +38,7 @@ constexpr int kWaves = kThreads / 64;
 // Pairwise rounds cover up to kGroupKeys keys and kGroupWords bit words.
 constexpr int kGroupKeys = 1024;
 constexpr int kGroupWords = 8192;
+constexpr int kGroupTiles = 8;   // at most this many tiles per round (and per workgroup of a split row)
 
 // One bit per byte of 4 bytes (nonzero -> 1), byte k to bit k: OR-fold each
 // byte onto its lowest bit, then one multiply moves the four bits next to each
@@ -111,6 +116,25 @@ __device__ __forceinline__ uint32_t key_bits(const int* keys, int j0, int n, int
   return m;
 }
 
+// n / d for n < 2^14 and d < 2^13 by one high multiply (exact on that range: m = floor(2^32/d) + 1).
+struct FastDiv {
+  uint32_t d, m;
+  __device__ explicit FastDiv(uint32_t d_) : d(d_), m(d_ > 1 ? (uint32_t)(0xFFFFFFFFu / d_) + 1u : 0u) {}
+  __device__ uint32_t div(uint32_t n) const { return d > 1 ? __umulhi(n, m) : n; }
+};
+
+// Key tiles per pairwise round (and per workgroup of a split row): bounded by the keys staged
+// and by the bit words held in LDS.
+__host__ __device__ inline int group_tiles(int bq, int bk) {
+  const int tw = bq * ((bk + 31) >> 5);
+  return max(1, min(kGroupTiles, min(kGroupKeys / bk, kGroupWords / tw)));
+}
+
+__device__ __forceinline__ void compact_row_impl(const MaskParams& p, int64_t crow, const uint8_t* cls_s, int* wsum);
+__device__ __forceinline__ void compact_row(const MaskParams& p, int64_t crow, const uint8_t* cls_s, int* wsum) {
+  compact_row_impl(p, crow, cls_s, wsum);
+}
+
 __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
   __shared__ uint8_t cls_s[kMaxMaskCols];
   __shared__ int qpos_s[kMaxMaskTile], qseg_s[kMaxMaskTile];
@@ -118,10 +142,14 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
   __shared__ __attribute__((aligned(16))) int kseg_s[kGroupKeys];
   __shared__ int red[2 * kWaves];
   __shared__ int wsum[kWaves];
-  __shared__ uint32_t bits_s[kGroupWords];
+  // the bit words of a round: group_tiles * words per tile (sized at launch, at most kGroupWords)
+  extern __shared__ uint32_t bits_s[];
   __shared__ int flag_s[kGroupKeys / 16];
+  __shared__ int open_s[kGroupKeys / 16];   // a group has at most kGroupKeys / 16 tiles
+  __shared__ int n_open_s;
 
-  const int qb = blockIdx.x, b = blockIdx.y, c = blockIdx.z;
+  const int qb = blockIdx.x / p.kv_split, b = blockIdx.y, c = blockIdx.z;
+  const int split = blockIdx.x - qb * p.kv_split;   // this workgroup's group of key tiles
   const int tid = threadIdx.x;
   const int q0 = qb * p.bq;
   const int nq = min(p.Sq, q0 + p.bq) - q0;
@@ -180,6 +208,23 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
     // of tiles per round. Each thread builds 32-pair words of the tiles' bit
     // rows; per-tile flags (bit 0: a pair allowed, bit 1: a pair excluded)
     // give the classes.
+    const int tg = group_tiles(p.bq, p.bk);
+    // a split row: this workgroup's group only
+    const int kb_first = p.kv_split > 1 ? split * tg : 0;
+    const int kb_end = p.kv_split > 1 ? min(p.nKb, kb_first + tg) : p.nKb;
+    // The keys of a group into LDS (and its flags cleared); the first group's loads are issued
+    // here, beside the rows' (the barriers below cover them).
+    auto stage_group = [&](int kbg) {
+      const int ng = min(tg, p.nKb - kbg);
+      const int g0 = kbg * p.bk;
+      const int gk = min(p.Skv, (kbg + ng) * p.bk) - g0;
+      for (int j = tid; j < gk; j += kThreads) {
+        kpos_s[j] = kvpos ? kvpos[g0 + j] : kv_base + g0 + j;
+        kseg_s[j] = kvseg ? kvseg[g0 + j] : 0;
+      }
+      for (int t = tid; t < ng; t += kThreads) flag_s[t] = 0;
+    };
+    if (kb_first < kb_end) stage_group(kb_first);
     // ranges over the rows that can have an allowed key (padding rows have none)
     int qpl = 0x7fffffff, qph = -0x7fffffff - 1, qsl = 0x7fffffff, qsh = -0x7fffffff - 1;
     bool qpad = false;
@@ -208,17 +253,12 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
     const bool any_qpad = __syncthreads_or(qpad);
     const int W = (p.bk + 31) >> 5;   // words per tile row
     const int tw = p.bq * W;          // words per tile
-    const int tg = max(1, min(kGroupKeys / p.bk, kGroupWords / tw));
     const uint8_t* drow0 = p.dense ? p.dense + (int64_t)q0 * p.dense_ld + (int64_t)c * p.dense_col_step : nullptr;
-    for (int kbg = 0; kbg < p.nKb; kbg += tg) {
+    for (int kbg = kb_first; kbg < kb_end; kbg += tg) {
       const int ng = min(tg, p.nKb - kbg);
       const int g0 = kbg * p.bk;                           // first key of the group
       const int gk = min(p.Skv, (kbg + ng) * p.bk) - g0;   // keys of the group
-      for (int j = tid; j < gk; j += kThreads) {
-        kpos_s[j] = kvpos ? kvpos[g0 + j] : kv_base + g0 + j;
-        kseg_s[j] = kvseg ? kvseg[g0 + j] : 0;
-      }
-      for (int t = tid; t < ng; t += kThreads) flag_s[t] = 0;
+      if (kbg != kb_first) stage_group(kbg);
       __syncthreads();
       // the group's tiles by their ranges, 16 threads per tile
       bool open = false;
@@ -258,8 +298,17 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
         }
       }
       if (!__syncthreads_or(open)) continue;   // every tile of the group decided
-      const int nw = ng * tw;
-      const int gw = ng * W;   // words per tile row across the round
+      // the tiles left open, in order: only their words are checked
+      if (tid == 0) {
+        int no = 0;
+        for (int t = 0; t < ng; ++t)
+          if (cls_s[kbg + t] == 3) open_s[no++] = t;
+        n_open_s = no;
+      }
+      __syncthreads();
+      const int nw = n_open_s * tw;   // words of the open tiles
+      const int gw = n_open_s * W;    // words per query row across them
+      const FastDiv div_gw((uint32_t)gw), div_w((uint32_t)W), div_tw((uint32_t)tw);
       // Words are taken row by row (consecutive threads: consecutive 32-key words
       // of one query row), so the dense mask is read in long contiguous runs, and
       // kBatch words per thread at a time: their positions and segments first,
@@ -272,8 +321,9 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
           const int u = u0 + k * kThreads;
-          const int i = u / gw, jw = u - i * gw;
-          const int tl = jw / W, wi = jw - tl * W;
+          const int i = (int)div_gw.div((uint32_t)u), jw = u - i * gw;
+          const int oi = (int)div_w.div((uint32_t)jw), wi = jw - oi * W;
+          const int tl = u < nw ? open_s[oi] : 0;
           const int j0 = tl * p.bk + wi * 32;                // first key of the word within the group
           const int jn = u < nw ? min(min(32, gk - j0), (tl + 1) * p.bk - j0) : 0;
           tv[k] = tl * tw + i * W + wi;                      // the word's place in bits_s (tile-major)
@@ -336,19 +386,36 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
         if (cls_s[kbg + t] == 3) cls_s[kbg + t] = (f & 1) ? ((f & 2) ? 1 : 2) : 0;
       }
       if (p.bits) {
+        // the bits of the open tiles that came out PARTIAL
         uint32_t* dst = p.bits + ((size_t)crow * p.nKb + kbg) * tw;
-        for (int t = tid; t < nw; t += kThreads)
-          if (flag_s[t / tw] == 3) dst[t] = bits_s[t];
+        for (int u = tid; u < nw; u += kThreads) {
+          const int oi = (int)div_tw.div((uint32_t)u);
+          const int t = open_s[oi], o = t * tw + (u - oi * tw);
+          if (flag_s[t] == 3) dst[o] = bits_s[o];
+        }
       }
       __syncthreads();   // the next group rewrites kpos_s / kseg_s / bits_s / flag_s
     }
   }
   __syncthreads();
 
-  // Write classes and compact the non-EMPTY tiles in ascending order.
   uint8_t* cls_out = p.tile_class + crow * p.nKb;
-  int32_t* col_out = p.col_idx + crow * p.nKb;
+  if (p.kv_split > 1) {
+    // a split row: this group's classes; block_mask_compact makes the list
+    const int tg = group_tiles(p.bq, p.bk);
+    const int kb_first = split * tg, kb_end = min(p.nKb, kb_first + tg);
+    for (int kb = kb_first + tid; kb < kb_end; kb += kThreads) cls_out[kb] = cls_s[kb];
+    return;
+  }
+  // Write classes and compact the non-EMPTY tiles in ascending order.
   for (int kb = tid; kb < p.nKb; kb += kThreads) cls_out[kb] = cls_s[kb];
+  compact_row(p, crow, cls_s, wsum);
+}
+
+// The compacted list and count of one row of tiles from its classes in LDS.
+__device__ __forceinline__ void compact_row_impl(const MaskParams& p, int64_t crow, const uint8_t* cls_s, int* wsum) {
+  const int tid = threadIdx.x;
+  int32_t* col_out = p.col_idx + crow * p.nKb;
   const int lane = tid & 63, w = tid >> 6;
   int running = 0;
   for (int base = 0; base < p.nKb; base += kThreads) {
@@ -372,11 +439,82 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
   if (tid == 0) p.row_cnt[crow] = running;
 }
 
+// Lists of the rows block_mask_kernel classified in split groups: one workgroup per row.
+__global__ __launch_bounds__(kThreads) void block_mask_compact(MaskParams p) {
+  __shared__ uint8_t cls_s[kMaxMaskCols];
+  __shared__ int wsum[kWaves];
+  const int64_t crow = ((int64_t)blockIdx.z * p.B + blockIdx.y) * p.nQb + blockIdx.x;
+  const uint8_t* cls_in = p.tile_class + crow * p.nKb;
+  for (int kb = threadIdx.x; kb < p.nKb; kb += kThreads) cls_s[kb] = cls_in[kb];
+  __syncthreads();
+  compact_row_impl(p, crow, cls_s, wsum);
+}
+
+// Counting sort of the rows by their total tile count, most first (one workgroup).
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderKeys = 4096;
+__global__ __launch_bounds__(kOrderThreads) void row_order_kernel(const int32_t* row_cnt, int n_chunks, int64_t rows,
+                                                                  int max_key, int32_t* order) {
+  __shared__ int hist[kOrderKeys];
+  const int tid = threadIdx.x;
+  const int nk = max_key + 1;   // keys 0 .. max_key, histogram slot max_key - key (most first)
+  for (int i = tid; i < nk; i += kOrderThreads) hist[i] = 0;
+  __syncthreads();
+  auto key = [&](int64_t r) {
+    int64_t t = 0;
+    for (int c = 0; c < n_chunks; ++c) t += row_cnt[c * rows + r];
+    return (int)min<int64_t>(t, max_key);
+  };
+  for (int64_t r = tid; r < rows; r += kOrderThreads) atomicAdd(&hist[max_key - key(r)], 1);
+  __syncthreads();
+  // exclusive prefix sum over the slots, by one wave (each lane a contiguous run of slots)
+  if (tid < 64) {
+    const int per = (nk + 63) / 64;
+    const int s0 = min(nk, tid * per), s1 = min(nk, s0 + per);
+    int run = 0;
+    for (int i = s0; i < s1; ++i) run += hist[i];
+    int incl = run;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (tid >= o) incl += v;
+    }
+    int base = incl - run;
+    for (int i = s0; i < s1; ++i) {
+      const int c = hist[i];
+      hist[i] = base;
+      base += c;
+    }
+  }
+  __syncthreads();
+  for (int64_t r = tid; r < rows; r += kOrderThreads) order[atomicAdd(&hist[max_key - key(r)], 1)] = (int32_t)r;
+}
+
 }  // namespace
 
-hipError_t launch_block_mask(const MaskParams& p, int n_chunks, hipStream_t s) {
-  if (p.B == 0 || p.nQb == 0 || n_chunks == 0) return hipSuccess;
-  hipLaunchKernelGGL(block_mask_kernel, dim3(p.nQb, p.B, n_chunks), dim3(kThreads), 0, s, p);
+hipError_t launch_row_order(const int32_t* row_cnt, int n_chunks, int64_t rows, int max_tiles, int32_t* order,
+                            hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int max_key = (int)std::min<int64_t>((int64_t)max_tiles * n_chunks, kOrderKeys - 1);
+  hipLaunchKernelGGL(row_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, row_cnt, n_chunks, rows, max_key, order);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_mask(const MaskParams& p_in, int n_chunks, hipStream_t s) {
+  if (p_in.B == 0 || p_in.nQb == 0 || n_chunks == 0) return hipSuccess;
+  MaskParams p = p_in;
+  // Rows checked pair by pair (segments, a dense mask or stored bits) take one workgroup per
+  // group of key tiles when a row has several groups, so that a row's rounds run side by side.
+  const bool pairwise = p.q_seg != nullptr || p.dense != nullptr || p.bits != nullptr;
+  const int tg = group_tiles(p.bq, p.bk);
+  p.kv_split = pairwise ? (p.nKb + tg - 1) / tg : 1;
+  if (p.kv_split < 1) p.kv_split = 1;
+  // LDS for the round's bit words only where pairs are checked
+  const size_t words = pairwise ? (size_t)tg * p.bq * ((p.bk + 31) / 32) : 0;
+  hipLaunchKernelGGL(block_mask_kernel, dim3(p.nQb * p.kv_split, p.B, n_chunks), dim3(kThreads),
+                     words * sizeof(uint32_t), s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.kv_split == 1) return e;
+  hipLaunchKernelGGL(block_mask_compact, dim3(p.nQb, p.B, n_chunks), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -254,7 +254,7 @@ ram::AttnParams attn_params(const ram_attn_desc* d, const void* q, const void* k
 }
 
 struct RingLayout {
-  size_t acc_off, cls_off, cnt_off, col_off, bits_off, acc2_off, lse2_off, total;
+  size_t acc_off, cls_off, cnt_off, col_off, bits_off, order_off, acc2_off, lse2_off, total;
 };
 
 // The bf16 kernel for D = 128 runs a whole ring in one launch; the others run one chunk per launch.
@@ -283,7 +283,14 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Words of tile bits per backward mask tile (block_q rows of block_kv / 32 words).
 constexpr int64_t kBwdTileWords = (int64_t)ram::kBlockQ * (ram::kBlockKV / 32);
 
-RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits) {
+// Whether the one-launch ring takes its rows of q tiles most tiles first (an order it sorts on the
+// GPU): when positions, segment IDs or a dense mask make a row's work unrelated to its index. With
+// sequential positions the natural order (last q tile first) already is.
+bool ring_row_order(const ram_attn_desc* d, const ram_mask_src* m) {
+  return alt_kernel(d) && m && (m->q_pos || m->kv_pos || m->q_seg || m->kv_seg || m->dense);
+}
+
+RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits, bool with_order) {
   RingLayout L{};
   const int bq = ram::fwd_block_q(d->dtype, d->D);
   const int64_t nQb = cdiv(d->Sq, bq), nKb = cdiv(d->Skv, ram::kBlockKV);
@@ -300,6 +307,8 @@ RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits)
   off += align256((size_t)tiles * sizeof(int32_t));
   L.bits_off = off;
   if (with_bits) off += align256((size_t)tiles * bq * (ram::kBlockKV / 32) * sizeof(uint32_t));
+  L.order_off = off;
+  if (with_order) off += align256((size_t)d->B * nQb * sizeof(int32_t));
   const bool split = ring_split_shape(d, n_chunks);
   L.acc2_off = off;
   if (split) off += align256((size_t)d->B * d->Sq * d->H * d->D * sizeof(float));
@@ -462,7 +471,7 @@ size_t ring_attn_workspace_bytes(const ram_attn_desc* desc, int32_t n_chunks, co
   ram_attn_desc dt = *desc;
   dt.block_q = ram::fwd_block_q(desc->dtype, desc->D);
   dt.block_kv = ram::kBlockKV;
-  return ring_layout(&dt, n_chunks, fwd_needs_bits(&dt, src)).total;
+  return ring_layout(&dt, n_chunks, fwd_needs_bits(&dt, src), ring_row_order(&dt, src)).total;
 }
 
 ram_status ring_attn_fwd_masks(const ram_attn_desc* desc, int32_t n_chunks, const ram_mask_src* src,
@@ -474,11 +483,13 @@ ram_status ring_attn_fwd_masks(const ram_attn_desc* desc, int32_t n_chunks, cons
   RAM_TRY(check_desc(&dt, kFwdTile, true));
   if (n_chunks < 1) return fail(RAM_ERR_INVALID, "n_chunks=%d must be >= 1", n_chunks);
   const bool with_bits = fwd_needs_bits(&dt, src);
-  const RingLayout L = ring_layout(&dt, n_chunks, with_bits);
+  const bool with_order = ring_row_order(&dt, src);
+  const RingLayout L = ring_layout(&dt, n_chunks, with_bits, with_order);
   out->cls_off = (int64_t)L.cls_off;
   out->cnt_off = (int64_t)L.cnt_off;
   out->col_off = (int64_t)L.col_off;
   out->bits_off = with_bits ? (int64_t)L.bits_off : -1;
+  out->order_off = with_order ? (int64_t)L.order_off : -1;
   out->block_q = dt.block_q;
   out->block_kv = dt.block_kv;
   out->nQb = (int32_t)cdiv(dt.Sq, dt.block_q);
@@ -501,6 +512,7 @@ ram_status ring_attn_bwd_masks(const ram_attn_desc* desc, int32_t n_chunks, cons
   out->cnt_off = (int64_t)L.cnt_off;
   out->col_off = (int64_t)L.col_off;
   out->bits_off = with_bits ? (int64_t)L.bits_off : -1;
+  out->order_off = -1;
   out->block_q = dt.block_q;
   out->block_kv = dt.block_kv;
   out->nQb = (int32_t)cdiv(dt.Sq, dt.block_q);
@@ -539,7 +551,8 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   if (!lse || !aligned(lse, 4)) return fail(RAM_ERR_INVALID, "lse null or misaligned");
   if (sinks && !aligned(sinks, 4)) return fail(RAM_ERR_INVALID, "sinks misaligned");
   const bool with_bits = fwd_needs_bits(desc, src);
-  const RingLayout L = ring_layout(desc, n_chunks, with_bits);
+  const bool with_order = ring_row_order(desc, src);
+  const RingLayout L = ring_layout(desc, n_chunks, with_bits, with_order);
   if (!workspace || !aligned(workspace, 256))
     return fail(RAM_ERR_WORKSPACE, "workspace null or not 256-byte aligned");
   if (workspace_bytes < L.total)
@@ -583,6 +596,12 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
     p.kv_chunk_elems = (int64_t)desc->Skv * desc->Hkv * desc->D;
     p.mask_chunk_tiles = (int64_t)desc->B * nQb * nKb;
     p.mask_chunk_rows = (int64_t)desc->B * nQb;
+    if (with_order) {
+      int32_t* order = reinterpret_cast<int32_t*>(ws + L.order_off);
+      e = ram::launch_row_order(bm.row_cnt, n_chunks, (int64_t)desc->B * nQb, (int)nKb, order, stream);
+      if (e != hipSuccess) return hip_fail(e, "ring row order launch");
+      p.row_order = order;
+    }
     const bool split = ring_split_shape(desc, n_chunks);
     float* acc2 = reinterpret_cast<float*>(ws + L.acc2_off);
     float* lse2 = reinterpret_cast<float*>(ws + L.lse2_off);

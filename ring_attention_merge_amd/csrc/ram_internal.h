@@ -59,6 +59,9 @@ struct AttnParams {
   int64_t kv_chunk_elems;
   int64_t mask_chunk_tiles;
   int64_t mask_chunk_rows;
+  // or null: the rows (b * nQb + qb) in the order workgroups take them (most tiles first, made by
+  // launch_row_order); heads are the inner index, workgroups go to the XCDs round robin
+  const int32_t* row_order;
 };
 
 // A split ring (launch_attn_alt with this given): each q tile row's visits go to two
@@ -86,6 +89,7 @@ struct MaskParams {
   int32_t* row_cnt;        // chunk c at + c * B*nQb
   int32_t* col_idx;        // chunk c at + c * B*nQb*nKb
   uint32_t* bits;          // or null; tile t at + t * bq*ceil(bk/32), t counted like tile_class
+  int32_t kv_split;        // workgroups per row of tiles (set by the launcher; 1: one does it all)
 };
 
 // Backward of one chunk: `a` carries q, k, v, lse, the masks and sizes of the
@@ -122,6 +126,11 @@ hipError_t launch_col_lists(const MaskParams& p, int n_chunks, int32_t* col_cnt,
 // with any of them, PARTIAL tiles are masked from mask_bits, which must then be set.
 hipError_t launch_attn_alt(const AttnParams& p, const RingSplit* split, hipStream_t s);
 hipError_t launch_block_mask(const MaskParams& p, int n_chunks, hipStream_t s);
+// order[0 .. rows): the rows of tiles sorted by their non-EMPTY tiles summed over the n_chunks
+// chunks' counts (row_cnt + c * rows, each at most max_tiles), most first (totals above 4095
+// count as 4095; rows with equal totals in any order).
+hipError_t launch_row_order(const int32_t* row_cnt, int n_chunks, int64_t rows, int max_tiles, int32_t* order,
+                            hipStream_t s);
 hipError_t launch_merge(int B, int Sq, int H, int D, float* out_acc, float* lse_acc,
                         const float* out_blk, const float* lse_blk, hipStream_t s);
 hipError_t launch_cast_bf16(const float* src, void* dst, int64_t n, hipStream_t s);

@@ -154,11 +154,12 @@ def test_ring_mask_layout(lib):
     m = ram.ring_attn_fwd_masks(d, 4)
     acc = 4096 * 8 * 128 * 4
     tiles = 4 * 32 * 64
-    assert (m["cls_off"], m["cnt_off"], m["col_off"], m["bits_off"]) == (acc, acc + al(tiles),
-                                                                         acc + al(tiles) + al(4 * 32 * 4), -1)
+    assert (m["cls_off"], m["cnt_off"], m["col_off"], m["bits_off"], m["order_off"]) == (
+        acc, acc + al(tiles), acc + al(tiles) + al(4 * 32 * 4), -1, -1)
     assert (m["block_q"], m["block_kv"], m["nQb"], m["nKb"], m["tile_words"]) == (128, 64, 32, 64, 256)
     mb = ram.ring_attn_fwd_masks(d, 4, ram.MaskSrc(dense=torch.zeros(1, dtype=torch.uint8)))
     assert mb["bits_off"] == m["col_off"] + tiles * 4
+    assert mb["order_off"] == mb["bits_off"] + tiles * 256 * 4
     b = ram.ring_attn_bwd_masks(d, 4)
     assert b["bits_off"] == -1 and (b["block_q"], b["block_kv"], b["tile_words"]) == (128, 64, 256)
     assert b["cls_off"] > 0 and b["cnt_off"] == b["cls_off"] + al(tiles)
@@ -213,9 +214,11 @@ def test_dense_mask_validation(lib):
     base = lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, None)
     plain = lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src()))
     dense = lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src(dense=FAKE2)))
-    assert base == plain and dense == base + 4 * 4 * 8 * 1024
+    # (and, with any position, segment or dense array, the order of the rows of q tiles: 4 of them,
+    # one 256-byte block)
+    assert base == plain and dense == base + 4 * 4 * 8 * 1024 + 256
     assert lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src(kv_pos=FAKE2))) == dense
-    assert lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src(q_pos=FAKE2))) == base
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(dr), 4, ctypes.byref(_src(q_pos=FAKE2))) == base + 256
     d64 = _desc(B=1, Sq=512, Skv=512, H=4, Hkv=4, D=64)
     b64 = lib.ring_attn_workspace_bytes(ctypes.byref(d64), 4, None)
     assert lib.ring_attn_workspace_bytes(ctypes.byref(d64), 4, ctypes.byref(_src(kv_pos=FAKE2))) == b64

@@ -104,6 +104,15 @@ def test_ring_fwd_masks_bitexact(name):
     lay = ram.ring_attn_fwd_masks(d, w.n_chunks, src)
     assert (lay["bits_off"] >= 0) == (w.dense is not None or w.q_seg is not None or w.kv_pos is not None)
     _check_masks(w, ws, lay, f"fwd {name}")
+    if lay["order_off"] >= 0:
+        # the rows the ring takes most tiles first: a permutation of the rows with non-increasing
+        # total counts over the chunks
+        rows = w.B * lay["nQb"]
+        order = _read(ws, lay["order_off"], rows, np.int32)
+        cnt = _read(ws, lay["cnt_off"], w.n_chunks * rows, np.int32).reshape(w.n_chunks, rows).sum(axis=0)
+        assert np.array_equal(np.sort(order), np.arange(rows)), "row order is not a permutation"
+        assert np.all(np.diff(np.minimum(cnt[order], 4095)) <= 0), "row order not by descending tile count"
+        say(f"fwd {name}: row order of {rows} rows by descending tile count")
 
 
 BWD_CASES = {
