@@ -113,16 +113,21 @@ __device__ __forceinline__ bf16x8 lds_v_operand(uint32_t byte) {
 // offset) masked, 2 from bits `bw` (key 8*(i>>2) + 4*lg + (i&3) at bit 8*(i>>2) + 4*lg + (i&3)).
 template <bool BITS>
 __device__ __forceinline__ void step_mask(f32x16& S, int kind, int thr, uint32_t bw, int lg) {
-  if (kind == 1) {
-    asm volatile("" : "+v"(thr));   // keep the compares next to their use
+  if constexpr (!BITS) {
+    if (kind == 1) {
+      asm volatile("" : "+v"(thr));   // keep the compares next to their use
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) >= thr) S[i] = neg_inf();
+    }
+  } else if (kind != 0) {
+    // Both kinds as one word whose bit 8*(i>>2) + (i&3) keeps score i: one masking pass over the
+    // scores (two separately masked copies of them would not fit the register budget).
+    const uint32_t below = thr <= 0 ? 0u : (thr >= 32 ? ~0u : (1u << thr) - 1u);
+    const uint32_t keep = kind == 1 ? below : (bw >> (4 * lg));
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (8 * (i >> 2) + (i & 3) >= thr) S[i] = neg_inf();
-  } else if (BITS && kind == 2) {
-    const uint32_t x = bw >> (4 * lg);
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (((x >> (8 * (i >> 2) + (i & 3))) & 1u) == 0u) S[i] = neg_inf();
+      if (((keep >> (8 * (i >> 2) + (i & 3))) & 1u) == 0u) S[i] = neg_inf();
   }
 }
 
