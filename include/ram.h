@@ -289,8 +289,8 @@ ram_status ring_attn_bwd_masks(const ram_attn_desc* desc, int32_t n_chunks, cons
                                ram_ring_masks* out);
 
 /* The tile (block_q, block_kv) the forward kernel of (dtype, D) walks: block
- * masks passed to attn_fwd_chunk must be built at this tile (256 x 64 for bf16
- * with D = 128, 128 x 64 otherwise). */
+ * masks passed to attn_fwd_chunk must be built at this tile (128 x 64 for
+ * every built dtype and head dim). */
 ram_status ram_kernel_tile(int32_t dtype, int32_t D, int32_t* block_q, int32_t* block_kv);
 
 /* The tile the backward kernels walk (128 x 64): block masks passed to
