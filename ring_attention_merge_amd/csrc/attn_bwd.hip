@@ -145,6 +145,10 @@ __device__ __forceinline__ void weights_and_grads(f32x16& S, const f32x16& dP, f
 }
 
 // ------------------------------------------------------------------------------ dq
+// One workgroup per (batch, head, q tile). A chunk call (n_chunks <= 1) walks one chunk's tiles
+// and writes or adds float32 dq. A ring (n_chunks > 1) visits every chunk in ring order with dQ
+// held in registers across the visits (dq is the sum of the chunks' terms), and writes the
+// result once, in bf16, to dq_out.
 template <int D, bool CAP, bool BITS>
 __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
   const AttnParams& p = bp.a;
@@ -163,12 +167,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
   const int g = h / G;
   const int q_row = qb * kBlockQ + w * 32 + ln;
   const bool q_ok = q_row < p.Sq;
-
+  const bool ring = p.n_chunks > 1;
   const int64_t mrow = (int64_t)b * p.nQb + qb;
-  const int cnt = p.row_cnt[mrow];
-  if (cnt == 0 && bp.dq_mode == 1) return;   // adds nothing
-  const auto cols = as_const_space(p.col_idx + mrow * p.nKb);
-  const auto cls = as_const_space(p.tile_class + mrow * p.nKb);
+  if (!ring && p.row_cnt[mrow] == 0 && bp.dq_mode == 1) return;   // adds nothing
 
   // q and dout rows as B operands: lane holds row q_row, dims ds*16 + lg*8 .. +7
   bf16x8 qf[NDS], dof[NDS];
@@ -209,17 +210,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
 
   const int64_t krs = (int64_t)p.Hkv * D;
   const uint32_t row_bytes = (uint32_t)krs * 2;
-  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.kv_stride_b + g * D;
-  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.kv_stride_b + g * D;
   uint32_t off[16 / Gm::kSlabRows];
   dma_offsets<D>(off, w, lane, row_bytes);
-  auto dma = [&](int kb, int buf) {
-    const int k0 = kb * BK;
-    const uint32_t bytes = (uint32_t)min(p.Skv - k0, BK) * row_bytes;
-    __bf16* Ks = smem + buf * 2 * kTileElems;
-    dma_tile(tile_rsrc(kbase + (int64_t)k0 * krs, bytes), Ks, off, w, D);
-    dma_tile(tile_rsrc(vbase + (int64_t)k0 * krs, bytes), Ks + kTileElems, off, w, D);
-  };
   if (p.Skv % BK) {
     // a ragged last tile leaves rows unwritten: start from zeros (finite, masked)
     for (int i = tid; i < 2 * 2 * kTileElems / 8; i += kThreads)
@@ -227,102 +219,137 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq(BwdParams bp) {
     __syncthreads();
   }
 
-  auto needs_mask = [&](int kb) {
-    const int c = cls[kb];
-    if constexpr (BITS)
-      if (c == 1) return 2;
-    return (c != 2 || (kb + 1) * BK > p.Skv) ? 1 : 0;
-  };
-  int kb_cur = cnt > 0 ? cols[0] : 0;
-  int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
-  int mk_cur = cnt > 0 ? needs_mask(kb_cur) : 0;   // no class array to read when the row is empty
-  if (cnt > 0) dma(kb_cur, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int it = 0; it < cnt; ++it) {
-    const int kb = kb_cur;
-    const int need_mask = mk_cur;
-    const int buf = it & 1;
-    if (it + 1 < cnt) dma(kb_nxt, buf ^ 1);
-    const char* Kt = reinterpret_cast<const char*>(smem + buf * 2 * kTileElems);
-    const char* Vt = Kt + kTileElems * 2;
-
-    // S^T = K Q^T and dP^T = V dO^T: A = key rows of K / V, B = q / dout in registers
-    f32x16 S[2], dP[2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      S[kb2] = f32x16{};
-      dP[kb2] = f32x16{};
-    }
-    // in phases of 8 operands each (NDS / 4 per product), so that few operands are live at once
-    constexpr int kPh = NDS / 4;
-#pragma unroll
-    for (int ph = 0; ph < 2 * kPh; ++ph) {
-      const char* T = (ph < kPh) ? Kt : Vt;
-      bf16x8 a[4][2];
-#pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4)
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) a[d4][kb2] = lds_row<D>(T, kb2 * 32 + ln, 2 * ((ph % kPh) * 4 + d4) + lg);
-#pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4)
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const int ds = (ph % kPh) * 4 + d4;
-          if (ph < kPh) S[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4][kb2], qf[ds], S[kb2], 0, 0, 0);
-          else dP[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4][kb2], dof[ds], dP[kb2], 0, 0, 0);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (CAP) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
-    }
-    if (BITS && need_mask == 2)
-      apply_bits(S, p.mask_bits + ((mrow * p.nKb + kb) * kBlockQ + w * 32 + ln) * 2, lg);
-    else if (need_mask)
-      apply_mask(S, p, b, kb * BK, lg, qpos, qseg);
-    bf16x8 DS[4];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      f32x16 Pw;
-      weights_and_grads<CAP>(S[kb2], dP[kb2], Pw, lse2v, dlv, p);
-      bf16x8 two[2];
-      pack_b(S[kb2], two);
-      DS[2 * kb2] = two[0];
-      DS[2 * kb2 + 1] = two[1];
-    }
-    // dQ^T += K^T dS^T: A = K read transposed (lane = dim), B = dS^T (lane = query);
-    // 4 * NDB products in batches of 8
-    constexpr int kKsPer = 8 / NDB;
-#pragma unroll
-    for (int half = 0; half < 4 / kKsPer; ++half) {
-      TrPair kt8[8];
-#pragma unroll
-      for (int f = 0; f < 8; ++f) kt8[f] = lds_tr<D>(Kt, (half * kKsPer + f / NDB) * 16, f % NDB, lane);
-      lds_settle(kt8);
-#pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const int ks = half * kKsPer + f / NDB, db = f % NDB;
-        dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(kt8[f]), DS[ks], dQ[db], 0, 0, 0);
-      }
-    }
-
-    const int kb_nn = cols[min(it + 2, cnt - 1)];
-    const int mk_nxt = needs_mask(kb_nxt);
+  const int n_vis = ring ? p.n_chunks : 1;
+  for (int t = 0; t < n_vis; ++t) {
+    AttnParams pc = p;   // this visit's chunk
+    if (ring) ring_chunk_view(pc, p, t);
+    const int cnt = pc.row_cnt[mrow];
+    if (cnt == 0) continue;
+    const auto cols = as_const_space(pc.col_idx + mrow * p.nKb);
+    const auto cls = as_const_space(pc.tile_class + mrow * p.nKb);
+    const __bf16* kbase = reinterpret_cast<const __bf16*>(pc.k) + (int64_t)b * p.kv_stride_b + g * D;
+    const __bf16* vbase = reinterpret_cast<const __bf16*>(pc.v) + (int64_t)b * p.kv_stride_b + g * D;
+    auto dma = [&](int kb, int buf) {
+      const int k0 = kb * BK;
+      const uint32_t bytes = (uint32_t)min(p.Skv - k0, BK) * row_bytes;
+      __bf16* Ks = smem + buf * 2 * kTileElems;
+      dma_tile(tile_rsrc(kbase + (int64_t)k0 * krs, bytes), Ks, off, w, D);
+      dma_tile(tile_rsrc(vbase + (int64_t)k0 * krs, bytes), Ks + kTileElems, off, w, D);
+    };
+    auto needs_mask = [&](int kb) {
+      const int c = cls[kb];
+      if constexpr (BITS)
+        if (c == 1) return 2;
+      return (c != 2 || (kb + 1) * BK > p.Skv) ? 1 : 0;
+    };
+    int kb_cur = cols[0];
+    int kb_nxt = cnt > 1 ? cols[1] : kb_cur;
+    int mk_cur = needs_mask(kb_cur);
+    // every wave is done with both stages (the previous visit's last step ended in a barrier)
+    dma(kb_cur, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    kb_cur = kb_nxt;
-    kb_nxt = kb_nn;
-    mk_cur = mk_nxt;
+
+    for (int it = 0; it < cnt; ++it) {
+      const int kb = kb_cur;
+      const int need_mask = mk_cur;
+      const int buf = it & 1;
+      if (it + 1 < cnt) dma(kb_nxt, buf ^ 1);
+      const char* Kt = reinterpret_cast<const char*>(smem + buf * 2 * kTileElems);
+      const char* Vt = Kt + kTileElems * 2;
+
+      // S^T = K Q^T and dP^T = V dO^T: A = key rows of K / V, B = q / dout in registers
+      f32x16 S[2], dP[2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        S[kb2] = f32x16{};
+        dP[kb2] = f32x16{};
+      }
+      // in phases of 8 operands each (NDS / 4 per product), so that few operands are live at once
+      constexpr int kPh = NDS / 4;
+#pragma unroll
+      for (int ph = 0; ph < 2 * kPh; ++ph) {
+        const char* T = (ph < kPh) ? Kt : Vt;
+        bf16x8 a[4][2];
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2) a[d4][kb2] = lds_row<D>(T, kb2 * 32 + ln, 2 * ((ph % kPh) * 4 + d4) + lg);
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const int ds = (ph % kPh) * 4 + d4;
+            if (ph < kPh) S[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4][kb2], qf[ds], S[kb2], 0, 0, 0);
+            else dP[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4][kb2], dof[ds], dP[kb2], 0, 0, 0);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (CAP) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) S[kb2][i] = capped_log2(S[kb2][i], p.cap_k2, p.cap_log2);
+      }
+      if (BITS && need_mask == 2)
+        apply_bits(S, pc.mask_bits + ((mrow * p.nKb + kb) * kBlockQ + w * 32 + ln) * 2, lg);
+      else if (need_mask)
+        apply_mask(S, pc, b, kb * BK, lg, qpos, qseg);
+      bf16x8 DS[4];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        f32x16 Pw;
+        weights_and_grads<CAP>(S[kb2], dP[kb2], Pw, lse2v, dlv, p);
+        bf16x8 two[2];
+        pack_b(S[kb2], two);
+        DS[2 * kb2] = two[0];
+        DS[2 * kb2 + 1] = two[1];
+      }
+      // dQ^T += K^T dS^T: A = K read transposed (lane = dim), B = dS^T (lane = query);
+      // 4 * NDB products in batches of 8
+      constexpr int kKsPer = 8 / NDB;
+#pragma unroll
+      for (int half = 0; half < 4 / kKsPer; ++half) {
+        TrPair kt8[8];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) kt8[f] = lds_tr<D>(Kt, (half * kKsPer + f / NDB) * 16, f % NDB, lane);
+        lds_settle(kt8);
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+          const int ks = half * kKsPer + f / NDB, db = f % NDB;
+          dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(kt8[f]), DS[ks], dQ[db], 0, 0, 0);
+        }
+      }
+
+      const int kb_nn = cols[min(it + 2, cnt - 1)];
+      const int mk_nxt = needs_mask(kb_nxt);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      kb_cur = kb_nxt;
+      kb_nxt = kb_nn;
+      mk_cur = mk_nxt;
+    }
   }
 
   if (!q_ok) return;
   const float sc = p.scale_log2 * kLn2;   // the score scale
-  float* dq = bp.dq + (((int64_t)b * p.Sq + q_row) * p.H + h) * D;
+  const int64_t o = (((int64_t)b * p.Sq + q_row) * p.H + h) * D;
+  if (ring) {
+    __bf16* dq = reinterpret_cast<__bf16*>(bp.dq_out) + o;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int col = db * 32 + 8 * i4 + 4 * lg;
+        f32x2 lo = {dQ[db][4 * i4] * sc, dQ[db][4 * i4 + 1] * sc};
+        f32x2 hi = {dQ[db][4 * i4 + 2] * sc, dQ[db][4 * i4 + 3] * sc};
+        const bf16x2 a = __builtin_convertvector(lo, bf16x2), c = __builtin_convertvector(hi, bf16x2);
+        *reinterpret_cast<uint2*>(dq + col) =
+            make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c));
+      }
+    return;
+  }
+  float* dq = bp.dq + o;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -893,31 +920,40 @@ hipError_t launch_grid(K kernel, int64_t items, int threads, const BwdParams& p,
 }
 
 template <int D>
-hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
+hipError_t launch_bwd_dq_d(const BwdParams& p, hipStream_t s) {
   const AttnParams& a = p.a;
   const bool cap = a.softcap_on != 0, bits = a.mask_bits != nullptr;
   const int64_t q_items = (int64_t)a.B * a.H * a.nQb;
+  if (q_items == 0) return hipSuccess;
+  const int t = kThreads;
+  if (cap) return bits ? launch_grid(attn_bwd_dq<D, true, true>, q_items, t, p, s) : launch_grid(attn_bwd_dq<D, true, false>, q_items, t, p, s);
+  return bits ? launch_grid(attn_bwd_dq<D, false, true>, q_items, t, p, s) : launch_grid(attn_bwd_dq<D, false, false>, q_items, t, p, s);
+}
+
+template <int D>
+hipError_t launch_bwd_dkv_d(const BwdParams& p, hipStream_t s) {
+  const AttnParams& a = p.a;
+  const bool cap = a.softcap_on != 0, bits = a.mask_bits != nullptr;
   const int64_t kv_items = (int64_t)a.B * a.Hkv * a.nKb * p.head_split;
-  hipError_t e;
-  if (q_items > 0) {
-    const int t = kThreads;
-    if (cap) e = bits ? launch_grid(attn_bwd_dq<D, true, true>, q_items, t, p, s) : launch_grid(attn_bwd_dq<D, true, false>, q_items, t, p, s);
-    else e = bits ? launch_grid(attn_bwd_dq<D, false, true>, q_items, t, p, s) : launch_grid(attn_bwd_dq<D, false, false>, q_items, t, p, s);
-    if (e != hipSuccess) return e;
-  }
-  if (kv_items > 0) {
-    const int t = kDkvThreads;
-    if (cap) e = bits ? launch_grid(attn_bwd_dkv<D, true, true>, kv_items, t, p, s) : launch_grid(attn_bwd_dkv<D, true, false>, kv_items, t, p, s);
-    else e = bits ? launch_grid(attn_bwd_dkv<D, false, true>, kv_items, t, p, s) : launch_grid(attn_bwd_dkv<D, false, false>, kv_items, t, p, s);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  if (kv_items == 0) return hipSuccess;
+  const int t = kDkvThreads;
+  if (cap) return bits ? launch_grid(attn_bwd_dkv<D, true, true>, kv_items, t, p, s) : launch_grid(attn_bwd_dkv<D, true, false>, kv_items, t, p, s);
+  return bits ? launch_grid(attn_bwd_dkv<D, false, true>, kv_items, t, p, s) : launch_grid(attn_bwd_dkv<D, false, false>, kv_items, t, p, s);
 }
 
 }  // namespace
 
+hipError_t launch_attn_bwd_dq(const BwdParams& p, hipStream_t s) {
+  return p.a.D == 64 ? launch_bwd_dq_d<64>(p, s) : launch_bwd_dq_d<128>(p, s);
+}
+
+hipError_t launch_attn_bwd_dkv(const BwdParams& p, hipStream_t s) {
+  return p.a.D == 64 ? launch_bwd_dkv_d<64>(p, s) : launch_bwd_dkv_d<128>(p, s);
+}
+
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s) {
-  return p.a.D == 64 ? launch_bwd_d<64>(p, s) : launch_bwd_d<128>(p, s);
+  const hipError_t e = launch_attn_bwd_dq(p, s);
+  return e != hipSuccess ? e : launch_attn_bwd_dkv(p, s);
 }
 
 hipError_t launch_bwd_prep(int dtype, int B, int Sq, int H, int Dd, const void* out, const void* dout,

@@ -804,6 +804,30 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   if (e != hipSuccess) return hip_fail(e, "ring backward transposed lists launch");
 
   const int64_t esz = desc->dtype == RAM_BF16 ? 2 : 4;
+  // bf16 with several chunks: dq of all chunks in one launch, each workgroup visiting every chunk
+  // with its dq in registers and writing the bf16 result once; the chunk loop below then runs
+  // the dk / dv kernel alone
+  const bool dq_ring = desc->dtype == RAM_BF16 && n_chunks > 1 && desc->Sq > 0;
+  if (dq_ring) {
+    ram_attn_desc dc = *desc;
+    dc.kv_stride_b = kv_full_stride;
+    ram_mask_src sc = *src;
+    sc.q_pos_base = q_base;
+    sc.kv_meta_stride_b = kvm_full;
+    ram::BwdParams bp{};
+    bp.a = attn_params(&dc, q, k_all, v_all, &sc, &bm, nullptr, 0, nullptr, const_cast<float*>(lse), ram::kBlockQ);
+    bp.a.n_chunks = n_chunks;
+    bp.a.ring_shard = q_shard;
+    bp.a.kv_chunk_elems = (int64_t)desc->Skv * desc->Hkv * desc->D;
+    bp.a.mask_chunk_tiles = (int64_t)desc->B * nQb * nKb;
+    bp.a.mask_chunk_rows = (int64_t)desc->B * nQb;
+    bp.dout = dout;
+    bp.delta = delta;
+    bp.dq_out = dq;
+    bp.head_split = 1;
+    e = ram::launch_attn_bwd_dq(bp, stream);
+    if (e != hipSuccess) return hip_fail(e, "ring backward dq launch");
+  }
   for (int t = 0; t < n_chunks; ++t) {
     const int c = q_shard >= 0 ? ((q_shard - t) % n_chunks + n_chunks) % n_chunks : t;
     ram_attn_desc dc = *desc;
@@ -840,7 +864,8 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
       bp.dkv_stride_b = (int64_t)desc->Skv * desc->Hkv * desc->D;
       bp.part_stride = (int64_t)desc->B * bp.dkv_stride_b;
     }
-    e = desc->dtype == RAM_F32 ? ram::launch_attn_bwd_f32(bp, stream) : ram::launch_attn_bwd(bp, stream);
+    if (desc->dtype == RAM_F32) e = ram::launch_attn_bwd_f32(bp, stream);
+    else e = dq_ring ? ram::launch_attn_bwd_dkv(bp, stream) : ram::launch_attn_bwd(bp, stream);
     if (e != hipSuccess) return hip_fail(e, "ring backward chunk launch");
     if (head_split > 1) {
       const int64_t n = (int64_t)desc->Skv * desc->Hkv * desc->D;
@@ -865,8 +890,10 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
     if (e != hipSuccess) return hip_fail(e, "dq / dk / dv copy");
     return ok();
   }
-  e = ram::launch_cast_bf16(dq_acc, dq, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
-  if (e != hipSuccess) return hip_fail(e, "dq cast launch");
+  if (!dq_ring) {
+    e = ram::launch_cast_bf16(dq_acc, dq, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
+    if (e != hipSuccess) return hip_fail(e, "dq cast launch");
+  }
   for (int b = 0; b < desc->B; ++b) {
     e = ram::launch_cast_bf16(dk_acc + b * kv_acc_stride, static_cast<char*>(dk_all) + b * kv_full_stride * esz,
                               kv_acc_stride, stream);

@@ -99,6 +99,8 @@ struct BwdParams {
   const void* dout;        // [B,Sq,H,D] in the q dtype
   const float* delta;      // [B,H,Sq]: rowsum(dout * out)
   float* dq;               // float32 [B,Sq,H,D], written (dq_mode 0) or added to (1)
+  // ring (a.n_chunks > 1, bf16): dq over all chunks, written once as bf16 [B,Sq,H,D]
+  void* dq_out;
   float* dk;               // float32 [B, Skv, Hkv, D] rows, batch stride dkv_stride_b
   float* dv;
   int64_t dkv_stride_b;    // elements
@@ -115,6 +117,8 @@ struct BwdParams {
 // float32 (D = 64 / 128) and bf16 D = 64: the four-wave kernels, one chunk per launch.
 hipError_t launch_attn(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s);       // bf16, D = 64 / 128: dq, then dk / dv
+hipError_t launch_attn_bwd_dq(const BwdParams& p, hipStream_t s);    // bf16: dq alone (a ring if a.n_chunks > 1)
+hipError_t launch_attn_bwd_dkv(const BwdParams& p, hipStream_t s);   // bf16: dk / dv alone
 hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s);   // float32, D = 64 / 128
 // delta (and dsinks) from out and dout in `dtype` (RAM_BF16 / RAM_F32 codes)
 hipError_t launch_bwd_prep(int dtype, int B, int Sq, int H, int D, const void* out, const void* dout,

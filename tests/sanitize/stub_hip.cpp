@@ -8,6 +8,8 @@
 namespace ram {
 hipError_t launch_attn(const AttnParams&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_attn_bwd(const BwdParams&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_attn_bwd_dq(const BwdParams&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_attn_bwd_dkv(const BwdParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_attn_bwd_f32(const BwdParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_bwd_prep(int, int, int, int, int, const void*, const void*, const float*, const float*, float*,
                            float*, hipStream_t) {
