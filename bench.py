@@ -105,11 +105,6 @@ def ring_chunk_src(w, c, dev, dense=None):
                        q_seg=t(w.q_seg), kv_seg=ks, dense=dv, dense_ld=w.Skv if dense is not None else 0)
 
 
-def order(w):
-    N = w.n_chunks
-    return [((w.q_shard - t) % N) if w.q_shard >= 0 else t for t in range(N)]
-
-
 def tile_counts(w, desc, dev, tile_q, tile_kv, dense=None):
     """Non-EMPTY tiles per chunk at (tile_q, tile_kv), from the library's block-mask builder."""
     counts = []
@@ -177,11 +172,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic_bwd(workload: str):
-    """HBM bytes per chunk backward call (dq + dk/dv kernels) from the committed counter summary, if
-    it was taken on the current backward source (else None)."""
+def recorded_bwd(workload: str, what: str, key: str):
+    """A figure of the ring backward (the dq ring and the dk/dv launches) from the committed counter
+    summary profiles/attn_bwd_<workload>_<what>.md, if it was taken on the current backward source
+    (else None)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"attn_bwd_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"attn_bwd_{workload}_{what}.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -196,7 +192,7 @@ def recorded_traffic_bwd(workload: str):
     if fields.get("source_sha256") != h.hexdigest():
         return None
     try:
-        return int(fields["traffic_bytes_per_call_dq"]) + int(fields["traffic_bytes_per_call_dkv"])
+        return float(fields[key])
     except (KeyError, ValueError):
         return None
 
@@ -243,7 +239,8 @@ def recorded_mfma_busy(workload: str):
 
 
 def backward(args, w, desc, q, k, v, src, sinks, out, lse, ws, stream, dense, eff_flops_chunk, fwd_step):
-    """The --backward leg: ring_attn_bwd_1gpu steps, then each chunk's attn_bwd_chunk timed alone."""
+    """The --backward leg: ring_attn_bwd_1gpu steps, with the library recording HIP events around
+    the ring backward's attention launches (the dq ring and the dk/dv launches) in every step."""
     dev = q.device
     fwd_step()
     dout = torch.from_numpy(np.random.default_rng(4242).standard_normal(tuple(q.shape), dtype=np.float32)).to(
@@ -261,57 +258,40 @@ def backward(args, w, desc, q, k, v, src, sinks, out, lse, ws, stream, dense, ef
     for _ in range(args.warmup):
         bstep()
     torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(args.steps):
+    for a, b in evs:
+        ram.set_kernel_events(a, b, stream=stream)
         bstep()
     e1.record(stream)
+    ram.set_kernel_events()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     tflops = eff / (ms * 1e-3) / 1e12
     log(f"backward step {ms:.3f} ms, {tflops:.1f} effective TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak)")
-    del wsb
-
-    # roofline leg: each chunk's backward call alone (dq written on the first visit, added after)
-    bq, bk = ram.kernel_tile(ram.RAM_BF16, w.D)
-    dkd = ram.Desc(**{**desc.__dict__, "block_q": bq, "block_kv": bk, "kv_stride_b": w.Skv * w.Hkv * w.D})
-    delta = torch.empty(2, w.B, w.H, w.Sq, dtype=torch.float32, device=dev)
-    ram.attn_bwd_prep(dkd, out, dout, lse, sinks, delta, dsinks, stream=stream)
-    dq32 = torch.empty(w.B, w.Sq, w.H, w.D, dtype=torch.float32, device=dev)
-    dk32 = torch.empty(w.B, w.Skv, w.Hkv, w.D, dtype=torch.float32, device=dev)
-    dv32 = torch.empty_like(dk32)
-    kv_elems = w.chunk * w.Hkv * w.D
-    masks, srcs = [], []
-    for c in range(w.n_chunks):
-        srcs.append(ring_chunk_src(w, c, dev, dense))
-        bm = ram.alloc_block_mask(dkd, device=dev, with_bits=dense is not None, with_cols=True)
-        ram.build_block_mask(dkd, srcs[c], bm, stream=stream)
-        masks.append(bm)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.n_chunks)]
-    reps = max(1, args.steps // 2)
-    per_chunk_ms = [0.0] * w.n_chunks
-    for rep in range(reps + 1):
-        for t_, c in enumerate(order(w)):
-            a, b = evs[t_]
-            a.record(stream)
-            ram.attn_bwd_chunk(dkd, q, k.view(-1)[c * kv_elems:], v.view(-1)[c * kv_elems:], dout, lse, delta, srcs[c],
-                               masks[c], 0 if t_ == 0 else 1, dq32, dk32.view(-1)[c * kv_elems:],
-                               dv32.view(-1)[c * kv_elems:], stream=stream)
-            b.record(stream)
-        torch.cuda.synchronize()
-        if rep > 0:
-            for t_ in range(w.n_chunks):
-                per_chunk_ms[t_] += evs[t_][0].elapsed_time(evs[t_][1]) / reps
-    kern_ms = sum(per_chunk_ms)
+    kern = sorted(a.elapsed_time(b) for a, b in evs)
+    kern_ms = float(np.median(kern))
     achieved = eff / (kern_ms * 1e-3) / 1e12
-    log("chunk backward ms (visit order): " + ", ".join(f"{x:.3f}" for x in per_chunk_ms))
+    ring_dq = w.dtype == "bf16" and w.n_chunks > 1
+    launches = (1 if ring_dq else w.n_chunks) + w.n_chunks
+    log(f"backward attention kernels median {kern_ms:.3f} ms per step (min {kern[0]:.3f}, max {kern[-1]:.3f}; "
+        f"{launches} launches), {achieved:.1f} TFLOP/s")
+    del wsb
     if args.copy_calibration:
         copy_calibration(dev)
+    traffic = recorded_bwd(args.workload, "traffic", "traffic_bytes_per_step")   # HBM bytes per step
+    traffic = None if traffic is None else int(traffic)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic_bwd(args.workload),
-                "kernel": "attn_bwd_dq + attn_bwd_dkv (one attn_bwd_chunk call)",
-                "launches_per_step": w.n_chunks, "mean_launch_us": round(1e3 * kern_ms / w.n_chunks, 2),
-                "flops_per_launch_mean": eff / w.n_chunks}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": ("attn_bwd_dq (one launch over all chunks) + attn_bwd_dkv (one launch per chunk)"
+                           if ring_dq else "attn_bwd_dq + attn_bwd_dkv (one launch each per chunk)"),
+                "launches_per_step": launches, "median_step_kernel_us": round(1e3 * kern_ms, 1),
+                "timing": "HIP events around the ring backward's attention launches in each of the timed steps; "
+                          "median",
+                "flops_per_step": eff,
+                "hbm_gbs": round(traffic / (kern_ms * 1e-3) / 1e9, 1) if traffic else None,
+                "mfma_busy": recorded_bwd(args.workload, "counters", "mfma_busy_frac")}
     line = {
         "metric": METRIC_BWD, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",

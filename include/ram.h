@@ -301,11 +301,12 @@ ram_status ram_bwd_kernel_tile(int32_t dtype, int32_t D, int32_t* block_q, int32
 const char* ram_last_error(void);
 
 /* Measurement aid: until called again with (NULL, NULL), ring_attn_fwd_1gpu
- * calls made on this thread record `start` on their stream right before their
- * first attention-kernel launch and `stop` right after the last one (the
- * block-mask build and the final cast fall outside), so a caller can time the
- * attention kernels alone. The events stay owned by the caller. Returns
- * RAM_ERR_INVALID if exactly one of them is NULL. */
+ * and ring_attn_bwd_1gpu calls made on this thread record `start` on their
+ * stream right before their first attention-kernel launch and `stop` right
+ * after the last one (the block-mask build, the backward's row dots and the
+ * final casts fall outside), so a caller can time the attention kernels alone.
+ * The events stay owned by the caller. Returns RAM_ERR_INVALID if exactly one
+ * of them is NULL. */
 ram_status ram_set_kernel_events(hipEvent_t start, hipEvent_t stop);
 
 /* Measurement aid, not part of the attention path: n_blocks workgroups of 8

@@ -293,7 +293,7 @@ def attn_fwd_chunk(desc: Desc, q, k, v, src: MaskSrc, mask: BlockMask, sinks, mo
 
 def set_kernel_events(start=None, stop=None, stream=None):
     """ram_set_kernel_events: torch.cuda.Event pair (enable_timing) that this thread's ring forward
-    calls record around their attention launches; no arguments to stop. Both events are recorded
+    and backward calls record around their attention launches; no arguments to stop. Both events are recorded
     once here on `stream` (torch measures only events it has seen recorded); the ring calls record
     them again at their launches, and elapsed_time reads those last records."""
     if (start is None) != (stop is None):

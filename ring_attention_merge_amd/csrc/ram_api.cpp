@@ -17,7 +17,7 @@
 namespace {
 
 thread_local std::string g_err;
-// Events ring_attn_fwd_1gpu records around its attention launches (ram_set_kernel_events).
+// Events the rings record around their attention launches (ram_set_kernel_events).
 thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 ram_status fail(ram_status s, const char* fmt, ...) {
@@ -808,6 +808,7 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   // with its dq in registers and writing the bf16 result once; the chunk loop below then runs
   // the dk / dv kernel alone
   const bool dq_ring = desc->dtype == RAM_BF16 && n_chunks > 1 && desc->Sq > 0;
+  if (g_ev_start && (e = hipEventRecord(g_ev_start, stream)) != hipSuccess) return hip_fail(e, "event record");
   if (dq_ring) {
     ram_attn_desc dc = *desc;
     dc.kv_stride_b = kv_full_stride;
@@ -876,6 +877,7 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
       if (e != hipSuccess) return hip_fail(e, "ring backward partial sums launch");
     }
   }
+  if (g_ev_stop && (e = hipEventRecord(g_ev_stop, stream)) != hipSuccess) return hip_fail(e, "event record");
   if (desc->dtype == RAM_F32) {
     // float32 results: the accumulators are the answer, copied into the caller's layout
     const size_t dq_bytes = (size_t)desc->B * desc->Sq * desc->H * desc->D * 4;
