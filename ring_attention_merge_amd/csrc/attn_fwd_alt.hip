@@ -140,17 +140,23 @@ __device__ __forceinline__ bool step_max(const f32x16& S, float m_ref, float& m_
 #pragma unroll
   for (int i = 0; i < 16; ++i) all[i] = S[i];
   const float mx = pair_max(max_tree3(all));
-  const float umax = CAP ? mx : mx * p.scale_log2;
+  const float umax = CAP ? __builtin_fmaf(mx, 2.0f * p.cap_log2, p.cap_log2) : mx * p.scale_log2;
   m_new = fmaxf(m_ref, umax);
   alpha = (m_new == neg_inf()) ? 1.0f : fast_exp2(m_ref - m_new);
   return __builtin_amdgcn_ballot_w64(umax > m_ref + kRescaleThreshold) != 0;
 }
 
+// With a soft cap the step's scores are kept as u = -1 / (1 + exp2(k2 * s)), k2 = 2 scale log2(e) /
+// cap, in [-1, 0] and increasing in s: the capped logit in log2 units, cap log2(e) tanh(scale s /
+// cap), is c (1 + 2u) with c = cap log2(e). That affine map is folded into the products that use
+// it (the row maximum, one value per lane, and the exponentials' FMA), which saves two VALU
+// operations per score over forming the capped logit itself. Masked scores are -inf in either
+// form.
 template <bool CAP>
 __device__ __forceinline__ void step_cap(f32x16& S, const AttnParams& p) {
   if constexpr (CAP) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) S[i] = capped_log2(S[i], p.cap_k2, p.cap_log2);
+    for (int i = 0; i < 16; ++i) S[i] = __builtin_amdgcn_rcpf(-1.0f - fast_exp2(S[i] * p.cap_k2));
   }
 }
 
@@ -389,12 +395,14 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         Sn = f32x16{};
         {
           const float msub = (m_ref == neg_inf()) ? 0.0f : m_ref;
-          const float sc = CAP ? 1.0f : p.scale_log2;
+          // weight = exp2(logit - m): the logit is sc * s without a cap, c (1 + 2u) with one
+          const float sc = CAP ? 2.0f * p.cap_log2 : p.scale_log2;
+          const float sub = CAP ? p.cap_log2 - msub : -msub;
 #pragma unroll
           for (int ds = 0; ds < 8; ++ds) {
             Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[ds], Sn, 0, 0, 0);
-            float e0 = fast_exp2(__builtin_fmaf(Sc[2 * ds], sc, -msub));
-            float e1 = fast_exp2(__builtin_fmaf(Sc[2 * ds + 1], sc, -msub));
+            float e0 = fast_exp2(__builtin_fmaf(Sc[2 * ds], sc, sub));
+            float e1 = fast_exp2(__builtin_fmaf(Sc[2 * ds + 1], sc, sub));
             // pin the product and the two exponentials to this group (the compiler would
             // otherwise move the products next to their use)
             asm volatile("" : "+v"(Sn), "+v"(e0), "+v"(e1));

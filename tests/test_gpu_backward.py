@@ -230,6 +230,10 @@ RING = {
     "shard1of3_ragged_gqa": lambda: wl.make("b1", B=2, H=4, Hkv=2, Sq=200, chunk=200, n_chunks=3, D=128,
                                             q_shard=1, seed=32),
     "docs": lambda: wl.c3_packed_docs(S=1024, B=2, H=2, len_lo=32, len_hi=256, seed=33),
+    # documents across three chunks: the dq ring masks every visit from the chunk's positions and
+    # segment IDs (tile bits)
+    "docs_3chunks_gqa": lambda: wl.make("rd128", B=2, H=4, Hkv=2, Sq=768, chunk=256, n_chunks=3, D=128,
+                                        docs=(32, 200, 0.05), seed=43),
     "gqa_cap_sinks": lambda: wl.c4_gqa_cap_sinks(S=1024, H=8, Hkv=2, seed=34),
     "mqa_cap_sinks": lambda: wl.c4_gqa_cap_sinks(S=768, H=4, Hkv=1, seed=35),
     # 16 heads on one kv head, 4 kv tiles per chunk: the dk / dv launch splits the group's heads
