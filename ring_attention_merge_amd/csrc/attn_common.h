@@ -324,6 +324,7 @@ __device__ __forceinline__ void ring_chunk_view(AttnParams& pc, const AttnParams
   pc.sinks = t == 0 ? p.sinks : nullptr;
   pc.mode = t == 0 ? p.mode : 1;
   pc.out_final = t == n - 1 ? p.out_final : nullptr;
+  pc.vt = p.vt ? static_cast<const char*>(p.vt) + c * p.vt_chunk_bytes : nullptr;
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));

@@ -53,6 +53,7 @@ template <bool BITS>
 constexpr int alt_stage_bytes() {
   return 2 * kAltTile + (BITS ? kAltBitsBytes : 0);
 }
+static_assert(kPackKeys == kAltKeys && kPackTileBytes == kAltTile, "repacked V tiles are the kernel's steps");
 // the stages and the longest tile list (one 8-byte record per tile) fit a CU's 160 KiB of LDS
 static_assert(kAltStages * alt_stage_bytes<true>() + 8 * kMaxMaskCols <= 160 * 1024, "LDS budget");
 
@@ -160,7 +161,7 @@ __device__ __forceinline__ void step_cap(f32x16& S, const AttnParams& p) {
   }
 }
 
-template <bool CAP, bool BITS, bool SPLIT>
+template <bool CAP, bool BITS, bool SPLIT, bool VP>
 __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p, RingSplit rs) {
   constexpr int D = 128;
   constexpr int NS = kAltStages;
@@ -208,12 +209,15 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
   // DMA: wave w fills rows 4*(w + kAltWaves*i) .. +3 of a step tile (i < kDmaPerTile); lane l
   // writes physical 16-byte chunk l & 15 of row 4*(w + kAltWaves*i) + (l >> 4), i.e. 1 KiB of
   // consecutive LDS bytes per instruction.
+  // VP: V comes repacked (launch_pack_v), each step tile the 8 KiB LDS image itself, so the same
+  // wave copies the same 1 KiB pieces of it linearly.
   uint32_t koff[kDmaPerTile], voff[kDmaPerTile];
 #pragma unroll
   for (int i = 0; i < kDmaPerTile; ++i) {
     const int dr = 4 * (w + kAltWaves * i) + (lane >> 4), phys = lane & 15;
     koff[i] = (uint32_t)dr * row_bytes + (uint32_t)((phys ^ (dr & 15)) * 16);
-    voff[i] = (uint32_t)dr * row_bytes + (uint32_t)((phys ^ (4 * (dr & 3))) * 16);
+    voff[i] = VP ? (uint32_t)(w + kAltWaves * i) * 1024 + (uint32_t)lane * 16
+                 : (uint32_t)dr * row_bytes + (uint32_t)((phys ^ (4 * (dr & 3))) * 16);
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   // Operand read offsets inside a stage. K: row ln, logical chunk 2*ds + lg.
@@ -272,18 +276,23 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
     // masked). Byte offsets into it fit 32 bits (the host checks Skv * row_bytes).
     const auto krs = tile_rsrc(reinterpret_cast<const __bf16*>(pc.k) + (int64_t)b * p.kv_stride_b + g * D,
                                (uint32_t)p.Skv * row_bytes);
-    const auto vrs = tile_rsrc(reinterpret_cast<const __bf16*>(pc.v) + (int64_t)b * p.kv_stride_b + g * D,
-                               (uint32_t)p.Skv * row_bytes);
+    const int n_vt = (p.Skv + kAltKeys - 1) / kAltKeys;   // packed V tiles of the chunk
+    const auto vrs = VP ? tile_rsrc(static_cast<const char*>(pc.vt) + ((int64_t)b * p.Hkv + g) * n_vt * kAltTile,
+                                    (uint32_t)n_vt * kAltTile)
+                        : tile_rsrc(reinterpret_cast<const __bf16*>(pc.v) + (int64_t)b * p.kv_stride_b + g * D,
+                                    (uint32_t)p.Skv * row_bytes);
     // DMA of step s (parity PAR, tile record `tr`) into stage st: this wave's rows of K and V and
     // (BITS) its 32 rows' bit words of the tile when it is PARTIAL.
     auto dma_step = [&](auto PAR_, int st, uint2 tr) {
       constexpr int PAR = decltype(PAR_)::value;
       const uint32_t soff = (tr.x & ~63u) + (PAR ? half_bytes : 0u);
+      // packed V: tile (first key / 32 + PAR) of the chunk
+      const uint32_t soff_v = VP ? tr.y * (kAltTile / kAltKeys) + (PAR ? (uint32_t)kAltTile : 0u) : soff;
       const uint32_t sb = lds0 + st * SB;
 #pragma unroll
       for (int i = 0; i < kDmaPerTile; ++i) {
         dma16(krs, sb + 4 * (w + kAltWaves * i) * 256, koff[i] + soff);
-        dma16(vrs, sb + kAltTile + 4 * (w + kAltWaves * i) * 256, voff[i] + soff);
+        dma16(vrs, sb + kAltTile + 4 * (w + kAltWaves * i) * 256, voff[i] + soff_v);
       }
       if constexpr (BITS) {
         const int kb = (int)(tr.y >> 6);
@@ -372,7 +381,8 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
 #pragma unroll
       for (int ds = 0; ds < 8; ++ds) kf[ds] = lds_b128(kad[ds] + SB);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) vf[i] = lds_v_operand(vad[i & 3] + (i >> 2) * 4096);
+      for (int i = 0; i < 8; ++i)
+        vf[i] = VP ? lds_b128(kad[i] + kAltTile) : lds_v_operand(vad[i & 3] + (i >> 2) * 4096);
       uint2 inf_dma = info(NS), inf_msk = info(1);
 
       // Step j (stage j % NS == JS): products, barrier, loads. STEADY: a step at least 2 NS - 1
@@ -466,7 +476,9 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         }
         if (has_next) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) vf[i] = lds_v_operand(vad[i & 3] + ST1 * SB + (i >> 2) * 4096);
+          for (int i = 0; i < 8; ++i)
+            vf[i] = VP ? lds_b128(kad[i] + kAltTile + ST1 * SB)
+                       : lds_v_operand(vad[i & 3] + ST1 * SB + (i >> 2) * 4096);
           inf_dma = info(j + 1 + NS);
           inf_msk = info(j + 2);
           int kind, thr;
@@ -511,28 +523,88 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
   }
 }
 
-template <bool CAP, bool BITS, bool SPLIT>
+template <bool CAP, bool BITS, bool SPLIT, bool VP>
 hipError_t launch_alt(const AttnParams& p, const RingSplit& rs, hipStream_t s) {
   const int S = SPLIT ? 2 : 1;
   const int64_t T = (int64_t)p.B * p.H * p.nQb * S;
   const size_t lds = (size_t)kAltStages * alt_stage_bytes<BITS>() + sizeof(uint2) * (size_t)max(1, p.nKb);
-  hipLaunchKernelGGL((attn_fwd_bf16_alt<CAP, BITS, SPLIT>), dim3((unsigned)(8 * ((T + 7) / 8))), dim3(kAltThreads),
-                     lds, s, p, rs);
+  hipLaunchKernelGGL((attn_fwd_bf16_alt<CAP, BITS, SPLIT, VP>), dim3((unsigned)(8 * ((T + 7) / 8))),
+                     dim3(kAltThreads), lds, s, p, rs);
   return hipGetLastError();
+}
+
+// Repacked V (VP) is built without the soft cap only: the host repacks V for rings without one.
+template <bool VP>
+hipError_t launch_alt_v(const AttnParams& p, const RingSplit* split, hipStream_t s) {
+  const bool cap = p.softcap_on != 0, bits = p.mask_bits != nullptr;
+  const RingSplit rs = split ? *split : RingSplit{nullptr, nullptr};
+  if constexpr (VP) {
+    if (cap) return hipErrorInvalidValue;
+    if (split) return bits ? launch_alt<false, true, true, true>(p, rs, s) : launch_alt<false, false, true, true>(p, rs, s);
+    return bits ? launch_alt<false, true, false, true>(p, rs, s) : launch_alt<false, false, false, true>(p, rs, s);
+  } else {
+    if (split) {
+      if (cap) return bits ? launch_alt<true, true, true, false>(p, rs, s) : launch_alt<true, false, true, false>(p, rs, s);
+      return bits ? launch_alt<false, true, true, false>(p, rs, s) : launch_alt<false, false, true, false>(p, rs, s);
+    }
+    if (cap) return bits ? launch_alt<true, true, false, false>(p, rs, s) : launch_alt<true, false, false, false>(p, rs, s);
+    return bits ? launch_alt<false, true, false, false>(p, rs, s) : launch_alt<false, false, false, false>(p, rs, s);
+  }
+}
+
+// V repacked for row reads. Workgroup = one 32-key step tile of one (chunk, batch, kv head): the
+// tile's 32 key rows of 128 dims come into LDS with coalesced 16-byte loads (rows past Skv as
+// zeros), then each thread writes two 16-byte chunks of the tile's LDS image. Image chunk
+// o = 16 r + p holds logical chunk c = p ^ (r & 15) of row r (the kernel's swizzle for row
+// reads), and logical chunk c = 2 i + g of row r is what lane (r, g) reads as V operand i:
+// dim 32 (i & 3) + r of the keys 16 (i >> 2) + 8 (m >> 2) + 4 g + (m & 3), m = 0..7, the key
+// order in which the weights' accumulator hands its 16 values to the product.
+__global__ __launch_bounds__(256) void pack_v_kernel(const __bf16* v_all, int64_t kv_stride_b, int B, int Skv,
+                                                     int Hkv, int n_vt, char* vt) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(16))) __bf16 tile[kAltKeys * D];
+  const int g = blockIdx.x / n_vt, t = blockIdx.x - g * n_vt;
+  const int b = blockIdx.y, c = blockIdx.z;
+  const int tid = threadIdx.x;
+  const __bf16* src = v_all + (int64_t)b * kv_stride_b + ((int64_t)c * Skv * Hkv + g) * D;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int e = tid + 256 * r;              // 16-byte piece: key e / 16, dims 8 (e % 16) ..
+    const int key = t * kAltKeys + e / 16;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (key < Skv) x = *reinterpret_cast<const uint4*>(src + (int64_t)key * Hkv * D + (e % 16) * 8);
+    *reinterpret_cast<uint4*>(tile + (e / 16) * D + (e % 16) * 8) = x;
+  }
+  __syncthreads();
+  char* dst = vt + (((int64_t)c * B + b) * Hkv + g) * n_vt * kAltTile + (int64_t)t * kAltTile;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int o = tid + 256 * r;
+    const int row = o / 16, lc = (o % 16) ^ (row & 15);
+    const int i = lc >> 1, lg = lc & 1;
+    const int dim = 32 * (i & 3) + row;
+    __bf16 out[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) out[m] = tile[(16 * (i >> 2) + 8 * (m >> 2) + 4 * lg + (m & 3)) * D + dim];
+    *reinterpret_cast<uint4*>(dst + o * 16) = *reinterpret_cast<const uint4*>(out);
+  }
 }
 
 }  // namespace
 
+hipError_t launch_pack_v(const void* v_all, int64_t kv_stride_b, int B, int n_chunks, int Skv, int Hkv, void* vt,
+                         hipStream_t s) {
+  const int n_vt = (Skv + kAltKeys - 1) / kAltKeys;
+  if ((int64_t)B * n_chunks * n_vt * Hkv == 0) return hipSuccess;
+  if (B > 65535 || n_chunks > 65535 || (int64_t)n_vt * Hkv > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_v_kernel, dim3((unsigned)(n_vt * Hkv), (unsigned)B, (unsigned)n_chunks), dim3(256), 0, s,
+                     static_cast<const __bf16*>(v_all), kv_stride_b, B, Skv, Hkv, n_vt, static_cast<char*>(vt));
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_alt(const AttnParams& p, const RingSplit* split, hipStream_t s) {
   if (p.n_chunks < 1) return hipErrorInvalidValue;
-  const bool cap = p.softcap_on != 0, bits = p.mask_bits != nullptr;
-  const RingSplit rs = split ? *split : RingSplit{nullptr, nullptr};
-  if (split) {
-    if (cap) return bits ? launch_alt<true, true, true>(p, rs, s) : launch_alt<true, false, true>(p, rs, s);
-    return bits ? launch_alt<false, true, true>(p, rs, s) : launch_alt<false, false, true>(p, rs, s);
-  }
-  if (cap) return bits ? launch_alt<true, true, false>(p, rs, s) : launch_alt<true, false, false>(p, rs, s);
-  return bits ? launch_alt<false, true, false>(p, rs, s) : launch_alt<false, false, false>(p, rs, s);
+  return p.vt ? launch_alt_v<true>(p, split, s) : launch_alt_v<false>(p, split, s);
 }
 
 }  // namespace ram

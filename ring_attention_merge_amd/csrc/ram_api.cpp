@@ -44,6 +44,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int64_t kMaxSeq = int64_t(1) << 30;
+constexpr int32_t kMaxGridYZ = 65535;
 constexpr int kMaxHeads = 1 << 16;
 
 // Which tile a call needs its block masks at.
@@ -254,7 +255,7 @@ ram::AttnParams attn_params(const ram_attn_desc* d, const void* q, const void* k
 }
 
 struct RingLayout {
-  size_t acc_off, cls_off, cnt_off, col_off, bits_off, order_off, acc2_off, lse2_off, total;
+  size_t acc_off, cls_off, cnt_off, col_off, bits_off, order_off, acc2_off, lse2_off, vt_off, total;
 };
 
 // The bf16 kernel for D = 128 runs a whole ring in one launch; the others run one chunk per launch.
@@ -279,6 +280,18 @@ bool ring_split_shape(const ram_attn_desc* d, int32_t n_chunks) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Whether the one-launch ring reads V repacked for row reads (ram::launch_pack_v). The repack
+// reads and writes V once (2 bytes read and written per element); it saves about 3% of the
+// kernel's time, whose work per V element grows with the query rows that attend a key times the
+// query heads per kv head. It pays when that product is in the tens of thousands, which
+// Sq * (H / Hkv) >= 32768 stands for (half of it for a causal ring). Not with a soft cap: that
+// kernel is bound by its vector arithmetic, not its LDS reads.
+constexpr int64_t kPackMinRowsPerKey = 32768;
+bool ring_packs_v(const ram_attn_desc* d) {
+  return alt_kernel(d) && !(d->softcap > 0.0f) && d->Skv > 0 &&
+         (int64_t)d->Sq * (d->H / d->Hkv) >= kPackMinRowsPerKey;
+}
 
 // Words of tile bits per backward mask tile (block_q rows of block_kv / 32 words).
 constexpr int64_t kBwdTileWords = (int64_t)ram::kBlockQ * (ram::kBlockKV / 32);
@@ -314,6 +327,9 @@ RingLayout ring_layout(const ram_attn_desc* d, int32_t n_chunks, bool with_bits,
   if (split) off += align256((size_t)d->B * d->Sq * d->H * d->D * sizeof(float));
   L.lse2_off = off;
   if (split) off += align256((size_t)d->B * d->H * d->Sq * sizeof(float));
+  // the one-launch ring reads V repacked for row reads (ram::launch_pack_v)
+  L.vt_off = off;
+  if (ring_packs_v(d)) off += align256(ram::pack_v_bytes(d->B, n_chunks, d->Skv, d->Hkv));
   L.total = off;
   return L;
 }
@@ -482,6 +498,9 @@ ram_status ring_attn_fwd_masks(const ram_attn_desc* desc, int32_t n_chunks, cons
   dt.block_kv = ram::kBlockKV;
   RAM_TRY(check_desc(&dt, kFwdTile, true));
   if (n_chunks < 1) return fail(RAM_ERR_INVALID, "n_chunks=%d must be >= 1", n_chunks);
+  // the rings' per-chunk launches put batch rows and chunks in the grid's y and z (at most 65535)
+  if (n_chunks > kMaxGridYZ || desc->B > kMaxGridYZ)
+    return fail(RAM_ERR_UNSUPPORTED, "n_chunks=%d or B=%d above %d", n_chunks, desc->B, kMaxGridYZ);
   const bool with_bits = fwd_needs_bits(&dt, src);
   const bool with_order = ring_row_order(&dt, src);
   const RingLayout L = ring_layout(&dt, n_chunks, with_bits, with_order);
@@ -506,6 +525,9 @@ ram_status ring_attn_bwd_masks(const ram_attn_desc* desc, int32_t n_chunks, cons
   dt.block_kv = ram::kBlockKV;
   RAM_TRY(check_desc(&dt, kBwdTile, true));
   if (n_chunks < 1) return fail(RAM_ERR_INVALID, "n_chunks=%d must be >= 1", n_chunks);
+  // the rings' per-chunk launches put batch rows and chunks in the grid's y and z (at most 65535)
+  if (n_chunks > kMaxGridYZ || desc->B > kMaxGridYZ)
+    return fail(RAM_ERR_UNSUPPORTED, "n_chunks=%d or B=%d above %d", n_chunks, desc->B, kMaxGridYZ);
   const bool with_bits = src && src->dense;
   const BwdLayout L = bwd_layout(&dt, n_chunks, with_bits);
   out->cls_off = (int64_t)L.cls_off;
@@ -532,6 +554,9 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   desc = &dt;
   RAM_TRY(check_desc(desc, kFwdTile, true));
   if (n_chunks < 1) return fail(RAM_ERR_INVALID, "n_chunks=%d must be >= 1", n_chunks);
+  // the rings' per-chunk launches put batch rows and chunks in the grid's y and z (at most 65535)
+  if (n_chunks > kMaxGridYZ || desc->B > kMaxGridYZ)
+    return fail(RAM_ERR_UNSUPPORTED, "n_chunks=%d or B=%d above %d", n_chunks, desc->B, kMaxGridYZ);
   if (q_shard < -1 || q_shard >= n_chunks)
     return fail(RAM_ERR_INVALID, "q_shard=%d outside [-1, %d)", q_shard, n_chunks);
   const int64_t kv_total = (int64_t)n_chunks * desc->Skv;
@@ -607,6 +632,13 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
     float* lse2 = reinterpret_cast<float*>(ws + L.lse2_off);
     const ram::RingSplit halves{acc2, lse2};
     if (!split) p.out_final = out;   // the last visit writes the bf16 result
+    if (ring_packs_v(desc)) {
+      // V of every chunk repacked so that the kernel reads its operands with row reads
+      e = ram::launch_pack_v(v_all, kv_full_stride, desc->B, n_chunks, desc->Skv, desc->Hkv, ws + L.vt_off, stream);
+      if (e != hipSuccess) return hip_fail(e, "ring V pack launch");
+      p.vt = ws + L.vt_off;
+      p.vt_chunk_bytes = (int64_t)ram::pack_v_bytes(desc->B, 1, desc->Skv, desc->Hkv);
+    }
     if (g_ev_start && (e = hipEventRecord(g_ev_start, stream)) != hipSuccess) return hip_fail(e, "event record");
     e = ram::launch_attn_alt(p, split ? &halves : nullptr, stream);
     if (e != hipSuccess) return hip_fail(e, "ring launch");
@@ -738,6 +770,9 @@ ram_status ring_attn_bwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
   RAM_TRY(check_desc(desc, kBwdTile, true));
   RAM_TRY(check_bwd_support(desc));
   if (n_chunks < 1) return fail(RAM_ERR_INVALID, "n_chunks=%d must be >= 1", n_chunks);
+  // the rings' per-chunk launches put batch rows and chunks in the grid's y and z (at most 65535)
+  if (n_chunks > kMaxGridYZ || desc->B > kMaxGridYZ)
+    return fail(RAM_ERR_UNSUPPORTED, "n_chunks=%d or B=%d above %d", n_chunks, desc->B, kMaxGridYZ);
   if (q_shard < -1 || q_shard >= n_chunks)
     return fail(RAM_ERR_INVALID, "q_shard=%d outside [-1, %d)", q_shard, n_chunks);
   const int64_t kv_total = (int64_t)n_chunks * desc->Skv;

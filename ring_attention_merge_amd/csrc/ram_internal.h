@@ -62,6 +62,10 @@ struct AttnParams {
   // or null: the rows (b * nQb + qb) in the order workgroups take them (most tiles first, made by
   // launch_row_order); heads are the inner index, workgroups go to the XCDs round robin
   const int32_t* row_order;
+  // or null (bf16, D = 128 kernel only): V repacked by launch_pack_v, read with row reads instead
+  // of transposing ones; chunk c at + c * vt_chunk_bytes, then [B][Hkv][ceil(Skv / 32)] tiles
+  const void* vt;
+  int64_t vt_chunk_bytes;
 };
 
 // A split ring (launch_attn_alt with this given): each q tile row's visits go to two
@@ -128,6 +132,17 @@ hipError_t launch_col_lists(const MaskParams& p, int n_chunks, int32_t* col_cnt,
 // bf16, D = 128, mask tiles of kAltRows rows: one visit per chunk (n_chunks = 1 for a single chunk).
 // Kernels without kv positions, kv segments or tile bits mask PARTIAL tiles by positions;
 // with any of them, PARTIAL tiles are masked from mask_bits, which must then be set.
+// V of every chunk of a ring [B, kv_stride_b (elements), keys n_chunks * Skv, Hkv, D = 128], bf16,
+// repacked for the bf16 D = 128 kernel: per (chunk, batch, kv head) ceil(Skv / 32) tiles of 8 KiB,
+// each the LDS image of one 32-key step of V in the order of the weights' operand (keys past Skv
+// zero).
+constexpr int kPackKeys = 32;                   // keys per repacked V tile (one kernel step)
+constexpr int kPackTileBytes = kPackKeys * 256; // 32 keys x 128 dims x 2 bytes
+inline size_t pack_v_bytes(int B, int n_chunks, int Skv, int Hkv) {
+  return (size_t)n_chunks * B * Hkv * ((Skv + kPackKeys - 1) / kPackKeys) * kPackTileBytes;
+}
+hipError_t launch_pack_v(const void* v_all, int64_t kv_stride_b, int B, int n_chunks, int Skv, int Hkv, void* vt,
+                         hipStream_t s);
 hipError_t launch_attn_alt(const AttnParams& p, const RingSplit* split, hipStream_t s);
 hipError_t launch_block_mask(const MaskParams& p, int n_chunks, hipStream_t s);
 // order[0 .. rows): the rows of tiles sorted by their non-EMPTY tiles summed over the n_chunks

@@ -281,6 +281,15 @@ def test_ring_validation_and_workspace(lib):
     tiles2 = 4 * 64 * 64
     assert lib.ring_attn_workspace_bytes(ctypes.byref(d2), 4, None) == (
         2 * acc + al(tiles2) + al(4 * 64 * 4) + tiles2 * 4)
+    # Sq * H / Hkv >= 32768 without a cap: V of every chunk also rearranged for the kernel, in
+    # tiles of 32 keys x 128 dims (8 KiB) per kv head, a ragged chunk rounded up to 32 keys
+    d3 = _desc(B=1, Sq=32768, Skv=4000, H=32, Hkv=8)
+    acc3, tiles3 = 32768 * 32 * 128 * 4, 8 * 256 * 63
+    base3 = acc3 + al(tiles3) + al(8 * 256 * 4) + al(tiles3 * 4)
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(d3), 8, None) == base3 + 8 * 8 * 125 * 8192
+    d3c = _desc(B=1, Sq=32768, Skv=4000, H=32, Hkv=8, softcap=50.0)
+    assert lib.ring_attn_workspace_bytes(ctypes.byref(d3c), 8, None) == base3
+    assert _ring(lib, d, 65536, -1) == _lib.RAM_ERR_UNSUPPORTED and "65535" in _err(lib)
     assert lib.ring_attn_workspace_bytes(ctypes.byref(d), 0, None) == 0
     assert _ring(lib, d, 0, -1) == _lib.RAM_ERR_INVALID
     assert _ring(lib, d, 4, 4) == _lib.RAM_ERR_INVALID and "q_shard" in _err(lib)

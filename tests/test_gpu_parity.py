@@ -230,6 +230,10 @@ SMALL_RING = {
                                     dtype="f32", seed=18, with_sinks=True, softcap=2.0),
     "ragged_chunks_noncausal": lambda: wl.make("nc", B=1, H=2, Hkv=2, Sq=100, chunk=70, n_chunks=3, D=128,
                                                causal=False, seed=19, with_sinks=True),
+    # Sq * H / Hkv = 32768 without a cap: V is repacked for row reads; 256 rows of q tiles, so the
+    # visits are split over two workgroups; chunks of 1000 keys end inside a 32-key tile
+    "packed_v_mqa_split_ragged": lambda: wl.make("pv", B=1, H=8, Hkv=1, Sq=4096, chunk=1000, n_chunks=3, D=128,
+                                                 q_shard=1, seed=20),
 }
 
 
@@ -250,6 +254,12 @@ UNSPLIT_RING = {
                                 docs=(64, 700, 0.05), seed=32),
     "cap_sinks_h64": lambda: wl.make("u3", B=1, H=64, Hkv=4, Sq=1024, chunk=384, n_chunks=3, D=128, softcap=30.0,
                                      with_sinks=True, seed=33),
+    # Sq * H / Hkv >= 32768 without a cap: the ring reads V repacked (the chunk calls read it as
+    # given), so bit-identity checks the repacked operands element for element; ragged chunks
+    "packed_v_shard2of4_h64": lambda: wl.make("u4", B=1, H=64, Hkv=2, Sq=1024, chunk=500, n_chunks=4, D=128,
+                                              q_shard=2, seed=34),
+    "packed_v_docs_h64": lambda: wl.make("u5", B=2, H=64, Hkv=4, Sq=2080, chunk=520, n_chunks=4, D=128,
+                                         docs=(64, 700, 0.05), seed=35),
 }
 
 
