@@ -20,9 +20,11 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// With out_bf16 set, the merged rows (and the rows the block leaves unchanged) are written there
+// in bf16 instead of back into out_acc: the merge and the final cast in one pass.
 __global__ __launch_bounds__(kThreads) void merge_kernel(int B, int Sq, int H, int D, float* out_acc,
                                                          float* lse_acc, const float* out_blk,
-                                                         const float* lse_blk) {
+                                                         const float* lse_blk, __bf16* out_bf16) {
   const int lpr = D / 4;                      // lanes per row (16 or 32)
   const int rows_per_block = kThreads / lpr;
   const int64_t row = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / lpr;
@@ -36,15 +38,17 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int B, int Sq, int H, i
   const int64_t li = ((int64_t)b * H + h) * Sq + q;
   const float la = lse_acc[li];
   const float lb = lse_blk[li];
-  if (lb == -__builtin_inff()) return;
+  if (lb == -__builtin_inff() && !out_bf16) return;
   float4* pa = reinterpret_cast<float4*>(out_acc + row * D) + part;
-  const float4 ob = reinterpret_cast<const float4*>(out_blk + row * D)[part];
   float4 o;
-  float nl;
-  if (la == -__builtin_inff()) {
-    o = ob;
+  float nl = la;
+  if (lb == -__builtin_inff()) {
+    o = *pa;
+  } else if (la == -__builtin_inff()) {
+    o = reinterpret_cast<const float4*>(out_blk + row * D)[part];
     nl = lb;
   } else {
+    const float4 ob = reinterpret_cast<const float4*>(out_blk + row * D)[part];
     const float x = lb - la;
     const float sig = 1.0f / (1.0f + expf(-x));
     nl = la + (fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))));
@@ -54,7 +58,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int B, int Sq, int H, i
     o.z = a.z - sig * (a.z - ob.z);
     o.w = a.w - sig * (a.w - ob.w);
   }
-  *pa = o;
+  if (out_bf16) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 v = {o.x, o.y, o.z, o.w};
+    reinterpret_cast<bf16x4*>(out_bf16 + row * D)[part] = __builtin_convertvector(v, bf16x4);
+  } else {
+    *pa = o;
+  }
   if (part == 0) lse_acc[li] = nl;
 }
 
@@ -72,13 +83,13 @@ __global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const float* src, _
 }  // namespace
 
 hipError_t launch_merge(int B, int Sq, int H, int D, float* out_acc, float* lse_acc,
-                        const float* out_blk, const float* lse_blk, hipStream_t s) {
+                        const float* out_blk, const float* lse_blk, hipStream_t s, void* out_bf16) {
   const int64_t n_rows = (int64_t)B * Sq * H;
   if (n_rows == 0) return hipSuccess;
   const int rows_per_block = kThreads / (D / 4);
   const int64_t grid = (n_rows + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, B, Sq, H, D, out_acc,
-                     lse_acc, out_blk, lse_blk);
+                     lse_acc, out_blk, lse_blk, static_cast<__bf16*>(out_bf16));
   return hipGetLastError();
 }
 

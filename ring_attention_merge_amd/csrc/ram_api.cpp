@@ -644,9 +644,8 @@ ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32
     if (e != hipSuccess) return hip_fail(e, "ring launch");
     if (g_ev_stop && (e = hipEventRecord(g_ev_stop, stream)) != hipSuccess) return hip_fail(e, "event record");
     if (split) {
-      // the second half's running result merged into the first's, then the bf16 result
-      e = ram::launch_merge(desc->B, desc->Sq, desc->H, desc->D, acc, lse, acc2, lse2, stream);
-      if (e == hipSuccess) e = ram::launch_cast_bf16(acc, out, (int64_t)desc->B * desc->Sq * desc->H * desc->D, stream);
+      // the second half's running result merged into the first's, written as the bf16 result
+      e = ram::launch_merge(desc->B, desc->Sq, desc->H, desc->D, acc, lse, acc2, lse2, stream, out);
       if (e != hipSuccess) return hip_fail(e, "split ring merge launch");
     }
     return ok();

@@ -150,8 +150,10 @@ hipError_t launch_block_mask(const MaskParams& p, int n_chunks, hipStream_t s);
 // count as 4095; rows with equal totals in any order).
 hipError_t launch_row_order(const int32_t* row_cnt, int n_chunks, int64_t rows, int max_tiles, int32_t* order,
                             hipStream_t s);
+// lse merge of a block's (out, lse) into the running ones; with out_bf16 set, the merged rows go
+// there in bf16 (bf16 [B,Sq,H,D]) instead of back into out_acc
 hipError_t launch_merge(int B, int Sq, int H, int D, float* out_acc, float* lse_acc,
-                        const float* out_blk, const float* lse_blk, hipStream_t s);
+                        const float* out_blk, const float* lse_blk, hipStream_t s, void* out_bf16 = nullptr);
 hipError_t launch_cast_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
 // dst[b * dst_stride + i] = sum over s < S of src[s * part_stride + b * n + i], i < n, b < B
 // (a fixed order: deterministic).

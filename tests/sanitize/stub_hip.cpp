@@ -20,7 +20,7 @@ hipError_t launch_attn_alt(const AttnParams&, const RingSplit*, hipStream_t) { r
 hipError_t launch_pack_v(const void*, int64_t, int, int, int, int, void*, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_block_mask(const MaskParams&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_row_order(const int32_t*, int, int64_t, int, int32_t*, hipStream_t) { return hipErrorNoDevice; }
-hipError_t launch_merge(int, int, int, int, float*, float*, const float*, const float*, hipStream_t) {
+hipError_t launch_merge(int, int, int, int, float*, float*, const float*, const float*, hipStream_t, void*) {
   return hipErrorNoDevice;
 }
 hipError_t launch_cast_bf16(const float*, void*, int64_t, hipStream_t) { return hipErrorNoDevice; }
