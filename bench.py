@@ -62,16 +62,23 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
 KERNEL = "attn_fwd_bf16_alt"    # the bf16 D = 128 forward kernel the ring launches
 
 
-def ring_kernel_name(cap: bool, bits: bool, split: bool) -> str:
-    """The kernel instantiation a ring launch runs (soft cap, stored mask bits, split ring)."""
+def ring_kernel_name(cap: bool, bits: bool, split: bool, packed_v: bool) -> str:
+    """The kernel instantiation a ring launch runs (soft cap, stored mask bits, split ring, V
+    repacked for row reads)."""
     f = lambda x: str(bool(x)).lower()
-    return f"{KERNEL}<{f(cap)}, {f(bits)}, {f(split)}>"
+    return f"{KERNEL}<{f(cap)}, {f(bits)}, {f(split)}, {f(packed_v)}>"
 
 
 def ring_splits(w, bq: int) -> bool:
     """Whether the ring runs each row of q tiles as two half rings (the library does so when its
     rows of 128-row tiles give fewer than 512 workgroups)."""
     return w.n_chunks >= 2 and w.B * w.H * -(-w.Sq // bq) < 512
+
+
+def ring_packs_v(w) -> bool:
+    """Whether the ring reads V repacked for row reads (the library does so without a soft cap when
+    Sq * H / Hkv >= 32768)."""
+    return not w.softcap and w.Sq * (w.H // w.Hkv) >= 32768
 
 
 def log(*a):
@@ -511,7 +518,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": recorded_traffic(args.workload) if alt else None,
-                "kernel": ring_kernel_name(w.softcap, bits, split) if alt else "per-chunk launches",
+                "kernel": ring_kernel_name(w.softcap, bits, split, ring_packs_v(w)) if alt else "per-chunk launches",
                 "launches_per_step": launches, "median_step_kernel_us": round(1e3 * kern_ms, 1),
                 "mean_launch_us": round(1e3 * kern_ms / launches, 2),
                 "timing": "HIP events around the attention launch in each of the timed steps; median",
