@@ -19,13 +19,20 @@
 //    S(j); then O^T += V(j)^T P(j)^T beside the bf16 packing and row sum of S(j); one barrier;
 //    then the DMA of step j+kAltStages, the LDS reads of the next operands (K(j+2), V(j+1)),
 //    and the mask and row max of S(j+1). The loop is unrolled by the ring depth, so stage
-//    offsets are immediates of the reads and the two score register sets alternate. Scores are transposed, so a lane owns one query row:
-//    row max and row sum are in-lane plus one v_permlane32_swap with the partner lane.
+//    offsets are immediates of the reads and the two score register sets alternate. Scores are
+//    transposed, so a lane owns one query row: row max and row sum are in-lane plus one
+//    v_permlane32_swap with the partner lane.
 //  * K / V step tiles (32 keys x 256 B each, 16-byte chunks XOR-swizzled so the operand reads
 //    are free of bank conflicts) come into a ring of kAltStages LDS stages by LDS DMA. The DMA
 //    is issued from inline assembly, so the compiler does not see its LDS writes and places
 //    its own waits only for the LDS reads it issues; the kernel orders the DMA with vmcnt waits
 //    (only for the tile the next reads need) and barriers, both compiler memory barriers.
+//  * V operands: read with transposing LDS reads from V's own rows, or (VP instantiations, the
+//    rings that repack V with pack_v_kernel) with row reads like K's, from tiles that already
+//    hold each lane's eight keys in the order the weights feed the product. A transposing read
+//    moves under half the bytes per cycle of a row read.
+//  * Soft cap: a step keeps u = -1 / (1 + exp2(2 scale log2(e) s / cap)); the capped logit is
+//    cap log2(e) (1 + 2u), an affine map folded into the row maximum and the exponentials.
 //  * Masks: FULL tiles run no mask code. PARTIAL tiles are masked either by one compare per
 //    score against a per-row key limit (sequential key positions, no segments, no dense mask)
 //    or, in the BITS instantiations, from the tile's stored element bits, which come into LDS
