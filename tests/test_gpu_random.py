@@ -1,0 +1,89 @@
+"""Randomized parity sweep of ring_attn_fwd_1gpu against the float64 oracle.
+
+Seeded random small rings crossing the features the fixed cases test one by one: batch rows,
+kv-head grouping (GQA / MQA), head dim, dtype, ragged query and chunk lengths, chunk count and
+ring shard, causal or not, soft cap, sinks, packed documents (segment IDs and positions that
+restart per document), and dense masks read either over all keys or reused at every step. A
+few cases have Sq * H / Hkv >= 32768, where the ring reads V repacked. Each case is compared
+element by element with oracle.chunked (the pages' per-chunk attention folded by the LSE
+merge) at the stated tolerances; the seed names the case."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_attention_merge_amd as ram
+from ring_attention_merge_amd import workloads as wl
+from gpu_util import compare, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+N_CASES = 100
+N_PACKED_V = 5
+
+
+def _case(seed: int) -> dict:
+    rng = np.random.default_rng(70_000 + seed)
+    if seed >= N_CASES:
+        # large enough for the repacked-V path: Sq * H / Hkv >= 32768, no soft cap
+        n = int(rng.integers(1, 4))
+        return dict(dtype="bf16", D=128, B=1, Hkv=1, H=8, Sq=4096, chunk=int(rng.integers(200, 700)), n=n,
+                    q_shard=int(rng.integers(-1, n)), causal=bool(rng.random() < 0.7), cap=None,
+                    sinks=bool(rng.random() < 0.5), feature="dense" if rng.random() < 0.4 else "plain",
+                    reuse=bool(rng.random() < 0.3), seed=seed)
+    feature = str(rng.choice(["plain", "docs", "dense"], p=[0.5, 0.25, 0.25]))
+    dtype = "f32" if rng.random() < 0.15 else "bf16"
+    n = int(rng.integers(1, 5))
+    c = dict(dtype=dtype, D=64 if rng.random() < 0.3 else 128, B=int(rng.integers(1, 3)),
+             Hkv=int(rng.choice([1, 2, 4])), n=n, causal=bool(rng.random() < 0.7),
+             cap=float(rng.uniform(2.0, 60.0)) if rng.random() < 0.3 else None, sinks=bool(rng.random() < 0.3),
+             feature=feature, reuse=bool(rng.random() < 0.3), seed=seed)
+    c["H"] = c["Hkv"] * int(rng.choice([1, 2, 4]))
+    if feature == "docs":
+        c["chunk"] = int(rng.integers(16, 400))
+        c["Sq"] = c["chunk"] * n
+        c["q_shard"] = -1
+    else:
+        c["chunk"] = int(rng.integers(1, 500))
+        c["Sq"] = int(rng.integers(1, 600))
+        c["q_shard"] = int(rng.integers(-1, n))
+    return c
+
+
+@pytest.mark.parametrize("seed", list(range(N_CASES + N_PACKED_V)))
+def test_random_ring(seed):
+    c = _case(seed)
+    docs = (16, max(32, c["Sq"] // 2), 0.05) if c["feature"] == "docs" else None
+    w = wl.make(f"rand{seed}", B=c["B"], H=c["H"], Hkv=c["Hkv"], Sq=c["Sq"], chunk=c["chunk"], n_chunks=c["n"],
+                D=c["D"], dtype=c["dtype"], causal=c["causal"], softcap=c["cap"], with_sinks=c["sinks"],
+                q_shard=c["q_shard"], docs=docs, seed=seed)
+    C, n, r = c["chunk"], c["n"], c["q_shard"]
+    dense, step = None, 0
+    if c["feature"] == "dense":
+        rng = np.random.default_rng(90_000 + seed)
+        step = 0 if c["reuse"] else C
+        cols = C + (n - 1) * step
+        dense = wl.dense_mask(rng, w.Sq, cols, q_offset=0 if c["reuse"] else w.q_pos_base,
+                              window=int(rng.integers(8, 200)), n_global=int(rng.integers(0, 8)), block=64)
+    say(f"random ring {seed}: {c}")
+    d = ram.Desc(B=w.B, Sq=w.Sq, Skv=C, H=w.H, Hkv=w.Hkv, D=w.D,
+                 dtype=ram.RAM_BF16 if w.dtype == "bf16" else ram.RAM_F32, scale=w.scale,
+                 softcap=w.softcap or 0.0, causal=w.causal)
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(DEV)
+    src = ram.MaskSrc(q_pos=t(w.q_pos), kv_pos=t(w.kv_pos), q_seg=t(w.q_seg), kv_seg=t(w.kv_seg),
+                      dense=None if dense is None else torch.from_numpy(dense).to(DEV), dense_chunk_step=step)
+    out = torch.full((w.B, w.Sq, w.H, w.D), float("nan"), device=DEV).to(w.q.dtype)
+    lse = torch.full((w.B, w.H, w.Sq), float("nan"), device=DEV)
+    ws = torch.empty(max(1, ram.ring_attn_workspace_bytes(d, n, src)), dtype=torch.uint8, device=DEV)
+    sinks = None if w.sinks is None else w.sinks.to(DEV)
+    ram.ring_attn_fwd_1gpu(d, n, r, w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), src, sinks, out, lse, ws)
+    torch.cuda.synchronize()
+    q, k, v, s64 = w.as_f64()
+    qp, kp = w.positions()
+    order = [(r - i) % n for i in range(n)] if r >= 0 else list(range(n))
+    ro, rl = oracle.chunked(q, k, v, scale=w.scale, q_pos=qp, kv_pos=kp, bounds=[(i * C, (i + 1) * C) for i in range(n)],
+                            order=order, q_seg=w.q_seg, kv_seg=w.kv_seg, causal=w.causal, softcap=w.softcap,
+                            sinks=s64, dense=dense, dense_col0=None if dense is None else [i * step for i in range(n)])
+    compare(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, w.dtype, f"random ring {seed}")
