@@ -24,9 +24,9 @@ N_CASES = 100
 N_PACKED_V = 5
 
 
-def _case(seed: int) -> dict:
+def _case(seed: int, large: bool = False) -> dict:
     rng = np.random.default_rng(70_000 + seed)
-    if seed >= N_CASES:
+    if large:
         # large enough for the repacked-V path: Sq * H / Hkv >= 32768, no soft cap
         n = int(rng.integers(1, 4))
         return dict(dtype="bf16", D=128, B=1, Hkv=1, H=8, Sq=4096, chunk=int(rng.integers(200, 700)), n=n,
@@ -54,7 +54,7 @@ def _case(seed: int) -> dict:
 
 @pytest.mark.parametrize("seed", list(range(N_CASES + N_PACKED_V)))
 def test_random_ring(seed):
-    c = _case(seed)
+    c = _case(seed, large=seed >= N_CASES)
     docs = (16, max(32, c["Sq"] // 2), 0.05) if c["feature"] == "docs" else None
     w = wl.make(f"rand{seed}", B=c["B"], H=c["H"], Hkv=c["Hkv"], Sq=c["Sq"], chunk=c["chunk"], n_chunks=c["n"],
                 D=c["D"], dtype=c["dtype"], causal=c["causal"], softcap=c["cap"], with_sinks=c["sinks"],
@@ -87,3 +87,68 @@ def test_random_ring(seed):
                             order=order, q_seg=w.q_seg, kv_seg=w.kv_seg, causal=w.causal, softcap=w.softcap,
                             sinks=s64, dense=dense, dense_col0=None if dense is None else [i * step for i in range(n)])
     compare(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, w.dtype, f"random ring {seed}")
+
+
+# ------------------------------------------------------------------------------ backward
+N_BWD_CASES = 30
+
+
+@pytest.mark.parametrize("seed", list(range(N_BWD_CASES)))
+def test_random_ring_backward(seed):
+    """ring_attn_bwd_1gpu on seeded random small rings (the forward's feature mix at smaller sizes)
+    against oracle.chunked_bwd: dq, dk, dv at max error / max |ref|, dsinks against the sum of its
+    terms' magnitudes, at the backward tolerances."""
+    from test_gpu_backward import GRAD_TOL, GRAD_TOL_F32, SINK_TOL, _rel, _sinks_check
+    c = _case(5000 + seed)
+    c["Sq"] = min(c["Sq"], 400)
+    c["chunk"] = min(c["chunk"], 300)
+    if c["feature"] == "docs":
+        c["Sq"] = c["chunk"] * c["n"]
+    docs = (16, max(32, c["Sq"] // 2), 0.05) if c["feature"] == "docs" else None
+    w = wl.make(f"randb{seed}", B=c["B"], H=c["H"], Hkv=c["Hkv"], Sq=c["Sq"], chunk=c["chunk"], n_chunks=c["n"],
+                D=c["D"], dtype=c["dtype"], causal=c["causal"], softcap=c["cap"], with_sinks=c["sinks"],
+                q_shard=c["q_shard"], docs=docs, seed=20_000 + seed)
+    C, n, r = c["chunk"], c["n"], c["q_shard"]
+    dense, step = None, 0
+    if c["feature"] == "dense":
+        rng = np.random.default_rng(95_000 + seed)
+        step = 0 if c["reuse"] else C
+        cols = C + (n - 1) * step
+        dense = wl.dense_mask(rng, w.Sq, cols, q_offset=0 if c["reuse"] else w.q_pos_base,
+                              window=int(rng.integers(8, 200)), n_global=int(rng.integers(0, 8)), block=64)
+    say(f"random ring backward {seed}: {c}")
+    d = ram.Desc(B=w.B, Sq=w.Sq, Skv=C, H=w.H, Hkv=w.Hkv, D=w.D,
+                 dtype=ram.RAM_BF16 if w.dtype == "bf16" else ram.RAM_F32, scale=w.scale,
+                 softcap=w.softcap or 0.0, causal=w.causal)
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(DEV)
+    src = ram.MaskSrc(q_pos=t(w.q_pos), kv_pos=t(w.kv_pos), q_seg=t(w.q_seg), kv_seg=t(w.kv_seg),
+                      dense=None if dense is None else torch.from_numpy(dense).to(DEV), dense_chunk_step=step)
+    q, k, v = w.q.to(DEV), w.k.to(DEV), w.v.to(DEV)
+    sinks = None if w.sinks is None else w.sinks.to(DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.Sq, device=DEV)
+    ws = torch.empty(max(1, ram.ring_attn_workspace_bytes(d, n, src)), dtype=torch.uint8, device=DEV)
+    ram.ring_attn_fwd_1gpu(d, n, r, q, k, v, src, sinks, out, lse, ws)
+    dout = torch.from_numpy(np.random.default_rng(30_000 + seed).standard_normal(
+        (w.B, w.Sq, w.H, w.D)).astype(np.float32)).to(w.q.dtype)
+    dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+    dsinks = None if sinks is None else torch.full((w.H,), float("nan"), device=DEV)
+    wsb = torch.empty(max(1, ram.ring_attn_bwd_workspace_bytes(d, n, src)), dtype=torch.uint8, device=DEV)
+    ram.ring_attn_bwd_1gpu(d, n, r, q, k, v, out, lse, dout.to(DEV), src, sinks, dq, dk, dv, dsinks, wsb)
+    torch.cuda.synchronize()
+    q64, k64, v64, s64 = w.as_f64()
+    qp, kp = w.positions()
+    kw = dict(scale=w.scale, q_pos=qp, kv_pos=kp, q_seg=w.q_seg, kv_seg=w.kv_seg, causal=w.causal,
+              softcap=w.softcap, sinks=s64, dense=dense,
+              dense_col0=None if dense is None else [i * step for i in range(n)])
+    rq, rk, rv, rs = oracle.chunked_bwd(q64, k64, v64, dout.double().numpy(),
+                                        bounds=[(i * C, (i + 1) * C) for i in range(n)], **kw)
+    tol = GRAD_TOL_F32 if w.dtype == "f32" else GRAD_TOL
+    what = f"random ring backward {seed}"
+    for nm, g, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _rel(nm, g.float().cpu().numpy(), ref, tol, what)
+    if sinks is not None:
+        order = [(r - i) % n for i in range(n)] if r >= 0 else list(range(n))
+        ro, rl = oracle.chunked(q64, k64, v64, bounds=[(i * C, (i + 1) * C) for i in range(n)], order=order, **kw)
+        _sinks_check(dsinks.cpu().numpy(), rs, ro, rl, dout.double().numpy(), s64, what,
+                     GRAD_TOL_F32 if w.dtype == "f32" else SINK_TOL)
