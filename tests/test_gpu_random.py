@@ -152,3 +152,77 @@ def test_random_ring_backward(seed):
         ro, rl = oracle.chunked(q64, k64, v64, bounds=[(i * C, (i + 1) * C) for i in range(n)], order=order, **kw)
         _sinks_check(dsinks.cpu().numpy(), rs, ro, rl, dout.double().numpy(), s64, what,
                      GRAD_TOL_F32 if w.dtype == "f32" else SINK_TOL)
+
+
+# ------------------------------------------------------------------------------ block masks
+N_MASK_CASES = 60
+POISON = 0x5A5A5A5A
+
+
+@pytest.mark.parametrize("seed", list(range(N_MASK_CASES)))
+def test_random_block_mask_bitexact(seed):
+    """build_block_mask on seeded random inputs: tile sizes in [16, 512], ragged lengths,
+    sequential positions with offsets, shuffled positions or packed documents, random segment
+    IDs with padding, causal or not, with or without a dense mask and tile bits. Classes, row
+    counts, lists and the bits of PARTIAL tiles must equal oracle.block_mask / oracle.partial_bits
+    bit for bit, and no bits may be written outside PARTIAL tiles."""
+    rng = np.random.default_rng(110_000 + seed)
+    B = int(rng.integers(1, 3))
+    Sq, Skv = int(rng.integers(1, 1500)), int(rng.integers(1, 1500))
+    bq, bk = int(rng.integers(16, 513)), int(rng.integers(16, 513))
+    causal = bool(rng.random() < 0.7)
+    kind = str(rng.choice(["seq", "shuffle", "docs", "segs"]))
+    with_dense = bool(rng.random() < 0.4)
+    with_bits = with_dense or bool(rng.random() < 0.5)
+    qb = kb = 0
+    qp = kp = qs = ks = None
+    if kind == "seq":
+        qb, kb = int(rng.integers(-500, 3000)), int(rng.integers(0, 3000))
+    elif kind == "shuffle":
+        qp = rng.integers(0, 2000, size=(B, Sq)).astype(np.int32)
+        kp = rng.integers(0, 2000, size=(B, Skv)).astype(np.int32)
+    elif kind == "docs":
+        Skv = Sq
+        qs, qp, _ = wl.packed_documents(rng, B, Sq, 8, max(16, Sq // 3), 0.05)
+        ks, kp = qs, qp
+    else:
+        qs = rng.integers(-1, 4, size=(B, Sq)).astype(np.int32)
+        ks = rng.integers(-1, 4, size=(B, Skv)).astype(np.int32)
+    dense = None
+    if with_dense:
+        dense = wl.dense_mask(rng, Sq, Skv, q_offset=qb - kb, window=int(rng.integers(4, 300)),
+                              n_global=int(rng.integers(0, 20)), block=int(rng.integers(16, 200)))
+    say(f"random block mask {seed}: B={B} Sq={Sq} Skv={Skv} tile={bq}x{bk} causal={causal} {kind} "
+        f"dense={with_dense} bits={with_bits} q_base={qb} kv_base={kb}")
+    d = ram.Desc(B=B, Sq=Sq, Skv=Skv, H=1, Hkv=1, D=128, causal=causal, block_q=bq, block_kv=bk)
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(DEV)
+    src = ram.MaskSrc(q_pos=t(qp), kv_pos=t(kp), q_seg=t(qs), kv_seg=t(ks), q_pos_base=qb, kv_pos_base=kb,
+                      dense=None if dense is None else torch.from_numpy(dense).to(DEV))
+    bm = ram.alloc_block_mask(d, with_bits=with_bits)
+    bm.tile_class.fill_(0xAB)
+    bm.row_cnt.fill_(-7)
+    bm.col_idx.fill_(-7)
+    if with_bits:
+        bm.bits.fill_(POISON)
+    ram.build_block_mask(d, src, bm)
+    torch.cuda.synchronize()
+    nQb, nKb, W = bm.nQb, bm.nKb, -(-bk // 32)
+    cls = bm.tile_class.cpu().numpy()[: B * nQb * nKb].reshape(B, nQb, nKb)
+    cnt = bm.row_cnt.cpu().numpy()[: B * nQb].reshape(B, nQb)
+    col = bm.col_idx.cpu().numpy()[: B * nQb * nKb].reshape(B, nQb, nKb)
+    if with_bits:
+        bits = bm.bits.cpu().numpy().view(np.uint32)[: B * nQb * nKb * bq * W].reshape(B, nQb, nKb, bq, W)
+    for b in range(B):
+        qpb = qp[b] if qp is not None else qb + np.arange(Sq)
+        kpb = kp[b] if kp is not None else kb + np.arange(Skv)
+        ok = oracle.allowed(qpb, kpb, None if qs is None else qs[b], None if ks is None else ks[b], causal,
+                            dense=dense)
+        rc, rn, ri = oracle.block_mask(ok, bq, bk)
+        assert np.array_equal(cls[b], rc), f"classes differ (b={b})"
+        assert np.array_equal(cnt[b], rn), f"row counts differ (b={b})"
+        assert np.array_equal(col[b], ri), f"tile lists differ (b={b})"
+        if with_bits:
+            rb = oracle.partial_bits(ok, bq, bk)
+            part = rc == oracle.TILE_PARTIAL
+            assert np.array_equal(bits[b][part], rb[part]), f"PARTIAL tile bits differ (b={b})"
+            assert np.all(bits[b][~part] == POISON), f"bits written outside PARTIAL tiles (b={b})"
