@@ -54,7 +54,11 @@ def _case(seed: int, large: bool = False) -> dict:
 
 @pytest.mark.parametrize("seed", list(range(N_CASES + N_PACKED_V)))
 def test_random_ring(seed):
-    c = _case(seed, large=seed >= N_CASES)
+    check_ring(seed, _case(seed, large=seed >= N_CASES))
+
+
+def check_ring(seed: int, c: dict):
+    """One random ring forward against the oracle (the case drawn by _case)."""
     docs = (16, max(32, c["Sq"] // 2), 0.05) if c["feature"] == "docs" else None
     w = wl.make(f"rand{seed}", B=c["B"], H=c["H"], Hkv=c["Hkv"], Sq=c["Sq"], chunk=c["chunk"], n_chunks=c["n"],
                 D=c["D"], dtype=c["dtype"], causal=c["causal"], softcap=c["cap"], with_sinks=c["sinks"],
@@ -98,8 +102,13 @@ def test_random_ring_backward(seed):
     """ring_attn_bwd_1gpu on seeded random small rings (the forward's feature mix at smaller sizes)
     against oracle.chunked_bwd: dq, dk, dv at max error / max |ref|, dsinks against the sum of its
     terms' magnitudes, at the backward tolerances."""
+    check_ring_backward(seed, _case(5000 + seed))
+
+
+def check_ring_backward(seed: int, c: dict):
+    """One random ring backward against the oracle."""
     from test_gpu_backward import GRAD_TOL, GRAD_TOL_F32, SINK_TOL, _rel, _sinks_check
-    c = _case(5000 + seed)
+    c = dict(c)
     c["Sq"] = min(c["Sq"], 400)
     c["chunk"] = min(c["chunk"], 300)
     if c["feature"] == "docs":
