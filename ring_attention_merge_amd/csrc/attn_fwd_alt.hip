@@ -17,11 +17,12 @@
 //    keys. Step j of a wave: S(j+1) = K(j+1) Q^T (v_mfma_f32_32x32x16_bf16, K from registers,
 //    Q held for the whole launch) in fenced groups of one product beside two exponentials of
 //    S(j); then O^T += V(j)^T P(j)^T beside the bf16 packing and row sum of S(j); one barrier;
-//    then the DMA of step j+kAltStages, the LDS reads of the next operands (K(j+2), V(j+1)),
-//    and the mask and row max of S(j+1). The loop is unrolled by the ring depth, so stage
-//    offsets are immediates of the reads and the two score register sets alternate. Scores are
-//    transposed, so a lane owns one query row: row max and row sum are in-lane plus one
-//    v_permlane32_swap with the partner lane.
+//    then the LDS reads of the next operands (K(j+2), V(j+1)), and the mask and row max of
+//    S(j+1). The DMA of step j+kAltStages-1 goes out beside the last four products of S(j+1),
+//    one instruction each (with a soft cap: the DMA of step j+kAltStages after the barrier).
+//    The loop is unrolled by the ring depth, so stage offsets are immediates of the reads and
+//    the two score register sets alternate. Scores are transposed, so a lane owns one query
+//    row: row max and row sum are in-lane plus one v_permlane32_swap with the partner lane.
 //  * K / V step tiles (32 keys x 256 B each, 16-byte chunks XOR-swizzled so the operand reads
 //    are free of bank conflicts) come into a ring of kAltStages LDS stages by LDS DMA. The DMA
 //    is issued from inline assembly, so the compiler does not see its LDS writes and places
@@ -174,6 +175,11 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
   constexpr int NS = kAltStages;
   constexpr int SB = alt_stage_bytes<BITS>();
   constexpr int NDMA = 2 * kDmaPerTile + (BITS ? 1 : 0);   // DMA instructions per wave and step
+  // Where a step's DMA is issued. Without a soft cap, the DMA of step j + NS - 1 goes out one
+  // instruction beside each of the last products of S(j+1): a burst of LDS-DMA instructions from
+  // every wave right after the barrier holds each wave for tens of cycles per instruction. With
+  // a cap (VALU-bound), the DMA of step j + NS follows step j's barrier.
+  constexpr bool SPREAD = !CAP;
   // NS stages of SB bytes, then the visit's tile list (AltTile records, p.nKb of them), staged
   // once per visit so that the loop reads it from LDS instead of waiting on scalar loads
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -288,26 +294,34 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
                                     (uint32_t)n_vt * kAltTile)
                         : tile_rsrc(reinterpret_cast<const __bf16*>(pc.v) + (int64_t)b * p.kv_stride_b + g * D,
                                     (uint32_t)p.Skv * row_bytes);
-    // DMA of step s (parity PAR, tile record `tr`) into stage st: this wave's rows of K and V and
-    // (BITS) its 32 rows' bit words of the tile when it is PARTIAL.
-    auto dma_step = [&](auto PAR_, int st, uint2 tr) {
+    // DMA of step s (parity PAR, tile record `tr`) into stage st: this wave's rows of K and V
+    // (dma_piece, instruction i: K rows of piece i / 2 for even i, V rows for odd i) and (BITS,
+    // dma_bits) its 32 rows' bit words of the tile when it is PARTIAL.
+    auto dma_piece = [&](auto PAR_, int st, uint2 tr, int i) {
       constexpr int PAR = decltype(PAR_)::value;
       const uint32_t soff = (tr.x & ~63u) + (PAR ? half_bytes : 0u);
       // packed V: tile (first key / 32 + PAR) of the chunk
       const uint32_t soff_v = VP ? tr.y * (kAltTile / kAltKeys) + (PAR ? (uint32_t)kAltTile : 0u) : soff;
       const uint32_t sb = lds0 + st * SB;
-#pragma unroll
-      for (int i = 0; i < kDmaPerTile; ++i) {
-        dma16(krs, sb + 4 * (w + kAltWaves * i) * 256, koff[i] + soff);
-        dma16(vrs, sb + kAltTile + 4 * (w + kAltWaves * i) * 256, voff[i] + soff_v);
-      }
+      const int t = i >> 1;
+      if ((i & 1) == 0) dma16(krs, sb + 4 * (w + kAltWaves * t) * 256, koff[t] + soff);
+      else dma16(vrs, sb + kAltTile + 4 * (w + kAltWaves * t) * 256, voff[t] + soff_v);
+    };
+    auto dma_bits = [&](auto PAR_, int st, uint2 tr) {
+      constexpr int PAR = decltype(PAR_)::value;
       if constexpr (BITS) {
+        const uint32_t sb = lds0 + st * SB;
         const int kb = (int)(tr.y >> 6);
         const bool partial = ((tr.x >> (2 * PAR)) & 3u) == 2u;
         const uint32_t* words = pc.mask_bits + ((mrow * p.nKb + kb) * kAltRows + w * 32) * 2;
         const auto br = tile_rsrc(words, partial ? 256u : 0u);
         dma4(br, sb + 2 * kAltTile + w * 256, (uint32_t)lane * 4);
       }
+    };
+    auto dma_step = [&](auto PAR_, int st, uint2 tr) {   // all of it
+#pragma unroll
+      for (int i = 0; i < 2 * kDmaPerTile; ++i) dma_piece(PAR_, st, tr, i);
+      dma_bits(PAR_, st, tr);
     };
     // mask kind (0 none, 1 key limit, 2 bits) and lane-relative key limit of a step of parity PAR
     auto step_info = [&](auto PAR_, uint2 tr, int& kind, int& thr) {
@@ -340,7 +354,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
     }
     __syncthreads();
     if (n > 0) {
-      const int pre = min(NS, n);
+      const int pre = min(SPREAD ? NS - 1 : NS, n);
       {
         uint2 inf[(NS + 1) / 2];
 #pragma unroll
@@ -390,7 +404,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         vf[i] = VP ? lds_b128(kad[i] + kAltTile) : lds_v_operand(vad[i & 3] + (i >> 2) * 4096);
-      uint2 inf_dma = info(NS), inf_msk = info(1);
+      uint2 inf_dma = info(SPREAD ? NS - 1 : NS), inf_msk = info(1);
 
       // Step j (stage j % NS == JS): products, barrier, loads. STEADY: a step at least 2 NS - 1
       // steps before the end, which issues its DMA and reads the next operands unconditionally
@@ -410,6 +424,12 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         // matrix products are ready issues first and the other fills the slots between them.
         __builtin_amdgcn_s_setprio(1);
         Sn = f32x16{};
+        // SPREAD: the DMA of step j + NS - 1, into the stage of step j - 1 (every wave is past
+        // the barrier that followed its last reads)
+        const bool dma_now = SPREAD && (STEADY || j + NS - 1 < n);
+        using PD = std::integral_constant<int, (JS + 1) & 1>;
+        constexpr int STD = (JS + NS - 1) % NS;
+        const uint2 inf_ds = SPREAD ? uniform(inf_dma) : uint2{};
         {
           const float msub = (m_ref == neg_inf()) ? 0.0f : m_ref;
           // weight = exp2(logit - m): the logit is sc * s without a cap, c (1 + 2u) with one
@@ -425,7 +445,9 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
             asm volatile("" : "+v"(Sn), "+v"(e0), "+v"(e1));
             Sc[2 * ds] = e0;
             Sc[2 * ds + 1] = e1;
+            if (ds >= 8 - 2 * kDmaPerTile && dma_now) dma_piece(PD{}, STD, inf_ds, ds - (8 - 2 * kDmaPerTile));
           }
+          if (dma_now) dma_bits(PD{}, STD, inf_ds);
         }
 #pragma unroll
         for (int j2 = 0; j2 < 4; ++j2) {
@@ -474,9 +496,8 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         // the mask and row max of S(j+1) and, when a row's max grew by more than 2^8, the
         // rescale of O and l.
         const bool has_next = STEADY || j + 1 < n;
-        const uint2 inf_d = uniform(inf_dma);
         const uint2 inf_m = uniform(inf_msk);
-        if (STEADY || j + NS < n) dma_step(std::integral_constant<int, JS & 1>{}, JS, inf_d);
+        if (!SPREAD && (STEADY || j + NS < n)) dma_step(std::integral_constant<int, JS & 1>{}, JS, uniform(inf_dma));
         if (STEADY || j + 2 < n) {
 #pragma unroll
           for (int ds = 0; ds < 8; ++ds) kf[ds] = lds_b128(kad[ds] + ST2 * SB);
@@ -486,7 +507,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
           for (int i = 0; i < 8; ++i)
             vf[i] = VP ? lds_b128(kad[i] + kAltTile + ST1 * SB)
                        : lds_v_operand(vad[i & 3] + ST1 * SB + (i >> 2) * 4096);
-          inf_dma = info(j + 1 + NS);
+          inf_dma = info(SPREAD ? j + NS : j + 1 + NS);
           inf_msk = info(j + 2);
           int kind, thr;
           step_info(std::integral_constant<int, NXT>{}, inf_m, kind, thr);
