@@ -18,8 +18,8 @@
 //    Q held for the whole launch) in fenced groups of one product beside two exponentials of
 //    S(j); then O^T += V(j)^T P(j)^T beside the bf16 packing and row sum of S(j); one barrier;
 //    then the LDS reads of the next operands (K(j+2), V(j+1)), and the mask and row max of
-//    S(j+1). The DMA of step j+kAltStages-1 goes out beside the last four products of S(j+1),
-//    one instruction each (with a soft cap: the DMA of step j+kAltStages after the barrier).
+//    S(j+1). The DMA of step j+kAltStages-1 goes out one instruction beside each of the last
+//    four products of S(j+1) (with a soft cap: of the second half of O^T += V^T P^T).
 //    The loop is unrolled by the ring depth, so stage offsets are immediates of the reads and
 //    the two score register sets alternate. Scores are transposed, so a lane owns one query
 //    row: row max and row sum are in-lane plus one v_permlane32_swap with the partner lane.
@@ -175,11 +175,10 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
   constexpr int NS = kAltStages;
   constexpr int SB = alt_stage_bytes<BITS>();
   constexpr int NDMA = 2 * kDmaPerTile + (BITS ? 1 : 0);   // DMA instructions per wave and step
-  // Where a step's DMA is issued. Without a soft cap, the DMA of step j + NS - 1 goes out one
-  // instruction beside each of the last products of S(j+1): a burst of LDS-DMA instructions from
-  // every wave right after the barrier holds each wave for tens of cycles per instruction. With
-  // a cap (VALU-bound), the DMA of step j + NS follows step j's barrier.
-  constexpr bool SPREAD = !CAP;
+  // Step j issues the DMA of step j + NS - 1 one instruction at a time beside its products (the
+  // last four of S(j+1), or with a soft cap the second half of O += V P): a burst of LDS-DMA
+  // instructions from every wave right after the barrier holds each wave for tens of cycles per
+  // instruction.
   // NS stages of SB bytes, then the visit's tile list (AltTile records, p.nKb of them), staged
   // once per visit so that the loop reads it from LDS instead of waiting on scalar loads
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -354,7 +353,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
     }
     __syncthreads();
     if (n > 0) {
-      const int pre = min(SPREAD ? NS - 1 : NS, n);
+      const int pre = min(NS - 1, n);
       {
         uint2 inf[(NS + 1) / 2];
 #pragma unroll
@@ -404,7 +403,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         vf[i] = VP ? lds_b128(kad[i] + kAltTile) : lds_v_operand(vad[i & 3] + (i >> 2) * 4096);
-      uint2 inf_dma = info(SPREAD ? NS - 1 : NS), inf_msk = info(1);
+      uint2 inf_dma = info(NS - 1), inf_msk = info(1);
 
       // Step j (stage j % NS == JS): products, barrier, loads. STEADY: a step at least 2 NS - 1
       // steps before the end, which issues its DMA and reads the next operands unconditionally
@@ -424,12 +423,12 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         // matrix products are ready issues first and the other fills the slots between them.
         __builtin_amdgcn_s_setprio(1);
         Sn = f32x16{};
-        // SPREAD: the DMA of step j + NS - 1, into the stage of step j - 1 (every wave is past
-        // the barrier that followed its last reads)
-        const bool dma_now = SPREAD && (STEADY || j + NS - 1 < n);
+        // the DMA of step j + NS - 1, into the stage of step j - 1 (every wave is past the barrier
+        // that followed its last reads)
+        const bool dma_now = STEADY || j + NS - 1 < n;
         using PD = std::integral_constant<int, (JS + 1) & 1>;
         constexpr int STD = (JS + NS - 1) % NS;
-        const uint2 inf_ds = SPREAD ? uniform(inf_dma) : uint2{};
+        const uint2 inf_ds = uniform(inf_dma);
         {
           const float msub = (m_ref == neg_inf()) ? 0.0f : m_ref;
           // weight = exp2(logit - m): the logit is sc * s without a cap, c (1 + 2u) with one
@@ -445,7 +444,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
             asm volatile("" : "+v"(Sn), "+v"(e0), "+v"(e1));
             Sc[2 * ds] = e0;
             Sc[2 * ds + 1] = e1;
-            if (ds >= 8 - 2 * kDmaPerTile && dma_now) dma_piece(PD{}, STD, inf_ds, ds - (8 - 2 * kDmaPerTile));
+            if (!CAP && ds >= 8 - 2 * kDmaPerTile && dma_now) dma_piece(PD{}, STD, inf_ds, ds - (8 - 2 * kDmaPerTile));
           }
           if (dma_now) dma_bits(PD{}, STD, inf_ds);
         }
@@ -472,7 +471,11 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) O[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 + i], P[1], O[i], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          O[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 + i], P[1], O[i], 0, 0, 0);
+          if (CAP && dma_now) dma_piece(PD{}, STD, inf_ds, i);
+          if (CAP) __builtin_amdgcn_sched_barrier(0);
+        }
         __builtin_amdgcn_s_setprio(0);
         {
           // row sum as a tree, in fp32 (bf16 weights would put up to 2^-9 into the lse of a row
@@ -497,7 +500,6 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         // rescale of O and l.
         const bool has_next = STEADY || j + 1 < n;
         const uint2 inf_m = uniform(inf_msk);
-        if (!SPREAD && (STEADY || j + NS < n)) dma_step(std::integral_constant<int, JS & 1>{}, JS, uniform(inf_dma));
         if (STEADY || j + 2 < n) {
 #pragma unroll
           for (int ds = 0; ds < 8; ++ds) kf[ds] = lds_b128(kad[ds] + ST2 * SB);
@@ -507,7 +509,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
           for (int i = 0; i < 8; ++i)
             vf[i] = VP ? lds_b128(kad[i] + kAltTile + ST1 * SB)
                        : lds_v_operand(vad[i & 3] + ST1 * SB + (i >> 2) * 4096);
-          inf_dma = info(SPREAD ? j + NS : j + 1 + NS);
+          inf_dma = info(j + NS);
           inf_msk = info(j + 2);
           int kind, thr;
           step_info(std::integral_constant<int, NXT>{}, inf_m, kind, thr);
