@@ -19,7 +19,8 @@
 //    S(j); then O^T += V(j)^T P(j)^T beside the bf16 packing and row sum of S(j); one barrier;
 //    then the LDS reads of the next operands (K(j+2), V(j+1)), and the mask and row max of
 //    S(j+1). The DMA of step j+kAltStages-1 goes out one instruction beside each of the last
-//    four products of S(j+1) (with a soft cap: of the second half of O^T += V^T P^T).
+//    four products of S(j+1) (with a soft cap: of the second half of O^T += V^T P^T, and step
+//    j reads V(j) itself halfway through the products of S(j+1)).
 //    The loop is unrolled by the ring depth, so stage offsets are immediates of the reads and
 //    the two score register sets alternate. Scores are transposed, so a lane owns one query
 //    row: row max and row sum are in-lane plus one v_permlane32_swap with the partner lane.
@@ -179,6 +180,10 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
   // last four of S(j+1), or with a soft cap the second half of O += V P): a burst of LDS-DMA
   // instructions from every wave right after the barrier holds each wave for tens of cycles per
   // instruction.
+  // LATE_V: with a soft cap, step j reads its V operands itself, halfway through the products of
+  // S(j+1), instead of the step before reading them after its barrier (measured faster for the
+  // cap kernels only, whose step is longer).
+  constexpr bool LATE_V = CAP;
   // NS stages of SB bytes, then the visit's tile list (AltTile records, p.nKb of them), staged
   // once per visit so that the loop reads it from LDS instead of waiting on scalar loads
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -400,9 +405,11 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
       for (int db = 0; db < 4; ++db) vad[db] = lds0 + v_rd[db];
 #pragma unroll
       for (int ds = 0; ds < 8; ++ds) kf[ds] = lds_b128(kad[ds] + SB);
+      if constexpr (!LATE_V) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        vf[i] = VP ? lds_b128(kad[i] + kAltTile) : lds_v_operand(vad[i & 3] + (i >> 2) * 4096);
+        for (int i = 0; i < 8; ++i)
+          vf[i] = VP ? lds_b128(kad[i] + kAltTile) : lds_v_operand(vad[i & 3] + (i >> 2) * 4096);
+      }
       uint2 inf_dma = info(NS - 1), inf_msk = info(1);
 
       // Step j (stage j % NS == JS): products, barrier, loads. STEADY: a step at least 2 NS - 1
@@ -436,6 +443,14 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
           const float sub = CAP ? p.cap_log2 - msub : -msub;
 #pragma unroll
           for (int ds = 0; ds < 8; ++ds) {
+            if (LATE_V && ds == 4) {
+              // V(j): its tile landed before the barrier of step j - 2, and the barrier of step j
+              // follows the products that use it
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int i = 0; i < 8; ++i)
+                vf[i] = VP ? lds_b128(kad[i] + kAltTile + JS * SB) : lds_v_operand(vad[i & 3] + JS * SB + (i >> 2) * 4096);
+            }
             Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[ds], Sn, 0, 0, 0);
             float e0 = fast_exp2(__builtin_fmaf(Sc[2 * ds], sc, sub));
             float e1 = fast_exp2(__builtin_fmaf(Sc[2 * ds + 1], sc, sub));
@@ -505,10 +520,12 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
           for (int ds = 0; ds < 8; ++ds) kf[ds] = lds_b128(kad[ds] + ST2 * SB);
         }
         if (has_next) {
+          if constexpr (!LATE_V) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            vf[i] = VP ? lds_b128(kad[i] + kAltTile + ST1 * SB)
-                       : lds_v_operand(vad[i & 3] + ST1 * SB + (i >> 2) * 4096);
+            for (int i = 0; i < 8; ++i)
+              vf[i] = VP ? lds_b128(kad[i] + kAltTile + ST1 * SB)
+                         : lds_v_operand(vad[i & 3] + ST1 * SB + (i >> 2) * 4096);
+          }
           inf_dma = info(j + NS);
           inf_msk = info(j + 2);
           int kind, thr;
