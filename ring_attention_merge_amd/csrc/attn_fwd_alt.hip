@@ -184,6 +184,9 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
   // S(j+1), instead of the step before reading them after its barrier (measured faster for the
   // cap kernels only, whose step is longer).
   constexpr bool LATE_V = CAP;
+  // EARLY_MAX: with a soft cap, the mask, row max and rescale of S(j+1) run before step j's
+  // barrier (after its products) instead of after it (measured faster for the cap kernels only).
+  constexpr bool EARLY_MAX = CAP;
   // NS stages of SB bytes, then the visit's tile list (AltTile records, p.nKb of them), staged
   // once per visit so that the loop reads it from LDS instead of waiting on scalar loads
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -422,6 +425,23 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         constexpr int ST1 = (JS + 1) % NS, ST2 = (JS + 2) % NS;
         f32x16& Sc = S2[CUR];
         f32x16& Sn = S2[NXT];
+        // mask and row max of S(j+1) (tile record inf_m) and, when a row's max grew by more than
+        // 2^8, the rescale of O and l (after the products of step j, which used the previous max)
+        auto next_max = [&](uint2 inf_m) {
+          int kind, thr;
+          step_info(std::integral_constant<int, NXT>{}, inf_m, kind, thr);
+          step_cap<CAP>(Sn, p);
+          step_mask<BITS>(Sn, kind, thr, BITS ? lds_b32(lds0 + ST1 * SB + b_rd + 4 * ((JS + 1) & 1)) : 0u, lg);
+          float m_new, alpha;
+          if (step_max<CAP>(Sn, m_ref, m_new, alpha, p)) {
+            l_acc *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
+            m_ref = m_new;
+          }
+        };
         // ---------------------------------------------------------------- products of step j
         // S(j+1) = K(j+1) Q^T in fenced groups of one product and two exponentials of S(j), then
         // O^T += V(j)^T P(j)^T beside the bf16 packing. On the last step the first product runs
@@ -501,6 +521,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
           const float t3 = (Sc[12] + Sc[13]) + (Sc[14] + Sc[15]);
           l_acc += (t0 + t1) + (t2 + t3);
         }
+        if (EARLY_MAX && (STEADY || j + 1 < n)) next_max(uniform(inf_msk));
         // step j+2's tile (read below) has landed: this wave issued its DMA through step
         // min(n, j+NS)-1, the tile's being at most NS-3 steps before the newest; the barrier
         // makes every wave's share visible and shows that every wave is done with step j's
@@ -514,7 +535,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         // the mask and row max of S(j+1) and, when a row's max grew by more than 2^8, the
         // rescale of O and l.
         const bool has_next = STEADY || j + 1 < n;
-        const uint2 inf_m = uniform(inf_msk);
+        const uint2 inf_m = EARLY_MAX ? uint2{} : uniform(inf_msk);   // S(j+1)'s record
         if (STEADY || j + 2 < n) {
 #pragma unroll
           for (int ds = 0; ds < 8; ++ds) kf[ds] = lds_b128(kad[ds] + ST2 * SB);
@@ -528,19 +549,7 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
           }
           inf_dma = info(j + NS);
           inf_msk = info(j + 2);
-          int kind, thr;
-          step_info(std::integral_constant<int, NXT>{}, inf_m, kind, thr);
-          step_cap<CAP>(Sn, p);
-          step_mask<BITS>(Sn, kind, thr, BITS ? lds_b32(lds0 + ST1 * SB + b_rd + 4 * ((JS + 1) & 1)) : 0u, lg);
-          float m_new, alpha;
-          if (step_max<CAP>(Sn, m_ref, m_new, alpha, p)) {
-            l_acc *= alpha;
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
-            m_ref = m_new;
-          }
+          if constexpr (!EARLY_MAX) next_max(inf_m);
         }
       };
       static_assert(NS == 4, "the step loop is unrolled by the ring depth");
