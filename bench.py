@@ -434,6 +434,35 @@ def mfma_rates(dev, stream) -> dict:
     return res
 
 
+def graph_leg(args, step, eff_flops, out, lse):
+    """The same step captured once in a HIP graph and replayed: the ring call launches only
+    kernels on its stream (no allocation, memset or host synchronisation), so the replays run the
+    identical work without the host's launch gaps between the kernels. The first replay's result
+    is checked bit for bit against the eager step's."""
+    ref_out, ref_lse = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        step(torch.cuda.current_stream())
+    out.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, ref_out) and torch.equal(lse, ref_lse))
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = eff_flops / (ms * 1e-3) / 1e12
+    log(f"graph replay: step {ms:.3f} ms, {tflops:.1f} effective TFLOP/s; replay equals the eager step: {same}")
+    return {"ms_per_step": round(ms, 4), "value": round(tflops, 2), "replay_equals_eager": same,
+            "timing": "K replays of the captured step between two events"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -443,6 +472,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--backward", action="store_true", help="time the ring backward instead of the forward")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph and replayed (no host launch gaps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (to scale FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -480,8 +511,9 @@ def main():
         f"{'agrees' if lib_tiles == ref_tiles else lib_tiles}); effective FLOPs {eff_flops:.4e}")
     tiles_info = {"nonempty_tiles_128": sum(ref_tiles), "library_count_agrees": lib_tiles == ref_tiles}
 
-    def step():
-        ram.ring_attn_fwd_1gpu(desc, w.n_chunks, w.q_shard, q, k, v, src, sinks, out, lse, ws, stream=stream)
+    def step(on=None):
+        ram.ring_attn_fwd_1gpu(desc, w.n_chunks, w.q_shard, q, k, v, src, sinks, out, lse, ws,
+                               stream=stream if on is None else on)
 
     if args.backward:
         return backward(args, w, desc, q, k, v, src, sinks, out, lse, ws, stream, dense, eff_flops_chunk, step)
@@ -523,6 +555,7 @@ def main():
                 "mean_launch_us": round(1e3 * kern_ms / launches, 2),
                 "timing": "HIP events around the attention launch in each of the timed steps; median",
                 "flops_per_launch_mean": eff_flops / launches}
+    graph = graph_leg(args, step, eff_flops, out, lse) if args.graph else None
     measured = mfma_rates(dev, stream)
     roofline["measured_peak_random"] = measured["random"]
     roofline["frac_of_measured_random"] = round(achieved / measured["random"], 4)
@@ -558,6 +591,8 @@ def main():
     }
     if builder is not None:
         line["mask_builder"] = builder
+    if graph is not None:
+        line["graph"] = graph
     print(json.dumps(line), flush=True)
 
 
