@@ -313,8 +313,10 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
       // of one query row), so the dense mask is read in long contiguous runs, and
       // kBatch words per thread at a time: their positions and segments first,
       // then all their dense-mask loads together (latency, not bandwidth, bounds
-      // a thread that waits for each word's bytes before loading the next).
-      constexpr int kBatch = 4;
+      // a thread that waits for each word's bytes before loading the next). Two
+      // words measured fastest (2.4 TB/s over a 32k x 32k mask; four: 2.0, eight:
+      // 1.5), more workgroups per CU outweighing the loads each thread keeps in flight.
+      constexpr int kBatch = 2;
       for (int u0 = tid; u0 < nw; u0 += kBatch * kThreads) {
         uint32_t wv[kBatch], valv[kBatch];
         int tv[kBatch], tlv[kBatch], iv[kBatch], j0v[kBatch], jnv[kBatch];
