@@ -531,9 +531,9 @@ __global__ __launch_bounds__(kAltThreads, 2) void attn_fwd_bf16_alt(AttnParams p
         barrier();
 
         // ---------------------------------------------------------------- loads of step j
-        // The DMA into step j's stage, the operand and list reads for the next products, then
-        // the mask and row max of S(j+1) and, when a row's max grew by more than 2^8, the
-        // rescale of O and l.
+        // The operand reads for the next products (K(j+2), and V(j+1) unless LATE_V) and the
+        // list reads, then (unless EARLY_MAX) the mask and row max of S(j+1) and, when a row's
+        // max grew by more than 2^8, the rescale of O and l.
         const bool has_next = STEADY || j + 1 < n;
         const uint2 inf_m = EARLY_MAX ? uint2{} : uniform(inf_msk);   // S(j+1)'s record
         if (STEADY || j + 2 < n) {
