@@ -19,9 +19,9 @@ closed forms, library routines, brute force and invariants; the soft-cap
 formula itself is a reading (the pages give only the parameter), pinned to its
 closed form and its large-cap limit, but not to any value on the pages.
 """
-from .attention import (allowed, attention, attention_bwd, merge, chunked, chunked_bwd,
+from .attention import (allowed, attention, attention_bwd, attention_dq, merge, chunked, chunked_bwd,
                         DEFAULT_MASK_VALUE, PAD_SEGMENT_ID)
 from .blockmask import block_mask, partial_bits, TILE_EMPTY, TILE_PARTIAL, TILE_FULL
 
-__all__ = ["allowed", "attention", "attention_bwd", "merge", "chunked", "chunked_bwd", "block_mask", "partial_bits", "DEFAULT_MASK_VALUE",
+__all__ = ["allowed", "attention", "attention_bwd", "attention_dq", "merge", "chunked", "chunked_bwd", "block_mask", "partial_bits", "DEFAULT_MASK_VALUE",
            "PAD_SEGMENT_ID", "TILE_EMPTY", "TILE_PARTIAL", "TILE_FULL"]

@@ -264,6 +264,56 @@ def attention_bwd(q, k, v, dout, *, scale, q_pos, kv_pos, q_seg=None, kv_seg=Non
     return dq, dk, dv, dsinks
 
 
+def attention_dq(q, k, v, dout, *, scale, q_pos, kv_pos, q_seg=None, kv_seg=None, causal=True,
+                 softcap=None, sinks=None, dense=None):
+    """The query gradient alone, for the query rows passed, in float64.
+
+    [bwd] the chunk backward's dq term (its sum over the ring's chunks is the whole-KV
+    gradient, see ``chunked_bwd``). The gradient of ``attention`` with respect to query row i depends only on that row
+    and on every key, so a caller may pass a sample of rows (with their positions,
+    segment IDs and dense-mask rows) to check a full-size result row by row. With the
+    same notation as ``attention_bwd``:
+        dq_i = scale * sum over allowed j of p_ij (dp_ij - D_i) (1 - t_ij^2) k_j
+    where p_ij = exp(u_ij - lse_i), dp_ij = dout_i . v_j and D_i = dout_i . out_i, with
+    (out_i, lse_i) from ``attention`` on the same rows (the sink, when given, enters only
+    through lse_i and out_i). Returns dq with q's shape.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    dout = np.asarray(dout, np.float64)
+    B, Sq, H, D = q.shape
+    Hkv = k.shape[2]
+    if H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    per_kv = H // Hkv
+    out, lse = attention(q, k, v, scale=scale, q_pos=q_pos, kv_pos=kv_pos, q_seg=q_seg, kv_seg=kv_seg,
+                         causal=causal, softcap=softcap, sinks=sinks, dense=dense)
+    grad = np.zeros_like(q)
+    for b in range(B):
+        keep = allowed(np.asarray(q_pos)[b], np.asarray(kv_pos)[b],
+                       None if q_seg is None else np.asarray(q_seg)[b],
+                       None if kv_seg is None else np.asarray(kv_seg)[b], causal,
+                       None if dense is None else np.asarray(dense))
+        for h in range(H):
+            kv_h = h // per_kv
+            logz = lse[b, h]
+            seen = np.isfinite(logz)
+            logits = scale * np.einsum("id,jd->ij", q[b, :, h, :], k[b, :, kv_h, :])
+            tanh_t = None
+            if softcap is not None:
+                tanh_t = np.tanh(logits / softcap)
+                logits = softcap * tanh_t
+            prob = np.where(keep & seen[:, None], np.exp(logits - np.where(seen, logz, 0.0)[:, None]), 0.0)
+            g_prob = np.einsum("id,jd->ij", dout[b, :, h, :], v[b, :, kv_h, :])
+            delta = np.einsum("id,id->i", dout[b, :, h, :], out[b, :, h, :])
+            g_logit = prob * (g_prob - delta[:, None])
+            if tanh_t is not None:
+                g_logit = g_logit * (1.0 - tanh_t ** 2)
+            grad[b, :, h, :] = scale * np.einsum("ij,jd->id", g_logit, k[b, :, kv_h, :])
+    return grad
+
+
 def chunked_bwd(q, k, v, dout, *, scale, q_pos, kv_pos, bounds, q_seg=None, kv_seg=None, causal=True,
                 softcap=None, sinks=None, dense=None, dense_col0=None):
     """The ring backward: per-chunk gradients against the final (out, lse), summed.

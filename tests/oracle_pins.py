@@ -680,4 +680,37 @@ def pin_bwd_chunked_and_gqa(ora):
     _close(g1[3], g2[3], 1e-12, "gqa dsinks")
 
 
-ALL_PINS += [pin_bwd_autograd, pin_bwd_finite_differences, pin_bwd_chunked_and_gqa]
+def pin_bwd_dq_rows(ora):
+    """The query gradient of a sample of rows = torch autograd of the independent torch forward
+    over all rows, read at those rows (GQA, caps, sinks, segments with padding, shuffled
+    positions, dense masks with an empty row)."""
+    rng = np.random.default_rng(29)
+    for trial in range(8):
+        B, Hkv = 1 + trial % 2, int(rng.choice([1, 2]))
+        H = Hkv * int(rng.choice([2, 3]))
+        Sq, Skv, D = int(rng.integers(8, 40)), int(rng.integers(5, 40)), int(rng.choice([4, 8]))
+        segs = trial >= 4
+        q, k, v, qp, kp, qs, ks = _rand_problem(rng, B, Sq, Skv, H, Hkv, D, segs=segs,
+                                                shuffle_pos=trial % 3 == 1, pad=segs)
+        causal = trial % 4 != 3
+        cap = 1.7 if trial % 2 == 0 else None
+        sinks = rng.standard_normal(H) if trial % 3 != 2 else None
+        dense = (rng.random((Sq, Skv)) < 0.7) if trial in (1, 5) else None
+        if dense is not None:
+            dense[Sq // 3] = False
+        ok = np.stack([ora.allowed(qp[b], kp[b], None if qs is None else qs[b], None if ks is None else ks[b],
+                                   causal, dense) for b in range(B)])
+        dout = rng.standard_normal(q.shape)
+        tq = torch.from_numpy(q).requires_grad_()
+        o = _torch_forward(tq, torch.from_numpy(k), torch.from_numpy(v), 0.45, torch.from_numpy(ok), cap,
+                           None if sinks is None else torch.from_numpy(sinks))
+        (o * torch.from_numpy(dout)).sum().backward()
+        rows = np.sort(rng.choice(Sq, size=max(1, Sq // 3), replace=False))
+        got = ora.attention_dq(q[:, rows], k, v, dout[:, rows], scale=0.45, q_pos=qp[:, rows], kv_pos=kp,
+                               q_seg=None if qs is None else qs[:, rows], kv_seg=ks, causal=causal, softcap=cap,
+                               sinks=sinks, dense=None if dense is None else dense[rows])
+        _close(got, tq.grad.numpy()[:, rows], 1e-10, f"dq rows {trial}")
+        assert np.abs(got).max() > 0
+
+
+ALL_PINS += [pin_bwd_autograd, pin_bwd_finite_differences, pin_bwd_chunked_and_gqa, pin_bwd_dq_rows]

@@ -47,6 +47,10 @@ ATTN_MUTANTS = {
     "bwd_sink_every_chunk": ("sinks=sinks if c == 0 else None, dense=dense_c, out=out, lse=lse)",
                              "sinks=sinks, dense=dense_c, out=out, lse=lse)"),
     "bwd_chunk_local_lse": ("dense=dense_c, out=out, lse=lse)", "dense=dense_c, out=None, lse=None)"),
+    "dq_rows_delta_dropped": ("g_logit = prob * (g_prob - delta[:, None])", "g_logit = prob * g_prob"),
+    "dq_rows_cap_chain_dropped": ("g_logit = g_logit * (1.0 - tanh_t ** 2)", "g_logit = g_logit"),
+    "dq_rows_scale_dropped": ("grad[b, :, h, :] = scale * np.einsum", "grad[b, :, h, :] = np.einsum"),
+    "dq_rows_gqa_modulo": ("kv_h = h // per_kv", "kv_h = h % Hkv"),
 }
 MASK_MUTANTS = {
     "no_empty_tiles": ("elif tile.any():", "elif True:"),
@@ -78,7 +82,7 @@ def _mutant(which, key):
         m = _load(mask_path, "mut_blockmask", *MASK_MUTANTS[key])
     return types.SimpleNamespace(
         attention=a.attention, allowed=a.allowed, merge=a.merge, chunked=a.chunked,
-        attention_bwd=a.attention_bwd, chunked_bwd=a.chunked_bwd,
+        attention_bwd=a.attention_bwd, attention_dq=a.attention_dq, chunked_bwd=a.chunked_bwd,
         DEFAULT_MASK_VALUE=a.DEFAULT_MASK_VALUE, block_mask=m.block_mask, partial_bits=m.partial_bits,
         TILE_EMPTY=m.TILE_EMPTY, TILE_PARTIAL=m.TILE_PARTIAL, TILE_FULL=m.TILE_FULL)
 
