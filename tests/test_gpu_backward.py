@@ -336,44 +336,54 @@ def test_ring_backward_c2_full():
         _rel(nm, g, r, GRAD_TOL, "c2 full")
 
 
-def test_ring_backward_c5_sampled():
+FULL_SIZE_BWD = {
+    "c5": wl.c5_long_causal,
+    "c4_gqa_cap_sinks": wl.c4_gqa_cap_sinks,
+    "c4_mqa_cap_sinks": lambda: wl.c4_gqa_cap_sinks(Hkv=1),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_SIZE_BWD))
+def test_ring_backward_full_size_sampled(name):
     """The 32k causal ring that bench.py --backward times (B 1, H 32 / Hkv 8, Sq = Skv = 32768 in 8
-    chunks of 4096, D 128, bf16), at full size, against the oracle where it computes row by row:
+    chunks of 4096, D 128, bf16) and the soft-cap GQA / MQA rings with sinks (16384 keys in 4
+    chunks), at full size, against the oracle where it computes row by row:
     - dq at sampled query rows (edge rows of every chunk and seeded ones, every head), from
       oracle.attention_dq, which needs only those rows and every key;
     - dk and dv at the last 128 keys: under the causal mask only the last 128 query rows attend
       them, so oracle.attention_bwd over those rows (against every key) gives them exactly;
-    - an identity of the exact gradient over every key: within each KV head the dv rows sum to
-      the dout rows of all query rows and heads sharing it (each row's weights sum to one, and
-      every row here has an allowed key). Each GPU dv row is a bf16 value of float32 sums of
-      bf16 weights times dout, within 2^-8 of its exact value relative to its terms' magnitudes,
-      so the bound is 2^-8 of sum_j |dv_j| per element (plus float64 summation)."""
-    w = wl.c5_long_causal()
+    - without sinks, an identity of the exact gradient over every key: within each KV head the
+      dv rows sum to the dout rows of all query rows and heads sharing it (each row's weights
+      sum to one, and every row here has an allowed key). Each GPU dv row is a bf16 value of
+      float32 sums of bf16 weights times dout, within 2^-8 of its exact value relative to its
+      terms' magnitudes, so the bound is 2^-8 of sum_j |dv_j| per element (plus float64
+      summation)."""
+    w = FULL_SIZE_BWD[name]()
     dout = torch.from_numpy(np.random.default_rng(2005).standard_normal(
         (w.B, w.Sq, w.H, w.D)).astype(np.float32)).to(torch.bfloat16)
     say(f"ring_attn_bwd_1gpu {w.name} (full size, sampled rows and keys)")
     dq, dk, dv, _ = _run_ring_bwd(w, dout)
-    q64, k64, v64, _ = w.as_f64()
+    q64, k64, v64, s64 = w.as_f64()
     do64 = dout.double().numpy()
     qp, kp = w.positions()
+    kw = dict(scale=w.scale, kv_pos=kp, causal=True, softcap=w.softcap, sinks=s64)
     rows = wl.sampled_rows(w.Sq, w.chunk, n=24, seed=2006)
-    ref_dq = oracle.attention_dq(q64[:, rows], k64, v64, do64[:, rows], scale=w.scale, q_pos=qp[:, rows],
-                                 kv_pos=kp, causal=True)
-    _rel("dq", dq[:, rows], ref_dq, GRAD_TOL, f"c5 full, {len(rows)} sampled rows")
+    ref_dq = oracle.attention_dq(q64[:, rows], k64, v64, do64[:, rows], q_pos=qp[:, rows], **kw)
+    _rel("dq", dq[:, rows], ref_dq, GRAD_TOL, f"{name} full, {len(rows)} sampled rows")
     tail = 128
     r0 = w.Sq - tail
-    _, rdk, rdv, _ = oracle.attention_bwd(q64[:, r0:], k64, v64, do64[:, r0:], scale=w.scale, q_pos=qp[:, r0:],
-                                          kv_pos=kp, causal=True)
-    _rel("dk", dk[:, r0:], rdk[:, r0:], GRAD_TOL, f"c5 full, last {tail} keys")
-    _rel("dv", dv[:, r0:], rdv[:, r0:], GRAD_TOL, f"c5 full, last {tail} keys")
-    G = w.H // w.Hkv
-    lhs = dv.astype(np.float64).sum(axis=1)                                        # [B, Hkv, D]
-    rhs = do64.reshape(w.B, w.Sq, w.Hkv, G, w.D).sum(axis=(1, 3))                  # [B, Hkv, D]
-    bound = 2.0 ** -8 * np.abs(dv.astype(np.float64)).sum(axis=1) + 1e-9 * np.abs(rhs)
-    worst = float(np.max(np.abs(lhs - rhs) / bound))
-    say(f"c5 full: sum_j dv_j vs sum of dout over rows and heads: max |diff| {float(np.abs(lhs - rhs).max()):.3e}, "
-        f"at most {worst:.3f} of the rounding bound")
-    assert worst <= 1.0, f"c5 full: sum_j dv_j departs from the summed dout ({worst:.3f} of the bound)"
+    _, rdk, rdv, _ = oracle.attention_bwd(q64[:, r0:], k64, v64, do64[:, r0:], q_pos=qp[:, r0:], **kw)
+    _rel("dk", dk[:, r0:], rdk[:, r0:], GRAD_TOL, f"{name} full, last {tail} keys")
+    _rel("dv", dv[:, r0:], rdv[:, r0:], GRAD_TOL, f"{name} full, last {tail} keys")
+    if s64 is None:
+        G = w.H // w.Hkv
+        lhs = dv.astype(np.float64).sum(axis=1)                                        # [B, Hkv, D]
+        rhs = do64.reshape(w.B, w.Sq, w.Hkv, G, w.D).sum(axis=(1, 3))                  # [B, Hkv, D]
+        bound = 2.0 ** -8 * np.abs(dv.astype(np.float64)).sum(axis=1) + 1e-9 * np.abs(rhs)
+        worst = float(np.max(np.abs(lhs - rhs) / bound))
+        say(f"{name} full: sum_j dv_j vs sum of dout over rows and heads: max |diff| "
+            f"{float(np.abs(lhs - rhs).max()):.3e}, at most {worst:.3f} of the rounding bound")
+        assert worst <= 1.0, f"{name} full: sum_j dv_j departs from the summed dout ({worst:.3f} of the bound)"
 
 
 def test_backward_deterministic():
