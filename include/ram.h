@@ -192,8 +192,11 @@ ram_status lse_merge(int32_t B, int32_t Sq, int32_t H, int32_t D, float* out_acc
  * aligned; it holds the float32 output accumulator (bf16 only), the block
  * masks of every chunk (with their tile bits when the forward call would need
  * them, see attn_fwd_chunk), for a split ring the second half's running
- * result, and for bf16 with D = 128 a copy of v_all rearranged for the kernel
- * (the same size as v_all, rounded up to 32 keys per chunk).
+ * result, and, when the ring reads V repacked (bf16, D = 128, no soft cap and
+ * Sq * H / Hkv >= 32768), a copy of v_all rearranged for the kernel (the same
+ * size as v_all, rounded up to 32 keys per chunk).
+ * The call only launches kernels on `stream` (no allocation, memset or host
+ * synchronisation), so a caller may capture it in a HIP graph and replay it.
  * RAM_ERR_UNSUPPORTED for n_chunks or B above 65535. */
 ram_status ring_attn_fwd_1gpu(const ram_attn_desc* desc, int32_t n_chunks, int32_t q_shard,
                               const void* q, const void* k_all, const void* v_all,
