@@ -6,7 +6,9 @@ and replay it. Each case captures one call, then replays the graph three times w
 work on the same stream in between (the outputs refilled with NaN, and the ring run on other
 inputs into other buffers), and checks every replay bit for bit against an eager call on the same
 inputs. The cases cover the kernel's instantiations: repacked V (the 32k ring's path), packed
-documents (bits), a dense mask read over all keys, and a split ring with a soft cap and sinks."""
+documents (bits), a dense mask read over all keys, and a split ring with a soft cap and sinks.
+The no-allocation entry point, whose workspace is the GPU's static scratch, is captured the same
+way on two of them."""
 from __future__ import annotations
 
 import numpy as np
@@ -86,3 +88,36 @@ def test_ring_forward_graph_replays(name):
         assert torch.equal(io["out"], out_ref), f"{name}: replay {rep} output differs from the eager call"
         assert torch.equal(io["lse"], lse_ref), f"{name}: replay {rep} lse differs from the eager call"
     say(f"graph capture: {name} 3 replays bit-identical to the eager call")
+
+
+@pytest.mark.parametrize("name", ["packed_v_causal", "split_cap_sinks"])
+def test_noalloc_graph_replays(name):
+    """ring_attn_fwd_1gpu_noalloc, the entry point for callers that cannot allocate (code under
+    graph capture among them), captured in a graph and replayed three times with other eager
+    calls of it in between (they share the GPU's static scratch, one at a time on the stream):
+    every replay bit-identical to the eager call."""
+    c = CASES[name]
+    say(f"graph capture (no-alloc entry point): {name} {c}")
+    d, src, io = _setup(name, c, 4200)
+    d2, src2, io2 = _setup(name, c, 4201)
+
+    def call(d_, src_, io_):
+        ram.ring_attn_fwd_1gpu_noalloc(d_, c["n"], c["q_shard"], io_["q"], io_["k"], io_["v"], src_, io_["sinks"],
+                                       io_["out"], io_["lse"])
+
+    call(d, src, io)
+    torch.cuda.synchronize()
+    out_ref, lse_ref = io["out"].clone(), io["lse"].clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        call(d, src, io)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        io["out"].fill_(float("nan"))
+        io["lse"].fill_(float("nan"))
+        g.replay()
+        call(d2, src2, io2)
+        torch.cuda.synchronize()
+        assert torch.equal(io["out"], out_ref), f"{name}: no-alloc replay {rep} output differs from the eager call"
+        assert torch.equal(io["lse"], lse_ref), f"{name}: no-alloc replay {rep} lse differs from the eager call"
+    say(f"graph capture (no-alloc entry point): {name} 3 replays bit-identical to the eager call")
