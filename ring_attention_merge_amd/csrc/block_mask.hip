@@ -135,18 +135,49 @@ __device__ __forceinline__ void compact_row(const MaskParams& p, int64_t crow, c
   compact_row_impl(p, crow, cls_s, wsum);
 }
 
-__global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
-  __shared__ uint8_t cls_s[kMaxMaskCols];
-  __shared__ int qpos_s[kMaxMaskTile], qseg_s[kMaxMaskTile];
-  __shared__ __attribute__((aligned(16))) int kpos_s[kGroupKeys];
-  __shared__ __attribute__((aligned(16))) int kseg_s[kGroupKeys];
+// The parts of a workgroup's dynamic LDS, 16-byte aligned byte offsets: the bit words of a
+// round, the keys' positions and segments of a round, the rows' positions and segments, and the
+// row's tile classes. A part that a variant does not read has size 0.
+struct MaskLds {
+  int bits, kpos, kseg, qpos, qseg, cls, total;
+};
+__host__ __device__ inline int lds_round16(int b) { return (b + 15) & ~15; }
+__host__ __device__ inline MaskLds mask_lds(const MaskParams& p, bool pair, bool kpos, bool segs) {
+  const int tg = group_tiles(p.bq, p.bk);
+  MaskLds l;
+  int o = 0;
+  l.bits = o;
+  o += pair ? lds_round16(tg * p.bq * ((p.bk + 31) >> 5) * 4) : 0;
+  l.kpos = o;
+  o += pair && kpos ? lds_round16(tg * p.bk * 4) : 0;
+  l.kseg = o;
+  o += pair && segs ? lds_round16(tg * p.bk * 4) : 0;
+  l.qpos = o;
+  o += pair ? lds_round16(p.bq * 4) : 0;
+  l.qseg = o;
+  o += pair && segs ? lds_round16(p.bq * 4) : 0;
+  l.cls = o;
+  o += lds_round16(p.nKb);
+  l.total = o;
+  return l;
+}
+
+// PAIR: pairs are checked (segments, a dense mask or bits requested), else classes from ranges.
+// KPOS: explicit key positions (else sequential from kv_pos_base). SEGS: segment IDs on both
+// sides. DENSE: a dense mask. Each combination is its own kernel, so that one holds only the
+// registers and LDS its tests need; the dense mask alone fits 8 workgroups per CU (64 VGPRs).
+template <bool PAIR, bool KPOS, bool SEGS, bool DENSE>
+__global__ __launch_bounds__(kThreads, DENSE && !SEGS && !KPOS ? 8 : 4) void block_mask_kernel(MaskParams p) {
+  static_assert(2 * kGroupTiles <= 32, "two flag bits per tile of a round in one word");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int red[2 * kWaves];
   __shared__ int wsum[kWaves];
-  // the bit words of a round: group_tiles * words per tile (sized at launch, at most kGroupWords)
-  extern __shared__ uint32_t bits_s[];
-  __shared__ int flag_s[kGroupKeys / 16];
-  __shared__ int open_s[kGroupKeys / 16];   // a group has at most kGroupKeys / 16 tiles
+  __shared__ int open_s[kGroupTiles];
   __shared__ int n_open_s;
+  // per tile t of the round, bits 2t (a pair allowed) and 2t+1 (a pair excluded)
+  __shared__ uint32_t flags_s;
+  const MaskLds L = mask_lds(p, PAIR, KPOS, SEGS);
+  uint8_t* cls_s = lds + L.cls;
 
   const int qb = blockIdx.x / p.kv_split, b = blockIdx.y, c = blockIdx.z;
   const int split = blockIdx.x - qb * p.kv_split;   // this workgroup's group of key tiles
@@ -155,13 +186,13 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
   const int nq = min(p.Sq, q0 + p.bq) - q0;
   const int kv_base = p.kv_pos_base + c * p.kv_base_step;
   const int32_t* qpos = p.q_pos ? p.q_pos + (int64_t)b * p.qm_stride_b + q0 : nullptr;
-  const int32_t* qseg = p.q_seg ? p.q_seg + (int64_t)b * p.qm_stride_b + q0 : nullptr;
+  const int32_t* qseg = SEGS ? p.q_seg + (int64_t)b * p.qm_stride_b + q0 : nullptr;
   const int64_t kvoff = (int64_t)b * p.kvm_stride_b + (int64_t)c * p.kv_chunk_off;
-  const int32_t* kvpos = p.kv_pos ? p.kv_pos + kvoff : nullptr;
-  const int32_t* kvseg = p.kv_seg ? p.kv_seg + kvoff : nullptr;
+  const int32_t* kvpos = KPOS ? p.kv_pos + kvoff : nullptr;
+  const int32_t* kvseg = SEGS ? p.kv_seg + kvoff : nullptr;
   const int64_t crow = ((int64_t)c * p.B + b) * p.nQb + qb;   // row index over (chunk, batch, q tile)
 
-  if (qseg == nullptr && p.dense == nullptr && p.bits == nullptr) {
+  if constexpr (!PAIR) {
     // No segments or dense mask: classes from position ranges (exact: all pairs allowed iff
     // max kv <= min q; none iff max q < min kv).
     int qmin, qmax;
@@ -176,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
       qmin = p.q_pos_base + q0;
       qmax = p.q_pos_base + q0 + nq - 1;
     }
-    if (kvpos == nullptr) {
+    if constexpr (!KPOS) {
       for (int kb = tid; kb < p.nKb; kb += kThreads) {
         const int k0 = kb * p.bk;
         const int nk = min(p.Skv, k0 + p.bk) - k0;
@@ -206,23 +237,44 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
   } else {
     // Pairwise: positions, segments and the dense mask of every pair, a group
     // of tiles per round. Each thread builds 32-pair words of the tiles' bit
-    // rows; per-tile flags (bit 0: a pair allowed, bit 1: a pair excluded)
-    // give the classes.
+    // rows; per-tile flags (a pair allowed, a pair excluded) give the classes.
+    uint32_t* bits_s = reinterpret_cast<uint32_t*>(lds + L.bits);
+    int* kpos_s = reinterpret_cast<int*>(lds + L.kpos);
+    int* kseg_s = reinterpret_cast<int*>(lds + L.kseg);
+    int* qpos_s = reinterpret_cast<int*>(lds + L.qpos);
+    int* qseg_s = reinterpret_cast<int*>(lds + L.qseg);
     const int tg = group_tiles(p.bq, p.bk);
     // a split row: this workgroup's group only
     const int kb_first = p.kv_split > 1 ? split * tg : 0;
     const int kb_end = p.kv_split > 1 ? min(p.nKb, kb_first + tg) : p.nKb;
-    // The keys of a group into LDS (and its flags cleared); the first group's loads are issued
-    // here, beside the rows' (the barriers below cover them).
+    // The keys of a group into LDS, all of a thread's loads issued before the first store
+    // (a group holds at most kGroupKeys keys), and the flags cleared. The first group's loads
+    // are issued here, beside the rows' (the barriers below cover them).
     auto stage_group = [&](int kbg) {
-      const int ng = min(tg, p.nKb - kbg);
-      const int g0 = kbg * p.bk;
-      const int gk = min(p.Skv, (kbg + ng) * p.bk) - g0;
-      for (int j = tid; j < gk; j += kThreads) {
-        kpos_s[j] = kvpos ? kvpos[g0 + j] : kv_base + g0 + j;
-        kseg_s[j] = kvseg ? kvseg[g0 + j] : 0;
+      if constexpr (KPOS || SEGS) {
+        const int ng = min(tg, p.nKb - kbg);
+        const int g0 = kbg * p.bk;
+        const int gk = min(p.Skv, (kbg + ng) * p.bk) - g0;
+        constexpr int R = kGroupKeys / kThreads;
+        int pv[R] = {}, sv[R] = {};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int j = tid + r * kThreads;
+          if (j < gk) {
+            if constexpr (KPOS) pv[r] = kvpos[g0 + j];
+            if constexpr (SEGS) sv[r] = kvseg[g0 + j];
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int j = tid + r * kThreads;
+          if (j < gk) {
+            if constexpr (KPOS) kpos_s[j] = pv[r];
+            if constexpr (SEGS) kseg_s[j] = sv[r];
+          }
+        }
       }
-      for (int t = tid; t < ng; t += kThreads) flag_s[t] = 0;
+      if (tid == 0) flags_s = 0;
     };
     if (kb_first < kb_end) stage_group(kb_first);
     // ranges over the rows that can have an allowed key (padding rows have none)
@@ -230,15 +282,17 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
     bool qpad = false;
     for (int i = tid; i < nq; i += kThreads) {
       qpos_s[i] = qpos ? qpos[i] : p.q_pos_base + q0 + i;
-      qseg_s[i] = qseg ? qseg[i] : 0;
-      if (qseg_s[i] == -1 && qseg) {
-        qpad = true;
-        continue;
+      if constexpr (SEGS) {
+        qseg_s[i] = qseg[i];
+        if (qseg_s[i] == -1) {
+          qpad = true;
+          continue;
+        }
+        qsl = min(qsl, qseg_s[i]);
+        qsh = max(qsh, qseg_s[i]);
       }
       qpl = min(qpl, qpos_s[i]);
       qph = max(qph, qpos_s[i]);
-      qsl = min(qsl, qseg_s[i]);
-      qsh = max(qsh, qseg_s[i]);
     }
     // Tiles whose class follows from the rows' and keys' position and segment ranges are
     // decided before their pairs are checked (exactly: these are sufficient conditions); the
@@ -247,13 +301,13 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
     // (causal), disjoint segment ranges, or all rows or all keys padding. FULL (without a
     // dense mask, which can clear any pair): every key at or before every row, no padding,
     // and one segment on both sides.
-    int qpmin, qpmax, qsmin, qsmax;
+    int qpmin, qpmax, qsmin = 0, qsmax = 0;
     block_minmax(qpl, qph, red, qpmin, qpmax);
-    block_minmax(qsl, qsh, red, qsmin, qsmax);
-    const bool any_qpad = __syncthreads_or(qpad);
+    if constexpr (SEGS) block_minmax(qsl, qsh, red, qsmin, qsmax);
+    const bool any_qpad = SEGS ? __syncthreads_or(qpad) : false;
     const int W = (p.bk + 31) >> 5;   // words per tile row
     const int tw = p.bq * W;          // words per tile
-    const uint8_t* drow0 = p.dense ? p.dense + (int64_t)q0 * p.dense_ld + (int64_t)c * p.dense_col_step : nullptr;
+    const uint8_t* drow0 = DENSE ? p.dense + (int64_t)q0 * p.dense_ld + (int64_t)c * p.dense_col_step : nullptr;
     for (int kbg = kb_first; kbg < kb_end; kbg += tg) {
       const int ng = min(tg, p.nKb - kbg);
       const int g0 = kbg * p.bk;                           // first key of the group
@@ -266,32 +320,41 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
         const int t = t0 + (tid >> 4), l = tid & 15;
         const int nk = t < ng ? min(p.bk, gk - t * p.bk) : 0;
         int kpl = 0x7fffffff, kph = -0x7fffffff - 1, ksl = 0x7fffffff, ksh = -0x7fffffff - 1, kpad = 0;
-        for (int j = l; j < nk; j += 16) {
-          const int sg = kseg_s[t * p.bk + j];
-          if (sg == -1 && qseg) {
-            kpad = 1;
-            continue;
+        if constexpr (KPOS || SEGS) {
+          for (int j = l; j < nk; j += 16) {
+            int sg = 0;
+            if constexpr (SEGS) {
+              sg = kseg_s[t * p.bk + j];
+              if (sg == -1) {
+                kpad = 1;
+                continue;
+              }
+            }
+            const int kp = KPOS ? kpos_s[t * p.bk + j] : kv_base + g0 + t * p.bk + j;
+            kpl = min(kpl, kp);
+            kph = max(kph, kp);
+            ksl = min(ksl, sg);
+            ksh = max(ksh, sg);
           }
-          kpl = min(kpl, kpos_s[t * p.bk + j]);
-          kph = max(kph, kpos_s[t * p.bk + j]);
-          ksl = min(ksl, sg);
-          ksh = max(ksh, sg);
-        }
 #pragma unroll
-        for (int o = 8; o > 0; o >>= 1) {
-          kpl = min(kpl, __shfl_xor(kpl, o, 16));
-          kph = max(kph, __shfl_xor(kph, o, 16));
-          ksl = min(ksl, __shfl_xor(ksl, o, 16));
-          ksh = max(ksh, __shfl_xor(ksh, o, 16));
-          kpad |= __shfl_xor(kpad, o, 16);
+          for (int o = 8; o > 0; o >>= 1) {
+            kpl = min(kpl, __shfl_xor(kpl, o, 16));
+            kph = max(kph, __shfl_xor(kph, o, 16));
+            ksl = min(ksl, __shfl_xor(ksl, o, 16));
+            ksh = max(ksh, __shfl_xor(ksh, o, 16));
+            kpad |= __shfl_xor(kpad, o, 16);
+          }
+        } else if (nk > 0) {
+          // sequential keys, no padding
+          kpl = kv_base + g0 + t * p.bk;
+          kph = kpl + nk - 1;
         }
         if (t < ng) {
-          const bool segs = qseg != nullptr;
           // (with no non-padding rows or keys the ranges are empty: min > max)
           const bool empty = nk <= 0 || qpmin > qpmax || kpl > kph || (p.causal && kpl > qpmax) ||
-                             (segs && (ksh < qsmin || ksl > qsmax));
-          const bool full = p.dense == nullptr && !any_qpad && !kpad && (!p.causal || kph <= qpmin) &&
-                            (!segs || (qsmin == qsmax && ksl == ksh && qsmin == ksl));
+                             (SEGS && (ksh < qsmin || ksl > qsmax));
+          const bool full = !DENSE && !any_qpad && !kpad && (!p.causal || kph <= qpmin) &&
+                            (!SEGS || (qsmin == qsmax && ksl == ksh && qsmin == ksl));
           const uint8_t cl = empty ? 0 : (full ? 2 : 3);
           if (l == 0) cls_s[kbg + t] = cl;
           open = open || cl == 3;
@@ -312,11 +375,13 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
       // Words are taken row by row (consecutive threads: consecutive 32-key words
       // of one query row), so the dense mask is read in long contiguous runs, and
       // kBatch words per thread at a time: their positions and segments first,
-      // then all their dense-mask loads together (latency, not bandwidth, bounds
-      // a thread that waits for each word's bytes before loading the next). Two
-      // words measured fastest (2.4 TB/s over a 32k x 32k mask; four: 2.0, eight:
-      // 1.5), more workgroups per CU outweighing the loads each thread keeps in flight.
-      constexpr int kBatch = 2;
+      // then all their dense-mask loads together. A thread's flags stay in a
+      // register until the round ends. With a dense mask, one word per thread:
+      // the rate follows the workgroups resident per CU, not the loads each
+      // thread keeps in flight (over a 32k x 32k causal mask, 4.0 TB/s at one
+      // word and 8 waves per SIMD; 3.5 at two words and 5 waves; 3.1 at four).
+      constexpr int kBatch = DENSE ? 1 : 2;
+      uint32_t fl = 0;
       for (int u0 = tid; u0 < nw; u0 += kBatch * kThreads) {
         uint32_t wv[kBatch], valv[kBatch];
         int tv[kBatch], tlv[kBatch], iv[kBatch], j0v[kBatch], jnv[kBatch];
@@ -334,11 +399,11 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
           j0v[k] = j0;
           jnv[k] = jn;
           uint32_t w = 0, valid = 0;
-          if (u < nw && i < nq && jn > 0 && cls_s[kbg + tl] == 3) {
+          if (u < nw && i < nq && jn > 0) {
             valid = jn == 32 ? ~0u : ((1u << jn) - 1u);
             w = valid;
             if (p.causal) {
-              if (!kvpos) {
+              if constexpr (!KPOS) {
                 // sequential keys: the allowed ones are a prefix of the word
                 const int64_t lim = (int64_t)qpos_s[i] - ((int64_t)kv_base + g0 + j0);
                 w &= lim < 0 ? 0u : (lim >= 31 ? ~0u : ((2u << lim) - 1u));
@@ -346,15 +411,17 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
                 w &= key_bits<false>(kpos_s, j0, jn, qpos_s[i]);
               }
             }
-            if (qseg && w) {
-              const int qs = qseg_s[i];
-              w &= qs != -1 ? key_bits<true>(kseg_s, j0, jn, qs) : 0u;
+            if constexpr (SEGS) {
+              if (w) {
+                const int qs = qseg_s[i];
+                w &= qs != -1 ? key_bits<true>(kseg_s, j0, jn, qs) : 0u;
+              }
             }
           }
           wv[k] = w;
           valv[k] = valid;
         }
-        if (drow0) {
+        if constexpr (DENSE) {
           uint4 lo[kBatch], hi[kBatch];
 #pragma unroll
           for (int k = 0; k < kBatch; ++k) {
@@ -377,14 +444,19 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
         for (int k = 0; k < kBatch; ++k) {
           if (u0 + k * kThreads >= nw) continue;
           const uint32_t w = wv[k];
-          const int f = valv[k] ? ((w != 0 ? 1 : 0) | (w != valv[k] ? 2 : 0)) : 0;
-          if (f) atomicOr(&flag_s[tlv[k]], f);
+          const uint32_t f = valv[k] ? ((w != 0 ? 1u : 0u) | (w != valv[k] ? 2u : 0u)) : 0u;
+          fl |= f << (2 * tlv[k]);
           bits_s[tv[k]] = w;
         }
       }
+      // the round's flags: OR over the wave, then one LDS atomic per wave
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o);
+      if ((tid & 63) == 0 && fl) atomicOr(&flags_s, fl);
       __syncthreads();
+      const uint32_t flags = flags_s;
       for (int t = tid; t < ng; t += kThreads) {
-        const int f = flag_s[t];
+        const uint32_t f = (flags >> (2 * t)) & 3u;
         if (cls_s[kbg + t] == 3) cls_s[kbg + t] = (f & 1) ? ((f & 2) ? 1 : 2) : 0;
       }
       if (p.bits) {
@@ -393,10 +465,10 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(MaskParams p) {
         for (int u = tid; u < nw; u += kThreads) {
           const int oi = (int)div_tw.div((uint32_t)u);
           const int t = open_s[oi], o = t * tw + (u - oi * tw);
-          if (flag_s[t] == 3) dst[o] = bits_s[o];
+          if (((flags >> (2 * t)) & 3u) == 3u) dst[o] = bits_s[o];
         }
       }
-      __syncthreads();   // the next group rewrites kpos_s / kseg_s / bits_s / flag_s
+      __syncthreads();   // the next group rewrites kpos_s / kseg_s / bits_s / flags_s
     }
   }
   __syncthreads();
@@ -506,14 +578,22 @@ hipError_t launch_block_mask(const MaskParams& p_in, int n_chunks, hipStream_t s
   MaskParams p = p_in;
   // Rows checked pair by pair (segments, a dense mask or stored bits) take one workgroup per
   // group of key tiles when a row has several groups, so that a row's rounds run side by side.
-  const bool pairwise = p.q_seg != nullptr || p.dense != nullptr || p.bits != nullptr;
+  const bool segs = p.q_seg != nullptr, dense = p.dense != nullptr, kpos = p.kv_pos != nullptr;
+  const bool pair = segs || dense || p.bits != nullptr;
   const int tg = group_tiles(p.bq, p.bk);
-  p.kv_split = pairwise ? (p.nKb + tg - 1) / tg : 1;
+  p.kv_split = pair ? (p.nKb + tg - 1) / tg : 1;
   if (p.kv_split < 1) p.kv_split = 1;
-  // LDS for the round's bit words only where pairs are checked
-  const size_t words = pairwise ? (size_t)tg * p.bq * ((p.bk + 31) / 32) : 0;
-  hipLaunchKernelGGL(block_mask_kernel, dim3(p.nQb * p.kv_split, p.B, n_chunks), dim3(kThreads),
-                     words * sizeof(uint32_t), s, p);
+  using Kernel = void (*)(MaskParams);
+  static constexpr Kernel kRange[2] = {block_mask_kernel<false, false, false, false>,
+                                       block_mask_kernel<false, true, false, false>};
+  static constexpr Kernel kPair[8] = {
+      block_mask_kernel<true, false, false, false>, block_mask_kernel<true, false, false, true>,
+      block_mask_kernel<true, false, true, false>,  block_mask_kernel<true, false, true, true>,
+      block_mask_kernel<true, true, false, false>,  block_mask_kernel<true, true, false, true>,
+      block_mask_kernel<true, true, true, false>,   block_mask_kernel<true, true, true, true>};
+  const Kernel k = pair ? kPair[(kpos ? 4 : 0) | (segs ? 2 : 0) | (dense ? 1 : 0)] : kRange[kpos ? 1 : 0];
+  const size_t lds = (size_t)mask_lds(p, pair, kpos, segs).total;
+  hipLaunchKernelGGL(k, dim3(p.nQb * p.kv_split, p.B, n_chunks), dim3(kThreads), lds, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.kv_split == 1) return e;
   hipLaunchKernelGGL(block_mask_compact, dim3(p.nQb, p.B, n_chunks), dim3(kThreads), 0, s, p);
